@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""SplitZip codec benchmark on one MI355X.
+
+One step = one pass of the whole hot path over one batch: encode the
+Llama-3-8B-shaped KV cache (32 layers x {K,V} x 8 KV heads x 128 dims x
+8192 tokens = 536,870,912 BF16 values, 1 GiB) into a SplitZip stream and
+decode it back.  Inputs are generated on the device and resident in HBM
+before the timed region; the codebook is calibrated offline (host, untimed)
+on a layer-0 calibration tensor.
+
+Prints one JSON line:
+  value       uncompressed GB/s of the round trip = 2 N bytes / (encode + decode time)
+  encode_GBps / decode_GBps    the two directions, timed separately
+  ratio, escape_rate           compression ratio (input bytes / stream bytes) and E / N
+  roofline    the dominant kernel's algorithmic bytes / average duration
+              (HIP events recorded on the launch stream by the library's
+              instrumentation) against the 8 TB/s HBM peak
+  cpu_baseline the CPU oracle (single thread) on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = "llama3_8b_kv"
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=WORKLOAD)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-log2", type=int, default=28,
+                   help="elements of the workload the CPU oracle encodes and decodes (log2)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "fp8_kv_cache_sz_amd", "csrc", "splitzip.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
+    on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    entry = rec.get(workload, {}).get(kernel)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(x_dev, cb, dtype, log2_sample):
+    import oracle
+    import synth
+    n = min(x_dev.numel(), 1 << log2_sample)
+    bits = synth.as_bits_numpy(x_dev[:n])
+    cbn = list(cb.exps)
+    t0 = time.perf_counter()
+    stream = oracle.encode(bits, dtype, cbn)
+    t1 = time.perf_counter()
+    back = oracle.decode(stream, dtype, n)
+    t2 = time.perf_counter()
+    assert (back == bits).all()
+    elem = 2 if dtype == 0 else 1
+    gbps = 2 * n * elem / (t2 - t0) / 1e9
+    return {
+        "value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": "first %d elements (%d MiB) of the workload; one encode (%.2f s) and one "
+                  "decode (%.2f s), single-threaded C, host %s, %d logical CPUs"
+                  % (n, n * elem >> 20, t1 - t0, t2 - t1, platform.processor() or platform.machine(),
+                     os.cpu_count()),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the SplitZip codec has no cross-GPU step on this path "
+              "(each GPU encodes/decodes its own shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_kv_cache_sz_amd as sz
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x, dtype = synth.workload(args.workload, device=dev)
+    cal = synth.calibration_tensor(args.workload, device="cpu")
+    cb = sz.calibrate(cal)
+    n = x.numel()
+    elem = 2 if dtype == 0 else 1
+    cap = sz.encoded_size(dtype, n, n)
+    buf = torch.empty(cap, dtype=torch.uint8, device=dev)
+    ws = sz.workspace(dtype, n, dev)
+    ws_dec = sz.workspace(dtype, n, dev)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+
+    def encode():
+        sz.encode(x, cb, out=buf, ws=ws, sync=False)
+
+    def decode(in_bytes):
+        sz.decode(buf, dtype, n, out=y, ws=ws_dec, check=False, in_bytes=in_bytes)
+
+    # first pass: learn the stream size, check the round trip
+    encode()
+    torch.cuda.synchronize()
+    escapes = sz.read_escape_count(buf)
+    size = sz.encoded_size(dtype, n, escapes)
+    decode(size)
+    torch.cuda.synchronize()
+    if int(ws_dec[:4].cpu().view(torch.int32)[0]) != 0 or not torch.equal(
+            y.view(torch.uint8), x.view(torch.uint8)):
+        print("round trip mismatch", file=sys.stderr)
+        sys.exit(1)
+
+    for _ in range(args.warmup):
+        encode()
+        decode(size)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        encode()
+        decode(size)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = 2 * n * elem / (ms_per_step * 1e-3) / 1e9
+
+    # per-direction timing (events on the launch stream)
+    def time_loop(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / reps
+
+    reps = max(5, args.steps)
+    enc_ms = time_loop(encode, reps)
+    dec_ms = time_loop(lambda: decode(size), reps)
+
+    # per-kernel durations through the library's event instrumentation
+    sz.profile_enable(True)
+    for _ in range(reps):
+        encode()
+        decode(size)
+    stats = sz.profile_collect()
+    sz.profile_enable(False)
+    per_kernel = {k: {"launches": c, "avg_ms": round(ms / c, 5)} for k, (c, ms) in stats.items()}
+    dense = {k: v for k, v in per_kernel.items() if k.startswith(("sz_enc_dense", "sz_dec_bf16", "sz_dec_e5m2"))}
+    dominant = max(dense, key=lambda k: dense[k]["avg_ms"])
+    alg_bytes = int(3.5 * n) + 3 * escapes if dtype == 0 else int(1.875 * n) + 3 * escapes
+    avg_s = dense[dominant]["avg_ms"] * 1e-3
+    achieved = alg_bytes / avg_s / 1e9
+    traffic = load_traffic(dominant, args.workload)
+
+    # a plain device copy of the same bytes, as a practical streaming ceiling
+    alg_per_direction = alg_bytes // 2          # read half, write half
+    src = torch.empty(alg_per_direction, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = time_loop(lambda: dst.copy_(src), reps)
+    copy_gbps = 2 * src.numel() / (copy_ms * 1e-3) / 1e9
+    del src, dst
+
+    result = {
+        "metric": "encode/decode GB/s (uncompressed) + % of 8 TB/s HBM peak; compression ratio",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16" if dtype == 0 else "u8",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "description": synth.DESCRIPTION[args.workload],
+                   "elements": n, "bytes": n * elem, "codebook": list(cb.exps),
+                   "step": "encode + decode of the whole tensor"},
+        "encode_GBps": round(n * elem / (enc_ms * 1e-3) / 1e9, 2),
+        "decode_GBps": round(n * elem / (dec_ms * 1e-3) / 1e9, 2),
+        "encode_ms": round(enc_ms, 4),
+        "decode_ms": round(dec_ms, 4),
+        "ratio": round(n * elem / size, 6),
+        "escape_rate": round(escapes / n, 6),
+        "escapes": escapes,
+        "stream_bytes": size,
+        "kernels": per_kernel,
+        "copy_GBps": round(copy_gbps, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dominant,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x, cb, dtype, args.cpu_sample_log2)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

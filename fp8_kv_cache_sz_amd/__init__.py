@@ -1,0 +1,140 @@
+"""SplitZip lossless KV-cache codec for MI355X (gfx950).
+
+Thin Python layer over the C ABI of ``libsplitzip.so`` (include/splitzip.h):
+it only moves pointers, sizes and streams; calibration, encode and decode all
+run in the library.  Tensors:
+
+* BF16 data: ``torch.bfloat16`` (or ``int16``) tensors.
+* FP8 E5M2 data: ``torch.float8_e5m2`` or ``uint8`` tensors of raw bytes.
+* Streams: ``uint8`` device tensors.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _native
+from ._native import SZ_BF16, SZ_FP8_E5M2, SplitZipError
+
+BF16 = SZ_BF16
+E5M2 = SZ_FP8_E5M2
+
+__all__ = ["BF16", "E5M2", "Codebook", "SplitZipError", "calibrate", "encoded_size",
+           "workspace_size", "workspace", "encode", "decode", "read_escape_count",
+           "profile_enable", "profile_collect"]
+
+
+@dataclass(frozen=True)
+class Codebook:
+    """Top-16 exponent codebook: ``exps[c]`` is the exponent coded as ``c``."""
+    dtype: int
+    exps: tuple
+
+    def to_c(self) -> _native.sz_codebook:
+        cb = _native.sz_codebook()
+        cb.dtype = self.dtype
+        for c, e in enumerate(self.exps):
+            cb.exp[c] = int(e)
+        return cb
+
+
+def dtype_of(t: torch.Tensor) -> int:
+    if t.dtype in (torch.bfloat16, torch.int16):
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e5m2):
+        return E5M2
+    raise TypeError("SplitZip codes BF16 (bfloat16/int16) or FP8 E5M2 (float8_e5m2/uint8) tensors, "
+                    "got %s" % t.dtype)
+
+
+def _elem_size(dtype: int) -> int:
+    return 2 if dtype == BF16 else 1
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def calibrate(t: torch.Tensor) -> Codebook:
+    """Offline Top-16 calibration on the host (sz_calibrate)."""
+    dtype = dtype_of(t)
+    h = t.detach().reshape(-1).contiguous().cpu()
+    cb = _native.sz_calibrate(dtype, h.data_ptr() if h.numel() else None, h.numel())
+    return Codebook(dtype, tuple(int(x) for x in cb.exp))
+
+
+def encoded_size(dtype: int, n: int, n_escapes: int) -> int:
+    return _native.sz_encoded_size(dtype, n, n_escapes)
+
+
+def workspace_size(dtype: int, n: int) -> int:
+    return _native.sz_workspace_size(dtype, n)
+
+
+def workspace(dtype: int, n: int, device="cuda") -> torch.Tensor:
+    return torch.empty(workspace_size(dtype, n), dtype=torch.uint8, device=device)
+
+
+def read_escape_count(buf: torch.Tensor) -> int:
+    """E from a finished stream's header (u64 at byte 16); synchronises on the copy."""
+    return int(buf[16:24].cpu().view(torch.int64)[0])
+
+
+def encode(x: torch.Tensor, cb: Codebook, out: torch.Tensor | None = None,
+           ws: torch.Tensor | None = None, stream=None, sync: bool = True):
+    """Encode a device tensor.  Returns ``(buf, size, escapes)``; with
+    ``sync=False`` the call only enqueues the kernels and returns
+    ``(buf, None, None)`` (the size is known once the stream has run)."""
+    dtype = dtype_of(x)
+    if cb.dtype != dtype:
+        raise SplitZipError("sz_encode", -2)
+    x = x.reshape(-1)
+    if not x.is_contiguous():
+        raise ValueError("encode needs a contiguous tensor")
+    n = x.numel()
+    cap = encoded_size(dtype, n, n)
+    if out is None:
+        out = torch.empty(cap, dtype=torch.uint8, device=x.device)
+    if ws is None:
+        ws = workspace(dtype, n, x.device)
+    rc = _native.sz_encode(dtype, x.data_ptr() if n else None, n, cb.to_c(), out.data_ptr(),
+                           out.numel(), ws.data_ptr(), ws.numel(), _stream_handle(stream, x.device))
+    _native.check("sz_encode", rc)
+    if not sync:
+        return out, None, None
+    escapes = read_escape_count(out)
+    return out, encoded_size(dtype, n, escapes), escapes
+
+
+def decode(buf: torch.Tensor, dtype: int, n: int, out: torch.Tensor | None = None,
+           ws: torch.Tensor | None = None, stream=None, check: bool = True,
+           in_bytes: int | None = None) -> torch.Tensor:
+    """Decode a device stream into ``n`` values.  With ``check`` the call
+    synchronises and raises if the device-side validation failed."""
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16 if dtype == BF16 else torch.uint8, device=buf.device)
+    if out.numel() * out.element_size() < n * _elem_size(dtype):
+        raise ValueError("output tensor too small")
+    if ws is None:
+        ws = workspace(dtype, n, buf.device)
+    nbytes = buf.numel() if in_bytes is None else in_bytes
+    rc = _native.sz_decode(buf.data_ptr(), nbytes, dtype, out.data_ptr() if n else None, n,
+                           ws.data_ptr(), ws.numel(), _stream_handle(stream, buf.device))
+    _native.check("sz_decode", rc)
+    if check:
+        status = int(ws[:4].cpu().view(torch.int32)[0])
+        if status != 0:
+            raise SplitZipError("sz_decode (device check)", status)
+    return out
+
+
+def profile_enable(on: bool = True) -> None:
+    _native.check("sz_profile_enable", _native.sz_profile_enable(on))
+
+
+def profile_collect() -> dict:
+    """{kernel name: (launches, total ms)} since the last collect/enable."""
+    return _native.sz_profile_collect()

@@ -1,0 +1,869 @@
+// SplitZip codec for MI355X (gfx950, CDNA4): HIP kernels and the C ABI.
+//
+// Method: "SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
+// Serving" (gist.science summary page), Method section.  Encode splits every
+// value into a raw sign+mantissa symbol and an exponent mapped through a
+// Top-16 codebook to a 4-bit code; exponents outside the codebook become
+// (16-bit position, 8-bit exponent) escape records.  Decode is a dense
+// lookup-table pass followed by an overwrite of the escaped exponents.
+//
+// The work is integer bit manipulation streamed through HBM: there is no
+// contraction, so no MFMA.  Design points for CDNA4:
+//   * every global access of the dense passes is a full-wave coalesced
+//     dword / dwordx2 / dwordx4 access (lane l of a wave touches the l-th
+//     8-element chunk of a 512-element row);
+//   * code tables live in LDS (256-entry exponent->code bytes for encode,
+//     256-entry code-pair->shifted-exponent words for decode);
+//   * byte shuffles use v_perm_b32 / v_alignbyte_b32;
+//   * escape ranks come from a packed 64-lane prefix sum of per-chunk counts;
+//   * encode is dense+stage, a one-workgroup scan of tile counts, then a
+//     compaction of the staged escape records into their final order; decode
+//     is a one-workgroup scan of the block counts, then one workgroup per
+//     64K block: dense decode in registers, patched from an LDS map of the
+//     block's escapes before a single store.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "splitzip.h"
+
+namespace {
+
+constexpr uint64_t kBlock = 65536;          // elements per escape-position block
+constexpr uint32_t kMagic = 0x50495A53u;    // "SZIP"
+constexpr uint32_t kVersion = 1;
+constexpr uint32_t kLog2Block = 16;
+
+// Encode tiling: one wave per workgroup, 16K elements per tile, processed
+// as 4 rows of 4096 (64 lanes x 8 chunks x 8 elements for BF16).
+constexpr uint32_t kEncTile = 16384;
+constexpr uint32_t kTilesPerBlock = kBlock / kEncTile;   // 4
+constexpr uint32_t kScanThreads = 1024;
+constexpr uint32_t kDecThreads = 256;                    // 4 waves per 64K block
+constexpr uint32_t kCompactThreads = 256;
+
+constexpr uint64_t up256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
+
+struct Geometry {
+    uint64_t n, nb, nt;
+    uint64_t off_nib, nib_bytes, off_sm, sm_bytes, off_esc;
+};
+
+Geometry geometry(int dtype, uint64_t n)
+{
+    Geometry g;
+    g.n = n;
+    g.nb = (n + kBlock - 1) / kBlock;
+    g.nt = (n + kEncTile - 1) / kEncTile;
+    g.off_nib = up256(64 + 4 * g.nb);
+    g.nib_bytes = (n + 1) / 2;
+    g.off_sm = g.off_nib + up256(g.nib_bytes);
+    g.sm_bytes = dtype == SZ_BF16 ? n : 3 * ((n + 7) / 8);
+    g.off_esc = g.off_sm + up256(g.sm_bytes);
+    return g;
+}
+
+// Workspace layout (byte offsets): status word, tile counts, tile offsets
+// (encode) / block offsets (decode), escape staging (encode).
+struct WsLayout {
+    uint64_t counts, offsets, stage, total;
+};
+
+WsLayout ws_layout(int dtype, uint64_t n)
+{
+    Geometry g = geometry(dtype, n);
+    WsLayout w;
+    w.counts = 256;
+    w.offsets = w.counts + up256(4 * g.nt + 16);
+    uint64_t offsets_bytes = std::max<uint64_t>(8 * g.nt, 8 * g.nb);
+    w.stage = w.offsets + up256(offsets_bytes + 16);
+    w.total = w.stage + up256(3 * g.nt * kEncTile + 16);
+    return w;
+}
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    // v_perm_b32: byte i of the result = byte sel[i] of {hi, lo} (lo = bytes 0..3)
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x)
+{
+    const uint32_t lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint32_t y = __shfl_up(x, d, 64);
+        if (lane >= (uint32_t)d) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ uint32_t read_lane63(uint32_t x)
+{
+    return __builtin_amdgcn_readlane(x, 63);
+}
+
+__device__ __forceinline__ uint32_t popc64(uint64_t x) { return __popcll(x); }
+
+// Codebook packed as 4 little-endian words: byte c = exponent of code c.
+struct Codebook4 {
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ uint32_t cb_entry(const Codebook4 &cb, uint32_t c)
+{
+    return (cb.w[c >> 2] >> (8 * (c & 3))) & 0xFFu;
+}
+
+// Exponent -> code table for encode.  Byte v = code of exponent v, or 0x80
+// (code 0 with the escape flag) when v is not in the codebook.  64 lanes
+// fill 4 entries each.
+__device__ __forceinline__ void build_encode_table(uint32_t *table32, const Codebook4 &cb,
+                                                   uint32_t symbols)
+{
+    const uint32_t lane = threadIdx.x;
+    if (lane * 4 < symbols) {
+        uint32_t word = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < 4; ++k) {
+            uint32_t v = lane * 4 + k;
+            uint32_t code = 0x80u;
+#pragma unroll
+            for (uint32_t c = 0; c < 16; ++c)
+                if (cb_entry(cb, c) == v) code = c;
+            word |= code << (8 * k);
+        }
+        table32[lane] = word;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// BF16 encode, one 8-element chunk (16 bytes in).
+//   nib: 4 bytes of codes (element 2k low nibble)
+//   sm : 8 sign/mantissa bytes (sign << 7 | mantissa7)
+//   esc: escape flag of element k at bit 8k+7
+//   ex : exponent of element k in byte k
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void encode_chunk_bf16(const uint4 q, const uint8_t *table, uint32_t &nib,
+                                                  uint2 &sm, uint64_t &esc, uint64_t &ex)
+{
+    const uint32_t lo_a = perm(q.y, q.x, 0x06040200u);   // low bytes of elements 0..3
+    const uint32_t hi_a = perm(q.y, q.x, 0x07050301u);   // high bytes of elements 0..3
+    const uint32_t lo_b = perm(q.w, q.z, 0x06040200u);
+    const uint32_t hi_b = perm(q.w, q.z, 0x07050301u);
+    sm.x = (hi_a & 0x80808080u) | (lo_a & 0x7F7F7F7Fu);
+    sm.y = (hi_b & 0x80808080u) | (lo_b & 0x7F7F7F7Fu);
+    const uint32_t e_a = ((hi_a << 1) & 0xFEFEFEFEu) | ((lo_a >> 7) & 0x01010101u);
+    const uint32_t e_b = ((hi_b << 1) & 0xFEFEFEFEu) | ((lo_b >> 7) & 0x01010101u);
+    const uint32_t c_a = (uint32_t)table[e_a & 0xFFu] | ((uint32_t)table[(e_a >> 8) & 0xFFu] << 8) |
+                         ((uint32_t)table[(e_a >> 16) & 0xFFu] << 16) |
+                         ((uint32_t)table[e_a >> 24] << 24);
+    const uint32_t c_b = (uint32_t)table[e_b & 0xFFu] | ((uint32_t)table[(e_b >> 8) & 0xFFu] << 8) |
+                         ((uint32_t)table[(e_b >> 16) & 0xFFu] << 16) |
+                         ((uint32_t)table[e_b >> 24] << 24);
+    const uint32_t k_a = c_a & 0x0F0F0F0Fu;
+    const uint32_t k_b = c_b & 0x0F0F0F0Fu;
+    // byte 0 of (k | k >> 4) = code0 | code1 << 4, byte 2 = code2 | code3 << 4
+    nib = perm(k_b | (k_b >> 4), k_a | (k_a >> 4), 0x06040200u);
+    esc = (uint64_t)(c_a & 0x80808080u) | ((uint64_t)(c_b & 0x80808080u) << 32);
+    ex = (uint64_t)e_a | ((uint64_t)e_b << 32);
+}
+
+// Write the escape records of one chunk into the tile's staging area, in
+// ascending element order starting at rank `rank`.
+__device__ __forceinline__ void stage_records(uint8_t *tstage, uint32_t rank, uint64_t esc,
+                                              uint64_t ex, uint32_t pos0, uint32_t shift_per_elem)
+{
+    while (esc) {
+        const uint32_t bit = (uint32_t)__builtin_ctzll(esc);
+        esc &= esc - 1;
+        const uint32_t k = bit / shift_per_elem;
+        const uint32_t pos = (pos0 + k) & 0xFFFFu;
+        const uint32_t e = (uint32_t)(ex >> (8 * k)) & 0xFFu;
+        uint8_t *r = tstage + 3ull * rank;
+        r[0] = (uint8_t)pos;
+        r[1] = (uint8_t)(pos >> 8);
+        r[2] = (uint8_t)e;
+        ++rank;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: BF16 dense encode + escape staging.  One wave per 16K-element tile.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kBf16Chunks = 8;                        // chunks per lane per row
+constexpr uint32_t kBf16Row = 64 * 8 * kBf16Chunks;        // 4096 elements
+
+__global__ __launch_bounds__(64) void sz_enc_dense_bf16(const uint16_t *__restrict__ in, uint64_t n,
+                                                        uint8_t *__restrict__ out, uint64_t off_nib,
+                                                        uint64_t off_sm, Codebook4 cb,
+                                                        uint32_t *__restrict__ tile_counts,
+                                                        uint8_t *__restrict__ stage)
+{
+    __shared__ uint32_t table32[64];
+    build_encode_table(table32, cb, 256);
+    __syncthreads();
+    const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
+
+    const uint32_t lane = lane_id();
+    const uint64_t tile = blockIdx.x;
+    const uint64_t t0 = tile * kEncTile;
+    const bool full_tile = t0 + kEncTile <= n;
+    uint8_t *tstage = stage + tile * (3ull * kEncTile);
+    uint32_t tile_escapes = 0;
+
+    for (uint32_t row = 0; row < kEncTile / kBf16Row; ++row) {
+        const uint64_t base = t0 + (uint64_t)row * kBf16Row;
+        if (base >= n) break;
+        uint4 q[kBf16Chunks];
+#pragma unroll
+        for (uint32_t j = 0; j < kBf16Chunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+            if (full_tile || c0 + 8 <= n) {
+                q[j] = *reinterpret_cast<const uint4 *>(in + c0);
+            } else {
+                uint16_t v[8];
+#pragma unroll
+                for (uint32_t k = 0; k < 8; ++k) v[k] = (c0 + k < n) ? in[c0 + k] : 0;
+                q[j] = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                                  v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
+            }
+        }
+        uint64_t esc[kBf16Chunks], ex[kBf16Chunks];
+        uint32_t cnt[kBf16Chunks];
+#pragma unroll
+        for (uint32_t j = 0; j < kBf16Chunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+            uint32_t nib;
+            uint2 sm;
+            encode_chunk_bf16(q[j], table, nib, sm, esc[j], ex[j]);
+            if (full_tile || c0 + 8 <= n) {
+                *reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2) = nib;
+                *reinterpret_cast<uint2 *>(out + off_sm + c0) = sm;
+            } else if (c0 < n) {
+                // last, partial chunk: missing elements get code 0, sign/mantissa 0
+                // and no escape; the bytes past the data are section padding
+                const uint32_t valid = (uint32_t)(n - c0);
+                const uint64_t keep = (valid >= 8) ? ~0ull : ((1ull << (8 * valid)) - 1);
+                esc[j] &= keep;
+                nib &= (uint32_t)((1ull << (4 * valid)) - 1);
+                uint64_t smv = ((uint64_t)sm.y << 32 | sm.x) & keep;
+                *reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2) = nib;
+                *reinterpret_cast<uint2 *>(out + off_sm + c0) =
+                    make_uint2((uint32_t)smv, (uint32_t)(smv >> 32));
+            } else {
+                esc[j] = 0;
+            }
+            cnt[j] = popc64(esc[j]);
+        }
+        // escape ranks: packed 16-bit per-chunk counts, prefix-summed over lanes
+        uint32_t any = 0;
+#pragma unroll
+        for (uint32_t j = 0; j < kBf16Chunks; ++j) any |= cnt[j];
+        if (__ballot(any != 0) == 0) continue;
+        uint32_t packed[kBf16Chunks / 2], incl[kBf16Chunks / 2];
+#pragma unroll
+        for (uint32_t p = 0; p < kBf16Chunks / 2; ++p) {
+            packed[p] = cnt[2 * p] | (cnt[2 * p + 1] << 16);
+            incl[p] = wave_inclusive_sum(packed[p]);
+        }
+        uint32_t running = tile_escapes;
+#pragma unroll
+        for (uint32_t j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t sh = 16 * (j & 1);
+            const uint32_t total = (read_lane63(incl[j / 2]) >> sh) & 0xFFFFu;
+            const uint32_t before = ((incl[j / 2] - packed[j / 2]) >> sh) & 0xFFFFu;
+            if (esc[j]) {
+                const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+                stage_records(tstage, running + before, esc[j], ex[j], (uint32_t)(c0 & 0xFFFFu), 8);
+            }
+            running += total;
+        }
+        tile_escapes = running;
+    }
+    if (lane == 0) tile_counts[tile] = tile_escapes;
+}
+
+// ---------------------------------------------------------------------------
+// Block-level exclusive scan helper for the one-workgroup scan kernels.
+// Returns the exclusive prefix of x inside the workgroup and the total.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t workgroup_exclusive_sum(uint32_t x, uint32_t *wave_sums,
+                                                            uint32_t &total)
+{
+    const uint32_t lane = lane_id();
+    const uint32_t wave = threadIdx.x / 64;
+    const uint32_t nwaves = blockDim.x / 64;
+    const uint32_t incl = wave_inclusive_sum(x);
+    if (lane == 63) wave_sums[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t v = lane < nwaves ? wave_sums[lane] : 0;
+        uint32_t vi = wave_inclusive_sum(v);
+        if (lane < nwaves) wave_sums[lane] = vi - v;     // exclusive wave prefix
+        if (lane == 63) wave_sums[32] = vi;              // workgroup total
+    }
+    __syncthreads();
+    const uint32_t result = wave_sums[wave] + incl - x;
+    total = wave_sums[32];
+    __syncthreads();
+    return result;
+}
+
+struct HeaderArgs {
+    uint64_t n, nb;
+    uint32_t dtype;
+    Codebook4 cb;
+    uint64_t pad_start[3], pad_end[3];
+};
+
+// ---------------------------------------------------------------------------
+// Kernel: encode scan.  One workgroup: per-block escape counts from the tile
+// counts, exclusive tile offsets, header and padding.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__restrict__ tile_counts,
+                                                            uint64_t nt,
+                                                            uint64_t *__restrict__ tile_offsets,
+                                                            uint8_t *__restrict__ out, HeaderArgs h)
+{
+    __shared__ uint32_t wave_sums[33];
+    const uint32_t tid = threadIdx.x;
+    uint32_t *block_counts = reinterpret_cast<uint32_t *>(out + 64);
+    uint64_t carry = 0;
+    for (uint64_t b0 = 0; b0 < h.nb; b0 += kScanThreads) {
+        const uint64_t b = b0 + tid;
+        uint32_t c[kTilesPerBlock] = {0, 0, 0, 0};
+        if (b < h.nb) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b);
+            const uint64_t t = kTilesPerBlock * b;
+            c[0] = v.x;
+            c[1] = (t + 1 < nt) ? v.y : 0;
+            c[2] = (t + 2 < nt) ? v.z : 0;
+            c[3] = (t + 3 < nt) ? v.w : 0;
+        }
+        const uint32_t blk = c[0] + c[1] + c[2] + c[3];
+        uint32_t total;
+        const uint32_t excl = workgroup_exclusive_sum(blk, wave_sums, total);
+        if (b < h.nb) {
+            block_counts[b] = blk;
+            uint64_t off = carry + excl;
+            const uint64_t t = kTilesPerBlock * b;
+#pragma unroll
+            for (uint32_t k = 0; k < kTilesPerBlock; ++k) {
+                if (t + k < nt) tile_offsets[t + k] = off;
+                off += c[k];
+            }
+        }
+        carry += total;
+    }
+    // header: 16 little-endian words
+    if (tid < 16) {
+        uint32_t w = 0;
+        switch (tid) {
+        case 0: w = kMagic; break;
+        case 1: w = kVersion | (h.dtype << 16) | (kLog2Block << 24); break;
+        case 2: w = (uint32_t)h.n; break;
+        case 3: w = (uint32_t)(h.n >> 32); break;
+        case 4: w = (uint32_t)carry; break;
+        case 5: w = (uint32_t)(carry >> 32); break;
+        case 6: w = (uint32_t)h.nb; break;
+        case 8: w = h.cb.w[0]; break;
+        case 9: w = h.cb.w[1]; break;
+        case 10: w = h.cb.w[2]; break;
+        case 11: w = h.cb.w[3]; break;
+        default: w = 0; break;
+        }
+        reinterpret_cast<uint32_t *>(out)[tid] = w;
+    }
+    // zero padding between sections (each range is shorter than 256 bytes)
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        const uint64_t a = h.pad_start[r] + tid;
+        if (a < h.pad_end[r]) out[a] = 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: escape compaction.  Copies each tile's staged records (3 bytes
+// each) to out[off_esc + 3 * tile_offset ...).  The destination is written
+// with aligned dword stores built by v_alignbyte_b32 from the staged words;
+// the partial dwords at both ends (shared with the neighbouring tiles) are
+// written byte by byte.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCompactThreads) void sz_enc_compact(
+    const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
+    const uint64_t *__restrict__ tile_offsets, uint8_t *__restrict__ out, uint64_t off_esc)
+{
+    const uint64_t tile = blockIdx.x;
+    const uint32_t k = tile_counts[tile];
+    if (k == 0) return;
+    const uint8_t *src = stage + tile * (3ull * kEncTile);
+    const uint32_t *src32 = reinterpret_cast<const uint32_t *>(src);
+    const uint64_t dst0 = off_esc + 3 * tile_offsets[tile];
+    const uint64_t end = dst0 + 3ull * k;
+    const uint64_t head_end = std::min<uint64_t>((dst0 + 3) & ~uint64_t(3), end);
+    const uint64_t body_end = std::max<uint64_t>(end & ~uint64_t(3), head_end);
+    const uint32_t tid = threadIdx.x;
+    if (dst0 + tid < head_end) out[dst0 + tid] = src[tid];
+    const uint64_t body_words = (body_end - head_end) / 4;
+    const uint32_t s_first = (uint32_t)(head_end - dst0);
+    for (uint64_t w = tid; w < body_words; w += kCompactThreads) {
+        const uint32_t s = s_first + 4 * (uint32_t)w;
+        const uint32_t lo = src32[s >> 2];
+        const uint32_t hi = src32[(s >> 2) + 1];
+        *reinterpret_cast<uint32_t *>(out + head_end + 4 * w) =
+            __builtin_amdgcn_alignbyte(hi, lo, s & 3);
+    }
+    if (body_end + tid < end) out[body_end + tid] = src[body_end - dst0 + tid];
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: decode scan.  One workgroup validates the header and the block
+// counts and writes the exclusive escape offset of every block.  The status
+// word ends as 0 or a negative error code.
+// ---------------------------------------------------------------------------
+struct DecodeArgs {
+    uint64_t n, nb, in_bytes, off_nib, off_sm, off_esc;
+    uint32_t dtype, symbols;
+};
+
+__global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                            uint64_t *__restrict__ block_offsets,
+                                                            int32_t *__restrict__ status)
+{
+    __shared__ uint32_t wave_sums[33];
+    __shared__ int32_t bad;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t *h32 = reinterpret_cast<const uint32_t *>(in);
+    int32_t err = 0;
+    const uint32_t w1 = h32[1];
+    const uint64_t n_hdr = (uint64_t)h32[2] | ((uint64_t)h32[3] << 32);
+    const uint64_t e_hdr = (uint64_t)h32[4] | ((uint64_t)h32[5] << 32);
+    if (h32[0] != kMagic || (w1 & 0xFFFFu) != kVersion || (w1 >> 24) != kLog2Block) err = SZ_E_FORMAT;
+    else if (((w1 >> 16) & 0xFFu) != a.dtype) err = SZ_E_DTYPE;
+    else if (n_hdr != a.n || h32[6] != (uint32_t)a.nb || h32[7] != 0) err = SZ_E_FORMAT;
+    else if (e_hdr > a.n || a.off_esc + 3 * e_hdr > a.in_bytes) err = SZ_E_FORMAT;
+    else {
+        for (uint32_t c = 0; c < 16; ++c)
+            if (in[32 + c] >= a.symbols) err = SZ_E_FORMAT;
+    }
+    if (err) {
+        if (tid == 0) *status = err;
+        return;
+    }
+    if (tid == 0) bad = 0;
+    __syncthreads();
+    const uint32_t *counts = reinterpret_cast<const uint32_t *>(in + 64);
+    uint64_t carry = 0;
+    for (uint64_t b0 = 0; b0 < a.nb; b0 += kScanThreads) {
+        const uint64_t b = b0 + tid;
+        uint32_t c = 0;
+        if (b < a.nb) {
+            c = counts[b];
+            const uint64_t len = std::min<uint64_t>(kBlock, a.n - b * kBlock);
+            if (c > len) bad = 1;
+        }
+        uint32_t total;
+        const uint32_t excl = workgroup_exclusive_sum(c, wave_sums, total);
+        if (b < a.nb) block_offsets[b] = carry + excl;
+        carry += total;
+    }
+    __syncthreads();
+    if (tid == 0) *status = (bad || carry != e_hdr) ? SZ_E_FORMAT : 0;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: BF16 decode, one workgroup (4 waves) per 64K block.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kNoEscape = 0xFFFFu;
+
+// Escape record r of the stream: position and exponent.
+__device__ __forceinline__ void read_record(const uint8_t *esc, uint64_t r, uint32_t &pos, uint32_t &e)
+{
+    const uint8_t *p = esc + 3 * r;
+    pos = (uint32_t)p[0] | ((uint32_t)p[1] << 8);
+    e = p[2];
+}
+
+__device__ __forceinline__ uint4 decode_chunk_bf16(uint32_t nib, uint2 sm, const uint32_t *table)
+{
+    // table[b] = cb[b & 15] << 7 | cb[b >> 4] << 23: both exponents of a
+    // code byte, already in place for two packed BF16 values
+    uint4 o;
+    o.x = (perm(sm.x, sm.x, 0x01010000u) & 0x807F807Fu) | table[nib & 0xFFu];
+    o.y = (perm(sm.x, sm.x, 0x03030202u) & 0x807F807Fu) | table[(nib >> 8) & 0xFFu];
+    o.z = (perm(sm.y, sm.y, 0x01010000u) & 0x807F807Fu) | table[(nib >> 16) & 0xFFu];
+    o.w = (perm(sm.y, sm.y, 0x03030202u) & 0x807F807Fu) | table[nib >> 24];
+    return o;
+}
+
+__device__ __forceinline__ void patch_bf16(uint4 &o, uint32_t k, uint32_t e)
+{
+    const uint32_t sh = 7 + 16 * (k & 1);
+    const uint32_t clear = ~(0xFFu << sh);
+    const uint32_t set = e << sh;
+    switch (k >> 1) {
+    case 0: o.x = (o.x & clear) | set; break;
+    case 1: o.y = (o.y & clear) | set; break;
+    case 2: o.z = (o.z & clear) | set; break;
+    default: o.w = (o.w & clear) | set; break;
+    }
+}
+
+__global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                           const uint64_t *__restrict__ block_offsets,
+                                                           int32_t *__restrict__ status,
+                                                           uint16_t *__restrict__ out)
+{
+    __shared__ uint32_t table[256];
+    __shared__ uint16_t first[kBlock / 8];     // first escape record of each 8-element chunk
+    if (*status != 0) return;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t b = blockIdx.x;
+    const uint64_t e0 = b * kBlock;
+    const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
+    const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
+    const uint64_t r0 = block_offsets[b];
+    const uint8_t *esc = in + a.off_esc;
+    {
+        const uint32_t lo = in[32 + (tid & 15)];
+        const uint32_t hi = in[32 + (tid >> 4)];
+        table[tid] = (lo << 7) | (hi << 23);
+    }
+    if (k) {
+        uint4 *f4 = reinterpret_cast<uint4 *>(first);
+        const uint4 none = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+        for (uint32_t i = tid; i < kBlock / 8 / 8; i += kDecThreads) f4[i] = none;
+    }
+    __syncthreads();
+    if (k) {
+        bool bad = false;
+        for (uint32_t r = tid; r < k; r += kDecThreads) {
+            uint32_t pos, e;
+            read_record(esc, r0 + r, pos, e);
+            int32_t prev = -1;
+            if (r > 0) {
+                uint32_t pp, pe;
+                read_record(esc, r0 + r - 1, pp, pe);
+                prev = (int32_t)pp;
+            }
+            if (pos >= blen || (int32_t)pos <= prev) {
+                bad = true;
+                continue;
+            }
+            if (r == 0 || (uint32_t)(prev >> 3) != (pos >> 3)) first[pos >> 3] = (uint16_t)r;
+        }
+        if (bad) atomicExch(status, SZ_E_FORMAT);
+    }
+    __syncthreads();
+
+    const uint32_t lane = lane_id();
+    const uint32_t wave = tid / 64;
+    const bool full_block = blen == kBlock;
+    const uint8_t *nib_base = in + a.off_nib;
+    const uint8_t *sm_base = in + a.off_sm;
+    for (uint32_t row = 0; row < 4; ++row) {
+        const uint32_t rbase = wave * 16384 + row * kBf16Row;    // block-local element
+        if (rbase >= blen) break;
+        uint32_t nib[kBf16Chunks];
+        uint2 sm[kBf16Chunks];
+#pragma unroll
+        for (uint32_t j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            if (full_block || c < blen) {
+                const uint64_t g = e0 + c;
+                nib[j] = *reinterpret_cast<const uint32_t *>(nib_base + g / 2);
+                sm[j] = *reinterpret_cast<const uint2 *>(sm_base + g);
+            } else {
+                nib[j] = 0;
+                sm[j] = make_uint2(0, 0);
+            }
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            uint4 o = decode_chunk_bf16(nib[j], sm[j], table);
+            if (k) {
+                uint32_t r = first[c >> 3];
+                if (r != kNoEscape) {
+                    for (; r < k; ++r) {
+                        uint32_t pos, e;
+                        read_record(esc, r0 + r, pos, e);
+                        if ((pos >> 3) != (c >> 3)) break;
+                        patch_bf16(o, pos & 7, e);
+                    }
+                }
+            }
+            const uint64_t g = e0 + c;
+            if (full_block || c + 8 <= blen) {
+                *reinterpret_cast<uint4 *>(out + g) = o;
+            } else if (c < blen) {
+                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: launch bookkeeping and instrumentation
+// ---------------------------------------------------------------------------
+struct ProfRecord {
+    const char *name;
+    hipEvent_t start, stop;
+};
+
+std::mutex g_prof_mutex;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_records;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event()
+{
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+void release_records()
+{
+    for (auto &r : g_prof_records) {
+        g_event_pool.push_back(r.start);
+        g_event_pool.push_back(r.stop);
+    }
+    g_prof_records.clear();
+}
+
+struct LaunchScope {
+    const char *name;
+    hipStream_t stream;
+    hipEvent_t start = nullptr, stop = nullptr;
+    LaunchScope(const char *n, hipStream_t s) : name(n), stream(s)
+    {
+        std::lock_guard<std::mutex> lock(g_prof_mutex);
+        if (!g_prof_on) return;
+        start = take_event();
+        stop = take_event();
+        if (start && stop) (void)hipEventRecord(start, stream);
+    }
+    ~LaunchScope()
+    {
+        if (!start || !stop) return;
+        (void)hipEventRecord(stop, stream);
+        std::lock_guard<std::mutex> lock(g_prof_mutex);
+        g_prof_records.push_back({name, start, stop});
+    }
+};
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+Codebook4 pack_codebook(const uint8_t *e)
+{
+    Codebook4 cb;
+    for (int w = 0; w < 4; ++w)
+        cb.w[w] = (uint32_t)e[4 * w] | ((uint32_t)e[4 * w + 1] << 8) | ((uint32_t)e[4 * w + 2] << 16) |
+                  ((uint32_t)e[4 * w + 3] << 24);
+    return cb;
+}
+
+uint32_t symbols_of(int dtype) { return dtype == SZ_BF16 ? 256u : 32u; }
+
+constexpr uint64_t kMaxElems = 1ull << 40;
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" int sz_calibrate(int dtype, const void *host_data, uint64_t n_elems, sz_codebook *out)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    if (!out || (n_elems && !host_data)) return SZ_E_ARG;
+    const uint32_t symbols = symbols_of(dtype);
+    std::vector<uint64_t> hist(symbols, 0);
+    if (dtype == SZ_BF16) {
+        const uint16_t *h = static_cast<const uint16_t *>(host_data);
+        for (uint64_t i = 0; i < n_elems; ++i) ++hist[(h[i] >> 7) & 0xFFu];
+    } else {
+        const uint8_t *h = static_cast<const uint8_t *>(host_data);
+        for (uint64_t i = 0; i < n_elems; ++i) ++hist[(h[i] >> 2) & 0x1Fu];
+    }
+    std::vector<uint32_t> order(symbols);
+    for (uint32_t v = 0; v < symbols; ++v) order[v] = v;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](uint32_t x, uint32_t y) { return hist[x] > hist[y]; });
+    out->dtype = (uint32_t)dtype;
+    for (int c = 0; c < 16; ++c) out->exp[c] = (uint8_t)order[c];
+    return SZ_OK;
+}
+
+extern "C" uint64_t sz_encoded_size(int dtype, uint64_t n_elems, uint64_t n_escapes)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return 0;
+    return geometry(dtype, n_elems).off_esc + 3 * n_escapes;
+}
+
+extern "C" uint64_t sz_workspace_size(int dtype, uint64_t n_elems)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return 0;
+    return ws_layout(dtype, n_elems).total;
+}
+
+extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *cb, void *d_out,
+                         uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    if (!cb) return SZ_E_ARG;
+    if (cb->dtype != (uint32_t)dtype) return SZ_E_DTYPE;
+    const uint32_t symbols = symbols_of(dtype);
+    for (int c = 0; c < 16; ++c) {
+        if (cb->exp[c] >= symbols) return SZ_E_ARG;
+        for (int d = 0; d < c; ++d)
+            if (cb->exp[d] == cb->exp[c]) return SZ_E_ARG;
+    }
+    if (n_elems > kMaxElems) return SZ_E_ARG;
+    if (!d_out || !d_ws || (n_elems && !d_in)) return SZ_E_ARG;
+    if (!aligned16(d_out) || !aligned16(d_ws) || (n_elems && !aligned16(d_in))) return SZ_E_ALIGN;
+    if (out_capacity < sz_encoded_size(dtype, n_elems, n_elems)) return SZ_E_CAPACITY;
+    if (ws_bytes < sz_workspace_size(dtype, n_elems)) return SZ_E_WORKSPACE;
+    if (dtype != SZ_BF16) return SZ_E_DTYPE;  // E5M2 kernels: not in this build yet
+
+    const Geometry g = geometry(dtype, n_elems);
+    const WsLayout w = ws_layout(dtype, n_elems);
+    uint8_t *ws = static_cast<uint8_t *>(d_ws);
+    uint8_t *out = static_cast<uint8_t *>(d_out);
+    uint32_t *tile_counts = reinterpret_cast<uint32_t *>(ws + w.counts);
+    uint64_t *tile_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
+    uint8_t *stage = ws + w.stage;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Codebook4 cb4 = pack_codebook(cb->exp);
+
+    if (g.nt) {
+        LaunchScope scope("sz_enc_dense_bf16", s);
+        hipLaunchKernelGGL(sz_enc_dense_bf16, dim3((uint32_t)g.nt), dim3(64), 0, s,
+                           static_cast<const uint16_t *>(d_in), g.n, out, g.off_nib, g.off_sm, cb4,
+                           tile_counts, stage);
+    }
+    {
+        HeaderArgs h;
+        h.n = g.n;
+        h.nb = g.nb;
+        h.dtype = (uint32_t)dtype;
+        h.cb = cb4;
+        h.pad_start[0] = 64 + 4 * g.nb;
+        h.pad_end[0] = g.off_nib;
+        h.pad_start[1] = g.off_nib + g.nib_bytes;
+        h.pad_end[1] = g.off_sm;
+        h.pad_start[2] = g.off_sm + g.sm_bytes;
+        h.pad_end[2] = g.off_esc;
+        LaunchScope scope("sz_enc_scan", s);
+        hipLaunchKernelGGL(sz_enc_scan, dim3(1), dim3(kScanThreads), 0, s, tile_counts, g.nt, tile_offsets,
+                           out, h);
+    }
+    if (g.nt) {
+        LaunchScope scope("sz_enc_compact", s);
+        hipLaunchKernelGGL(sz_enc_compact, dim3((uint32_t)g.nt), dim3(kCompactThreads), 0, s, stage,
+                           tile_counts, tile_offsets, out, g.off_esc);
+    }
+    return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
+}
+
+extern "C" int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
+                         void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    if (n_elems > kMaxElems) return SZ_E_ARG;
+    if (!d_in || !d_ws || (n_elems && !d_out)) return SZ_E_ARG;
+    if (!aligned16(d_in) || !aligned16(d_ws) || (n_elems && !aligned16(d_out))) return SZ_E_ALIGN;
+    if (in_bytes < sz_encoded_size(dtype, n_elems, 0)) return SZ_E_FORMAT;
+    if (ws_bytes < sz_workspace_size(dtype, n_elems)) return SZ_E_WORKSPACE;
+    if (dtype != SZ_BF16) return SZ_E_DTYPE;  // E5M2 kernels: not in this build yet
+
+    const Geometry g = geometry(dtype, n_elems);
+    const WsLayout w = ws_layout(dtype, n_elems);
+    uint8_t *ws = static_cast<uint8_t *>(d_ws);
+    int32_t *status = reinterpret_cast<int32_t *>(ws);
+    uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DecodeArgs a;
+    a.n = g.n;
+    a.nb = g.nb;
+    a.in_bytes = in_bytes;
+    a.off_nib = g.off_nib;
+    a.off_sm = g.off_sm;
+    a.off_esc = g.off_esc;
+    a.dtype = (uint32_t)dtype;
+    a.symbols = symbols_of(dtype);
+    const uint8_t *in = static_cast<const uint8_t *>(d_in);
+    {
+        LaunchScope scope("sz_dec_scan", s);
+        hipLaunchKernelGGL(sz_dec_scan, dim3(1), dim3(kScanThreads), 0, s, in, a, block_offsets, status);
+    }
+    if (g.nb) {
+        LaunchScope scope("sz_dec_bf16", s);
+        hipLaunchKernelGGL(sz_dec_bf16, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, block_offsets,
+                           status, static_cast<uint16_t *>(d_out));
+    }
+    return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
+}
+
+extern "C" int sz_profile_enable(int on)
+{
+    std::lock_guard<std::mutex> lock(g_prof_mutex);
+    for (auto &r : g_prof_records) {
+        (void)hipEventSynchronize(r.stop);
+    }
+    release_records();
+    g_prof_on = on != 0;
+    return SZ_OK;
+}
+
+extern "C" int sz_profile_collect(sz_kernel_stat *stats, int max_stats)
+{
+    if (max_stats < 0 || (max_stats > 0 && !stats)) return SZ_E_ARG;
+    std::lock_guard<std::mutex> lock(g_prof_mutex);
+    std::vector<sz_kernel_stat> acc;
+    int rc = SZ_OK;
+    for (auto &r : g_prof_records) {
+        if (hipEventSynchronize(r.stop) != hipSuccess) {
+            rc = SZ_E_HIP;
+            continue;
+        }
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+            rc = SZ_E_HIP;
+            continue;
+        }
+        auto it = std::find_if(acc.begin(), acc.end(),
+                               [&](const sz_kernel_stat &k) { return std::strcmp(k.name, r.name) == 0; });
+        if (it == acc.end()) {
+            sz_kernel_stat k{};
+            std::strncpy(k.name, r.name, sizeof(k.name) - 1);
+            acc.push_back(k);
+            it = acc.end() - 1;
+        }
+        it->launches += 1;
+        it->total_ms += ms;
+    }
+    release_records();
+    if (rc != SZ_OK) return rc;
+    const int count = std::min<int>(max_stats, (int)acc.size());
+    for (int i = 0; i < count; ++i) stats[i] = acc[i];
+    return count;
+}

@@ -1,0 +1,142 @@
+/*
+ * splitzip.h -- C ABI of the MI355X (gfx950) SplitZip codec.
+ *
+ * SplitZip ("SplitZip: Ultra Fast Lossless KV Compression for Disaggregated
+ * LLM Serving", gist.science summary page) compresses BF16 and FP8-E5M2 KV
+ * tensors losslessly: each value splits into its exponent, mapped through an
+ * offline-calibrated Top-16 codebook to a 4-bit code (two per byte), and its
+ * sign+mantissa bits, stored raw; exponents outside the codebook become
+ * escape records (16-bit position, 8-bit exponent).  Decode rebuilds every
+ * value from its code through a lookup table and then overwrites the escaped
+ * exponents.
+ *
+ * Conventions for every call:
+ *   - Integers in streams are little-endian.  A stream is self-describing:
+ *     its 64-byte header carries N, the dtype, the escape count E and the
+ *     codebook.  Stream layout (A(x) = x rounded up to 256, B = 65536
+ *     elements per block, nb = ceil(N/B)):
+ *       [0,64)   header: u32 magic 0x50495A53, u16 version 1, u8 dtype,
+ *                u8 log2(B)=16, u64 N, u64 E, u32 nb, u32 0, u8 codebook[16],
+ *                16 zero bytes
+ *       [64, 64+4nb)  u32 escape count of each block
+ *       off_nib = A(64+4nb): ceil(N/2) code bytes, element 2k in the low nibble
+ *       off_sm  = off_nib + A(ceil(N/2)): BF16: N bytes sign<<7|mantissa7;
+ *                 E5M2: 3*ceil(N/8) bytes, 8 symbols (sign<<2|mantissa2) per
+ *                 3 bytes, symbol j of a group at bit 3j
+ *       off_esc = off_sm + A(sign/mantissa bytes): E records of 3 bytes
+ *                 (pos lo, pos hi, exponent), pos = index inside the block,
+ *                 records in ascending element order
+ *       size    = off_esc + 3E
+ *     Escaped elements carry code 0.  All padding and reserved bytes are 0.
+ *   - Device pointers must be 16-byte aligned (torch allocations are).
+ *     The caller allocates and owns every buffer; the library keeps no
+ *     buffers between calls.
+ *   - Device calls only enqueue work on `stream` (a hipStream_t; NULL is the
+ *     null stream) and return once it is launched.  Calls that share a
+ *     workspace must not overlap.
+ *   - Errors are negative return codes; nothing throws or aborts across the
+ *     ABI.  Checks made on the device (decode) land in the workspace status
+ *     word, an int32 at workspace offset 0: 0 or a negative SZ_E_* code, valid
+ *     once the stream has synchronised.
+ */
+#ifndef SPLITZIP_H
+#define SPLITZIP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types: BF16 (exponent 8 bits, sign+mantissa 8 bits) and FP8 E5M2
+ * (exponent 5 bits, sign+mantissa 3 bits; the page's FP8 extension,
+ * Contributions item 4). */
+enum { SZ_BF16 = 0, SZ_FP8_E5M2 = 1 };
+
+enum {
+    SZ_OK = 0,
+    SZ_E_ARG = -1,       /* null pointer, bad codebook, size out of range */
+    SZ_E_DTYPE = -2,     /* unknown dtype, or codebook/stream of another dtype */
+    SZ_E_CAPACITY = -3,  /* output smaller than the worst-case stream */
+    SZ_E_ALIGN = -4,     /* device pointer not 16-byte aligned */
+    SZ_E_FORMAT = -5,    /* malformed or truncated stream */
+    SZ_E_HIP = -6,       /* a HIP launch or runtime call failed */
+    SZ_E_WORKSPACE = -7  /* workspace smaller than sz_workspace_size() */
+};
+
+/* Top-16 exponent codebook: exp[c] is the exponent that code c stands for.
+ * Entries are distinct and below 256 (BF16) or 32 (E5M2). */
+typedef struct sz_codebook {
+    uint32_t dtype;
+    uint8_t exp[16];
+} sz_codebook;
+
+/* Offline calibration (page: Method, "fixed-length coding" bullet, and
+ * Results, calibration ablation: one offline codebook, no online histogram).
+ * Host call.  host_data holds n_elems raw BF16 (uint16) or E5M2 (uint8)
+ * values.  Counts every exponent value and orders all 256 (32) values by
+ * count descending, then exponent ascending; the first 16 form the codebook,
+ * so 16 entries exist even when fewer exponents occur.  Returns SZ_OK,
+ * SZ_E_DTYPE or SZ_E_ARG (null pointer with n_elems > 0, null out). */
+int sz_calibrate(int dtype, const void *host_data, uint64_t n_elems, sz_codebook *out);
+
+/* Exact stream size for n_elems values with n_escapes escapes: the fixed
+ * sections plus 3 bytes per escape record (page: Method, "escape stream"
+ * bullet).  n_escapes = n_elems gives the worst case, which sz_encode needs
+ * as output capacity.  Returns 0 for an unknown dtype. */
+uint64_t sz_encoded_size(int dtype, uint64_t n_elems, uint64_t n_escapes);
+
+/* Device workspace that sz_encode and sz_decode need for n_elems values
+ * (tile escape counts and offsets, block offsets, the status word and the
+ * escape staging area of up to 3 bytes per element).  Returns 0 for an
+ * unknown dtype. */
+uint64_t sz_workspace_size(int dtype, uint64_t n_elems);
+
+/* Encode (page: Method, encoding bullets).  d_in: n_elems raw values on the
+ * device.  d_out: stream buffer of out_capacity >= sz_encoded_size(dtype,
+ * n_elems, n_elems) bytes.  d_ws: ws_bytes >= sz_workspace_size(dtype,
+ * n_elems).  The stream is byte-identical to the format above for the given
+ * codebook; its size is sz_encoded_size(dtype, n_elems, E) with E the u64 at
+ * stream offset 16, readable after the stream synchronises.  Bytes of d_out
+ * past that size are unspecified.  n_elems <= 2^40.  Returns SZ_OK or a
+ * negative code (host checks: dtype, codebook, pointers, alignment, capacity,
+ * workspace; SZ_E_HIP on launch failure). */
+int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *cb,
+              void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes,
+              void *stream);
+
+/* Decode (page: Method, decoding bullets: dense unpack + lookup table, then
+ * the sparse escape stream overwrites the escaped exponents).  d_in: a
+ * stream of in_bytes bytes on the device.  d_out: n_elems values.  d_ws:
+ * ws_bytes >= sz_workspace_size(dtype, n_elems).  The host checks the
+ * arguments and in_bytes >= sz_encoded_size(dtype, n_elems, 0); the device
+ * checks the header (magic, version, dtype, N, nb), the escape counts (each
+ * at most its block length, summing to E), that the E records fit in
+ * in_bytes, and that positions ascend strictly inside each block and stay
+ * below the block length.  A failed device check sets the workspace status
+ * word; d_out is then unspecified, and no byte outside d_out[0, n_elems) is
+ * ever written.  Escape records whose exponent is in the codebook are
+ * applied like any other. */
+int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
+              void *d_ws, uint64_t ws_bytes, void *stream);
+
+/* Instrumentation (not part of the codec).  While enabled, every kernel the
+ * library launches is bracketed by a pair of HIP events recorded on the
+ * launch stream.  sz_profile_collect waits for the recorded events, writes
+ * up to max_stats per-kernel totals (kernel name, launches, summed
+ * milliseconds) and clears the record; it returns the number of kernels
+ * written, or a negative code.  Enabling or disabling clears the record. */
+typedef struct sz_kernel_stat {
+    char name[48];
+    uint64_t launches;
+    double total_ms;
+} sz_kernel_stat;
+
+int sz_profile_enable(int on);
+int sz_profile_collect(sz_kernel_stat *stats, int max_stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITZIP_H */

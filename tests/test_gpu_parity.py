@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Encoded streams must equal the oracle's byte for byte over [0, size);
+decoded tensors must equal the input bit for bit (tolerance 0: everything
+is integer work).  Output buffers are poison-filled (0xA5) before each call
+so bytes the kernels never write show up.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import streamfmt
+
+pytestmark = pytest.mark.gpu
+
+POISON = 0xA5
+
+
+def _sz():
+    import fp8_kv_cache_sz_amd as sz
+    return sz
+
+
+def _dev_input(bits_np, dtype):
+    t = torch.from_numpy(bits_np.copy())
+    if dtype == 0:
+        t = t.view(torch.int16).view(torch.bfloat16)
+    return t.cuda()
+
+
+def _encode_gpu(x, cb_exps, dtype):
+    sz = _sz()
+    n = x.numel()
+    cap = sz.encoded_size(dtype, n, n)
+    out = torch.full((cap,), POISON, dtype=torch.uint8, device="cuda")
+    ws = torch.full((sz.workspace_size(dtype, n),), POISON, dtype=torch.uint8, device="cuda")
+    buf, size, esc = sz.encode(x, sz.Codebook(dtype, tuple(int(v) for v in cb_exps)), out=out, ws=ws)
+    return buf, size, esc
+
+
+def _decode_gpu(stream_dev, dtype, n, in_bytes=None, check=True):
+    sz = _sz()
+    out = torch.full((max(n, 1) * (2 if dtype == 0 else 1),), POISON, dtype=torch.uint8, device="cuda")
+    ws = torch.full((sz.workspace_size(dtype, n),), POISON, dtype=torch.uint8, device="cuda")
+    view = out.view(torch.bfloat16) if dtype == 0 else out
+    sz.decode(stream_dev, dtype, n, out=view[:n] if n else view[:0], ws=ws, check=check, in_bytes=in_bytes)
+    return out, ws
+
+
+def _bits_of(out_u8, dtype, n):
+    a = out_u8.cpu().numpy()
+    return a[:2 * n].view(np.uint16) if dtype == 0 else a[:n]
+
+
+def roundtrip_check(bits, dtype, cb):
+    """Full byte-for-byte encode parity and bit-exact decode (oracle and GPU streams)."""
+    print("roundtrip n=%d dtype=%d" % (bits.size, dtype), flush=True)
+    expect = oracle.encode(bits, dtype, cb)
+    x = _dev_input(bits, dtype)
+    buf, size, esc = _encode_gpu(x, cb, dtype)
+    assert size == expect.size
+    got = buf[:size].cpu().numpy()
+    if not np.array_equal(got, expect):
+        bad = np.nonzero(got != expect)[0]
+        raise AssertionError("stream differs at %d bytes, first %s (got %02x want %02x)"
+                             % (bad.size, bad[:8], got[bad[0]], expect[bad[0]]))
+    # decode the GPU stream and, separately, the oracle's stream
+    out, _ = _decode_gpu(buf[:size], dtype, bits.size)
+    assert np.array_equal(_bits_of(out, dtype, bits.size), bits)
+    out2, _ = _decode_gpu(torch.from_numpy(expect).cuda(), dtype, bits.size)
+    assert np.array_equal(_bits_of(out2, dtype, bits.size), bits)
+    # no byte past the decoded values was touched
+    tail = out[bits.size * (2 if dtype == 0 else 1):].cpu().numpy()
+    assert np.all(tail == POISON)
+    return expect
+
+
+EDGE_SIZES = [0, 1, 2, 3, 7, 8, 9, 15, 16, 17, 511, 512, 513, 4095, 4096, 4097, 16383, 16384,
+              16385, 65535, 65536, 65537, 3 * 65536 + 1003]
+
+
+@pytest.mark.parametrize("n", EDGE_SIZES)
+@pytest.mark.parametrize("dtype", [0])
+def test_edge_sizes_random_bits(n, dtype):
+    rng = np.random.default_rng(n + 17)
+    if dtype == 0:
+        bits = rng.integers(0, 65536, n, dtype=np.uint32).astype(np.uint16)
+        cb = rng.permutation(256)[:16].astype(np.uint8)
+    else:
+        bits = rng.integers(0, 256, n, dtype=np.uint32).astype(np.uint8)
+        cb = rng.permutation(32)[:16].astype(np.uint8)
+    roundtrip_check(bits, dtype, cb)
+
+
+@pytest.mark.parametrize("n", [1, 9, 4097, 65537, 200000])
+@pytest.mark.parametrize("dtype", [0])
+def test_edge_sizes_kv_like(n, dtype):
+    """Narrow exponent distribution (few escapes), calibrated codebook."""
+    rng = np.random.default_rng(n)
+    if dtype == 0:
+        e = np.clip(np.rint(rng.normal(126, 2.5, n)), 0, 255).astype(np.uint16)
+        bits = ((rng.integers(0, 256, n).astype(np.uint16) & 0x80) << 8) | (e << 7) | rng.integers(0, 128, n).astype(np.uint16)
+        bits = bits.astype(np.uint16)
+    else:
+        e = np.clip(np.rint(rng.normal(14, 2.0, n)), 0, 31).astype(np.uint8)
+        bits = ((rng.integers(0, 2, n).astype(np.uint8) << 7) | (e << 2) | rng.integers(0, 4, n).astype(np.uint8)).astype(np.uint8)
+    cb = oracle.calibrate(bits, dtype)
+    roundtrip_check(bits, dtype, cb)
+
+
+def test_all_bf16_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    roundtrip_check(bits, 0, oracle.calibrate(bits, 0))
+
+
+def test_every_element_escapes():
+    """Two full blocks and a tail where no exponent is in the codebook."""
+    n = 2 * 65536 + 77
+    rng = np.random.default_rng(5)
+    e = rng.integers(16, 256, n).astype(np.uint16)
+    bits = ((rng.integers(0, 2, n).astype(np.uint16) << 15) | (e << 7) | rng.integers(0, 128, n).astype(np.uint16)).astype(np.uint16)
+    cb = np.arange(16, dtype=np.uint8)
+    expect = roundtrip_check(bits, 0, cb)
+    assert streamfmt.header(expect)["escapes"] == n
+
+
+def test_single_escapes_at_block_edges():
+    n = 3 * 65536
+    bits = np.full(n, 0x3F80, dtype=np.uint16)
+    for i in (0, 65535, 65536, 2 * 65536 + 7, n - 1):
+        bits[i] = 0x0080 | 0x8000            # exponent 1, negative
+    cb = np.array([127] + list(range(100, 115)), dtype=np.uint8)
+    expect = roundtrip_check(bits, 0, cb)
+    sec = streamfmt.sections(expect)
+    assert list(sec["counts"]) == [2, 1, 2]
+    assert list(sec["pos"]) == [0, 65535, 0, 7, 65535]
+
+
+def test_no_escapes_single_exponent():
+    bits = synth.as_bits_numpy(synth.single_exponent(41, 300000, 127))
+    cb = oracle.calibrate(synth.as_bits_numpy(synth.calibration_tensor("kv1m")), 0)
+    expect = roundtrip_check(bits, 0, cb)
+    assert streamfmt.header(expect)["escapes"] == 0
+
+
+@pytest.mark.parametrize("name", ["kv1m", "llama3_8b_kv", "longctx_kv", "stress_t3", "stress_oneexp",
+                                  "stress_random"])
+def test_workloads_small(name):
+    x, dtype = synth.workload(name, size="small")
+    cb = oracle.calibrate(synth.as_bits_numpy(synth.calibration_tensor(name)), dtype)
+    roundtrip_check(synth.as_bits_numpy(x), dtype, cb)
+
+
+def test_gpu_calibration_matches_oracle():
+    sz = _sz()
+    for name in ("kv1m", "llama3_8b_kv"):
+        cal = synth.calibration_tensor(name)
+        assert list(sz.calibrate(cal).exps) == list(oracle.calibrate(synth.as_bits_numpy(cal), 0))
+
+
+def test_encode_is_deterministic_and_stream_order_safe():
+    sz = _sz()
+    x, dtype = synth.workload("stress_t3", size="small")
+    cb = sz.calibrate(synth.calibration_tensor("kv1m"))
+    xd = x.cuda()
+    a, size_a, _ = sz.encode(xd, cb)
+    b, size_b, _ = sz.encode(xd, cb)
+    assert size_a == size_b
+    assert torch.equal(a[:size_a], b[:size_b])
+    # two encodes in flight on one stream with distinct workspaces, then decodes
+    y = torch.flip(xd, [0]).contiguous()
+    s1, _, _ = sz.encode(xd, cb, sync=False)
+    s2, _, _ = sz.encode(y, cb, sync=False)
+    torch.cuda.synchronize()
+    d1 = sz.decode(s1, dtype, xd.numel())
+    d2 = sz.decode(s2, dtype, y.numel())
+    assert torch.equal(d1.view(torch.int16), xd.view(torch.int16))
+    assert torch.equal(d2.view(torch.int16), y.view(torch.int16))
+
+
+def _corrupt_cases(stream, n):
+    L = streamfmt.layout(0, n)
+    first = L["off_esc"]
+    yield "magic", lambda t: t.__setitem__(0, 0)
+    yield "version", lambda t: t.__setitem__(4, 2)
+    yield "n", lambda t: t.__setitem__(8, (int(t[8]) + 1) % 256)
+    yield "escapes", lambda t: t.__setitem__(16, int(t[16]) + 1)
+    yield "count", lambda t: t.__setitem__(64, int(t[64]) + 1)
+    yield "pos_repeat", lambda t: t.__setitem__(slice(first + 3, first + 5), t[first:first + 2].copy())
+    yield "pos_range", lambda t: t.__setitem__(slice(first + 6 * 3, first + 6 * 3 + 2), [0xFF, 0xFF])
+    yield "cb_range", lambda t: t.__setitem__(32, 255)          # fine for BF16: stays valid
+
+
+def test_device_validation_matches_oracle():
+    n = 70000
+    rng = np.random.default_rng(9)
+    bits = np.full(n, 0x3F80, dtype=np.uint16)
+    idx = np.sort(rng.choice(n - 1, 40, replace=False))
+    bits[idx] = 0x0001
+    cb = np.array([127] + list(range(100, 115)), dtype=np.uint8)
+    good = oracle.encode(bits, 0, cb)
+    for name, mutate in _corrupt_cases(good, n):
+        t = good.copy()
+        mutate(t)
+        want = oracle.validate(t, 0, n)
+        _, ws = _decode_gpu(torch.from_numpy(t).cuda(), 0, n, check=False)
+        status = int(ws[:4].cpu().view(torch.int32)[0])
+        print(name, want, status, flush=True)
+        assert status == want, name
+    # the untouched stream passes
+    _, ws = _decode_gpu(torch.from_numpy(good).cuda(), 0, n, check=False)
+    assert int(ws[:4].cpu().view(torch.int32)[0]) == 0
+    # truncated: records past in_bytes
+    _, ws = _decode_gpu(torch.from_numpy(good).cuda(), 0, n, in_bytes=good.size - 1, check=False)
+    assert int(ws[:4].cpu().view(torch.int32)[0]) == oracle.E_FORMAT
+
+
+def test_profile_hooks_record_kernels():
+    sz = _sz()
+    x = synth.kv_layer(0).cuda()
+    cb = sz.calibrate(synth.calibration_tensor("kv1m"))
+    sz.profile_enable(True)
+    buf, size, _ = sz.encode(x, cb)
+    sz.decode(buf[:size], 0, x.numel())
+    stats = sz.profile_collect()
+    sz.profile_enable(False)
+    assert stats["sz_enc_dense_bf16"][0] == 1 and stats["sz_dec_bf16"][0] == 1
+    assert all(ms >= 0 for _, ms in stats.values())

@@ -1,0 +1,105 @@
+"""CPU checks of the C-ABI library: it loads, exports every call that
+include/splitzip.h declares, and its host-side logic (calibration, sizes,
+argument checks that fail before any launch) agrees with the oracle and the
+format's closed forms.  No GPU work is started here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _native():
+    from fp8_kv_cache_sz_amd import build
+    if not os.path.exists(build.LIBRARY):
+        build.build()
+    from fp8_kv_cache_sz_amd import _native
+    return _native
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "splitzip.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|uint64_t|void)\s*\*?\s*(sz_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    nat = _native()
+    names = declared_functions()
+    assert {"sz_calibrate", "sz_encoded_size", "sz_workspace_size", "sz_encode", "sz_decode"} <= set(names)
+    for name in names:
+        assert hasattr(nat.lib, name), name
+    assert set(names) == set(nat.EXPORTS)
+
+
+def test_encoded_size_matches_oracle():
+    nat = _native()
+    for dtype in (0, 1):
+        for n in (0, 1, 2, 7, 8, 9, 255, 256, 65535, 65536, 65537, 1 << 20, (1 << 29) + 3, 1879048192):
+            for e in (0, 1, n // 3, n):
+                assert nat.sz_encoded_size(dtype, n, e) == oracle.encoded_size(dtype, n, e), (dtype, n, e)
+    assert nat.sz_encoded_size(9, 10, 0) == 0
+    assert nat.sz_workspace_size(9, 10) == 0
+    for dtype in (0, 1):
+        for n in (0, 1, 1 << 20, 1879048192):
+            ws = nat.sz_workspace_size(dtype, n)
+            assert ws >= 256 and ws % 256 == 0
+            assert ws >= 3 * n                      # escape staging, 3 bytes per element
+
+
+@pytest.mark.parametrize("source", ["kv1m", "bruteforce", "random_cb_data", "empty"])
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_calibrate_matches_oracle(source, dtype):
+    nat = _native()
+    if source == "kv1m":
+        if dtype == 0:
+            data = synth.as_bits_numpy(synth.calibration_tensor("kv1m"))
+        else:
+            data = synth.as_bits_numpy(synth.calibration_tensor("llama3_8b_kv_e5m2"))
+    elif source == "bruteforce":
+        data = np.arange(65536 if dtype == 0 else 256, dtype=np.uint32).astype(np.uint16 if dtype == 0 else np.uint8)
+    elif source == "random_cb_data":
+        rng = np.random.default_rng(3)
+        data = rng.integers(0, 1 << (16 if dtype == 0 else 8), 50000).astype(np.uint16 if dtype == 0 else np.uint8)
+    else:
+        data = np.zeros(0, dtype=np.uint16 if dtype == 0 else np.uint8)
+    ptr = data.ctypes.data if data.size else None
+    cb = nat.sz_calibrate(dtype, ptr, data.size)
+    assert cb.dtype == dtype
+    assert list(cb.exp) == list(oracle.calibrate(data, dtype))
+
+
+def test_host_argument_checks():
+    nat = _native()
+    cb = nat.sz_codebook()
+    cb.dtype = 0
+    for c in range(16):
+        cb.exp[c] = 120 + c
+    dummy = 1 << 20        # never dereferenced: every call below fails a host check first
+    assert nat.sz_encode(5, dummy, 16, cb, dummy, 1 << 30, dummy, 1 << 30, None) == -2
+    cb.dtype = 1
+    assert nat.sz_encode(0, dummy, 16, cb, dummy, 1 << 30, dummy, 1 << 30, None) == -2
+    cb.dtype = 0
+    cb.exp[3] = cb.exp[2]
+    assert nat.sz_encode(0, dummy, 16, cb, dummy, 1 << 30, dummy, 1 << 30, None) == -1
+    cb.exp[3] = 123
+    assert nat.sz_encode(0, None, 16, cb, dummy, 1 << 30, dummy, 1 << 30, None) == -1
+    assert nat.sz_encode(0, dummy + 2, 16, cb, dummy, 1 << 30, dummy, 1 << 30, None) == -4
+    cap = nat.sz_encoded_size(0, 16, 16)
+    assert nat.sz_encode(0, dummy, 16, cb, dummy, cap - 1, dummy, 1 << 30, None) == -3
+    ws = nat.sz_workspace_size(0, 16)
+    assert nat.sz_encode(0, dummy, 16, cb, dummy, cap, dummy, ws - 1, None) == -7
+    assert nat.sz_encode(0, dummy, (1 << 40) + 1, cb, dummy, 1 << 62, dummy, 1 << 62, None) == -1
+    # decode: stream shorter than the fixed sections, bad dtype, alignment
+    fixed = nat.sz_encoded_size(0, 1000, 0)
+    assert nat.sz_decode(dummy, fixed - 1, 0, dummy, 1000, dummy, 1 << 30, None) == -5
+    assert nat.sz_decode(dummy, fixed, 3, dummy, 1000, dummy, 1 << 30, None) == -2
+    assert nat.sz_decode(dummy + 8, fixed, 0, dummy, 1000, dummy, 1 << 30, None) == -4
+    assert nat.sz_decode(dummy, fixed, 0, dummy, 1000, dummy, 16, None) == -7
