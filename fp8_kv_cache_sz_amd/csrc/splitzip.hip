@@ -296,6 +296,160 @@ __global__ __launch_bounds__(64) void sz_enc_dense_bf16(const uint16_t *__restri
 }
 
 // ---------------------------------------------------------------------------
+// FP8 E5M2 encode (the page's FP8 extension, Contributions item 4).
+// One 32-element chunk per lane: 32 bytes in, 16 code bytes (uint4) and
+// 12 sign/mantissa bytes (four 24-bit groups of eight 3-bit symbols) out.
+//   esc[s], ex[s]: escape flags (bit 8k+7) and exponents (byte k) of the
+//   eight elements 8s..8s+7.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pack_sm3_x4(uint32_t sym)
+{
+    // four 3-bit symbols held in bytes -> 12 contiguous bits
+    return (sym & 0x7u) | ((sym >> 5) & 0x38u) | ((sym >> 10) & 0x1C0u) | ((sym >> 15) & 0xE00u);
+}
+
+__device__ __forceinline__ void encode_chunk_e5m2(const uint4 q0, const uint4 q1, const uint8_t *table,
+                                                  uint4 &nib, uint32_t sm3[3], uint64_t esc[4],
+                                                  uint64_t ex[4])
+{
+    const uint32_t d[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    uint32_t nibw[4], grp[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t a = d[2 * s], b = d[2 * s + 1];
+        const uint32_t e_a = (a >> 2) & 0x1F1F1F1Fu;
+        const uint32_t e_b = (b >> 2) & 0x1F1F1F1Fu;
+        const uint32_t s_a = ((a >> 5) & 0x04040404u) | (a & 0x03030303u);
+        const uint32_t s_b = ((b >> 5) & 0x04040404u) | (b & 0x03030303u);
+        const uint32_t c_a = (uint32_t)table[e_a & 0xFFu] | ((uint32_t)table[(e_a >> 8) & 0xFFu] << 8) |
+                             ((uint32_t)table[(e_a >> 16) & 0xFFu] << 16) |
+                             ((uint32_t)table[e_a >> 24] << 24);
+        const uint32_t c_b = (uint32_t)table[e_b & 0xFFu] | ((uint32_t)table[(e_b >> 8) & 0xFFu] << 8) |
+                             ((uint32_t)table[(e_b >> 16) & 0xFFu] << 16) |
+                             ((uint32_t)table[e_b >> 24] << 24);
+        const uint32_t k_a = c_a & 0x0F0F0F0Fu;
+        const uint32_t k_b = c_b & 0x0F0F0F0Fu;
+        nibw[s] = perm(k_b | (k_b >> 4), k_a | (k_a >> 4), 0x06040200u);
+        esc[s] = (uint64_t)(c_a & 0x80808080u) | ((uint64_t)(c_b & 0x80808080u) << 32);
+        ex[s] = (uint64_t)e_a | ((uint64_t)e_b << 32);
+        grp[s] = pack_sm3_x4(s_a) | (pack_sm3_x4(s_b) << 12);
+    }
+    nib = make_uint4(nibw[0], nibw[1], nibw[2], nibw[3]);
+    sm3[0] = grp[0] | (grp[1] << 24);
+    sm3[1] = (grp[1] >> 8) | (grp[2] << 16);
+    sm3[2] = (grp[2] >> 16) | (grp[3] << 8);
+}
+
+constexpr uint32_t kE5Chunks = 2;                          // 32-element chunks per lane per row
+constexpr uint32_t kE5Row = 64 * 32 * kE5Chunks;           // 4096 elements
+
+__global__ __launch_bounds__(64) void sz_enc_dense_e5m2(const uint8_t *__restrict__ in, uint64_t n,
+                                                        uint8_t *__restrict__ out, uint64_t off_nib,
+                                                        uint64_t off_sm, uint64_t sm_bytes, Codebook4 cb,
+                                                        uint32_t *__restrict__ tile_counts,
+                                                        uint8_t *__restrict__ stage)
+{
+    __shared__ uint32_t table32[64];
+    build_encode_table(table32, cb, 32);
+    __syncthreads();
+    const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
+
+    const uint32_t lane = lane_id();
+    const uint64_t tile = blockIdx.x;
+    const uint64_t t0 = tile * kEncTile;
+    const bool full_tile = t0 + kEncTile <= n;
+    uint8_t *tstage = stage + tile * (3ull * kEncTile);
+    uint32_t tile_escapes = 0;
+
+    for (uint32_t row = 0; row < kEncTile / kE5Row; ++row) {
+        const uint64_t base = t0 + (uint64_t)row * kE5Row;
+        if (base >= n) break;
+        uint4 q[kE5Chunks][2];
+#pragma unroll
+        for (uint32_t j = 0; j < kE5Chunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+            if (full_tile || c0 + 32 <= n) {
+                q[j][0] = *reinterpret_cast<const uint4 *>(in + c0);
+                q[j][1] = *reinterpret_cast<const uint4 *>(in + c0 + 16);
+            } else {
+                uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                for (uint32_t k = 0; c0 + k < n && k < 32; ++k) w[k / 4] |= (uint32_t)in[c0 + k] << (8 * (k & 3));
+                q[j][0] = make_uint4(w[0], w[1], w[2], w[3]);
+                q[j][1] = make_uint4(w[4], w[5], w[6], w[7]);
+            }
+        }
+        uint64_t esc[kE5Chunks][4], ex[kE5Chunks][4];
+        uint32_t cnt[kE5Chunks];
+#pragma unroll
+        for (uint32_t j = 0; j < kE5Chunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+            uint4 nib;
+            uint32_t sm3[3];
+            encode_chunk_e5m2(q[j][0], q[j][1], table, nib, sm3, esc[j], ex[j]);
+            uint8_t *sm_dst = out + off_sm + (c0 / 32) * 12;
+            if (full_tile || c0 + 32 <= n) {
+                *reinterpret_cast<uint4 *>(out + off_nib + c0 / 2) = nib;
+                *reinterpret_cast<uint3 *>(sm_dst) = make_uint3(sm3[0], sm3[1], sm3[2]);
+            } else if (c0 < n) {
+                // last, partial chunk: missing elements get code 0, symbol 0 and
+                // no escape; only the groups that hold data are stored
+                const uint32_t valid = (uint32_t)(n - c0);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int v = (int)valid - 8 * s;
+                    const uint64_t keep = v >= 8 ? ~0ull : (v <= 0 ? 0ull : ((1ull << (8 * v)) - 1));
+                    esc[j][s] &= keep;
+                }
+                uint32_t nw[4] = {nib.x, nib.y, nib.z, nib.w};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int v = (int)valid - 8 * s;
+                    nw[s] &= v >= 8 ? 0xFFFFFFFFu : (v <= 0 ? 0u : (uint32_t)((1ull << (4 * v)) - 1));
+                }
+                *reinterpret_cast<uint4 *>(out + off_nib + c0 / 2) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+                // sign/mantissa: 3 bits per element, so the first 3 * valid bits
+                uint32_t sw[3] = {sm3[0], sm3[1], sm3[2]};
+                const uint32_t bits = 3 * valid;
+#pragma unroll
+                for (int w = 0; w < 3; ++w) {
+                    const int b = (int)bits - 32 * w;
+                    sw[w] &= b >= 32 ? 0xFFFFFFFFu : (b <= 0 ? 0u : ((1u << b) - 1));
+                }
+                const uint64_t sm_start = off_sm + (c0 / 32) * 12;
+                const uint64_t sm_end = off_sm + sm_bytes;
+                for (uint32_t i = 0; i < 12 && sm_start + i < sm_end; ++i)
+                    out[sm_start + i] = (uint8_t)(sw[i / 4] >> (8 * (i & 3)));
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) esc[j][s] = 0;
+            }
+            cnt[j] = popc64(esc[j][0]) + popc64(esc[j][1]) + popc64(esc[j][2]) + popc64(esc[j][3]);
+        }
+        if (__ballot((cnt[0] | cnt[1]) != 0) == 0) continue;
+        const uint32_t packed = cnt[0] | (cnt[1] << 16);
+        const uint32_t incl = wave_inclusive_sum(packed);
+        const uint32_t tot = read_lane63(incl);
+        const uint32_t excl = incl - packed;
+        uint32_t running = tile_escapes;
+#pragma unroll
+        for (uint32_t j = 0; j < kE5Chunks; ++j) {
+            uint32_t rank = running + ((excl >> (16 * j)) & 0xFFFFu);
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (esc[j][s]) {
+                    stage_records(tstage, rank, esc[j][s], ex[j][s], (uint32_t)((c0 + 8 * s) & 0xFFFFu), 8);
+                    rank += popc64(esc[j][s]);
+                }
+            }
+            running += (tot >> (16 * j)) & 0xFFFFu;
+        }
+        tile_escapes = running;
+    }
+    if (lane == 0) tile_counts[tile] = tile_escapes;
+}
+
+// ---------------------------------------------------------------------------
 // Block-level exclusive scan helper for the one-workgroup scan kernels.
 // Returns the exclusive prefix of x inside the workgroup and the total.
 // ---------------------------------------------------------------------------
@@ -617,6 +771,147 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
 }
 
 // ---------------------------------------------------------------------------
+// Kernel: FP8 E5M2 decode, one workgroup (4 waves) per 64K block.  A lane
+// decodes 32 elements: 16 code bytes + 12 sign/mantissa bytes -> 32 bytes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t unpack_sm3_x4(uint32_t v12)
+{
+    // 12 bits = four 3-bit symbols -> one symbol per byte
+    return (v12 & 0x7u) | ((v12 << 5) & 0x700u) | ((v12 << 10) & 0x70000u) | ((v12 << 15) & 0x7000000u);
+}
+
+__device__ __forceinline__ void decode_chunk_e5m2(const uint4 nib, const uint32_t sm3[3],
+                                                  const uint16_t *table, uint32_t o[8])
+{
+    // table[b] = (cb[b & 15] << 2) | (cb[b >> 4] << 10): the exponent fields of
+    // the two elements of code byte b, in place inside two E5M2 bytes
+    const uint32_t nw[4] = {nib.x, nib.y, nib.z, nib.w};
+    const uint32_t grp[4] = {sm3[0] & 0xFFFFFFu, (sm3[0] >> 24) | ((sm3[1] & 0xFFFFu) << 8),
+                             (sm3[1] >> 16) | ((sm3[2] & 0xFFu) << 16), sm3[2] >> 8};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t w = nw[s];
+        const uint32_t e_lo = (uint32_t)table[w & 0xFFu] | ((uint32_t)table[(w >> 8) & 0xFFu] << 16);
+        const uint32_t e_hi = (uint32_t)table[(w >> 16) & 0xFFu] | ((uint32_t)table[w >> 24] << 16);
+        const uint32_t t_lo = unpack_sm3_x4(grp[s] & 0xFFFu);
+        const uint32_t t_hi = unpack_sm3_x4(grp[s] >> 12);
+        o[2 * s] = ((t_lo & 0x04040404u) << 5) | (t_lo & 0x03030303u) | e_lo;
+        o[2 * s + 1] = ((t_hi & 0x04040404u) << 5) | (t_hi & 0x03030303u) | e_hi;
+    }
+}
+
+__global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                           const uint64_t *__restrict__ block_offsets,
+                                                           int32_t *__restrict__ status,
+                                                           uint8_t *__restrict__ out)
+{
+    __shared__ uint16_t table[256];
+    __shared__ uint16_t first[kBlock / 32];    // first escape record of each 32-element chunk
+    if (*status != 0) return;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t b = blockIdx.x;
+    const uint64_t e0 = b * kBlock;
+    const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
+    const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
+    const uint64_t r0 = block_offsets[b];
+    const uint8_t *esc = in + a.off_esc;
+    {
+        const uint32_t lo = in[32 + (tid & 15)];
+        const uint32_t hi = in[32 + (tid >> 4)];
+        table[tid] = (uint16_t)((lo << 2) | (hi << 10));
+    }
+    if (k) {
+        uint4 *f4 = reinterpret_cast<uint4 *>(first);
+        const uint4 none = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+        for (uint32_t i = tid; i < kBlock / 32 / 8; i += kDecThreads) f4[i] = none;
+    }
+    __syncthreads();
+    if (k) {
+        bool bad = false;
+        for (uint32_t r = tid; r < k; r += kDecThreads) {
+            uint32_t pos, e;
+            read_record(esc, r0 + r, pos, e);
+            int32_t prev = -1;
+            if (r > 0) {
+                uint32_t pp, pe;
+                read_record(esc, r0 + r - 1, pp, pe);
+                prev = (int32_t)pp;
+            }
+            if (pos >= blen || (int32_t)pos <= prev || e >= 32) {
+                bad = true;
+                continue;
+            }
+            if (r == 0 || (uint32_t)(prev >> 5) != (pos >> 5)) first[pos >> 5] = (uint16_t)r;
+        }
+        if (bad) atomicExch(status, SZ_E_FORMAT);
+    }
+    __syncthreads();
+
+    const uint32_t lane = lane_id();
+    const uint32_t wave = tid / 64;
+    const bool full_block = blen == kBlock;
+    const uint8_t *nib_base = in + a.off_nib;
+    const uint8_t *sm_base = in + a.off_sm;
+    const uint64_t sm_end = a.off_sm + 3 * ((a.n + 7) / 8);
+    for (uint32_t row = 0; row < 4; ++row) {
+        const uint32_t rbase = wave * 16384 + row * kE5Row;
+        if (rbase >= blen) break;
+        uint4 nib[kE5Chunks];
+        uint32_t sm3[kE5Chunks][3];
+#pragma unroll
+        for (uint32_t j = 0; j < kE5Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 32;
+            const uint64_t g = e0 + c;
+            if (full_block || c + 32 <= blen) {
+                nib[j] = *reinterpret_cast<const uint4 *>(nib_base + g / 2);
+                const uint3 v = *reinterpret_cast<const uint3 *>(sm_base + (g / 32) * 12);
+                sm3[j][0] = v.x;
+                sm3[j][1] = v.y;
+                sm3[j][2] = v.z;
+            } else if (c < blen) {
+                nib[j] = *reinterpret_cast<const uint4 *>(nib_base + g / 2);
+                sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
+                const uint64_t start = a.off_sm + (g / 32) * 12;
+                for (uint32_t i = 0; i < 12 && start + i < sm_end; ++i)
+                    sm3[j][i / 4] |= (uint32_t)in[start + i] << (8 * (i & 3));
+            } else {
+                nib[j] = make_uint4(0, 0, 0, 0);
+                sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
+            }
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < kE5Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 32;
+            uint32_t o[8];
+            decode_chunk_e5m2(nib[j], sm3[j], table, o);
+            if (k) {
+                uint32_t r = first[c >> 5];
+                if (r != kNoEscape) {
+                    for (; r < k; ++r) {
+                        uint32_t pos, e;
+                        read_record(esc, r0 + r, pos, e);
+                        if ((pos >> 5) != (c >> 5)) break;
+                        const uint32_t p = pos & 31;
+                        const uint32_t sh = 8 * (p & 3) + 2;
+                        const uint32_t clear = ~(0x1Fu << sh);
+#pragma unroll
+                        for (int w = 0; w < 8; ++w)
+                            if ((uint32_t)w == (p >> 2)) o[w] = (o[w] & clear) | (e << sh);
+                    }
+                }
+            }
+            const uint64_t g = e0 + c;
+            if (full_block || c + 32 <= blen) {
+                *reinterpret_cast<uint4 *>(out + g) = make_uint4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<uint4 *>(out + g + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+            } else if (c < blen) {
+                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint8_t)(o[i / 4] >> (8 * (i & 3)));
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side: launch bookkeeping and instrumentation
 // ---------------------------------------------------------------------------
 struct ProfRecord {
@@ -742,8 +1037,6 @@ extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz
     if (!aligned16(d_out) || !aligned16(d_ws) || (n_elems && !aligned16(d_in))) return SZ_E_ALIGN;
     if (out_capacity < sz_encoded_size(dtype, n_elems, n_elems)) return SZ_E_CAPACITY;
     if (ws_bytes < sz_workspace_size(dtype, n_elems)) return SZ_E_WORKSPACE;
-    if (dtype != SZ_BF16) return SZ_E_DTYPE;  // E5M2 kernels: not in this build yet
-
     const Geometry g = geometry(dtype, n_elems);
     const WsLayout w = ws_layout(dtype, n_elems);
     uint8_t *ws = static_cast<uint8_t *>(d_ws);
@@ -754,11 +1047,16 @@ extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Codebook4 cb4 = pack_codebook(cb->exp);
 
-    if (g.nt) {
+    if (g.nt && dtype == SZ_BF16) {
         LaunchScope scope("sz_enc_dense_bf16", s);
         hipLaunchKernelGGL(sz_enc_dense_bf16, dim3((uint32_t)g.nt), dim3(64), 0, s,
                            static_cast<const uint16_t *>(d_in), g.n, out, g.off_nib, g.off_sm, cb4,
                            tile_counts, stage);
+    } else if (g.nt) {
+        LaunchScope scope("sz_enc_dense_e5m2", s);
+        hipLaunchKernelGGL(sz_enc_dense_e5m2, dim3((uint32_t)g.nt), dim3(64), 0, s,
+                           static_cast<const uint8_t *>(d_in), g.n, out, g.off_nib, g.off_sm, g.sm_bytes,
+                           cb4, tile_counts, stage);
     }
     {
         HeaderArgs h;
@@ -793,8 +1091,6 @@ extern "C" int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d
     if (!aligned16(d_in) || !aligned16(d_ws) || (n_elems && !aligned16(d_out))) return SZ_E_ALIGN;
     if (in_bytes < sz_encoded_size(dtype, n_elems, 0)) return SZ_E_FORMAT;
     if (ws_bytes < sz_workspace_size(dtype, n_elems)) return SZ_E_WORKSPACE;
-    if (dtype != SZ_BF16) return SZ_E_DTYPE;  // E5M2 kernels: not in this build yet
-
     const Geometry g = geometry(dtype, n_elems);
     const WsLayout w = ws_layout(dtype, n_elems);
     uint8_t *ws = static_cast<uint8_t *>(d_ws);
@@ -815,10 +1111,14 @@ extern "C" int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d
         LaunchScope scope("sz_dec_scan", s);
         hipLaunchKernelGGL(sz_dec_scan, dim3(1), dim3(kScanThreads), 0, s, in, a, block_offsets, status);
     }
-    if (g.nb) {
+    if (g.nb && dtype == SZ_BF16) {
         LaunchScope scope("sz_dec_bf16", s);
         hipLaunchKernelGGL(sz_dec_bf16, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, block_offsets,
                            status, static_cast<uint16_t *>(d_out));
+    } else if (g.nb) {
+        LaunchScope scope("sz_dec_e5m2", s);
+        hipLaunchKernelGGL(sz_dec_e5m2, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, block_offsets,
+                           status, static_cast<uint8_t *>(d_out));
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }

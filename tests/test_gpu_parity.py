@@ -82,7 +82,7 @@ EDGE_SIZES = [0, 1, 2, 3, 7, 8, 9, 15, 16, 17, 511, 512, 513, 4095, 4096, 4097, 
 
 
 @pytest.mark.parametrize("n", EDGE_SIZES)
-@pytest.mark.parametrize("dtype", [0])
+@pytest.mark.parametrize("dtype", [0, 1])
 def test_edge_sizes_random_bits(n, dtype):
     rng = np.random.default_rng(n + 17)
     if dtype == 0:
@@ -94,8 +94,8 @@ def test_edge_sizes_random_bits(n, dtype):
     roundtrip_check(bits, dtype, cb)
 
 
-@pytest.mark.parametrize("n", [1, 9, 4097, 65537, 200000])
-@pytest.mark.parametrize("dtype", [0])
+@pytest.mark.parametrize("n", [1, 9, 31, 33, 4097, 65537, 200000])
+@pytest.mark.parametrize("dtype", [0, 1])
 def test_edge_sizes_kv_like(n, dtype):
     """Narrow exponent distribution (few escapes), calibrated codebook."""
     rng = np.random.default_rng(n)
@@ -113,6 +113,15 @@ def test_edge_sizes_kv_like(n, dtype):
 def test_all_bf16_patterns():
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     roundtrip_check(bits, 0, oracle.calibrate(bits, 0))
+
+
+def test_all_e5m2_patterns():
+    bits = np.arange(256, dtype=np.uint32).astype(np.uint8)
+    roundtrip_check(bits, 1, oracle.calibrate(bits, 1))
+    # every pattern 300 times, in a shuffled order over several blocks
+    rng = np.random.default_rng(2)
+    many = rng.permutation(np.tile(bits, 300))
+    roundtrip_check(many, 1, oracle.calibrate(many, 1))
 
 
 def test_every_element_escapes():
@@ -146,7 +155,7 @@ def test_no_escapes_single_exponent():
 
 
 @pytest.mark.parametrize("name", ["kv1m", "llama3_8b_kv", "longctx_kv", "stress_t3", "stress_oneexp",
-                                  "stress_random"])
+                                  "stress_random", "llama3_8b_kv_e5m2"])
 def test_workloads_small(name):
     x, dtype = synth.workload(name, size="small")
     cb = oracle.calibrate(synth.as_bits_numpy(synth.calibration_tensor(name)), dtype)
@@ -209,6 +218,9 @@ def test_device_validation_matches_oracle():
         status = int(ws[:4].cpu().view(torch.int32)[0])
         print(name, want, status, flush=True)
         assert status == want, name
+    # a BF16 stream handed to the E5M2 decoder
+    _, ws = _decode_gpu(torch.from_numpy(good).cuda(), 1, n, check=False)
+    assert int(ws[:4].cpu().view(torch.int32)[0]) == oracle.validate(good, 1, n) == oracle.E_DTYPE
     # the untouched stream passes
     _, ws = _decode_gpu(torch.from_numpy(good).cuda(), 0, n, check=False)
     assert int(ws[:4].cpu().view(torch.int32)[0]) == 0
@@ -228,3 +240,20 @@ def test_profile_hooks_record_kernels():
     sz.profile_enable(False)
     assert stats["sz_enc_dense_bf16"][0] == 1 and stats["sz_dec_bf16"][0] == 1
     assert all(ms >= 0 for _, ms in stats.values())
+
+
+def test_e5m2_device_validation():
+    n = 5000
+    bits = np.full(n, 0x3C, dtype=np.uint8)                  # 1.0: exponent 15
+    bits[[10, 20, 4000]] = 0x01                              # exponent 0
+    cb = np.array([15] + list(range(1, 15)) + [16], dtype=np.uint8)
+    good = oracle.encode(bits, 1, cb)
+    first = streamfmt.layout(1, n)["off_esc"]
+    for name, mutate in [("exp_range", lambda t: t.__setitem__(first + 2, 32)),
+                         ("pos_order", lambda t: t.__setitem__(slice(first + 3, first + 5), [5, 0])),
+                         ("pos_range", lambda t: t.__setitem__(slice(first + 6, first + 8), [0x88, 0x13]))]:
+        t = good.copy()
+        mutate(t)
+        want = oracle.validate(t, 1, n)
+        _, ws = _decode_gpu(torch.from_numpy(t).cuda(), 1, n, check=False)
+        assert int(ws[:4].cpu().view(torch.int32)[0]) == want == oracle.E_FORMAT, name
