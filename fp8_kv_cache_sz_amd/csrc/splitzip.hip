@@ -9,18 +9,20 @@
 //
 // The work is integer bit manipulation streamed through HBM: there is no
 // contraction, so no MFMA.  Design points for CDNA4:
-//   * every global access of the dense passes is a full-wave coalesced
-//     dword / dwordx2 / dwordx4 access (lane l of a wave touches the l-th
-//     8-element chunk of a 512-element row);
+//   * each wave streams one 4096-element row; every global access of the
+//     dense passes is a full-wave coalesced 4/8/16-byte access, issued with
+//     the non-temporal hint (the data is touched once);
 //   * code tables live in LDS (256-entry exponent->code bytes for encode,
 //     256-entry code-pair->shifted-exponent words for decode);
 //   * byte shuffles use v_perm_b32 / v_alignbyte_b32;
-//   * escape ranks come from a packed 64-lane prefix sum of per-chunk counts;
-//   * encode is dense+stage, a one-workgroup scan of tile counts, then a
-//     compaction of the staged escape records into their final order; decode
-//     is a one-workgroup scan of the block counts, then one workgroup per
-//     64K block: dense decode in registers, patched from an LDS map of the
-//     block's escapes before a single store.
+//   * escape ranks come from a packed 64-lane prefix sum of per-chunk counts
+//     plus a per-workgroup prefix over the waves;
+//   * encode = dense+stage (one 256-lane workgroup per 16K-element tile), a
+//     one-workgroup scan of the tile counts, then a compaction of the staged
+//     escape records into their final order;
+//   * decode = a one-workgroup validating scan of the block counts, then one
+//     1024-lane workgroup per 64K block: dense decode in registers, patched
+//     from an LDS map of the block's escapes before a single store.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -39,13 +41,15 @@ constexpr uint32_t kMagic = 0x50495A53u;    // "SZIP"
 constexpr uint32_t kVersion = 1;
 constexpr uint32_t kLog2Block = 16;
 
-// Encode tiling: one wave per workgroup, 16K elements per tile, processed
-// as 4 rows of 4096 (64 lanes x 8 chunks x 8 elements for BF16).
-constexpr uint32_t kEncTile = 16384;
-constexpr uint32_t kTilesPerBlock = kBlock / kEncTile;   // 4
+// Every dense kernel gives each lane 64 elements of one 4096-element row per
+// wave (BF16: eight 8-element chunks, E5M2: two 32-element chunks).
+constexpr uint32_t kRow = 4096;
+constexpr uint32_t kEncThreads = 256;                     // 4 waves = one 16K tile
+constexpr uint32_t kEncTile = kRow * (kEncThreads / 64);  // 16384
+constexpr uint32_t kTilesPerBlock = kBlock / kEncTile;    // 4
+constexpr uint32_t kDecThreads = 1024;                    // 16 waves = one 64K block
 constexpr uint32_t kScanThreads = 1024;
-constexpr uint32_t kDecThreads = 256;                    // 4 waves per 64K block
-constexpr uint32_t kCompactThreads = 256;
+constexpr uint32_t kCompactThreads = 64 * kTilesPerBlock; // one wave per tile
 
 constexpr uint64_t up256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 
@@ -80,7 +84,7 @@ WsLayout ws_layout(int dtype, uint64_t n)
     WsLayout w;
     w.counts = 256;
     w.offsets = w.counts + up256(4 * g.nt + 16);
-    uint64_t offsets_bytes = std::max<uint64_t>(8 * g.nt, 8 * g.nb);
+    const uint64_t offsets_bytes = std::max<uint64_t>(8 * g.nt, 8 * g.nb);
     w.stage = w.offsets + up256(offsets_bytes + 16);
     w.total = w.stage + up256(3 * g.nt * kEncTile + 16);
     return w;
@@ -89,6 +93,32 @@ WsLayout ws_layout(int dtype, uint64_t n)
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_nt(const uint4 *p)
+{
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_nt(const uint2 *p)
+{
+    const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u *>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t load_nt(const uint32_t *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_nt(uint4 *p, uint4 v)
+{
+    v4u w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<v4u *>(p));
+}
+__device__ __forceinline__ void store_nt(uint2 *p, uint2 v)
+{
+    v2u w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<v2u *>(p));
+}
+__device__ __forceinline__ void store_nt(uint32_t *p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 {
     // v_perm_b32: byte i of the result = byte sel[i] of {hi, lo} (lo = bytes 0..3)
@@ -97,22 +127,22 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: four row_shr
+// steps scan each 16-lane row, then row_bcast:15 and row_bcast:31 carry the
+// row totals forward (lanes of disabled rows add the 0 `old` operand).
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x)
 {
-    const uint32_t lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t y = __shfl_up(x, d, 64);
-        if (lane >= (uint32_t)d) x += y;
-    }
-    return x;
+    uint32_t v = x;
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return v;
 }
 
-__device__ __forceinline__ uint32_t read_lane63(uint32_t x)
-{
-    return __builtin_amdgcn_readlane(x, 63);
-}
+__device__ __forceinline__ uint32_t read_lane63(uint32_t x) { return __builtin_amdgcn_readlane(x, 63); }
 
 __device__ __forceinline__ uint32_t popc64(uint64_t x) { return __popcll(x); }
 
@@ -127,33 +157,53 @@ __device__ __forceinline__ uint32_t cb_entry(const Codebook4 &cb, uint32_t c)
 }
 
 // Exponent -> code table for encode.  Byte v = code of exponent v, or 0x80
-// (code 0 with the escape flag) when v is not in the codebook.  64 lanes
-// fill 4 entries each.
+// (code 0 with the escape flag) when v is not in the codebook.  Threads
+// 0..63 fill 4 entries each.
 __device__ __forceinline__ void build_encode_table(uint32_t *table32, const Codebook4 &cb,
                                                    uint32_t symbols)
 {
-    const uint32_t lane = threadIdx.x;
-    if (lane * 4 < symbols) {
+    const uint32_t t = threadIdx.x;
+    if (t < 64 && t * 4 < symbols) {
         uint32_t word = 0;
 #pragma unroll
         for (uint32_t k = 0; k < 4; ++k) {
-            uint32_t v = lane * 4 + k;
+            const uint32_t v = t * 4 + k;
             uint32_t code = 0x80u;
 #pragma unroll
             for (uint32_t c = 0; c < 16; ++c)
                 if (cb_entry(cb, c) == v) code = c;
             word |= code << (8 * k);
         }
-        table32[lane] = word;
+        table32[t] = word;
     }
 }
 
+// Looks up four exponent bytes in the encode table.
+__device__ __forceinline__ uint32_t lookup4(const uint8_t *table, uint32_t e4)
+{
+    return (uint32_t)table[e4 & 0xFFu] | ((uint32_t)table[(e4 >> 8) & 0xFFu] << 8) |
+           ((uint32_t)table[(e4 >> 16) & 0xFFu] << 16) | ((uint32_t)table[e4 >> 24] << 24);
+}
+
+// Code bytes of 8 elements (two words of table output) -> one word of nibbles
+// (element 2k in the low nibble).  Byte 0 of (k | k >> 4) = code0 | code1 << 4.
+__device__ __forceinline__ uint32_t pack_codes8(uint32_t c_a, uint32_t c_b)
+{
+    const uint32_t k_a = c_a & 0x0F0F0F0Fu;
+    const uint32_t k_b = c_b & 0x0F0F0F0Fu;
+    return perm(k_b | (k_b >> 4), k_a | (k_a >> 4), 0x06040200u);
+}
+
+// Escape flags of 8 elements: element k at bit 8k+7.
+__device__ __forceinline__ uint64_t escape_flags8(uint32_t c_a, uint32_t c_b)
+{
+    return (uint64_t)(c_a & 0x80808080u) | ((uint64_t)(c_b & 0x80808080u) << 32);
+}
+
 // ---------------------------------------------------------------------------
-// BF16 encode, one 8-element chunk (16 bytes in).
-//   nib: 4 bytes of codes (element 2k low nibble)
-//   sm : 8 sign/mantissa bytes (sign << 7 | mantissa7)
-//   esc: escape flag of element k at bit 8k+7
-//   ex : exponent of element k in byte k
+// BF16 encode of one 8-element chunk (16 bytes in).
+//   nib: 4 bytes of codes;  sm: 8 sign/mantissa bytes (sign << 7 | mantissa7)
+//   esc: escape flags (bit 8k+7);  ex: exponent of element k in byte k
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void encode_chunk_bf16(const uint4 q, const uint8_t *table, uint32_t &nib,
                                                   uint2 &sm, uint64_t &esc, uint64_t &ex)
@@ -166,141 +216,17 @@ __device__ __forceinline__ void encode_chunk_bf16(const uint4 q, const uint8_t *
     sm.y = (hi_b & 0x80808080u) | (lo_b & 0x7F7F7F7Fu);
     const uint32_t e_a = ((hi_a << 1) & 0xFEFEFEFEu) | ((lo_a >> 7) & 0x01010101u);
     const uint32_t e_b = ((hi_b << 1) & 0xFEFEFEFEu) | ((lo_b >> 7) & 0x01010101u);
-    const uint32_t c_a = (uint32_t)table[e_a & 0xFFu] | ((uint32_t)table[(e_a >> 8) & 0xFFu] << 8) |
-                         ((uint32_t)table[(e_a >> 16) & 0xFFu] << 16) |
-                         ((uint32_t)table[e_a >> 24] << 24);
-    const uint32_t c_b = (uint32_t)table[e_b & 0xFFu] | ((uint32_t)table[(e_b >> 8) & 0xFFu] << 8) |
-                         ((uint32_t)table[(e_b >> 16) & 0xFFu] << 16) |
-                         ((uint32_t)table[e_b >> 24] << 24);
-    const uint32_t k_a = c_a & 0x0F0F0F0Fu;
-    const uint32_t k_b = c_b & 0x0F0F0F0Fu;
-    // byte 0 of (k | k >> 4) = code0 | code1 << 4, byte 2 = code2 | code3 << 4
-    nib = perm(k_b | (k_b >> 4), k_a | (k_a >> 4), 0x06040200u);
-    esc = (uint64_t)(c_a & 0x80808080u) | ((uint64_t)(c_b & 0x80808080u) << 32);
+    const uint32_t c_a = lookup4(table, e_a);
+    const uint32_t c_b = lookup4(table, e_b);
+    nib = pack_codes8(c_a, c_b);
+    esc = escape_flags8(c_a, c_b);
     ex = (uint64_t)e_a | ((uint64_t)e_b << 32);
 }
 
-// Write the escape records of one chunk into the tile's staging area, in
-// ascending element order starting at rank `rank`.
-__device__ __forceinline__ void stage_records(uint8_t *tstage, uint32_t rank, uint64_t esc,
-                                              uint64_t ex, uint32_t pos0, uint32_t shift_per_elem)
-{
-    while (esc) {
-        const uint32_t bit = (uint32_t)__builtin_ctzll(esc);
-        esc &= esc - 1;
-        const uint32_t k = bit / shift_per_elem;
-        const uint32_t pos = (pos0 + k) & 0xFFFFu;
-        const uint32_t e = (uint32_t)(ex >> (8 * k)) & 0xFFu;
-        uint8_t *r = tstage + 3ull * rank;
-        r[0] = (uint8_t)pos;
-        r[1] = (uint8_t)(pos >> 8);
-        r[2] = (uint8_t)e;
-        ++rank;
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Kernel: BF16 dense encode + escape staging.  One wave per 16K-element tile.
-// ---------------------------------------------------------------------------
-constexpr uint32_t kBf16Chunks = 8;                        // chunks per lane per row
-constexpr uint32_t kBf16Row = 64 * 8 * kBf16Chunks;        // 4096 elements
-
-__global__ __launch_bounds__(64) void sz_enc_dense_bf16(const uint16_t *__restrict__ in, uint64_t n,
-                                                        uint8_t *__restrict__ out, uint64_t off_nib,
-                                                        uint64_t off_sm, Codebook4 cb,
-                                                        uint32_t *__restrict__ tile_counts,
-                                                        uint8_t *__restrict__ stage)
-{
-    __shared__ uint32_t table32[64];
-    build_encode_table(table32, cb, 256);
-    __syncthreads();
-    const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
-
-    const uint32_t lane = lane_id();
-    const uint64_t tile = blockIdx.x;
-    const uint64_t t0 = tile * kEncTile;
-    const bool full_tile = t0 + kEncTile <= n;
-    uint8_t *tstage = stage + tile * (3ull * kEncTile);
-    uint32_t tile_escapes = 0;
-
-    for (uint32_t row = 0; row < kEncTile / kBf16Row; ++row) {
-        const uint64_t base = t0 + (uint64_t)row * kBf16Row;
-        if (base >= n) break;
-        uint4 q[kBf16Chunks];
-#pragma unroll
-        for (uint32_t j = 0; j < kBf16Chunks; ++j) {
-            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
-            if (full_tile || c0 + 8 <= n) {
-                q[j] = *reinterpret_cast<const uint4 *>(in + c0);
-            } else {
-                uint16_t v[8];
-#pragma unroll
-                for (uint32_t k = 0; k < 8; ++k) v[k] = (c0 + k < n) ? in[c0 + k] : 0;
-                q[j] = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
-                                  v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
-            }
-        }
-        uint64_t esc[kBf16Chunks], ex[kBf16Chunks];
-        uint32_t cnt[kBf16Chunks];
-#pragma unroll
-        for (uint32_t j = 0; j < kBf16Chunks; ++j) {
-            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
-            uint32_t nib;
-            uint2 sm;
-            encode_chunk_bf16(q[j], table, nib, sm, esc[j], ex[j]);
-            if (full_tile || c0 + 8 <= n) {
-                *reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2) = nib;
-                *reinterpret_cast<uint2 *>(out + off_sm + c0) = sm;
-            } else if (c0 < n) {
-                // last, partial chunk: missing elements get code 0, sign/mantissa 0
-                // and no escape; the bytes past the data are section padding
-                const uint32_t valid = (uint32_t)(n - c0);
-                const uint64_t keep = (valid >= 8) ? ~0ull : ((1ull << (8 * valid)) - 1);
-                esc[j] &= keep;
-                nib &= (uint32_t)((1ull << (4 * valid)) - 1);
-                uint64_t smv = ((uint64_t)sm.y << 32 | sm.x) & keep;
-                *reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2) = nib;
-                *reinterpret_cast<uint2 *>(out + off_sm + c0) =
-                    make_uint2((uint32_t)smv, (uint32_t)(smv >> 32));
-            } else {
-                esc[j] = 0;
-            }
-            cnt[j] = popc64(esc[j]);
-        }
-        // escape ranks: packed 16-bit per-chunk counts, prefix-summed over lanes
-        uint32_t any = 0;
-#pragma unroll
-        for (uint32_t j = 0; j < kBf16Chunks; ++j) any |= cnt[j];
-        if (__ballot(any != 0) == 0) continue;
-        uint32_t packed[kBf16Chunks / 2], incl[kBf16Chunks / 2];
-#pragma unroll
-        for (uint32_t p = 0; p < kBf16Chunks / 2; ++p) {
-            packed[p] = cnt[2 * p] | (cnt[2 * p + 1] << 16);
-            incl[p] = wave_inclusive_sum(packed[p]);
-        }
-        uint32_t running = tile_escapes;
-#pragma unroll
-        for (uint32_t j = 0; j < kBf16Chunks; ++j) {
-            const uint32_t sh = 16 * (j & 1);
-            const uint32_t total = (read_lane63(incl[j / 2]) >> sh) & 0xFFFFu;
-            const uint32_t before = ((incl[j / 2] - packed[j / 2]) >> sh) & 0xFFFFu;
-            if (esc[j]) {
-                const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
-                stage_records(tstage, running + before, esc[j], ex[j], (uint32_t)(c0 & 0xFFFFu), 8);
-            }
-            running += total;
-        }
-        tile_escapes = running;
-    }
-    if (lane == 0) tile_counts[tile] = tile_escapes;
-}
-
-// ---------------------------------------------------------------------------
-// FP8 E5M2 encode (the page's FP8 extension, Contributions item 4).
-// One 32-element chunk per lane: 32 bytes in, 16 code bytes (uint4) and
-// 12 sign/mantissa bytes (four 24-bit groups of eight 3-bit symbols) out.
-//   esc[s], ex[s]: escape flags (bit 8k+7) and exponents (byte k) of the
-//   eight elements 8s..8s+7.
+// FP8 E5M2 encode of one 32-element chunk (32 bytes in): 16 code bytes and
+// 12 sign/mantissa bytes (four 24-bit groups of eight 3-bit symbols).
+//   esc[s], ex[s]: escape flags and exponents of elements 8s..8s+7.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack_sm3_x4(uint32_t sym)
 {
@@ -321,16 +247,10 @@ __device__ __forceinline__ void encode_chunk_e5m2(const uint4 q0, const uint4 q1
         const uint32_t e_b = (b >> 2) & 0x1F1F1F1Fu;
         const uint32_t s_a = ((a >> 5) & 0x04040404u) | (a & 0x03030303u);
         const uint32_t s_b = ((b >> 5) & 0x04040404u) | (b & 0x03030303u);
-        const uint32_t c_a = (uint32_t)table[e_a & 0xFFu] | ((uint32_t)table[(e_a >> 8) & 0xFFu] << 8) |
-                             ((uint32_t)table[(e_a >> 16) & 0xFFu] << 16) |
-                             ((uint32_t)table[e_a >> 24] << 24);
-        const uint32_t c_b = (uint32_t)table[e_b & 0xFFu] | ((uint32_t)table[(e_b >> 8) & 0xFFu] << 8) |
-                             ((uint32_t)table[(e_b >> 16) & 0xFFu] << 16) |
-                             ((uint32_t)table[e_b >> 24] << 24);
-        const uint32_t k_a = c_a & 0x0F0F0F0Fu;
-        const uint32_t k_b = c_b & 0x0F0F0F0Fu;
-        nibw[s] = perm(k_b | (k_b >> 4), k_a | (k_a >> 4), 0x06040200u);
-        esc[s] = (uint64_t)(c_a & 0x80808080u) | ((uint64_t)(c_b & 0x80808080u) << 32);
+        const uint32_t c_a = lookup4(table, e_a);
+        const uint32_t c_b = lookup4(table, e_b);
+        nibw[s] = pack_codes8(c_a, c_b);
+        esc[s] = escape_flags8(c_a, c_b);
         ex[s] = (uint64_t)e_a | ((uint64_t)e_b << 32);
         grp[s] = pack_sm3_x4(s_a) | (pack_sm3_x4(s_b) << 12);
     }
@@ -340,139 +260,315 @@ __device__ __forceinline__ void encode_chunk_e5m2(const uint4 q0, const uint4 q1
     sm3[2] = (grp[2] >> 16) | (grp[3] << 8);
 }
 
-constexpr uint32_t kE5Chunks = 2;                          // 32-element chunks per lane per row
-constexpr uint32_t kE5Row = 64 * 32 * kE5Chunks;           // 4096 elements
+// Writes the escape records of 8 elements (flags esc, exponents ex, first
+// block-local position pos0) into the tile's staging area, ascending, from
+// rank `rank` on.
+__device__ __forceinline__ void stage_records(uint8_t *tstage, uint32_t rank, uint64_t esc, uint64_t ex,
+                                              uint32_t pos0)
+{
+    while (esc) {
+        const uint32_t bit = (uint32_t)__builtin_ctzll(esc);
+        esc &= esc - 1;
+        const uint32_t k = bit >> 3;
+        const uint32_t pos = (pos0 + k) & 0xFFFFu;
+        const uint32_t e = (uint32_t)(ex >> (8 * k)) & 0xFFu;
+        uint8_t *r = tstage + 3ull * rank;
+        r[0] = (uint8_t)pos;
+        r[1] = (uint8_t)(pos >> 8);
+        r[2] = (uint8_t)e;
+        ++rank;
+    }
+}
 
-__global__ __launch_bounds__(64) void sz_enc_dense_e5m2(const uint8_t *__restrict__ in, uint64_t n,
-                                                        uint8_t *__restrict__ out, uint64_t off_nib,
-                                                        uint64_t off_sm, uint64_t sm_bytes, Codebook4 cb,
-                                                        uint32_t *__restrict__ tile_counts,
-                                                        uint8_t *__restrict__ stage)
+// Escape bookkeeping shared by both encoders.  Each lane holds J chunks of G
+// eight-element groups (BF16 J=8, G=1; E5M2 J=2, G=4); the rank order inside
+// a wave row is (chunk, lane, group, element).  Returns the wave's escape
+// total; `before[j]` = escapes of this wave before chunk j of this lane.
+template <int J>
+__device__ __forceinline__ uint32_t wave_chunk_ranks(const uint32_t (&cnt)[J], uint32_t (&before)[J])
+{
+    static_assert(J % 2 == 0, "chunk counts are scanned in pairs");
+    uint32_t running = 0;
+#pragma unroll
+    for (int p = 0; p < J / 2; ++p) {
+        const uint32_t packed = cnt[2 * p] | (cnt[2 * p + 1] << 16);
+        const uint32_t incl = wave_inclusive_sum(packed);
+        const uint32_t excl = incl - packed;
+        const uint32_t tot = read_lane63(incl);
+        before[2 * p] = running + (excl & 0xFFFFu);
+        running += tot & 0xFFFFu;
+        before[2 * p + 1] = running + (excl >> 16);
+        running += tot >> 16;
+    }
+    return running;
+}
+
+// Sums the per-wave escape totals of a workgroup through LDS.  Returns the
+// escapes of the waves before this one; `total` gets the workgroup's.
+template <int WAVES>
+__device__ __forceinline__ uint32_t workgroup_wave_prefix(uint32_t wave_total, uint32_t *lds,
+                                                          uint32_t &total)
+{
+    const uint32_t wave = threadIdx.x / 64;
+    if (lane_id() == 0) lds[wave] = wave_total;
+    __syncthreads();
+    uint32_t before = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+        const uint32_t v = lds[w];
+        if ((uint32_t)w < wave) before += v;
+        sum += v;
+    }
+    total = sum;
+    return before;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: BF16 dense encode + escape staging.  One 256-lane workgroup per
+// 16K-element tile; wave w streams elements [4096w, 4096w + 4096) of it.
+// ---------------------------------------------------------------------------
+constexpr int kBf16Chunks = 8;
+
+__global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t *__restrict__ in, uint64_t n,
+                                                                 uint8_t *__restrict__ out, uint64_t off_nib,
+                                                                 uint64_t off_sm, Codebook4 cb,
+                                                                 uint32_t *__restrict__ tile_counts,
+                                                                 uint8_t *__restrict__ stage)
 {
     __shared__ uint32_t table32[64];
+    __shared__ uint32_t wave_totals[kEncThreads / 64];
+    const uint32_t lane = lane_id();
+    const uint32_t wave = threadIdx.x / 64;
+    const uint64_t tile = blockIdx.x;
+    const uint64_t base = tile * kEncTile + (uint64_t)wave * kRow;
+    const bool full_row = base + kRow <= n;
+
+    // the row's loads are issued first and stay in flight while the table is built
+    uint4 q[kBf16Chunks];
+#pragma unroll
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+        if (full_row || c0 + 8 <= n) {
+            q[j] = load_nt(reinterpret_cast<const uint4 *>(in + c0));
+        } else {
+            uint16_t v[8];
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) v[k] = (c0 + k < n) ? in[c0 + k] : 0;
+            q[j] = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                              v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
+        }
+    }
+    build_encode_table(table32, cb, 256);
+    __syncthreads();
+    const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
+    uint64_t esc[kBf16Chunks], ex[kBf16Chunks];
+    uint32_t cnt[kBf16Chunks];
+#pragma unroll
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+        uint32_t nib;
+        uint2 sm;
+        encode_chunk_bf16(q[j], table, nib, sm, esc[j], ex[j]);
+        if (full_row || c0 + 8 <= n) {
+            store_nt(reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2), nib);
+            store_nt(reinterpret_cast<uint2 *>(out + off_sm + c0), sm);
+        } else if (c0 < n) {
+            // last, partial chunk: missing elements get code 0, sign/mantissa 0
+            // and no escape; the bytes past the data are section padding
+            const uint32_t valid = (uint32_t)(n - c0);
+            const uint64_t keep = (1ull << (8 * valid)) - 1;
+            esc[j] &= keep;
+            nib &= (uint32_t)((1ull << (4 * valid)) - 1);
+            const uint64_t smv = ((uint64_t)sm.y << 32 | sm.x) & keep;
+            *reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2) = nib;
+            *reinterpret_cast<uint2 *>(out + off_sm + c0) = make_uint2((uint32_t)smv, (uint32_t)(smv >> 32));
+        } else {
+            esc[j] = 0;
+        }
+        cnt[j] = popc64(esc[j]);
+    }
+    uint32_t before[kBf16Chunks];
+    const uint32_t wave_total = wave_chunk_ranks<kBf16Chunks>(cnt, before);
+    uint32_t tile_total;
+    const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
+    if (wave_total) {
+        uint8_t *tstage = stage + tile * (3ull * kEncTile);
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            if (esc[j]) {
+                const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+                stage_records(tstage, wave_before + before[j], esc[j], ex[j], (uint32_t)(c0 & 0xFFFFu));
+            }
+        }
+    }
+    if (threadIdx.x == 0) tile_counts[tile] = tile_total;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: FP8 E5M2 dense encode + escape staging (the page's FP8 extension,
+// Contributions item 4).  Same tiling as BF16; a lane holds two 32-element
+// chunks of its wave's row.
+// ---------------------------------------------------------------------------
+constexpr int kE5Chunks = 2;
+
+__global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *__restrict__ in, uint64_t n,
+                                                                 uint8_t *__restrict__ out, uint64_t off_nib,
+                                                                 uint64_t off_sm, uint64_t sm_bytes,
+                                                                 Codebook4 cb,
+                                                                 uint32_t *__restrict__ tile_counts,
+                                                                 uint8_t *__restrict__ stage)
+{
+    __shared__ uint32_t table32[64];
+    __shared__ uint32_t wave_totals[kEncThreads / 64];
+    const uint32_t lane = lane_id();
+    const uint32_t wave = threadIdx.x / 64;
+    const uint64_t tile = blockIdx.x;
+    const uint64_t base = tile * kEncTile + (uint64_t)wave * kRow;
+    const bool full_row = base + kRow <= n;
+
+    uint4 q[kE5Chunks][2];
+#pragma unroll
+    for (int j = 0; j < kE5Chunks; ++j) {
+        const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+        if (full_row || c0 + 32 <= n) {
+            q[j][0] = load_nt(reinterpret_cast<const uint4 *>(in + c0));
+            q[j][1] = load_nt(reinterpret_cast<const uint4 *>(in + c0 + 16));
+        } else {
+            uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (uint32_t k = 0; k < 32 && c0 + k < n; ++k) w[k / 4] |= (uint32_t)in[c0 + k] << (8 * (k & 3));
+            q[j][0] = make_uint4(w[0], w[1], w[2], w[3]);
+            q[j][1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+    }
     build_encode_table(table32, cb, 32);
     __syncthreads();
     const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
-
-    const uint32_t lane = lane_id();
-    const uint64_t tile = blockIdx.x;
-    const uint64_t t0 = tile * kEncTile;
-    const bool full_tile = t0 + kEncTile <= n;
-    uint8_t *tstage = stage + tile * (3ull * kEncTile);
-    uint32_t tile_escapes = 0;
-
-    for (uint32_t row = 0; row < kEncTile / kE5Row; ++row) {
-        const uint64_t base = t0 + (uint64_t)row * kE5Row;
-        if (base >= n) break;
-        uint4 q[kE5Chunks][2];
+    uint64_t esc[kE5Chunks][4], ex[kE5Chunks][4];
+    uint32_t cnt[kE5Chunks];
 #pragma unroll
-        for (uint32_t j = 0; j < kE5Chunks; ++j) {
-            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
-            if (full_tile || c0 + 32 <= n) {
-                q[j][0] = *reinterpret_cast<const uint4 *>(in + c0);
-                q[j][1] = *reinterpret_cast<const uint4 *>(in + c0 + 16);
-            } else {
-                uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                for (uint32_t k = 0; c0 + k < n && k < 32; ++k) w[k / 4] |= (uint32_t)in[c0 + k] << (8 * (k & 3));
-                q[j][0] = make_uint4(w[0], w[1], w[2], w[3]);
-                q[j][1] = make_uint4(w[4], w[5], w[6], w[7]);
+    for (int j = 0; j < kE5Chunks; ++j) {
+        const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+        uint4 nib;
+        uint32_t sm3[3];
+        encode_chunk_e5m2(q[j][0], q[j][1], table, nib, sm3, esc[j], ex[j]);
+        uint32_t *sm_dst = reinterpret_cast<uint32_t *>(out + off_sm + (c0 / 32) * 12);
+        if (full_row || c0 + 32 <= n) {
+            store_nt(reinterpret_cast<uint4 *>(out + off_nib + c0 / 2), nib);
+            store_nt(sm_dst, sm3[0]);
+            store_nt(sm_dst + 1, sm3[1]);
+            store_nt(sm_dst + 2, sm3[2]);
+        } else if (c0 < n) {
+            // last, partial chunk: missing elements get code 0, symbol 0 and
+            // no escape; only the sign/mantissa bytes that hold data are stored
+            const uint32_t valid = (uint32_t)(n - c0);
+            uint32_t nw[4] = {nib.x, nib.y, nib.z, nib.w};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int v = (int)valid - 8 * s;
+                esc[j][s] &= v >= 8 ? ~0ull : (v <= 0 ? 0ull : ((1ull << (8 * v)) - 1));
+                nw[s] &= v >= 8 ? 0xFFFFFFFFu : (v <= 0 ? 0u : (uint32_t)((1ull << (4 * v)) - 1));
             }
-        }
-        uint64_t esc[kE5Chunks][4], ex[kE5Chunks][4];
-        uint32_t cnt[kE5Chunks];
+            *reinterpret_cast<uint4 *>(out + off_nib + c0 / 2) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+            uint32_t sw[3] = {sm3[0], sm3[1], sm3[2]};
+            const uint32_t bits = 3 * valid;
 #pragma unroll
-        for (uint32_t j = 0; j < kE5Chunks; ++j) {
-            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
-            uint4 nib;
-            uint32_t sm3[3];
-            encode_chunk_e5m2(q[j][0], q[j][1], table, nib, sm3, esc[j], ex[j]);
-            uint8_t *sm_dst = out + off_sm + (c0 / 32) * 12;
-            if (full_tile || c0 + 32 <= n) {
-                *reinterpret_cast<uint4 *>(out + off_nib + c0 / 2) = nib;
-                *reinterpret_cast<uint3 *>(sm_dst) = make_uint3(sm3[0], sm3[1], sm3[2]);
-            } else if (c0 < n) {
-                // last, partial chunk: missing elements get code 0, symbol 0 and
-                // no escape; only the groups that hold data are stored
-                const uint32_t valid = (uint32_t)(n - c0);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int v = (int)valid - 8 * s;
-                    const uint64_t keep = v >= 8 ? ~0ull : (v <= 0 ? 0ull : ((1ull << (8 * v)) - 1));
-                    esc[j][s] &= keep;
-                }
-                uint32_t nw[4] = {nib.x, nib.y, nib.z, nib.w};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int v = (int)valid - 8 * s;
-                    nw[s] &= v >= 8 ? 0xFFFFFFFFu : (v <= 0 ? 0u : (uint32_t)((1ull << (4 * v)) - 1));
-                }
-                *reinterpret_cast<uint4 *>(out + off_nib + c0 / 2) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
-                // sign/mantissa: 3 bits per element, so the first 3 * valid bits
-                uint32_t sw[3] = {sm3[0], sm3[1], sm3[2]};
-                const uint32_t bits = 3 * valid;
-#pragma unroll
-                for (int w = 0; w < 3; ++w) {
-                    const int b = (int)bits - 32 * w;
-                    sw[w] &= b >= 32 ? 0xFFFFFFFFu : (b <= 0 ? 0u : ((1u << b) - 1));
-                }
-                const uint64_t sm_start = off_sm + (c0 / 32) * 12;
-                const uint64_t sm_end = off_sm + sm_bytes;
-                for (uint32_t i = 0; i < 12 && sm_start + i < sm_end; ++i)
-                    out[sm_start + i] = (uint8_t)(sw[i / 4] >> (8 * (i & 3)));
-            } else {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) esc[j][s] = 0;
+            for (int w = 0; w < 3; ++w) {
+                const int b = (int)bits - 32 * w;
+                sw[w] &= b >= 32 ? 0xFFFFFFFFu : (b <= 0 ? 0u : ((1u << b) - 1));
             }
-            cnt[j] = popc64(esc[j][0]) + popc64(esc[j][1]) + popc64(esc[j][2]) + popc64(esc[j][3]);
-        }
-        if (__ballot((cnt[0] | cnt[1]) != 0) == 0) continue;
-        const uint32_t packed = cnt[0] | (cnt[1] << 16);
-        const uint32_t incl = wave_inclusive_sum(packed);
-        const uint32_t tot = read_lane63(incl);
-        const uint32_t excl = incl - packed;
-        uint32_t running = tile_escapes;
+            const uint64_t sm_start = off_sm + (c0 / 32) * 12;
+            const uint64_t sm_end = off_sm + sm_bytes;
+            for (uint32_t i = 0; i < 12 && sm_start + i < sm_end; ++i)
+                out[sm_start + i] = (uint8_t)(sw[i / 4] >> (8 * (i & 3)));
+        } else {
 #pragma unroll
-        for (uint32_t j = 0; j < kE5Chunks; ++j) {
-            uint32_t rank = running + ((excl >> (16 * j)) & 0xFFFFu);
+            for (int s = 0; s < 4; ++s) esc[j][s] = 0;
+        }
+        cnt[j] = popc64(esc[j][0]) + popc64(esc[j][1]) + popc64(esc[j][2]) + popc64(esc[j][3]);
+    }
+    uint32_t before[kE5Chunks];
+    const uint32_t wave_total = wave_chunk_ranks<kE5Chunks>(cnt, before);
+    uint32_t tile_total;
+    const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
+    if (wave_total) {
+        uint8_t *tstage = stage + tile * (3ull * kEncTile);
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            uint32_t rank = wave_before + before[j];
             const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 if (esc[j][s]) {
-                    stage_records(tstage, rank, esc[j][s], ex[j][s], (uint32_t)((c0 + 8 * s) & 0xFFFFu), 8);
+                    stage_records(tstage, rank, esc[j][s], ex[j][s], (uint32_t)((c0 + 8 * s) & 0xFFFFu));
                     rank += popc64(esc[j][s]);
                 }
             }
-            running += (tot >> (16 * j)) & 0xFFFFu;
         }
-        tile_escapes = running;
     }
-    if (lane == 0) tile_counts[tile] = tile_escapes;
+    if (threadIdx.x == 0) tile_counts[tile] = tile_total;
 }
 
 // ---------------------------------------------------------------------------
-// Block-level exclusive scan helper for the one-workgroup scan kernels.
-// Returns the exclusive prefix of x inside the workgroup and the total.
+// One-workgroup scans.  Both scan kernels read their counts with coalesced
+// dwordx4 loads: in pass i, thread t holds item i * 1024 + t, where an item
+// is four consecutive counts (four tiles = one block for encode, four blocks
+// for decode).  Up to kScanBatch passes are loaded at once; each pass gets
+// its own 64-lane prefix sums, the 16 waves' totals meet in LDS, and one
+// thread per pass turns them into exclusive offsets.  A running 64-bit carry
+// joins successive batches.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t workgroup_exclusive_sum(uint32_t x, uint32_t *wave_sums,
-                                                            uint32_t &total)
+constexpr int kScanBatch = 8;
+constexpr uint32_t kScanWaves = kScanThreads / 64;
+
+struct ScanLds {
+    uint32_t wave_incl[kScanBatch][kScanWaves];   // per pass: inclusive wave totals -> exclusive prefixes
+    uint32_t pass_total[kScanBatch];
+    uint64_t pass_base[kScanBatch];                // per pass: offset of its first item
+    uint64_t carry;
+};
+
+// x[i] = item value of pass i for this thread (0 for missing items); on
+// return base[i] = exclusive prefix of this thread's item in pass i.
+// lds.carry holds the running total before the batch and is advanced.
+__device__ __forceinline__ void scan_batch(const uint32_t (&x)[kScanBatch], uint64_t (&base)[kScanBatch],
+                                           ScanLds &lds)
 {
+    static_assert(kScanBatch * kScanWaves <= kScanThreads && kScanWaves == 16, "one lane per (pass, wave)");
+    const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
-    const uint32_t wave = threadIdx.x / 64;
-    const uint32_t nwaves = blockDim.x / 64;
-    const uint32_t incl = wave_inclusive_sum(x);
-    if (lane == 63) wave_sums[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-        uint32_t v = lane < nwaves ? wave_sums[lane] : 0;
-        uint32_t vi = wave_inclusive_sum(v);
-        if (lane < nwaves) wave_sums[lane] = vi - v;     // exclusive wave prefix
-        if (lane == 63) wave_sums[32] = vi;              // workgroup total
+    const uint32_t wave = tid / 64;
+    uint32_t incl[kScanBatch];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) {
+        incl[i] = wave_inclusive_sum(x[i]);
+        if (lane == 63) lds.wave_incl[i][wave] = incl[i];
     }
     __syncthreads();
-    const uint32_t result = wave_sums[wave] + incl - x;
-    total = wave_sums[32];
+    // lane (pass i, wave w) for tid < 128: exclusive scan of the 16 wave
+    // totals of pass i inside a 16-lane segment
+    if (tid < kScanBatch * kScanWaves) {
+        const uint32_t i = tid / kScanWaves, w = tid % kScanWaves;
+        const uint32_t v0 = lds.wave_incl[i][w];
+        uint32_t v = v0;
+#pragma unroll
+        for (int d = 1; d < (int)kScanWaves; d <<= 1) {
+            const uint32_t y = __shfl_up(v, d, kScanWaves);
+            if (w >= (uint32_t)d) v += y;
+        }
+        lds.wave_incl[i][w] = v - v0;
+        if (w == kScanWaves - 1) lds.pass_total[i] = v;
+    }
     __syncthreads();
-    return result;
+    if (tid < kScanBatch) {
+        uint64_t b = lds.carry;
+        for (uint32_t i = 0; i < tid; ++i) b += lds.pass_total[i];
+        lds.pass_base[tid] = b;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) base[i] = lds.pass_base[i] + lds.wave_incl[i][wave] + (incl[i] - x[i]);
+    if (tid == 0) lds.carry = lds.pass_base[kScanBatch - 1] + lds.pass_total[kScanBatch - 1];
+    __syncthreads();    // the next batch reuses the LDS
 }
 
 struct HeaderArgs {
@@ -483,44 +579,45 @@ struct HeaderArgs {
 };
 
 // ---------------------------------------------------------------------------
-// Kernel: encode scan.  One workgroup: per-block escape counts from the tile
-// counts, exclusive tile offsets, header and padding.
+// Kernel: encode scan.  One workgroup turns the tile escape counts into the
+// per-block escape counts of the stream and the exclusive escape offset of
+// every block, then writes the header (with E) and the zero padding between
+// sections.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__restrict__ tile_counts,
-                                                            uint64_t nt,
-                                                            uint64_t *__restrict__ tile_offsets,
+                                                            uint32_t nt,
+                                                            uint64_t *__restrict__ block_offsets,
                                                             uint8_t *__restrict__ out, HeaderArgs h)
 {
-    __shared__ uint32_t wave_sums[33];
+    __shared__ ScanLds lds;
     const uint32_t tid = threadIdx.x;
+    const uint32_t nb = (uint32_t)h.nb;
+    if (tid == 0) lds.carry = 0;
     uint32_t *block_counts = reinterpret_cast<uint32_t *>(out + 64);
-    uint64_t carry = 0;
-    for (uint64_t b0 = 0; b0 < h.nb; b0 += kScanThreads) {
-        const uint64_t b = b0 + tid;
-        uint32_t c[kTilesPerBlock] = {0, 0, 0, 0};
-        if (b < h.nb) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b);
-            const uint64_t t = kTilesPerBlock * b;
-            c[0] = v.x;
-            c[1] = (t + 1 < nt) ? v.y : 0;
-            c[2] = (t + 2 < nt) ? v.z : 0;
-            c[3] = (t + 3 < nt) ? v.w : 0;
-        }
-        const uint32_t blk = c[0] + c[1] + c[2] + c[3];
-        uint32_t total;
-        const uint32_t excl = workgroup_exclusive_sum(blk, wave_sums, total);
-        if (b < h.nb) {
-            block_counts[b] = blk;
-            uint64_t off = carry + excl;
-            const uint64_t t = kTilesPerBlock * b;
+    for (uint32_t b0 = 0; b0 < nb; b0 += kScanBatch * kScanThreads) {
+        uint32_t x[kScanBatch];
 #pragma unroll
-            for (uint32_t k = 0; k < kTilesPerBlock; ++k) {
-                if (t + k < nt) tile_offsets[t + k] = off;
-                off += c[k];
+        for (int i = 0; i < kScanBatch; ++i) {
+            const uint32_t b = b0 + i * kScanThreads + tid;
+            x[i] = 0;
+            if (b < nb) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b);
+                const uint32_t t = kTilesPerBlock * b;
+                x[i] = v.x + ((t + 1 < nt) ? v.y : 0) + ((t + 2 < nt) ? v.z : 0) + ((t + 3 < nt) ? v.w : 0);
             }
         }
-        carry += total;
+        uint64_t base[kScanBatch];
+        scan_batch(x, base, lds);
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+            const uint32_t b = b0 + i * kScanThreads + tid;
+            if (b < nb) {
+                block_counts[b] = x[i];
+                block_offsets[b] = base[i];
+            }
+        }
     }
+    const uint64_t total = lds.carry;
     // header: 16 little-endian words
     if (tid < 16) {
         uint32_t w = 0;
@@ -529,8 +626,8 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
         case 1: w = kVersion | (h.dtype << 16) | (kLog2Block << 24); break;
         case 2: w = (uint32_t)h.n; break;
         case 3: w = (uint32_t)(h.n >> 32); break;
-        case 4: w = (uint32_t)carry; break;
-        case 5: w = (uint32_t)(carry >> 32); break;
+        case 4: w = (uint32_t)total; break;
+        case 5: w = (uint32_t)(total >> 32); break;
         case 6: w = (uint32_t)h.nb; break;
         case 8: w = h.cb.w[0]; break;
         case 9: w = h.cb.w[1]; break;
@@ -549,43 +646,63 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
 }
 
 // ---------------------------------------------------------------------------
-// Kernel: escape compaction.  Copies each tile's staged records (3 bytes
-// each) to out[off_esc + 3 * tile_offset ...).  The destination is written
-// with aligned dword stores built by v_alignbyte_b32 from the staged words;
-// the partial dwords at both ends (shared with the neighbouring tiles) are
-// written byte by byte.
+// Kernel: escape compaction.  One wave per block: lanes 0..3 fetch the
+// block's four tile counts, lane 4 its escape offset; then the wave copies
+// each tile's staged records (3 bytes each) to out[off_esc + 3 * offset ...).
+// The destination is written with aligned dword stores built by
+// v_alignbyte_b32 from the staged words; the partial dwords at both ends
+// (shared with the neighbouring tiles) are written byte by byte.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kCompactThreads) void sz_enc_compact(
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
-    const uint64_t *__restrict__ tile_offsets, uint8_t *__restrict__ out, uint64_t off_esc)
+    const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
+    uint64_t nb)
 {
-    const uint64_t tile = blockIdx.x;
-    const uint32_t k = tile_counts[tile];
-    if (k == 0) return;
-    const uint8_t *src = stage + tile * (3ull * kEncTile);
-    const uint32_t *src32 = reinterpret_cast<const uint32_t *>(src);
-    const uint64_t dst0 = off_esc + 3 * tile_offsets[tile];
-    const uint64_t end = dst0 + 3ull * k;
-    const uint64_t head_end = std::min<uint64_t>((dst0 + 3) & ~uint64_t(3), end);
-    const uint64_t body_end = std::max<uint64_t>(end & ~uint64_t(3), head_end);
-    const uint32_t tid = threadIdx.x;
-    if (dst0 + tid < head_end) out[dst0 + tid] = src[tid];
-    const uint64_t body_words = (body_end - head_end) / 4;
-    const uint32_t s_first = (uint32_t)(head_end - dst0);
-    for (uint64_t w = tid; w < body_words; w += kCompactThreads) {
-        const uint32_t s = s_first + 4 * (uint32_t)w;
-        const uint32_t lo = src32[s >> 2];
-        const uint32_t hi = src32[(s >> 2) + 1];
-        *reinterpret_cast<uint32_t *>(out + head_end + 4 * w) =
-            __builtin_amdgcn_alignbyte(hi, lo, s & 3);
+    const uint64_t b = (uint64_t)blockIdx.x * (kCompactThreads / 64) + threadIdx.x / 64;
+    if (b >= nb) return;
+    const uint32_t lane = lane_id();
+    uint64_t meta = 0;
+    if (lane < kTilesPerBlock && kTilesPerBlock * b + lane < nt) meta = tile_counts[kTilesPerBlock * b + lane];
+    else if (lane == kTilesPerBlock) meta = block_offsets[b];
+    const uint32_t m = (uint32_t)meta;
+    uint32_t cnt[kTilesPerBlock];
+#pragma unroll
+    for (uint32_t t = 0; t < kTilesPerBlock; ++t) cnt[t] = __builtin_amdgcn_readlane(m, t);
+    uint64_t off = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(meta >> 32), kTilesPerBlock) << 32) |
+                   (uint32_t)__builtin_amdgcn_readlane(m, kTilesPerBlock);
+#pragma unroll
+    for (uint32_t t = 0; t < kTilesPerBlock; ++t) {
+        const uint32_t k = cnt[t];
+        if (k) {
+            const uint64_t tile = kTilesPerBlock * b + t;
+            const uint8_t *src = stage + tile * (3ull * kEncTile);
+            const uint32_t *src32 = reinterpret_cast<const uint32_t *>(src);
+            const uint64_t dst0 = off_esc + 3 * off;
+            const uint64_t end = dst0 + 3ull * k;
+            const uint64_t head_end = std::min<uint64_t>((dst0 + 3) & ~uint64_t(3), end);
+            const uint64_t body_end = std::max<uint64_t>(end & ~uint64_t(3), head_end);
+            if (dst0 + lane < head_end) out[dst0 + lane] = src[lane];
+            const uint64_t body_words = (body_end - head_end) / 4;
+            const uint32_t s_first = (uint32_t)(head_end - dst0);
+            for (uint64_t w = lane; w < body_words; w += 64) {
+                const uint32_t s = s_first + 4 * (uint32_t)w;
+                const uint32_t lo = src32[s >> 2];
+                const uint32_t hi = src32[(s >> 2) + 1];
+                *reinterpret_cast<uint32_t *>(out + head_end + 4 * w) = __builtin_amdgcn_alignbyte(hi, lo, s & 3);
+            }
+            if (body_end + lane < end) out[body_end + lane] = src[body_end - dst0 + lane];
+        }
+        off += k;
     }
-    if (body_end + tid < end) out[body_end + tid] = src[body_end - dst0 + tid];
 }
 
 // ---------------------------------------------------------------------------
 // Kernel: decode scan.  One workgroup validates the header and the block
-// counts and writes the exclusive escape offset of every block.  The status
-// word ends as 0 or a negative error code.
+// counts (each at most its block length, summing to E) and writes the
+// exclusive escape offset of every block.  It writes its verdict (0 or a
+// negative error code) to status[0], the caller-visible status word, and to
+// status[1], which the block decoders read: they only ever write status[0],
+// so every wave of a decode workgroup sees the same verdict.
 // ---------------------------------------------------------------------------
 struct DecodeArgs {
     uint64_t n, nb, in_bytes, off_nib, off_sm, off_esc;
@@ -596,7 +713,7 @@ __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__res
                                                             uint64_t *__restrict__ block_offsets,
                                                             int32_t *__restrict__ status)
 {
-    __shared__ uint32_t wave_sums[33];
+    __shared__ ScanLds lds;
     __shared__ int32_t bad;
     const uint32_t tid = threadIdx.x;
     const uint32_t *h32 = reinterpret_cast<const uint32_t *>(in);
@@ -613,32 +730,73 @@ __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__res
             if (in[32 + c] >= a.symbols) err = SZ_E_FORMAT;
     }
     if (err) {
-        if (tid == 0) *status = err;
+        if (tid == 0) {
+            status[0] = err;
+            status[1] = err;
+        }
         return;
     }
-    if (tid == 0) bad = 0;
-    __syncthreads();
-    const uint32_t *counts = reinterpret_cast<const uint32_t *>(in + 64);
-    uint64_t carry = 0;
-    for (uint64_t b0 = 0; b0 < a.nb; b0 += kScanThreads) {
-        const uint64_t b = b0 + tid;
-        uint32_t c = 0;
-        if (b < a.nb) {
-            c = counts[b];
-            const uint64_t len = std::min<uint64_t>(kBlock, a.n - b * kBlock);
-            if (c > len) bad = 1;
-        }
-        uint32_t total;
-        const uint32_t excl = workgroup_exclusive_sum(c, wave_sums, total);
-        if (b < a.nb) block_offsets[b] = carry + excl;
-        carry += total;
+    if (tid == 0) {
+        bad = 0;
+        lds.carry = 0;
     }
+    // items are groups of four block counts: one aligned dwordx4 each (the
+    // count array starts at byte 64 and is followed by padding up to off_nib)
+    const uint32_t *counts = reinterpret_cast<const uint32_t *>(in + 64);
+    const uint32_t nb = (uint32_t)a.nb;
+    // the last block may be shorter than B: its count is bounded by its length
+    bool too_many = nb && tid == 0 && counts[nb - 1] > a.n - (uint64_t)(nb - 1) * kBlock;
+    for (uint32_t g0 = 0; g0 < nb; g0 += 4 * kScanBatch * kScanThreads) {
+        uint4 v[kScanBatch];
+        uint32_t x[kScanBatch];
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+            const uint32_t g = g0 + 4 * (i * kScanThreads + tid);
+            v[i] = make_uint4(0, 0, 0, 0);
+            if (g < nb) {
+                v[i] = *reinterpret_cast<const uint4 *>(counts + g);
+                if (g + 1 >= nb) v[i].y = 0;
+                if (g + 2 >= nb) v[i].z = 0;
+                if (g + 3 >= nb) v[i].w = 0;
+                too_many |= std::max(std::max(v[i].x, v[i].y), std::max(v[i].z, v[i].w)) > (uint32_t)kBlock;
+            }
+            x[i] = v[i].x + v[i].y + v[i].z + v[i].w;
+        }
+        uint64_t base[kScanBatch];
+        scan_batch(x, base, lds);
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+            const uint32_t g = g0 + 4 * (i * kScanThreads + tid);
+            if (g < nb) {
+                const uint64_t o1 = base[i] + v[i].x, o2 = o1 + v[i].y, o3 = o2 + v[i].z;
+                if (g + 3 < nb) {
+                    // 32 aligned bytes: two dwordx4 stores of offset pairs
+                    uint4 *dst = reinterpret_cast<uint4 *>(block_offsets + g);
+                    dst[0] = make_uint4((uint32_t)base[i], (uint32_t)(base[i] >> 32), (uint32_t)o1, (uint32_t)(o1 >> 32));
+                    dst[1] = make_uint4((uint32_t)o2, (uint32_t)(o2 >> 32), (uint32_t)o3, (uint32_t)(o3 >> 32));
+                } else {
+                    block_offsets[g] = base[i];
+                    if (g + 1 < nb) block_offsets[g + 1] = o1;
+                    if (g + 2 < nb) block_offsets[g + 2] = o2;
+                }
+            }
+        }
+    }
+    if (too_many) bad = 1;
     __syncthreads();
-    if (tid == 0) *status = (bad || carry != e_hdr) ? SZ_E_FORMAT : 0;
+    if (tid == 0) {
+        const int32_t verdict = (bad || lds.carry != e_hdr) ? SZ_E_FORMAT : 0;
+        status[0] = verdict;
+        status[1] = verdict;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Kernel: BF16 decode, one workgroup (4 waves) per 64K block.
+// Decode kernels: one 1024-lane workgroup per 64K block.  First an LDS map
+// from each chunk to the first escape record inside it is built from the
+// block's records (validating their order and range), then every wave
+// decodes one 4096-element row in registers, patches the escaped exponents
+// and stores once.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kNoEscape = 0xFFFFu;
 
@@ -648,6 +806,31 @@ __device__ __forceinline__ void read_record(const uint8_t *esc, uint64_t r, uint
     const uint8_t *p = esc + 3 * r;
     pos = (uint32_t)p[0] | ((uint32_t)p[1] << 8);
     e = p[2];
+}
+
+// Builds first[chunk] for the k records of a block (chunk = pos >> log2_chunk)
+// and reports malformed records through the status word.
+template <int LOG2_CHUNK>
+__device__ __forceinline__ void map_block_escapes(const uint8_t *esc, uint64_t r0, uint32_t k, uint32_t blen,
+                                                  uint32_t symbols, uint16_t *first, int32_t *status)
+{
+    bool bad = false;
+    for (uint32_t r = threadIdx.x; r < k; r += blockDim.x) {
+        uint32_t pos, e;
+        read_record(esc, r0 + r, pos, e);
+        int32_t prev = -1;
+        if (r > 0) {
+            uint32_t pp, pe;
+            read_record(esc, r0 + r - 1, pp, pe);
+            prev = (int32_t)pp;
+        }
+        if (pos >= blen || (int32_t)pos <= prev || e >= symbols) {
+            bad = true;
+            continue;
+        }
+        if (r == 0 || (uint32_t)(prev >> LOG2_CHUNK) != (pos >> LOG2_CHUNK)) first[pos >> LOG2_CHUNK] = (uint16_t)r;
+    }
+    if (bad) atomicExch(status, SZ_E_FORMAT);
 }
 
 __device__ __forceinline__ uint4 decode_chunk_bf16(uint32_t nib, uint2 sm, const uint32_t *table)
@@ -682,7 +865,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
 {
     __shared__ uint32_t table[256];
     __shared__ uint16_t first[kBlock / 8];     // first escape record of each 8-element chunk
-    if (*status != 0) return;
+    if (status[1] != 0) return;
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x;
     const uint64_t e0 = b * kBlock;
@@ -690,90 +873,64 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
     const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
     const uint64_t r0 = block_offsets[b];
     const uint8_t *esc = in + a.off_esc;
-    {
+    if (tid < 256) {
         const uint32_t lo = in[32 + (tid & 15)];
         const uint32_t hi = in[32 + (tid >> 4)];
         table[tid] = (lo << 7) | (hi << 23);
     }
-    if (k) {
-        uint4 *f4 = reinterpret_cast<uint4 *>(first);
-        const uint4 none = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
-        for (uint32_t i = tid; i < kBlock / 8 / 8; i += kDecThreads) f4[i] = none;
-    }
-    __syncthreads();
-    if (k) {
-        bool bad = false;
-        for (uint32_t r = tid; r < k; r += kDecThreads) {
-            uint32_t pos, e;
-            read_record(esc, r0 + r, pos, e);
-            int32_t prev = -1;
-            if (r > 0) {
-                uint32_t pp, pe;
-                read_record(esc, r0 + r - 1, pp, pe);
-                prev = (int32_t)pp;
-            }
-            if (pos >= blen || (int32_t)pos <= prev) {
-                bad = true;
-                continue;
-            }
-            if (r == 0 || (uint32_t)(prev >> 3) != (pos >> 3)) first[pos >> 3] = (uint16_t)r;
-        }
-        if (bad) atomicExch(status, SZ_E_FORMAT);
-    }
-    __syncthreads();
-
+    // the row's loads are issued first and stay in flight while the escape
+    // map is built (the barriers only wait for LDS traffic)
     const uint32_t lane = lane_id();
-    const uint32_t wave = tid / 64;
-    const bool full_block = blen == kBlock;
+    const uint32_t rbase = (tid / 64) * kRow;                  // block-local first element of the row
+    const bool full_row = rbase + kRow <= blen;
     const uint8_t *nib_base = in + a.off_nib;
     const uint8_t *sm_base = in + a.off_sm;
-    for (uint32_t row = 0; row < 4; ++row) {
-        const uint32_t rbase = wave * 16384 + row * kBf16Row;    // block-local element
-        if (rbase >= blen) break;
-        uint32_t nib[kBf16Chunks];
-        uint2 sm[kBf16Chunks];
+    uint32_t nib[kBf16Chunks];
+    uint2 sm[kBf16Chunks];
 #pragma unroll
-        for (uint32_t j = 0; j < kBf16Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 8;
-            if (full_block || c < blen) {
-                const uint64_t g = e0 + c;
-                nib[j] = *reinterpret_cast<const uint32_t *>(nib_base + g / 2);
-                sm[j] = *reinterpret_cast<const uint2 *>(sm_base + g);
-            } else {
-                nib[j] = 0;
-                sm[j] = make_uint2(0, 0);
-            }
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + lane) * 8;
+        const uint64_t g = e0 + c;
+        if (full_row || c < blen) {
+            nib[j] = load_nt(reinterpret_cast<const uint32_t *>(nib_base + g / 2));
+            sm[j] = load_nt(reinterpret_cast<const uint2 *>(sm_base + g));
+        } else {
+            nib[j] = 0;
+            sm[j] = make_uint2(0, 0);
         }
+    }
+    if (k) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+    __syncthreads();
+    if (k) map_block_escapes<3>(esc, r0, k, blen, 256, first, status);
+    __syncthreads();
+    if (rbase >= blen) return;
 #pragma unroll
-        for (uint32_t j = 0; j < kBf16Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 8;
-            uint4 o = decode_chunk_bf16(nib[j], sm[j], table);
-            if (k) {
-                uint32_t r = first[c >> 3];
-                if (r != kNoEscape) {
-                    for (; r < k; ++r) {
-                        uint32_t pos, e;
-                        read_record(esc, r0 + r, pos, e);
-                        if ((pos >> 3) != (c >> 3)) break;
-                        patch_bf16(o, pos & 7, e);
-                    }
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + lane) * 8;
+        uint4 o = decode_chunk_bf16(nib[j], sm[j], table);
+        if (k) {
+            uint32_t r = first[c >> 3];
+            if (r != kNoEscape) {
+                for (; r < k; ++r) {
+                    uint32_t pos, e;
+                    read_record(esc, r0 + r, pos, e);
+                    if ((pos >> 3) != (c >> 3)) break;
+                    patch_bf16(o, pos & 7, e);
                 }
             }
-            const uint64_t g = e0 + c;
-            if (full_block || c + 8 <= blen) {
-                *reinterpret_cast<uint4 *>(out + g) = o;
-            } else if (c < blen) {
-                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
-                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
-            }
+        }
+        const uint64_t g = e0 + c;
+        if (full_row || c + 8 <= blen) {
+            store_nt(reinterpret_cast<uint4 *>(out + g), o);
+        } else if (c < blen) {
+            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+            for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
         }
     }
 }
 
-// ---------------------------------------------------------------------------
-// Kernel: FP8 E5M2 decode, one workgroup (4 waves) per 64K block.  A lane
-// decodes 32 elements: 16 code bytes + 12 sign/mantissa bytes -> 32 bytes.
-// ---------------------------------------------------------------------------
+// FP8 E5M2 decode: a lane decodes two 32-element chunks (16 code bytes + 12
+// sign/mantissa bytes -> 32 bytes each).
 __device__ __forceinline__ uint32_t unpack_sm3_x4(uint32_t v12)
 {
     // 12 bits = four 3-bit symbols -> one symbol per byte
@@ -807,7 +964,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
 {
     __shared__ uint16_t table[256];
     __shared__ uint16_t first[kBlock / 32];    // first escape record of each 32-element chunk
-    if (*status != 0) return;
+    if (status[1] != 0) return;
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x;
     const uint64_t e0 = b * kBlock;
@@ -815,98 +972,72 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
     const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
     const uint64_t r0 = block_offsets[b];
     const uint8_t *esc = in + a.off_esc;
-    {
+    if (tid < 256) {
         const uint32_t lo = in[32 + (tid & 15)];
         const uint32_t hi = in[32 + (tid >> 4)];
         table[tid] = (uint16_t)((lo << 2) | (hi << 10));
     }
-    if (k) {
-        uint4 *f4 = reinterpret_cast<uint4 *>(first);
-        const uint4 none = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
-        for (uint32_t i = tid; i < kBlock / 32 / 8; i += kDecThreads) f4[i] = none;
-    }
-    __syncthreads();
-    if (k) {
-        bool bad = false;
-        for (uint32_t r = tid; r < k; r += kDecThreads) {
-            uint32_t pos, e;
-            read_record(esc, r0 + r, pos, e);
-            int32_t prev = -1;
-            if (r > 0) {
-                uint32_t pp, pe;
-                read_record(esc, r0 + r - 1, pp, pe);
-                prev = (int32_t)pp;
-            }
-            if (pos >= blen || (int32_t)pos <= prev || e >= 32) {
-                bad = true;
-                continue;
-            }
-            if (r == 0 || (uint32_t)(prev >> 5) != (pos >> 5)) first[pos >> 5] = (uint16_t)r;
-        }
-        if (bad) atomicExch(status, SZ_E_FORMAT);
-    }
-    __syncthreads();
-
     const uint32_t lane = lane_id();
-    const uint32_t wave = tid / 64;
-    const bool full_block = blen == kBlock;
+    const uint32_t rbase = (tid / 64) * kRow;
+    const bool full_row = rbase + kRow <= blen;
     const uint8_t *nib_base = in + a.off_nib;
     const uint8_t *sm_base = in + a.off_sm;
     const uint64_t sm_end = a.off_sm + 3 * ((a.n + 7) / 8);
-    for (uint32_t row = 0; row < 4; ++row) {
-        const uint32_t rbase = wave * 16384 + row * kE5Row;
-        if (rbase >= blen) break;
-        uint4 nib[kE5Chunks];
-        uint32_t sm3[kE5Chunks][3];
+    uint4 nib[kE5Chunks];
+    uint32_t sm3[kE5Chunks][3];
 #pragma unroll
-        for (uint32_t j = 0; j < kE5Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 32;
-            const uint64_t g = e0 + c;
-            if (full_block || c + 32 <= blen) {
-                nib[j] = *reinterpret_cast<const uint4 *>(nib_base + g / 2);
-                const uint3 v = *reinterpret_cast<const uint3 *>(sm_base + (g / 32) * 12);
-                sm3[j][0] = v.x;
-                sm3[j][1] = v.y;
-                sm3[j][2] = v.z;
-            } else if (c < blen) {
-                nib[j] = *reinterpret_cast<const uint4 *>(nib_base + g / 2);
-                sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
-                const uint64_t start = a.off_sm + (g / 32) * 12;
-                for (uint32_t i = 0; i < 12 && start + i < sm_end; ++i)
-                    sm3[j][i / 4] |= (uint32_t)in[start + i] << (8 * (i & 3));
-            } else {
-                nib[j] = make_uint4(0, 0, 0, 0);
-                sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
-            }
+    for (int j = 0; j < kE5Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + lane) * 32;
+        const uint64_t g = e0 + c;
+        if (full_row || c + 32 <= blen) {
+            nib[j] = load_nt(reinterpret_cast<const uint4 *>(nib_base + g / 2));
+            const uint32_t *s32 = reinterpret_cast<const uint32_t *>(sm_base + (g / 32) * 12);
+            sm3[j][0] = load_nt(s32);
+            sm3[j][1] = load_nt(s32 + 1);
+            sm3[j][2] = load_nt(s32 + 2);
+        } else if (c < blen) {
+            nib[j] = *reinterpret_cast<const uint4 *>(nib_base + g / 2);
+            sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
+            const uint64_t start = a.off_sm + (g / 32) * 12;
+            for (uint32_t i = 0; i < 12 && start + i < sm_end; ++i)
+                sm3[j][i / 4] |= (uint32_t)in[start + i] << (8 * (i & 3));
+        } else {
+            nib[j] = make_uint4(0, 0, 0, 0);
+            sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
         }
+    }
+    if (k && tid < kBlock / 32 / 8) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+    __syncthreads();
+    if (k) map_block_escapes<5>(esc, r0, k, blen, 32, first, status);
+    __syncthreads();
+    if (rbase >= blen) return;
 #pragma unroll
-        for (uint32_t j = 0; j < kE5Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 32;
-            uint32_t o[8];
-            decode_chunk_e5m2(nib[j], sm3[j], table, o);
-            if (k) {
-                uint32_t r = first[c >> 5];
-                if (r != kNoEscape) {
-                    for (; r < k; ++r) {
-                        uint32_t pos, e;
-                        read_record(esc, r0 + r, pos, e);
-                        if ((pos >> 5) != (c >> 5)) break;
-                        const uint32_t p = pos & 31;
-                        const uint32_t sh = 8 * (p & 3) + 2;
-                        const uint32_t clear = ~(0x1Fu << sh);
+    for (int j = 0; j < kE5Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + lane) * 32;
+        uint32_t o[8];
+        decode_chunk_e5m2(nib[j], sm3[j], table, o);
+        if (k) {
+            uint32_t r = first[c >> 5];
+            if (r != kNoEscape) {
+                for (; r < k; ++r) {
+                    uint32_t pos, e;
+                    read_record(esc, r0 + r, pos, e);
+                    if ((pos >> 5) != (c >> 5)) break;
+                    const uint32_t p = pos & 31;
+                    const uint32_t sh = 8 * (p & 3) + 2;
+                    const uint32_t clear = ~(0x1Fu << sh);
 #pragma unroll
-                        for (int w = 0; w < 8; ++w)
-                            if ((uint32_t)w == (p >> 2)) o[w] = (o[w] & clear) | (e << sh);
-                    }
+                    for (int w = 0; w < 8; ++w)
+                        if ((uint32_t)w == (p >> 2)) o[w] = (o[w] & clear) | (e << sh);
                 }
             }
-            const uint64_t g = e0 + c;
-            if (full_block || c + 32 <= blen) {
-                *reinterpret_cast<uint4 *>(out + g) = make_uint4(o[0], o[1], o[2], o[3]);
-                *reinterpret_cast<uint4 *>(out + g + 16) = make_uint4(o[4], o[5], o[6], o[7]);
-            } else if (c < blen) {
-                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint8_t)(o[i / 4] >> (8 * (i & 3)));
-            }
+        }
+        const uint64_t g = e0 + c;
+        if (full_row || c + 32 <= blen) {
+            store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
+            store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
+        } else if (c < blen) {
+            for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint8_t)(o[i / 4] >> (8 * (i & 3)));
         }
     }
 }
@@ -1042,19 +1173,19 @@ extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz
     uint8_t *ws = static_cast<uint8_t *>(d_ws);
     uint8_t *out = static_cast<uint8_t *>(d_out);
     uint32_t *tile_counts = reinterpret_cast<uint32_t *>(ws + w.counts);
-    uint64_t *tile_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
+    uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
     uint8_t *stage = ws + w.stage;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Codebook4 cb4 = pack_codebook(cb->exp);
 
     if (g.nt && dtype == SZ_BF16) {
         LaunchScope scope("sz_enc_dense_bf16", s);
-        hipLaunchKernelGGL(sz_enc_dense_bf16, dim3((uint32_t)g.nt), dim3(64), 0, s,
+        hipLaunchKernelGGL(sz_enc_dense_bf16, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s,
                            static_cast<const uint16_t *>(d_in), g.n, out, g.off_nib, g.off_sm, cb4,
                            tile_counts, stage);
     } else if (g.nt) {
         LaunchScope scope("sz_enc_dense_e5m2", s);
-        hipLaunchKernelGGL(sz_enc_dense_e5m2, dim3((uint32_t)g.nt), dim3(64), 0, s,
+        hipLaunchKernelGGL(sz_enc_dense_e5m2, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s,
                            static_cast<const uint8_t *>(d_in), g.n, out, g.off_nib, g.off_sm, g.sm_bytes,
                            cb4, tile_counts, stage);
     }
@@ -1071,13 +1202,14 @@ extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz
         h.pad_start[2] = g.off_sm + g.sm_bytes;
         h.pad_end[2] = g.off_esc;
         LaunchScope scope("sz_enc_scan", s);
-        hipLaunchKernelGGL(sz_enc_scan, dim3(1), dim3(kScanThreads), 0, s, tile_counts, g.nt, tile_offsets,
-                           out, h);
+        hipLaunchKernelGGL(sz_enc_scan, dim3(1), dim3(kScanThreads), 0, s, tile_counts, (uint32_t)g.nt,
+                           block_offsets, out, h);
     }
     if (g.nt) {
         LaunchScope scope("sz_enc_compact", s);
-        hipLaunchKernelGGL(sz_enc_compact, dim3((uint32_t)g.nt), dim3(kCompactThreads), 0, s, stage,
-                           tile_counts, tile_offsets, out, g.off_esc);
+        const uint32_t groups = (uint32_t)((g.nb + kCompactThreads / 64 - 1) / (kCompactThreads / 64));
+        hipLaunchKernelGGL(sz_enc_compact, dim3(groups), dim3(kCompactThreads), 0, s, stage, tile_counts,
+                           block_offsets, out, g.off_esc, g.nt, g.nb);
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }
