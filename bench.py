@@ -43,6 +43,9 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-log2", type=int, default=28,
                    help="elements of the workload the CPU oracle encodes and decodes (log2)")
+    p.add_argument("--ingest-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"),
+                   help="record HBM traffic per kernel from two rocprofv3 --pmc runs of this "
+                        "benchmark (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json and exit")
     return p.parse_args()
 
 
@@ -53,18 +56,64 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
 def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch measured by rocprofv3 counters, if they were taken
     on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(TRAFFIC_PATH):
         return None
-    with open(path) as f:
+    with open(TRAFFIC_PATH) as f:
         rec = json.load(f)
     entry = rec.get(workload, {}).get(kernel)
     if not entry or entry.get("source_hash") != kernel_source_hash():
         return None
     return entry.get("bytes_per_launch")
+
+
+def _pmc_per_kernel(csv_path, counter):
+    """{kernel short name: [values in KiB per dispatch]} from a rocprofv3 counter CSV."""
+    import csv
+    out = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+            out.setdefault(name, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def ingest_pmc(workload, fetch_csv, write_csv, copy_bytes):
+    """Turns FETCH_SIZE / WRITE_SIZE runs into HBM bytes per launch of every
+    library kernel.  Each counter is scaled by what it reads for the plain
+    device copy of `copy_bytes` bytes in the same run (the largest copy
+    dispatch), and the record is tied to the current kernel source."""
+    fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
+    f_scale = copy_bytes / (max(fetch[COPY_KERNEL]) * 1024.0)
+    w_scale = copy_bytes / (max(write[COPY_KERNEL]) * 1024.0)
+    rec = {}
+    if os.path.exists(TRAFFIC_PATH):
+        with open(TRAFFIC_PATH) as f:
+            rec = json.load(f)
+    entry = {}
+    for k in sorted(set(fetch) & set(write)):
+        if not k.startswith("sz_"):
+            continue
+        fk = sum(fetch[k]) / len(fetch[k])
+        wk = sum(write[k]) / len(write[k])
+        entry[k] = {"source_hash": kernel_source_hash(),
+                    "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                    "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                    "bytes_per_launch": int(fk * 1024 * f_scale + wk * 1024 * w_scale)}
+    rec[workload] = entry
+    with open(TRAFFIC_PATH, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return entry
 
 
 def cpu_baseline(x_dev, cb, dtype, log2_sample):
@@ -92,6 +141,10 @@ def cpu_baseline(x_dev, cb, dtype, log2_sample):
 
 def main():
     args = parse_args()
+    if args.ingest_pmc:
+        f_csv, w_csv, copy_bytes = args.ingest_pmc
+        print(json.dumps(ingest_pmc(args.workload, f_csv, w_csv, int(copy_bytes)), indent=1))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the SplitZip codec has no cross-GPU step on this path "
               "(each GPU encodes/decodes its own shard); run with --gpus 1", file=sys.stderr)
@@ -209,6 +262,7 @@ def main():
         "stream_bytes": size,
         "kernels": per_kernel,
         "copy_GBps": round(copy_gbps, 1),
+        "copy_bytes": alg_per_direction,
         "roofline": {
             "bound": "hbm",
             "kernel": dominant,
