@@ -49,7 +49,7 @@ constexpr uint32_t kEncTile = kRow * (kEncThreads / 64);  // 16384
 constexpr uint32_t kTilesPerBlock = kBlock / kEncTile;    // 4
 constexpr uint32_t kDecThreads = 1024;                    // 16 waves = one 64K block
 constexpr uint32_t kScanThreads = 1024;
-constexpr uint32_t kCompactThreads = 64 * kTilesPerBlock; // one wave per tile
+constexpr uint32_t kCompactThreads = 256;                 // one wave per block
 
 constexpr uint64_t up256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 
@@ -144,7 +144,6 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x)
 
 __device__ __forceinline__ uint32_t read_lane63(uint32_t x) { return __builtin_amdgcn_readlane(x, 63); }
 
-__device__ __forceinline__ uint32_t popc64(uint64_t x) { return __popcll(x); }
 
 // Codebook packed as 4 little-endian words: byte c = exponent of code c.
 struct Codebook4 {
@@ -194,19 +193,23 @@ __device__ __forceinline__ uint32_t pack_codes8(uint32_t c_a, uint32_t c_b)
     return perm(k_b | (k_b >> 4), k_a | (k_a >> 4), 0x06040200u);
 }
 
-// Escape flags of 8 elements: element k at bit 8k+7.
-__device__ __forceinline__ uint64_t escape_flags8(uint32_t c_a, uint32_t c_b)
+// Escape flags of 8 elements (bit 7 of each table byte) -> bit k = element k.
+// (x >> 7) holds the four flags at bits 0, 8, 16, 24; the multiply moves flag
+// k to bit 28 + k without carries.
+__device__ __forceinline__ uint32_t escape_mask8(uint32_t c_a, uint32_t c_b)
 {
-    return (uint64_t)(c_a & 0x80808080u) | ((uint64_t)(c_b & 0x80808080u) << 32);
+    const uint32_t lo = (((c_a & 0x80808080u) >> 7) * 0x10204080u) >> 28;
+    const uint32_t hi = (((c_b & 0x80808080u) >> 7) * 0x10204080u) >> 28;
+    return lo | (hi << 4);
 }
 
 // ---------------------------------------------------------------------------
 // BF16 encode of one 8-element chunk (16 bytes in).
 //   nib: 4 bytes of codes;  sm: 8 sign/mantissa bytes (sign << 7 | mantissa7)
-//   esc: escape flags (bit 8k+7);  ex: exponent of element k in byte k
+//   esc: escape mask (bit k = element k);  ex: exponent of element k in byte k
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void encode_chunk_bf16(const uint4 q, const uint8_t *table, uint32_t &nib,
-                                                  uint2 &sm, uint64_t &esc, uint64_t &ex)
+                                                  uint2 &sm, uint32_t &esc, uint64_t &ex)
 {
     const uint32_t lo_a = perm(q.y, q.x, 0x06040200u);   // low bytes of elements 0..3
     const uint32_t hi_a = perm(q.y, q.x, 0x07050301u);   // high bytes of elements 0..3
@@ -219,14 +222,15 @@ __device__ __forceinline__ void encode_chunk_bf16(const uint4 q, const uint8_t *
     const uint32_t c_a = lookup4(table, e_a);
     const uint32_t c_b = lookup4(table, e_b);
     nib = pack_codes8(c_a, c_b);
-    esc = escape_flags8(c_a, c_b);
+    esc = escape_mask8(c_a, c_b);
     ex = (uint64_t)e_a | ((uint64_t)e_b << 32);
 }
 
 // ---------------------------------------------------------------------------
 // FP8 E5M2 encode of one 32-element chunk (32 bytes in): 16 code bytes and
 // 12 sign/mantissa bytes (four 24-bit groups of eight 3-bit symbols).
-//   esc[s], ex[s]: escape flags and exponents of elements 8s..8s+7.
+//   esc: escape mask (bit k = element k of the 32);  ex[s]: exponents of
+//   elements 8s..8s+7.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack_sm3_x4(uint32_t sym)
 {
@@ -235,11 +239,11 @@ __device__ __forceinline__ uint32_t pack_sm3_x4(uint32_t sym)
 }
 
 __device__ __forceinline__ void encode_chunk_e5m2(const uint4 q0, const uint4 q1, const uint8_t *table,
-                                                  uint4 &nib, uint32_t sm3[3], uint64_t esc[4],
-                                                  uint64_t ex[4])
+                                                  uint4 &nib, uint32_t sm3[3], uint32_t &esc, uint64_t ex[4])
 {
     const uint32_t d[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     uint32_t nibw[4], grp[4];
+    esc = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const uint32_t a = d[2 * s], b = d[2 * s + 1];
@@ -250,7 +254,7 @@ __device__ __forceinline__ void encode_chunk_e5m2(const uint4 q0, const uint4 q1
         const uint32_t c_a = lookup4(table, e_a);
         const uint32_t c_b = lookup4(table, e_b);
         nibw[s] = pack_codes8(c_a, c_b);
-        esc[s] = escape_flags8(c_a, c_b);
+        esc |= escape_mask8(c_a, c_b) << (8 * s);
         ex[s] = (uint64_t)e_a | ((uint64_t)e_b << 32);
         grp[s] = pack_sm3_x4(s_a) | (pack_sm3_x4(s_b) << 12);
     }
@@ -260,32 +264,95 @@ __device__ __forceinline__ void encode_chunk_e5m2(const uint4 q0, const uint4 q1
     sm3[2] = (grp[2] >> 16) | (grp[3] << 8);
 }
 
-// Writes the escape records of 8 elements (flags esc, exponents ex, first
-// block-local position pos0) into the tile's staging area, ascending, from
-// rank `rank` on.
-__device__ __forceinline__ void stage_records(uint8_t *tstage, uint32_t rank, uint64_t esc, uint64_t ex,
-                                              uint32_t pos0)
+// ---------------------------------------------------------------------------
+// Escape staging.  Inside a wave the records of a tile come in element order:
+// (chunk j, lane, element).  A "segment" is 512 consecutive elements of a
+// row (BF16: chunk j of all 64 lanes; E5M2: chunk j of 16 lanes), so it holds
+// at most 512 records.  Each lane writes its records of the segment into the
+// wave's LDS buffer, shifted by the byte misalignment of the segment's
+// destination, and the wave then copies the buffer to the tile's staging
+// slot with aligned dword stores; the dwords at both ends, which neighbouring
+// segments (possibly of another wave) share, are written byte by byte.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSegElems = 512;
+constexpr uint32_t kSegBytes = 3 * kSegElems + 8;          // + alignment shift, rounded to dwords
+
+// Appends the records of 8 elements (escape mask esc, exponents ex,
+// block-local position of the first element pos0) to an LDS buffer at byte
+// `off`; returns the byte after them.
+__device__ __forceinline__ uint32_t lds_put_records(uint8_t *buf, uint32_t off, uint32_t esc, uint64_t ex,
+                                                    uint32_t pos0)
 {
     while (esc) {
-        const uint32_t bit = (uint32_t)__builtin_ctzll(esc);
+        const uint32_t k = (uint32_t)__builtin_ctz(esc);
         esc &= esc - 1;
-        const uint32_t k = bit >> 3;
         const uint32_t pos = (pos0 + k) & 0xFFFFu;
-        const uint32_t e = (uint32_t)(ex >> (8 * k)) & 0xFFu;
+        buf[off] = (uint8_t)pos;
+        buf[off + 1] = (uint8_t)(pos >> 8);
+        buf[off + 2] = (uint8_t)(ex >> (8 * k));
+        off += 3;
+    }
+    return off;
+}
+
+__device__ __forceinline__ void wave_lds_fence()
+{
+    // LDS operations of one wave complete in order; this only keeps the
+    // compiler from moving LDS accesses across the hand-over point
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Copies `len` bytes, held in buf[g0 & 3, (g0 & 3) + len), to dst[g0, g0 + len).
+__device__ __forceinline__ void flush_segment(const uint8_t *buf, uint8_t *dst, uint32_t g0, uint32_t len)
+{
+    const uint32_t lane = lane_id();
+    const uint32_t first_dw = g0 >> 2;
+    const uint32_t end = g0 + len;
+    const uint32_t last_dw = (end - 1) >> 2;
+    const uint32_t head = g0 & 3;
+    const uint32_t tail = ((end - 1) & 3) + 1;
+    for (uint32_t i = lane; i <= last_dw - first_dw; i += 64) {
+        const uint32_t w = reinterpret_cast<const uint32_t *>(buf)[i];
+        const uint32_t lo = (i == 0) ? head : 0;
+        const uint32_t hi = (first_dw + i == last_dw) ? tail : 4;
+        uint8_t *d = dst + 4ull * (first_dw + i);
+        if (lo == 0 && hi == 4) {
+            *reinterpret_cast<uint32_t *>(d) = w;
+        } else {
+            for (uint32_t b = lo; b < hi; ++b) d[b] = (uint8_t)(w >> (8 * b));
+        }
+    }
+}
+
+// Writes the escape records of 8 elements (escape mask esc, exponents ex,
+// first block-local position pos0) straight into the staging area,
+// ascending, from rank `rank` on.  Used for rows with few escapes.
+__device__ __forceinline__ void put_records(uint8_t *tstage, uint32_t rank, uint32_t esc, uint64_t ex,
+                                            uint32_t pos0)
+{
+    while (esc) {
+        const uint32_t k = (uint32_t)__builtin_ctz(esc);
+        esc &= esc - 1;
+        const uint32_t pos = (pos0 + k) & 0xFFFFu;
         uint8_t *r = tstage + 3ull * rank;
         r[0] = (uint8_t)pos;
         r[1] = (uint8_t)(pos >> 8);
-        r[2] = (uint8_t)e;
+        r[2] = (uint8_t)(ex >> (8 * k));
         ++rank;
     }
 }
 
-// Escape bookkeeping shared by both encoders.  Each lane holds J chunks of G
-// eight-element groups (BF16 J=8, G=1; E5M2 J=2, G=4); the rank order inside
-// a wave row is (chunk, lane, group, element).  Returns the wave's escape
-// total; `before[j]` = escapes of this wave before chunk j of this lane.
+// Rows with more escapes than this go through the LDS segment buffer.
+constexpr uint32_t kDirectRecords = 32;
+
+// Per-chunk rank data of a wave row (J chunks per lane): row_base[j] = escapes
+// of the wave before chunk row j, row_total[j] = escapes in chunk row j (both
+// wave-uniform), lane_before[j] = escapes of lanes below this one in row j.
+// Returns the wave's escape total.
 template <int J>
-__device__ __forceinline__ uint32_t wave_chunk_ranks(const uint32_t (&cnt)[J], uint32_t (&before)[J])
+__device__ __forceinline__ uint32_t wave_chunk_ranks(const uint32_t (&cnt)[J], uint32_t (&row_base)[J],
+                                                     uint32_t (&row_total)[J], uint32_t (&lane_before)[J])
 {
     static_assert(J % 2 == 0, "chunk counts are scanned in pairs");
     uint32_t running = 0;
@@ -295,9 +362,13 @@ __device__ __forceinline__ uint32_t wave_chunk_ranks(const uint32_t (&cnt)[J], u
         const uint32_t incl = wave_inclusive_sum(packed);
         const uint32_t excl = incl - packed;
         const uint32_t tot = read_lane63(incl);
-        before[2 * p] = running + (excl & 0xFFFFu);
+        row_base[2 * p] = running;
+        row_total[2 * p] = tot & 0xFFFFu;
+        lane_before[2 * p] = excl & 0xFFFFu;
         running += tot & 0xFFFFu;
-        before[2 * p + 1] = running + (excl >> 16);
+        row_base[2 * p + 1] = running;
+        row_total[2 * p + 1] = tot >> 16;
+        lane_before[2 * p + 1] = excl >> 16;
         running += tot >> 16;
     }
     return running;
@@ -325,18 +396,23 @@ __device__ __forceinline__ uint32_t workgroup_wave_prefix(uint32_t wave_total, u
 
 // ---------------------------------------------------------------------------
 // Kernel: BF16 dense encode + escape staging.  One 256-lane workgroup per
-// 16K-element tile; wave w streams elements [4096w, 4096w + 4096) of it.
+// 16K-element tile; wave w streams elements [4096w, 4096w + 4096) of it.  The
+// tile's records are staged in element order in the tile's slot (3 bytes per
+// element); tile_counts[tile] gets their number.
 // ---------------------------------------------------------------------------
 constexpr int kBf16Chunks = 8;
 
 __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t *__restrict__ in, uint64_t n,
-                                                                 uint8_t *__restrict__ out, uint64_t off_nib,
-                                                                 uint64_t off_sm, Codebook4 cb,
-                                                                 uint32_t *__restrict__ tile_counts,
-                                                                 uint8_t *__restrict__ stage)
+                                                              uint8_t *__restrict__ out, uint64_t off_nib,
+                                                              uint64_t off_sm, Codebook4 cb,
+                                                              uint32_t *__restrict__ tile_counts,
+                                                              uint8_t *__restrict__ stage)
 {
     __shared__ uint32_t table32[64];
     __shared__ uint32_t wave_totals[kEncThreads / 64];
+    __shared__ __align__(16) uint8_t seg_buf[kEncThreads / 64][kSegBytes];
+    // exponents of chunks that hold escapes, parked until the ranks are known
+    __shared__ uint64_t ex_park[kEncThreads / 64][kBf16Chunks][64];
     const uint32_t lane = lane_id();
     const uint32_t wave = threadIdx.x / 64;
     const uint64_t tile = blockIdx.x;
@@ -361,14 +437,16 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
     build_encode_table(table32, cb, 256);
     __syncthreads();
     const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
-    uint64_t esc[kBf16Chunks], ex[kBf16Chunks];
+    uint32_t esc[kBf16Chunks];
     uint32_t cnt[kBf16Chunks];
 #pragma unroll
     for (int j = 0; j < kBf16Chunks; ++j) {
         const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
         uint32_t nib;
         uint2 sm;
-        encode_chunk_bf16(q[j], table, nib, sm, esc[j], ex[j]);
+        uint64_t ex;
+        encode_chunk_bf16(q[j], table, nib, sm, esc[j], ex);
+        if (esc[j]) ex_park[wave][j][lane] = ex;
         if (full_row || c0 + 8 <= n) {
             store_nt(reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2), nib);
             store_nt(reinterpret_cast<uint2 *>(out + off_sm + c0), sm);
@@ -377,7 +455,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
             // and no escape; the bytes past the data are section padding
             const uint32_t valid = (uint32_t)(n - c0);
             const uint64_t keep = (1ull << (8 * valid)) - 1;
-            esc[j] &= keep;
+            esc[j] &= (1u << valid) - 1;
             nib &= (uint32_t)((1ull << (4 * valid)) - 1);
             const uint64_t smv = ((uint64_t)sm.y << 32 | sm.x) & keep;
             *reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2) = nib;
@@ -385,19 +463,28 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
         } else {
             esc[j] = 0;
         }
-        cnt[j] = popc64(esc[j]);
+        cnt[j] = __popc(esc[j]);
     }
-    uint32_t before[kBf16Chunks];
-    const uint32_t wave_total = wave_chunk_ranks<kBf16Chunks>(cnt, before);
+    uint32_t row_base[kBf16Chunks], row_total[kBf16Chunks], lane_before[kBf16Chunks];
+    const uint32_t wave_total = wave_chunk_ranks<kBf16Chunks>(cnt, row_base, row_total, lane_before);
     uint32_t tile_total;
     const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
     if (wave_total) {
         uint8_t *tstage = stage + tile * (3ull * kEncTile);
+        uint8_t *buf = seg_buf[wave];
 #pragma unroll
         for (int j = 0; j < kBf16Chunks; ++j) {
-            if (esc[j]) {
-                const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
-                stage_records(tstage, wave_before + before[j], esc[j], ex[j], (uint32_t)(c0 & 0xFFFFu));
+            const uint32_t pos0 = (uint32_t)((base + (uint64_t)(j * 64 + lane) * 8) & 0xFFFFu);
+            const uint32_t rank = wave_before + row_base[j];
+            if (row_total[j] <= kDirectRecords) {                      // wave-uniform
+                if (esc[j]) put_records(tstage, rank + lane_before[j], esc[j], ex_park[wave][j][lane], pos0);
+            } else {
+                const uint32_t g0 = 3 * rank;
+                if (esc[j])
+                    lds_put_records(buf, (g0 & 3) + 3 * lane_before[j], esc[j], ex_park[wave][j][lane], pos0);
+                wave_lds_fence();
+                flush_segment(buf, tstage, g0, 3 * row_total[j]);
+                wave_lds_fence();
             }
         }
     }
@@ -407,19 +494,21 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
 // ---------------------------------------------------------------------------
 // Kernel: FP8 E5M2 dense encode + escape staging (the page's FP8 extension,
 // Contributions item 4).  Same tiling as BF16; a lane holds two 32-element
-// chunks of its wave's row.
+// chunks of its wave's row.  A chunk row with many escapes is staged through
+// LDS as four segments of 16 lanes.
 // ---------------------------------------------------------------------------
 constexpr int kE5Chunks = 2;
 
 __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *__restrict__ in, uint64_t n,
-                                                                 uint8_t *__restrict__ out, uint64_t off_nib,
-                                                                 uint64_t off_sm, uint64_t sm_bytes,
-                                                                 Codebook4 cb,
-                                                                 uint32_t *__restrict__ tile_counts,
-                                                                 uint8_t *__restrict__ stage)
+                                                              uint8_t *__restrict__ out, uint64_t off_nib,
+                                                              uint64_t off_sm, uint64_t sm_bytes,
+                                                              Codebook4 cb,
+                                                              uint32_t *__restrict__ tile_counts,
+                                                              uint8_t *__restrict__ stage)
 {
     __shared__ uint32_t table32[64];
     __shared__ uint32_t wave_totals[kEncThreads / 64];
+    __shared__ __align__(16) uint8_t seg_buf[kEncThreads / 64][kSegBytes];
     const uint32_t lane = lane_id();
     const uint32_t wave = threadIdx.x / 64;
     const uint64_t tile = blockIdx.x;
@@ -443,7 +532,8 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
     build_encode_table(table32, cb, 32);
     __syncthreads();
     const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
-    uint64_t esc[kE5Chunks][4], ex[kE5Chunks][4];
+    uint32_t esc[kE5Chunks];
+    uint64_t ex[kE5Chunks][4];
     uint32_t cnt[kE5Chunks];
 #pragma unroll
     for (int j = 0; j < kE5Chunks; ++j) {
@@ -461,11 +551,11 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
             // last, partial chunk: missing elements get code 0, symbol 0 and
             // no escape; only the sign/mantissa bytes that hold data are stored
             const uint32_t valid = (uint32_t)(n - c0);
+            esc[j] &= (uint32_t)((1ull << valid) - 1);
             uint32_t nw[4] = {nib.x, nib.y, nib.z, nib.w};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int v = (int)valid - 8 * s;
-                esc[j][s] &= v >= 8 ? ~0ull : (v <= 0 ? 0ull : ((1ull << (8 * v)) - 1));
                 nw[s] &= v >= 8 ? 0xFFFFFFFFu : (v <= 0 ? 0u : (uint32_t)((1ull << (4 * v)) - 1));
             }
             *reinterpret_cast<uint4 *>(out + off_nib + c0 / 2) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
@@ -481,27 +571,51 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
             for (uint32_t i = 0; i < 12 && sm_start + i < sm_end; ++i)
                 out[sm_start + i] = (uint8_t)(sw[i / 4] >> (8 * (i & 3)));
         } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) esc[j][s] = 0;
+            esc[j] = 0;
         }
-        cnt[j] = popc64(esc[j][0]) + popc64(esc[j][1]) + popc64(esc[j][2]) + popc64(esc[j][3]);
+        cnt[j] = __popc(esc[j]);
     }
-    uint32_t before[kE5Chunks];
-    const uint32_t wave_total = wave_chunk_ranks<kE5Chunks>(cnt, before);
+    uint32_t row_base[kE5Chunks], row_total[kE5Chunks], lane_before[kE5Chunks];
+    const uint32_t wave_total = wave_chunk_ranks<kE5Chunks>(cnt, row_base, row_total, lane_before);
     uint32_t tile_total;
     const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
     if (wave_total) {
         uint8_t *tstage = stage + tile * (3ull * kEncTile);
+        uint8_t *buf = seg_buf[wave];
 #pragma unroll
         for (int j = 0; j < kE5Chunks; ++j) {
-            uint32_t rank = wave_before + before[j];
             const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+            const uint32_t rank = wave_before + row_base[j];
+            if (row_total[j] <= kDirectRecords) {                      // wave-uniform
+                if (cnt[j]) {
+                    uint32_t r = rank + lane_before[j];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                if (esc[j][s]) {
-                    stage_records(tstage, rank, esc[j][s], ex[j][s], (uint32_t)((c0 + 8 * s) & 0xFFFFu));
-                    rank += popc64(esc[j][s]);
+                    for (int s8 = 0; s8 < 4; ++s8) {
+                        const uint32_t m = (esc[j] >> (8 * s8)) & 0xFFu;
+                        put_records(tstage, r, m, ex[j][s8], (uint32_t)((c0 + 8 * s8) & 0xFFFFu));
+                        r += __popc(m);
+                    }
                 }
+                continue;
+            }
+            // four segments of 16 lanes x 32 elements
+#pragma unroll
+            for (uint32_t q4 = 0; q4 < 4; ++q4) {
+                const uint32_t seg_first = __builtin_amdgcn_readlane(lane_before[j], 16 * q4);
+                const uint32_t seg_end =
+                    q4 < 3 ? (uint32_t)__builtin_amdgcn_readlane(lane_before[j], 16 * (q4 + 1)) : row_total[j];
+                if (seg_end == seg_first) continue;                    // wave-uniform
+                const uint32_t g0 = 3 * (rank + seg_first);
+                if (lane / 16 == q4 && cnt[j]) {
+                    uint32_t off = (g0 & 3) + 3 * (lane_before[j] - seg_first);
+#pragma unroll
+                    for (int s8 = 0; s8 < 4; ++s8)
+                        off = lds_put_records(buf, off, (esc[j] >> (8 * s8)) & 0xFFu, ex[j][s8],
+                                              (uint32_t)((c0 + 8 * s8) & 0xFFFFu));
+                }
+                wave_lds_fence();
+                flush_segment(buf, tstage, g0, 3 * (seg_end - seg_first));
+                wave_lds_fence();
             }
         }
     }
@@ -646,13 +760,38 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
 }
 
 // ---------------------------------------------------------------------------
-// Kernel: escape compaction.  One wave per block: lanes 0..3 fetch the
-// block's four tile counts, lane 4 its escape offset; then the wave copies
-// each tile's staged records (3 bytes each) to out[off_esc + 3 * offset ...).
-// The destination is written with aligned dword stores built by
-// v_alignbyte_b32 from the staged words; the partial dwords at both ends
-// (shared with the neighbouring tiles) are written byte by byte.
+// Kernel: escape compaction.  One wave per block (four blocks per workgroup)
+// copies the staged records of the block's four tiles (3 bytes each) to
+// out[off_esc + 3 * offset ...), tile after tile.  The body of each copy is
+// written with 16-byte aligned dwordx4 stores assembled by v_alignbyte_b32
+// from five staged words; the unaligned bytes at both ends, whose dwords the
+// neighbouring tiles share, are written byte by byte.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void copy_records(const uint8_t *__restrict__ src, uint8_t *__restrict__ out,
+                                             uint64_t dst0, uint32_t len)
+{
+    const uint32_t lane = lane_id();
+    const uint64_t end = dst0 + len;
+    const uint64_t body_begin = std::min<uint64_t>((dst0 + 15) & ~uint64_t(15), end);
+    const uint64_t body_end = std::max<uint64_t>(end & ~uint64_t(15), body_begin);
+    const uint32_t head = (uint32_t)(body_begin - dst0);
+    if (lane < head) out[dst0 + lane] = src[lane];
+    const uint32_t *src32 = reinterpret_cast<const uint32_t *>(src);
+    const uint32_t chunks = (uint32_t)((body_end - body_begin) / 16);
+    const uint32_t sh = head & 3;
+#pragma unroll 4
+    for (uint32_t c = lane; c < chunks; c += 64) {
+        const uint32_t w0 = (head >> 2) + 4 * c;                 // first source word
+        const uint32_t a0 = src32[w0], a1 = src32[w0 + 1], a2 = src32[w0 + 2], a3 = src32[w0 + 3],
+                       a4 = src32[w0 + 4];
+        const uint4 v = make_uint4(__builtin_amdgcn_alignbyte(a1, a0, sh), __builtin_amdgcn_alignbyte(a2, a1, sh),
+                                   __builtin_amdgcn_alignbyte(a3, a2, sh), __builtin_amdgcn_alignbyte(a4, a3, sh));
+        *reinterpret_cast<uint4 *>(out + body_begin + 16ull * c) = v;
+    }
+    const uint32_t tail_src = (uint32_t)(body_end - dst0);
+    if (body_end + lane < end) out[body_end + lane] = src[tail_src + lane];
+}
+
 __global__ __launch_bounds__(kCompactThreads) void sz_enc_compact(
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
     const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
@@ -661,37 +800,17 @@ __global__ __launch_bounds__(kCompactThreads) void sz_enc_compact(
     const uint64_t b = (uint64_t)blockIdx.x * (kCompactThreads / 64) + threadIdx.x / 64;
     if (b >= nb) return;
     const uint32_t lane = lane_id();
+    // lanes 0..3 fetch the tile counts, lane 4 the block's escape offset
+    const uint64_t t0 = kTilesPerBlock * b;
     uint64_t meta = 0;
-    if (lane < kTilesPerBlock && kTilesPerBlock * b + lane < nt) meta = tile_counts[kTilesPerBlock * b + lane];
+    if (lane < kTilesPerBlock && t0 + lane < nt) meta = tile_counts[t0 + lane];
     else if (lane == kTilesPerBlock) meta = block_offsets[b];
-    const uint32_t m = (uint32_t)meta;
-    uint32_t cnt[kTilesPerBlock];
-#pragma unroll
-    for (uint32_t t = 0; t < kTilesPerBlock; ++t) cnt[t] = __builtin_amdgcn_readlane(m, t);
     uint64_t off = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(meta >> 32), kTilesPerBlock) << 32) |
-                   (uint32_t)__builtin_amdgcn_readlane(m, kTilesPerBlock);
+                   (uint32_t)__builtin_amdgcn_readlane((uint32_t)meta, kTilesPerBlock);
 #pragma unroll
     for (uint32_t t = 0; t < kTilesPerBlock; ++t) {
-        const uint32_t k = cnt[t];
-        if (k) {
-            const uint64_t tile = kTilesPerBlock * b + t;
-            const uint8_t *src = stage + tile * (3ull * kEncTile);
-            const uint32_t *src32 = reinterpret_cast<const uint32_t *>(src);
-            const uint64_t dst0 = off_esc + 3 * off;
-            const uint64_t end = dst0 + 3ull * k;
-            const uint64_t head_end = std::min<uint64_t>((dst0 + 3) & ~uint64_t(3), end);
-            const uint64_t body_end = std::max<uint64_t>(end & ~uint64_t(3), head_end);
-            if (dst0 + lane < head_end) out[dst0 + lane] = src[lane];
-            const uint64_t body_words = (body_end - head_end) / 4;
-            const uint32_t s_first = (uint32_t)(head_end - dst0);
-            for (uint64_t w = lane; w < body_words; w += 64) {
-                const uint32_t s = s_first + 4 * (uint32_t)w;
-                const uint32_t lo = src32[s >> 2];
-                const uint32_t hi = src32[(s >> 2) + 1];
-                *reinterpret_cast<uint32_t *>(out + head_end + 4 * w) = __builtin_amdgcn_alignbyte(hi, lo, s & 3);
-            }
-            if (body_end + lane < end) out[body_end + lane] = src[body_end - dst0 + lane];
-        }
+        const uint32_t k = __builtin_amdgcn_readlane((uint32_t)meta, t);
+        if (k) copy_records(stage + (t0 + t) * (3ull * kEncTile), out, off_esc + 3 * off, 3 * k);
         off += k;
     }
 }
@@ -858,6 +977,100 @@ __device__ __forceinline__ void patch_bf16(uint4 &o, uint32_t k, uint32_t e)
     }
 }
 
+// Blocks with many escapes skip the LDS map: the dense values are stored
+// first, then every record is applied on its own (consecutive lanes take
+// consecutive records, so the record reads, the sign/mantissa re-reads and
+// the patch stores are all nearly contiguous).  The dense stores of the
+// workgroup precede the patch stores: all its waves run on one CU and the
+// barrier in between orders their issue.
+constexpr uint32_t kMappedEscapes = 8192;
+
+// Four consecutive records from one 16-byte window of aligned words.  The
+// window never leaves the record section: it starts at most 3 bytes before
+// record R and ends at most 3 bytes after record R+3, and callers use it only
+// while a whole record group past R+3 remains in the stream (otherwise they
+// read the records byte by byte).
+__device__ __forceinline__ void read_records4(const uint8_t *esc, uint64_t r, uint32_t pos[4], uint32_t e[4])
+{
+    const uint64_t byte0 = 3 * r;
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(esc + (byte0 & ~uint64_t(3)));
+    const uint32_t sh = (uint32_t)(byte0 & 3);
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+    const uint32_t d0 = __builtin_amdgcn_alignbyte(w1, w0, sh);   // bytes 0..3 of the 12
+    const uint32_t d1 = __builtin_amdgcn_alignbyte(w2, w1, sh);   // bytes 4..7
+    const uint32_t d2 = __builtin_amdgcn_alignbyte(w3, w2, sh);   // bytes 8..11
+    pos[0] = d0 & 0xFFFFu;
+    e[0] = (d0 >> 16) & 0xFFu;
+    pos[1] = (d0 >> 24) | ((d1 & 0xFFu) << 8);
+    e[1] = (d1 >> 8) & 0xFFu;
+    pos[2] = d1 >> 16;
+    e[2] = d2 & 0xFFu;
+    pos[3] = (d2 >> 8) & 0xFFFFu;
+    e[3] = d2 >> 24;
+}
+
+template <int DT>
+__device__ __forceinline__ void scatter_patch(const uint8_t *__restrict__ in, const DecodeArgs &a, uint64_t e0,
+                                              uint64_t r0, uint32_t k, uint32_t blen, void *__restrict__ out,
+                                              int32_t *__restrict__ status)
+{
+    const uint8_t *esc = in + a.off_esc;
+    const uint32_t lane = lane_id();
+    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
+    bool bad = false;
+    // thread t takes records 4t..4t+3 of each group of 4 * blockDim.x
+    for (uint32_t r = 4 * threadIdx.x; r < k; r += 4 * blockDim.x) {
+        uint32_t pos[4], e[4];
+        const uint32_t cnt = std::min<uint32_t>(4, k - r);
+        if (r0 + r + 5 < e_total) {
+            read_records4(esc, r0 + r, pos, e);
+        } else {
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q) {
+                pos[q] = 0xFFFFFFFFu;
+                e[q] = 0;
+                if (q < cnt) read_record(esc, r0 + r + q, pos[q], e[q]);
+            }
+        }
+        uint32_t prev = __shfl_up(pos[3], 1, 64);        // lane l-1 holds records r-4..r-1
+        if (lane == 0 && r > 0) {
+            uint32_t pe;
+            read_record(esc, r0 + r - 1, prev, pe);
+        }
+        uint32_t sm[4];
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q) {
+            const bool ok = q < cnt && pos[q] < blen && e[q] < a.symbols &&
+                            ((r + q == 0) || pos[q] > (q == 0 ? prev : pos[q - 1]));
+            if (q < cnt && !ok) bad = true;
+            if (!ok) pos[q] = 0xFFFFFFFFu;
+            sm[q] = 0;
+            if (pos[q] != 0xFFFFFFFFu) {
+                const uint64_t i = e0 + pos[q];
+                if (DT == SZ_BF16) {
+                    sm[q] = in[a.off_sm + i];
+                } else {
+                    const uint64_t bit = 3 * i;
+                    uint32_t v = in[a.off_sm + (bit >> 3)];
+                    if ((bit & 7) > 5) v |= (uint32_t)in[a.off_sm + (bit >> 3) + 1] << 8;
+                    sm[q] = (v >> (bit & 7)) & 7u;
+                }
+            }
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q) {
+            if (pos[q] == 0xFFFFFFFFu) continue;
+            const uint64_t i = e0 + pos[q];
+            if (DT == SZ_BF16)
+                reinterpret_cast<uint16_t *>(out)[i] =
+                    (uint16_t)(((sm[q] & 0x80u) << 8) | (e[q] << 7) | (sm[q] & 0x7Fu));
+            else
+                reinterpret_cast<uint8_t *>(out)[i] = (uint8_t)(((sm[q] & 4u) << 5) | (e[q] << 2) | (sm[q] & 3u));
+        }
+    }
+    if (bad) atomicExch(status, SZ_E_FORMAT);
+}
+
 __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__restrict__ in, DecodeArgs a,
                                                            const uint64_t *__restrict__ block_offsets,
                                                            int32_t *__restrict__ status,
@@ -899,16 +1112,17 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
             sm[j] = make_uint2(0, 0);
         }
     }
-    if (k) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+    const bool mapped = k != 0 && k <= kMappedEscapes;          // workgroup-uniform
+    if (mapped) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
     __syncthreads();
-    if (k) map_block_escapes<3>(esc, r0, k, blen, 256, first, status);
+    if (mapped) map_block_escapes<3>(esc, r0, k, blen, 256, first, status);
     __syncthreads();
-    if (rbase >= blen) return;
 #pragma unroll
     for (int j = 0; j < kBf16Chunks; ++j) {
         const uint32_t c = rbase + (j * 64 + lane) * 8;
+        if (c >= blen) continue;
         uint4 o = decode_chunk_bf16(nib[j], sm[j], table);
-        if (k) {
+        if (mapped) {
             uint32_t r = first[c >> 3];
             if (r != kNoEscape) {
                 for (; r < k; ++r) {
@@ -921,11 +1135,16 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
         }
         const uint64_t g = e0 + c;
         if (full_row || c + 8 <= blen) {
-            store_nt(reinterpret_cast<uint4 *>(out + g), o);
-        } else if (c < blen) {
+            if (k <= kMappedEscapes) store_nt(reinterpret_cast<uint4 *>(out + g), o);
+            else *reinterpret_cast<uint4 *>(out + g) = o;       // patched again right after
+        } else {
             const uint32_t w[4] = {o.x, o.y, o.z, o.w};
             for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
         }
+    }
+    if (k > kMappedEscapes) {
+        __syncthreads();
+        scatter_patch<SZ_BF16>(in, a, e0, r0, k, blen, out, status);
     }
 }
 
@@ -1006,17 +1225,18 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
             sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
         }
     }
-    if (k && tid < kBlock / 32 / 8) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+    const bool mapped = k != 0 && k <= kMappedEscapes;          // workgroup-uniform
+    if (mapped && tid < kBlock / 32 / 8) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
     __syncthreads();
-    if (k) map_block_escapes<5>(esc, r0, k, blen, 32, first, status);
+    if (mapped) map_block_escapes<5>(esc, r0, k, blen, 32, first, status);
     __syncthreads();
-    if (rbase >= blen) return;
 #pragma unroll
     for (int j = 0; j < kE5Chunks; ++j) {
         const uint32_t c = rbase + (j * 64 + lane) * 32;
+        if (c >= blen) continue;
         uint32_t o[8];
         decode_chunk_e5m2(nib[j], sm3[j], table, o);
-        if (k) {
+        if (mapped) {
             uint32_t r = first[c >> 5];
             if (r != kNoEscape) {
                 for (; r < k; ++r) {
@@ -1034,11 +1254,20 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
         }
         const uint64_t g = e0 + c;
         if (full_row || c + 32 <= blen) {
-            store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
-            store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
-        } else if (c < blen) {
+            if (k <= kMappedEscapes) {
+                store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
+                store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
+            } else {
+                *reinterpret_cast<uint4 *>(out + g) = make_uint4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<uint4 *>(out + g + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+            }
+        } else {
             for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint8_t)(o[i / 4] >> (8 * (i & 3)));
         }
+    }
+    if (k > kMappedEscapes) {
+        __syncthreads();
+        scatter_patch<SZ_FP8_E5M2>(in, a, e0, r0, k, blen, out, status);
     }
 }
 
