@@ -767,20 +767,21 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
 // from five staged words; the unaligned bytes at both ends, whose dwords the
 // neighbouring tiles share, are written byte by byte.
 // ---------------------------------------------------------------------------
+// Copies len bytes of staged records to out[dst0, dst0 + len) with the lanes
+// [0, width) of a lane group (lane = index inside the group).
 __device__ __forceinline__ void copy_records(const uint8_t *__restrict__ src, uint8_t *__restrict__ out,
-                                             uint64_t dst0, uint32_t len)
+                                             uint64_t dst0, uint32_t len, uint32_t lane, uint32_t width)
 {
-    const uint32_t lane = lane_id();
     const uint64_t end = dst0 + len;
     const uint64_t body_begin = std::min<uint64_t>((dst0 + 15) & ~uint64_t(15), end);
     const uint64_t body_end = std::max<uint64_t>(end & ~uint64_t(15), body_begin);
     const uint32_t head = (uint32_t)(body_begin - dst0);
-    if (lane < head) out[dst0 + lane] = src[lane];
+    for (uint32_t i = lane; i < head; i += width) out[dst0 + i] = src[i];
     const uint32_t *src32 = reinterpret_cast<const uint32_t *>(src);
     const uint32_t chunks = (uint32_t)((body_end - body_begin) / 16);
     const uint32_t sh = head & 3;
 #pragma unroll 4
-    for (uint32_t c = lane; c < chunks; c += 64) {
+    for (uint32_t c = lane; c < chunks; c += width) {
         const uint32_t w0 = (head >> 2) + 4 * c;                 // first source word
         const uint32_t a0 = src32[w0], a1 = src32[w0 + 1], a2 = src32[w0 + 2], a3 = src32[w0 + 3],
                        a4 = src32[w0 + 4];
@@ -789,8 +790,13 @@ __device__ __forceinline__ void copy_records(const uint8_t *__restrict__ src, ui
         *reinterpret_cast<uint4 *>(out + body_begin + 16ull * c) = v;
     }
     const uint32_t tail_src = (uint32_t)(body_end - dst0);
-    if (body_end + lane < end) out[body_end + lane] = src[tail_src + lane];
+    for (uint32_t i = lane; body_end + i < end; i += width) out[body_end + i] = src[tail_src + i];
 }
+
+// Tiles with at most this many records are copied by 16-lane groups, the
+// block's four tiles at once; heavier blocks copy tile after tile with the
+// whole wave.
+constexpr uint32_t kGroupCopyRecords = 1024;
 
 __global__ __launch_bounds__(kCompactThreads) void sz_enc_compact(
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
@@ -805,13 +811,32 @@ __global__ __launch_bounds__(kCompactThreads) void sz_enc_compact(
     uint64_t meta = 0;
     if (lane < kTilesPerBlock && t0 + lane < nt) meta = tile_counts[t0 + lane];
     else if (lane == kTilesPerBlock) meta = block_offsets[b];
-    uint64_t off = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(meta >> 32), kTilesPerBlock) << 32) |
-                   (uint32_t)__builtin_amdgcn_readlane((uint32_t)meta, kTilesPerBlock);
+    const uint64_t off = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(meta >> 32), kTilesPerBlock) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((uint32_t)meta, kTilesPerBlock);
+    uint32_t cnt[kTilesPerBlock], before[kTilesPerBlock], most = 0, run = 0;
 #pragma unroll
     for (uint32_t t = 0; t < kTilesPerBlock; ++t) {
-        const uint32_t k = __builtin_amdgcn_readlane((uint32_t)meta, t);
-        if (k) copy_records(stage + (t0 + t) * (3ull * kEncTile), out, off_esc + 3 * off, 3 * k);
-        off += k;
+        cnt[t] = __builtin_amdgcn_readlane((uint32_t)meta, t);
+        before[t] = run;
+        run += cnt[t];
+        most = std::max(most, cnt[t]);
+    }
+    if (most <= kGroupCopyRecords) {                               // wave-uniform
+        const uint32_t g = lane >> 4;
+        uint32_t k = 0, bef = 0;
+#pragma unroll
+        for (uint32_t t = 0; t < kTilesPerBlock; ++t)
+            if (g == t) {
+                k = cnt[t];
+                bef = before[t];
+            }
+        if (k) copy_records(stage + (t0 + g) * (3ull * kEncTile), out, off_esc + 3 * (off + bef), 3 * k, lane & 15, 16);
+    } else {
+#pragma unroll
+        for (uint32_t t = 0; t < kTilesPerBlock; ++t)
+            if (cnt[t])
+                copy_records(stage + (t0 + t) * (3ull * kEncTile), out, off_esc + 3 * (off + before[t]), 3 * cnt[t],
+                             lane, 64);
     }
 }
 
@@ -918,6 +943,9 @@ __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__res
 // and stores once.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kNoEscape = 0xFFFFu;
+// Blocks with up to this many escapes decode through an LDS map of their
+// records; blocks with more patch after the dense store (scatter_patch).
+constexpr uint32_t kMappedEscapes = 8192;
 
 // Escape record r of the stream: position and exponent.
 __device__ __forceinline__ void read_record(const uint8_t *esc, uint64_t r, uint32_t &pos, uint32_t &e)
@@ -927,23 +955,65 @@ __device__ __forceinline__ void read_record(const uint8_t *esc, uint64_t r, uint
     e = p[2];
 }
 
-// Builds first[chunk] for the k records of a block (chunk = pos >> log2_chunk)
-// and reports malformed records through the status word.
+// Four consecutive records from one 16-byte window of aligned words.  The
+// window never leaves the record section: it starts at most 3 bytes before
+// record R and ends at most 3 bytes after record R+3, and callers use it only
+// while a whole record group past R+3 remains in the stream (otherwise they
+// read the records byte by byte).
+__device__ __forceinline__ void read_records4(const uint8_t *esc, uint64_t r, uint32_t pos[4], uint32_t e[4])
+{
+    const uint64_t byte0 = 3 * r;
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(esc + (byte0 & ~uint64_t(3)));
+    const uint32_t sh = (uint32_t)(byte0 & 3);
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+    const uint32_t d0 = __builtin_amdgcn_alignbyte(w1, w0, sh);   // bytes 0..3 of the 12
+    const uint32_t d1 = __builtin_amdgcn_alignbyte(w2, w1, sh);   // bytes 4..7
+    const uint32_t d2 = __builtin_amdgcn_alignbyte(w3, w2, sh);   // bytes 8..11
+    pos[0] = d0 & 0xFFFFu;
+    e[0] = (d0 >> 16) & 0xFFu;
+    pos[1] = (d0 >> 24) | ((d1 & 0xFFu) << 8);
+    e[1] = (d1 >> 8) & 0xFFu;
+    pos[2] = d1 >> 16;
+    e[2] = d2 & 0xFFu;
+    pos[3] = (d2 >> 8) & 0xFFFFu;
+    e[3] = d2 >> 24;
+}
+
+// Loads the k (<= kMappedEscapes) records of a block into LDS as
+// pos | exponent << 16, four records per aligned three-word window where the
+// window stays inside the record section, one by one at its end.
+__device__ __forceinline__ void load_block_records(const uint8_t *esc, uint64_t r0, uint32_t k, uint64_t e_total,
+                                                   uint32_t *rec)
+{
+    for (uint32_t r = 4 * threadIdx.x; r < k; r += 4 * blockDim.x) {
+        uint32_t pos[4], e[4];
+        if (r0 + r + 5 < e_total) {
+            read_records4(esc, r0 + r, pos, e);
+        } else {
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q) {
+                pos[q] = e[q] = 0;
+                if (r + q < k) read_record(esc, r0 + r + q, pos[q], e[q]);
+            }
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q)
+            if (r + q < k) rec[r + q] = pos[q] | (e[q] << 16);
+    }
+}
+
+// Builds first[chunk] for the k records of a block held in LDS (chunk =
+// pos >> log2_chunk) and reports malformed records through the status word.
 template <int LOG2_CHUNK>
-__device__ __forceinline__ void map_block_escapes(const uint8_t *esc, uint64_t r0, uint32_t k, uint32_t blen,
-                                                  uint32_t symbols, uint16_t *first, int32_t *status)
+__device__ __forceinline__ void map_block_escapes(const uint32_t *rec, uint32_t k, uint32_t blen, uint32_t symbols,
+                                                  uint16_t *first, int32_t *status)
 {
     bool bad = false;
     for (uint32_t r = threadIdx.x; r < k; r += blockDim.x) {
-        uint32_t pos, e;
-        read_record(esc, r0 + r, pos, e);
-        int32_t prev = -1;
-        if (r > 0) {
-            uint32_t pp, pe;
-            read_record(esc, r0 + r - 1, pp, pe);
-            prev = (int32_t)pp;
-        }
-        if (pos >= blen || (int32_t)pos <= prev || e >= symbols) {
+        const uint32_t v = rec[r];
+        const uint32_t pos = v & 0xFFFFu;
+        const int32_t prev = r > 0 ? (int32_t)(rec[r - 1] & 0xFFFFu) : -1;
+        if (pos >= blen || (int32_t)pos <= prev || (v >> 16) >= symbols) {
             bad = true;
             continue;
         }
@@ -983,31 +1053,6 @@ __device__ __forceinline__ void patch_bf16(uint4 &o, uint32_t k, uint32_t e)
 // the patch stores are all nearly contiguous).  The dense stores of the
 // workgroup precede the patch stores: all its waves run on one CU and the
 // barrier in between orders their issue.
-constexpr uint32_t kMappedEscapes = 8192;
-
-// Four consecutive records from one 16-byte window of aligned words.  The
-// window never leaves the record section: it starts at most 3 bytes before
-// record R and ends at most 3 bytes after record R+3, and callers use it only
-// while a whole record group past R+3 remains in the stream (otherwise they
-// read the records byte by byte).
-__device__ __forceinline__ void read_records4(const uint8_t *esc, uint64_t r, uint32_t pos[4], uint32_t e[4])
-{
-    const uint64_t byte0 = 3 * r;
-    const uint32_t *w = reinterpret_cast<const uint32_t *>(esc + (byte0 & ~uint64_t(3)));
-    const uint32_t sh = (uint32_t)(byte0 & 3);
-    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
-    const uint32_t d0 = __builtin_amdgcn_alignbyte(w1, w0, sh);   // bytes 0..3 of the 12
-    const uint32_t d1 = __builtin_amdgcn_alignbyte(w2, w1, sh);   // bytes 4..7
-    const uint32_t d2 = __builtin_amdgcn_alignbyte(w3, w2, sh);   // bytes 8..11
-    pos[0] = d0 & 0xFFFFu;
-    e[0] = (d0 >> 16) & 0xFFu;
-    pos[1] = (d0 >> 24) | ((d1 & 0xFFu) << 8);
-    e[1] = (d1 >> 8) & 0xFFu;
-    pos[2] = d1 >> 16;
-    e[2] = d2 & 0xFFu;
-    pos[3] = (d2 >> 8) & 0xFFFFu;
-    e[3] = d2 >> 24;
-}
 
 template <int DT>
 __device__ __forceinline__ void scatter_patch(const uint8_t *__restrict__ in, const DecodeArgs &a, uint64_t e0,
@@ -1078,6 +1123,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
 {
     __shared__ uint32_t table[256];
     __shared__ uint16_t first[kBlock / 8];     // first escape record of each 8-element chunk
+    __shared__ uint32_t rec[kMappedEscapes];   // the block's records: pos | exponent << 16
     if (status[1] != 0) return;
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x;
@@ -1113,9 +1159,12 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
         }
     }
     const bool mapped = k != 0 && k <= kMappedEscapes;          // workgroup-uniform
-    if (mapped) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+    if (mapped) {
+        reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+        load_block_records(esc, r0, k, *reinterpret_cast<const uint64_t *>(in + 16), rec);
+    }
     __syncthreads();
-    if (mapped) map_block_escapes<3>(esc, r0, k, blen, 256, first, status);
+    if (mapped) map_block_escapes<3>(rec, k, blen, 256, first, status);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kBf16Chunks; ++j) {
@@ -1126,10 +1175,9 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
             uint32_t r = first[c >> 3];
             if (r != kNoEscape) {
                 for (; r < k; ++r) {
-                    uint32_t pos, e;
-                    read_record(esc, r0 + r, pos, e);
-                    if ((pos >> 3) != (c >> 3)) break;
-                    patch_bf16(o, pos & 7, e);
+                    const uint32_t v = rec[r];
+                    if (((v & 0xFFFFu) >> 3) != (c >> 3)) break;
+                    patch_bf16(o, v & 7, v >> 16);
                 }
             }
         }
@@ -1183,6 +1231,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
 {
     __shared__ uint16_t table[256];
     __shared__ uint16_t first[kBlock / 32];    // first escape record of each 32-element chunk
+    __shared__ uint32_t rec[kMappedEscapes];   // the block's records: pos | exponent << 16
     if (status[1] != 0) return;
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x;
@@ -1226,9 +1275,12 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
         }
     }
     const bool mapped = k != 0 && k <= kMappedEscapes;          // workgroup-uniform
-    if (mapped && tid < kBlock / 32 / 8) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+    if (mapped) {
+        if (tid < kBlock / 32 / 8) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+        load_block_records(esc, r0, k, *reinterpret_cast<const uint64_t *>(in + 16), rec);
+    }
     __syncthreads();
-    if (mapped) map_block_escapes<5>(esc, r0, k, blen, 32, first, status);
+    if (mapped) map_block_escapes<5>(rec, k, blen, 32, first, status);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kE5Chunks; ++j) {
@@ -1240,8 +1292,8 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
             uint32_t r = first[c >> 5];
             if (r != kNoEscape) {
                 for (; r < k; ++r) {
-                    uint32_t pos, e;
-                    read_record(esc, r0 + r, pos, e);
+                    const uint32_t v = rec[r];
+                    const uint32_t pos = v & 0xFFFFu, e = v >> 16;
                     if ((pos >> 5) != (c >> 5)) break;
                     const uint32_t p = pos & 31;
                     const uint32_t sh = 8 * (p & 3) + 2;
