@@ -944,7 +944,7 @@ __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__res
 // ---------------------------------------------------------------------------
 constexpr uint32_t kNoEscape = 0xFFFFu;
 // Blocks with up to this many escapes decode through an LDS map of their
-// records; blocks with more patch after the dense store (scatter_patch).
+// records; blocks with more go through the exponent plane.
 constexpr uint32_t kMappedEscapes = 8192;
 
 // Escape record r of the stream: position and exponent.
@@ -1047,23 +1047,43 @@ __device__ __forceinline__ void patch_bf16(uint4 &o, uint32_t k, uint32_t e)
     }
 }
 
-// Blocks with many escapes skip the LDS map: the dense values are stored
-// first, then every record is applied on its own (consecutive lanes take
-// consecutive records, so the record reads, the sign/mantissa re-reads and
-// the patch stores are all nearly contiguous).  The dense stores of the
-// workgroup precede the patch stores: all its waves run on one CU and the
-// barrier in between orders their issue.
+// Blocks with more than kMappedEscapes escapes decode through an exponent
+// plane: every element's dense exponent goes to a 64 KB LDS byte array, the
+// block's records overwrite their entries (validated on the way), and the
+// values are rebuilt from the plane and stored once.
 
-template <int DT>
-__device__ __forceinline__ void scatter_patch(const uint8_t *__restrict__ in, const DecodeArgs &a, uint64_t e0,
-                                              uint64_t r0, uint32_t k, uint32_t blen, void *__restrict__ out,
-                                              int32_t *__restrict__ status)
+// Register code -> exponent lookup for the eight codes of a code word d
+// (element 2k in the low nibble of byte k); cb0..cb3 = codebook bytes.
+// v_perm_b32 indexes eight bytes, so each half of the book is one v_perm and
+// bit 3 of every code picks the half through a byte mask that v_perm's
+// sign-replication selectors build (8: bit 15 of the low word, 9: bit 31 of
+// the low word, 10/11: the same bits of the high word).  Returns the eight
+// exponents in element order (bytes 0..3 then 4..7).
+struct CodebookRegs {
+    uint32_t w0, w1, w2, w3;
+};
+
+__device__ __forceinline__ uint2 lookup_codes8(uint32_t d, const CodebookRegs &cb)
 {
-    const uint8_t *esc = in + a.off_esc;
+    const uint32_t sel_e = d & 0x07070707u;
+    const uint32_t sel_o = (d >> 4) & 0x07070707u;
+    const uint32_t m_e = perm(d << 4, d << 12, 0x0B090A08u);      // bit 3 of the even codes
+    const uint32_t m_o = perm(d, d << 8, 0x0B090A08u);            // bit 3 of the odd codes
+    const uint32_t e_even = (perm(cb.w3, cb.w2, sel_e) & m_e) | (perm(cb.w1, cb.w0, sel_e) & ~m_e);
+    const uint32_t e_odd = (perm(cb.w3, cb.w2, sel_o) & m_o) | (perm(cb.w1, cb.w0, sel_o) & ~m_o);
+    return make_uint2(perm(e_odd, e_even, 0x05010400u), perm(e_odd, e_even, 0x07030602u));
+}
+
+// Overwrites plane[pos] with the exponent of each of the block's k records,
+// four records per aligned three-word window; invalid records (position out
+// of the block or not ascending, exponent out of range) are skipped and
+// reported through the status word.
+__device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ esc, uint64_t r0, uint32_t k,
+                                                    uint32_t blen, uint32_t symbols, uint64_t e_total,
+                                                    uint8_t *plane, int32_t *__restrict__ status)
+{
     const uint32_t lane = lane_id();
-    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
     bool bad = false;
-    // thread t takes records 4t..4t+3 of each group of 4 * blockDim.x
     for (uint32_t r = 4 * threadIdx.x; r < k; r += 4 * blockDim.x) {
         uint32_t pos[4], e[4];
         const uint32_t cnt = std::min<uint32_t>(4, k - r);
@@ -1082,35 +1102,12 @@ __device__ __forceinline__ void scatter_patch(const uint8_t *__restrict__ in, co
             uint32_t pe;
             read_record(esc, r0 + r - 1, prev, pe);
         }
-        uint32_t sm[4];
 #pragma unroll
         for (uint32_t q = 0; q < 4; ++q) {
-            const bool ok = q < cnt && pos[q] < blen && e[q] < a.symbols &&
-                            ((r + q == 0) || pos[q] > (q == 0 ? prev : pos[q - 1]));
-            if (q < cnt && !ok) bad = true;
-            if (!ok) pos[q] = 0xFFFFFFFFu;
-            sm[q] = 0;
-            if (pos[q] != 0xFFFFFFFFu) {
-                const uint64_t i = e0 + pos[q];
-                if (DT == SZ_BF16) {
-                    sm[q] = in[a.off_sm + i];
-                } else {
-                    const uint64_t bit = 3 * i;
-                    uint32_t v = in[a.off_sm + (bit >> 3)];
-                    if ((bit & 7) > 5) v |= (uint32_t)in[a.off_sm + (bit >> 3) + 1] << 8;
-                    sm[q] = (v >> (bit & 7)) & 7u;
-                }
-            }
-        }
-#pragma unroll
-        for (uint32_t q = 0; q < 4; ++q) {
-            if (pos[q] == 0xFFFFFFFFu) continue;
-            const uint64_t i = e0 + pos[q];
-            if (DT == SZ_BF16)
-                reinterpret_cast<uint16_t *>(out)[i] =
-                    (uint16_t)(((sm[q] & 0x80u) << 8) | (e[q] << 7) | (sm[q] & 0x7Fu));
-            else
-                reinterpret_cast<uint8_t *>(out)[i] = (uint8_t)(((sm[q] & 4u) << 5) | (e[q] << 2) | (sm[q] & 3u));
+            if (q >= cnt) continue;
+            const uint32_t before = q == 0 ? prev : pos[q - 1];
+            if (pos[q] < blen && e[q] < symbols && (r + q == 0 || pos[q] > before)) plane[pos[q]] = (uint8_t)e[q];
+            else bad = true;
         }
     }
     if (bad) atomicExch(status, SZ_E_FORMAT);
@@ -1122,8 +1119,12 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
                                                            uint16_t *__restrict__ out)
 {
     __shared__ uint32_t table[256];
-    __shared__ uint16_t first[kBlock / 8];     // first escape record of each 8-element chunk
-    __shared__ uint32_t rec[kMappedEscapes];   // the block's records: pos | exponent << 16
+    // mapped blocks: first[] (first record of each 8-element chunk, 16 KB) and
+    // rec[] (the records, 32 KB); heavy blocks: the exponent plane (64 KB)
+    __shared__ __align__(16) uint8_t pool[kBlock];
+    uint16_t *first = reinterpret_cast<uint16_t *>(pool);
+    uint32_t *rec = reinterpret_cast<uint32_t *>(pool + kBlock / 4);
+    uint8_t *plane = pool;
     if (status[1] != 0) return;
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x;
@@ -1131,7 +1132,9 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
     const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
     const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
     const uint64_t r0 = block_offsets[b];
+    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
     const uint8_t *esc = in + a.off_esc;
+    const bool heavy = k > kMappedEscapes;                        // workgroup-uniform
     if (tid < 256) {
         const uint32_t lo = in[32 + (tid & 15)];
         const uint32_t hi = in[32 + (tid >> 4)];
@@ -1158,20 +1161,50 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
             sm[j] = make_uint2(0, 0);
         }
     }
-    const bool mapped = k != 0 && k <= kMappedEscapes;          // workgroup-uniform
-    if (mapped) {
+    if (heavy) {
+        const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
+        const CodebookRegs cb = {cbw[0], cbw[1], cbw[2], cbw[3]};
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            if (c < blen) *reinterpret_cast<uint2 *>(plane + c) = lookup_codes8(nib[j], cb);
+        }
+        __syncthreads();
+        overwrite_exponents(esc, r0, k, blen, 256, e_total, plane, status);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            if (c >= blen) continue;
+            const uint2 ex = *reinterpret_cast<const uint2 *>(plane + c);   // exponents, element order
+            uint4 o;
+            o.x = (perm(sm[j].x, sm[j].x, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C010C00u) << 7);
+            o.y = (perm(sm[j].x, sm[j].x, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C030C02u) << 7);
+            o.z = (perm(sm[j].y, sm[j].y, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C050C04u) << 7);
+            o.w = (perm(sm[j].y, sm[j].y, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C070C06u) << 7);
+            const uint64_t g = e0 + c;
+            if (full_row || c + 8 <= blen) {
+                store_nt(reinterpret_cast<uint4 *>(out + g), o);
+            } else {
+                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+            }
+        }
+        return;
+    }
+    if (k) {
         reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
-        load_block_records(esc, r0, k, *reinterpret_cast<const uint64_t *>(in + 16), rec);
+        load_block_records(esc, r0, k, e_total, rec);
     }
     __syncthreads();
-    if (mapped) map_block_escapes<3>(rec, k, blen, 256, first, status);
+    if (k) map_block_escapes<3>(rec, k, blen, 256, first, status);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kBf16Chunks; ++j) {
         const uint32_t c = rbase + (j * 64 + lane) * 8;
         if (c >= blen) continue;
         uint4 o = decode_chunk_bf16(nib[j], sm[j], table);
-        if (mapped) {
+        if (k) {
             uint32_t r = first[c >> 3];
             if (r != kNoEscape) {
                 for (; r < k; ++r) {
@@ -1183,16 +1216,11 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
         }
         const uint64_t g = e0 + c;
         if (full_row || c + 8 <= blen) {
-            if (k <= kMappedEscapes) store_nt(reinterpret_cast<uint4 *>(out + g), o);
-            else *reinterpret_cast<uint4 *>(out + g) = o;       // patched again right after
+            store_nt(reinterpret_cast<uint4 *>(out + g), o);
         } else {
             const uint32_t w[4] = {o.x, o.y, o.z, o.w};
             for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
         }
-    }
-    if (k > kMappedEscapes) {
-        __syncthreads();
-        scatter_patch<SZ_BF16>(in, a, e0, r0, k, blen, out, status);
     }
 }
 
@@ -1230,8 +1258,12 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
                                                            uint8_t *__restrict__ out)
 {
     __shared__ uint16_t table[256];
-    __shared__ uint16_t first[kBlock / 32];    // first escape record of each 32-element chunk
-    __shared__ uint32_t rec[kMappedEscapes];   // the block's records: pos | exponent << 16
+    // mapped blocks: first[] (first record of each 32-element chunk, 4 KB) and
+    // rec[] (the records, 32 KB); heavy blocks: the exponent plane (64 KB)
+    __shared__ __align__(16) uint8_t pool[kBlock];
+    uint16_t *first = reinterpret_cast<uint16_t *>(pool);
+    uint32_t *rec = reinterpret_cast<uint32_t *>(pool + kBlock / 16);
+    uint8_t *plane = pool;
     if (status[1] != 0) return;
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x;
@@ -1239,7 +1271,9 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
     const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
     const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
     const uint64_t r0 = block_offsets[b];
+    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
     const uint8_t *esc = in + a.off_esc;
+    const bool heavy = k > kMappedEscapes;                        // workgroup-uniform
     if (tid < 256) {
         const uint32_t lo = in[32 + (tid & 15)];
         const uint32_t hi = in[32 + (tid >> 4)];
@@ -1274,13 +1308,51 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
             sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
         }
     }
-    const bool mapped = k != 0 && k <= kMappedEscapes;          // workgroup-uniform
-    if (mapped) {
+    if (heavy) {
+        const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
+        const CodebookRegs cb = {cbw[0], cbw[1], cbw[2], cbw[3]};
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 32;
+            if (c >= blen) continue;
+            const uint32_t nw[4] = {nib[j].x, nib[j].y, nib[j].z, nib[j].w};
+#pragma unroll
+            for (int s8 = 0; s8 < 4; ++s8) *reinterpret_cast<uint2 *>(plane + c + 8 * s8) = lookup_codes8(nw[s8], cb);
+        }
+        __syncthreads();
+        overwrite_exponents(esc, r0, k, blen, 32, e_total, plane, status);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 32;
+            if (c >= blen) continue;
+            const uint32_t grp[4] = {sm3[j][0] & 0xFFFFFFu, (sm3[j][0] >> 24) | ((sm3[j][1] & 0xFFFFu) << 8),
+                                     (sm3[j][1] >> 16) | ((sm3[j][2] & 0xFFu) << 16), sm3[j][2] >> 8};
+            uint32_t o[8];
+#pragma unroll
+            for (int s8 = 0; s8 < 4; ++s8) {
+                const uint2 ex = *reinterpret_cast<const uint2 *>(plane + c + 8 * s8);
+                const uint32_t t_lo = unpack_sm3_x4(grp[s8] & 0xFFFu);
+                const uint32_t t_hi = unpack_sm3_x4(grp[s8] >> 12);
+                o[2 * s8] = ((t_lo & 0x04040404u) << 5) | (t_lo & 0x03030303u) | (ex.x << 2);
+                o[2 * s8 + 1] = ((t_hi & 0x04040404u) << 5) | (t_hi & 0x03030303u) | (ex.y << 2);
+            }
+            const uint64_t g = e0 + c;
+            if (full_row || c + 32 <= blen) {
+                store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
+                store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
+            } else {
+                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint8_t)(o[i / 4] >> (8 * (i & 3)));
+            }
+        }
+        return;
+    }
+    if (k) {
         if (tid < kBlock / 32 / 8) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
-        load_block_records(esc, r0, k, *reinterpret_cast<const uint64_t *>(in + 16), rec);
+        load_block_records(esc, r0, k, e_total, rec);
     }
     __syncthreads();
-    if (mapped) map_block_escapes<5>(rec, k, blen, 32, first, status);
+    if (k) map_block_escapes<5>(rec, k, blen, 32, first, status);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kE5Chunks; ++j) {
@@ -1288,7 +1360,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
         if (c >= blen) continue;
         uint32_t o[8];
         decode_chunk_e5m2(nib[j], sm3[j], table, o);
-        if (mapped) {
+        if (k) {
             uint32_t r = first[c >> 5];
             if (r != kNoEscape) {
                 for (; r < k; ++r) {
@@ -1306,20 +1378,11 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
         }
         const uint64_t g = e0 + c;
         if (full_row || c + 32 <= blen) {
-            if (k <= kMappedEscapes) {
-                store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
-                store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
-            } else {
-                *reinterpret_cast<uint4 *>(out + g) = make_uint4(o[0], o[1], o[2], o[3]);
-                *reinterpret_cast<uint4 *>(out + g + 16) = make_uint4(o[4], o[5], o[6], o[7]);
-            }
+            store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
+            store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
         } else {
             for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint8_t)(o[i / 4] >> (8 * (i & 3)));
         }
-    }
-    if (k > kMappedEscapes) {
-        __syncthreads();
-        scatter_patch<SZ_FP8_E5M2>(in, a, e0, r0, k, blen, out, status);
     }
 }
 

@@ -257,3 +257,37 @@ def test_e5m2_device_validation():
         want = oracle.validate(t, 1, n)
         _, ws = _decode_gpu(torch.from_numpy(t).cuda(), 1, n, check=False)
         assert int(ws[:4].cpu().view(torch.int32)[0]) == want == oracle.E_FORMAT, name
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_device_validation_heavy_blocks(dtype):
+    """Malformed records inside blocks with more escapes than the LDS map
+    holds (the exponent-plane decode path) are reported like the light ones."""
+    n = 65536 + 20000
+    rng = np.random.default_rng(11)
+    if dtype == 0:
+        e = rng.integers(16, 256, n).astype(np.uint16)
+        bits = ((rng.integers(0, 2, n).astype(np.uint16) << 15) | (e << 7) | rng.integers(0, 128, n).astype(np.uint16)).astype(np.uint16)
+    else:
+        e = rng.integers(16, 32, n).astype(np.uint8)
+        bits = ((rng.integers(0, 2, n).astype(np.uint8) << 7) | (e << 2) | rng.integers(0, 4, n).astype(np.uint8)).astype(np.uint8)
+    cb = np.arange(16, dtype=np.uint8)
+    good = oracle.encode(bits, dtype, cb)
+    assert streamfmt.sections(good)["counts"][0] > 8192
+    first = streamfmt.layout(dtype, n)["off_esc"]
+    second_block = first + 3 * 65536
+    cases = [("repeat", lambda t: t.__setitem__(slice(first + 3000, first + 3002), t[first + 2997:first + 2999].copy())),
+             ("descend", lambda t: t.__setitem__(slice(first + 3, first + 5), [0, 0])),
+             ("range_last_block", lambda t: t.__setitem__(slice(second_block + 3 * 19999, second_block + 3 * 19999 + 2), [0x30, 0x75]))]
+    if dtype == 1:
+        cases.append(("exp_range", lambda t: t.__setitem__(first + 3 * 500 + 2, 40)))
+    for name, mutate in cases:
+        t = good.copy()
+        mutate(t)
+        want = oracle.validate(t, dtype, n)
+        assert want == oracle.E_FORMAT, name
+        _, ws = _decode_gpu(torch.from_numpy(t).cuda(), dtype, n, check=False)
+        assert int(ws[:4].cpu().view(torch.int32)[0]) == want, name
+    out, ws = _decode_gpu(torch.from_numpy(good).cuda(), dtype, n, check=False)
+    assert int(ws[:4].cpu().view(torch.int32)[0]) == 0
+    assert np.array_equal(_bits_of(out, dtype, n), bits)
