@@ -1252,6 +1252,35 @@ __device__ __forceinline__ void decode_chunk_e5m2(const uint4 nib, const uint32_
     }
 }
 
+// E5M2 rows are decoded with lane 2m on chunk m and lane 2m+1 on chunk
+// 32 + m of each 64-chunk row, so that after the two lanes swap the half
+// (16 bytes) each one does not keep, each of the two stores of a row writes
+// 1 KB of contiguous output.
+__device__ __forceinline__ uint32_t e5m2_chunk_of_lane(uint32_t lane)
+{
+    return (lane & 1) ? 32 + (lane >> 1) : (lane >> 1);
+}
+
+__device__ __forceinline__ void store_chunk_pairs(uint8_t *row_out, const uint32_t o[8], uint32_t lane)
+{
+    const bool odd = lane & 1;
+    uint32_t keep[4], give[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        keep[i] = odd ? o[4 + i] : o[i];
+        give[i] = odd ? o[i] : o[4 + i];
+        give[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)give[i], 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    }
+    // even lanes: bytes [16l, 16l+16) of the first KB = their own low half;
+    // odd lanes: the same range = the partner's high half
+    const uint4 first_kb = odd ? make_uint4(give[0], give[1], give[2], give[3])
+                               : make_uint4(keep[0], keep[1], keep[2], keep[3]);
+    const uint4 second_kb = odd ? make_uint4(keep[0], keep[1], keep[2], keep[3])
+                                : make_uint4(give[0], give[1], give[2], give[3]);
+    store_nt(reinterpret_cast<uint4 *>(row_out + 16 * lane), first_kb);
+    store_nt(reinterpret_cast<uint4 *>(row_out + 1024 + 16 * lane), second_kb);
+}
+
 __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__restrict__ in, DecodeArgs a,
                                                            const uint64_t *__restrict__ block_offsets,
                                                            int32_t *__restrict__ status,
@@ -1289,7 +1318,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
     uint32_t sm3[kE5Chunks][3];
 #pragma unroll
     for (int j = 0; j < kE5Chunks; ++j) {
-        const uint32_t c = rbase + (j * 64 + lane) * 32;
+        const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
         const uint64_t g = e0 + c;
         if (full_row || c + 32 <= blen) {
             nib[j] = load_nt(reinterpret_cast<const uint4 *>(nib_base + g / 2));
@@ -1313,7 +1342,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
         const CodebookRegs cb = {cbw[0], cbw[1], cbw[2], cbw[3]};
 #pragma unroll
         for (int j = 0; j < kE5Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 32;
+            const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
             if (c >= blen) continue;
             const uint32_t nw[4] = {nib[j].x, nib[j].y, nib[j].z, nib[j].w};
 #pragma unroll
@@ -1324,7 +1353,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kE5Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 32;
+            const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
             if (c >= blen) continue;
             const uint32_t grp[4] = {sm3[j][0] & 0xFFFFFFu, (sm3[j][0] >> 24) | ((sm3[j][1] & 0xFFFFu) << 8),
                                      (sm3[j][1] >> 16) | ((sm3[j][2] & 0xFFu) << 16), sm3[j][2] >> 8};
@@ -1338,7 +1367,9 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
                 o[2 * s8 + 1] = ((t_hi & 0x04040404u) << 5) | (t_hi & 0x03030303u) | (ex.y << 2);
             }
             const uint64_t g = e0 + c;
-            if (full_row || c + 32 <= blen) {
+            if (full_row) {
+                store_chunk_pairs(out + e0 + rbase + j * 2048, o, lane);
+            } else if (c + 32 <= blen) {
                 store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
                 store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
             } else {
@@ -1356,7 +1387,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kE5Chunks; ++j) {
-        const uint32_t c = rbase + (j * 64 + lane) * 32;
+        const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
         if (c >= blen) continue;
         uint32_t o[8];
         decode_chunk_e5m2(nib[j], sm3[j], table, o);
@@ -1377,7 +1408,9 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
             }
         }
         const uint64_t g = e0 + c;
-        if (full_row || c + 32 <= blen) {
+        if (full_row) {
+            store_chunk_pairs(out + e0 + rbase + j * 2048, o, lane);
+        } else if (c + 32 <= blen) {
             store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
             store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
         } else {
