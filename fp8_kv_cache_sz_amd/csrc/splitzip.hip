@@ -345,6 +345,12 @@ __device__ __forceinline__ void put_records(uint8_t *tstage, uint32_t rank, uint
 
 // Rows with more escapes than this go through the LDS segment buffer.
 constexpr uint32_t kDirectRecords = 32;
+// Tiles with more escapes than this are not staged: the compaction kernel
+// derives their records again from the input, which moves 2 bytes per
+// element instead of writing and re-reading 3 bytes per escape.  Their tile
+// count carries kRederiveFlag.
+constexpr uint32_t kRederiveRecords = kEncTile / 4;
+constexpr uint32_t kRederiveFlag = 0x80000000u;
 
 // Per-chunk rank data of a wave row (J chunks per lane): row_base[j] = escapes
 // of the wave before chunk row j, row_total[j] = escapes in chunk row j (both
@@ -469,7 +475,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
     const uint32_t wave_total = wave_chunk_ranks<kBf16Chunks>(cnt, row_base, row_total, lane_before);
     uint32_t tile_total;
     const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
-    if (wave_total) {
+    if (wave_total && tile_total <= kRederiveRecords) {
         uint8_t *tstage = stage + tile * (3ull * kEncTile);
         uint8_t *buf = seg_buf[wave];
 #pragma unroll
@@ -488,7 +494,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
             }
         }
     }
-    if (threadIdx.x == 0) tile_counts[tile] = tile_total;
+    if (threadIdx.x == 0) tile_counts[tile] = tile_total | (tile_total > kRederiveRecords ? kRederiveFlag : 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -579,7 +585,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
     const uint32_t wave_total = wave_chunk_ranks<kE5Chunks>(cnt, row_base, row_total, lane_before);
     uint32_t tile_total;
     const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
-    if (wave_total) {
+    if (wave_total && tile_total <= kRederiveRecords) {
         uint8_t *tstage = stage + tile * (3ull * kEncTile);
         uint8_t *buf = seg_buf[wave];
 #pragma unroll
@@ -619,7 +625,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
             }
         }
     }
-    if (threadIdx.x == 0) tile_counts[tile] = tile_total;
+    if (threadIdx.x == 0) tile_counts[tile] = tile_total | (tile_total > kRederiveRecords ? kRederiveFlag : 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -717,7 +723,9 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
             if (b < nb) {
                 const uint4 v = *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b);
                 const uint32_t t = kTilesPerBlock * b;
-                x[i] = v.x + ((t + 1 < nt) ? v.y : 0) + ((t + 2 < nt) ? v.z : 0) + ((t + 3 < nt) ? v.w : 0);
+                const uint32_t m = ~kRederiveFlag;
+                x[i] = (v.x & m) + ((t + 1 < nt) ? v.y & m : 0) + ((t + 2 < nt) ? v.z & m : 0) +
+                       ((t + 3 < nt) ? v.w & m : 0);
             }
         }
         uint64_t base[kScanBatch];
@@ -793,16 +801,144 @@ __device__ __forceinline__ void copy_records(const uint8_t *__restrict__ src, ui
     for (uint32_t i = lane; body_end + i < end; i += width) out[body_end + i] = src[tail_src + i];
 }
 
+// Derives the records of an escape-heavy tile again from the input, with one
+// wave walking the tile's four rows, and writes them at their final place
+// (dst = aligned base, shift = byte misalignment of the tile's first record).
+// Half rows keep the re-derivation's register footprint close to the copy
+// path's, so both share one occupancy.
+constexpr int kRedChunks = 4;
+constexpr uint32_t kRedRow = kRedChunks * 64 * 8;
+
+__device__ __forceinline__ void rederive_tile_bf16(const uint16_t *__restrict__ in, uint64_t n, uint64_t tile,
+                                                   const uint8_t *table, uint8_t *buf, uint8_t *dst, uint32_t shift)
+{
+    const uint32_t lane = lane_id();
+    uint32_t rank = 0;                                          // wave-uniform
+    for (uint32_t row = 0; row < kEncTile / kRedRow; ++row) {
+        const uint64_t base = tile * kEncTile + (uint64_t)row * kRedRow;
+        if (base >= n) break;
+        const bool full_row = base + kRedRow <= n;
+        uint4 q[kRedChunks];
+#pragma unroll
+        for (int j = 0; j < kRedChunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+            if (full_row || c0 + 8 <= n) {
+                q[j] = load_nt(reinterpret_cast<const uint4 *>(in + c0));
+            } else {
+                uint16_t v[8];
+#pragma unroll
+                for (uint32_t k = 0; k < 8; ++k) v[k] = (c0 + k < n) ? in[c0 + k] : 0;
+                q[j] = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                                  v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
+            }
+        }
+        uint32_t esc[kRedChunks], cnt[kRedChunks];
+        uint64_t ex[kRedChunks];
+#pragma unroll
+        for (int j = 0; j < kRedChunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+            uint32_t nib;
+            uint2 sm;
+            encode_chunk_bf16(q[j], table, nib, sm, esc[j], ex[j]);
+            if (c0 >= n) esc[j] = 0;
+            else if (c0 + 8 > n) esc[j] &= (1u << (uint32_t)(n - c0)) - 1;
+            cnt[j] = __popc(esc[j]);
+        }
+        uint32_t row_base[kRedChunks], row_total[kRedChunks], lane_before[kRedChunks];
+        const uint32_t total = wave_chunk_ranks<kRedChunks>(cnt, row_base, row_total, lane_before);
+#pragma unroll
+        for (int j = 0; j < kRedChunks; ++j) {
+            if (row_total[j] == 0) continue;                    // wave-uniform
+            const uint32_t g0 = shift + 3 * (rank + row_base[j]);
+            const uint32_t pos0 = (uint32_t)((base + (uint64_t)(j * 64 + lane) * 8) & 0xFFFFu);
+            if (esc[j]) lds_put_records(buf, (g0 & 3) + 3 * lane_before[j], esc[j], ex[j], pos0);
+            wave_lds_fence();
+            flush_segment(buf, dst, g0, 3 * row_total[j]);
+            wave_lds_fence();
+        }
+        rank += total;
+    }
+}
+
+__device__ __forceinline__ void rederive_tile_e5m2(const uint8_t *__restrict__ in, uint64_t n, uint64_t tile,
+                                                   const uint8_t *table, uint8_t *buf, uint8_t *dst, uint32_t shift)
+{
+    const uint32_t lane = lane_id();
+    uint32_t rank = 0;                                          // wave-uniform
+    for (uint32_t row = 0; row < kEncTile / kRow; ++row) {
+        const uint64_t base = tile * kEncTile + (uint64_t)row * kRow;
+        if (base >= n) break;
+        const bool full_row = base + kRow <= n;
+        uint4 q[kE5Chunks][2];
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+            if (full_row || c0 + 32 <= n) {
+                q[j][0] = load_nt(reinterpret_cast<const uint4 *>(in + c0));
+                q[j][1] = load_nt(reinterpret_cast<const uint4 *>(in + c0 + 16));
+            } else {
+                uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                for (uint32_t k = 0; k < 32 && c0 + k < n; ++k) w[k / 4] |= (uint32_t)in[c0 + k] << (8 * (k & 3));
+                q[j][0] = make_uint4(w[0], w[1], w[2], w[3]);
+                q[j][1] = make_uint4(w[4], w[5], w[6], w[7]);
+            }
+        }
+        uint32_t esc[kE5Chunks], cnt[kE5Chunks];
+        uint64_t ex[kE5Chunks][4];
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+            uint4 nib;
+            uint32_t sm3[3];
+            encode_chunk_e5m2(q[j][0], q[j][1], table, nib, sm3, esc[j], ex[j]);
+            if (c0 >= n) esc[j] = 0;
+            else if (c0 + 32 > n) esc[j] &= (uint32_t)((1ull << (n - c0)) - 1);
+            cnt[j] = __popc(esc[j]);
+        }
+        uint32_t row_base[kE5Chunks], row_total[kE5Chunks], lane_before[kE5Chunks];
+        const uint32_t total = wave_chunk_ranks<kE5Chunks>(cnt, row_base, row_total, lane_before);
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            if (row_total[j] == 0) continue;                    // wave-uniform
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+#pragma unroll
+            for (uint32_t q4 = 0; q4 < 4; ++q4) {
+                const uint32_t seg_first = __builtin_amdgcn_readlane(lane_before[j], 16 * q4);
+                const uint32_t seg_end =
+                    q4 < 3 ? (uint32_t)__builtin_amdgcn_readlane(lane_before[j], 16 * (q4 + 1)) : row_total[j];
+                if (seg_end == seg_first) continue;             // wave-uniform
+                const uint32_t g0 = shift + 3 * (rank + row_base[j] + seg_first);
+                if (lane / 16 == q4 && cnt[j]) {
+                    uint32_t off = (g0 & 3) + 3 * (lane_before[j] - seg_first);
+#pragma unroll
+                    for (int s8 = 0; s8 < 4; ++s8)
+                        off = lds_put_records(buf, off, (esc[j] >> (8 * s8)) & 0xFFu, ex[j][s8],
+                                              (uint32_t)((c0 + 8 * s8) & 0xFFFFu));
+                }
+                wave_lds_fence();
+                flush_segment(buf, dst, g0, 3 * (seg_end - seg_first));
+                wave_lds_fence();
+            }
+        }
+        rank += total;
+    }
+}
+
 // Tiles with at most this many records are copied by 16-lane groups, the
 // block's four tiles at once; heavier blocks copy tile after tile with the
 // whole wave.
 constexpr uint32_t kGroupCopyRecords = 1024;
 
-__global__ __launch_bounds__(kCompactThreads) void sz_enc_compact(
+template <int DT>
+__global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_compact(
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
     const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
-    uint64_t nb)
+    uint64_t nb, const void *__restrict__ in, uint64_t n, Codebook4 cb)
 {
+    __shared__ uint32_t table32[64];
+    __shared__ __align__(16) uint8_t seg_buf[kCompactThreads / 64][kSegBytes];
+    build_encode_table(table32, cb, DT == SZ_BF16 ? 256 : 32);
+    __syncthreads();
     const uint64_t b = (uint64_t)blockIdx.x * (kCompactThreads / 64) + threadIdx.x / 64;
     if (b >= nb) return;
     const uint32_t lane = lane_id();
@@ -813,15 +949,17 @@ __global__ __launch_bounds__(kCompactThreads) void sz_enc_compact(
     else if (lane == kTilesPerBlock) meta = block_offsets[b];
     const uint64_t off = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(meta >> 32), kTilesPerBlock) << 32) |
                          (uint32_t)__builtin_amdgcn_readlane((uint32_t)meta, kTilesPerBlock);
-    uint32_t cnt[kTilesPerBlock], before[kTilesPerBlock], most = 0, run = 0;
+    uint32_t cnt[kTilesPerBlock], before[kTilesPerBlock], most = 0, run = 0, rederive = 0;
 #pragma unroll
     for (uint32_t t = 0; t < kTilesPerBlock; ++t) {
-        cnt[t] = __builtin_amdgcn_readlane((uint32_t)meta, t);
+        const uint32_t v = __builtin_amdgcn_readlane((uint32_t)meta, t);
+        cnt[t] = v & ~kRederiveFlag;
+        rederive |= (v >> 31) << t;
         before[t] = run;
         run += cnt[t];
         most = std::max(most, cnt[t]);
     }
-    if (most <= kGroupCopyRecords) {                               // wave-uniform
+    if (most <= kGroupCopyRecords && !rederive) {               // wave-uniform
         const uint32_t g = lane >> 4;
         uint32_t k = 0, bef = 0;
 #pragma unroll
@@ -831,12 +969,24 @@ __global__ __launch_bounds__(kCompactThreads) void sz_enc_compact(
                 bef = before[t];
             }
         if (k) copy_records(stage + (t0 + g) * (3ull * kEncTile), out, off_esc + 3 * (off + bef), 3 * k, lane & 15, 16);
-    } else {
+        return;
+    }
+    uint8_t *buf = seg_buf[threadIdx.x / 64];
 #pragma unroll
-        for (uint32_t t = 0; t < kTilesPerBlock; ++t)
-            if (cnt[t])
-                copy_records(stage + (t0 + t) * (3ull * kEncTile), out, off_esc + 3 * (off + before[t]), 3 * cnt[t],
-                             lane, 64);
+    for (uint32_t t = 0; t < kTilesPerBlock; ++t) {
+        if (cnt[t] == 0) continue;
+        const uint64_t dst0 = off_esc + 3 * (off + before[t]);
+        if ((rederive >> t) & 1) {
+            const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
+            if (DT == SZ_BF16)
+                rederive_tile_bf16(static_cast<const uint16_t *>(in), n, t0 + t, table, buf, out + (dst0 & ~uint64_t(3)),
+                                   (uint32_t)(dst0 & 3));
+            else
+                rederive_tile_e5m2(static_cast<const uint8_t *>(in), n, t0 + t, table, buf, out + (dst0 & ~uint64_t(3)),
+                                   (uint32_t)(dst0 & 3));
+        } else {
+            copy_records(stage + (t0 + t) * (3ull * kEncTile), out, dst0, 3 * cnt[t], lane, 64);
+        }
     }
 }
 
@@ -1585,8 +1735,12 @@ extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz
     if (g.nt) {
         LaunchScope scope("sz_enc_compact", s);
         const uint32_t groups = (uint32_t)((g.nb + kCompactThreads / 64 - 1) / (kCompactThreads / 64));
-        hipLaunchKernelGGL(sz_enc_compact, dim3(groups), dim3(kCompactThreads), 0, s, stage, tile_counts,
-                           block_offsets, out, g.off_esc, g.nt, g.nb);
+        if (dtype == SZ_BF16)
+            hipLaunchKernelGGL(sz_enc_compact<SZ_BF16>, dim3(groups), dim3(kCompactThreads), 0, s, stage, tile_counts,
+                               block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4);
+        else
+            hipLaunchKernelGGL(sz_enc_compact<SZ_FP8_E5M2>, dim3(groups), dim3(kCompactThreads), 0, s, stage,
+                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4);
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }
