@@ -73,6 +73,14 @@ def load_traffic(kernel: str, workload: str):
     return entry.get("bytes_per_launch")
 
 
+def short_kernel_name(name: str) -> str:
+    """'void (anonymous namespace)::sz_enc_compact<0>(...)' -> 'sz_enc_compact'."""
+    name = name.replace("(anonymous namespace)::", "").split("(")[0]
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("<")[0].strip()
+
+
 def _pmc_per_kernel(csv_path, counter):
     """{kernel short name: [values in KiB per dispatch]} from a rocprofv3 counter CSV."""
     import csv
@@ -81,7 +89,7 @@ def _pmc_per_kernel(csv_path, counter):
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
                 continue
-            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+            name = short_kernel_name(r["Kernel_Name"])
             out.setdefault(name, []).append(float(r["Counter_Value"]))
     return out
 
