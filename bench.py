@@ -50,10 +50,15 @@ def parse_args():
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    with open(os.path.join(ROOT, "fp8_kv_cache_sz_amd", "csrc", "splitzip.hip"), "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of the kernel source with comments and blank space removed, so
+    that recorded counters stay tied to the code, not to its commentary."""
+    import re
+    with open(os.path.join(ROOT, "fp8_kv_cache_sz_amd", "csrc", "splitzip.hip")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")

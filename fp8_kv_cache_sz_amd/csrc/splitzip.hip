@@ -404,7 +404,10 @@ __device__ __forceinline__ uint32_t workgroup_wave_prefix(uint32_t wave_total, u
 // Kernel: BF16 dense encode + escape staging.  One 256-lane workgroup per
 // 16K-element tile; wave w streams elements [4096w, 4096w + 4096) of it.  The
 // tile's records are staged in element order in the tile's slot (3 bytes per
-// element); tile_counts[tile] gets their number.
+// element); tile_counts[tile] gets their number.  A tile with more than
+// kRederiveRecords escapes stages nothing and is flagged with kRederiveFlag:
+// the compaction kernel derives its records again from the input, which
+// costs less traffic than writing and re-reading them.
 // ---------------------------------------------------------------------------
 constexpr int kBf16Chunks = 8;
 
@@ -770,10 +773,13 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
 // ---------------------------------------------------------------------------
 // Kernel: escape compaction.  One wave per block (four blocks per workgroup)
 // copies the staged records of the block's four tiles (3 bytes each) to
-// out[off_esc + 3 * offset ...), tile after tile.  The body of each copy is
-// written with 16-byte aligned dwordx4 stores assembled by v_alignbyte_b32
-// from five staged words; the unaligned bytes at both ends, whose dwords the
-// neighbouring tiles share, are written byte by byte.
+// out[off_esc + 3 * offset ...), tile after tile; when no tile of the block
+// holds more than kGroupCopyRecords records, four 16-lane groups copy the four
+// tiles at once.  The body of each copy is written with 16-byte aligned
+// dwordx4 stores assembled by v_alignbyte_b32 from five staged words; the
+// unaligned bytes at both ends, whose dwords the neighbouring tiles share, are
+// written byte by byte.  Flagged (escape-heavy) tiles are re-encoded from the
+// input instead and their records written straight to their final place.
 // ---------------------------------------------------------------------------
 // Copies len bytes of staged records to out[dst0, dst0 + len) with the lanes
 // [0, width) of a lane group (lane = index inside the group).
