@@ -16,7 +16,7 @@ LIBRARY = os.environ.get("SPLITZIP_LIB", os.path.join(HERE, "libsplitzip.so"))
 
 if not os.path.exists(LIBRARY):
     raise ImportError(
-        "libsplitzip.so not found at %s; build it with `python -m fp8_kv_cache_sz_amd.build` "
+        "libsplitzip.so not found at %s; build it with `python fp8_kv_cache_sz_amd/build.py` "
         "(or __graft_entry__.build())" % LIBRARY)
 
 lib = ctypes.CDLL(LIBRARY)
@@ -49,6 +49,12 @@ lib.sz_workspace_size.argtypes = [_i32, _u64]
 lib.sz_workspace_size.restype = _u64
 lib.sz_encode.argtypes = [_i32, _vp, _u64, ctypes.POINTER(sz_codebook), _vp, _u64, _vp, _u64, _vp]
 lib.sz_encode.restype = _i32
+lib.sz_encode_devcb.argtypes = [_i32, _vp, _u64, _vp, _vp, _u64, _vp, _u64, _vp]
+lib.sz_encode_devcb.restype = _i32
+lib.sz_calibrate_workspace_size.argtypes = [_i32]
+lib.sz_calibrate_workspace_size.restype = _u64
+lib.sz_calibrate_device.argtypes = [_i32, _vp, _u64, _u64, _vp, _vp, _vp, _u64, _vp]
+lib.sz_calibrate_device.restype = _i32
 lib.sz_decode.argtypes = [_vp, _u64, _i32, _vp, _u64, _vp, _u64, _vp]
 lib.sz_decode.restype = _i32
 lib.sz_profile_enable.argtypes = [_i32]
@@ -56,8 +62,9 @@ lib.sz_profile_enable.restype = _i32
 lib.sz_profile_collect.argtypes = [ctypes.POINTER(sz_kernel_stat), _i32]
 lib.sz_profile_collect.restype = _i32
 
-EXPORTS = ("sz_calibrate", "sz_encoded_size", "sz_workspace_size", "sz_encode", "sz_decode",
-           "sz_profile_enable", "sz_profile_collect")
+EXPORTS = ("sz_calibrate", "sz_encoded_size", "sz_workspace_size", "sz_encode", "sz_encode_devcb",
+           "sz_calibrate_workspace_size", "sz_calibrate_device", "sz_decode", "sz_profile_enable",
+           "sz_profile_collect")
 
 
 class SplitZipError(RuntimeError):
@@ -89,6 +96,18 @@ def sz_workspace_size(dtype: int, n: int) -> int:
 def sz_encode(dtype, d_in, n, cb, d_out, out_capacity, d_ws, ws_bytes, stream) -> int:
     return int(lib.sz_encode(dtype, d_in, n, ctypes.byref(cb), d_out, out_capacity, d_ws, ws_bytes,
                              stream))
+
+
+def sz_encode_devcb(dtype, d_in, n, d_cb, d_out, out_capacity, d_ws, ws_bytes, stream) -> int:
+    return int(lib.sz_encode_devcb(dtype, d_in, n, d_cb, d_out, out_capacity, d_ws, ws_bytes, stream))
+
+
+def sz_calibrate_workspace_size(dtype: int) -> int:
+    return int(lib.sz_calibrate_workspace_size(dtype))
+
+
+def sz_calibrate_device(dtype, d_in, n, sample_every, d_cb, d_hist, d_ws, ws_bytes, stream) -> int:
+    return int(lib.sz_calibrate_device(dtype, d_in, n, sample_every, d_cb, d_hist, d_ws, ws_bytes, stream))
 
 
 def sz_decode(d_in, in_bytes, dtype, d_out, n, d_ws, ws_bytes, stream) -> int:

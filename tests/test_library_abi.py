@@ -17,7 +17,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _native():
-    from fp8_kv_cache_sz_amd import build
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_splitzip_build", os.path.join(ROOT, "fp8_kv_cache_sz_amd", "build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
     if not os.path.exists(build.LIBRARY):
         build.build()
     from fp8_kv_cache_sz_amd import _native
