@@ -241,6 +241,29 @@ def main():
     achieved = alg_bytes / avg_s / 1e9
     traffic = load_traffic(dominant, args.workload)
 
+    # on-device calibration (per-tensor codebook at run time): the whole
+    # tensor, and every 16th 64K block; then encode with the device codebook
+    cal_ws = torch.empty(sz._native.sz_calibrate_workspace_size(dtype), dtype=torch.uint8, device=dev)
+    d_cb = torch.zeros(sz.DEVICE_CODEBOOK_BYTES, dtype=torch.uint8, device=dev)
+    cal_full_ms = time_loop(lambda: sz.calibrate_device(x, 1, out=d_cb, ws=cal_ws), reps)
+    cal_s16_ms = time_loop(lambda: sz.calibrate_device(x, 16, out=d_cb, ws=cal_ws), reps)
+    sz.calibrate_device(x, 1, out=d_cb, ws=cal_ws)
+    enc_dcb_ms = time_loop(lambda: sz.encode(x, d_cb, out=buf, ws=ws, sync=False), reps)
+    torch.cuda.synchronize()
+    if int(ws[:4].cpu().view(torch.int32)[0]) != 0:
+        print("device codebook rejected", file=sys.stderr)
+        sys.exit(1)
+    dyn_cb = sz.codebook_from_device(d_cb)
+    calibration = {
+        "device_full_ms": round(cal_full_ms, 4),
+        "device_full_read_GBps": round(n * elem / (cal_full_ms * 1e-3) / 1e9, 1),
+        "device_every16_ms": round(cal_s16_ms, 4),
+        "encode_with_device_codebook_ms": round(enc_dcb_ms, 4),
+        "calibrate_plus_encode_GBps": round(n * elem / ((cal_full_ms + enc_dcb_ms) * 1e-3) / 1e9, 1),
+        "per_tensor_codebook": list(dyn_cb.exps),
+        "per_tensor_codebook_equals_offline": list(dyn_cb.exps) == list(cb.exps),
+    }
+
     # a plain device copy of the same bytes, as a practical streaming ceiling
     alg_per_direction = alg_bytes // 2          # read half, write half
     src = torch.empty(alg_per_direction, dtype=torch.uint8, device=dev)
@@ -274,6 +297,7 @@ def main():
         "escapes": escapes,
         "stream_bytes": size,
         "kernels": per_kernel,
+        "calibration": calibration,
         "copy_GBps": round(copy_gbps, 1),
         "copy_bytes": alg_per_direction,
         "roofline": {

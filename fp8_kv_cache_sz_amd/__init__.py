@@ -20,9 +20,13 @@ from ._native import SZ_BF16, SZ_FP8_E5M2, SplitZipError
 BF16 = SZ_BF16
 E5M2 = SZ_FP8_E5M2
 
-__all__ = ["BF16", "E5M2", "Codebook", "SplitZipError", "calibrate", "encoded_size",
-           "workspace_size", "workspace", "encode", "decode", "read_escape_count",
-           "profile_enable", "profile_collect"]
+__all__ = ["BF16", "E5M2", "Codebook", "SplitZipError", "calibrate", "calibrate_device",
+           "codebook_from_device", "encoded_size", "workspace_size", "workspace", "encode", "decode",
+           "read_escape_count", "profile_enable", "profile_collect"]
+
+# An sz_codebook in device memory: u32 dtype, 16 exponent bytes (20 bytes,
+# padded to 32 so that the tensor size keeps 16-byte multiples).
+DEVICE_CODEBOOK_BYTES = 32
 
 
 @dataclass(frozen=True)
@@ -66,6 +70,35 @@ def calibrate(t: torch.Tensor) -> Codebook:
     return Codebook(dtype, tuple(int(x) for x in cb.exp))
 
 
+def calibrate_device(t: torch.Tensor, sample_every: int = 1, out: torch.Tensor | None = None,
+                     hist: bool = False, ws: torch.Tensor | None = None, stream=None):
+    """On-device Top-16 calibration (sz_calibrate_device) over the 64K blocks
+    0, s, 2s, ... of a device tensor.  Returns the codebook as a uint8 device
+    tensor in sz_codebook layout, usable by ``encode`` without a host round
+    trip; with ``hist=True`` returns ``(codebook, uint64 counts)``."""
+    dtype = dtype_of(t)
+    t = t.reshape(-1)
+    if not t.is_contiguous():
+        raise ValueError("calibrate_device needs a contiguous tensor")
+    n = t.numel()
+    if out is None:
+        out = torch.zeros(DEVICE_CODEBOOK_BYTES, dtype=torch.uint8, device=t.device)
+    h = torch.empty(256 if dtype == BF16 else 32, dtype=torch.int64, device=t.device) if hist else None
+    if ws is None:
+        ws = torch.empty(_native.sz_calibrate_workspace_size(dtype), dtype=torch.uint8, device=t.device)
+    rc = _native.sz_calibrate_device(dtype, t.data_ptr() if n else None, n, sample_every, out.data_ptr(),
+                                     h.data_ptr() if h is not None else None, ws.data_ptr(), ws.numel(),
+                                     _stream_handle(stream, t.device))
+    _native.check("sz_calibrate_device", rc)
+    return (out, h) if hist else out
+
+
+def codebook_from_device(d_cb: torch.Tensor) -> Codebook:
+    """Reads a device codebook (sz_codebook layout) back to the host."""
+    raw = d_cb[:20].cpu()
+    return Codebook(int(raw[:4].view(torch.int32)[0]), tuple(int(x) for x in raw[4:20]))
+
+
 def encoded_size(dtype: int, n: int, n_escapes: int) -> int:
     return _native.sz_encoded_size(dtype, n, n_escapes)
 
@@ -83,13 +116,16 @@ def read_escape_count(buf: torch.Tensor) -> int:
     return int(buf[16:24].cpu().view(torch.int64)[0])
 
 
-def encode(x: torch.Tensor, cb: Codebook, out: torch.Tensor | None = None,
+def encode(x: torch.Tensor, cb, out: torch.Tensor | None = None,
            ws: torch.Tensor | None = None, stream=None, sync: bool = True):
-    """Encode a device tensor.  Returns ``(buf, size, escapes)``; with
-    ``sync=False`` the call only enqueues the kernels and returns
-    ``(buf, None, None)`` (the size is known once the stream has run)."""
+    """Encode a device tensor with a host ``Codebook`` (sz_encode) or a device
+    codebook tensor from ``calibrate_device`` (sz_encode_devcb).  Returns
+    ``(buf, size, escapes)``; with ``sync=False`` the call only enqueues the
+    kernels and returns ``(buf, None, None)`` (the size is known once the
+    stream has run)."""
     dtype = dtype_of(x)
-    if cb.dtype != dtype:
+    on_device = isinstance(cb, torch.Tensor)
+    if not on_device and cb.dtype != dtype:
         raise SplitZipError("sz_encode", -2)
     x = x.reshape(-1)
     if not x.is_contiguous():
@@ -100,11 +136,20 @@ def encode(x: torch.Tensor, cb: Codebook, out: torch.Tensor | None = None,
         out = torch.empty(cap, dtype=torch.uint8, device=x.device)
     if ws is None:
         ws = workspace(dtype, n, x.device)
-    rc = _native.sz_encode(dtype, x.data_ptr() if n else None, n, cb.to_c(), out.data_ptr(),
-                           out.numel(), ws.data_ptr(), ws.numel(), _stream_handle(stream, x.device))
-    _native.check("sz_encode", rc)
+    if on_device:
+        rc = _native.sz_encode_devcb(dtype, x.data_ptr() if n else None, n, cb.data_ptr(), out.data_ptr(),
+                                     out.numel(), ws.data_ptr(), ws.numel(), _stream_handle(stream, x.device))
+        _native.check("sz_encode_devcb", rc)
+    else:
+        rc = _native.sz_encode(dtype, x.data_ptr() if n else None, n, cb.to_c(), out.data_ptr(),
+                               out.numel(), ws.data_ptr(), ws.numel(), _stream_handle(stream, x.device))
+        _native.check("sz_encode", rc)
     if not sync:
         return out, None, None
+    if on_device:
+        status = int(ws[:4].cpu().view(torch.int32)[0])
+        if status != 0:
+            raise SplitZipError("sz_encode_devcb (device codebook check)", status)
     escapes = read_escape_count(out)
     return out, encoded_size(dtype, n, escapes), escapes
 

@@ -155,6 +155,16 @@ __device__ __forceinline__ uint32_t cb_entry(const Codebook4 &cb, uint32_t c)
     return (cb.w[c >> 2] >> (8 * (c & 3))) & 0xFFu;
 }
 
+// A codebook that lives in device memory as an sz_codebook (word 0 = dtype,
+// words 1..4 = the 16 exponent bytes), as sz_calibrate_device writes it.
+__device__ __forceinline__ Codebook4 load_codebook(const uint32_t *cb_dev)
+{
+    Codebook4 cb;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) cb.w[w] = cb_dev[1 + w];
+    return cb;
+}
+
 // Exponent -> code table for encode.  Byte v = code of exponent v, or 0x80
 // (code 0 with the escape flag) when v is not in the codebook.  Threads
 // 0..63 fill 4 entries each.
@@ -414,6 +424,7 @@ constexpr int kBf16Chunks = 8;
 __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t *__restrict__ in, uint64_t n,
                                                               uint8_t *__restrict__ out, uint64_t off_nib,
                                                               uint64_t off_sm, Codebook4 cb,
+                                                              const uint32_t *__restrict__ cb_dev,
                                                               uint32_t *__restrict__ tile_counts,
                                                               uint8_t *__restrict__ stage)
 {
@@ -443,6 +454,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
                               v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
         }
     }
+    if (cb_dev) cb = load_codebook(cb_dev);
     build_encode_table(table32, cb, 256);
     __syncthreads();
     const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
@@ -512,6 +524,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
                                                               uint8_t *__restrict__ out, uint64_t off_nib,
                                                               uint64_t off_sm, uint64_t sm_bytes,
                                                               Codebook4 cb,
+                                                              const uint32_t *__restrict__ cb_dev,
                                                               uint32_t *__restrict__ tile_counts,
                                                               uint8_t *__restrict__ stage)
 {
@@ -538,6 +551,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
             q[j][1] = make_uint4(w[4], w[5], w[6], w[7]);
         }
     }
+    if (cb_dev) cb = load_codebook(cb_dev);
     build_encode_table(table32, cb, 32);
     __syncthreads();
     const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
@@ -710,10 +724,29 @@ struct HeaderArgs {
 __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__restrict__ tile_counts,
                                                             uint32_t nt,
                                                             uint64_t *__restrict__ block_offsets,
-                                                            uint8_t *__restrict__ out, HeaderArgs h)
+                                                            uint8_t *__restrict__ out, HeaderArgs h,
+                                                            const uint32_t *__restrict__ cb_dev,
+                                                            int32_t *__restrict__ status)
 {
     __shared__ ScanLds lds;
     const uint32_t tid = threadIdx.x;
+    // A device codebook is checked here (its dtype word, entries below the
+    // symbol count, no repeats); a bad one zeroes the magic, so the stream
+    // cannot be decoded, and sets the status word.
+    int32_t verdict = 0;
+    Codebook4 cb = h.cb;
+    if (cb_dev) {
+        cb = load_codebook(cb_dev);
+        const uint32_t symbols = h.dtype == SZ_BF16 ? 256u : 32u;
+        bool bad = false;
+        if (tid < 16) {
+            const uint32_t e = cb_entry(cb, tid);
+            bad = e >= symbols;
+            for (uint32_t d = 0; d < tid; ++d) bad = bad || cb_entry(cb, d) == e;
+        }
+        if (__syncthreads_or(bad)) verdict = SZ_E_ARG;
+        if (cb_dev[0] != h.dtype) verdict = SZ_E_DTYPE;
+    }
     const uint32_t nb = (uint32_t)h.nb;
     if (tid == 0) lds.carry = 0;
     uint32_t *block_counts = reinterpret_cast<uint32_t *>(out + 64);
@@ -747,21 +780,22 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
     if (tid < 16) {
         uint32_t w = 0;
         switch (tid) {
-        case 0: w = kMagic; break;
+        case 0: w = verdict ? 0u : kMagic; break;
         case 1: w = kVersion | (h.dtype << 16) | (kLog2Block << 24); break;
         case 2: w = (uint32_t)h.n; break;
         case 3: w = (uint32_t)(h.n >> 32); break;
         case 4: w = (uint32_t)total; break;
         case 5: w = (uint32_t)(total >> 32); break;
         case 6: w = (uint32_t)h.nb; break;
-        case 8: w = h.cb.w[0]; break;
-        case 9: w = h.cb.w[1]; break;
-        case 10: w = h.cb.w[2]; break;
-        case 11: w = h.cb.w[3]; break;
+        case 8: w = cb.w[0]; break;
+        case 9: w = cb.w[1]; break;
+        case 10: w = cb.w[2]; break;
+        case 11: w = cb.w[3]; break;
         default: w = 0; break;
         }
         reinterpret_cast<uint32_t *>(out)[tid] = w;
     }
+    if (tid == 0) status[0] = verdict;
     // zero padding between sections (each range is shorter than 256 bytes)
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
@@ -939,10 +973,11 @@ template <int DT>
 __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_compact(
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
     const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
-    uint64_t nb, const void *__restrict__ in, uint64_t n, Codebook4 cb)
+    uint64_t nb, const void *__restrict__ in, uint64_t n, Codebook4 cb, const uint32_t *__restrict__ cb_dev)
 {
     __shared__ uint32_t table32[64];
     __shared__ __align__(16) uint8_t seg_buf[kCompactThreads / 64][kSegBytes];
+    if (cb_dev) cb = load_codebook(cb_dev);
     build_encode_table(table32, cb, DT == SZ_BF16 ? 256 : 32);
     __syncthreads();
     const uint64_t b = (uint64_t)blockIdx.x * (kCompactThreads / 64) + threadIdx.x / 64;
@@ -1576,6 +1611,122 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
 }
 
 // ---------------------------------------------------------------------------
+// On-device calibration: the exponent histogram and the Top-16 selection run
+// on the GPU, so a codebook can be fitted to each tensor, or to a sample of
+// its 64K blocks, with no host round trip.  (The page's calibration ablation
+// weighs such per-tensor books against one offline book.)
+//
+// sz_cal_hist: every 512-lane workgroup walks 4096-element rows of the
+// sampled blocks (grid-stride over rows) and counts exponents in LDS with one
+// counter per (symbol, lane), so the 64 lanes of a ds_add never share a word
+// and the waves of the workgroup meet only through the atomic add.  It then
+// writes its per-symbol totals to column g of partial[symbol][groups].
+// sz_cal_select: one workgroup sums each symbol's row of partial counts with
+// dwordx4 loads, ranks the symbols by (count descending, symbol ascending),
+// and writes the first 16 as the codebook (and the histogram, if asked).
+// ---------------------------------------------------------------------------
+constexpr uint32_t kCalThreads = 512;
+constexpr uint32_t kCalMaxGroups = 512;          // two workgroups per CU
+constexpr uint32_t kCalRowsPerBlock = kBlock / kRow;
+constexpr uint32_t kSelectThreads = 1024;
+
+template <int DT>
+__global__ __launch_bounds__(kCalThreads) void sz_cal_hist(const void *__restrict__ in, uint64_t n, uint64_t every,
+                                                           uint64_t rows, uint32_t *__restrict__ partial,
+                                                           uint32_t groups)
+{
+    constexpr uint32_t S = DT == SZ_BF16 ? 256 : 32;
+    __shared__ uint32_t cnt[S * 64];
+    for (uint32_t i = threadIdx.x; i < S * 64; i += kCalThreads) cnt[i] = 0;
+    __syncthreads();
+    const uint32_t lane = lane_id();
+    const uint64_t waves = (uint64_t)gridDim.x * (kCalThreads / 64);
+    for (uint64_t r = (uint64_t)blockIdx.x * (kCalThreads / 64) + threadIdx.x / 64; r < rows; r += waves) {
+        const uint64_t base = (r / kCalRowsPerBlock) * every * kBlock + (r % kCalRowsPerBlock) * kRow;
+        if (base >= n) continue;
+        const bool full_row = base + kRow <= n;
+        if (DT == SZ_BF16) {
+            const uint16_t *src = static_cast<const uint16_t *>(in) + base;
+            if (full_row) {
+                uint4 q[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) q[j] = load_nt(reinterpret_cast<const uint4 *>(src) + j * 64 + lane);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t w[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        atomicAdd(&cnt[((w[k] >> 7) & 0xFFu) * 64 + lane], 1u);
+                        atomicAdd(&cnt[((w[k] >> 23) & 0xFFu) * 64 + lane], 1u);
+                    }
+                }
+            } else {
+                for (uint64_t k = lane; base + k < n; k += 64) atomicAdd(&cnt[((src[k] >> 7) & 0xFFu) * 64 + lane], 1u);
+            }
+        } else {
+            const uint8_t *src = static_cast<const uint8_t *>(in) + base;
+            if (full_row) {
+                uint4 q[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) q[j] = load_nt(reinterpret_cast<const uint4 *>(src) + j * 64 + lane);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t w[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) atomicAdd(&cnt[((w[k] >> (8 * b + 2)) & 0x1Fu) * 64 + lane], 1u);
+                }
+            } else {
+                for (uint64_t k = lane; base + k < n; k += 64) atomicAdd(&cnt[((src[k] >> 2) & 0x1Fu) * 64 + lane], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    for (uint32_t v = threadIdx.x; v < S; v += kCalThreads) {
+        uint32_t sum = 0;
+        for (uint32_t c = 0; c < 64; ++c) sum += cnt[v * 64 + ((c + v) & 63u)];   // rotated: no bank conflicts
+        partial[(uint64_t)v * groups + blockIdx.x] = sum;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kSelectThreads) void sz_cal_select(const uint32_t *__restrict__ partial, uint32_t groups,
+                                                                uint32_t *__restrict__ cb_out,
+                                                                uint64_t *__restrict__ hist_out)
+{
+    constexpr uint32_t S = DT == SZ_BF16 ? 256 : 32;
+    constexpr uint32_t P = kSelectThreads / S;        // threads per symbol, consecutive lanes
+    __shared__ uint64_t hist[S];
+    const uint32_t t = threadIdx.x;
+    const uint32_t v = t / P, part = t % P;
+    const uint4 *row = reinterpret_cast<const uint4 *>(partial + (uint64_t)v * groups);
+    uint64_t sum = 0;
+    for (uint32_t i = part; i < groups / 4; i += P) {
+        const uint4 q = row[i];
+        sum += (uint64_t)q.x + q.y + q.z + q.w;
+    }
+    for (uint32_t o = 1; o < P; o <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)sum, o, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)(sum >> 32), o, 64);
+        sum += ((uint64_t)hi << 32) | lo;
+    }
+    if (part == 0) hist[v] = sum;
+    __syncthreads();
+    if (t < S) {
+        const uint64_t h = hist[t];
+        uint32_t rank = 0;
+        for (uint32_t u = 0; u < S; ++u) {
+            const uint64_t hu = hist[u];
+            rank += (hu > h || (hu == h && u < t)) ? 1u : 0u;
+        }
+        if (rank < 16) reinterpret_cast<uint8_t *>(cb_out)[4 + rank] = (uint8_t)t;
+        if (hist_out) hist_out[t] = h;
+    }
+    if (t == 0) cb_out[0] = (uint32_t)DT;
+}
+
+// ---------------------------------------------------------------------------
 // Host side: launch bookkeeping and instrumentation
 // ---------------------------------------------------------------------------
 struct ProfRecord {
@@ -1684,18 +1835,12 @@ extern "C" uint64_t sz_workspace_size(int dtype, uint64_t n_elems)
     return ws_layout(dtype, n_elems).total;
 }
 
-extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *cb, void *d_out,
-                         uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream)
+namespace {
+
+// Encode behind sz_encode (host codebook cb4) and sz_encode_devcb (cb_dev).
+int encode_impl(int dtype, const void *d_in, uint64_t n_elems, const Codebook4 &cb4, const uint32_t *cb_dev,
+                void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream)
 {
-    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
-    if (!cb) return SZ_E_ARG;
-    if (cb->dtype != (uint32_t)dtype) return SZ_E_DTYPE;
-    const uint32_t symbols = symbols_of(dtype);
-    for (int c = 0; c < 16; ++c) {
-        if (cb->exp[c] >= symbols) return SZ_E_ARG;
-        for (int d = 0; d < c; ++d)
-            if (cb->exp[d] == cb->exp[c]) return SZ_E_ARG;
-    }
     if (n_elems > kMaxElems) return SZ_E_ARG;
     if (!d_out || !d_ws || (n_elems && !d_in)) return SZ_E_ARG;
     if (!aligned16(d_out) || !aligned16(d_ws) || (n_elems && !aligned16(d_in))) return SZ_E_ALIGN;
@@ -1705,22 +1850,22 @@ extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz
     const WsLayout w = ws_layout(dtype, n_elems);
     uint8_t *ws = static_cast<uint8_t *>(d_ws);
     uint8_t *out = static_cast<uint8_t *>(d_out);
+    int32_t *status = reinterpret_cast<int32_t *>(ws);
     uint32_t *tile_counts = reinterpret_cast<uint32_t *>(ws + w.counts);
     uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
     uint8_t *stage = ws + w.stage;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const Codebook4 cb4 = pack_codebook(cb->exp);
 
     if (g.nt && dtype == SZ_BF16) {
         LaunchScope scope("sz_enc_dense_bf16", s);
         hipLaunchKernelGGL(sz_enc_dense_bf16, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s,
-                           static_cast<const uint16_t *>(d_in), g.n, out, g.off_nib, g.off_sm, cb4,
+                           static_cast<const uint16_t *>(d_in), g.n, out, g.off_nib, g.off_sm, cb4, cb_dev,
                            tile_counts, stage);
     } else if (g.nt) {
         LaunchScope scope("sz_enc_dense_e5m2", s);
         hipLaunchKernelGGL(sz_enc_dense_e5m2, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s,
                            static_cast<const uint8_t *>(d_in), g.n, out, g.off_nib, g.off_sm, g.sm_bytes,
-                           cb4, tile_counts, stage);
+                           cb4, cb_dev, tile_counts, stage);
     }
     {
         HeaderArgs h;
@@ -1736,17 +1881,94 @@ extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz
         h.pad_end[2] = g.off_esc;
         LaunchScope scope("sz_enc_scan", s);
         hipLaunchKernelGGL(sz_enc_scan, dim3(1), dim3(kScanThreads), 0, s, tile_counts, (uint32_t)g.nt,
-                           block_offsets, out, h);
+                           block_offsets, out, h, cb_dev, status);
     }
     if (g.nt) {
         LaunchScope scope("sz_enc_compact", s);
         const uint32_t groups = (uint32_t)((g.nb + kCompactThreads / 64 - 1) / (kCompactThreads / 64));
         if (dtype == SZ_BF16)
             hipLaunchKernelGGL(sz_enc_compact<SZ_BF16>, dim3(groups), dim3(kCompactThreads), 0, s, stage, tile_counts,
-                               block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4);
+                               block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev);
         else
             hipLaunchKernelGGL(sz_enc_compact<SZ_FP8_E5M2>, dim3(groups), dim3(kCompactThreads), 0, s, stage,
-                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4);
+                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev);
+    }
+    return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
+}
+
+}  // namespace
+
+extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *cb, void *d_out,
+                         uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    if (!cb) return SZ_E_ARG;
+    if (cb->dtype != (uint32_t)dtype) return SZ_E_DTYPE;
+    const uint32_t symbols = symbols_of(dtype);
+    for (int c = 0; c < 16; ++c) {
+        if (cb->exp[c] >= symbols) return SZ_E_ARG;
+        for (int d = 0; d < c; ++d)
+            if (cb->exp[d] == cb->exp[c]) return SZ_E_ARG;
+    }
+    return encode_impl(dtype, d_in, n_elems, pack_codebook(cb->exp), nullptr, d_out, out_capacity, d_ws, ws_bytes,
+                       stream);
+}
+
+extern "C" int sz_encode_devcb(int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *d_cb,
+                               void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    if (!d_cb) return SZ_E_ARG;
+    if (!aligned16(d_cb)) return SZ_E_ALIGN;
+    const uint8_t zero[16] = {0};
+    return encode_impl(dtype, d_in, n_elems, pack_codebook(zero), reinterpret_cast<const uint32_t *>(d_cb), d_out,
+                       out_capacity, d_ws, ws_bytes, stream);
+}
+
+extern "C" uint64_t sz_calibrate_workspace_size(int dtype)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return 0;
+    return (uint64_t)symbols_of(dtype) * kCalMaxGroups * 4;
+}
+
+extern "C" int sz_calibrate_device(int dtype, const void *d_in, uint64_t n_elems, uint64_t sample_every,
+                                   sz_codebook *d_cb, uint64_t *d_hist, void *d_ws, uint64_t ws_bytes,
+                                   void *stream)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    if (n_elems > kMaxElems || sample_every == 0) return SZ_E_ARG;
+    if (!d_cb || !d_ws || (n_elems && !d_in)) return SZ_E_ARG;
+    if (!aligned16(d_cb) || !aligned16(d_ws) || (n_elems && !aligned16(d_in)) || (d_hist && !aligned16(d_hist)))
+        return SZ_E_ALIGN;
+    if (ws_bytes < sz_calibrate_workspace_size(dtype)) return SZ_E_WORKSPACE;
+    const uint64_t nb = (n_elems + kBlock - 1) / kBlock;
+    const uint64_t sampled = (nb + sample_every - 1) / sample_every;
+    const uint64_t rows = sampled * kCalRowsPerBlock;
+    const uint64_t waves = kCalThreads / 64;
+    // one row per wave at least, and a multiple of 4 columns for the dwordx4 sums
+    uint64_t groups = std::min<uint64_t>(kCalMaxGroups, (rows + waves - 1) / waves);
+    groups = std::max<uint64_t>(4, (groups + 3) & ~uint64_t(3));
+    uint32_t *partial = static_cast<uint32_t *>(d_ws);
+    uint32_t *cb_out = reinterpret_cast<uint32_t *>(d_cb);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == SZ_BF16) {
+        {
+            LaunchScope scope("sz_cal_hist_bf16", s);
+            hipLaunchKernelGGL(sz_cal_hist<SZ_BF16>, dim3((uint32_t)groups), dim3(kCalThreads), 0, s, d_in, n_elems,
+                               sample_every, rows, partial, (uint32_t)groups);
+        }
+        LaunchScope scope("sz_cal_select", s);
+        hipLaunchKernelGGL(sz_cal_select<SZ_BF16>, dim3(1), dim3(kSelectThreads), 0, s, partial, (uint32_t)groups,
+                           cb_out, d_hist);
+    } else {
+        {
+            LaunchScope scope("sz_cal_hist_e5m2", s);
+            hipLaunchKernelGGL(sz_cal_hist<SZ_FP8_E5M2>, dim3((uint32_t)groups), dim3(kCalThreads), 0, s, d_in,
+                               n_elems, sample_every, rows, partial, (uint32_t)groups);
+        }
+        LaunchScope scope("sz_cal_select", s);
+        hipLaunchKernelGGL(sz_cal_select<SZ_FP8_E5M2>, dim3(1), dim3(kSelectThreads), 0, s, partial,
+                           (uint32_t)groups, cb_out, d_hist);
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }

@@ -35,9 +35,10 @@
  *     null stream) and return once it is launched.  Calls that share a
  *     workspace must not overlap.
  *   - Errors are negative return codes; nothing throws or aborts across the
- *     ABI.  Checks made on the device (decode) land in the workspace status
- *     word, an int32 at workspace offset 0: 0 or a negative SZ_E_* code, valid
- *     once the stream has synchronised.
+ *     ABI.  Checks made on the device (the stream checks of sz_decode, the
+ *     codebook check of sz_encode_devcb) land in the workspace status word,
+ *     an int32 at workspace offset 0: 0 or a negative SZ_E_* code, valid once
+ *     the stream has synchronised.  sz_encode sets it to 0.
  */
 #ifndef SPLITZIP_H
 #define SPLITZIP_H
@@ -104,6 +105,38 @@ uint64_t sz_workspace_size(int dtype, uint64_t n_elems);
 int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *cb,
               void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes,
               void *stream);
+
+/* sz_encode with the codebook read from device memory: d_cb is an
+ * sz_codebook in device memory (16-byte aligned), for instance one written
+ * by sz_calibrate_device earlier on the same stream, so a per-tensor book
+ * needs no host round trip.  The stream equals sz_encode's for the same
+ * codebook.  The codebook is checked on the device: a dtype word other than
+ * dtype sets the status word to SZ_E_DTYPE, an entry >= 256 (BF16) / 32
+ * (E5M2) or a repeated entry sets SZ_E_ARG; either way the stream's magic is
+ * written as 0, so sz_decode rejects it.  Other arguments and return codes
+ * as sz_encode. */
+int sz_encode_devcb(int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *d_cb,
+                    void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes,
+                    void *stream);
+
+/* On-device calibration (page: Results, calibration ablation, which sets
+ * per-tensor books fitted at run time against one offline book; the Top-16
+ * rule of Method, fixed-length coding bullet).  The rule of sz_calibrate,
+ * computed on the GPU over the 64K blocks 0, s, 2s, ... of d_in
+ * (s = sample_every >= 1; s = 1 takes the whole tensor): the exponents of
+ * those blocks' elements are counted, all 256 (32) values are ordered by
+ * count descending, then value ascending, and the first 16 are written to
+ * d_cb (an sz_codebook in device memory, dtype word included).  d_hist, if
+ * not NULL, receives the 256 (BF16) or 32 (E5M2) uint64 exponent counts.
+ * d_ws: ws_bytes >= sz_calibrate_workspace_size(dtype) (partial counts).
+ * Enqueue only; the results are valid once the stream has run past them.
+ * Returns SZ_OK, SZ_E_DTYPE, SZ_E_ARG (null pointer, sample_every = 0,
+ * n_elems > 2^40), SZ_E_ALIGN (d_in, d_cb, d_hist, d_ws not 16-byte
+ * aligned), SZ_E_WORKSPACE or SZ_E_HIP. */
+uint64_t sz_calibrate_workspace_size(int dtype);
+int sz_calibrate_device(int dtype, const void *d_in, uint64_t n_elems, uint64_t sample_every,
+                        sz_codebook *d_cb, uint64_t *d_hist, void *d_ws, uint64_t ws_bytes,
+                        void *stream);
 
 /* Decode (page: Method, decoding bullets: dense unpack + lookup table, then
  * the sparse escape stream overwrites the escaped exponents).  d_in: a

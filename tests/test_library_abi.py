@@ -107,3 +107,28 @@ def test_host_argument_checks():
     assert nat.sz_decode(dummy, fixed, 3, dummy, 1000, dummy, 1 << 30, None) == -2
     assert nat.sz_decode(dummy + 8, fixed, 0, dummy, 1000, dummy, 1 << 30, None) == -4
     assert nat.sz_decode(dummy, fixed, 0, dummy, 1000, dummy, 16, None) == -7
+
+
+def test_host_argument_checks_device_calibration():
+    """sz_calibrate_device and sz_encode_devcb reject bad arguments before any
+    launch (the pointers are never dereferenced)."""
+    nat = _native()
+    dummy = 1 << 20
+    cws = nat.sz_calibrate_workspace_size(0)
+    assert cws == 256 * 512 * 4 and nat.sz_calibrate_workspace_size(1) == 32 * 512 * 4
+    assert nat.sz_calibrate_workspace_size(7) == 0
+    assert nat.sz_calibrate_device(7, dummy, 16, 1, dummy, None, dummy, cws, None) == -2
+    assert nat.sz_calibrate_device(0, dummy, 16, 0, dummy, None, dummy, cws, None) == -1
+    assert nat.sz_calibrate_device(0, dummy, 16, 1, None, None, dummy, cws, None) == -1
+    assert nat.sz_calibrate_device(0, None, 16, 1, dummy, None, dummy, cws, None) == -1
+    assert nat.sz_calibrate_device(0, dummy, 16, 1, dummy + 4, None, dummy, cws, None) == -4
+    assert nat.sz_calibrate_device(0, dummy, 16, 1, dummy, dummy + 8, dummy, cws, None) == -4
+    assert nat.sz_calibrate_device(0, dummy, 16, 1, dummy, None, dummy, cws - 1, None) == -7
+    assert nat.sz_calibrate_device(0, dummy, (1 << 40) + 1, 1, dummy, None, dummy, cws, None) == -1
+    cap = nat.sz_encoded_size(1, 16, 16)
+    ws = nat.sz_workspace_size(1, 16)
+    assert nat.sz_encode_devcb(4, dummy, 16, dummy, dummy, cap, dummy, ws, None) == -2
+    assert nat.sz_encode_devcb(1, dummy, 16, None, dummy, cap, dummy, ws, None) == -1
+    assert nat.sz_encode_devcb(1, dummy, 16, dummy + 4, dummy, cap, dummy, ws, None) == -4
+    assert nat.sz_encode_devcb(1, dummy, 16, dummy, dummy, cap - 1, dummy, ws, None) == -3
+    assert nat.sz_encode_devcb(1, dummy, 16, dummy, dummy, cap, dummy, ws - 1, None) == -7
