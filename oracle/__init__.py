@@ -70,6 +70,17 @@ def lib() -> ctypes.CDLL:
         L.szo_decode.restype = i32
         L.szo_check_canonical.argtypes = [vp, u64, i32, u64]
         L.szo_check_canonical.restype = i32
+        u32 = ctypes.c_uint32
+        L.szo_encoded_size_variant.argtypes = [u32, u64, u64]
+        L.szo_encoded_size_variant.restype = u64
+        L.szo_count_escapes_variant.argtypes = [u32, vp, u64, vp]
+        L.szo_count_escapes_variant.restype = u64
+        L.szo_encode_variant.argtypes = [u32, vp, u64, vp, vp, u64]
+        L.szo_encode_variant.restype = i64
+        L.szo_validate_variant.argtypes = [u32, vp, u64, u64]
+        L.szo_validate_variant.restype = i32
+        L.szo_decode_variant.argtypes = [u32, vp, u64, vp, u64]
+        L.szo_decode_variant.restype = i32
         _lib = L
     return _lib
 
@@ -166,3 +177,56 @@ def validate(stream, dtype: int, n: int) -> int:
 def check_canonical(stream, dtype: int, n: int) -> int:
     s = np.ascontiguousarray(stream, dtype=np.uint8).reshape(-1)
     return int(lib().szo_check_canonical(_ptr(s), s.size, dtype, n))
+
+
+# ---------------------------------------------------------------------------
+# Ablation variants, BF16 only: version 2 = Top-8 (3-bit codes + position
+# records), version 3 = Top-15 with code 15 as escape sentinel (exponent
+# bytes, no positions).  Version 1 is the Top-16 format above.
+# ---------------------------------------------------------------------------
+TOP16, TOP8, TOP15S = 1, 2, 3
+BOOK_ENTRIES = {TOP16: 16, TOP8: 8, TOP15S: 15}
+
+
+def encoded_size_variant(version: int, n: int, n_escapes: int) -> int:
+    return int(lib().szo_encoded_size_variant(version, n, n_escapes))
+
+
+def count_escapes_variant(version: int, data, codebook) -> int:
+    a = _as_input(data, BF16)
+    cb = np.ascontiguousarray(codebook, dtype=np.uint8)
+    return int(lib().szo_count_escapes_variant(version, _ptr(a), a.size, cb.ctypes.data_as(ctypes.c_void_p)))
+
+
+def encode_variant(data, version: int, codebook, capacity: int | None = None) -> np.ndarray:
+    """Encode BF16 bits in format `version`; returns the stream."""
+    a = _as_input(data, BF16)
+    cb = np.zeros(16, dtype=np.uint8)
+    cb[:len(codebook)] = np.asarray(codebook, dtype=np.uint8)
+    if capacity is None:
+        capacity = encoded_size_variant(version, a.size, count_escapes_variant(version, a, cb))
+    out = np.zeros(max(capacity, 1), dtype=np.uint8)
+    rc = lib().szo_encode_variant(version, _ptr(a), a.size, cb.ctypes.data_as(ctypes.c_void_p),
+                                  out.ctypes.data_as(ctypes.c_void_p), capacity)
+    if rc < 0:
+        raise ValueError("szo_encode_variant failed: %d" % rc)
+    return out[:rc]
+
+
+def validate_variant(stream, version: int, n: int) -> int:
+    s = np.ascontiguousarray(stream, dtype=np.uint8)
+    return int(lib().szo_validate_variant(version, _ptr(s), s.size, n))
+
+
+def decode_variant_rc(stream, version: int, n: int):
+    s = np.ascontiguousarray(stream, dtype=np.uint8)
+    out = np.zeros(max(n, 1), dtype=np.uint16)
+    rc = lib().szo_decode_variant(version, _ptr(s), s.size, out.ctypes.data_as(ctypes.c_void_p), n)
+    return rc, out[:n]
+
+
+def decode_variant(stream, version: int, n: int) -> np.ndarray:
+    rc, out = decode_variant_rc(stream, version, n)
+    if rc:
+        raise ValueError("szo_decode_variant failed: %d" % rc)
+    return out

@@ -419,3 +419,243 @@ int szo_check_canonical(const uint8_t *in, uint64_t in_bytes, int dtype, uint64_
     free(values);
     return result;
 }
+
+/* ========================================================================= */
+/* Ablation variants (BF16 only).  The page chose a Top-16 book with explicit */
+/* escape positions over two alternatives (Method, decoding "design choice"   */
+/* bullet; Results, ablations "Top-16 vs Top-8" and "metadata trade-off"):    */
+/*                                                                           */
+/* Version 2, Top-8: the 8 most frequent exponents get 3-bit codes; every    */
+/*   other exponent is an escape with a (position, exponent) record as in    */
+/*   version 1, and its code is 0.  Sections:                                 */
+/*     off_code = A(64 + 4 nb): 3 * ceil(N/8) bytes; bit 3i + k of the        */
+/*                section is bit k of element i's code (LSB first)            */
+/*     off_sm   = off_code + A(3 * ceil(N/8)): N bytes sign << 7 | mantissa7  */
+/*     off_esc  = off_sm + A(N): E records of 3 bytes as in version 1         */
+/*   Header codebook bytes 8..15 are 0.                                       */
+/* Version 3, Top-15 + sentinel: the 15 most frequent exponents get codes    */
+/*   0..14; code 15 marks an escape whose exponent is the next byte of the    */
+/*   escape section (no position is stored).  Sections:                       */
+/*     off_nib, off_sm as version 1 (BF16)                                    */
+/*     off_esc  = off_sm + A(N): E bytes, the escaped exponents in ascending  */
+/*                element order                                                */
+/*   counts[b] = escapes of block b as in version 1; header codebook byte 15  */
+/*   is 0.                                                                    */
+/* The header is the version 1 header with the version field set to 2 or 3. */
+/* ========================================================================= */
+#define SZO_TOP8 2u
+#define SZO_TOP15S 3u
+
+/* Number of codebook entries a version uses. */
+static unsigned book_entries(unsigned version)
+{
+    if (version == SZO_TOP8) return 8;
+    if (version == SZO_TOP15S) return 15;
+    return 16;
+}
+
+static uint64_t code_bytes_v(unsigned version, uint64_t n)
+{
+    return version == SZO_TOP8 ? 3u * ((n + 7) / 8) : nibble_bytes(n);
+}
+
+static layout_t variant_layout(unsigned version, uint64_t n)
+{
+    layout_t L;
+    L.nb = block_count(n);
+    L.off_counts = 64;
+    L.off_nib = round_up_256(64 + 4 * L.nb);
+    L.off_sm = L.off_nib + round_up_256(code_bytes_v(version, n));
+    L.off_esc = L.off_sm + round_up_256(n);
+    return L;
+}
+
+static uint64_t escape_bytes_v(unsigned version) { return version == SZO_TOP15S ? 1u : 3u; }
+
+uint64_t szo_encoded_size_variant(unsigned version, uint64_t n, uint64_t n_escapes)
+{
+    if (version == 1) return szo_encoded_size(SZO_BF16, n, n_escapes);
+    if (version != SZO_TOP8 && version != SZO_TOP15S) return 0;
+    return variant_layout(version, n).off_esc + escape_bytes_v(version) * n_escapes;
+}
+
+/* Code of exponent v among the first `entries` codebook bytes, or -1. */
+static int code_of_first(const uint8_t *codebook, unsigned entries, unsigned v)
+{
+    for (unsigned c = 0; c < entries; c++)
+        if (codebook[c] == v) return (int)c;
+    return -1;
+}
+
+uint64_t szo_count_escapes_variant(unsigned version, const uint16_t *data, uint64_t n, const uint8_t *codebook)
+{
+    uint64_t e = 0;
+    unsigned entries = book_entries(version);
+    for (uint64_t i = 0; i < n; i++)
+        if (code_of_first(codebook, entries, bf16_exponent(data[i])) < 0) e++;
+    return e;
+}
+
+/* Encode a BF16 tensor in version 2 or 3 (version 1 is szo_encode).  Only
+ * the first 8 (15) codebook bytes are used and must be distinct.  Returns
+ * the stream size or a negative error. */
+int64_t szo_encode_variant(unsigned version, const uint16_t *data, uint64_t n, const uint8_t *codebook,
+                           uint8_t *out, uint64_t capacity)
+{
+    if (version == 1) return szo_encode(SZO_BF16, data, n, codebook, out, capacity);
+    if (version != SZO_TOP8 && version != SZO_TOP15S) return SZO_E_ARG;
+    if (!codebook || !out || (n && !data)) return SZO_E_ARG;
+    unsigned entries = book_entries(version);
+    for (unsigned c = 0; c < entries; c++)
+        for (unsigned d = 0; d < c; d++)
+            if (codebook[d] == codebook[c]) return SZO_E_ARG;
+
+    uint64_t total_escapes = szo_count_escapes_variant(version, data, n, codebook);
+    uint64_t size = szo_encoded_size_variant(version, n, total_escapes);
+    if (capacity < size) return SZO_E_CAPACITY;
+    layout_t L = variant_layout(version, n);
+    memset(out, 0, size);
+
+    put_u32(out + 0, SZO_MAGIC);
+    put_u16(out + 4, version);
+    out[6] = (uint8_t)SZO_BF16;
+    out[7] = (uint8_t)SZO_LOG2_BLOCK;
+    put_u64(out + 8, n);
+    put_u64(out + 16, total_escapes);
+    put_u32(out + 24, (uint32_t)L.nb);
+    put_u32(out + 28, 0);
+    for (unsigned c = 0; c < entries; c++) out[32 + c] = codebook[c];
+
+    uint64_t escapes_written = 0;
+    for (uint64_t b = 0; b < L.nb; b++) {
+        uint64_t first = b * SZO_BLOCK;
+        uint64_t last = first + SZO_BLOCK < n ? first + SZO_BLOCK : n;
+        uint32_t block_escapes = 0;
+        for (uint64_t i = first; i < last; i++) {
+            uint16_t h = data[i];
+            unsigned exponent = bf16_exponent(h);
+            int code = code_of_first(codebook, entries, exponent);
+            if (code < 0) {
+                if (version == SZO_TOP8) {
+                    uint8_t *rec = out + L.off_esc + 3 * escapes_written;
+                    put_u16(rec, (uint32_t)(i - first));
+                    rec[2] = (uint8_t)exponent;
+                    code = 0;
+                } else {
+                    out[L.off_esc + escapes_written] = (uint8_t)exponent;
+                    code = 15;
+                }
+                escapes_written++;
+                block_escapes++;
+            }
+            if (version == SZO_TOP8) {
+                uint64_t bit = 3 * i;
+                for (int k = 0; k < 3; k++, bit++)
+                    if (((unsigned)code >> k) & 1u)
+                        out[L.off_nib + bit / 8] |= (uint8_t)(1u << (bit % 8));
+            } else {
+                out[L.off_nib + i / 2] |= (uint8_t)(code << (4 * (i % 2)));
+            }
+            out[L.off_sm + i] = (uint8_t)((bf16_sign(h) << 7) | bf16_mantissa(h));
+        }
+        put_u32(out + L.off_counts + 4 * b, block_escapes);
+    }
+    return (int64_t)size;
+}
+
+static unsigned variant_code(unsigned version, const uint8_t *in, const layout_t *L, uint64_t i)
+{
+    if (version == SZO_TOP8) {
+        unsigned code = 0;
+        uint64_t bit = 3 * i;
+        for (int k = 0; k < 3; k++, bit++)
+            code |= (unsigned)((in[L->off_nib + bit / 8] >> (bit % 8)) & 1u) << k;
+        return code;
+    }
+    return (in[L->off_nib + i / 2] >> (4 * (i % 2))) & 0xFu;
+}
+
+/* Validation of a version 2 or 3 stream: the version 1 header rules, unused
+ * codebook bytes zero, per-block counts at most the block length and summing
+ * to E, and, per block, version 2 records strictly ascending inside the
+ * block, version 3 sentinel codes exactly as many as the block's count. */
+int szo_validate_variant(unsigned version, const uint8_t *in, uint64_t in_bytes, uint64_t n)
+{
+    if (version == 1) return szo_validate(in, in_bytes, SZO_BF16, n);
+    if (version != SZO_TOP8 && version != SZO_TOP15S) return SZO_E_ARG;
+    if (!in) return SZO_E_ARG;
+    if (in_bytes < 64) return SZO_E_FORMAT;
+    if (get_u32(in) != SZO_MAGIC || get_u16(in + 4) != version) return SZO_E_FORMAT;
+    if (in[6] != (uint8_t)SZO_BF16) return SZO_E_DTYPE;
+    if (in[7] != SZO_LOG2_BLOCK) return SZO_E_FORMAT;
+    if (get_u64(in + 8) != n) return SZO_E_FORMAT;
+    layout_t L = variant_layout(version, n);
+    if (get_u32(in + 24) != L.nb || get_u32(in + 28) != 0) return SZO_E_FORMAT;
+    for (unsigned c = book_entries(version); c < 16; c++)
+        if (in[32 + c] != 0) return SZO_E_FORMAT;
+    uint64_t total_escapes = get_u64(in + 16);
+    if (total_escapes > n) return SZO_E_FORMAT;
+    if (in_bytes < szo_encoded_size_variant(version, n, total_escapes)) return SZO_E_FORMAT;
+
+    uint64_t sum = 0, r = 0;
+    for (uint64_t b = 0; b < L.nb; b++) {
+        uint64_t first = b * SZO_BLOCK;
+        uint64_t len = (first + SZO_BLOCK < n ? SZO_BLOCK : n - first);
+        uint64_t count = get_u32(in + L.off_counts + 4 * b);
+        if (count > len) return SZO_E_FORMAT;
+        sum += count;
+        if (sum > total_escapes) return SZO_E_FORMAT;
+        if (version == SZO_TOP8) {
+            int64_t previous = -1;
+            for (uint64_t k = 0; k < count; k++, r++) {
+                int64_t pos = (int64_t)get_u16(in + L.off_esc + 3 * r);
+                if ((uint64_t)pos >= len || pos <= previous) return SZO_E_FORMAT;
+                previous = pos;
+            }
+        } else {
+            uint64_t sentinels = 0;
+            for (uint64_t i = first; i < first + len; i++)
+                if (variant_code(version, in, &L, i) == 15) sentinels++;
+            if (sentinels != count) return SZO_E_FORMAT;
+        }
+    }
+    if (sum != total_escapes) return SZO_E_FORMAT;
+    return SZO_OK;
+}
+
+/* Decode a version 2 or 3 stream.  Version 2: the dense path rebuilds every
+ * value from its 3-bit code, then the records overwrite the escaped
+ * exponents (as version 1).  Version 3: one pass in element order; a code
+ * of 15 takes the next exponent byte of the escape section. */
+int szo_decode_variant(unsigned version, const uint8_t *in, uint64_t in_bytes, uint16_t *out, uint64_t n)
+{
+    if (version == 1) return szo_decode(in, in_bytes, SZO_BF16, out, n);
+    int rc = szo_validate_variant(version, in, in_bytes, n);
+    if (rc) return rc;
+    if (n && !out) return SZO_E_ARG;
+    layout_t L = variant_layout(version, n);
+    const uint8_t *codebook = in + 32;
+    uint64_t next_escape = 0;
+    for (uint64_t i = 0; i < n; i++) {
+        unsigned code = variant_code(version, in, &L, i);
+        unsigned signmant = in[L.off_sm + i];
+        unsigned exponent;
+        if (version == SZO_TOP15S && code == 15)
+            exponent = in[L.off_esc + next_escape++];
+        else
+            exponent = codebook[code];
+        out[i] = bf16_join(signmant >> 7, exponent, signmant & 0x7Fu);
+    }
+    if (version == SZO_TOP8) {
+        uint64_t r = 0;
+        for (uint64_t b = 0; b < L.nb; b++) {
+            uint64_t count = get_u32(in + L.off_counts + 4 * b);
+            for (uint64_t k = 0; k < count; k++, r++) {
+                const uint8_t *rec = in + L.off_esc + 3 * r;
+                uint64_t i = b * SZO_BLOCK + get_u16(rec);
+                out[i] = bf16_join(bf16_sign(out[i]), rec[2], bf16_mantissa(out[i]));
+            }
+        }
+    }
+    return SZO_OK;
+}
