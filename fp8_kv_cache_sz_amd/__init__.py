@@ -15,12 +15,17 @@ from dataclasses import dataclass
 import torch
 
 from . import _native
-from ._native import SZ_BF16, SZ_FP8_E5M2, SplitZipError
+from ._native import (SZ_BF16, SZ_FP8_E5M2, SZ_FORMAT_TOP16, SZ_FORMAT_TOP8, SZ_FORMAT_TOP15_SENTINEL,
+                      SplitZipError)
 
 BF16 = SZ_BF16
 E5M2 = SZ_FP8_E5M2
+# stream formats: the page's Top-16 design and its two ablation alternatives (BF16 only)
+TOP16 = SZ_FORMAT_TOP16
+TOP8 = SZ_FORMAT_TOP8
+TOP15S = SZ_FORMAT_TOP15_SENTINEL
 
-__all__ = ["BF16", "E5M2", "Codebook", "SplitZipError", "calibrate", "calibrate_device",
+__all__ = ["BF16", "E5M2", "TOP16", "TOP8", "TOP15S", "Codebook", "SplitZipError", "calibrate", "calibrate_device",
            "codebook_from_device", "encoded_size", "workspace_size", "workspace", "encode", "decode",
            "read_escape_count", "profile_enable", "profile_collect"]
 
@@ -99,8 +104,10 @@ def codebook_from_device(d_cb: torch.Tensor) -> Codebook:
     return Codebook(int(raw[:4].view(torch.int32)[0]), tuple(int(x) for x in raw[4:20]))
 
 
-def encoded_size(dtype: int, n: int, n_escapes: int) -> int:
-    return _native.sz_encoded_size(dtype, n, n_escapes)
+def encoded_size(dtype: int, n: int, n_escapes: int, fmt: int = TOP16) -> int:
+    if fmt == TOP16:
+        return _native.sz_encoded_size(dtype, n, n_escapes)
+    return _native.sz_encoded_size_format(fmt, dtype, n, n_escapes)
 
 
 def workspace_size(dtype: int, n: int) -> int:
@@ -117,26 +124,33 @@ def read_escape_count(buf: torch.Tensor) -> int:
 
 
 def encode(x: torch.Tensor, cb, out: torch.Tensor | None = None,
-           ws: torch.Tensor | None = None, stream=None, sync: bool = True):
+           ws: torch.Tensor | None = None, stream=None, sync: bool = True, fmt: int = TOP16):
     """Encode a device tensor with a host ``Codebook`` (sz_encode) or a device
     codebook tensor from ``calibrate_device`` (sz_encode_devcb).  Returns
     ``(buf, size, escapes)``; with ``sync=False`` the call only enqueues the
     kernels and returns ``(buf, None, None)`` (the size is known once the
-    stream has run)."""
+    stream has run).  ``fmt`` selects an ablation format (TOP8, TOP15S; BF16
+    with a host codebook only)."""
     dtype = dtype_of(x)
     on_device = isinstance(cb, torch.Tensor)
+    if fmt != TOP16 and on_device:
+        raise ValueError("the ablation formats take a host Codebook")
     if not on_device and cb.dtype != dtype:
         raise SplitZipError("sz_encode", -2)
     x = x.reshape(-1)
     if not x.is_contiguous():
         raise ValueError("encode needs a contiguous tensor")
     n = x.numel()
-    cap = encoded_size(dtype, n, n)
+    cap = encoded_size(dtype, n, n, fmt)
     if out is None:
-        out = torch.empty(cap, dtype=torch.uint8, device=x.device)
+        out = torch.empty(max(cap, 1), dtype=torch.uint8, device=x.device)
     if ws is None:
         ws = workspace(dtype, n, x.device)
-    if on_device:
+    if fmt != TOP16:
+        rc = _native.sz_encode_format(fmt, dtype, x.data_ptr() if n else None, n, cb.to_c(), out.data_ptr(),
+                                      out.numel(), ws.data_ptr(), ws.numel(), _stream_handle(stream, x.device))
+        _native.check("sz_encode_format", rc)
+    elif on_device:
         rc = _native.sz_encode_devcb(dtype, x.data_ptr() if n else None, n, cb.data_ptr(), out.data_ptr(),
                                      out.numel(), ws.data_ptr(), ws.numel(), _stream_handle(stream, x.device))
         _native.check("sz_encode_devcb", rc)
@@ -151,12 +165,12 @@ def encode(x: torch.Tensor, cb, out: torch.Tensor | None = None,
         if status != 0:
             raise SplitZipError("sz_encode_devcb (device codebook check)", status)
     escapes = read_escape_count(out)
-    return out, encoded_size(dtype, n, escapes), escapes
+    return out, encoded_size(dtype, n, escapes, fmt), escapes
 
 
 def decode(buf: torch.Tensor, dtype: int, n: int, out: torch.Tensor | None = None,
            ws: torch.Tensor | None = None, stream=None, check: bool = True,
-           in_bytes: int | None = None) -> torch.Tensor:
+           in_bytes: int | None = None, fmt: int = TOP16) -> torch.Tensor:
     """Decode a device stream into ``n`` values.  With ``check`` the call
     synchronises and raises if the device-side validation failed."""
     if out is None:
@@ -166,9 +180,14 @@ def decode(buf: torch.Tensor, dtype: int, n: int, out: torch.Tensor | None = Non
     if ws is None:
         ws = workspace(dtype, n, buf.device)
     nbytes = buf.numel() if in_bytes is None else in_bytes
-    rc = _native.sz_decode(buf.data_ptr(), nbytes, dtype, out.data_ptr() if n else None, n,
-                           ws.data_ptr(), ws.numel(), _stream_handle(stream, buf.device))
-    _native.check("sz_decode", rc)
+    if fmt != TOP16:
+        rc = _native.sz_decode_format(fmt, buf.data_ptr(), nbytes, dtype, out.data_ptr() if n else None, n,
+                                      ws.data_ptr(), ws.numel(), _stream_handle(stream, buf.device))
+        _native.check("sz_decode_format", rc)
+    else:
+        rc = _native.sz_decode(buf.data_ptr(), nbytes, dtype, out.data_ptr() if n else None, n,
+                               ws.data_ptr(), ws.numel(), _stream_handle(stream, buf.device))
+        _native.check("sz_decode", rc)
     if check:
         status = int(ws[:4].cpu().view(torch.int32)[0])
         if status != 0:

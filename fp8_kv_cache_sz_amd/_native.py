@@ -55,6 +55,12 @@ lib.sz_calibrate_workspace_size.argtypes = [_i32]
 lib.sz_calibrate_workspace_size.restype = _u64
 lib.sz_calibrate_device.argtypes = [_i32, _vp, _u64, _u64, _vp, _vp, _vp, _u64, _vp]
 lib.sz_calibrate_device.restype = _i32
+lib.sz_encoded_size_format.argtypes = [_i32, _i32, _u64, _u64]
+lib.sz_encoded_size_format.restype = _u64
+lib.sz_encode_format.argtypes = [_i32, _i32, _vp, _u64, ctypes.POINTER(sz_codebook), _vp, _u64, _vp, _u64, _vp]
+lib.sz_encode_format.restype = _i32
+lib.sz_decode_format.argtypes = [_i32, _vp, _u64, _i32, _vp, _u64, _vp, _u64, _vp]
+lib.sz_decode_format.restype = _i32
 lib.sz_decode.argtypes = [_vp, _u64, _i32, _vp, _u64, _vp, _u64, _vp]
 lib.sz_decode.restype = _i32
 lib.sz_profile_enable.argtypes = [_i32]
@@ -63,8 +69,12 @@ lib.sz_profile_collect.argtypes = [ctypes.POINTER(sz_kernel_stat), _i32]
 lib.sz_profile_collect.restype = _i32
 
 EXPORTS = ("sz_calibrate", "sz_encoded_size", "sz_workspace_size", "sz_encode", "sz_encode_devcb",
-           "sz_calibrate_workspace_size", "sz_calibrate_device", "sz_decode", "sz_profile_enable",
-           "sz_profile_collect")
+           "sz_calibrate_workspace_size", "sz_calibrate_device", "sz_decode", "sz_encoded_size_format",
+           "sz_encode_format", "sz_decode_format", "sz_profile_enable", "sz_profile_collect")
+
+SZ_FORMAT_TOP16 = 1
+SZ_FORMAT_TOP8 = 2
+SZ_FORMAT_TOP15_SENTINEL = 3
 
 
 class SplitZipError(RuntimeError):
@@ -108,6 +118,19 @@ def sz_calibrate_workspace_size(dtype: int) -> int:
 
 def sz_calibrate_device(dtype, d_in, n, sample_every, d_cb, d_hist, d_ws, ws_bytes, stream) -> int:
     return int(lib.sz_calibrate_device(dtype, d_in, n, sample_every, d_cb, d_hist, d_ws, ws_bytes, stream))
+
+
+def sz_encoded_size_format(fmt: int, dtype: int, n: int, n_escapes: int) -> int:
+    return int(lib.sz_encoded_size_format(fmt, dtype, n, n_escapes))
+
+
+def sz_encode_format(fmt, dtype, d_in, n, cb, d_out, out_capacity, d_ws, ws_bytes, stream) -> int:
+    return int(lib.sz_encode_format(fmt, dtype, d_in, n, ctypes.byref(cb), d_out, out_capacity, d_ws, ws_bytes,
+                                    stream))
+
+
+def sz_decode_format(fmt, d_in, in_bytes, dtype, d_out, n, d_ws, ws_bytes, stream) -> int:
+    return int(lib.sz_decode_format(fmt, d_in, in_bytes, dtype, d_out, n, d_ws, ws_bytes, stream))
 
 
 def sz_decode(d_in, in_bytes, dtype, d_out, n, d_ws, ws_bytes, stream) -> int:

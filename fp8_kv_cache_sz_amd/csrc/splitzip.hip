@@ -38,7 +38,6 @@ namespace {
 
 constexpr uint64_t kBlock = 65536;          // elements per escape-position block
 constexpr uint32_t kMagic = 0x50495A53u;    // "SZIP"
-constexpr uint32_t kVersion = 1;
 constexpr uint32_t kLog2Block = 16;
 
 // Every dense kernel gives each lane 64 elements of one 4096-element row per
@@ -58,14 +57,16 @@ struct Geometry {
     uint64_t off_nib, nib_bytes, off_sm, sm_bytes, off_esc;
 };
 
-Geometry geometry(int dtype, uint64_t n)
+// Section offsets of a stream; version 2 (Top-8) has 3-bit codes, the
+// others 4-bit codes.
+Geometry geometry(int dtype, uint64_t n, uint32_t version = 1)
 {
     Geometry g;
     g.n = n;
     g.nb = (n + kBlock - 1) / kBlock;
     g.nt = (n + kEncTile - 1) / kEncTile;
     g.off_nib = up256(64 + 4 * g.nb);
-    g.nib_bytes = (n + 1) / 2;
+    g.nib_bytes = version == 2 ? 3 * ((n + 7) / 8) : (n + 1) / 2;
     g.off_sm = g.off_nib + up256(g.nib_bytes);
     g.sm_bytes = dtype == SZ_BF16 ? n : 3 * ((n + 7) / 8);
     g.off_esc = g.off_sm + up256(g.sm_bytes);
@@ -165,11 +166,13 @@ __device__ __forceinline__ Codebook4 load_codebook(const uint32_t *cb_dev)
     return cb;
 }
 
-// Exponent -> code table for encode.  Byte v = code of exponent v, or 0x80
-// (code 0 with the escape flag) when v is not in the codebook.  Threads
-// 0..63 fill 4 entries each.
+// Exponent -> code table for encode.  Byte v = code of exponent v, or
+// `escape` (the escape flag 0x80 plus the code an escaped element carries)
+// when v is not among the first `entries` codebook entries.  Threads 0..63
+// fill 4 entries each.
 __device__ __forceinline__ void build_encode_table(uint32_t *table32, const Codebook4 &cb,
-                                                   uint32_t symbols)
+                                                   uint32_t symbols, uint32_t entries = 16,
+                                                   uint32_t escape = 0x80u)
 {
     const uint32_t t = threadIdx.x;
     if (t < 64 && t * 4 < symbols) {
@@ -177,10 +180,10 @@ __device__ __forceinline__ void build_encode_table(uint32_t *table32, const Code
 #pragma unroll
         for (uint32_t k = 0; k < 4; ++k) {
             const uint32_t v = t * 4 + k;
-            uint32_t code = 0x80u;
+            uint32_t code = escape;
 #pragma unroll
             for (uint32_t c = 0; c < 16; ++c)
-                if (cb_entry(cb, c) == v) code = c;
+                if (c < entries && cb_entry(cb, c) == v) code = c;
             word |= code << (8 * k);
         }
         table32[t] = word;
@@ -218,6 +221,17 @@ __device__ __forceinline__ uint32_t escape_mask8(uint32_t c_a, uint32_t c_b)
 //   nib: 4 bytes of codes;  sm: 8 sign/mantissa bytes (sign << 7 | mantissa7)
 //   esc: escape mask (bit k = element k);  ex: exponent of element k in byte k
 // ---------------------------------------------------------------------------
+// Version 2 (Top-8) packing: 3-bit codes of 8 elements (table bytes c_a =
+// elements 0..3, c_b = 4..7) -> 24 bits, element k at bit 3k.
+__device__ __forceinline__ uint32_t pack_codes8_top8(uint32_t c_a, uint32_t c_b)
+{
+    const uint32_t t_a = c_a & 0x07070707u, t_b = c_b & 0x07070707u;
+    const uint32_t u_a = (t_a & 7u) | ((t_a >> 5) & 0x38u) | ((t_a >> 10) & 0x1C0u) | ((t_a >> 15) & 0xE00u);
+    const uint32_t u_b = (t_b & 7u) | ((t_b >> 5) & 0x38u) | ((t_b >> 10) & 0x1C0u) | ((t_b >> 15) & 0xE00u);
+    return u_a | (u_b << 12);
+}
+
+template <int V = 1>
 __device__ __forceinline__ void encode_chunk_bf16(const uint4 q, const uint8_t *table, uint32_t &nib,
                                                   uint2 &sm, uint32_t &esc, uint64_t &ex)
 {
@@ -231,7 +245,7 @@ __device__ __forceinline__ void encode_chunk_bf16(const uint4 q, const uint8_t *
     const uint32_t e_b = ((hi_b << 1) & 0xFEFEFEFEu) | ((lo_b >> 7) & 0x01010101u);
     const uint32_t c_a = lookup4(table, e_a);
     const uint32_t c_b = lookup4(table, e_b);
-    nib = pack_codes8(c_a, c_b);
+    nib = V == 2 ? pack_codes8_top8(c_a, c_b) : pack_codes8(c_a, c_b);
     esc = escape_mask8(c_a, c_b);
     ex = (uint64_t)e_a | ((uint64_t)e_b << 32);
 }
@@ -421,6 +435,38 @@ __device__ __forceinline__ uint32_t workgroup_wave_prefix(uint32_t wave_total, u
 // ---------------------------------------------------------------------------
 constexpr int kBf16Chunks = 8;
 
+// Format versions: 1 = Top-16 (the page's design), 2 = Top-8 (3-bit codes,
+// position records), 3 = Top-15 with code 15 as escape sentinel (one
+// exponent byte per escape, no positions).  2 and 3 are the ablation
+// alternatives of the page (Method, decoding design-choice bullet; Results,
+// ablations) and exist for BF16 only.
+constexpr uint32_t kTop16 = 1, kTop8 = 2, kTop15S = 3;
+__host__ __device__ constexpr uint32_t book_entries(uint32_t v) { return v == kTop8 ? 8 : v == kTop15S ? 15 : 16; }
+__host__ __device__ constexpr uint32_t escape_item_bytes(uint32_t v) { return v == kTop15S ? 1 : 3; }
+
+// Version 3 staging: the exponent bytes of the escaped elements of 8
+// elements, into an LDS buffer at `off` (returns the byte after them) or
+// straight into the staging slot at item `rank`.
+__device__ __forceinline__ uint32_t lds_put_exponents(uint8_t *buf, uint32_t off, uint32_t esc, uint64_t ex)
+{
+    while (esc) {
+        const uint32_t k = (uint32_t)__builtin_ctz(esc);
+        esc &= esc - 1;
+        buf[off++] = (uint8_t)(ex >> (8 * k));
+    }
+    return off;
+}
+
+__device__ __forceinline__ void put_exponents(uint8_t *tstage, uint32_t rank, uint32_t esc, uint64_t ex)
+{
+    while (esc) {
+        const uint32_t k = (uint32_t)__builtin_ctz(esc);
+        esc &= esc - 1;
+        tstage[rank++] = (uint8_t)(ex >> (8 * k));
+    }
+}
+
+template <int V>
 __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t *__restrict__ in, uint64_t n,
                                                               uint8_t *__restrict__ out, uint64_t off_nib,
                                                               uint64_t off_sm, Codebook4 cb,
@@ -455,9 +501,10 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
         }
     }
     if (cb_dev) cb = load_codebook(cb_dev);
-    build_encode_table(table32, cb, 256);
+    build_encode_table(table32, cb, 256, book_entries(V), V == kTop15S ? 0x8Fu : 0x80u);
     __syncthreads();
     const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
+    uint8_t *buf = seg_buf[wave];
     uint32_t esc[kBf16Chunks];
     uint32_t cnt[kBf16Chunks];
 #pragma unroll
@@ -466,10 +513,10 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
         uint32_t nib;
         uint2 sm;
         uint64_t ex;
-        encode_chunk_bf16(q[j], table, nib, sm, esc[j], ex);
+        encode_chunk_bf16<V>(q[j], table, nib, sm, esc[j], ex);
         if (esc[j]) ex_park[wave][j][lane] = ex;
         if (full_row || c0 + 8 <= n) {
-            store_nt(reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2), nib);
+            if (V != kTop8) store_nt(reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2), nib);
             store_nt(reinterpret_cast<uint2 *>(out + off_sm + c0), sm);
         } else if (c0 < n) {
             // last, partial chunk: missing elements get code 0, sign/mantissa 0
@@ -477,39 +524,71 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
             const uint32_t valid = (uint32_t)(n - c0);
             const uint64_t keep = (1ull << (8 * valid)) - 1;
             esc[j] &= (1u << valid) - 1;
-            nib &= (uint32_t)((1ull << (4 * valid)) - 1);
+            nib &= (uint32_t)((1ull << ((V == kTop8 ? 3 : 4) * valid)) - 1);
             const uint64_t smv = ((uint64_t)sm.y << 32 | sm.x) & keep;
-            *reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2) = nib;
+            if (V != kTop8) *reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2) = nib;
             *reinterpret_cast<uint2 *>(out + off_sm + c0) = make_uint2((uint32_t)smv, (uint32_t)(smv >> 32));
         } else {
             esc[j] = 0;
+            nib = 0;
+        }
+        if (V == kTop8) {
+            // 3 code bytes per chunk: the wave's row of codes (1536 bytes) is
+            // assembled in LDS and stored as whole dwords below
+            const uint32_t o = j * 192 + 3 * lane;
+            buf[o] = (uint8_t)nib;
+            buf[o + 1] = (uint8_t)(nib >> 8);
+            buf[o + 2] = (uint8_t)(nib >> 16);
         }
         cnt[j] = __popc(esc[j]);
+    }
+    if (V == kTop8) {
+        // the row's code bytes start at 3 * base / 8, a multiple of 1536;
+        // dwords past the section's last byte hold only padding and are skipped
+        wave_lds_fence();
+        const uint64_t row0 = 3 * (base / 8);
+        const uint64_t code_bytes = 3 * ((n + 7) / 8);
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const uint32_t d = i * 64 + lane;
+            if (row0 + 4 * d < code_bytes)
+                *reinterpret_cast<uint32_t *>(out + off_nib + row0 + 4 * d) = reinterpret_cast<const uint32_t *>(buf)[d];
+        }
+        wave_lds_fence();
     }
     uint32_t row_base[kBf16Chunks], row_total[kBf16Chunks], lane_before[kBf16Chunks];
     const uint32_t wave_total = wave_chunk_ranks<kBf16Chunks>(cnt, row_base, row_total, lane_before);
     uint32_t tile_total;
     const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
-    if (wave_total && tile_total <= kRederiveRecords) {
+    // only the Top-16 format re-derives escape-heavy tiles in the compaction
+    const bool rederive = V == kTop16 && tile_total > kRederiveRecords;
+    if (wave_total && !rederive) {
         uint8_t *tstage = stage + tile * (3ull * kEncTile);
-        uint8_t *buf = seg_buf[wave];
 #pragma unroll
         for (int j = 0; j < kBf16Chunks; ++j) {
             const uint32_t pos0 = (uint32_t)((base + (uint64_t)(j * 64 + lane) * 8) & 0xFFFFu);
             const uint32_t rank = wave_before + row_base[j];
+            constexpr uint32_t item = escape_item_bytes(V);
             if (row_total[j] <= kDirectRecords) {                      // wave-uniform
-                if (esc[j]) put_records(tstage, rank + lane_before[j], esc[j], ex_park[wave][j][lane], pos0);
+                if (esc[j]) {
+                    if (V == kTop15S) put_exponents(tstage, rank + lane_before[j], esc[j], ex_park[wave][j][lane]);
+                    else put_records(tstage, rank + lane_before[j], esc[j], ex_park[wave][j][lane], pos0);
+                }
             } else {
-                const uint32_t g0 = 3 * rank;
-                if (esc[j])
-                    lds_put_records(buf, (g0 & 3) + 3 * lane_before[j], esc[j], ex_park[wave][j][lane], pos0);
+                const uint32_t g0 = item * rank;
+                if (esc[j]) {
+                    if (V == kTop15S)
+                        lds_put_exponents(buf, (g0 & 3) + lane_before[j], esc[j], ex_park[wave][j][lane]);
+                    else
+                        lds_put_records(buf, (g0 & 3) + 3 * lane_before[j], esc[j], ex_park[wave][j][lane], pos0);
+                }
                 wave_lds_fence();
-                flush_segment(buf, tstage, g0, 3 * row_total[j]);
+                flush_segment(buf, tstage, g0, item * row_total[j]);
                 wave_lds_fence();
             }
         }
     }
-    if (threadIdx.x == 0) tile_counts[tile] = tile_total | (tile_total > kRederiveRecords ? kRederiveFlag : 0u);
+    if (threadIdx.x == 0) tile_counts[tile] = tile_total | (rederive ? kRederiveFlag : 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -710,7 +789,7 @@ __device__ __forceinline__ void scan_batch(const uint32_t (&x)[kScanBatch], uint
 
 struct HeaderArgs {
     uint64_t n, nb;
-    uint32_t dtype;
+    uint32_t dtype, version;
     Codebook4 cb;
     uint64_t pad_start[3], pad_end[3];
 };
@@ -781,7 +860,7 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
         uint32_t w = 0;
         switch (tid) {
         case 0: w = verdict ? 0u : kMagic; break;
-        case 1: w = kVersion | (h.dtype << 16) | (kLog2Block << 24); break;
+        case 1: w = h.version | (h.dtype << 16) | (kLog2Block << 24); break;
         case 2: w = (uint32_t)h.n; break;
         case 3: w = (uint32_t)(h.n >> 32); break;
         case 4: w = (uint32_t)total; break;
@@ -973,7 +1052,8 @@ template <int DT>
 __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_compact(
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
     const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
-    uint64_t nb, const void *__restrict__ in, uint64_t n, Codebook4 cb, const uint32_t *__restrict__ cb_dev)
+    uint64_t nb, const void *__restrict__ in, uint64_t n, Codebook4 cb, const uint32_t *__restrict__ cb_dev,
+    uint32_t item)
 {
     __shared__ uint32_t table32[64];
     __shared__ __align__(16) uint8_t seg_buf[kCompactThreads / 64][kSegBytes];
@@ -1009,14 +1089,14 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
                 k = cnt[t];
                 bef = before[t];
             }
-        if (k) copy_records(stage + (t0 + g) * (3ull * kEncTile), out, off_esc + 3 * (off + bef), 3 * k, lane & 15, 16);
+        if (k) copy_records(stage + (t0 + g) * (3ull * kEncTile), out, off_esc + item * (off + bef), item * k, lane & 15, 16);
         return;
     }
     uint8_t *buf = seg_buf[threadIdx.x / 64];
 #pragma unroll
     for (uint32_t t = 0; t < kTilesPerBlock; ++t) {
         if (cnt[t] == 0) continue;
-        const uint64_t dst0 = off_esc + 3 * (off + before[t]);
+        const uint64_t dst0 = off_esc + item * (off + before[t]);
         if ((rederive >> t) & 1) {
             const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
             if (DT == SZ_BF16)
@@ -1026,7 +1106,7 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
                 rederive_tile_e5m2(static_cast<const uint8_t *>(in), n, t0 + t, table, buf, out + (dst0 & ~uint64_t(3)),
                                    (uint32_t)(dst0 & 3));
         } else {
-            copy_records(stage + (t0 + t) * (3ull * kEncTile), out, dst0, 3 * cnt[t], lane, 64);
+            copy_records(stage + (t0 + t) * (3ull * kEncTile), out, dst0, item * cnt[t], lane, 64);
         }
     }
 }
@@ -1042,6 +1122,7 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
 struct DecodeArgs {
     uint64_t n, nb, in_bytes, off_nib, off_sm, off_esc;
     uint32_t dtype, symbols;
+    uint32_t version, item, entries;      // format version, escape item bytes, codebook entries used
 };
 
 __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__restrict__ in, DecodeArgs a,
@@ -1056,13 +1137,14 @@ __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__res
     const uint32_t w1 = h32[1];
     const uint64_t n_hdr = (uint64_t)h32[2] | ((uint64_t)h32[3] << 32);
     const uint64_t e_hdr = (uint64_t)h32[4] | ((uint64_t)h32[5] << 32);
-    if (h32[0] != kMagic || (w1 & 0xFFFFu) != kVersion || (w1 >> 24) != kLog2Block) err = SZ_E_FORMAT;
+    if (h32[0] != kMagic || (w1 & 0xFFFFu) != a.version || (w1 >> 24) != kLog2Block) err = SZ_E_FORMAT;
     else if (((w1 >> 16) & 0xFFu) != a.dtype) err = SZ_E_DTYPE;
     else if (n_hdr != a.n || h32[6] != (uint32_t)a.nb || h32[7] != 0) err = SZ_E_FORMAT;
-    else if (e_hdr > a.n || a.off_esc + 3 * e_hdr > a.in_bytes) err = SZ_E_FORMAT;
+    else if (e_hdr > a.n || a.off_esc + a.item * e_hdr > a.in_bytes) err = SZ_E_FORMAT;
     else {
+        // used entries must be exponent values, unused ones zero
         for (uint32_t c = 0; c < 16; ++c)
-            if (in[32 + c] >= a.symbols) err = SZ_E_FORMAT;
+            if (c < a.entries ? in[32 + c] >= a.symbols : in[32 + c] != 0) err = SZ_E_FORMAT;
     }
     if (err) {
         if (tid == 0) {
@@ -1395,6 +1477,198 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__rest
         const uint32_t c = rbase + (j * 64 + lane) * 8;
         if (c >= blen) continue;
         uint4 o = decode_chunk_bf16(nib[j], sm[j], table);
+        if (k) {
+            uint32_t r = first[c >> 3];
+            if (r != kNoEscape) {
+                for (; r < k; ++r) {
+                    const uint32_t v = rec[r];
+                    if (((v & 0xFFFFu) >> 3) != (c >> 3)) break;
+                    patch_bf16(o, v & 7, v >> 16);
+                }
+            }
+        }
+        const uint64_t g = e0 + c;
+        if (full_row || c + 8 <= blen) {
+            store_nt(reinterpret_cast<uint4 *>(out + g), o);
+        } else {
+            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+            for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode of the ablation formats (BF16), in the shape of sz_dec_bf16: one
+// 1024-lane workgroup per 64K block, one 4096-element row per wave, eight
+// 8-element chunks per lane, one store per chunk.
+//   Version 2 (Top-8): a chunk's codes are the 3 bytes at 3 * chunk, taken
+//   from two aligned words; a 64-entry LDS table turns each pair of 3-bit
+//   codes into both exponents.  Escapes are position records, patched as in
+//   sz_dec_bf16 (an LDS map for blocks with up to kMappedEscapes records,
+//   the exponent plane above that).
+//   Version 3 (Top-15 + sentinel): nibble codes as in version 1, code 15
+//   marks an escape whose exponent is the next byte of the block's escape
+//   bytes.  Each sentinel's rank inside its block comes from per-chunk
+//   counts, a wave prefix sum and a prefix over the waves; the block's
+//   sentinels must number exactly its count.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 decode_chunk_top8(uint32_t code24, uint2 sm, const uint32_t *table64)
+{
+    // table64[p] = cb[p & 7] << 7 | cb[p >> 3] << 23 for a pair p of 3-bit codes
+    uint4 o;
+    o.x = (perm(sm.x, sm.x, 0x01010000u) & 0x807F807Fu) | table64[code24 & 63u];
+    o.y = (perm(sm.x, sm.x, 0x03030202u) & 0x807F807Fu) | table64[(code24 >> 6) & 63u];
+    o.z = (perm(sm.y, sm.y, 0x01010000u) & 0x807F807Fu) | table64[(code24 >> 12) & 63u];
+    o.w = (perm(sm.y, sm.y, 0x03030202u) & 0x807F807Fu) | table64[(code24 >> 18) & 63u];
+    return o;
+}
+
+// Four 3-bit codes (12 bits) -> one code per byte, as v_perm selectors.
+__device__ __forceinline__ uint32_t spread_codes3x4(uint32_t x)
+{
+    return (x & 7u) | ((x << 5) & 0x700u) | ((x << 10) & 0x70000u) | ((x << 15) & 0x7000000u);
+}
+
+// Nibbles equal to 15 (the version 3 sentinel): bit 4k set for element k.
+__device__ __forceinline__ uint32_t sentinel_bits(uint32_t nib)
+{
+    return nib & (nib >> 1) & (nib >> 2) & (nib >> 3) & 0x11111111u;
+}
+
+template <int V>
+__global__ __launch_bounds__(kDecThreads) void sz_dec_variant(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                              const uint64_t *__restrict__ block_offsets,
+                                                              int32_t *__restrict__ status,
+                                                              uint16_t *__restrict__ out)
+{
+    __shared__ uint32_t table[256];
+    __shared__ uint32_t wave_totals[kDecThreads / 64];
+    __shared__ __align__(16) uint8_t pool[V == kTop8 ? kBlock : 16];
+    uint16_t *first = reinterpret_cast<uint16_t *>(pool);
+    uint32_t *rec = reinterpret_cast<uint32_t *>(pool + kBlock / 4);
+    uint8_t *plane = pool;
+    if (status[1] != 0) return;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t b = blockIdx.x;
+    const uint64_t e0 = b * kBlock;
+    const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
+    const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
+    const uint64_t r0 = block_offsets[b];
+    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
+    const uint8_t *esc = in + a.off_esc;
+    const bool heavy = V == kTop8 && k > kMappedEscapes;          // workgroup-uniform
+    if (V == kTop8) {
+        if (tid < 64) table[tid] = ((uint32_t)in[32 + (tid & 7)] << 7) | ((uint32_t)in[32 + (tid >> 3)] << 23);
+    } else if (tid < 256) {
+        table[tid] = ((uint32_t)in[32 + (tid & 15)] << 7) | ((uint32_t)in[32 + (tid >> 4)] << 23);
+    }
+    const uint32_t lane = lane_id();
+    const uint32_t rbase = (tid / 64) * kRow;
+    const bool full_row = rbase + kRow <= blen;
+    uint32_t code[kBf16Chunks];
+    uint2 sm[kBf16Chunks];
+#pragma unroll
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + lane) * 8;
+        const uint64_t g = e0 + c;
+        code[j] = 0;
+        sm[j] = make_uint2(0, 0);
+        if (full_row || c < blen) {
+            if (V == kTop8) {
+                const uint64_t byte0 = 3 * (g / 8);
+                const uint32_t *w = reinterpret_cast<const uint32_t *>(in + a.off_nib + (byte0 & ~uint64_t(3)));
+                code[j] = __builtin_amdgcn_alignbit(w[1], w[0], 8 * (uint32_t)(byte0 & 3)) & 0xFFFFFFu;
+            } else {
+                code[j] = load_nt(reinterpret_cast<const uint32_t *>(in + a.off_nib + g / 2));
+            }
+            sm[j] = load_nt(reinterpret_cast<const uint2 *>(in + a.off_sm + g));
+        }
+    }
+    if (V == kTop15S) {
+        // ranks of the sentinels inside the block
+        uint32_t sbits[kBf16Chunks], cnt[kBf16Chunks];
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            sbits[j] = sentinel_bits(code[j]);
+            if (c >= blen) sbits[j] = 0;
+            else if (c + 8 > blen) sbits[j] &= (1u << (4 * (blen - c))) - 1;   // padding nibbles do not count
+            cnt[j] = __popc(sbits[j]);
+        }
+        uint32_t row_base[kBf16Chunks], row_total[kBf16Chunks], lane_before[kBf16Chunks];
+        const uint32_t wave_total = wave_chunk_ranks<kBf16Chunks>(cnt, row_base, row_total, lane_before);
+        uint32_t block_total;
+        const uint32_t wave_before = workgroup_wave_prefix<kDecThreads / 64>(wave_total, wave_totals, block_total);
+        bool bad = block_total != k;
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            if (c >= blen) continue;
+            uint4 o = decode_chunk_bf16(code[j], sm[j], table);
+            uint32_t rank = wave_before + row_base[j] + lane_before[j];
+            for (uint32_t m = sbits[j]; m; m &= m - 1, ++rank) {
+                uint32_t e = 0;
+                if (rank < k) e = esc[r0 + rank];
+                else bad = true;
+                patch_bf16(o, (uint32_t)__builtin_ctz(m) / 4, e);
+            }
+            const uint64_t g = e0 + c;
+            if (full_row || c + 8 <= blen) {
+                store_nt(reinterpret_cast<uint4 *>(out + g), o);
+            } else {
+                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+            }
+        }
+        if (bad) atomicExch(status, SZ_E_FORMAT);
+        return;
+    }
+    // version 2: position records
+    if (heavy) {
+        const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
+        const uint32_t cb0 = cbw[0], cb1 = cbw[1];
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            if (c < blen)
+                *reinterpret_cast<uint2 *>(plane + c) = make_uint2(perm(cb1, cb0, spread_codes3x4(code[j] & 0xFFFu)),
+                                                                   perm(cb1, cb0, spread_codes3x4(code[j] >> 12)));
+        }
+        __syncthreads();
+        overwrite_exponents(esc, r0, k, blen, 256, e_total, plane, status);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            if (c >= blen) continue;
+            const uint2 ex = *reinterpret_cast<const uint2 *>(plane + c);
+            uint4 o;
+            o.x = (perm(sm[j].x, sm[j].x, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C010C00u) << 7);
+            o.y = (perm(sm[j].x, sm[j].x, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C030C02u) << 7);
+            o.z = (perm(sm[j].y, sm[j].y, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C050C04u) << 7);
+            o.w = (perm(sm[j].y, sm[j].y, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C070C06u) << 7);
+            const uint64_t g = e0 + c;
+            if (full_row || c + 8 <= blen) {
+                store_nt(reinterpret_cast<uint4 *>(out + g), o);
+            } else {
+                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+            }
+        }
+        return;
+    }
+    if (k) {
+        reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+        load_block_records(esc, r0, k, e_total, rec);
+    }
+    __syncthreads();
+    if (k) map_block_escapes<3>(rec, k, blen, 256, first, status);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + lane) * 8;
+        if (c >= blen) continue;
+        uint4 o = decode_chunk_top8(code[j], sm[j], table);
         if (k) {
             uint32_t r = first[c >> 3];
             if (r != kNoEscape) {
@@ -1837,16 +2111,23 @@ extern "C" uint64_t sz_workspace_size(int dtype, uint64_t n_elems)
 
 namespace {
 
-// Encode behind sz_encode (host codebook cb4) and sz_encode_devcb (cb_dev).
-int encode_impl(int dtype, const void *d_in, uint64_t n_elems, const Codebook4 &cb4, const uint32_t *cb_dev,
-                void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream)
+uint64_t encoded_size_v(uint32_t version, int dtype, uint64_t n, uint64_t e)
+{
+    return geometry(dtype, n, version).off_esc + escape_item_bytes(version) * e;
+}
+
+// Encode behind sz_encode (host codebook cb4), sz_encode_devcb (cb_dev) and
+// sz_encode_format (version 2, 3).
+int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems, const Codebook4 &cb4,
+                const uint32_t *cb_dev, void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes,
+                void *stream)
 {
     if (n_elems > kMaxElems) return SZ_E_ARG;
     if (!d_out || !d_ws || (n_elems && !d_in)) return SZ_E_ARG;
     if (!aligned16(d_out) || !aligned16(d_ws) || (n_elems && !aligned16(d_in))) return SZ_E_ALIGN;
-    if (out_capacity < sz_encoded_size(dtype, n_elems, n_elems)) return SZ_E_CAPACITY;
+    if (out_capacity < encoded_size_v(version, dtype, n_elems, n_elems)) return SZ_E_CAPACITY;
     if (ws_bytes < sz_workspace_size(dtype, n_elems)) return SZ_E_WORKSPACE;
-    const Geometry g = geometry(dtype, n_elems);
+    const Geometry g = geometry(dtype, n_elems, version);
     const WsLayout w = ws_layout(dtype, n_elems);
     uint8_t *ws = static_cast<uint8_t *>(d_ws);
     uint8_t *out = static_cast<uint8_t *>(d_out);
@@ -1857,10 +2138,20 @@ int encode_impl(int dtype, const void *d_in, uint64_t n_elems, const Codebook4 &
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if (g.nt && dtype == SZ_BF16) {
-        LaunchScope scope("sz_enc_dense_bf16", s);
-        hipLaunchKernelGGL(sz_enc_dense_bf16, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s,
-                           static_cast<const uint16_t *>(d_in), g.n, out, g.off_nib, g.off_sm, cb4, cb_dev,
-                           tile_counts, stage);
+        const uint16_t *in16 = static_cast<const uint16_t *>(d_in);
+        if (version == kTop8) {
+            LaunchScope scope("sz_enc_dense_top8", s);
+            hipLaunchKernelGGL(sz_enc_dense_bf16<kTop8>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16, g.n,
+                               out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage);
+        } else if (version == kTop15S) {
+            LaunchScope scope("sz_enc_dense_top15s", s);
+            hipLaunchKernelGGL(sz_enc_dense_bf16<kTop15S>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16,
+                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage);
+        } else {
+            LaunchScope scope("sz_enc_dense_bf16", s);
+            hipLaunchKernelGGL(sz_enc_dense_bf16<kTop16>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16,
+                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage);
+        }
     } else if (g.nt) {
         LaunchScope scope("sz_enc_dense_e5m2", s);
         hipLaunchKernelGGL(sz_enc_dense_e5m2, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s,
@@ -1872,6 +2163,7 @@ int encode_impl(int dtype, const void *d_in, uint64_t n_elems, const Codebook4 &
         h.n = g.n;
         h.nb = g.nb;
         h.dtype = (uint32_t)dtype;
+        h.version = version;
         h.cb = cb4;
         h.pad_start[0] = 64 + 4 * g.nb;
         h.pad_end[0] = g.off_nib;
@@ -1888,10 +2180,11 @@ int encode_impl(int dtype, const void *d_in, uint64_t n_elems, const Codebook4 &
         const uint32_t groups = (uint32_t)((g.nb + kCompactThreads / 64 - 1) / (kCompactThreads / 64));
         if (dtype == SZ_BF16)
             hipLaunchKernelGGL(sz_enc_compact<SZ_BF16>, dim3(groups), dim3(kCompactThreads), 0, s, stage, tile_counts,
-                               block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev);
+                               block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev,
+                               escape_item_bytes(version));
         else
             hipLaunchKernelGGL(sz_enc_compact<SZ_FP8_E5M2>, dim3(groups), dim3(kCompactThreads), 0, s, stage,
-                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev);
+                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev, 3u);
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }
@@ -1910,8 +2203,37 @@ extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz
         for (int d = 0; d < c; ++d)
             if (cb->exp[d] == cb->exp[c]) return SZ_E_ARG;
     }
-    return encode_impl(dtype, d_in, n_elems, pack_codebook(cb->exp), nullptr, d_out, out_capacity, d_ws, ws_bytes,
-                       stream);
+    return encode_impl(kTop16, dtype, d_in, n_elems, pack_codebook(cb->exp), nullptr, d_out, out_capacity, d_ws,
+                       ws_bytes, stream);
+}
+
+extern "C" uint64_t sz_encoded_size_format(int format, int dtype, uint64_t n_elems, uint64_t n_escapes)
+{
+    if (format == SZ_FORMAT_TOP16) return sz_encoded_size(dtype, n_elems, n_escapes);
+    if ((format != SZ_FORMAT_TOP8 && format != SZ_FORMAT_TOP15_SENTINEL) || dtype != SZ_BF16) return 0;
+    return encoded_size_v((uint32_t)format, dtype, n_elems, n_escapes);
+}
+
+extern "C" int sz_encode_format(int format, int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *cb,
+                                void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (format == SZ_FORMAT_TOP16)
+        return sz_encode(dtype, d_in, n_elems, cb, d_out, out_capacity, d_ws, ws_bytes, stream);
+    if (format != SZ_FORMAT_TOP8 && format != SZ_FORMAT_TOP15_SENTINEL) return SZ_E_ARG;
+    if (dtype != SZ_BF16) return SZ_E_DTYPE;
+    if (!cb) return SZ_E_ARG;
+    if (cb->dtype != (uint32_t)dtype) return SZ_E_DTYPE;
+    // only the first 8 (15) entries are used; they must be distinct, and the
+    // stream's header carries zeros in the others
+    const uint32_t entries = book_entries((uint32_t)format);
+    uint8_t used[16] = {0};
+    for (uint32_t c = 0; c < entries; ++c) {
+        used[c] = cb->exp[c];
+        for (uint32_t d = 0; d < c; ++d)
+            if (cb->exp[d] == cb->exp[c]) return SZ_E_ARG;
+    }
+    return encode_impl((uint32_t)format, dtype, d_in, n_elems, pack_codebook(used), nullptr, d_out, out_capacity,
+                       d_ws, ws_bytes, stream);
 }
 
 extern "C" int sz_encode_devcb(int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *d_cb,
@@ -1921,8 +2243,8 @@ extern "C" int sz_encode_devcb(int dtype, const void *d_in, uint64_t n_elems, co
     if (!d_cb) return SZ_E_ARG;
     if (!aligned16(d_cb)) return SZ_E_ALIGN;
     const uint8_t zero[16] = {0};
-    return encode_impl(dtype, d_in, n_elems, pack_codebook(zero), reinterpret_cast<const uint32_t *>(d_cb), d_out,
-                       out_capacity, d_ws, ws_bytes, stream);
+    return encode_impl(kTop16, dtype, d_in, n_elems, pack_codebook(zero), reinterpret_cast<const uint32_t *>(d_cb),
+                       d_out, out_capacity, d_ws, ws_bytes, stream);
 }
 
 extern "C" uint64_t sz_calibrate_workspace_size(int dtype)
@@ -1973,16 +2295,17 @@ extern "C" int sz_calibrate_device(int dtype, const void *d_in, uint64_t n_elems
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }
 
-extern "C" int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
-                         void *d_ws, uint64_t ws_bytes, void *stream)
+namespace {
+
+int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
+                void *d_ws, uint64_t ws_bytes, void *stream)
 {
-    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
     if (n_elems > kMaxElems) return SZ_E_ARG;
     if (!d_in || !d_ws || (n_elems && !d_out)) return SZ_E_ARG;
     if (!aligned16(d_in) || !aligned16(d_ws) || (n_elems && !aligned16(d_out))) return SZ_E_ALIGN;
-    if (in_bytes < sz_encoded_size(dtype, n_elems, 0)) return SZ_E_FORMAT;
+    if (in_bytes < encoded_size_v(version, dtype, n_elems, 0)) return SZ_E_FORMAT;
     if (ws_bytes < sz_workspace_size(dtype, n_elems)) return SZ_E_WORKSPACE;
-    const Geometry g = geometry(dtype, n_elems);
+    const Geometry g = geometry(dtype, n_elems, version);
     const WsLayout w = ws_layout(dtype, n_elems);
     uint8_t *ws = static_cast<uint8_t *>(d_ws);
     int32_t *status = reinterpret_cast<int32_t *>(ws);
@@ -1997,12 +2320,23 @@ extern "C" int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d
     a.off_esc = g.off_esc;
     a.dtype = (uint32_t)dtype;
     a.symbols = symbols_of(dtype);
+    a.version = version;
+    a.item = escape_item_bytes(version);
+    a.entries = book_entries(version);
     const uint8_t *in = static_cast<const uint8_t *>(d_in);
     {
         LaunchScope scope("sz_dec_scan", s);
         hipLaunchKernelGGL(sz_dec_scan, dim3(1), dim3(kScanThreads), 0, s, in, a, block_offsets, status);
     }
-    if (g.nb && dtype == SZ_BF16) {
+    if (g.nb && version == kTop8) {
+        LaunchScope scope("sz_dec_top8", s);
+        hipLaunchKernelGGL(sz_dec_variant<kTop8>, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a,
+                           block_offsets, status, static_cast<uint16_t *>(d_out));
+    } else if (g.nb && version == kTop15S) {
+        LaunchScope scope("sz_dec_top15s", s);
+        hipLaunchKernelGGL(sz_dec_variant<kTop15S>, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a,
+                           block_offsets, status, static_cast<uint16_t *>(d_out));
+    } else if (g.nb && dtype == SZ_BF16) {
         LaunchScope scope("sz_dec_bf16", s);
         hipLaunchKernelGGL(sz_dec_bf16, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, block_offsets,
                            status, static_cast<uint16_t *>(d_out));
@@ -2012,6 +2346,24 @@ extern "C" int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d
                            status, static_cast<uint8_t *>(d_out));
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
+}
+
+}  // namespace
+
+extern "C" int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
+                         void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    return decode_impl(kTop16, d_in, in_bytes, dtype, d_out, n_elems, d_ws, ws_bytes, stream);
+}
+
+extern "C" int sz_decode_format(int format, const void *d_in, uint64_t in_bytes, int dtype, void *d_out,
+                                uint64_t n_elems, void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (format == SZ_FORMAT_TOP16) return sz_decode(d_in, in_bytes, dtype, d_out, n_elems, d_ws, ws_bytes, stream);
+    if (format != SZ_FORMAT_TOP8 && format != SZ_FORMAT_TOP15_SENTINEL) return SZ_E_ARG;
+    if (dtype != SZ_BF16) return SZ_E_DTYPE;
+    return decode_impl((uint32_t)format, d_in, in_bytes, dtype, d_out, n_elems, d_ws, ws_bytes, stream);
 }
 
 extern "C" int sz_profile_enable(int on)

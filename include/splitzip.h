@@ -138,6 +138,38 @@ int sz_calibrate_device(int dtype, const void *d_in, uint64_t n_elems, uint64_t 
                         sz_codebook *d_cb, uint64_t *d_hist, void *d_ws, uint64_t ws_bytes,
                         void *stream);
 
+/* Ablation formats (page: Method, decoding "design choice" bullet, which
+ * prefers Top-16 with explicit positions to a Top-15 book with a sentinel
+ * code; Results, ablations "Top-16 vs Top-8" and "metadata trade-off").
+ * BF16 only.  A format is the stream's version field:
+ *   SZ_FORMAT_TOP16 (1): the format above (sz_encode / sz_decode).
+ *   SZ_FORMAT_TOP8 (2): the 8 most frequent exponents get 3-bit codes; the
+ *     code section holds 3*ceil(N/8) bytes, bit 3i+k = bit k of element i's
+ *     code; escapes carry code 0 and a 3-byte record as in format 1; header
+ *     codebook bytes 8..15 are 0; size = sections + 3 E.
+ *   SZ_FORMAT_TOP15_SENTINEL (3): codes 0..14 for the 15 most frequent
+ *     exponents, code 15 marks an escape; the escape section holds one byte
+ *     per escape, the original exponent, in ascending element order (no
+ *     positions); header codebook byte 15 is 0; size = sections + E.
+ * Sections are 256-byte aligned as in format 1 (header, u32 counts[nb],
+ * codes, N sign/mantissa bytes, escapes).  sz_encode_format uses the first
+ * 8 (15) entries of cb, which must be distinct; sz_decode_format checks, on
+ * the device, the header (version included), the unused codebook bytes,
+ * the counts, the records (format 2) or that each block's sentinel codes
+ * number exactly its count (format 3).  sz_encoded_size_format returns 0
+ * for an unknown format or a dtype other than BF16 with formats 2 and 3;
+ * the calls return SZ_E_ARG for an unknown format and SZ_E_DTYPE for E5M2
+ * with formats 2 and 3.  Workspace, capacity, alignment and status rules as
+ * for sz_encode / sz_decode; the output capacity is
+ * sz_encoded_size_format(format, dtype, n_elems, n_elems). */
+enum { SZ_FORMAT_TOP16 = 1, SZ_FORMAT_TOP8 = 2, SZ_FORMAT_TOP15_SENTINEL = 3 };
+
+uint64_t sz_encoded_size_format(int format, int dtype, uint64_t n_elems, uint64_t n_escapes);
+int sz_encode_format(int format, int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *cb,
+                     void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream);
+int sz_decode_format(int format, const void *d_in, uint64_t in_bytes, int dtype, void *d_out,
+                     uint64_t n_elems, void *d_ws, uint64_t ws_bytes, void *stream);
+
 /* Decode (page: Method, decoding bullets: dense unpack + lookup table, then
  * the sparse escape stream overwrites the escaped exponents).  d_in: a
  * stream of in_bytes bytes on the device.  d_out: n_elems values.  d_ws:

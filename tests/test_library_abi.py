@@ -132,3 +132,35 @@ def test_host_argument_checks_device_calibration():
     assert nat.sz_encode_devcb(1, dummy, 16, dummy + 4, dummy, cap, dummy, ws, None) == -4
     assert nat.sz_encode_devcb(1, dummy, 16, dummy, dummy, cap - 1, dummy, ws, None) == -3
     assert nat.sz_encode_devcb(1, dummy, 16, dummy, dummy, cap, dummy, ws - 1, None) == -7
+
+
+def test_host_argument_checks_formats():
+    """sz_encode_format / sz_decode_format / sz_encoded_size_format reject bad
+    arguments before any launch, and the sizes match the oracle's."""
+    nat = _native()
+    dummy = 1 << 20
+    cb = nat.sz_codebook()
+    cb.dtype = 0
+    for c in range(16):
+        cb.exp[c] = 120 + c
+    for fmt in (2, 3):
+        for n, e in [(0, 0), (1, 1), (65537, 300), (1 << 29, 12345)]:
+            assert nat.sz_encoded_size_format(fmt, 0, n, e) == oracle.encoded_size_variant(fmt, n, e)
+        assert nat.sz_encoded_size_format(fmt, 1, 100, 0) == 0
+        cap = nat.sz_encoded_size_format(fmt, 0, 16, 16)
+        ws = nat.sz_workspace_size(0, 16)
+        assert nat.sz_encode_format(fmt, 1, dummy, 16, cb, dummy, cap, dummy, ws, None) == -2
+        assert nat.sz_decode_format(fmt, dummy, 1 << 20, 1, dummy, 16, dummy, ws, None) == -2
+        assert nat.sz_encode_format(fmt, 0, dummy, 16, cb, dummy, cap - 1, dummy, ws, None) == -3
+        assert nat.sz_encode_format(fmt, 0, dummy, 16, cb, dummy, cap, dummy, ws - 1, None) == -7
+        fixed = nat.sz_encoded_size_format(fmt, 0, 1000, 0)
+        assert nat.sz_decode_format(fmt, dummy, fixed - 1, 0, dummy, 1000, dummy, 1 << 30, None) == -5
+        # a repeat among the used entries is refused; one beyond them is ignored
+        used = 8 if fmt == 2 else 15
+        cb.exp[used - 1] = cb.exp[0]
+        assert nat.sz_encode_format(fmt, 0, dummy, 16, cb, dummy, cap, dummy, ws, None) == -1
+        cb.exp[used - 1] = 120 + used - 1
+    assert nat.sz_encoded_size_format(9, 0, 100, 0) == 0
+    assert nat.sz_encode_format(9, 0, dummy, 16, cb, dummy, 1 << 30, dummy, 1 << 30, None) == -1
+    assert nat.sz_decode_format(0, dummy, 1 << 30, 0, dummy, 16, dummy, 1 << 30, None) == -1
+    assert nat.sz_encoded_size_format(1, 0, 1000, 7) == nat.sz_encoded_size(0, 1000, 7)
