@@ -264,6 +264,32 @@ def main():
         "per_tensor_codebook_equals_offline": list(dyn_cb.exps) == list(cb.exps),
     }
 
+    # the page's ablation formats on the same tensor (BF16 only): Top-8 and
+    # Top-15 with a sentinel code, against the Top-16 numbers above
+    formats = None
+    if dtype == 0:
+        formats = {}
+        for name, fmt in (("top8", sz.TOP8), ("top15_sentinel", sz.TOP15S)):
+            cap_f = sz.encoded_size(dtype, n, n, fmt)
+            buf_f = torch.empty(cap_f, dtype=torch.uint8, device=dev)
+            _, size_f, esc_f = sz.encode(x, cb, out=buf_f, ws=ws, fmt=fmt)
+            sz.decode(buf_f, dtype, n, out=y, ws=ws_dec, in_bytes=size_f, fmt=fmt)
+            if not torch.equal(y.view(torch.uint8), x.view(torch.uint8)):
+                print("round trip mismatch (%s)" % name, file=sys.stderr)
+                sys.exit(1)
+            e_ms = time_loop(lambda: sz.encode(x, cb, out=buf_f, ws=ws, sync=False, fmt=fmt), reps)
+            d_ms = time_loop(lambda: sz.decode(buf_f, dtype, n, out=y, ws=ws_dec, check=False,
+                                               in_bytes=size_f, fmt=fmt), reps)
+            formats[name] = {
+                "encode_GBps": round(n * elem / (e_ms * 1e-3) / 1e9, 1),
+                "decode_GBps": round(n * elem / (d_ms * 1e-3) / 1e9, 1),
+                "ratio": round(n * elem / size_f, 6),
+                "escape_rate": round(esc_f / n, 6),
+                "top16_decode_speedup": round(d_ms / dec_ms, 3),
+                "top16_encode_speedup": round(e_ms / enc_ms, 3),
+            }
+            del buf_f
+
     # a plain device copy of the same bytes, as a practical streaming ceiling
     alg_per_direction = alg_bytes // 2          # read half, write half
     src = torch.empty(alg_per_direction, dtype=torch.uint8, device=dev)
@@ -298,6 +324,7 @@ def main():
         "stream_bytes": size,
         "kernels": per_kernel,
         "calibration": calibration,
+        "formats": formats,
         "copy_GBps": round(copy_gbps, 1),
         "copy_bytes": alg_per_direction,
         "roofline": {
