@@ -290,6 +290,36 @@ def main():
             }
             del buf_f
 
+    # chunked transfer through pinned host memory (PCIe both ways stands in
+    # for the prefill-to-decode link): raw against SplitZip-compressed, one
+    # 2^24-value chunk (one Llama-3-8B layer, K and V) at a time
+    chunk = min(n, 1 << 24)
+    staging = sz.transfer_buffers(dtype, n, chunk, 3, dev)
+    runs = {}
+    for mode, book in (("raw", None), ("splitzip", cb)):
+        best = None
+        for _ in range(3):
+            _, st = sz.transfer(x, chunk, book, depth=3, out=y, staging=staging)
+            if best is None or st["total_ms"] < best["total_ms"]:
+                best = st
+        if not torch.equal(y.view(torch.uint8), x.view(torch.uint8)):
+            print("transfer mismatch (%s)" % mode, file=sys.stderr)
+            sys.exit(1)
+        runs[mode] = best
+    transfer = {
+        "link": "PCIe via pinned host memory, device->host then host->device, pipelined (depth 3)",
+        "chunk_elems": chunk,
+        "chunks": runs["raw"]["chunks"],
+        "raw_ms": round(runs["raw"]["total_ms"], 3),
+        "raw_GBps": round(n * elem / (runs["raw"]["total_ms"] * 1e-3) / 1e9, 2),
+        "splitzip_ms": round(runs["splitzip"]["total_ms"], 3),
+        "splitzip_GBps": round(n * elem / (runs["splitzip"]["total_ms"] * 1e-3) / 1e9, 2),
+        "wire_bytes": runs["splitzip"]["wire_bytes"],
+        "wire_ratio": round(n * elem / runs["splitzip"]["wire_bytes"], 6),
+        "speedup": round(runs["raw"]["total_ms"] / runs["splitzip"]["total_ms"], 4),
+    }
+    del staging
+
     # a plain device copy of the same bytes, as a practical streaming ceiling
     alg_per_direction = alg_bytes // 2          # read half, write half
     src = torch.empty(alg_per_direction, dtype=torch.uint8, device=dev)
@@ -325,6 +355,7 @@ def main():
         "kernels": per_kernel,
         "calibration": calibration,
         "formats": formats,
+        "transfer": transfer,
         "copy_GBps": round(copy_gbps, 1),
         "copy_bytes": alg_per_direction,
         "roofline": {

@@ -27,7 +27,7 @@ TOP15S = SZ_FORMAT_TOP15_SENTINEL
 
 __all__ = ["BF16", "E5M2", "TOP16", "TOP8", "TOP15S", "Codebook", "SplitZipError", "calibrate", "calibrate_device",
            "codebook_from_device", "encoded_size", "workspace_size", "workspace", "encode", "decode",
-           "read_escape_count", "profile_enable", "profile_collect"]
+           "read_escape_count", "transfer", "transfer_buffers", "profile_enable", "profile_collect"]
 
 # An sz_codebook in device memory: u32 dtype, 16 exponent bytes (20 bytes,
 # padded to 32 so that the tensor size keeps 16-byte multiples).
@@ -193,6 +193,38 @@ def decode(buf: torch.Tensor, dtype: int, n: int, out: torch.Tensor | None = Non
         if status != 0:
             raise SplitZipError("sz_decode (device check)", status)
     return out
+
+
+def transfer_buffers(dtype: int, n: int, chunk: int, depth: int = 3, device="cuda"):
+    """Pinned host staging and device workspace for ``transfer``."""
+    h = torch.empty(_native.sz_transfer_host_bytes(dtype, n, chunk, depth), dtype=torch.uint8, pin_memory=True)
+    ws = torch.empty(_native.sz_transfer_workspace_size(dtype, chunk, depth), dtype=torch.uint8, device=device)
+    return h, ws
+
+
+def transfer(x: torch.Tensor, chunk: int, cb: Codebook | None = None, depth: int = 3,
+             out: torch.Tensor | None = None, staging=None, stream=None):
+    """Send a device tensor through pinned host memory in chunks of ``chunk``
+    values (sz_transfer): SplitZip-compressed with ``cb``, or raw when ``cb``
+    is None.  Synchronous.  Returns ``(out, stats)`` with stats a dict of the
+    library's sz_transfer_stats."""
+    dtype = dtype_of(x)
+    x = x.reshape(-1)
+    n = x.numel()
+    if out is None:
+        out = torch.empty_like(x)
+    if staging is None:
+        staging = transfer_buffers(dtype, n, chunk, depth, x.device)
+    h, ws = staging
+    rc, st = _native.sz_transfer(dtype, x.data_ptr() if n else None, n, chunk,
+                                 cb.to_c() if cb is not None else None, 1 if cb is not None else 0, depth,
+                                 h.data_ptr(), h.numel(), out.data_ptr() if n else None, ws.data_ptr(), ws.numel(),
+                                 _stream_handle(stream, x.device))
+    _native.check("sz_transfer", rc)
+    stats = {k: getattr(st, k) for k, _ in st._fields_}
+    if stats["decode_status"] != 0:
+        raise SplitZipError("sz_transfer (chunk decode)", stats["decode_status"])
+    return out, stats
 
 
 def profile_enable(on: bool = True) -> None:

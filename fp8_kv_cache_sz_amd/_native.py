@@ -34,6 +34,11 @@ class sz_codebook(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_uint32), ("exp", ctypes.c_uint8 * 16)]
 
 
+class sz_transfer_stats(ctypes.Structure):
+    _fields_ = [("total_ms", ctypes.c_double), ("chunks", ctypes.c_uint64), ("raw_bytes", ctypes.c_uint64),
+                ("wire_bytes", ctypes.c_uint64), ("escapes", ctypes.c_uint64), ("decode_status", ctypes.c_int32)]
+
+
 class sz_kernel_stat(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_uint64),
                 ("total_ms", ctypes.c_double)]
@@ -61,6 +66,13 @@ lib.sz_encode_format.argtypes = [_i32, _i32, _vp, _u64, ctypes.POINTER(sz_codebo
 lib.sz_encode_format.restype = _i32
 lib.sz_decode_format.argtypes = [_i32, _vp, _u64, _i32, _vp, _u64, _vp, _u64, _vp]
 lib.sz_decode_format.restype = _i32
+lib.sz_transfer_workspace_size.argtypes = [_i32, _u64, _i32]
+lib.sz_transfer_workspace_size.restype = _u64
+lib.sz_transfer_host_bytes.argtypes = [_i32, _u64, _u64, _i32]
+lib.sz_transfer_host_bytes.restype = _u64
+lib.sz_transfer.argtypes = [_i32, _vp, _u64, _u64, _vp, _i32, _i32, _vp, _u64, _vp, _vp, _u64, _vp,
+                            ctypes.POINTER(sz_transfer_stats)]
+lib.sz_transfer.restype = _i32
 lib.sz_decode.argtypes = [_vp, _u64, _i32, _vp, _u64, _vp, _u64, _vp]
 lib.sz_decode.restype = _i32
 lib.sz_profile_enable.argtypes = [_i32]
@@ -70,7 +82,8 @@ lib.sz_profile_collect.restype = _i32
 
 EXPORTS = ("sz_calibrate", "sz_encoded_size", "sz_workspace_size", "sz_encode", "sz_encode_devcb",
            "sz_calibrate_workspace_size", "sz_calibrate_device", "sz_decode", "sz_encoded_size_format",
-           "sz_encode_format", "sz_decode_format", "sz_profile_enable", "sz_profile_collect")
+           "sz_encode_format", "sz_decode_format", "sz_transfer_workspace_size", "sz_transfer_host_bytes",
+           "sz_transfer", "sz_profile_enable", "sz_profile_collect")
 
 SZ_FORMAT_TOP16 = 1
 SZ_FORMAT_TOP8 = 2
@@ -131,6 +144,22 @@ def sz_encode_format(fmt, dtype, d_in, n, cb, d_out, out_capacity, d_ws, ws_byte
 
 def sz_decode_format(fmt, d_in, in_bytes, dtype, d_out, n, d_ws, ws_bytes, stream) -> int:
     return int(lib.sz_decode_format(fmt, d_in, in_bytes, dtype, d_out, n, d_ws, ws_bytes, stream))
+
+
+def sz_transfer_workspace_size(dtype: int, chunk: int, depth: int) -> int:
+    return int(lib.sz_transfer_workspace_size(dtype, chunk, depth))
+
+
+def sz_transfer_host_bytes(dtype: int, n: int, chunk: int, depth: int) -> int:
+    return int(lib.sz_transfer_host_bytes(dtype, n, chunk, depth))
+
+
+def sz_transfer(dtype, d_src, n, chunk, cb, compress, depth, h_staging, h_bytes, d_dst, d_ws, ws_bytes, stream):
+    """Returns (rc, sz_transfer_stats)."""
+    stats = sz_transfer_stats()
+    rc = lib.sz_transfer(dtype, d_src, n, chunk, ctypes.byref(cb) if cb is not None else None, compress, depth,
+                         h_staging, h_bytes, d_dst, d_ws, ws_bytes, stream, ctypes.byref(stats))
+    return int(rc), stats
 
 
 def sz_decode(d_in, in_bytes, dtype, d_out, n, d_ws, ws_bytes, stream) -> int:

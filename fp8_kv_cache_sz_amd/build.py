@@ -6,7 +6,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "splitzip.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "splitzip.hip"), os.path.join(HERE, "csrc", "transfer.hip")]
 HEADERS = [os.path.join(ROOT, "include", "splitzip.h")]
 LIBRARY = os.path.join(HERE, "libsplitzip.so")
 ARCH = "gfx950"

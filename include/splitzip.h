@@ -170,6 +170,51 @@ int sz_encode_format(int format, int dtype, const void *d_in, uint64_t n_elems, 
 int sz_decode_format(int format, const void *d_in, uint64_t in_bytes, int dtype, void *d_out,
                      uint64_t n_elems, void *d_ws, uint64_t ws_bytes, void *stream);
 
+/* Chunked transfer over a bandwidth-limited link (page: Problem section,
+ * the prefill-to-decode KV transfer over 50-100 GB/s links; Results,
+ * transfer latency, where the smaller payload shortens the transfer and
+ * the codec's time is a small share of it).  One GPU stands in for both
+ * ends: the link is PCIe through pinned host memory (device -> host, then
+ * host -> device), the host buffer playing the wire.  d_src (n_elems
+ * values on the device) is sent in chunks of chunk_elems values (the last
+ * may be shorter; chunk_elems * element size must be a multiple of 16) and
+ * arrives in d_dst.  With compress != 0, each chunk is encoded with cb into
+ * its own stream, exactly the stream's bytes cross the link both ways, and
+ * the chunk is decoded into place; with compress = 0 the raw bytes cross.
+ * `depth` (1..8) buffer slots let the encode, D2H, H2D and decode of
+ * consecutive chunks overlap on three library-owned streams (codec, D2H,
+ * H2D).
+ *   h_staging: pinned host memory mapped into the device's address space
+ *     (hipHostMalloc; torch's pin_memory) of h_bytes >=
+ *     sz_transfer_host_bytes(dtype, n_elems, chunk_elems, depth); the
+ *     library writes stream headers and decode statuses into it from
+ *     kernels (SZ_E_ARG if the device cannot address it).
+ *   d_ws: ws_bytes >= sz_transfer_workspace_size(dtype, chunk_elems, depth).
+ *   stream: the caller's stream; the transfer starts once the work already
+ *     queued on it is done.
+ * Synchronous: returns once d_dst holds the whole tensor.  stats gets the
+ * host wall time from the first enqueue to the last completion, the chunk
+ * count, the raw bytes, the bytes that crossed the link (each direction),
+ * the escape total and the first non-zero decode status (0 when every chunk
+ * decoded cleanly).  Returns SZ_OK, SZ_E_DTYPE, SZ_E_ARG (depth, chunk size,
+ * null pointers), SZ_E_ALIGN (16 bytes for every pointer), SZ_E_WORKSPACE
+ * (either buffer too small), SZ_E_HIP, or an error of sz_encode /
+ * sz_decode. */
+typedef struct sz_transfer_stats {
+    double total_ms;
+    uint64_t chunks;
+    uint64_t raw_bytes;
+    uint64_t wire_bytes;
+    uint64_t escapes;
+    int32_t decode_status;
+} sz_transfer_stats;
+
+uint64_t sz_transfer_workspace_size(int dtype, uint64_t chunk_elems, int depth);
+uint64_t sz_transfer_host_bytes(int dtype, uint64_t n_elems, uint64_t chunk_elems, int depth);
+int sz_transfer(int dtype, const void *d_src, uint64_t n_elems, uint64_t chunk_elems,
+                const sz_codebook *cb, int compress, int depth, void *h_staging, uint64_t h_bytes,
+                void *d_dst, void *d_ws, uint64_t ws_bytes, void *stream, sz_transfer_stats *stats);
+
 /* Decode (page: Method, decoding bullets: dense unpack + lookup table, then
  * the sparse escape stream overwrites the escaped exponents).  d_in: a
  * stream of in_bytes bytes on the device.  d_out: n_elems values.  d_ws:

@@ -164,3 +164,30 @@ def test_host_argument_checks_formats():
     assert nat.sz_encode_format(9, 0, dummy, 16, cb, dummy, 1 << 30, dummy, 1 << 30, None) == -1
     assert nat.sz_decode_format(0, dummy, 1 << 30, 0, dummy, 16, dummy, 1 << 30, None) == -1
     assert nat.sz_encoded_size_format(1, 0, 1000, 7) == nat.sz_encoded_size(0, 1000, 7)
+
+
+def test_host_argument_checks_transfer():
+    """sz_transfer rejects bad arguments before touching any buffer."""
+    nat = _native()
+    dummy = 1 << 20
+    cb = nat.sz_codebook()
+    cb.dtype = 0
+    for c in range(16):
+        cb.exp[c] = 120 + c
+    ws = nat.sz_transfer_workspace_size(0, 65536, 3)
+    hb = nat.sz_transfer_host_bytes(0, 1 << 20, 65536, 3)
+    slot = (nat.sz_encoded_size(0, 65536, 65536) + 255) // 256 * 256
+    assert ws == 2 * 3 * slot + 2 * ((nat.sz_workspace_size(0, 65536) + 255) // 256 * 256)
+    assert hb == 3 * slot + 3 * 64 + 256
+    assert nat.sz_transfer_workspace_size(0, 65536, 0) == 0 and nat.sz_transfer_workspace_size(0, 65536, 9) == 0
+    assert nat.sz_transfer_host_bytes(5, 100, 16, 1) == 0
+    args = lambda **kw: dict(dict(dtype=0, d_src=dummy, n=1 << 20, chunk=65536, cb=cb, compress=1, depth=3,
+                                  h_staging=dummy, h_bytes=hb, d_dst=dummy, d_ws=dummy, ws_bytes=ws,
+                                  stream=None), **kw)
+    call = lambda **kw: nat.sz_transfer(**args(**kw))[0]
+    assert call(dtype=4) == -2
+    assert call(depth=0) == -1 and call(depth=9) == -1
+    assert call(chunk=0) == -1 and call(chunk=65537) == -1
+    assert call(cb=None) == -1 and call(h_staging=None) == -1 and call(d_ws=None) == -1
+    assert call(d_src=dummy + 4) == -4 and call(h_staging=dummy + 8) == -4
+    assert call(h_bytes=hb - 1) == -7 and call(ws_bytes=ws - 1) == -7
