@@ -41,6 +41,9 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default=WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--core-only", action="store_true",
+                   help="time only the encode+decode step (no calibration, format or transfer sections), "
+                        "e.g. under a profiler")
     p.add_argument("--cpu-sample-log2", type=int, default=28,
                    help="elements of the workload the CPU oracle encodes and decodes (log2)")
     p.add_argument("--ingest-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"),
@@ -78,12 +81,25 @@ def load_traffic(kernel: str, workload: str):
     return entry.get("bytes_per_launch")
 
 
+# kernel template instances -> the names the library's instrumentation uses
+LAUNCH_NAMES = {
+    "sz_enc_dense_bf16<1>": "sz_enc_dense_bf16", "sz_enc_dense_bf16<2>": "sz_enc_dense_top8",
+    "sz_enc_dense_bf16<3>": "sz_enc_dense_top15s", "sz_dec_variant<2>": "sz_dec_top8",
+    "sz_dec_variant<3>": "sz_dec_top15s", "sz_enc_compact<0>": "sz_enc_compact",
+    "sz_enc_compact<1>": "sz_enc_compact", "sz_cal_hist<0>": "sz_cal_hist_bf16",
+    "sz_cal_hist<1>": "sz_cal_hist_e5m2", "sz_cal_select<0>": "sz_cal_select",
+    "sz_cal_select<1>": "sz_cal_select",
+}
+
+
 def short_kernel_name(name: str) -> str:
-    """'void (anonymous namespace)::sz_enc_compact<0>(...)' -> 'sz_enc_compact'."""
+    """'void (anonymous namespace)::sz_enc_compact<0>(...)' -> 'sz_enc_compact'
+    (the launch name the library's instrumentation records)."""
     name = name.replace("(anonymous namespace)::", "").split("(")[0]
     if name.startswith("void "):
         name = name[5:]
-    return name.split("<")[0].strip()
+    name = name.strip()
+    return LAUNCH_NAMES.get(name, name.split("<")[0])
 
 
 def _pmc_per_kernel(csv_path, counter):
@@ -241,6 +257,69 @@ def main():
     achieved = alg_bytes / avg_s / 1e9
     traffic = load_traffic(dominant, args.workload)
 
+    calibration = formats = transfer = None
+    if not args.core_only:
+        calibration, formats, transfer = extra_sections(sz, x, cb, dtype, n, elem, buf, ws, ws_dec, y, dev,
+                                                        time_loop, reps, enc_ms, dec_ms)
+
+    # a plain device copy of the same bytes, as a practical streaming ceiling
+    alg_per_direction = alg_bytes // 2          # read half, write half
+    src = torch.empty(alg_per_direction, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = time_loop(lambda: dst.copy_(src), reps)
+    copy_gbps = 2 * src.numel() / (copy_ms * 1e-3) / 1e9
+    del src, dst
+
+    result = {
+        "metric": "encode/decode GB/s (uncompressed) + % of 8 TB/s HBM peak; compression ratio",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16" if dtype == 0 else "u8",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "description": synth.DESCRIPTION[args.workload],
+                   "elements": n, "bytes": n * elem, "codebook": list(cb.exps),
+                   "step": "encode + decode of the whole tensor"},
+        "encode_GBps": round(n * elem / (enc_ms * 1e-3) / 1e9, 2),
+        "decode_GBps": round(n * elem / (dec_ms * 1e-3) / 1e9, 2),
+        "encode_ms": round(enc_ms, 4),
+        "decode_ms": round(dec_ms, 4),
+        "ratio": round(n * elem / size, 6),
+        "escape_rate": round(escapes / n, 6),
+        "escapes": escapes,
+        "stream_bytes": size,
+        "kernels": per_kernel,
+        "calibration": calibration,
+        "formats": formats,
+        "transfer": transfer,
+        "copy_GBps": round(copy_gbps, 1),
+        "copy_bytes": alg_per_direction,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dominant,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x, cb, dtype, args.cpu_sample_log2)
+    print(json.dumps(result), flush=True)
+
+
+
+def extra_sections(sz, x, cb, dtype, n, elem, buf, ws, ws_dec, y, dev, time_loop, reps, enc_ms, dec_ms):
+    """Rows beyond the encode+decode step: on-device calibration, the
+    ablation formats and the chunked transfer."""
+    import torch
     # on-device calibration (per-tensor codebook at run time): the whole
     # tensor, and every 16th 64K block; then encode with the device codebook
     cal_ws = torch.empty(sz._native.sz_calibrate_workspace_size(dtype), dtype=torch.uint8, device=dev)
@@ -319,58 +398,7 @@ def main():
         "speedup": round(runs["raw"]["total_ms"] / runs["splitzip"]["total_ms"], 4),
     }
     del staging
-
-    # a plain device copy of the same bytes, as a practical streaming ceiling
-    alg_per_direction = alg_bytes // 2          # read half, write half
-    src = torch.empty(alg_per_direction, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    copy_ms = time_loop(lambda: dst.copy_(src), reps)
-    copy_gbps = 2 * src.numel() / (copy_ms * 1e-3) / 1e9
-    del src, dst
-
-    result = {
-        "metric": "encode/decode GB/s (uncompressed) + % of 8 TB/s HBM peak; compression ratio",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "u16" if dtype == 0 else "u8",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "description": synth.DESCRIPTION[args.workload],
-                   "elements": n, "bytes": n * elem, "codebook": list(cb.exps),
-                   "step": "encode + decode of the whole tensor"},
-        "encode_GBps": round(n * elem / (enc_ms * 1e-3) / 1e9, 2),
-        "decode_GBps": round(n * elem / (dec_ms * 1e-3) / 1e9, 2),
-        "encode_ms": round(enc_ms, 4),
-        "decode_ms": round(dec_ms, 4),
-        "ratio": round(n * elem / size, 6),
-        "escape_rate": round(escapes / n, 6),
-        "escapes": escapes,
-        "stream_bytes": size,
-        "kernels": per_kernel,
-        "calibration": calibration,
-        "formats": formats,
-        "transfer": transfer,
-        "copy_GBps": round(copy_gbps, 1),
-        "copy_bytes": alg_per_direction,
-        "roofline": {
-            "bound": "hbm",
-            "kernel": dominant,
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-        },
-    }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(x, cb, dtype, args.cpu_sample_log2)
-    print(json.dumps(result), flush=True)
+    return calibration, formats, transfer
 
 
 if __name__ == "__main__":
