@@ -108,6 +108,21 @@ __device__ __forceinline__ uint2 load_nt(const uint2 *p)
     return make_uint2(v.x, v.y);
 }
 __device__ __forceinline__ uint32_t load_nt(const uint32_t *p) { return __builtin_nontemporal_load(p); }
+// three consecutive words (4-byte aligned): one dwordx3 access per lane, so a
+// wave's 12-byte groups make one contiguous 768-byte access
+typedef uint32_t v3u_a4 __attribute__((ext_vector_type(3), aligned(4)));
+__device__ __forceinline__ void load3_nt(const uint32_t *p, uint32_t w[3])
+{
+    const v3u_a4 v = __builtin_nontemporal_load(reinterpret_cast<const v3u_a4 *>(p));
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+}
+__device__ __forceinline__ void store3_nt(uint32_t *p, const uint32_t w[3])
+{
+    const v3u_a4 v = {w[0], w[1], w[2]};
+    __builtin_nontemporal_store(v, reinterpret_cast<v3u_a4 *>(p));
+}
 __device__ __forceinline__ void store_nt(uint4 *p, uint4 v)
 {
     v4u w = {v.x, v.y, v.z, v.w};
@@ -286,6 +301,82 @@ __device__ __forceinline__ void encode_chunk_e5m2(const uint4 q0, const uint4 q1
     sm3[0] = grp[0] | (grp[1] << 24);
     sm3[1] = (grp[1] >> 8) | (grp[2] << 16);
     sm3[2] = (grp[2] >> 16) | (grp[3] << 8);
+}
+
+// E5M2 encode through a code-pair table: table16[e0 | e1 << 5] holds, for
+// two neighbouring elements with exponents e0 and e1, their two codes as one
+// code byte (low byte: code0 | code1 << 4, escapes coded 0) and their escape
+// flags (high byte: bit 0 = element 0, bit 1 = element 1).  One LDS read per
+// two elements replaces two reads, the nibble packing and the escape-mask
+// arithmetic of the byte table.
+__device__ __forceinline__ void build_pair_table(uint32_t *table16x2, const uint8_t *tab8)
+{
+    // thread t fills entries 4t .. 4t+3 (two words); e1 is the same for all four
+    const uint32_t t = threadIdx.x;
+    if (t < 256) {
+        const uint32_t c1 = tab8[t >> 3];
+        const uint32_t hi = ((c1 & 0xFu) << 4) | ((c1 >> 7) << 9);
+        uint32_t e[4];
+#pragma unroll
+        for (uint32_t k = 0; k < 4; ++k) {
+            const uint32_t c0 = tab8[(4 * t + k) & 31u];
+            e[k] = (c0 & 0xFu) | ((c0 >> 7) << 8) | hi;
+        }
+        table16x2[2 * t] = e[0] | (e[1] << 16);
+        table16x2[2 * t + 1] = e[2] | (e[3] << 16);
+    }
+}
+
+// Four 3-bit symbols held in bytes (bits 0-2 of each byte, the rest zero) ->
+// 12 contiguous bits.
+__device__ __forceinline__ uint32_t pack_sym3x4(uint32_t sym)
+{
+    const uint32_t u = sym | (sym >> 5);              // f0 | f1 << 3 at bit 0, f2 | f3 << 3 at bit 16
+    return (u & 0x3Fu) | ((u >> 10) & 0xFC0u);
+}
+
+// One 32-element chunk: 16 code bytes, 12 sign/mantissa bytes, and per group
+// of 8 elements a flag word fl[s] whose byte k holds the escape flags of
+// elements 2k (bit 0) and 2k + 1 (bit 1) of the group.
+__device__ __forceinline__ void encode_chunk_e5m2_pairs(const uint4 q0, const uint4 q1, const uint16_t *table16,
+                                                        uint4 &nib, uint32_t sm3[3], uint32_t fl[4])
+{
+    const uint32_t d[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    uint32_t nibw[4], grp[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t a = d[2 * s], b = d[2 * s + 1];
+        // pair index e0 | e1 << 5 of elements (0,1) and (2,3) of a word
+        const uint32_t p0 = table16[((a >> 2) & 0x1Fu) | ((a >> 5) & 0x3E0u)];
+        const uint32_t p1 = table16[((a >> 18) & 0x1Fu) | ((a >> 21) & 0x3E0u)];
+        const uint32_t p2 = table16[((b >> 2) & 0x1Fu) | ((b >> 5) & 0x3E0u)];
+        const uint32_t p3 = table16[((b >> 18) & 0x1Fu) | ((b >> 21) & 0x3E0u)];
+        const uint32_t lo = perm(p1, p0, 0x0C0C0400u), hi = perm(p3, p2, 0x04000C0Cu);
+        nibw[s] = lo | hi;
+        fl[s] = perm(p1, p0, 0x0C0C0501u) | perm(p3, p2, 0x05010C0Cu);
+        const uint32_t s_a = ((a >> 5) & 0x04040404u) | (a & 0x03030303u);
+        const uint32_t s_b = ((b >> 5) & 0x04040404u) | (b & 0x03030303u);
+        grp[s] = pack_sym3x4(s_a) | (pack_sym3x4(s_b) << 12);
+    }
+    nib = make_uint4(nibw[0], nibw[1], nibw[2], nibw[3]);
+    sm3[0] = grp[0] | (grp[1] << 24);
+    sm3[1] = (grp[1] >> 8) | (grp[2] << 16);
+    sm3[2] = (grp[2] >> 16) | (grp[3] << 8);
+}
+
+// Flag word of a group (byte k = flags of elements 2k, 2k+1) -> 8-bit mask.
+__device__ __forceinline__ uint32_t flags_to_mask8(uint32_t f)
+{
+    return (f & 3u) | ((f >> 6) & 0xCu) | ((f >> 12) & 0x30u) | ((f >> 18) & 0xC0u);
+}
+
+// Flag bits of the first v elements of a group (v in 0..8).
+__device__ __forceinline__ uint32_t group_flag_keep(int v)
+{
+    uint32_t m = 0;
+    for (int i = 0; i < 8; ++i)
+        if (i < v) m |= 1u << ((i / 2) * 8 + (i & 1));
+    return m;
 }
 
 // ---------------------------------------------------------------------------
@@ -608,6 +699,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
                                                               uint8_t *__restrict__ stage)
 {
     __shared__ uint32_t table32[64];
+    __shared__ uint32_t table16x2[512];
     __shared__ uint32_t wave_totals[kEncThreads / 64];
     __shared__ __align__(16) uint8_t seg_buf[kEncThreads / 64][kSegBytes];
     const uint32_t lane = lane_id();
@@ -633,32 +725,31 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
     if (cb_dev) cb = load_codebook(cb_dev);
     build_encode_table(table32, cb, 32);
     __syncthreads();
-    const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
-    uint32_t esc[kE5Chunks];
-    uint64_t ex[kE5Chunks][4];
+    build_pair_table(table16x2, reinterpret_cast<const uint8_t *>(table32));
+    __syncthreads();
+    const uint16_t *table16 = reinterpret_cast<const uint16_t *>(table16x2);
+    uint32_t fl[kE5Chunks][4];
     uint32_t cnt[kE5Chunks];
 #pragma unroll
     for (int j = 0; j < kE5Chunks; ++j) {
         const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
         uint4 nib;
         uint32_t sm3[3];
-        encode_chunk_e5m2(q[j][0], q[j][1], table, nib, sm3, esc[j], ex[j]);
+        encode_chunk_e5m2_pairs(q[j][0], q[j][1], table16, nib, sm3, fl[j]);
         uint32_t *sm_dst = reinterpret_cast<uint32_t *>(out + off_sm + (c0 / 32) * 12);
         if (full_row || c0 + 32 <= n) {
             store_nt(reinterpret_cast<uint4 *>(out + off_nib + c0 / 2), nib);
-            store_nt(sm_dst, sm3[0]);
-            store_nt(sm_dst + 1, sm3[1]);
-            store_nt(sm_dst + 2, sm3[2]);
+            store3_nt(sm_dst, sm3);
         } else if (c0 < n) {
             // last, partial chunk: missing elements get code 0, symbol 0 and
             // no escape; only the sign/mantissa bytes that hold data are stored
             const uint32_t valid = (uint32_t)(n - c0);
-            esc[j] &= (uint32_t)((1ull << valid) - 1);
             uint32_t nw[4] = {nib.x, nib.y, nib.z, nib.w};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int v = (int)valid - 8 * s;
                 nw[s] &= v >= 8 ? 0xFFFFFFFFu : (v <= 0 ? 0u : (uint32_t)((1ull << (4 * v)) - 1));
+                fl[j][s] &= group_flag_keep(v);
             }
             *reinterpret_cast<uint4 *>(out + off_nib + c0 / 2) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
             uint32_t sw[3] = {sm3[0], sm3[1], sm3[2]};
@@ -673,9 +764,10 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
             for (uint32_t i = 0; i < 12 && sm_start + i < sm_end; ++i)
                 out[sm_start + i] = (uint8_t)(sw[i / 4] >> (8 * (i & 3)));
         } else {
-            esc[j] = 0;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) fl[j][s] = 0;
         }
-        cnt[j] = __popc(esc[j]);
+        cnt[j] = __popc(fl[j][0]) + __popc(fl[j][1]) + __popc(fl[j][2]) + __popc(fl[j][3]);
     }
     uint32_t row_base[kE5Chunks], row_total[kE5Chunks], lane_before[kE5Chunks];
     const uint32_t wave_total = wave_chunk_ranks<kE5Chunks>(cnt, row_base, row_total, lane_before);
@@ -688,14 +780,24 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
         for (int j = 0; j < kE5Chunks; ++j) {
             const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
             const uint32_t rank = wave_before + row_base[j];
+            // escape masks and exponents of the chunk, from its flag words and input words
+            const uint32_t dw[8] = {q[j][0].x, q[j][0].y, q[j][0].z, q[j][0].w,
+                                    q[j][1].x, q[j][1].y, q[j][1].z, q[j][1].w};
+            uint32_t esc8[4];
+            uint64_t ex[4];
+#pragma unroll
+            for (int s8 = 0; s8 < 4; ++s8) {
+                esc8[s8] = flags_to_mask8(fl[j][s8]);
+                ex[s8] = (uint64_t)((dw[2 * s8] >> 2) & 0x1F1F1F1Fu) |
+                         ((uint64_t)((dw[2 * s8 + 1] >> 2) & 0x1F1F1F1Fu) << 32);
+            }
             if (row_total[j] <= kDirectRecords) {                      // wave-uniform
                 if (cnt[j]) {
                     uint32_t r = rank + lane_before[j];
 #pragma unroll
                     for (int s8 = 0; s8 < 4; ++s8) {
-                        const uint32_t m = (esc[j] >> (8 * s8)) & 0xFFu;
-                        put_records(tstage, r, m, ex[j][s8], (uint32_t)((c0 + 8 * s8) & 0xFFFFu));
-                        r += __popc(m);
+                        put_records(tstage, r, esc8[s8], ex[s8], (uint32_t)((c0 + 8 * s8) & 0xFFFFu));
+                        r += __popc(esc8[s8]);
                     }
                 }
                 continue;
@@ -712,8 +814,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
                     uint32_t off = (g0 & 3) + 3 * (lane_before[j] - seg_first);
 #pragma unroll
                     for (int s8 = 0; s8 < 4; ++s8)
-                        off = lds_put_records(buf, off, (esc[j] >> (8 * s8)) & 0xFFu, ex[j][s8],
-                                              (uint32_t)((c0 + 8 * s8) & 0xFFFFu));
+                        off = lds_put_records(buf, off, esc8[s8], ex[s8], (uint32_t)((c0 + 8 * s8) & 0xFFFFu));
                 }
                 wave_lds_fence();
                 flush_segment(buf, tstage, g0, 3 * (seg_end - seg_first));
@@ -1787,10 +1888,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__rest
         const uint64_t g = e0 + c;
         if (full_row || c + 32 <= blen) {
             nib[j] = load_nt(reinterpret_cast<const uint4 *>(nib_base + g / 2));
-            const uint32_t *s32 = reinterpret_cast<const uint32_t *>(sm_base + (g / 32) * 12);
-            sm3[j][0] = load_nt(s32);
-            sm3[j][1] = load_nt(s32 + 1);
-            sm3[j][2] = load_nt(s32 + 2);
+            load3_nt(reinterpret_cast<const uint32_t *>(sm_base + (g / 32) * 12), sm3[j]);
         } else if (c < blen) {
             nib[j] = *reinterpret_cast<const uint4 *>(nib_base + g / 2);
             sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
