@@ -2074,6 +2074,8 @@ __global__ __launch_bounds__(kSelectThreads) void sz_cal_select(const uint32_t *
     const uint32_t v = t / P, part = t % P;
     const uint4 *row = reinterpret_cast<const uint4 *>(partial + (uint64_t)v * groups);
     uint64_t sum = 0;
+    // unrolled so that eight loads are in flight at once
+#pragma unroll 8
     for (uint32_t i = part; i < groups / 4; i += P) {
         const uint4 q = row[i];
         sum += (uint64_t)q.x + q.y + q.z + q.w;
