@@ -298,6 +298,10 @@ def main():
         "calibration": calibration,
         "formats": formats,
         "transfer": transfer,
+        "hbm": hbm_rates(per_kernel, args.workload),
+        "page_numbers": {"encode_GBps": 613.3, "decode_GBps": 2181.8, "ratio": 1.324,
+                         "hardware": "not named on the page", "workload": "real BF16 activations",
+                         "note": "context only, not this workload or machine"},
         "copy_GBps": round(copy_gbps, 1),
         "copy_bytes": alg_per_direction,
         "roofline": {
@@ -314,6 +318,18 @@ def main():
         result["cpu_baseline"] = cpu_baseline(x, cb, dtype, args.cpu_sample_log2)
     print(json.dumps(result), flush=True)
 
+
+
+def hbm_rates(per_kernel, workload):
+    """Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, when
+    taken on the current kernel source) over this run's average duration."""
+    out = {}
+    for k, v in per_kernel.items():
+        t = load_traffic(k, workload)
+        if t:
+            gbps = t / (v["avg_ms"] * 1e-3) / 1e9
+            out[k] = {"bytes_per_launch": t, "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    return out or None
 
 
 def extra_sections(sz, x, cb, dtype, n, elem, buf, ws, ws_dec, y, dev, time_loop, reps, enc_ms, dec_ms):
