@@ -33,7 +33,11 @@
  *     buffers between calls.
  *   - Device calls only enqueue work on `stream` (a hipStream_t; NULL is the
  *     null stream) and return once it is launched.  Calls that share a
- *     workspace must not overlap.
+ *     workspace must not overlap.  sz_encode, sz_encode_devcb,
+ *     sz_encode_format, sz_decode, sz_decode_format and sz_calibrate_device
+ *     allocate nothing, issue no memset and never synchronise, so they can
+ *     be captured into a HIP graph (with instrumentation off).  sz_transfer
+ *     synchronises and cannot.
  *   - Errors are negative return codes; nothing throws or aborts across the
  *     ABI.  Checks made on the device (the stream checks of sz_decode, the
  *     codebook check of sz_encode_devcb) land in the workspace status word,
