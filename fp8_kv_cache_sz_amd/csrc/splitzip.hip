@@ -19,10 +19,15 @@
 //     plus a per-workgroup prefix over the waves;
 //   * encode = dense+stage (one 256-lane workgroup per 16K-element tile), a
 //     one-workgroup scan of the tile counts, then a compaction of the staged
-//     escape records into their final order;
+//     escape records into their final order (escape-heavy tiles are encoded
+//     again from the input there instead of being staged);
 //   * decode = a one-workgroup validating scan of the block counts, then one
 //     1024-lane workgroup per 64K block: dense decode in registers, patched
-//     from an LDS map of the block's escapes before a single store.
+//     from an LDS map of the block's escapes before a single store (blocks
+//     with very many escapes go through an LDS exponent plane);
+//   * also here: on-device calibration (exponent histogram + Top-16
+//     selection) and the two ablation formats the page weighs against its
+//     Top-16 design (Top-8 and Top-15 with a sentinel code, BF16 only).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -271,10 +276,12 @@ __device__ __forceinline__ void encode_chunk_bf16(const uint4 q, const uint8_t *
 //   esc: escape mask (bit k = element k of the 32);  ex[s]: exponents of
 //   elements 8s..8s+7.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t pack_sm3_x4(uint32_t sym)
+// Four 3-bit symbols held in bytes (bits 0-2 of each byte, the rest zero) ->
+// 12 contiguous bits.
+__device__ __forceinline__ uint32_t pack_sym3x4(uint32_t sym)
 {
-    // four 3-bit symbols held in bytes -> 12 contiguous bits
-    return (sym & 0x7u) | ((sym >> 5) & 0x38u) | ((sym >> 10) & 0x1C0u) | ((sym >> 15) & 0xE00u);
+    const uint32_t u = sym | (sym >> 5);              // f0 | f1 << 3 at bit 0, f2 | f3 << 3 at bit 16
+    return (u & 0x3Fu) | ((u >> 10) & 0xFC0u);
 }
 
 __device__ __forceinline__ void encode_chunk_e5m2(const uint4 q0, const uint4 q1, const uint8_t *table,
@@ -295,7 +302,7 @@ __device__ __forceinline__ void encode_chunk_e5m2(const uint4 q0, const uint4 q1
         nibw[s] = pack_codes8(c_a, c_b);
         esc |= escape_mask8(c_a, c_b) << (8 * s);
         ex[s] = (uint64_t)e_a | ((uint64_t)e_b << 32);
-        grp[s] = pack_sm3_x4(s_a) | (pack_sm3_x4(s_b) << 12);
+        grp[s] = pack_sym3x4(s_a) | (pack_sym3x4(s_b) << 12);
     }
     nib = make_uint4(nibw[0], nibw[1], nibw[2], nibw[3]);
     sm3[0] = grp[0] | (grp[1] << 24);
@@ -325,14 +332,6 @@ __device__ __forceinline__ void build_pair_table(uint32_t *table16x2, const uint
         table16x2[2 * t] = e[0] | (e[1] << 16);
         table16x2[2 * t + 1] = e[2] | (e[3] << 16);
     }
-}
-
-// Four 3-bit symbols held in bytes (bits 0-2 of each byte, the rest zero) ->
-// 12 contiguous bits.
-__device__ __forceinline__ uint32_t pack_sym3x4(uint32_t sym)
-{
-    const uint32_t u = sym | (sym >> 5);              // f0 | f1 << 3 at bit 0, f2 | f3 << 3 at bit 16
-    return (u & 0x3Fu) | ((u >> 10) & 0xFC0u);
 }
 
 // One 32-element chunk: 16 code bytes, 12 sign/mantissa bytes, and per group
