@@ -27,7 +27,8 @@ TOP15S = SZ_FORMAT_TOP15_SENTINEL
 
 __all__ = ["BF16", "E5M2", "TOP16", "TOP8", "TOP15S", "Codebook", "SplitZipError", "calibrate", "calibrate_device",
            "codebook_from_device", "encoded_size", "workspace_size", "workspace", "encode", "decode",
-           "read_escape_count", "transfer", "transfer_buffers", "profile_enable", "profile_collect"]
+           "read_escape_count", "transfer", "transfer_buffers", "reference_copy", "profile_enable",
+           "profile_collect"]
 
 # An sz_codebook in device memory: u32 dtype, 16 exponent bytes (20 bytes,
 # padded to 32 so that the tensor size keeps 16-byte multiples).
@@ -225,6 +226,21 @@ def transfer(x: torch.Tensor, chunk: int, cb: Codebook | None = None, depth: int
     if stats["decode_status"] != 0:
         raise SplitZipError("sz_transfer (chunk decode)", stats["decode_status"])
     return out, stats
+
+
+def reference_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
+    """The library's plain streaming copy (sz_reference_copy) of a contiguous
+    device tensor into another of the same byte size; not part of the codec,
+    it times the practical streaming ceiling."""
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("reference_copy needs contiguous tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("reference_copy needs tensors of the same byte size")
+    rc = _native.sz_reference_copy(src.data_ptr() if nbytes else None, dst.data_ptr() if nbytes else None,
+                                   nbytes, _stream_handle(stream, src.device))
+    _native.check("sz_reference_copy", rc)
+    return dst
 
 
 def profile_enable(on: bool = True) -> None:

@@ -79,11 +79,13 @@ lib.sz_profile_enable.argtypes = [_i32]
 lib.sz_profile_enable.restype = _i32
 lib.sz_profile_collect.argtypes = [ctypes.POINTER(sz_kernel_stat), _i32]
 lib.sz_profile_collect.restype = _i32
+lib.sz_reference_copy.argtypes = [_vp, _vp, _u64, _vp]
+lib.sz_reference_copy.restype = _i32
 
 EXPORTS = ("sz_calibrate", "sz_encoded_size", "sz_workspace_size", "sz_encode", "sz_encode_devcb",
            "sz_calibrate_workspace_size", "sz_calibrate_device", "sz_decode", "sz_encoded_size_format",
            "sz_encode_format", "sz_decode_format", "sz_transfer_workspace_size", "sz_transfer_host_bytes",
-           "sz_transfer", "sz_profile_enable", "sz_profile_collect")
+           "sz_transfer", "sz_profile_enable", "sz_profile_collect", "sz_reference_copy")
 
 SZ_FORMAT_TOP16 = 1
 SZ_FORMAT_TOP8 = 2
@@ -164,6 +166,10 @@ def sz_transfer(dtype, d_src, n, chunk, cb, compress, depth, h_staging, h_bytes,
 
 def sz_decode(d_in, in_bytes, dtype, d_out, n, d_ws, ws_bytes, stream) -> int:
     return int(lib.sz_decode(d_in, in_bytes, dtype, d_out, n, d_ws, ws_bytes, stream))
+
+
+def sz_reference_copy(d_src, d_dst, nbytes, stream) -> int:
+    return int(lib.sz_reference_copy(d_src, d_dst, nbytes, stream))
 
 
 def sz_profile_enable(on: bool) -> int:

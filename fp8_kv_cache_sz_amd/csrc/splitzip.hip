@@ -2465,6 +2465,41 @@ extern "C" int sz_decode_format(int format, const void *d_in, uint64_t in_bytes,
     return decode_impl((uint32_t)format, d_in, in_bytes, dtype, d_out, n_elems, d_ws, ws_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Kernel: reference streaming copy (not part of the codec).  Each 256-lane
+// workgroup moves one 4 KB tile, one 16-byte word per lane, with a
+// non-temporal load and store.  Streaming probes on MI355X found this the
+// fastest plain copy shape: more words per lane (larger tiles) copy more
+// slowly, so this is the practical ceiling of a two-stream byte mix.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kCopyThreads = 256;
+
+__global__ __launch_bounds__(kCopyThreads) void sz_ref_copy(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                            uint64_t words)
+{
+    const uint64_t i = (uint64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    if (i < words) store_nt(dst + i, load_nt(src + i));
+}
+
+extern "C" int sz_reference_copy(const void *d_src, void *d_dst, uint64_t bytes, void *stream)
+{
+    if (bytes % 16 != 0) return SZ_E_ARG;
+    if (bytes == 0) return SZ_OK;
+    if (!d_src || !d_dst) return SZ_E_ARG;
+    if (!aligned16(d_src) || !aligned16(d_dst)) return SZ_E_ALIGN;
+    const uint8_t *s8 = static_cast<const uint8_t *>(d_src);
+    const uint8_t *d8 = static_cast<const uint8_t *>(d_dst);
+    if (s8 < d8 + bytes && d8 < s8 + bytes) return SZ_E_ARG;      // overlapping ranges
+    const uint64_t words = bytes / 16;
+    const uint64_t groups = (words + kCopyThreads - 1) / kCopyThreads;
+    if (groups > 0xFFFFFFFFull) return SZ_E_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    LaunchScope scope("sz_ref_copy", s);
+    hipLaunchKernelGGL(sz_ref_copy, dim3((uint32_t)groups), dim3(kCopyThreads), 0, s,
+                       static_cast<const uint4 *>(d_src), static_cast<uint4 *>(d_dst), words);
+    return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
+}
+
 extern "C" int sz_profile_enable(int on)
 {
     std::lock_guard<std::mutex> lock(g_prof_mutex);

@@ -249,6 +249,16 @@ typedef struct sz_kernel_stat {
 int sz_profile_enable(int on);
 int sz_profile_collect(sz_kernel_stat *stats, int max_stats);
 
+/* Reference streaming copy (not part of the codec).  Copies `bytes` bytes
+ * (a multiple of 16) from d_src to d_dst on the device, one non-temporal
+ * 16-byte load and store per lane, 4 KB per 256-lane workgroup (the fastest
+ * plain copy shape measured on MI355X), so its rate is the practical
+ * streaming ceiling the codec kernels are measured against.  Both pointers
+ * 16-byte aligned, the ranges must not overlap.  Enqueue only.  Returns
+ * SZ_OK (also for bytes = 0), SZ_E_ARG (null pointer, bytes not a multiple
+ * of 16, overlapping ranges), SZ_E_ALIGN or SZ_E_HIP. */
+int sz_reference_copy(const void *d_src, void *d_dst, uint64_t bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

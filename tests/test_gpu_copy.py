@@ -1,0 +1,28 @@
+"""The library's reference streaming copy (sz_reference_copy), which bench.py
+times as the practical streaming ceiling: it must copy every byte of ragged
+sizes (partial tiles and partial workgroups) and touch nothing past the end."""
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 32768 - 16, 32768, 32768 + 16, 3 * 32768 + 48, 64 << 20])
+def test_reference_copy(nbytes):
+    import fp8_kv_cache_sz_amd as sz
+    print("reference_copy", nbytes, flush=True)
+    g = torch.Generator(device="cpu").manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).cuda()
+    dst = torch.full((nbytes + 256,), 0xA5, dtype=torch.uint8, device="cuda")
+    sz.reference_copy(src, dst[:nbytes])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert bool((dst[nbytes:] == 0xA5).all())
+
+
+def test_reference_copy_rejects_overlap():
+    import fp8_kv_cache_sz_amd as sz
+    buf = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sz.SplitZipError) as e:
+        sz.reference_copy(buf[:2048], buf[1024:3072])
+    assert e.value.code == -1

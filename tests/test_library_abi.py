@@ -191,3 +191,18 @@ def test_host_argument_checks_transfer():
     assert call(cb=None) == -1 and call(h_staging=None) == -1 and call(d_ws=None) == -1
     assert call(d_src=dummy + 4) == -4 and call(h_staging=dummy + 8) == -4
     assert call(h_bytes=hb - 1) == -7 and call(ws_bytes=ws - 1) == -7
+
+
+def test_host_argument_checks_reference_copy():
+    """sz_reference_copy checks size, pointers, alignment and overlap on the
+    host, before any launch."""
+    nat = _native()
+    a, b = 1 << 20, 1 << 30
+    assert nat.sz_reference_copy(None, None, 0, None) == 0           # nothing to copy
+    assert nat.sz_reference_copy(a, b, 24, None) == -1                 # not a multiple of 16
+    assert nat.sz_reference_copy(None, b, 32, None) == -1
+    assert nat.sz_reference_copy(a, None, 32, None) == -1
+    assert nat.sz_reference_copy(a + 8, b, 32, None) == -4
+    assert nat.sz_reference_copy(a, b + 4, 32, None) == -4
+    assert nat.sz_reference_copy(a, a + 16, 32, None) == -1            # overlapping ranges
+    assert nat.sz_reference_copy(a + 16, a, 32, None) == -1
