@@ -189,6 +189,39 @@ def test_encode_is_deterministic_and_stream_order_safe():
     assert torch.equal(d2.view(torch.int16), y.view(torch.int16))
 
 
+def test_concurrent_streams_with_own_workspaces():
+    """Round trips on two streams at once, each with its own buffers and
+    workspaces: the library keeps no state between calls, so both streams
+    equal the oracle's byte for byte and both decodes are exact."""
+    sz = _sz()
+    cb = sz.calibrate(synth.calibration_tensor("kv1m"))
+    xs = [synth.workload("stress_t3", size="small")[0].cuda(),
+          synth.workload("llama3_8b_kv", size="small")[0].cuda()]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    runs = []
+    for x, s in zip(xs, streams):
+        n = x.numel()
+        buf = torch.empty(sz.encoded_size(0, n, n), dtype=torch.uint8, device="cuda")
+        ws_enc, ws_dec = sz.workspace(0, n), sz.workspace(0, n)
+        y = torch.empty_like(x)
+        runs.append((x, s, buf, ws_enc, ws_dec, y))
+    torch.cuda.synchronize()
+    for _ in range(3):                       # interleave the two streams' launches
+        for x, s, buf, ws_enc, ws_dec, y in runs:
+            sz.encode(x, cb, out=buf, ws=ws_enc, stream=s, sync=False)
+            sz.decode(buf, 0, x.numel(), out=y, ws=ws_dec, stream=s, check=False)
+    torch.cuda.synchronize()
+    for x, s, buf, ws_enc, ws_dec, y in runs:
+        bits = synth.as_bits_numpy(x)
+        expect = oracle.encode(bits, 0, list(cb.exps))
+        size = sz.encoded_size(0, x.numel(), sz.read_escape_count(buf))
+        assert size == expect.size
+        assert np.array_equal(buf[:size].cpu().numpy(), expect)
+        assert int(ws_dec[:4].cpu().view(torch.int32)[0]) == 0
+        assert torch.equal(y.view(torch.int16), x.view(torch.int16))
+
+
 def _corrupt_cases(stream, n):
     L = streamfmt.layout(0, n)
     first = L["off_esc"]
