@@ -44,8 +44,9 @@ def parse_args():
     p.add_argument("--core-only", action="store_true",
                    help="time only the encode+decode step (no calibration, format or transfer sections), "
                         "e.g. under a profiler")
-    p.add_argument("--cpu-sample-log2", type=int, default=28,
-                   help="elements of the workload the CPU oracle encodes and decodes (log2)")
+    p.add_argument("--cpu-sample-log2", type=int, default=29,
+                   help="elements of the workload the CPU oracle encodes and decodes (log2; the default, 2^29, is the "
+                        "whole Llama-3-8B cache, about 12 s of single-core work)")
     p.add_argument("--ingest-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"),
                    help="record HBM traffic per kernel from two rocprofv3 --pmc runs of this "
                         "benchmark (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json and exit")
