@@ -110,6 +110,33 @@ def test_edge_sizes_kv_like(n, dtype):
     roundtrip_check(bits, dtype, cb)
 
 
+# Streams up to 2048 tiles (32M elements) are ordered by one compaction launch
+# that sums the tile counts itself, larger ones through the scan; streams up
+# to 1024 blocks (64M elements) are decoded by workgroups that sum the block
+# counts themselves, larger ones after the scan.  Sizes at and just past the
+# encode limit and at the decode limit, so the fused paths and the mixed
+# case (scan encode, fused decode) are checked against the oracle byte for
+# byte; the full-size workloads take both scans.
+PATH_SIZES = [2048 * 16384, 2048 * 16384 + 1, 1024 * 65536]
+
+
+@pytest.mark.parametrize("n", PATH_SIZES)
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_prefix_path_limits(n, dtype):
+    # exponents from a sum of small uniform terms (a bell over 18 or 20
+    # values, so the Top-16 leaves a few per cent of escapes); integer draws
+    # keep 64M elements quick
+    r = np.random.default_rng(n % 1000 + 7).integers(0, 2 ** 32, n, dtype=np.uint32)
+    if dtype == 0:
+        e = 120 + (r & 7) + ((r >> 3) & 7) + ((r >> 6) & 3)
+        bits = (((r >> 16) & 0x807F) | (e << 7)).astype(np.uint16)
+    else:
+        e = 8 + (r & 3) + ((r >> 2) & 3) + ((r >> 4) & 3) + ((r >> 6) & 3) + ((r >> 8) & 7)
+        bits = (((r >> 16) & 0x83) | (e << 2)).astype(np.uint8)
+    cb = oracle.calibrate(bits, dtype)
+    roundtrip_check(bits, dtype, cb)
+
+
 def test_all_bf16_patterns():
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     roundtrip_check(bits, 0, oracle.calibrate(bits, 0))
