@@ -146,6 +146,18 @@ def ingest_pmc(workload, fetch_csv, write_csv, copy_bytes):
     return entry
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(x_dev, cb, dtype, log2_sample):
     import oracle
     import synth
@@ -164,8 +176,7 @@ def cpu_baseline(x_dev, cb, dtype, log2_sample):
         "value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "sample": "first %d elements (%d MiB) of the workload; one encode (%.2f s) and one "
                   "decode (%.2f s), single-threaded C, host %s, %d logical CPUs"
-                  % (n, n * elem >> 20, t1 - t0, t2 - t1, platform.processor() or platform.machine(),
-                     os.cpu_count()),
+                  % (n, n * elem >> 20, t1 - t0, t2 - t1, cpu_model(), os.cpu_count()),
     }
 
 
