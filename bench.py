@@ -54,11 +54,16 @@ def parse_args():
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel source with comments and blank space removed, so
-    that recorded counters stay tied to the code, not to its commentary."""
+    """Hash of the kernel sources (every file under csrc/, in name order) with
+    comments and blank space removed, so that recorded counters stay tied to
+    the code, not to its commentary."""
     import re
-    with open(os.path.join(ROOT, "fp8_kv_cache_sz_amd", "csrc", "splitzip.hip")) as f:
-        src = f.read()
+    csrc = os.path.join(ROOT, "fp8_kv_cache_sz_amd", "csrc")
+    src = ""
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name)) as f:
+                src += f.read() + "\n"
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())
@@ -94,12 +99,12 @@ LAUNCH_NAMES = {
 
 
 def short_kernel_name(name: str) -> str:
-    """'void (anonymous namespace)::sz_enc_compact<0>(...)' -> 'sz_enc_compact'
+    """'void sz::(anonymous namespace)::sz_cal_hist<0>(...)' -> 'sz_cal_hist_bf16'
     (the launch name the library's instrumentation records)."""
     name = name.replace("(anonymous namespace)::", "").split("(")[0]
     if name.startswith("void "):
         name = name[5:]
-    name = name.strip()
+    name = name.strip().split("::")[-1]
     return LAUNCH_NAMES.get(name, name.split("<")[0])
 
 
@@ -279,7 +284,15 @@ def main():
     alg_per_direction = alg_bytes // 2 // 16 * 16          # read half, write half
     src = torch.empty(alg_per_direction, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    copy_ms = time_loop(lambda: sz.reference_copy(src, dst), reps)
+    # timed per launch through the library's event instrumentation, as the
+    # codec kernels are, so that host gaps between launches do not count
+    sz.reference_copy(src, dst)
+    sz.profile_enable(True)
+    for _ in range(reps):
+        sz.reference_copy(src, dst)
+    launches, total_ms = sz.profile_collect()["sz_ref_copy"]
+    sz.profile_enable(False)
+    copy_ms = total_ms / launches
     copy_gbps = 2 * src.numel() / (copy_ms * 1e-3) / 1e9
     del src, dst
 

@@ -6,8 +6,9 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "splitzip.hip"), os.path.join(HERE, "csrc", "transfer.hip")]
-HEADERS = [os.path.join(ROOT, "include", "splitzip.h")]
+SOURCES = [os.path.join(HERE, "csrc", name) for name in
+           ("encode.hip", "decode.hip", "calibrate.hip", "runtime.hip", "transfer.hip")]
+HEADERS = [os.path.join(ROOT, "include", "splitzip.h"), os.path.join(HERE, "csrc", "common.hpp")]
 LIBRARY = os.path.join(HERE, "libsplitzip.so")
 ARCH = "gfx950"
 

@@ -1,0 +1,932 @@
+// SplitZip decode for MI355X: stream validation and block escape offsets
+// (one-workgroup scan, or for small streams a header check and per-workgroup
+// offsets), the dense decoders with the escape patch fused before the store,
+// the ablation-format decoders, and the decode entry points of the C ABI
+// ("SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
+// Serving", gist.science summary page, Method, decoding bullets).
+#include "common.hpp"
+
+namespace sz {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Kernel: decode scan.  One workgroup validates the header and the block
+// counts (each at most its block length, summing to E) and writes the
+// exclusive escape offset of every block.  It writes its verdict (0 or a
+// negative error code) to status[0], the caller-visible status word, and to
+// status[1], which the block decoders read: they only ever write status[0],
+// so every wave of a decode workgroup sees the same verdict.
+// ---------------------------------------------------------------------------
+struct DecodeArgs {
+    uint64_t n, nb, in_bytes, off_nib, off_sm, off_esc;
+    uint32_t dtype, symbols;
+    uint32_t version, item, entries;      // format version, escape item bytes, codebook entries used
+};
+
+// The stream header's verdict: 0, or the error of the first failed check
+// (magic, version, block size, dtype, N, nb, reserved word, E against N and
+// in_bytes, codebook entries).
+__device__ __forceinline__ int32_t header_verdict(const uint8_t *__restrict__ in, const DecodeArgs &a)
+{
+    const uint32_t *h32 = reinterpret_cast<const uint32_t *>(in);
+    const uint32_t w1 = h32[1];
+    const uint64_t n_hdr = (uint64_t)h32[2] | ((uint64_t)h32[3] << 32);
+    const uint64_t e_hdr = (uint64_t)h32[4] | ((uint64_t)h32[5] << 32);
+    if (h32[0] != kMagic || (w1 & 0xFFFFu) != a.version || (w1 >> 24) != kLog2Block) return SZ_E_FORMAT;
+    if (((w1 >> 16) & 0xFFu) != a.dtype) return SZ_E_DTYPE;
+    if (n_hdr != a.n || h32[6] != (uint32_t)a.nb || h32[7] != 0) return SZ_E_FORMAT;
+    if (e_hdr > a.n || a.off_esc + a.item * e_hdr > a.in_bytes) return SZ_E_FORMAT;
+    // used entries must be exponent values, unused ones zero
+    int32_t err = 0;
+    for (uint32_t c = 0; c < 16; ++c)
+        if (c < a.entries ? in[32 + c] >= a.symbols : in[32 + c] != 0) err = SZ_E_FORMAT;
+    return err;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: decode header check, in place of sz_dec_scan for streams of up to
+// kFusedPrefixBlocks blocks, whose decoders find their escape offsets
+// themselves (on MI355X 1.5-4.6 us faster per decode up to 64M elements; far
+// beyond, every decoder re-reading the counts before it costs more than the
+// scan).  One wave checks the header and writes the verdict to both
+// status words, as sz_dec_scan does; the block counts are checked by the
+// decoders.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kFusedPrefixBlocks = 1024;
+
+__global__ __launch_bounds__(64) void sz_dec_head(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                  int32_t *__restrict__ status)
+{
+    if (threadIdx.x == 0) {
+        const int32_t err = header_verdict(in, a);
+        status[0] = err;
+        status[1] = err;
+    }
+}
+
+__global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                            uint64_t *__restrict__ block_offsets,
+                                                            int32_t *__restrict__ status)
+{
+    __shared__ ScanLds lds;
+    __shared__ int32_t bad;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t e_hdr = *reinterpret_cast<const uint64_t *>(in + 16);
+    const int32_t err = header_verdict(in, a);
+    if (err) {
+        if (tid == 0) {
+            status[0] = err;
+            status[1] = err;
+        }
+        return;
+    }
+    if (tid == 0) {
+        bad = 0;
+        lds.carry = 0;
+    }
+    // items are groups of four block counts: one aligned dwordx4 each (the
+    // count array starts at byte 64 and is followed by padding up to off_nib)
+    const uint32_t *counts = reinterpret_cast<const uint32_t *>(in + 64);
+    const uint32_t nb = (uint32_t)a.nb;
+    // the last block may be shorter than B: its count is bounded by its length
+    bool too_many = nb && tid == 0 && counts[nb - 1] > a.n - (uint64_t)(nb - 1) * kBlock;
+    for (uint32_t g0 = 0; g0 < nb; g0 += 4 * kScanBatch * kScanThreads) {
+        uint4 v[kScanBatch];
+        uint32_t x[kScanBatch];
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+            const uint32_t g = g0 + 4 * (i * kScanThreads + tid);
+            v[i] = make_uint4(0, 0, 0, 0);
+            if (g < nb) {
+                v[i] = *reinterpret_cast<const uint4 *>(counts + g);
+                if (g + 1 >= nb) v[i].y = 0;
+                if (g + 2 >= nb) v[i].z = 0;
+                if (g + 3 >= nb) v[i].w = 0;
+                too_many |= std::max(std::max(v[i].x, v[i].y), std::max(v[i].z, v[i].w)) > (uint32_t)kBlock;
+            }
+            x[i] = v[i].x + v[i].y + v[i].z + v[i].w;
+        }
+        uint64_t base[kScanBatch];
+        scan_batch(x, base, lds);
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+            const uint32_t g = g0 + 4 * (i * kScanThreads + tid);
+            if (g < nb) {
+                const uint64_t o1 = base[i] + v[i].x, o2 = o1 + v[i].y, o3 = o2 + v[i].z;
+                if (g + 3 < nb) {
+                    // 32 aligned bytes: two dwordx4 stores of offset pairs
+                    uint4 *dst = reinterpret_cast<uint4 *>(block_offsets + g);
+                    dst[0] = make_uint4((uint32_t)base[i], (uint32_t)(base[i] >> 32), (uint32_t)o1, (uint32_t)(o1 >> 32));
+                    dst[1] = make_uint4((uint32_t)o2, (uint32_t)(o2 >> 32), (uint32_t)o3, (uint32_t)(o3 >> 32));
+                } else {
+                    block_offsets[g] = base[i];
+                    if (g + 1 < nb) block_offsets[g + 1] = o1;
+                    if (g + 2 < nb) block_offsets[g + 2] = o2;
+                }
+            }
+        }
+    }
+    if (too_many) bad = 1;
+    __syncthreads();
+    if (tid == 0) {
+        const int32_t verdict = (bad || lds.carry != e_hdr) ? SZ_E_FORMAT : 0;
+        status[0] = verdict;
+        status[1] = verdict;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernels: one 1024-lane workgroup per 64K block.  First an LDS map
+// from each chunk to the first escape record inside it is built from the
+// block's records (validating their order and range), then every wave
+// decodes one 4096-element row in registers, patches the escaped exponents
+// and stores once.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kNoEscape = 0xFFFFu;
+
+// Escape offset of block b and its count check.  With block_offsets (from
+// sz_dec_scan, which has checked every count) the offset is read.  Without
+// them (at most kFusedPrefixBlocks blocks) the whole workgroup sums the
+// counts of blocks 0..b-1 from the stream with aligned dwordx4 loads (the
+// count array starts at byte 64 and its section is padded to 256 bytes, so a
+// load of four counts never leaves it), each count capped at the block
+// length so that 32-bit sums cannot wrap, and checks the block's own count:
+// at most the block length, the records inside the E of the header, and for
+// the last block offset + count = E.  A failed check sets the status word
+// and zeroes k, so the block decodes without touching records; a count
+// above its block length fails its own block's check.  Called by every
+// thread; the result is workgroup-uniform.
+__device__ uint64_t block_escape_offset(const uint8_t *__restrict__ in, const DecodeArgs &a, uint64_t b,
+                                        uint32_t blen, uint64_t e_total, const uint64_t *__restrict__ block_offsets,
+                                        uint32_t &k, int32_t *__restrict__ status, uint32_t *part)
+{
+    if (block_offsets) return block_offsets[b];
+    if (k == 0 && b + 1 != a.nb) return 0;                      // no records and not the last block
+    const uint32_t *counts = reinterpret_cast<const uint32_t *>(in + 64);
+    const uint32_t bb = (uint32_t)b;                            // b < kFusedPrefixBlocks
+    uint32_t sum = 0;
+#pragma unroll 1
+    for (uint32_t g = 4 * threadIdx.x; g < bb; g += 4 * kDecThreads) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(counts + g);
+        sum += std::min<uint32_t>(v.x, kBlock) + (g + 1 < bb ? std::min<uint32_t>(v.y, kBlock) : 0u) +
+               (g + 2 < bb ? std::min<uint32_t>(v.z, kBlock) : 0u) +
+               (g + 3 < bb ? std::min<uint32_t>(v.w, kBlock) : 0u);
+    }
+    sum = read_lane63(wave_inclusive_sum(sum));
+    if (lane_id() == 0) part[threadIdx.x / 64] = sum;
+    __syncthreads();
+    uint32_t r0 = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kDecThreads / 64; ++w) r0 += part[w];
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+    if (k > blen || r0 + (uint64_t)k > e_total || (b + 1 == a.nb && r0 + (uint64_t)k != e_total)) {
+        if (threadIdx.x == 0) atomicExch(status, SZ_E_FORMAT);
+        k = 0;
+    }
+    return r0;
+}
+// Blocks with up to this many escapes decode through an LDS map of their
+// records; blocks with more go through the exponent plane.
+constexpr uint32_t kMappedEscapes = 8192;
+
+// Escape record r of the stream: position and exponent.
+__device__ __forceinline__ void read_record(const uint8_t *esc, uint64_t r, uint32_t &pos, uint32_t &e)
+{
+    const uint8_t *p = esc + 3 * r;
+    pos = (uint32_t)p[0] | ((uint32_t)p[1] << 8);
+    e = p[2];
+}
+
+// Four consecutive records from one 16-byte window of aligned words.  The
+// window never leaves the record section: it starts at most 3 bytes before
+// record R and ends at most 3 bytes after record R+3, and callers use it only
+// while a whole record group past R+3 remains in the stream (otherwise they
+// read the records byte by byte).
+__device__ __forceinline__ void read_records4(const uint8_t *esc, uint64_t r, uint32_t pos[4], uint32_t e[4])
+{
+    const uint64_t byte0 = 3 * r;
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(esc + (byte0 & ~uint64_t(3)));
+    const uint32_t sh = (uint32_t)(byte0 & 3);
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+    const uint32_t d0 = __builtin_amdgcn_alignbyte(w1, w0, sh);   // bytes 0..3 of the 12
+    const uint32_t d1 = __builtin_amdgcn_alignbyte(w2, w1, sh);   // bytes 4..7
+    const uint32_t d2 = __builtin_amdgcn_alignbyte(w3, w2, sh);   // bytes 8..11
+    pos[0] = d0 & 0xFFFFu;
+    e[0] = (d0 >> 16) & 0xFFu;
+    pos[1] = (d0 >> 24) | ((d1 & 0xFFu) << 8);
+    e[1] = (d1 >> 8) & 0xFFu;
+    pos[2] = d1 >> 16;
+    e[2] = d2 & 0xFFu;
+    pos[3] = (d2 >> 8) & 0xFFFFu;
+    e[3] = d2 >> 24;
+}
+
+// Loads the k (<= kMappedEscapes) records of a block into LDS as
+// pos | exponent << 16, four records per aligned three-word window where the
+// window stays inside the record section, one by one at its end.
+__device__ __forceinline__ void load_block_records(const uint8_t *esc, uint64_t r0, uint32_t k, uint64_t e_total,
+                                                   uint32_t *rec)
+{
+    for (uint32_t r = 4 * threadIdx.x; r < k; r += 4 * blockDim.x) {
+        uint32_t pos[4], e[4];
+        if (r0 + r + 5 < e_total) {
+            read_records4(esc, r0 + r, pos, e);
+        } else {
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q) {
+                pos[q] = e[q] = 0;
+                if (r + q < k) read_record(esc, r0 + r + q, pos[q], e[q]);
+            }
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q)
+            if (r + q < k) rec[r + q] = pos[q] | (e[q] << 16);
+    }
+}
+
+// Builds first[chunk] for the k records of a block held in LDS (chunk =
+// pos >> log2_chunk) and reports malformed records through the status word.
+template <int LOG2_CHUNK>
+__device__ __forceinline__ void map_block_escapes(const uint32_t *rec, uint32_t k, uint32_t blen, uint32_t symbols,
+                                                  uint16_t *first, int32_t *status)
+{
+    bool bad = false;
+    for (uint32_t r = threadIdx.x; r < k; r += blockDim.x) {
+        const uint32_t v = rec[r];
+        const uint32_t pos = v & 0xFFFFu;
+        const int32_t prev = r > 0 ? (int32_t)(rec[r - 1] & 0xFFFFu) : -1;
+        if (pos >= blen || (int32_t)pos <= prev || (v >> 16) >= symbols) {
+            bad = true;
+            continue;
+        }
+        if (r == 0 || (uint32_t)(prev >> LOG2_CHUNK) != (pos >> LOG2_CHUNK)) first[pos >> LOG2_CHUNK] = (uint16_t)r;
+    }
+    if (bad) atomicExch(status, SZ_E_FORMAT);
+}
+
+__device__ __forceinline__ uint4 decode_chunk_bf16(uint32_t nib, uint2 sm, const uint32_t *table)
+{
+    // table[b] = cb[b & 15] << 7 | cb[b >> 4] << 23: both exponents of a
+    // code byte, already in place for two packed BF16 values
+    uint4 o;
+    o.x = (perm(sm.x, sm.x, 0x01010000u) & 0x807F807Fu) | table[nib & 0xFFu];
+    o.y = (perm(sm.x, sm.x, 0x03030202u) & 0x807F807Fu) | table[(nib >> 8) & 0xFFu];
+    o.z = (perm(sm.y, sm.y, 0x01010000u) & 0x807F807Fu) | table[(nib >> 16) & 0xFFu];
+    o.w = (perm(sm.y, sm.y, 0x03030202u) & 0x807F807Fu) | table[nib >> 24];
+    return o;
+}
+
+__device__ __forceinline__ void patch_bf16(uint4 &o, uint32_t k, uint32_t e)
+{
+    const uint32_t sh = 7 + 16 * (k & 1);
+    const uint32_t clear = ~(0xFFu << sh);
+    const uint32_t set = e << sh;
+    switch (k >> 1) {
+    case 0: o.x = (o.x & clear) | set; break;
+    case 1: o.y = (o.y & clear) | set; break;
+    case 2: o.z = (o.z & clear) | set; break;
+    default: o.w = (o.w & clear) | set; break;
+    }
+}
+
+// Blocks with more than kMappedEscapes escapes decode through an exponent
+// plane: every element's dense exponent goes to a 64 KB LDS byte array, the
+// block's records overwrite their entries (validated on the way), and the
+// values are rebuilt from the plane and stored once.
+
+// Register code -> exponent lookup for the eight codes of a code word d
+// (element 2k in the low nibble of byte k); cb0..cb3 = codebook bytes.
+// v_perm_b32 indexes eight bytes, so each half of the book is one v_perm and
+// bit 3 of every code picks the half through a byte mask that v_perm's
+// sign-replication selectors build (8: bit 15 of the low word, 9: bit 31 of
+// the low word, 10/11: the same bits of the high word).  Returns the eight
+// exponents in element order (bytes 0..3 then 4..7).
+struct CodebookRegs {
+    uint32_t w0, w1, w2, w3;
+};
+
+__device__ __forceinline__ uint2 lookup_codes8(uint32_t d, const CodebookRegs &cb)
+{
+    const uint32_t sel_e = d & 0x07070707u;
+    const uint32_t sel_o = (d >> 4) & 0x07070707u;
+    const uint32_t m_e = perm(d << 4, d << 12, 0x0B090A08u);      // bit 3 of the even codes
+    const uint32_t m_o = perm(d, d << 8, 0x0B090A08u);            // bit 3 of the odd codes
+    const uint32_t e_even = (perm(cb.w3, cb.w2, sel_e) & m_e) | (perm(cb.w1, cb.w0, sel_e) & ~m_e);
+    const uint32_t e_odd = (perm(cb.w3, cb.w2, sel_o) & m_o) | (perm(cb.w1, cb.w0, sel_o) & ~m_o);
+    return make_uint2(perm(e_odd, e_even, 0x05010400u), perm(e_odd, e_even, 0x07030602u));
+}
+
+// Overwrites plane[pos] with the exponent of each of the block's k records,
+// four records per aligned three-word window; invalid records (position out
+// of the block or not ascending, exponent out of range) are skipped and
+// reported through the status word.
+__device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ esc, uint64_t r0, uint32_t k,
+                                                    uint32_t blen, uint32_t symbols, uint64_t e_total,
+                                                    uint8_t *plane, int32_t *__restrict__ status)
+{
+    const uint32_t lane = lane_id();
+    bool bad = false;
+    for (uint32_t r = 4 * threadIdx.x; r < k; r += 4 * blockDim.x) {
+        uint32_t pos[4], e[4];
+        const uint32_t cnt = std::min<uint32_t>(4, k - r);
+        if (r0 + r + 5 < e_total) {
+            read_records4(esc, r0 + r, pos, e);
+        } else {
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q) {
+                pos[q] = 0xFFFFFFFFu;
+                e[q] = 0;
+                if (q < cnt) read_record(esc, r0 + r + q, pos[q], e[q]);
+            }
+        }
+        uint32_t prev = __shfl_up(pos[3], 1, 64);        // lane l-1 holds records r-4..r-1
+        if (lane == 0 && r > 0) {
+            uint32_t pe;
+            read_record(esc, r0 + r - 1, prev, pe);
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q) {
+            if (q >= cnt) continue;
+            const uint32_t before = q == 0 ? prev : pos[q - 1];
+            if (pos[q] < blen && e[q] < symbols && (r + q == 0 || pos[q] > before)) plane[pos[q]] = (uint8_t)e[q];
+            else bad = true;
+        }
+    }
+    if (bad) atomicExch(status, SZ_E_FORMAT);
+}
+
+__global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                           const uint64_t *__restrict__ block_offsets,
+                                                           int32_t *__restrict__ status,
+                                                           uint16_t *__restrict__ out)
+{
+    __shared__ uint32_t table[256];
+    __shared__ uint32_t prefix_part[kDecThreads / 64];
+    // mapped blocks: first[] (first record of each 8-element chunk, 16 KB) and
+    // rec[] (the records, 32 KB); heavy blocks: the exponent plane (64 KB)
+    __shared__ __align__(16) uint8_t pool[kBlock];
+    uint16_t *first = reinterpret_cast<uint16_t *>(pool);
+    uint32_t *rec = reinterpret_cast<uint32_t *>(pool + kBlock / 4);
+    uint8_t *plane = pool;
+    if (status[1] != 0) return;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t b = blockIdx.x;
+    const uint64_t e0 = b * kBlock;
+    const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
+    uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
+    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
+    const uint8_t *esc = in + a.off_esc;
+    if (tid < 256) {
+        const uint32_t lo = in[32 + (tid & 15)];
+        const uint32_t hi = in[32 + (tid >> 4)];
+        table[tid] = (lo << 7) | (hi << 23);
+    }
+    // the row's loads are issued first and stay in flight while the escape
+    // map is built (the barriers only wait for LDS traffic)
+    const uint32_t lane = lane_id();
+    const uint32_t rbase = (tid / 64) * kRow;                  // block-local first element of the row
+    const bool full_row = rbase + kRow <= blen;
+    const uint8_t *nib_base = in + a.off_nib;
+    const uint8_t *sm_base = in + a.off_sm;
+    uint32_t nib[kBf16Chunks];
+    uint2 sm[kBf16Chunks];
+#pragma unroll
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + lane) * 8;
+        const uint64_t g = e0 + c;
+        if (full_row || c < blen) {
+            nib[j] = load_nt(reinterpret_cast<const uint32_t *>(nib_base + g / 2));
+            sm[j] = load_nt(reinterpret_cast<const uint2 *>(sm_base + g));
+        } else {
+            nib[j] = 0;
+            sm[j] = make_uint2(0, 0);
+        }
+    }
+    const uint64_t r0 = block_escape_offset(in, a, b, blen, e_total, block_offsets, k, status, prefix_part);
+    const bool heavy = k > kMappedEscapes;                        // workgroup-uniform
+    if (heavy) {
+        const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
+        const CodebookRegs cb = {cbw[0], cbw[1], cbw[2], cbw[3]};
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            if (c < blen) *reinterpret_cast<uint2 *>(plane + c) = lookup_codes8(nib[j], cb);
+        }
+        __syncthreads();
+        overwrite_exponents(esc, r0, k, blen, 256, e_total, plane, status);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            if (c >= blen) continue;
+            const uint2 ex = *reinterpret_cast<const uint2 *>(plane + c);   // exponents, element order
+            uint4 o;
+            o.x = (perm(sm[j].x, sm[j].x, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C010C00u) << 7);
+            o.y = (perm(sm[j].x, sm[j].x, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C030C02u) << 7);
+            o.z = (perm(sm[j].y, sm[j].y, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C050C04u) << 7);
+            o.w = (perm(sm[j].y, sm[j].y, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C070C06u) << 7);
+            const uint64_t g = e0 + c;
+            if (full_row || c + 8 <= blen) {
+                store_nt(reinterpret_cast<uint4 *>(out + g), o);
+            } else {
+                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+            }
+        }
+        return;
+    }
+    if (k) {
+        reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+        load_block_records(esc, r0, k, e_total, rec);
+    }
+    __syncthreads();
+    if (k) map_block_escapes<3>(rec, k, blen, 256, first, status);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + lane) * 8;
+        if (c >= blen) continue;
+        uint4 o = decode_chunk_bf16(nib[j], sm[j], table);
+        if (k) {
+            uint32_t r = first[c >> 3];
+            if (r != kNoEscape) {
+                for (; r < k; ++r) {
+                    const uint32_t v = rec[r];
+                    if (((v & 0xFFFFu) >> 3) != (c >> 3)) break;
+                    patch_bf16(o, v & 7, v >> 16);
+                }
+            }
+        }
+        const uint64_t g = e0 + c;
+        if (full_row || c + 8 <= blen) {
+            store_nt(reinterpret_cast<uint4 *>(out + g), o);
+        } else {
+            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+            for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode of the ablation formats (BF16), in the shape of sz_dec_bf16: one
+// 1024-lane workgroup per 64K block, one 4096-element row per wave, eight
+// 8-element chunks per lane, one store per chunk.
+//   Version 2 (Top-8): a chunk's codes are the 3 bytes at 3 * chunk, taken
+//   from two aligned words; a 64-entry LDS table turns each pair of 3-bit
+//   codes into both exponents.  Escapes are position records, patched as in
+//   sz_dec_bf16 (an LDS map for blocks with up to kMappedEscapes records,
+//   the exponent plane above that).
+//   Version 3 (Top-15 + sentinel): nibble codes as in version 1, code 15
+//   marks an escape whose exponent is the next byte of the block's escape
+//   bytes.  Each sentinel's rank inside its block comes from per-chunk
+//   counts, a wave prefix sum and a prefix over the waves; the block's
+//   sentinels must number exactly its count.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 decode_chunk_top8(uint32_t code24, uint2 sm, const uint32_t *table64)
+{
+    // table64[p] = cb[p & 7] << 7 | cb[p >> 3] << 23 for a pair p of 3-bit codes
+    uint4 o;
+    o.x = (perm(sm.x, sm.x, 0x01010000u) & 0x807F807Fu) | table64[code24 & 63u];
+    o.y = (perm(sm.x, sm.x, 0x03030202u) & 0x807F807Fu) | table64[(code24 >> 6) & 63u];
+    o.z = (perm(sm.y, sm.y, 0x01010000u) & 0x807F807Fu) | table64[(code24 >> 12) & 63u];
+    o.w = (perm(sm.y, sm.y, 0x03030202u) & 0x807F807Fu) | table64[(code24 >> 18) & 63u];
+    return o;
+}
+
+// Four 3-bit codes (12 bits) -> one code per byte, as v_perm selectors.
+__device__ __forceinline__ uint32_t spread_codes3x4(uint32_t x)
+{
+    return (x & 7u) | ((x << 5) & 0x700u) | ((x << 10) & 0x70000u) | ((x << 15) & 0x7000000u);
+}
+
+// Nibbles equal to 15 (the version 3 sentinel): bit 4k set for element k.
+__device__ __forceinline__ uint32_t sentinel_bits(uint32_t nib)
+{
+    return nib & (nib >> 1) & (nib >> 2) & (nib >> 3) & 0x11111111u;
+}
+
+template <int V>
+__global__ __launch_bounds__(kDecThreads) void sz_dec_variant(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                              const uint64_t *__restrict__ block_offsets,
+                                                              int32_t *__restrict__ status,
+                                                              uint16_t *__restrict__ out)
+{
+    __shared__ uint32_t table[256];
+    __shared__ uint32_t wave_totals[kDecThreads / 64];
+    __shared__ uint32_t prefix_part[kDecThreads / 64];
+    __shared__ __align__(16) uint8_t pool[V == kTop8 ? kBlock : 16];
+    uint16_t *first = reinterpret_cast<uint16_t *>(pool);
+    uint32_t *rec = reinterpret_cast<uint32_t *>(pool + kBlock / 4);
+    uint8_t *plane = pool;
+    if (status[1] != 0) return;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t b = blockIdx.x;
+    const uint64_t e0 = b * kBlock;
+    const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
+    uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
+    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
+    const uint8_t *esc = in + a.off_esc;
+    if (V == kTop8) {
+        if (tid < 64) table[tid] = ((uint32_t)in[32 + (tid & 7)] << 7) | ((uint32_t)in[32 + (tid >> 3)] << 23);
+    } else if (tid < 256) {
+        table[tid] = ((uint32_t)in[32 + (tid & 15)] << 7) | ((uint32_t)in[32 + (tid >> 4)] << 23);
+    }
+    const uint32_t lane = lane_id();
+    const uint32_t rbase = (tid / 64) * kRow;
+    const bool full_row = rbase + kRow <= blen;
+    uint32_t code[kBf16Chunks];
+    uint2 sm[kBf16Chunks];
+#pragma unroll
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + lane) * 8;
+        const uint64_t g = e0 + c;
+        code[j] = 0;
+        sm[j] = make_uint2(0, 0);
+        if (full_row || c < blen) {
+            if (V == kTop8) {
+                const uint64_t byte0 = 3 * (g / 8);
+                const uint32_t *w = reinterpret_cast<const uint32_t *>(in + a.off_nib + (byte0 & ~uint64_t(3)));
+                code[j] = __builtin_amdgcn_alignbit(w[1], w[0], 8 * (uint32_t)(byte0 & 3)) & 0xFFFFFFu;
+            } else {
+                code[j] = load_nt(reinterpret_cast<const uint32_t *>(in + a.off_nib + g / 2));
+            }
+            sm[j] = load_nt(reinterpret_cast<const uint2 *>(in + a.off_sm + g));
+        }
+    }
+    const uint64_t r0 = block_escape_offset(in, a, b, blen, e_total, block_offsets, k, status, prefix_part);
+    const bool heavy = V == kTop8 && k > kMappedEscapes;          // workgroup-uniform
+    if (V == kTop15S) {
+        // ranks of the sentinels inside the block
+        uint32_t sbits[kBf16Chunks], cnt[kBf16Chunks];
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            sbits[j] = sentinel_bits(code[j]);
+            if (c >= blen) sbits[j] = 0;
+            else if (c + 8 > blen) sbits[j] &= (1u << (4 * (blen - c))) - 1;   // padding nibbles do not count
+            cnt[j] = __popc(sbits[j]);
+        }
+        uint32_t row_base[kBf16Chunks], row_total[kBf16Chunks], lane_before[kBf16Chunks];
+        const uint32_t wave_total = wave_chunk_ranks<kBf16Chunks>(cnt, row_base, row_total, lane_before);
+        uint32_t block_total;
+        const uint32_t wave_before = workgroup_wave_prefix<kDecThreads / 64>(wave_total, wave_totals, block_total);
+        bool bad = block_total != k;
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            if (c >= blen) continue;
+            uint4 o = decode_chunk_bf16(code[j], sm[j], table);
+            uint32_t rank = wave_before + row_base[j] + lane_before[j];
+            for (uint32_t m = sbits[j]; m; m &= m - 1, ++rank) {
+                uint32_t e = 0;
+                if (rank < k) e = esc[r0 + rank];
+                else bad = true;
+                patch_bf16(o, (uint32_t)__builtin_ctz(m) / 4, e);
+            }
+            const uint64_t g = e0 + c;
+            if (full_row || c + 8 <= blen) {
+                store_nt(reinterpret_cast<uint4 *>(out + g), o);
+            } else {
+                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+            }
+        }
+        if (bad) atomicExch(status, SZ_E_FORMAT);
+        return;
+    }
+    // version 2: position records
+    if (heavy) {
+        const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
+        const uint32_t cb0 = cbw[0], cb1 = cbw[1];
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            if (c < blen)
+                *reinterpret_cast<uint2 *>(plane + c) = make_uint2(perm(cb1, cb0, spread_codes3x4(code[j] & 0xFFFu)),
+                                                                   perm(cb1, cb0, spread_codes3x4(code[j] >> 12)));
+        }
+        __syncthreads();
+        overwrite_exponents(esc, r0, k, blen, 256, e_total, plane, status);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + lane) * 8;
+            if (c >= blen) continue;
+            const uint2 ex = *reinterpret_cast<const uint2 *>(plane + c);
+            uint4 o;
+            o.x = (perm(sm[j].x, sm[j].x, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C010C00u) << 7);
+            o.y = (perm(sm[j].x, sm[j].x, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C030C02u) << 7);
+            o.z = (perm(sm[j].y, sm[j].y, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C050C04u) << 7);
+            o.w = (perm(sm[j].y, sm[j].y, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C070C06u) << 7);
+            const uint64_t g = e0 + c;
+            if (full_row || c + 8 <= blen) {
+                store_nt(reinterpret_cast<uint4 *>(out + g), o);
+            } else {
+                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+            }
+        }
+        return;
+    }
+    if (k) {
+        reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+        load_block_records(esc, r0, k, e_total, rec);
+    }
+    __syncthreads();
+    if (k) map_block_escapes<3>(rec, k, blen, 256, first, status);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + lane) * 8;
+        if (c >= blen) continue;
+        uint4 o = decode_chunk_top8(code[j], sm[j], table);
+        if (k) {
+            uint32_t r = first[c >> 3];
+            if (r != kNoEscape) {
+                for (; r < k; ++r) {
+                    const uint32_t v = rec[r];
+                    if (((v & 0xFFFFu) >> 3) != (c >> 3)) break;
+                    patch_bf16(o, v & 7, v >> 16);
+                }
+            }
+        }
+        const uint64_t g = e0 + c;
+        if (full_row || c + 8 <= blen) {
+            store_nt(reinterpret_cast<uint4 *>(out + g), o);
+        } else {
+            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+            for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+        }
+    }
+}
+
+// FP8 E5M2 decode: a lane decodes two 32-element chunks (16 code bytes + 12
+// sign/mantissa bytes -> 32 bytes each).
+__device__ __forceinline__ uint32_t unpack_sm3_x4(uint32_t v12)
+{
+    // 12 bits = four 3-bit symbols -> one symbol per byte
+    return (v12 & 0x7u) | ((v12 << 5) & 0x700u) | ((v12 << 10) & 0x70000u) | ((v12 << 15) & 0x7000000u);
+}
+
+__device__ __forceinline__ void decode_chunk_e5m2(const uint4 nib, const uint32_t sm3[3],
+                                                  const uint16_t *table, uint32_t o[8])
+{
+    // table[b] = (cb[b & 15] << 2) | (cb[b >> 4] << 10): the exponent fields of
+    // the two elements of code byte b, in place inside two E5M2 bytes
+    const uint32_t nw[4] = {nib.x, nib.y, nib.z, nib.w};
+    const uint32_t grp[4] = {sm3[0] & 0xFFFFFFu, (sm3[0] >> 24) | ((sm3[1] & 0xFFFFu) << 8),
+                             (sm3[1] >> 16) | ((sm3[2] & 0xFFu) << 16), sm3[2] >> 8};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t w = nw[s];
+        const uint32_t e_lo = (uint32_t)table[w & 0xFFu] | ((uint32_t)table[(w >> 8) & 0xFFu] << 16);
+        const uint32_t e_hi = (uint32_t)table[(w >> 16) & 0xFFu] | ((uint32_t)table[w >> 24] << 16);
+        const uint32_t t_lo = unpack_sm3_x4(grp[s] & 0xFFFu);
+        const uint32_t t_hi = unpack_sm3_x4(grp[s] >> 12);
+        o[2 * s] = ((t_lo & 0x04040404u) << 5) | (t_lo & 0x03030303u) | e_lo;
+        o[2 * s + 1] = ((t_hi & 0x04040404u) << 5) | (t_hi & 0x03030303u) | e_hi;
+    }
+}
+
+// E5M2 rows are decoded with lane 2m on chunk m and lane 2m+1 on chunk
+// 32 + m of each 64-chunk row, so that after the two lanes swap the half
+// (16 bytes) each one does not keep, each of the two stores of a row writes
+// 1 KB of contiguous output.
+__device__ __forceinline__ uint32_t e5m2_chunk_of_lane(uint32_t lane)
+{
+    return (lane & 1) ? 32 + (lane >> 1) : (lane >> 1);
+}
+
+__device__ __forceinline__ void store_chunk_pairs(uint8_t *row_out, const uint32_t o[8], uint32_t lane)
+{
+    const bool odd = lane & 1;
+    uint32_t keep[4], give[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        keep[i] = odd ? o[4 + i] : o[i];
+        give[i] = odd ? o[i] : o[4 + i];
+        give[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)give[i], 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    }
+    // even lanes: bytes [16l, 16l+16) of the first KB = their own low half;
+    // odd lanes: the same range = the partner's high half
+    const uint4 first_kb = odd ? make_uint4(give[0], give[1], give[2], give[3])
+                               : make_uint4(keep[0], keep[1], keep[2], keep[3]);
+    const uint4 second_kb = odd ? make_uint4(keep[0], keep[1], keep[2], keep[3])
+                                : make_uint4(give[0], give[1], give[2], give[3]);
+    store_nt(reinterpret_cast<uint4 *>(row_out + 16 * lane), first_kb);
+    store_nt(reinterpret_cast<uint4 *>(row_out + 1024 + 16 * lane), second_kb);
+}
+
+__global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                           const uint64_t *__restrict__ block_offsets,
+                                                           int32_t *__restrict__ status,
+                                                           uint8_t *__restrict__ out)
+{
+    __shared__ uint16_t table[256];
+    __shared__ uint32_t prefix_part[kDecThreads / 64];
+    // mapped blocks: first[] (first record of each 32-element chunk, 4 KB) and
+    // rec[] (the records, 32 KB); heavy blocks: the exponent plane (64 KB)
+    __shared__ __align__(16) uint8_t pool[kBlock];
+    uint16_t *first = reinterpret_cast<uint16_t *>(pool);
+    uint32_t *rec = reinterpret_cast<uint32_t *>(pool + kBlock / 16);
+    uint8_t *plane = pool;
+    if (status[1] != 0) return;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t b = blockIdx.x;
+    const uint64_t e0 = b * kBlock;
+    const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
+    uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
+    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
+    const uint8_t *esc = in + a.off_esc;
+    if (tid < 256) {
+        const uint32_t lo = in[32 + (tid & 15)];
+        const uint32_t hi = in[32 + (tid >> 4)];
+        table[tid] = (uint16_t)((lo << 2) | (hi << 10));
+    }
+    const uint32_t lane = lane_id();
+    const uint32_t rbase = (tid / 64) * kRow;
+    const bool full_row = rbase + kRow <= blen;
+    const uint8_t *nib_base = in + a.off_nib;
+    const uint8_t *sm_base = in + a.off_sm;
+    const uint64_t sm_end = a.off_sm + 3 * ((a.n + 7) / 8);
+    uint4 nib[kE5Chunks];
+    uint32_t sm3[kE5Chunks][3];
+#pragma unroll
+    for (int j = 0; j < kE5Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
+        const uint64_t g = e0 + c;
+        if (full_row || c + 32 <= blen) {
+            nib[j] = load_nt(reinterpret_cast<const uint4 *>(nib_base + g / 2));
+            load3_nt(reinterpret_cast<const uint32_t *>(sm_base + (g / 32) * 12), sm3[j]);
+        } else if (c < blen) {
+            nib[j] = *reinterpret_cast<const uint4 *>(nib_base + g / 2);
+            sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
+            const uint64_t start = a.off_sm + (g / 32) * 12;
+            for (uint32_t i = 0; i < 12 && start + i < sm_end; ++i)
+                sm3[j][i / 4] |= (uint32_t)in[start + i] << (8 * (i & 3));
+        } else {
+            nib[j] = make_uint4(0, 0, 0, 0);
+            sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
+        }
+    }
+    const uint64_t r0 = block_escape_offset(in, a, b, blen, e_total, block_offsets, k, status, prefix_part);
+    const bool heavy = k > kMappedEscapes;                        // workgroup-uniform
+    if (heavy) {
+        const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
+        const CodebookRegs cb = {cbw[0], cbw[1], cbw[2], cbw[3]};
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
+            if (c >= blen) continue;
+            const uint32_t nw[4] = {nib[j].x, nib[j].y, nib[j].z, nib[j].w};
+#pragma unroll
+            for (int s8 = 0; s8 < 4; ++s8) *reinterpret_cast<uint2 *>(plane + c + 8 * s8) = lookup_codes8(nw[s8], cb);
+        }
+        __syncthreads();
+        overwrite_exponents(esc, r0, k, blen, 32, e_total, plane, status);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
+            if (c >= blen) continue;
+            const uint32_t grp[4] = {sm3[j][0] & 0xFFFFFFu, (sm3[j][0] >> 24) | ((sm3[j][1] & 0xFFFFu) << 8),
+                                     (sm3[j][1] >> 16) | ((sm3[j][2] & 0xFFu) << 16), sm3[j][2] >> 8};
+            uint32_t o[8];
+#pragma unroll
+            for (int s8 = 0; s8 < 4; ++s8) {
+                const uint2 ex = *reinterpret_cast<const uint2 *>(plane + c + 8 * s8);
+                const uint32_t t_lo = unpack_sm3_x4(grp[s8] & 0xFFFu);
+                const uint32_t t_hi = unpack_sm3_x4(grp[s8] >> 12);
+                o[2 * s8] = ((t_lo & 0x04040404u) << 5) | (t_lo & 0x03030303u) | (ex.x << 2);
+                o[2 * s8 + 1] = ((t_hi & 0x04040404u) << 5) | (t_hi & 0x03030303u) | (ex.y << 2);
+            }
+            const uint64_t g = e0 + c;
+            if (full_row) {
+                store_chunk_pairs(out + e0 + rbase + j * 2048, o, lane);
+            } else if (c + 32 <= blen) {
+                store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
+                store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
+            } else {
+                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint8_t)(o[i / 4] >> (8 * (i & 3)));
+            }
+        }
+        return;
+    }
+    if (k) {
+        if (tid < kBlock / 32 / 8) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
+        load_block_records(esc, r0, k, e_total, rec);
+    }
+    __syncthreads();
+    if (k) map_block_escapes<5>(rec, k, blen, 32, first, status);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kE5Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
+        if (c >= blen) continue;
+        uint32_t o[8];
+        decode_chunk_e5m2(nib[j], sm3[j], table, o);
+        if (k) {
+            uint32_t r = first[c >> 5];
+            if (r != kNoEscape) {
+                for (; r < k; ++r) {
+                    const uint32_t v = rec[r];
+                    const uint32_t pos = v & 0xFFFFu, e = v >> 16;
+                    if ((pos >> 5) != (c >> 5)) break;
+                    const uint32_t p = pos & 31;
+                    const uint32_t sh = 8 * (p & 3) + 2;
+                    const uint32_t clear = ~(0x1Fu << sh);
+#pragma unroll
+                    for (int w = 0; w < 8; ++w)
+                        if ((uint32_t)w == (p >> 2)) o[w] = (o[w] & clear) | (e << sh);
+                }
+            }
+        }
+        const uint64_t g = e0 + c;
+        if (full_row) {
+            store_chunk_pairs(out + e0 + rbase + j * 2048, o, lane);
+        } else if (c + 32 <= blen) {
+            store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
+            store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
+        } else {
+            for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint8_t)(o[i / 4] >> (8 * (i & 3)));
+        }
+    }
+}
+
+int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
+                void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (n_elems > kMaxElems) return SZ_E_ARG;
+    if (!d_in || !d_ws || (n_elems && !d_out)) return SZ_E_ARG;
+    if (!aligned16(d_in) || !aligned16(d_ws) || (n_elems && !aligned16(d_out))) return SZ_E_ALIGN;
+    if (in_bytes < encoded_size_v(version, dtype, n_elems, 0)) return SZ_E_FORMAT;
+    if (ws_bytes < sz_workspace_size(dtype, n_elems)) return SZ_E_WORKSPACE;
+    const Geometry g = geometry(dtype, n_elems, version);
+    const WsLayout w = ws_layout(dtype, n_elems);
+    uint8_t *ws = static_cast<uint8_t *>(d_ws);
+    int32_t *status = reinterpret_cast<int32_t *>(ws);
+    uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DecodeArgs a;
+    a.n = g.n;
+    a.nb = g.nb;
+    a.in_bytes = in_bytes;
+    a.off_nib = g.off_nib;
+    a.off_sm = g.off_sm;
+    a.off_esc = g.off_esc;
+    a.dtype = (uint32_t)dtype;
+    a.symbols = symbols_of(dtype);
+    a.version = version;
+    a.item = escape_item_bytes(version);
+    a.entries = book_entries(version);
+    const uint8_t *in = static_cast<const uint8_t *>(d_in);
+    if (g.nb <= kFusedPrefixBlocks) {
+        // the decoders sum the counts before their block themselves
+        block_offsets = nullptr;
+        LaunchScope scope("sz_dec_head", s);
+        hipLaunchKernelGGL(sz_dec_head, dim3(1), dim3(64), 0, s, in, a, status);
+    } else {
+        LaunchScope scope("sz_dec_scan", s);
+        hipLaunchKernelGGL(sz_dec_scan, dim3(1), dim3(kScanThreads), 0, s, in, a, block_offsets, status);
+    }
+    if (g.nb && version == kTop8) {
+        LaunchScope scope("sz_dec_top8", s);
+        hipLaunchKernelGGL(sz_dec_variant<kTop8>, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a,
+                           block_offsets, status, static_cast<uint16_t *>(d_out));
+    } else if (g.nb && version == kTop15S) {
+        LaunchScope scope("sz_dec_top15s", s);
+        hipLaunchKernelGGL(sz_dec_variant<kTop15S>, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a,
+                           block_offsets, status, static_cast<uint16_t *>(d_out));
+    } else if (g.nb && dtype == SZ_BF16) {
+        LaunchScope scope("sz_dec_bf16", s);
+        hipLaunchKernelGGL(sz_dec_bf16, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, block_offsets,
+                           status, static_cast<uint16_t *>(d_out));
+    } else if (g.nb) {
+        LaunchScope scope("sz_dec_e5m2", s);
+        hipLaunchKernelGGL(sz_dec_e5m2, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, block_offsets,
+                           status, static_cast<uint8_t *>(d_out));
+    }
+    return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
+}
+
+}  // namespace
+}  // namespace sz
+
+using namespace sz;
+
+extern "C" int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
+                         void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    return decode_impl(kTop16, d_in, in_bytes, dtype, d_out, n_elems, d_ws, ws_bytes, stream);
+}
+
+extern "C" int sz_decode_format(int format, const void *d_in, uint64_t in_bytes, int dtype, void *d_out,
+                                uint64_t n_elems, void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (format == SZ_FORMAT_TOP16) return sz_decode(d_in, in_bytes, dtype, d_out, n_elems, d_ws, ws_bytes, stream);
+    if (format != SZ_FORMAT_TOP8 && format != SZ_FORMAT_TOP15_SENTINEL) return SZ_E_ARG;
+    if (dtype != SZ_BF16) return SZ_E_DTYPE;
+    return decode_impl((uint32_t)format, d_in, in_bytes, dtype, d_out, n_elems, d_ws, ws_bytes, stream);
+}
+

@@ -1,0 +1,1190 @@
+// SplitZip encode for MI355X: the dense kernels (codes, sign/mantissa
+// bytes, escape staging), the ordering of the escape records (one-workgroup
+// scan + compaction, or for small streams one compaction launch that finds
+// its own offsets), the stream header, and the encode entry points of the
+// C ABI ("SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
+// Serving", gist.science summary page, Method, encoding bullets).
+#include "common.hpp"
+
+namespace sz {
+namespace {
+
+// Exponent -> code table for encode.  Byte v = code of exponent v, or
+// `escape` (the escape flag 0x80 plus the code an escaped element carries)
+// when v is not among the first `entries` codebook entries.  Threads 0..63
+// fill 4 entries each.
+__device__ __forceinline__ void build_encode_table(uint32_t *table32, const Codebook4 &cb,
+                                                   uint32_t symbols, uint32_t entries = 16,
+                                                   uint32_t escape = 0x80u)
+{
+    const uint32_t t = threadIdx.x;
+    if (t < 64 && t * 4 < symbols) {
+        uint32_t word = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < 4; ++k) {
+            const uint32_t v = t * 4 + k;
+            uint32_t code = escape;
+#pragma unroll
+            for (uint32_t c = 0; c < 16; ++c)
+                if (c < entries && cb_entry(cb, c) == v) code = c;
+            word |= code << (8 * k);
+        }
+        table32[t] = word;
+    }
+}
+
+// Looks up four exponent bytes in the encode table.
+__device__ __forceinline__ uint32_t lookup4(const uint8_t *table, uint32_t e4)
+{
+    return (uint32_t)table[e4 & 0xFFu] | ((uint32_t)table[(e4 >> 8) & 0xFFu] << 8) |
+           ((uint32_t)table[(e4 >> 16) & 0xFFu] << 16) | ((uint32_t)table[e4 >> 24] << 24);
+}
+
+// Code bytes of 8 elements (two words of table output) -> one word of nibbles
+// (element 2k in the low nibble).  Byte 0 of (k | k >> 4) = code0 | code1 << 4.
+__device__ __forceinline__ uint32_t pack_codes8(uint32_t c_a, uint32_t c_b)
+{
+    const uint32_t k_a = c_a & 0x0F0F0F0Fu;
+    const uint32_t k_b = c_b & 0x0F0F0F0Fu;
+    return perm(k_b | (k_b >> 4), k_a | (k_a >> 4), 0x06040200u);
+}
+
+// Escape flags of 8 elements (bit 7 of each table byte) -> bit k = element k.
+// (x >> 7) holds the four flags at bits 0, 8, 16, 24; the multiply moves flag
+// k to bit 28 + k without carries.
+__device__ __forceinline__ uint32_t escape_mask8(uint32_t c_a, uint32_t c_b)
+{
+    const uint32_t lo = (((c_a & 0x80808080u) >> 7) * 0x10204080u) >> 28;
+    const uint32_t hi = (((c_b & 0x80808080u) >> 7) * 0x10204080u) >> 28;
+    return lo | (hi << 4);
+}
+
+// ---------------------------------------------------------------------------
+// BF16 encode of one 8-element chunk (16 bytes in).
+//   nib: 4 bytes of codes;  sm: 8 sign/mantissa bytes (sign << 7 | mantissa7)
+//   esc: escape mask (bit k = element k);  ex: exponent of element k in byte k
+// ---------------------------------------------------------------------------
+// Version 2 (Top-8) packing: 3-bit codes of 8 elements (table bytes c_a =
+// elements 0..3, c_b = 4..7) -> 24 bits, element k at bit 3k.
+__device__ __forceinline__ uint32_t pack_codes8_top8(uint32_t c_a, uint32_t c_b)
+{
+    const uint32_t t_a = c_a & 0x07070707u, t_b = c_b & 0x07070707u;
+    const uint32_t u_a = (t_a & 7u) | ((t_a >> 5) & 0x38u) | ((t_a >> 10) & 0x1C0u) | ((t_a >> 15) & 0xE00u);
+    const uint32_t u_b = (t_b & 7u) | ((t_b >> 5) & 0x38u) | ((t_b >> 10) & 0x1C0u) | ((t_b >> 15) & 0xE00u);
+    return u_a | (u_b << 12);
+}
+
+template <int V = 1>
+__device__ __forceinline__ void encode_chunk_bf16(const uint4 q, const uint8_t *table, uint32_t &nib,
+                                                  uint2 &sm, uint32_t &esc, uint64_t &ex)
+{
+    const uint32_t lo_a = perm(q.y, q.x, 0x06040200u);   // low bytes of elements 0..3
+    const uint32_t hi_a = perm(q.y, q.x, 0x07050301u);   // high bytes of elements 0..3
+    const uint32_t lo_b = perm(q.w, q.z, 0x06040200u);
+    const uint32_t hi_b = perm(q.w, q.z, 0x07050301u);
+    sm.x = (hi_a & 0x80808080u) | (lo_a & 0x7F7F7F7Fu);
+    sm.y = (hi_b & 0x80808080u) | (lo_b & 0x7F7F7F7Fu);
+    const uint32_t e_a = ((hi_a << 1) & 0xFEFEFEFEu) | ((lo_a >> 7) & 0x01010101u);
+    const uint32_t e_b = ((hi_b << 1) & 0xFEFEFEFEu) | ((lo_b >> 7) & 0x01010101u);
+    const uint32_t c_a = lookup4(table, e_a);
+    const uint32_t c_b = lookup4(table, e_b);
+    nib = V == 2 ? pack_codes8_top8(c_a, c_b) : pack_codes8(c_a, c_b);
+    esc = escape_mask8(c_a, c_b);
+    ex = (uint64_t)e_a | ((uint64_t)e_b << 32);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 E5M2 encode of one 32-element chunk (32 bytes in): 16 code bytes and
+// 12 sign/mantissa bytes (four 24-bit groups of eight 3-bit symbols).
+//   esc: escape mask (bit k = element k of the 32);  ex[s]: exponents of
+//   elements 8s..8s+7.
+// ---------------------------------------------------------------------------
+// Four 3-bit symbols held in bytes (bits 0-2 of each byte, the rest zero) ->
+// 12 contiguous bits.
+__device__ __forceinline__ uint32_t pack_sym3x4(uint32_t sym)
+{
+    const uint32_t u = sym | (sym >> 5);              // f0 | f1 << 3 at bit 0, f2 | f3 << 3 at bit 16
+    return (u & 0x3Fu) | ((u >> 10) & 0xFC0u);
+}
+
+__device__ __forceinline__ void encode_chunk_e5m2(const uint4 q0, const uint4 q1, const uint8_t *table,
+                                                  uint4 &nib, uint32_t sm3[3], uint32_t &esc, uint64_t ex[4])
+{
+    const uint32_t d[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    uint32_t nibw[4], grp[4];
+    esc = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t a = d[2 * s], b = d[2 * s + 1];
+        const uint32_t e_a = (a >> 2) & 0x1F1F1F1Fu;
+        const uint32_t e_b = (b >> 2) & 0x1F1F1F1Fu;
+        const uint32_t s_a = ((a >> 5) & 0x04040404u) | (a & 0x03030303u);
+        const uint32_t s_b = ((b >> 5) & 0x04040404u) | (b & 0x03030303u);
+        const uint32_t c_a = lookup4(table, e_a);
+        const uint32_t c_b = lookup4(table, e_b);
+        nibw[s] = pack_codes8(c_a, c_b);
+        esc |= escape_mask8(c_a, c_b) << (8 * s);
+        ex[s] = (uint64_t)e_a | ((uint64_t)e_b << 32);
+        grp[s] = pack_sym3x4(s_a) | (pack_sym3x4(s_b) << 12);
+    }
+    nib = make_uint4(nibw[0], nibw[1], nibw[2], nibw[3]);
+    sm3[0] = grp[0] | (grp[1] << 24);
+    sm3[1] = (grp[1] >> 8) | (grp[2] << 16);
+    sm3[2] = (grp[2] >> 16) | (grp[3] << 8);
+}
+
+// E5M2 encode through a code-pair table: table16[e0 | e1 << 5] holds, for
+// two neighbouring elements with exponents e0 and e1, their two codes as one
+// code byte (low byte: code0 | code1 << 4, escapes coded 0) and their escape
+// flags (high byte: bit 0 = element 0, bit 1 = element 1).  One LDS read per
+// two elements replaces two reads, the nibble packing and the escape-mask
+// arithmetic of the byte table.
+__device__ __forceinline__ void build_pair_table(uint32_t *table16x2, const uint8_t *tab8)
+{
+    // thread t fills entries 4t .. 4t+3 (two words); e1 is the same for all four
+    const uint32_t t = threadIdx.x;
+    if (t < 256) {
+        const uint32_t c1 = tab8[t >> 3];
+        const uint32_t hi = ((c1 & 0xFu) << 4) | ((c1 >> 7) << 9);
+        uint32_t e[4];
+#pragma unroll
+        for (uint32_t k = 0; k < 4; ++k) {
+            const uint32_t c0 = tab8[(4 * t + k) & 31u];
+            e[k] = (c0 & 0xFu) | ((c0 >> 7) << 8) | hi;
+        }
+        table16x2[2 * t] = e[0] | (e[1] << 16);
+        table16x2[2 * t + 1] = e[2] | (e[3] << 16);
+    }
+}
+
+// One 32-element chunk: 16 code bytes, 12 sign/mantissa bytes, and per group
+// of 8 elements a flag word fl[s] whose byte k holds the escape flags of
+// elements 2k (bit 0) and 2k + 1 (bit 1) of the group.
+__device__ __forceinline__ void encode_chunk_e5m2_pairs(const uint4 q0, const uint4 q1, const uint16_t *table16,
+                                                        uint4 &nib, uint32_t sm3[3], uint32_t fl[4])
+{
+    const uint32_t d[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    uint32_t nibw[4], grp[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t a = d[2 * s], b = d[2 * s + 1];
+        // pair index e0 | e1 << 5 of elements (0,1) and (2,3) of a word
+        const uint32_t p0 = table16[((a >> 2) & 0x1Fu) | ((a >> 5) & 0x3E0u)];
+        const uint32_t p1 = table16[((a >> 18) & 0x1Fu) | ((a >> 21) & 0x3E0u)];
+        const uint32_t p2 = table16[((b >> 2) & 0x1Fu) | ((b >> 5) & 0x3E0u)];
+        const uint32_t p3 = table16[((b >> 18) & 0x1Fu) | ((b >> 21) & 0x3E0u)];
+        const uint32_t lo = perm(p1, p0, 0x0C0C0400u), hi = perm(p3, p2, 0x04000C0Cu);
+        nibw[s] = lo | hi;
+        fl[s] = perm(p1, p0, 0x0C0C0501u) | perm(p3, p2, 0x05010C0Cu);
+        const uint32_t s_a = ((a >> 5) & 0x04040404u) | (a & 0x03030303u);
+        const uint32_t s_b = ((b >> 5) & 0x04040404u) | (b & 0x03030303u);
+        grp[s] = pack_sym3x4(s_a) | (pack_sym3x4(s_b) << 12);
+    }
+    nib = make_uint4(nibw[0], nibw[1], nibw[2], nibw[3]);
+    sm3[0] = grp[0] | (grp[1] << 24);
+    sm3[1] = (grp[1] >> 8) | (grp[2] << 16);
+    sm3[2] = (grp[2] >> 16) | (grp[3] << 8);
+}
+
+// Flag word of a group (byte k = flags of elements 2k, 2k+1) -> 8-bit mask.
+__device__ __forceinline__ uint32_t flags_to_mask8(uint32_t f)
+{
+    return (f & 3u) | ((f >> 6) & 0xCu) | ((f >> 12) & 0x30u) | ((f >> 18) & 0xC0u);
+}
+
+// Flag bits of the first v elements of a group (v in 0..8).
+__device__ __forceinline__ uint32_t group_flag_keep(int v)
+{
+    uint32_t m = 0;
+    for (int i = 0; i < 8; ++i)
+        if (i < v) m |= 1u << ((i / 2) * 8 + (i & 1));
+    return m;
+}
+
+// ---------------------------------------------------------------------------
+// Escape staging.  Inside a wave the records of a tile come in element order:
+// (chunk j, lane, element).  A "segment" is 512 consecutive elements of a
+// row (BF16: chunk j of all 64 lanes; E5M2: chunk j of 16 lanes), so it holds
+// at most 512 records.  Each lane writes its records of the segment into the
+// wave's LDS buffer, shifted by the byte misalignment of the segment's
+// destination, and the wave then copies the buffer to the tile's staging
+// slot with aligned dword stores; the dwords at both ends, which neighbouring
+// segments (possibly of another wave) share, are written byte by byte.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSegElems = 512;
+constexpr uint32_t kSegBytes = 3 * kSegElems + 8;          // + alignment shift, rounded to dwords
+
+// Appends the records of 8 elements (escape mask esc, exponents ex,
+// block-local position of the first element pos0) to an LDS buffer at byte
+// `off`; returns the byte after them.
+__device__ __forceinline__ uint32_t lds_put_records(uint8_t *buf, uint32_t off, uint32_t esc, uint64_t ex,
+                                                    uint32_t pos0)
+{
+    while (esc) {
+        const uint32_t k = (uint32_t)__builtin_ctz(esc);
+        esc &= esc - 1;
+        const uint32_t pos = (pos0 + k) & 0xFFFFu;
+        buf[off] = (uint8_t)pos;
+        buf[off + 1] = (uint8_t)(pos >> 8);
+        buf[off + 2] = (uint8_t)(ex >> (8 * k));
+        off += 3;
+    }
+    return off;
+}
+
+__device__ __forceinline__ void wave_lds_fence()
+{
+    // LDS operations of one wave complete in order; this only keeps the
+    // compiler from moving LDS accesses across the hand-over point
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Copies `len` bytes, held in buf[g0 & 3, (g0 & 3) + len), to dst[g0, g0 + len).
+__device__ __forceinline__ void flush_segment(const uint8_t *buf, uint8_t *dst, uint32_t g0, uint32_t len)
+{
+    const uint32_t lane = lane_id();
+    const uint32_t first_dw = g0 >> 2;
+    const uint32_t end = g0 + len;
+    const uint32_t last_dw = (end - 1) >> 2;
+    const uint32_t head = g0 & 3;
+    const uint32_t tail = ((end - 1) & 3) + 1;
+    for (uint32_t i = lane; i <= last_dw - first_dw; i += 64) {
+        const uint32_t w = reinterpret_cast<const uint32_t *>(buf)[i];
+        const uint32_t lo = (i == 0) ? head : 0;
+        const uint32_t hi = (first_dw + i == last_dw) ? tail : 4;
+        uint8_t *d = dst + 4ull * (first_dw + i);
+        if (lo == 0 && hi == 4) {
+            *reinterpret_cast<uint32_t *>(d) = w;
+        } else {
+            for (uint32_t b = lo; b < hi; ++b) d[b] = (uint8_t)(w >> (8 * b));
+        }
+    }
+}
+
+// Writes the escape records of 8 elements (escape mask esc, exponents ex,
+// first block-local position pos0) straight into the staging area,
+// ascending, from rank `rank` on.  Used for rows with few escapes.
+__device__ __forceinline__ void put_records(uint8_t *tstage, uint32_t rank, uint32_t esc, uint64_t ex,
+                                            uint32_t pos0)
+{
+    while (esc) {
+        const uint32_t k = (uint32_t)__builtin_ctz(esc);
+        esc &= esc - 1;
+        const uint32_t pos = (pos0 + k) & 0xFFFFu;
+        uint8_t *r = tstage + 3ull * rank;
+        r[0] = (uint8_t)pos;
+        r[1] = (uint8_t)(pos >> 8);
+        r[2] = (uint8_t)(ex >> (8 * k));
+        ++rank;
+    }
+}
+
+// Rows with more escapes than this go through the LDS segment buffer.
+constexpr uint32_t kDirectRecords = 32;
+// Tiles with more escapes than this are not staged: the compaction kernel
+// derives their records again from the input, which moves 2 bytes per
+// element instead of writing and re-reading 3 bytes per escape.  Their tile
+// count carries kRederiveFlag.
+constexpr uint32_t kRederiveRecords = kEncTile / 4;
+constexpr uint32_t kRederiveFlag = 0x80000000u;
+
+// ---------------------------------------------------------------------------
+// Kernel: BF16 dense encode + escape staging.  One 256-lane workgroup per
+// 16K-element tile; wave w streams elements [4096w, 4096w + 4096) of it.  The
+// tile's records are staged in element order in the tile's slot (3 bytes per
+// element); tile_counts[tile] gets their number.  A tile with more than
+// kRederiveRecords escapes stages nothing and is flagged with kRederiveFlag:
+// the compaction kernel derives its records again from the input, which
+// costs less traffic than writing and re-reading them.
+// ---------------------------------------------------------------------------
+
+// Version 3 staging: the exponent bytes of the escaped elements of 8
+// elements, into an LDS buffer at `off` (returns the byte after them) or
+// straight into the staging slot at item `rank`.
+__device__ __forceinline__ uint32_t lds_put_exponents(uint8_t *buf, uint32_t off, uint32_t esc, uint64_t ex)
+{
+    while (esc) {
+        const uint32_t k = (uint32_t)__builtin_ctz(esc);
+        esc &= esc - 1;
+        buf[off++] = (uint8_t)(ex >> (8 * k));
+    }
+    return off;
+}
+
+__device__ __forceinline__ void put_exponents(uint8_t *tstage, uint32_t rank, uint32_t esc, uint64_t ex)
+{
+    while (esc) {
+        const uint32_t k = (uint32_t)__builtin_ctz(esc);
+        esc &= esc - 1;
+        tstage[rank++] = (uint8_t)(ex >> (8 * k));
+    }
+}
+
+template <int V>
+__global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t *__restrict__ in, uint64_t n,
+                                                              uint8_t *__restrict__ out, uint64_t off_nib,
+                                                              uint64_t off_sm, Codebook4 cb,
+                                                              const uint32_t *__restrict__ cb_dev,
+                                                              uint32_t *__restrict__ tile_counts,
+                                                              uint8_t *__restrict__ stage)
+{
+    __shared__ uint32_t table32[64];
+    __shared__ uint32_t wave_totals[kEncThreads / 64];
+    __shared__ __align__(16) uint8_t seg_buf[kEncThreads / 64][kSegBytes];
+    // exponents of chunks that hold escapes, parked until the ranks are known
+    __shared__ uint64_t ex_park[kEncThreads / 64][kBf16Chunks][64];
+    const uint32_t lane = lane_id();
+    const uint32_t wave = threadIdx.x / 64;
+    const uint64_t tile = blockIdx.x;
+    const uint64_t base = tile * kEncTile + (uint64_t)wave * kRow;
+    const bool full_row = base + kRow <= n;
+
+    // the row's loads are issued first and stay in flight while the table is built
+    uint4 q[kBf16Chunks];
+#pragma unroll
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+        if (full_row || c0 + 8 <= n) {
+            q[j] = load_nt(reinterpret_cast<const uint4 *>(in + c0));
+        } else {
+            uint16_t v[8];
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) v[k] = (c0 + k < n) ? in[c0 + k] : 0;
+            q[j] = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                              v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
+        }
+    }
+    if (cb_dev) cb = load_codebook(cb_dev);
+    build_encode_table(table32, cb, 256, book_entries(V), V == kTop15S ? 0x8Fu : 0x80u);
+    __syncthreads();
+    const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
+    uint8_t *buf = seg_buf[wave];
+    uint32_t esc[kBf16Chunks];
+    uint32_t cnt[kBf16Chunks];
+#pragma unroll
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+        uint32_t nib;
+        uint2 sm;
+        uint64_t ex;
+        encode_chunk_bf16<V>(q[j], table, nib, sm, esc[j], ex);
+        if (esc[j]) ex_park[wave][j][lane] = ex;
+        if (full_row || c0 + 8 <= n) {
+            if (V != kTop8) store_nt(reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2), nib);
+            store_nt(reinterpret_cast<uint2 *>(out + off_sm + c0), sm);
+        } else if (c0 < n) {
+            // last, partial chunk: missing elements get code 0, sign/mantissa 0
+            // and no escape; the bytes past the data are section padding
+            const uint32_t valid = (uint32_t)(n - c0);
+            const uint64_t keep = (1ull << (8 * valid)) - 1;
+            esc[j] &= (1u << valid) - 1;
+            nib &= (uint32_t)((1ull << ((V == kTop8 ? 3 : 4) * valid)) - 1);
+            const uint64_t smv = ((uint64_t)sm.y << 32 | sm.x) & keep;
+            if (V != kTop8) *reinterpret_cast<uint32_t *>(out + off_nib + c0 / 2) = nib;
+            *reinterpret_cast<uint2 *>(out + off_sm + c0) = make_uint2((uint32_t)smv, (uint32_t)(smv >> 32));
+        } else {
+            esc[j] = 0;
+            nib = 0;
+        }
+        if (V == kTop8) {
+            // 3 code bytes per chunk: the wave's row of codes (1536 bytes) is
+            // assembled in LDS and stored as whole dwords below
+            const uint32_t o = j * 192 + 3 * lane;
+            buf[o] = (uint8_t)nib;
+            buf[o + 1] = (uint8_t)(nib >> 8);
+            buf[o + 2] = (uint8_t)(nib >> 16);
+        }
+        cnt[j] = __popc(esc[j]);
+    }
+    if (V == kTop8) {
+        // the row's code bytes start at 3 * base / 8, a multiple of 1536;
+        // dwords past the section's last byte hold only padding and are skipped
+        wave_lds_fence();
+        const uint64_t row0 = 3 * (base / 8);
+        const uint64_t code_bytes = 3 * ((n + 7) / 8);
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const uint32_t d = i * 64 + lane;
+            if (row0 + 4 * d < code_bytes)
+                *reinterpret_cast<uint32_t *>(out + off_nib + row0 + 4 * d) = reinterpret_cast<const uint32_t *>(buf)[d];
+        }
+        wave_lds_fence();
+    }
+    uint32_t row_base[kBf16Chunks], row_total[kBf16Chunks], lane_before[kBf16Chunks];
+    const uint32_t wave_total = wave_chunk_ranks<kBf16Chunks>(cnt, row_base, row_total, lane_before);
+    uint32_t tile_total;
+    const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
+    // only the Top-16 format re-derives escape-heavy tiles in the compaction
+    const bool rederive = V == kTop16 && tile_total > kRederiveRecords;
+    if (wave_total && !rederive) {
+        uint8_t *tstage = stage + tile * (3ull * kEncTile);
+#pragma unroll
+        for (int j = 0; j < kBf16Chunks; ++j) {
+            const uint32_t pos0 = (uint32_t)((base + (uint64_t)(j * 64 + lane) * 8) & 0xFFFFu);
+            const uint32_t rank = wave_before + row_base[j];
+            constexpr uint32_t item = escape_item_bytes(V);
+            if (row_total[j] <= kDirectRecords) {                      // wave-uniform
+                if (esc[j]) {
+                    if (V == kTop15S) put_exponents(tstage, rank + lane_before[j], esc[j], ex_park[wave][j][lane]);
+                    else put_records(tstage, rank + lane_before[j], esc[j], ex_park[wave][j][lane], pos0);
+                }
+            } else {
+                const uint32_t g0 = item * rank;
+                if (esc[j]) {
+                    if (V == kTop15S)
+                        lds_put_exponents(buf, (g0 & 3) + lane_before[j], esc[j], ex_park[wave][j][lane]);
+                    else
+                        lds_put_records(buf, (g0 & 3) + 3 * lane_before[j], esc[j], ex_park[wave][j][lane], pos0);
+                }
+                wave_lds_fence();
+                flush_segment(buf, tstage, g0, item * row_total[j]);
+                wave_lds_fence();
+            }
+        }
+    }
+    if (threadIdx.x == 0) tile_counts[tile] = tile_total | (rederive ? kRederiveFlag : 0u);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: FP8 E5M2 dense encode + escape staging (the page's FP8 extension,
+// Contributions item 4).  Same tiling as BF16; a lane holds two 32-element
+// chunks of its wave's row.  A chunk row with many escapes is staged through
+// LDS as four segments of 16 lanes.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *__restrict__ in, uint64_t n,
+                                                              uint8_t *__restrict__ out, uint64_t off_nib,
+                                                              uint64_t off_sm, uint64_t sm_bytes,
+                                                              Codebook4 cb,
+                                                              const uint32_t *__restrict__ cb_dev,
+                                                              uint32_t *__restrict__ tile_counts,
+                                                              uint8_t *__restrict__ stage)
+{
+    __shared__ uint32_t table32[64];
+    __shared__ uint32_t table16x2[512];
+    __shared__ uint32_t wave_totals[kEncThreads / 64];
+    __shared__ __align__(16) uint8_t seg_buf[kEncThreads / 64][kSegBytes];
+    const uint32_t lane = lane_id();
+    const uint32_t wave = threadIdx.x / 64;
+    const uint64_t tile = blockIdx.x;
+    const uint64_t base = tile * kEncTile + (uint64_t)wave * kRow;
+    const bool full_row = base + kRow <= n;
+
+    uint4 q[kE5Chunks][2];
+#pragma unroll
+    for (int j = 0; j < kE5Chunks; ++j) {
+        const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+        if (full_row || c0 + 32 <= n) {
+            q[j][0] = load_nt(reinterpret_cast<const uint4 *>(in + c0));
+            q[j][1] = load_nt(reinterpret_cast<const uint4 *>(in + c0 + 16));
+        } else {
+            uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (uint32_t k = 0; k < 32 && c0 + k < n; ++k) w[k / 4] |= (uint32_t)in[c0 + k] << (8 * (k & 3));
+            q[j][0] = make_uint4(w[0], w[1], w[2], w[3]);
+            q[j][1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+    }
+    if (cb_dev) cb = load_codebook(cb_dev);
+    build_encode_table(table32, cb, 32);
+    __syncthreads();
+    build_pair_table(table16x2, reinterpret_cast<const uint8_t *>(table32));
+    __syncthreads();
+    const uint16_t *table16 = reinterpret_cast<const uint16_t *>(table16x2);
+    uint32_t fl[kE5Chunks][4];
+    uint32_t cnt[kE5Chunks];
+#pragma unroll
+    for (int j = 0; j < kE5Chunks; ++j) {
+        const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+        uint4 nib;
+        uint32_t sm3[3];
+        encode_chunk_e5m2_pairs(q[j][0], q[j][1], table16, nib, sm3, fl[j]);
+        uint32_t *sm_dst = reinterpret_cast<uint32_t *>(out + off_sm + (c0 / 32) * 12);
+        if (full_row || c0 + 32 <= n) {
+            store_nt(reinterpret_cast<uint4 *>(out + off_nib + c0 / 2), nib);
+            store3_nt(sm_dst, sm3);
+        } else if (c0 < n) {
+            // last, partial chunk: missing elements get code 0, symbol 0 and
+            // no escape; only the sign/mantissa bytes that hold data are stored
+            const uint32_t valid = (uint32_t)(n - c0);
+            uint32_t nw[4] = {nib.x, nib.y, nib.z, nib.w};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int v = (int)valid - 8 * s;
+                nw[s] &= v >= 8 ? 0xFFFFFFFFu : (v <= 0 ? 0u : (uint32_t)((1ull << (4 * v)) - 1));
+                fl[j][s] &= group_flag_keep(v);
+            }
+            *reinterpret_cast<uint4 *>(out + off_nib + c0 / 2) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+            uint32_t sw[3] = {sm3[0], sm3[1], sm3[2]};
+            const uint32_t bits = 3 * valid;
+#pragma unroll
+            for (int w = 0; w < 3; ++w) {
+                const int b = (int)bits - 32 * w;
+                sw[w] &= b >= 32 ? 0xFFFFFFFFu : (b <= 0 ? 0u : ((1u << b) - 1));
+            }
+            const uint64_t sm_start = off_sm + (c0 / 32) * 12;
+            const uint64_t sm_end = off_sm + sm_bytes;
+            for (uint32_t i = 0; i < 12 && sm_start + i < sm_end; ++i)
+                out[sm_start + i] = (uint8_t)(sw[i / 4] >> (8 * (i & 3)));
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) fl[j][s] = 0;
+        }
+        cnt[j] = __popc(fl[j][0]) + __popc(fl[j][1]) + __popc(fl[j][2]) + __popc(fl[j][3]);
+    }
+    uint32_t row_base[kE5Chunks], row_total[kE5Chunks], lane_before[kE5Chunks];
+    const uint32_t wave_total = wave_chunk_ranks<kE5Chunks>(cnt, row_base, row_total, lane_before);
+    uint32_t tile_total;
+    const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
+    if (wave_total && tile_total <= kRederiveRecords) {
+        uint8_t *tstage = stage + tile * (3ull * kEncTile);
+        uint8_t *buf = seg_buf[wave];
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+            const uint32_t rank = wave_before + row_base[j];
+            // escape masks and exponents of the chunk, from its flag words and input words
+            const uint32_t dw[8] = {q[j][0].x, q[j][0].y, q[j][0].z, q[j][0].w,
+                                    q[j][1].x, q[j][1].y, q[j][1].z, q[j][1].w};
+            uint32_t esc8[4];
+            uint64_t ex[4];
+#pragma unroll
+            for (int s8 = 0; s8 < 4; ++s8) {
+                esc8[s8] = flags_to_mask8(fl[j][s8]);
+                ex[s8] = (uint64_t)((dw[2 * s8] >> 2) & 0x1F1F1F1Fu) |
+                         ((uint64_t)((dw[2 * s8 + 1] >> 2) & 0x1F1F1F1Fu) << 32);
+            }
+            if (row_total[j] <= kDirectRecords) {                      // wave-uniform
+                if (cnt[j]) {
+                    uint32_t r = rank + lane_before[j];
+#pragma unroll
+                    for (int s8 = 0; s8 < 4; ++s8) {
+                        put_records(tstage, r, esc8[s8], ex[s8], (uint32_t)((c0 + 8 * s8) & 0xFFFFu));
+                        r += __popc(esc8[s8]);
+                    }
+                }
+                continue;
+            }
+            // four segments of 16 lanes x 32 elements
+#pragma unroll
+            for (uint32_t q4 = 0; q4 < 4; ++q4) {
+                const uint32_t seg_first = __builtin_amdgcn_readlane(lane_before[j], 16 * q4);
+                const uint32_t seg_end =
+                    q4 < 3 ? (uint32_t)__builtin_amdgcn_readlane(lane_before[j], 16 * (q4 + 1)) : row_total[j];
+                if (seg_end == seg_first) continue;                    // wave-uniform
+                const uint32_t g0 = 3 * (rank + seg_first);
+                if (lane / 16 == q4 && cnt[j]) {
+                    uint32_t off = (g0 & 3) + 3 * (lane_before[j] - seg_first);
+#pragma unroll
+                    for (int s8 = 0; s8 < 4; ++s8)
+                        off = lds_put_records(buf, off, esc8[s8], ex[s8], (uint32_t)((c0 + 8 * s8) & 0xFFFFu));
+                }
+                wave_lds_fence();
+                flush_segment(buf, tstage, g0, 3 * (seg_end - seg_first));
+                wave_lds_fence();
+            }
+        }
+    }
+    if (threadIdx.x == 0) tile_counts[tile] = tile_total | (tile_total > kRederiveRecords ? kRederiveFlag : 0u);
+}
+
+struct HeaderArgs {
+    uint64_t n, nb;
+    uint32_t dtype, version;
+    Codebook4 cb;
+    uint64_t pad_start[3], pad_end[3];
+};
+
+// A device codebook (sz_codebook in device memory) replaces `cb` and is
+// checked: its dtype word, entries below the symbol count, no repeats.
+// Returns 0 or the error code; called by every thread of the workgroup.
+__device__ __forceinline__ int32_t device_codebook_verdict(const uint32_t *__restrict__ cb_dev, uint32_t dtype,
+                                                           Codebook4 &cb)
+{
+    if (!cb_dev) return 0;
+    cb = load_codebook(cb_dev);
+    const uint32_t symbols = dtype == SZ_BF16 ? 256u : 32u;
+    bool bad = false;
+    if (threadIdx.x < 16) {
+        const uint32_t e = cb_entry(cb, threadIdx.x);
+        bad = e >= symbols;
+        for (uint32_t d = 0; d < threadIdx.x; ++d) bad = bad || cb_entry(cb, d) == e;
+    }
+    int32_t verdict = __syncthreads_or(bad) ? SZ_E_ARG : 0;
+    if (cb_dev[0] != dtype) verdict = SZ_E_DTYPE;
+    return verdict;
+}
+
+// Writes the stream header (16 little-endian words; E, words 4 and 5, only
+// when write_e, as 0), the zero padding between sections and the status
+// word.  A bad device codebook (verdict != 0) zeroes the magic, so the
+// stream cannot be decoded.  Threads 0..255 of the workgroup take part.
+__device__ __forceinline__ void write_header(uint8_t *__restrict__ out, const HeaderArgs &h, const Codebook4 &cb,
+                                             int32_t verdict, bool write_e, int32_t *__restrict__ status)
+{
+    const uint32_t tid = threadIdx.x;
+    if (tid < 16 && (write_e || (tid != 4 && tid != 5))) {
+        uint32_t w = 0;
+        switch (tid) {
+        case 0: w = verdict ? 0u : kMagic; break;
+        case 1: w = h.version | (h.dtype << 16) | (kLog2Block << 24); break;
+        case 2: w = (uint32_t)h.n; break;
+        case 3: w = (uint32_t)(h.n >> 32); break;
+        case 6: w = (uint32_t)h.nb; break;
+        case 8: w = cb.w[0]; break;
+        case 9: w = cb.w[1]; break;
+        case 10: w = cb.w[2]; break;
+        case 11: w = cb.w[3]; break;
+        default: w = 0; break;
+        }
+        reinterpret_cast<uint32_t *>(out)[tid] = w;
+    }
+    if (tid == 0) status[0] = verdict;
+    // zero padding between sections (each range is shorter than 256 bytes)
+    if (tid < 256) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const uint64_t a = h.pad_start[r] + tid;
+            if (a < h.pad_end[r]) out[a] = 0;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: encode scan.  One workgroup turns the tile escape counts into the
+// per-block escape counts of the stream and the exclusive escape offset of
+// every block, then writes the header (with E) and the zero padding between
+// sections.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__restrict__ tile_counts,
+                                                            uint32_t nt,
+                                                            uint64_t *__restrict__ block_offsets,
+                                                            uint8_t *__restrict__ out, HeaderArgs h,
+                                                            const uint32_t *__restrict__ cb_dev,
+                                                            int32_t *__restrict__ status)
+{
+    __shared__ ScanLds lds;
+    const uint32_t tid = threadIdx.x;
+    // a bad device codebook zeroes the magic and sets the status word
+    Codebook4 cb = h.cb;
+    const int32_t verdict = device_codebook_verdict(cb_dev, h.dtype, cb);
+    const uint32_t nb = (uint32_t)h.nb;
+    if (tid == 0) lds.carry = 0;
+    uint32_t *block_counts = reinterpret_cast<uint32_t *>(out + 64);
+    for (uint32_t b0 = 0; b0 < nb; b0 += kScanBatch * kScanThreads) {
+        uint32_t x[kScanBatch];
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+            const uint32_t b = b0 + i * kScanThreads + tid;
+            x[i] = 0;
+            if (b < nb) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b);
+                const uint32_t t = kTilesPerBlock * b;
+                const uint32_t m = ~kRederiveFlag;
+                x[i] = (v.x & m) + ((t + 1 < nt) ? v.y & m : 0) + ((t + 2 < nt) ? v.z & m : 0) +
+                       ((t + 3 < nt) ? v.w & m : 0);
+            }
+        }
+        uint64_t base[kScanBatch];
+        scan_batch(x, base, lds);
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+            const uint32_t b = b0 + i * kScanThreads + tid;
+            if (b < nb) {
+                block_counts[b] = x[i];
+                block_offsets[b] = base[i];
+            }
+        }
+    }
+    const uint64_t total = lds.carry;
+    write_header(out, h, cb, verdict, false, status);
+    if (tid == 0) {
+        reinterpret_cast<uint32_t *>(out)[4] = (uint32_t)total;
+        reinterpret_cast<uint32_t *>(out)[5] = (uint32_t)(total >> 32);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: escape compaction.  One wave per block (four blocks per workgroup)
+// copies the staged records of the block's four tiles (3 bytes each) to
+// out[off_esc + 3 * offset ...), tile after tile; when no tile of the block
+// holds more than kGroupCopyRecords records, four 16-lane groups copy the four
+// tiles at once.  The body of each copy is written with 16-byte aligned
+// dwordx4 stores assembled by v_alignbyte_b32 from five staged words; the
+// unaligned bytes at both ends, whose dwords the neighbouring tiles share, are
+// written byte by byte.  Flagged (escape-heavy) tiles are re-encoded from the
+// input instead and their records written straight to their final place.
+// ---------------------------------------------------------------------------
+// Copies len bytes of staged records to out[dst0, dst0 + len) with the lanes
+// [0, width) of a lane group (lane = index inside the group).
+__device__ __forceinline__ void copy_records(const uint8_t *__restrict__ src, uint8_t *__restrict__ out,
+                                             uint64_t dst0, uint32_t len, uint32_t lane, uint32_t width)
+{
+    const uint64_t end = dst0 + len;
+    const uint64_t body_begin = std::min<uint64_t>((dst0 + 15) & ~uint64_t(15), end);
+    const uint64_t body_end = std::max<uint64_t>(end & ~uint64_t(15), body_begin);
+    const uint32_t head = (uint32_t)(body_begin - dst0);
+    for (uint32_t i = lane; i < head; i += width) out[dst0 + i] = src[i];
+    const uint32_t *src32 = reinterpret_cast<const uint32_t *>(src);
+    const uint32_t chunks = (uint32_t)((body_end - body_begin) / 16);
+    const uint32_t sh = head & 3;
+#pragma unroll 4
+    for (uint32_t c = lane; c < chunks; c += width) {
+        const uint32_t w0 = (head >> 2) + 4 * c;                 // first source word
+        const uint32_t a0 = src32[w0], a1 = src32[w0 + 1], a2 = src32[w0 + 2], a3 = src32[w0 + 3],
+                       a4 = src32[w0 + 4];
+        const uint4 v = make_uint4(__builtin_amdgcn_alignbyte(a1, a0, sh), __builtin_amdgcn_alignbyte(a2, a1, sh),
+                                   __builtin_amdgcn_alignbyte(a3, a2, sh), __builtin_amdgcn_alignbyte(a4, a3, sh));
+        *reinterpret_cast<uint4 *>(out + body_begin + 16ull * c) = v;
+    }
+    const uint32_t tail_src = (uint32_t)(body_end - dst0);
+    for (uint32_t i = lane; body_end + i < end; i += width) out[body_end + i] = src[tail_src + i];
+}
+
+// Derives the records of an escape-heavy tile again from the input, with one
+// wave walking the tile's four rows, and writes them at their final place
+// (dst = aligned base, shift = byte misalignment of the tile's first record).
+// Half rows keep the re-derivation's register footprint close to the copy
+// path's, so both share one occupancy.
+constexpr int kRedChunks = 4;
+constexpr uint32_t kRedRow = kRedChunks * 64 * 8;
+
+__device__ __forceinline__ void rederive_tile_bf16(const uint16_t *__restrict__ in, uint64_t n, uint64_t tile,
+                                                   const uint8_t *table, uint8_t *buf, uint8_t *dst, uint32_t shift)
+{
+    const uint32_t lane = lane_id();
+    uint32_t rank = 0;                                          // wave-uniform
+    for (uint32_t row = 0; row < kEncTile / kRedRow; ++row) {
+        const uint64_t base = tile * kEncTile + (uint64_t)row * kRedRow;
+        if (base >= n) break;
+        const bool full_row = base + kRedRow <= n;
+        uint4 q[kRedChunks];
+#pragma unroll
+        for (int j = 0; j < kRedChunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+            if (full_row || c0 + 8 <= n) {
+                q[j] = load_nt(reinterpret_cast<const uint4 *>(in + c0));
+            } else {
+                uint16_t v[8];
+#pragma unroll
+                for (uint32_t k = 0; k < 8; ++k) v[k] = (c0 + k < n) ? in[c0 + k] : 0;
+                q[j] = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                                  v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
+            }
+        }
+        uint32_t esc[kRedChunks], cnt[kRedChunks];
+        uint64_t ex[kRedChunks];
+#pragma unroll
+        for (int j = 0; j < kRedChunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+            uint32_t nib;
+            uint2 sm;
+            encode_chunk_bf16(q[j], table, nib, sm, esc[j], ex[j]);
+            if (c0 >= n) esc[j] = 0;
+            else if (c0 + 8 > n) esc[j] &= (1u << (uint32_t)(n - c0)) - 1;
+            cnt[j] = __popc(esc[j]);
+        }
+        uint32_t row_base[kRedChunks], row_total[kRedChunks], lane_before[kRedChunks];
+        const uint32_t total = wave_chunk_ranks<kRedChunks>(cnt, row_base, row_total, lane_before);
+#pragma unroll
+        for (int j = 0; j < kRedChunks; ++j) {
+            if (row_total[j] == 0) continue;                    // wave-uniform
+            const uint32_t g0 = shift + 3 * (rank + row_base[j]);
+            const uint32_t pos0 = (uint32_t)((base + (uint64_t)(j * 64 + lane) * 8) & 0xFFFFu);
+            if (esc[j]) lds_put_records(buf, (g0 & 3) + 3 * lane_before[j], esc[j], ex[j], pos0);
+            wave_lds_fence();
+            flush_segment(buf, dst, g0, 3 * row_total[j]);
+            wave_lds_fence();
+        }
+        rank += total;
+    }
+}
+
+__device__ __forceinline__ void rederive_tile_e5m2(const uint8_t *__restrict__ in, uint64_t n, uint64_t tile,
+                                                   const uint8_t *table, uint8_t *buf, uint8_t *dst, uint32_t shift)
+{
+    const uint32_t lane = lane_id();
+    uint32_t rank = 0;                                          // wave-uniform
+    for (uint32_t row = 0; row < kEncTile / kRow; ++row) {
+        const uint64_t base = tile * kEncTile + (uint64_t)row * kRow;
+        if (base >= n) break;
+        const bool full_row = base + kRow <= n;
+        uint4 q[kE5Chunks][2];
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+            if (full_row || c0 + 32 <= n) {
+                q[j][0] = load_nt(reinterpret_cast<const uint4 *>(in + c0));
+                q[j][1] = load_nt(reinterpret_cast<const uint4 *>(in + c0 + 16));
+            } else {
+                uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                for (uint32_t k = 0; k < 32 && c0 + k < n; ++k) w[k / 4] |= (uint32_t)in[c0 + k] << (8 * (k & 3));
+                q[j][0] = make_uint4(w[0], w[1], w[2], w[3]);
+                q[j][1] = make_uint4(w[4], w[5], w[6], w[7]);
+            }
+        }
+        uint32_t esc[kE5Chunks], cnt[kE5Chunks];
+        uint64_t ex[kE5Chunks][4];
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+            uint4 nib;
+            uint32_t sm3[3];
+            encode_chunk_e5m2(q[j][0], q[j][1], table, nib, sm3, esc[j], ex[j]);
+            if (c0 >= n) esc[j] = 0;
+            else if (c0 + 32 > n) esc[j] &= (uint32_t)((1ull << (n - c0)) - 1);
+            cnt[j] = __popc(esc[j]);
+        }
+        uint32_t row_base[kE5Chunks], row_total[kE5Chunks], lane_before[kE5Chunks];
+        const uint32_t total = wave_chunk_ranks<kE5Chunks>(cnt, row_base, row_total, lane_before);
+#pragma unroll
+        for (int j = 0; j < kE5Chunks; ++j) {
+            if (row_total[j] == 0) continue;                    // wave-uniform
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
+#pragma unroll
+            for (uint32_t q4 = 0; q4 < 4; ++q4) {
+                const uint32_t seg_first = __builtin_amdgcn_readlane(lane_before[j], 16 * q4);
+                const uint32_t seg_end =
+                    q4 < 3 ? (uint32_t)__builtin_amdgcn_readlane(lane_before[j], 16 * (q4 + 1)) : row_total[j];
+                if (seg_end == seg_first) continue;             // wave-uniform
+                const uint32_t g0 = shift + 3 * (rank + row_base[j] + seg_first);
+                if (lane / 16 == q4 && cnt[j]) {
+                    uint32_t off = (g0 & 3) + 3 * (lane_before[j] - seg_first);
+#pragma unroll
+                    for (int s8 = 0; s8 < 4; ++s8)
+                        off = lds_put_records(buf, off, (esc[j] >> (8 * s8)) & 0xFFu, ex[j][s8],
+                                              (uint32_t)((c0 + 8 * s8) & 0xFFFFu));
+                }
+                wave_lds_fence();
+                flush_segment(buf, dst, g0, 3 * (seg_end - seg_first));
+                wave_lds_fence();
+            }
+        }
+        rank += total;
+    }
+}
+
+// Tiles with at most this many records are copied by 16-lane groups, the
+// block's four tiles at once; heavier blocks copy tile after tile with the
+// whole wave.
+constexpr uint32_t kGroupCopyRecords = 1024;
+
+// Moves the records of block b to their place in the stream with one wave.
+// Lanes 0..3 of `meta` hold the block's four tile counts (flag bit
+// included; 0 past the last tile); `off` is the escape offset of the block's
+// first record.
+template <int DT>
+__device__ __forceinline__ void compact_block(const uint8_t *__restrict__ stage, uint32_t meta, uint64_t b,
+                                              uint64_t off, uint8_t *__restrict__ out, uint64_t off_esc,
+                                              const void *__restrict__ in, uint64_t n, const uint8_t *table,
+                                              uint8_t *buf, uint32_t item)
+{
+    const uint32_t lane = lane_id();
+    const uint64_t t0 = kTilesPerBlock * b;
+    uint32_t cnt[kTilesPerBlock], before[kTilesPerBlock], most = 0, run = 0, rederive = 0;
+#pragma unroll
+    for (uint32_t t = 0; t < kTilesPerBlock; ++t) {
+        const uint32_t v = __builtin_amdgcn_readlane(meta, t);
+        cnt[t] = v & ~kRederiveFlag;
+        rederive |= (v >> 31) << t;
+        before[t] = run;
+        run += cnt[t];
+        most = std::max(most, cnt[t]);
+    }
+    if (most <= kGroupCopyRecords && !rederive) {               // wave-uniform
+        const uint32_t g = lane >> 4;
+        uint32_t k = 0, bef = 0;
+#pragma unroll
+        for (uint32_t t = 0; t < kTilesPerBlock; ++t)
+            if (g == t) {
+                k = cnt[t];
+                bef = before[t];
+            }
+        if (k) copy_records(stage + (t0 + g) * (3ull * kEncTile), out, off_esc + item * (off + bef), item * k, lane & 15, 16);
+        return;
+    }
+#pragma unroll
+    for (uint32_t t = 0; t < kTilesPerBlock; ++t) {
+        if (cnt[t] == 0) continue;
+        const uint64_t dst0 = off_esc + item * (off + before[t]);
+        if ((rederive >> t) & 1) {
+            if (DT == SZ_BF16)
+                rederive_tile_bf16(static_cast<const uint16_t *>(in), n, t0 + t, table, buf, out + (dst0 & ~uint64_t(3)),
+                                   (uint32_t)(dst0 & 3));
+            else
+                rederive_tile_e5m2(static_cast<const uint8_t *>(in), n, t0 + t, table, buf, out + (dst0 & ~uint64_t(3)),
+                                   (uint32_t)(dst0 & 3));
+        } else {
+            copy_records(stage + (t0 + t) * (3ull * kEncTile), out, dst0, item * cnt[t], lane, 64);
+        }
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_compact(
+    const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
+    const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
+    uint64_t nb, const void *__restrict__ in, uint64_t n, Codebook4 cb, const uint32_t *__restrict__ cb_dev,
+    uint32_t item)
+{
+    __shared__ uint32_t table32[64];
+    __shared__ __align__(16) uint8_t seg_buf[kCompactThreads / 64][kSegBytes];
+    if (cb_dev) cb = load_codebook(cb_dev);
+    build_encode_table(table32, cb, DT == SZ_BF16 ? 256 : 32);
+    __syncthreads();
+    const uint64_t b = (uint64_t)blockIdx.x * (kCompactThreads / 64) + threadIdx.x / 64;
+    if (b >= nb) return;
+    const uint32_t lane = lane_id();
+    // lanes 0..3 fetch the tile counts, lane 4 the block's escape offset
+    const uint64_t t0 = kTilesPerBlock * b;
+    uint64_t meta = 0;
+    if (lane < kTilesPerBlock && t0 + lane < nt) meta = tile_counts[t0 + lane];
+    else if (lane == kTilesPerBlock) meta = block_offsets[b];
+    const uint64_t off = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(meta >> 32), kTilesPerBlock) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((uint32_t)meta, kTilesPerBlock);
+    compact_block<DT>(stage, (uint32_t)meta, b, off, out, off_esc, in, n, reinterpret_cast<const uint8_t *>(table32),
+                      seg_buf[threadIdx.x / 64], item);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: compaction with its own prefix, in place of sz_enc_scan plus
+// sz_enc_compact for streams of up to kFusedPrefixTiles tiles.  A 1024-lane
+// workgroup owns 16 consecutive blocks: all its lanes sum the counts of the
+// tiles before its first block (aligned dwordx4 loads, from L2 after the
+// first workgroups), the 16 block totals meet in LDS, and each wave then
+// moves its block's records as sz_enc_compact does.  The wave of a block
+// also writes the block's count into the stream, the wave of the last block
+// writes E, and workgroup 0 writes the rest of the header, the section
+// padding and the status word (device codebook check) as sz_enc_scan does.
+// The tile counts before a workgroup are re-read by every later workgroup, a
+// cost that grows with the square of the tile count: on MI355X this path
+// saves 2-3 us per encode up to 16M elements, breaks even at 32M and loses
+// beyond, so larger streams take the scan.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kFusedThreads = 1024;
+constexpr uint32_t kFusedBlocks = kFusedThreads / 64;
+constexpr uint64_t kFusedPrefixTiles = 2048;
+
+template <int DT>
+__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_compact_fused(
+    const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts, uint8_t *__restrict__ out,
+    uint64_t off_esc, uint64_t nt, const void *__restrict__ in, HeaderArgs h, const uint32_t *__restrict__ cb_dev,
+    int32_t *__restrict__ status, uint32_t item)
+{
+    __shared__ uint32_t table32[64];
+    __shared__ __align__(16) uint8_t seg_buf[kFusedBlocks][kSegBytes];
+    __shared__ uint64_t wave_part[kFusedBlocks];
+    __shared__ uint32_t block_total[kFusedBlocks];
+    const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
+    const uint64_t nb = h.nb;
+    Codebook4 cb = h.cb;
+    const int32_t verdict = device_codebook_verdict(cb_dev, h.dtype, cb);
+    build_encode_table(table32, cb, DT == SZ_BF16 ? 256 : 32);
+    // escapes of the tiles before this workgroup's first block (a multiple of
+    // 64 tiles, all of them below nt)
+    const uint64_t b0 = (uint64_t)blockIdx.x * kFusedBlocks;
+    const uint64_t tiles_before = kTilesPerBlock * b0;
+    uint64_t part = 0;
+#pragma unroll 4
+    for (uint64_t t = 4 * tid; t < tiles_before; t += 4 * kFusedThreads) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(tile_counts + t);
+        part += (uint64_t)(v.x & ~kRederiveFlag) + (v.y & ~kRederiveFlag) + (v.z & ~kRederiveFlag) +
+                (v.w & ~kRederiveFlag);
+    }
+    part = wave_sum_u64(part);
+    // this wave's block: lanes 0..3 fetch its tile counts
+    const uint64_t b = b0 + wave;
+    const uint64_t t0 = kTilesPerBlock * b;
+    uint32_t meta = 0;
+    if (lane < kTilesPerBlock && t0 + lane < nt) meta = tile_counts[t0 + lane];
+    uint32_t total = 0;
+#pragma unroll
+    for (uint32_t t = 0; t < kTilesPerBlock; ++t) total += __builtin_amdgcn_readlane(meta, t) & ~kRederiveFlag;
+    if (lane == 0) {
+        wave_part[wave] = part;
+        block_total[wave] = total;
+    }
+    __syncthreads();
+    uint64_t acc = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kFusedBlocks; ++w) {
+        acc += wave_part[w];
+        if (w < wave) acc += block_total[w];
+    }
+    // wave-uniform: kept in scalar registers for the copy and re-derivation
+    const uint64_t off = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(acc >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)acc);
+    uint32_t *header32 = reinterpret_cast<uint32_t *>(out);
+    if (b < nb && lane == 0) {
+        reinterpret_cast<uint32_t *>(out + 64)[b] = total;
+        if (b == nb - 1) {
+            const uint64_t e = off + total;
+            header32[4] = (uint32_t)e;
+            header32[5] = (uint32_t)(e >> 32);
+        }
+    }
+    if (blockIdx.x == 0) write_header(out, h, cb, verdict, nb == 0, status);
+    if (b >= nb) return;
+    compact_block<DT>(stage, meta, b, off, out, off_esc, in, h.n, reinterpret_cast<const uint8_t *>(table32),
+                      seg_buf[wave], item);
+}
+
+// Encode behind sz_encode (host codebook cb4), sz_encode_devcb (cb_dev) and
+// sz_encode_format (version 2, 3).
+int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems, const Codebook4 &cb4,
+                const uint32_t *cb_dev, void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes,
+                void *stream)
+{
+    if (n_elems > kMaxElems) return SZ_E_ARG;
+    if (!d_out || !d_ws || (n_elems && !d_in)) return SZ_E_ARG;
+    if (!aligned16(d_out) || !aligned16(d_ws) || (n_elems && !aligned16(d_in))) return SZ_E_ALIGN;
+    if (out_capacity < encoded_size_v(version, dtype, n_elems, n_elems)) return SZ_E_CAPACITY;
+    if (ws_bytes < sz_workspace_size(dtype, n_elems)) return SZ_E_WORKSPACE;
+    const Geometry g = geometry(dtype, n_elems, version);
+    const WsLayout w = ws_layout(dtype, n_elems);
+    uint8_t *ws = static_cast<uint8_t *>(d_ws);
+    uint8_t *out = static_cast<uint8_t *>(d_out);
+    int32_t *status = reinterpret_cast<int32_t *>(ws);
+    uint32_t *tile_counts = reinterpret_cast<uint32_t *>(ws + w.counts);
+    uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
+    uint8_t *stage = ws + w.stage;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (g.nt && dtype == SZ_BF16) {
+        const uint16_t *in16 = static_cast<const uint16_t *>(d_in);
+        if (version == kTop8) {
+            LaunchScope scope("sz_enc_dense_top8", s);
+            hipLaunchKernelGGL(sz_enc_dense_bf16<kTop8>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16, g.n,
+                               out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage);
+        } else if (version == kTop15S) {
+            LaunchScope scope("sz_enc_dense_top15s", s);
+            hipLaunchKernelGGL(sz_enc_dense_bf16<kTop15S>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16,
+                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage);
+        } else {
+            LaunchScope scope("sz_enc_dense_bf16", s);
+            hipLaunchKernelGGL(sz_enc_dense_bf16<kTop16>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16,
+                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage);
+        }
+    } else if (g.nt) {
+        LaunchScope scope("sz_enc_dense_e5m2", s);
+        hipLaunchKernelGGL(sz_enc_dense_e5m2, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s,
+                           static_cast<const uint8_t *>(d_in), g.n, out, g.off_nib, g.off_sm, g.sm_bytes,
+                           cb4, cb_dev, tile_counts, stage);
+    }
+    {
+        HeaderArgs h;
+        h.n = g.n;
+        h.nb = g.nb;
+        h.dtype = (uint32_t)dtype;
+        h.version = version;
+        h.cb = cb4;
+        h.pad_start[0] = 64 + 4 * g.nb;
+        h.pad_end[0] = g.off_nib;
+        h.pad_start[1] = g.off_nib + g.nib_bytes;
+        h.pad_end[1] = g.off_sm;
+        h.pad_start[2] = g.off_sm + g.sm_bytes;
+        h.pad_end[2] = g.off_esc;
+        if (g.nt <= kFusedPrefixTiles) {
+            // one launch orders the records and writes the header
+            const uint32_t groups = (uint32_t)std::max<uint64_t>(1, (g.nb + kFusedBlocks - 1) / kFusedBlocks);
+            LaunchScope scope("sz_enc_compact_fused", s);
+            if (dtype == SZ_BF16)
+                hipLaunchKernelGGL(sz_enc_compact_fused<SZ_BF16>, dim3(groups), dim3(kFusedThreads), 0, s, stage,
+                                   tile_counts, out, g.off_esc, g.nt, d_in, h, cb_dev, status,
+                                   escape_item_bytes(version));
+            else
+                hipLaunchKernelGGL(sz_enc_compact_fused<SZ_FP8_E5M2>, dim3(groups), dim3(kFusedThreads), 0, s, stage,
+                                   tile_counts, out, g.off_esc, g.nt, d_in, h, cb_dev, status, 3u);
+            return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
+        }
+        LaunchScope scope("sz_enc_scan", s);
+        hipLaunchKernelGGL(sz_enc_scan, dim3(1), dim3(kScanThreads), 0, s, tile_counts, (uint32_t)g.nt,
+                           block_offsets, out, h, cb_dev, status);
+    }
+    if (g.nt) {
+        LaunchScope scope("sz_enc_compact", s);
+        const uint32_t groups = (uint32_t)((g.nb + kCompactThreads / 64 - 1) / (kCompactThreads / 64));
+        if (dtype == SZ_BF16)
+            hipLaunchKernelGGL(sz_enc_compact<SZ_BF16>, dim3(groups), dim3(kCompactThreads), 0, s, stage, tile_counts,
+                               block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev,
+                               escape_item_bytes(version));
+        else
+            hipLaunchKernelGGL(sz_enc_compact<SZ_FP8_E5M2>, dim3(groups), dim3(kCompactThreads), 0, s, stage,
+                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev, 3u);
+    }
+    return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
+}
+
+}  // namespace
+}  // namespace sz
+
+using namespace sz;
+
+extern "C" uint64_t sz_encoded_size(int dtype, uint64_t n_elems, uint64_t n_escapes)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return 0;
+    return geometry(dtype, n_elems).off_esc + 3 * n_escapes;
+}
+
+extern "C" uint64_t sz_workspace_size(int dtype, uint64_t n_elems)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return 0;
+    return ws_layout(dtype, n_elems).total;
+}
+
+extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *cb, void *d_out,
+                         uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    if (!cb) return SZ_E_ARG;
+    if (cb->dtype != (uint32_t)dtype) return SZ_E_DTYPE;
+    const uint32_t symbols = symbols_of(dtype);
+    for (int c = 0; c < 16; ++c) {
+        if (cb->exp[c] >= symbols) return SZ_E_ARG;
+        for (int d = 0; d < c; ++d)
+            if (cb->exp[d] == cb->exp[c]) return SZ_E_ARG;
+    }
+    return encode_impl(kTop16, dtype, d_in, n_elems, pack_codebook(cb->exp), nullptr, d_out, out_capacity, d_ws,
+                       ws_bytes, stream);
+}
+
+extern "C" uint64_t sz_encoded_size_format(int format, int dtype, uint64_t n_elems, uint64_t n_escapes)
+{
+    if (format == SZ_FORMAT_TOP16) return sz_encoded_size(dtype, n_elems, n_escapes);
+    if ((format != SZ_FORMAT_TOP8 && format != SZ_FORMAT_TOP15_SENTINEL) || dtype != SZ_BF16) return 0;
+    return encoded_size_v((uint32_t)format, dtype, n_elems, n_escapes);
+}
+
+extern "C" int sz_encode_format(int format, int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *cb,
+                                void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (format == SZ_FORMAT_TOP16)
+        return sz_encode(dtype, d_in, n_elems, cb, d_out, out_capacity, d_ws, ws_bytes, stream);
+    if (format != SZ_FORMAT_TOP8 && format != SZ_FORMAT_TOP15_SENTINEL) return SZ_E_ARG;
+    if (dtype != SZ_BF16) return SZ_E_DTYPE;
+    if (!cb) return SZ_E_ARG;
+    if (cb->dtype != (uint32_t)dtype) return SZ_E_DTYPE;
+    // only the first 8 (15) entries are used; they must be distinct, and the
+    // stream's header carries zeros in the others
+    const uint32_t entries = book_entries((uint32_t)format);
+    uint8_t used[16] = {0};
+    for (uint32_t c = 0; c < entries; ++c) {
+        used[c] = cb->exp[c];
+        for (uint32_t d = 0; d < c; ++d)
+            if (cb->exp[d] == cb->exp[c]) return SZ_E_ARG;
+    }
+    return encode_impl((uint32_t)format, dtype, d_in, n_elems, pack_codebook(used), nullptr, d_out, out_capacity,
+                       d_ws, ws_bytes, stream);
+}
+
+extern "C" int sz_encode_devcb(int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *d_cb,
+                               void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    if (!d_cb) return SZ_E_ARG;
+    if (!aligned16(d_cb)) return SZ_E_ALIGN;
+    const uint8_t zero[16] = {0};
+    return encode_impl(kTop16, dtype, d_in, n_elems, pack_codebook(zero), reinterpret_cast<const uint32_t *>(d_cb),
+                       d_out, out_capacity, d_ws, ws_bytes, stream);
+}
+
