@@ -197,20 +197,14 @@ __device__ __forceinline__ void read_record(const uint8_t *esc, uint64_t r, uint
     e = p[2];
 }
 
-// Four consecutive records from one 16-byte window of aligned words.  The
-// window never leaves the record section: it starts at most 3 bytes before
-// record R and ends at most 3 bytes after record R+3, and callers use it only
-// while a whole record group past R+3 remains in the stream (otherwise they
-// read the records byte by byte).
-__device__ __forceinline__ void read_records4(const uint8_t *esc, uint64_t r, uint32_t pos[4], uint32_t e[4])
+// Four consecutive records from the 16 bytes w[0..3] of aligned words that
+// start `sh` bytes before the first record.
+__device__ __forceinline__ void records4_from_words(const uint32_t (&w)[4], uint32_t sh, uint32_t pos[4],
+                                                    uint32_t e[4])
 {
-    const uint64_t byte0 = 3 * r;
-    const uint32_t *w = reinterpret_cast<const uint32_t *>(esc + (byte0 & ~uint64_t(3)));
-    const uint32_t sh = (uint32_t)(byte0 & 3);
-    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
-    const uint32_t d0 = __builtin_amdgcn_alignbyte(w1, w0, sh);   // bytes 0..3 of the 12
-    const uint32_t d1 = __builtin_amdgcn_alignbyte(w2, w1, sh);   // bytes 4..7
-    const uint32_t d2 = __builtin_amdgcn_alignbyte(w3, w2, sh);   // bytes 8..11
+    const uint32_t d0 = __builtin_amdgcn_alignbyte(w[1], w[0], sh);   // bytes 0..3 of the 12
+    const uint32_t d1 = __builtin_amdgcn_alignbyte(w[2], w[1], sh);   // bytes 4..7
+    const uint32_t d2 = __builtin_amdgcn_alignbyte(w[3], w[2], sh);   // bytes 8..11
     pos[0] = d0 & 0xFFFFu;
     e[0] = (d0 >> 16) & 0xFFu;
     pos[1] = (d0 >> 24) | ((d1 & 0xFFu) << 8);
@@ -219,6 +213,19 @@ __device__ __forceinline__ void read_records4(const uint8_t *esc, uint64_t r, ui
     e[2] = d2 & 0xFFu;
     pos[3] = (d2 >> 8) & 0xFFFFu;
     e[3] = d2 >> 24;
+}
+
+// Four consecutive records from one 16-byte window of aligned words.  The
+// window never leaves the record section: it starts at most 3 bytes before
+// record R and ends at most 3 bytes after record R+3, and callers use it only
+// while a whole record group past R+3 remains in the stream (otherwise they
+// read the records byte by byte).
+__device__ __forceinline__ void read_records4(const uint8_t *esc, uint64_t r, uint32_t pos[4], uint32_t e[4])
+{
+    const uint64_t byte0 = 3 * r;
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(esc + (byte0 & ~uint64_t(3)));
+    const uint32_t w[4] = {p[0], p[1], p[2], p[3]};
+    records4_from_words(w, (uint32_t)(byte0 & 3), pos, e);
 }
 
 // Loads the k (<= kMappedEscapes) records of a block into LDS as
@@ -325,12 +332,26 @@ __device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ 
                                                     uint8_t *plane, int32_t *__restrict__ status)
 {
     const uint32_t lane = lane_id();
+    const uint32_t step = 4 * blockDim.x;
     bool bad = false;
-    for (uint32_t r = 4 * threadIdx.x; r < k; r += 4 * blockDim.x) {
+    // the aligned words of a four-record group, loaded one group ahead so that
+    // a load is always in flight while the previous group is applied
+    auto window = [&](uint32_t r, uint32_t (&w)[4]) {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(esc + ((3 * (r0 + r)) & ~uint64_t(3)));
+        w[0] = p[0];
+        w[1] = p[1];
+        w[2] = p[2];
+        w[3] = p[3];
+    };
+    uint32_t w[4] = {0, 0, 0, 0};
+    uint32_t r = 4 * threadIdx.x;
+    bool fast = r < k && r0 + r + 5 < e_total;
+    if (fast) window(r, w);
+    for (; r < k; r += step) {
         uint32_t pos[4], e[4];
         const uint32_t cnt = std::min<uint32_t>(4, k - r);
-        if (r0 + r + 5 < e_total) {
-            read_records4(esc, r0 + r, pos, e);
+        if (fast) {
+            records4_from_words(w, (uint32_t)((3 * (r0 + r)) & 3), pos, e);
         } else {
 #pragma unroll
             for (uint32_t q = 0; q < 4; ++q) {
@@ -339,6 +360,9 @@ __device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ 
                 if (q < cnt) read_record(esc, r0 + r + q, pos[q], e[q]);
             }
         }
+        const uint32_t rn = r + step;
+        fast = rn < k && r0 + rn + 5 < e_total;
+        if (fast) window(rn, w);
         uint32_t prev = __shfl_up(pos[3], 1, 64);        // lane l-1 holds records r-4..r-1
         if (lane == 0 && r > 0) {
             uint32_t pe;
