@@ -429,6 +429,18 @@ def extra_sections(sz, x, cb, dtype, n, elem, buf, ws, ws_dec, y, dev, time_loop
             print("transfer mismatch (%s)" % mode, file=sys.stderr)
             sys.exit(1)
         runs[mode] = best
+    # the codec's own time per chunk (encode + decode of one chunk on the
+    # device, no link), and its share of the compressed transfer's wall time
+    xc = x[:chunk]
+    bc = torch.empty(sz.encoded_size(dtype, chunk, chunk), dtype=torch.uint8, device=dev)
+    wc_e, wc_d = sz.workspace(dtype, chunk, dev), sz.workspace(dtype, chunk, dev)
+    yc = torch.empty_like(xc)
+
+    def chunk_codec():
+        sz.encode(xc, cb, out=bc, ws=wc_e, sync=False)
+        sz.decode(bc, dtype, chunk, out=yc, ws=wc_d, check=False)
+    codec_ms = time_loop(chunk_codec, reps)
+    del bc, wc_e, wc_d, yc
     transfer = {
         "link": "PCIe via pinned host memory, device->host then host->device, pipelined (depth 3)",
         "chunk_elems": chunk,
@@ -440,6 +452,8 @@ def extra_sections(sz, x, cb, dtype, n, elem, buf, ws, ws_dec, y, dev, time_loop
         "wire_bytes": runs["splitzip"]["wire_bytes"],
         "wire_ratio": round(n * elem / runs["splitzip"]["wire_bytes"], 6),
         "speedup": round(runs["raw"]["total_ms"] / runs["splitzip"]["total_ms"], 4),
+        "codec_ms_per_chunk": round(codec_ms, 4),
+        "codec_share": round(runs["splitzip"]["chunks"] * codec_ms / runs["splitzip"]["total_ms"], 4),
     }
     del staging
     return calibration, formats, transfer
