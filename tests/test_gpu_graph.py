@@ -13,14 +13,19 @@ import synth
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype", [0, 1])
-def test_graph_replays_match_eager(dtype):
+# small tensors take the fused kernels (one compaction launch, header check);
+# 80M elements take the scans
+@pytest.mark.parametrize("dtype,n_big", [(0, 0), (1, 0), (0, 80 << 20)])
+def test_graph_replays_match_eager(dtype, n_big):
     import fp8_kv_cache_sz_amd as sz
     name = "llama3_8b_kv" if dtype == 0 else "llama3_8b_kv_e5m2"
-    x0, _ = synth.workload(name, size="small")
+    if n_big:
+        x0 = synth.workload(name, device="cuda")[0][:n_big].contiguous()
+    else:
+        x0 = synth.workload(name, size="small")[0].cuda()
     cb = sz.calibrate(synth.calibration_tensor(name))
     n = x0.numel()
-    x = x0.cuda()
+    x = x0.clone()
     cap = sz.encoded_size(dtype, n, n)
     buf = torch.zeros(cap, dtype=torch.uint8, device="cuda")
     ws_e = torch.zeros(sz.workspace_size(dtype, n), dtype=torch.uint8, device="cuda")
@@ -40,9 +45,7 @@ def test_graph_replays_match_eager(dtype):
     for rep in range(4):
         print("graph replay", rep, flush=True)
         # change the input in place (eager work between replays)
-        gen = torch.Generator(device="cpu").manual_seed(rep)
-        perm = torch.randperm(n, generator=gen).cuda()
-        x.copy_(x0.cuda()[perm])
+        x.copy_(torch.roll(x0, shifts=12345 * (rep + 1)))
         torch.cuda.synchronize()
         buf.fill_(0xA5)
         y.fill_(0)
