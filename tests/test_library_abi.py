@@ -43,6 +43,31 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(nat.EXPORTS)
 
 
+def test_header_is_plain_c(tmp_path):
+    """include/splitzip.h is a C header: a C11 program that takes the address
+    of every declared call compiles with -pedantic -Werror and links against
+    the library."""
+    import shutil
+    import subprocess
+    nat = _native()
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    names = declared_functions()
+    src = tmp_path / "abi.c"
+    src.write_text('#include "splitzip.h"\n#include <stddef.h>\n'
+                   "typedef void (*any_call)(void);\n"
+                   "any_call const calls[] = {\n" + ",\n".join("    (any_call)%s" % n for n in names) + "\n};\n"
+                   "int main(void) { size_t k = 0; for (size_t i = 0; i < sizeof calls / sizeof calls[0]; ++i) "
+                   "k += calls[i] != NULL; return k == sizeof calls / sizeof calls[0] ? 0 : 1; }\n")
+    lib_dir = os.path.dirname(nat.LIBRARY)
+    exe = tmp_path / "abi"
+    subprocess.check_call([gcc, "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                           "-I", os.path.join(ROOT, "include"), str(src), "-L", lib_dir, "-lsplitzip",
+                           "-Wl,-rpath," + lib_dir, "-o", str(exe)])
+    assert os.path.exists(exe)
+
+
 def test_encoded_size_matches_oracle():
     nat = _native()
     for dtype in (0, 1):
