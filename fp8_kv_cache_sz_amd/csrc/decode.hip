@@ -1,7 +1,7 @@
 // SplitZip decode for MI355X: stream validation and block escape offsets
-// (one-workgroup scan, or for small streams a header check and per-workgroup
-// offsets), the dense decoders with the escape patch fused before the store,
-// the ablation-format decoders, and the decode entry points of the C ABI
+// (a one-workgroup scan, or one wave for small streams), the span decoders
+// with the escape patch fused before the store, the ablation-format
+// decoders, and the decode entry points of the C ABI
 // ("SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
 // Serving", gist.science summary page, Method, decoding bullets).
 #include "common.hpp"
@@ -14,8 +14,8 @@ namespace {
 // counts (each at most its block length, summing to E) and writes the
 // exclusive escape offset of every block.  It writes its verdict (0 or a
 // negative error code) to status[0], the caller-visible status word, and to
-// status[1], which the block decoders read: they only ever write status[0],
-// so every wave of a decode workgroup sees the same verdict.
+// status[1], which the decoders read: they only ever write status[0], so
+// every wave of a decode workgroup sees the same verdict.
 // ---------------------------------------------------------------------------
 struct DecodeArgs {
     uint64_t n, nb, in_bytes, off_nib, off_sm, off_esc;
@@ -44,23 +44,75 @@ __device__ __forceinline__ int32_t header_verdict(const uint8_t *__restrict__ in
 }
 
 // ---------------------------------------------------------------------------
-// Kernel: decode header check, in place of sz_dec_scan for streams of up to
-// kFusedPrefixBlocks blocks, whose decoders find their escape offsets
-// themselves (on MI355X 1.5-4.6 us faster per decode up to 64M elements; far
-// beyond, every decoder re-reading the counts before it costs more than the
-// scan).  One wave checks the header and writes the verdict to both
-// status words, as sz_dec_scan does; the block counts are checked by the
-// decoders.
+// Kernel: decode scan of a small stream (at most kSmallScanBlocks blocks), in
+// place of sz_dec_scan, with the same checks and outputs.  One wave: each lane
+// loads sixteen block counts (the count array starts at byte 64 and its
+// section is padded to 256 bytes, so the four dwordx4 loads of a lane whose
+// first count exists never leave it), a wave prefix sum of the lane totals
+// (counts capped at the block length, so 32-bit sums cannot wrap) gives every
+// block's offset, and the lane writes its sixteen offsets.  A 1024-lane
+// workgroup spends most of its time on launch and barriers; one wave does the
+// same work in a single round of loads and stores.
 // ---------------------------------------------------------------------------
-constexpr uint64_t kFusedPrefixBlocks = 1024;
+constexpr uint64_t kSmallScanBlocks = 1024;
 
-__global__ __launch_bounds__(64) void sz_dec_head(const uint8_t *__restrict__ in, DecodeArgs a,
-                                                  int32_t *__restrict__ status)
+__global__ __launch_bounds__(64) void sz_dec_scan_small(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                        uint64_t *__restrict__ block_offsets,
+                                                        int32_t *__restrict__ status)
 {
-    if (threadIdx.x == 0) {
-        const int32_t err = header_verdict(in, a);
-        status[0] = err;
-        status[1] = err;
+    const uint32_t lane = threadIdx.x;
+    const uint32_t nb = (uint32_t)a.nb;
+    const uint32_t g = 16 * lane;
+    const uint32_t *counts = reinterpret_cast<const uint32_t *>(in + 64);
+    uint32_t c[16];
+    if (g < nb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(counts + g + 4 * q);
+            c[4 * q] = v.x;
+            c[4 * q + 1] = v.y;
+            c[4 * q + 2] = v.z;
+            c[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[i] = 0;
+    }
+    const int32_t err = header_verdict(in, a);
+    const uint64_t e_hdr = *reinterpret_cast<const uint64_t *>(in + 16);
+    // the last block may be shorter than B: its count is bounded by its length
+    const uint32_t last_len = nb ? (uint32_t)(a.n - (uint64_t)(nb - 1) * kBlock) : 0;
+    bool too_many = false;
+    uint32_t sum = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < 16; ++i) {
+        if (g + i >= nb) c[i] = 0;
+        too_many |= c[i] > (g + i + 1 == nb ? last_len : (uint32_t)kBlock);
+        c[i] = std::min<uint32_t>(c[i], kBlock);
+        sum += c[i];
+    }
+    const uint32_t incl = wave_inclusive_sum(sum);
+    const uint32_t total = read_lane63(incl);
+    if (!err && g < nb) {
+        uint64_t o[16];
+        o[0] = incl - sum;
+#pragma unroll
+        for (int i = 1; i < 16; ++i) o[i] = o[i - 1] + c[i - 1];
+        if (g + 16 <= nb) {
+            uint4 *dst = reinterpret_cast<uint4 *>(block_offsets + g);   // 128 aligned bytes
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                dst[q] = make_uint4((uint32_t)o[2 * q], (uint32_t)(o[2 * q] >> 32), (uint32_t)o[2 * q + 1],
+                                    (uint32_t)(o[2 * q + 1] >> 32));
+        } else {
+            for (uint32_t i = 0; g + i < nb; ++i) block_offsets[g + i] = o[i];
+        }
+    }
+    const bool bad = __ballot(too_many) != 0 || total != e_hdr;
+    if (lane == 0) {
+        const int32_t verdict = err ? err : bad ? SZ_E_FORMAT : 0;
+        status[0] = verdict;
+        status[1] = verdict;
     }
 }
 
@@ -136,55 +188,14 @@ __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__res
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernels: one 1024-lane workgroup per 64K block.  First an LDS map
-// from each chunk to the first escape record inside it is built from the
-// block's records (validating their order and range), then every wave
-// decodes one 4096-element row in registers, patches the escaped exponents
-// and stores once.
+// Escape records, code lookup and value assembly shared by the decoders.  The
+// block-wide pieces (an LDS map from each chunk to the first escape record
+// inside it, built from all of a block's records while checking their order
+// and range) serve the ablation decoders, which give a 64K block to one
+// 1024-lane workgroup.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kNoEscape = 0xFFFFu;
 
-// Escape offset of block b and its count check.  With block_offsets (from
-// sz_dec_scan, which has checked every count) the offset is read.  Without
-// them (at most kFusedPrefixBlocks blocks) the whole workgroup sums the
-// counts of blocks 0..b-1 from the stream with aligned dwordx4 loads (the
-// count array starts at byte 64 and its section is padded to 256 bytes, so a
-// load of four counts never leaves it), each count capped at the block
-// length so that 32-bit sums cannot wrap, and checks the block's own count:
-// at most the block length, the records inside the E of the header, and for
-// the last block offset + count = E.  A failed check sets the status word
-// and zeroes k, so the block decodes without touching records; a count
-// above its block length fails its own block's check.  Called by every
-// thread; the result is workgroup-uniform.
-__device__ uint64_t block_escape_offset(const uint8_t *__restrict__ in, const DecodeArgs &a, uint64_t b,
-                                        uint32_t blen, uint64_t e_total, const uint64_t *__restrict__ block_offsets,
-                                        uint32_t &k, int32_t *__restrict__ status, uint32_t *part)
-{
-    if (block_offsets) return block_offsets[b];
-    if (k == 0 && b + 1 != a.nb) return 0;                      // no records and not the last block
-    const uint32_t *counts = reinterpret_cast<const uint32_t *>(in + 64);
-    const uint32_t bb = (uint32_t)b;                            // b < kFusedPrefixBlocks
-    uint32_t sum = 0;
-#pragma unroll 1
-    for (uint32_t g = 4 * threadIdx.x; g < bb; g += 4 * kDecThreads) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(counts + g);
-        sum += std::min<uint32_t>(v.x, kBlock) + (g + 1 < bb ? std::min<uint32_t>(v.y, kBlock) : 0u) +
-               (g + 2 < bb ? std::min<uint32_t>(v.z, kBlock) : 0u) +
-               (g + 3 < bb ? std::min<uint32_t>(v.w, kBlock) : 0u);
-    }
-    sum = read_lane63(wave_inclusive_sum(sum));
-    if (lane_id() == 0) part[threadIdx.x / 64] = sum;
-    __syncthreads();
-    uint32_t r0 = 0;
-#pragma unroll
-    for (uint32_t w = 0; w < kDecThreads / 64; ++w) r0 += part[w];
-    r0 = __builtin_amdgcn_readfirstlane(r0);
-    if (k > blen || r0 + (uint64_t)k > e_total || (b + 1 == a.nb && r0 + (uint64_t)k != e_total)) {
-        if (threadIdx.x == 0) atomicExch(status, SZ_E_FORMAT);
-        k = 0;
-    }
-    return r0;
-}
 // Blocks with up to this many escapes decode through an LDS map of their
 // records; blocks with more go through the exponent plane.
 constexpr uint32_t kMappedEscapes = 8192;
@@ -323,13 +334,27 @@ __device__ __forceinline__ uint2 lookup_codes8(uint32_t d, const CodebookRegs &c
     return make_uint2(perm(e_odd, e_even, 0x05010400u), perm(e_odd, e_even, 0x07030602u));
 }
 
-// Overwrites plane[pos] with the exponent of each of the block's k records,
-// four records per aligned three-word window; invalid records (position out
-// of the block or not ascending, exponent out of range) are skipped and
-// reported through the status word.
-__device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ esc, uint64_t r0, uint32_t k,
-                                                    uint32_t blen, uint32_t symbols, uint64_t e_total,
-                                                    uint8_t *plane, int32_t *__restrict__ status)
+// Eight BF16 values from their sign/mantissa bytes and their exponents
+// (both in element order).
+__device__ __forceinline__ uint4 assemble_bf16(uint2 sm, uint2 ex)
+{
+    uint4 o;
+    o.x = (perm(sm.x, sm.x, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C010C00u) << 7);
+    o.y = (perm(sm.x, sm.x, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C030C02u) << 7);
+    o.z = (perm(sm.y, sm.y, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C050C04u) << 7);
+    o.w = (perm(sm.y, sm.y, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C070C06u) << 7);
+    return o;
+}
+
+// Checks records i0 .. i1-1 of a block (each against the one before it) and
+// overwrites plane[pos - lo] with the exponent of each whose position lies in
+// [lo, lo + span), four records per aligned three-word window; invalid records
+// (position out of the block or not ascending, exponent out of range) are
+// skipped and reported through the status word.
+__device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ esc, uint64_t r0, uint32_t i0,
+                                                    uint32_t i1, uint32_t blen, uint32_t symbols, uint64_t e_total,
+                                                    uint8_t *plane, uint32_t lo, uint32_t span,
+                                                    int32_t *__restrict__ status)
 {
     const uint32_t lane = lane_id();
     const uint32_t step = 4 * blockDim.x;
@@ -344,12 +369,12 @@ __device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ 
         w[3] = p[3];
     };
     uint32_t w[4] = {0, 0, 0, 0};
-    uint32_t r = 4 * threadIdx.x;
-    bool fast = r < k && r0 + r + 5 < e_total;
+    uint32_t r = i0 + 4 * threadIdx.x;
+    bool fast = r < i1 && r0 + r + 5 < e_total;
     if (fast) window(r, w);
-    for (; r < k; r += step) {
+    for (; r < i1; r += step) {
         uint32_t pos[4], e[4];
-        const uint32_t cnt = std::min<uint32_t>(4, k - r);
+        const uint32_t cnt = std::min<uint32_t>(4, i1 - r);
         if (fast) {
             records4_from_words(w, (uint32_t)((3 * (r0 + r)) & 3), pos, e);
         } else {
@@ -361,7 +386,7 @@ __device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ 
             }
         }
         const uint32_t rn = r + step;
-        fast = rn < k && r0 + rn + 5 < e_total;
+        fast = rn < i1 && r0 + rn + 5 < e_total;
         if (fast) window(rn, w);
         uint32_t prev = __shfl_up(pos[3], 1, 64);        // lane l-1 holds records r-4..r-1
         if (lane == 0 && r > 0) {
@@ -372,134 +397,26 @@ __device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ 
         for (uint32_t q = 0; q < 4; ++q) {
             if (q >= cnt) continue;
             const uint32_t before = q == 0 ? prev : pos[q - 1];
-            if (pos[q] < blen && e[q] < symbols && (r + q == 0 || pos[q] > before)) plane[pos[q]] = (uint8_t)e[q];
-            else bad = true;
+            if (pos[q] < blen && e[q] < symbols && (r + q == 0 || pos[q] > before)) {
+                if (pos[q] - lo < span) plane[pos[q] - lo] = (uint8_t)e[q];
+            } else {
+                bad = true;
+            }
         }
     }
     if (bad) atomicExch(status, SZ_E_FORMAT);
 }
 
-__global__ __launch_bounds__(kDecThreads) void sz_dec_bf16(const uint8_t *__restrict__ in, DecodeArgs a,
-                                                           const uint64_t *__restrict__ block_offsets,
-                                                           int32_t *__restrict__ status,
-                                                           uint16_t *__restrict__ out)
-{
-    __shared__ uint32_t table[256];
-    __shared__ uint32_t prefix_part[kDecThreads / 64];
-    // mapped blocks: first[] (first record of each 8-element chunk, 16 KB) and
-    // rec[] (the records, 32 KB); heavy blocks: the exponent plane (64 KB)
-    __shared__ __align__(16) uint8_t pool[kBlock];
-    uint16_t *first = reinterpret_cast<uint16_t *>(pool);
-    uint32_t *rec = reinterpret_cast<uint32_t *>(pool + kBlock / 4);
-    uint8_t *plane = pool;
-    if (status[1] != 0) return;
-    const uint32_t tid = threadIdx.x;
-    const uint64_t b = blockIdx.x;
-    const uint64_t e0 = b * kBlock;
-    const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
-    uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
-    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
-    const uint8_t *esc = in + a.off_esc;
-    if (tid < 256) {
-        const uint32_t lo = in[32 + (tid & 15)];
-        const uint32_t hi = in[32 + (tid >> 4)];
-        table[tid] = (lo << 7) | (hi << 23);
-    }
-    // the row's loads are issued first and stay in flight while the escape
-    // map is built (the barriers only wait for LDS traffic)
-    const uint32_t lane = lane_id();
-    const uint32_t rbase = (tid / 64) * kRow;                  // block-local first element of the row
-    const bool full_row = rbase + kRow <= blen;
-    const uint8_t *nib_base = in + a.off_nib;
-    const uint8_t *sm_base = in + a.off_sm;
-    uint32_t nib[kBf16Chunks];
-    uint2 sm[kBf16Chunks];
-#pragma unroll
-    for (int j = 0; j < kBf16Chunks; ++j) {
-        const uint32_t c = rbase + (j * 64 + lane) * 8;
-        const uint64_t g = e0 + c;
-        if (full_row || c < blen) {
-            nib[j] = load_nt(reinterpret_cast<const uint32_t *>(nib_base + g / 2));
-            sm[j] = load_nt(reinterpret_cast<const uint2 *>(sm_base + g));
-        } else {
-            nib[j] = 0;
-            sm[j] = make_uint2(0, 0);
-        }
-    }
-    const uint64_t r0 = block_escape_offset(in, a, b, blen, e_total, block_offsets, k, status, prefix_part);
-    const bool heavy = k > kMappedEscapes;                        // workgroup-uniform
-    if (heavy) {
-        const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
-        const CodebookRegs cb = {cbw[0], cbw[1], cbw[2], cbw[3]};
-#pragma unroll
-        for (int j = 0; j < kBf16Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 8;
-            if (c < blen) *reinterpret_cast<uint2 *>(plane + c) = lookup_codes8(nib[j], cb);
-        }
-        __syncthreads();
-        overwrite_exponents(esc, r0, k, blen, 256, e_total, plane, status);
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kBf16Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 8;
-            if (c >= blen) continue;
-            const uint2 ex = *reinterpret_cast<const uint2 *>(plane + c);   // exponents, element order
-            uint4 o;
-            o.x = (perm(sm[j].x, sm[j].x, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C010C00u) << 7);
-            o.y = (perm(sm[j].x, sm[j].x, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C030C02u) << 7);
-            o.z = (perm(sm[j].y, sm[j].y, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C050C04u) << 7);
-            o.w = (perm(sm[j].y, sm[j].y, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C070C06u) << 7);
-            const uint64_t g = e0 + c;
-            if (full_row || c + 8 <= blen) {
-                store_nt(reinterpret_cast<uint4 *>(out + g), o);
-            } else {
-                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
-                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
-            }
-        }
-        return;
-    }
-    if (k) {
-        reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
-        load_block_records(esc, r0, k, e_total, rec);
-    }
-    __syncthreads();
-    if (k) map_block_escapes<3>(rec, k, blen, 256, first, status);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kBf16Chunks; ++j) {
-        const uint32_t c = rbase + (j * 64 + lane) * 8;
-        if (c >= blen) continue;
-        uint4 o = decode_chunk_bf16(nib[j], sm[j], table);
-        if (k) {
-            uint32_t r = first[c >> 3];
-            if (r != kNoEscape) {
-                for (; r < k; ++r) {
-                    const uint32_t v = rec[r];
-                    if (((v & 0xFFFFu) >> 3) != (c >> 3)) break;
-                    patch_bf16(o, v & 7, v >> 16);
-                }
-            }
-        }
-        const uint64_t g = e0 + c;
-        if (full_row || c + 8 <= blen) {
-            store_nt(reinterpret_cast<uint4 *>(out + g), o);
-        } else {
-            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
-            for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Decode of the ablation formats (BF16), in the shape of sz_dec_bf16: one
-// 1024-lane workgroup per 64K block, one 4096-element row per wave, eight
-// 8-element chunks per lane, one store per chunk.
+// Decode of the ablation formats (BF16): one 1024-lane workgroup per 64K
+// block, one 4096-element row per wave, eight 8-element chunks per lane, one
+// store per chunk.
 //   Version 2 (Top-8): a chunk's codes are the 3 bytes at 3 * chunk, taken
 //   from two aligned words; a 64-entry LDS table turns each pair of 3-bit
-//   codes into both exponents.  Escapes are position records, patched as in
-//   sz_dec_bf16 (an LDS map for blocks with up to kMappedEscapes records,
-//   the exponent plane above that).
+//   codes into both exponents.  Escapes are position records, patched in
+//   registers before the store through the LDS map of the block's records
+//   (blocks with up to kMappedEscapes records) or through the exponent plane
+//   (blocks with more).
 //   Version 3 (Top-15 + sentinel): nibble codes as in version 1, code 15
 //   marks an escape whose exponent is the next byte of the block's escape
 //   bytes.  Each sentinel's rank inside its block comes from per-chunk
@@ -537,7 +454,6 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_variant(const uint8_t *__r
 {
     __shared__ uint32_t table[256];
     __shared__ uint32_t wave_totals[kDecThreads / 64];
-    __shared__ uint32_t prefix_part[kDecThreads / 64];
     __shared__ __align__(16) uint8_t pool[V == kTop8 ? kBlock : 16];
     uint16_t *first = reinterpret_cast<uint16_t *>(pool);
     uint32_t *rec = reinterpret_cast<uint32_t *>(pool + kBlock / 4);
@@ -577,7 +493,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_variant(const uint8_t *__r
             sm[j] = load_nt(reinterpret_cast<const uint2 *>(in + a.off_sm + g));
         }
     }
-    const uint64_t r0 = block_escape_offset(in, a, b, blen, e_total, block_offsets, k, status, prefix_part);
+    const uint64_t r0 = block_offsets[b];
     const bool heavy = V == kTop8 && k > kMappedEscapes;          // workgroup-uniform
     if (V == kTop15S) {
         // ranks of the sentinels inside the block
@@ -630,7 +546,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_variant(const uint8_t *__r
                                                                    perm(cb1, cb0, spread_codes3x4(code[j] >> 12)));
         }
         __syncthreads();
-        overwrite_exponents(esc, r0, k, blen, 256, e_total, plane, status);
+        overwrite_exponents(esc, r0, 0, k, blen, 256, e_total, plane, 0, kBlock, status);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kBf16Chunks; ++j) {
@@ -692,23 +608,18 @@ __device__ __forceinline__ uint32_t unpack_sm3_x4(uint32_t v12)
     return (v12 & 0x7u) | ((v12 << 5) & 0x700u) | ((v12 << 10) & 0x70000u) | ((v12 << 15) & 0x7000000u);
 }
 
-__device__ __forceinline__ void decode_chunk_e5m2(const uint4 nib, const uint32_t sm3[3],
-                                                  const uint16_t *table, uint32_t o[8])
+// 32 E5M2 values from their packed 3-bit sign/mantissa symbols and their
+// exponents (both in element order).
+__device__ __forceinline__ void assemble_e5m2(const uint32_t sm3[3], const uint2 ex[4], uint32_t o[8])
 {
-    // table[b] = (cb[b & 15] << 2) | (cb[b >> 4] << 10): the exponent fields of
-    // the two elements of code byte b, in place inside two E5M2 bytes
-    const uint32_t nw[4] = {nib.x, nib.y, nib.z, nib.w};
     const uint32_t grp[4] = {sm3[0] & 0xFFFFFFu, (sm3[0] >> 24) | ((sm3[1] & 0xFFFFu) << 8),
                              (sm3[1] >> 16) | ((sm3[2] & 0xFFu) << 16), sm3[2] >> 8};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const uint32_t w = nw[s];
-        const uint32_t e_lo = (uint32_t)table[w & 0xFFu] | ((uint32_t)table[(w >> 8) & 0xFFu] << 16);
-        const uint32_t e_hi = (uint32_t)table[(w >> 16) & 0xFFu] | ((uint32_t)table[w >> 24] << 16);
         const uint32_t t_lo = unpack_sm3_x4(grp[s] & 0xFFFu);
         const uint32_t t_hi = unpack_sm3_x4(grp[s] >> 12);
-        o[2 * s] = ((t_lo & 0x04040404u) << 5) | (t_lo & 0x03030303u) | e_lo;
-        o[2 * s + 1] = ((t_hi & 0x04040404u) << 5) | (t_hi & 0x03030303u) | e_hi;
+        o[2 * s] = ((t_lo & 0x04040404u) << 5) | (t_lo & 0x03030303u) | (ex[s].x << 2);
+        o[2 * s + 1] = ((t_hi & 0x04040404u) << 5) | (t_hi & 0x03030303u) | (ex[s].y << 2);
     }
 }
 
@@ -741,137 +652,300 @@ __device__ __forceinline__ void store_chunk_pairs(uint8_t *row_out, const uint32
     store_nt(reinterpret_cast<uint4 *>(row_out + 1024 + 16 * lane), second_kb);
 }
 
-__global__ __launch_bounds__(kDecThreads) void sz_dec_e5m2(const uint8_t *__restrict__ in, DecodeArgs a,
-                                                           const uint64_t *__restrict__ block_offsets,
-                                                           int32_t *__restrict__ status,
-                                                           uint8_t *__restrict__ out)
+// ---------------------------------------------------------------------------
+// Span decoders (the Top-16 format, every stream size).  Each 64K block is
+// decoded by 256-lane workgroups that own one span of it each: 4096 or 8192
+// elements for BF16 (a lane holding two or four 8-element chunks), 8192 for
+// E5M2 (a lane holding one 32-element chunk).  With 4-16 KB of LDS and few
+// registers, eight of them stay resident per compute unit, so a stream of a
+// few blocks still spreads over all 256 compute units, and no workgroup waits
+// at barriers for sixteen waves.  A workgroup reads its block's escape offset
+// (written by the scan), starts the loads of its escape records, looks the
+// codes up in registers and, when the block has records, parks the span's
+// exponents in an LDS plane, lets its records overwrite them, then rebuilds
+// the values and stores once.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSpanThreads = 256;
+// BF16 streams of more than this many blocks use spans of 8192 elements
+// (four chunks per lane): at 16M elements the 4096-element grid needs two
+// rounds of resident workgroups, and the wide one decodes 16% faster; below
+// that, and for E5M2 at every size, the narrow spans are as fast or faster
+constexpr uint64_t kSpanWideBlocks = 128;
+
+__device__ __forceinline__ uint32_t record_pos(const uint8_t *esc, uint64_t r)
 {
-    __shared__ uint16_t table[256];
-    __shared__ uint32_t prefix_part[kDecThreads / 64];
-    // mapped blocks: first[] (first record of each 32-element chunk, 4 KB) and
-    // rec[] (the records, 32 KB); heavy blocks: the exponent plane (64 KB)
-    __shared__ __align__(16) uint8_t pool[kBlock];
-    uint16_t *first = reinterpret_cast<uint16_t *>(pool);
-    uint32_t *rec = reinterpret_cast<uint32_t *>(pool + kBlock / 16);
-    uint8_t *plane = pool;
-    if (status[1] != 0) return;
-    const uint32_t tid = threadIdx.x;
-    const uint64_t b = blockIdx.x;
-    const uint64_t e0 = b * kBlock;
-    const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
-    uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
-    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
-    const uint8_t *esc = in + a.off_esc;
-    if (tid < 256) {
-        const uint32_t lo = in[32 + (tid & 15)];
-        const uint32_t hi = in[32 + (tid >> 4)];
-        table[tid] = (uint16_t)((lo << 2) | (hi << 10));
+    const uint8_t *p = esc + 3 * r;
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8);
+}
+
+// The escape records of one span workgroup.  The block's span s has the
+// share [k s / D, k (s+1) / D) of its records (D = kBlock / SPAN; the block's
+// last span takes the rest), so the span workgroups of a block together
+// check all k.  Each workgroup reads its share widened by a margin of
+// 64 + k / 64 on both sides (about four standard deviations of where a span's
+// records start when the escapes are spread evenly), checks those records and
+// applies the ones inside its span to the span's exponent plane.  The record
+// just before the window and the one just after it show whether the window
+// holds every record of the span (positions are sorted); if not, the span's
+// records are found by a two-round search (every stride-th record, then the
+// records inside each bound's bracket) and applied as well.  On a malformed
+// block the search may find the wrong range, but it stays inside [0, k),
+// writes stay inside the span, and the windows report the block.
+//
+// issue() starts the loads as soon as the block's offset is known, so they
+// overlap with the data loads: when the window holds at most four records per
+// lane, each lane loads the aligned words of its four records and the record
+// before them, and every lane loads both guard records, all without branches
+// (lanes with nothing to load read the stream header instead).  apply() runs
+// after the dense exponents are in the plane.
+template <uint32_t SPAN>
+struct SpanEscapes {
+    static constexpr uint32_t kLog2D = kLog2Block - __builtin_ctz(SPAN);
+    static_assert((kBlock >> kLog2D) == SPAN && SPAN >= 4096, "span: a power of two of 4096 elements or more");
+
+    const uint8_t *esc;
+    uint64_t r0, e_total;
+    uint32_t k, blen, lo, w0, w1;
+    bool light;                    // one four-record group per lane covers the window
+    bool fast;                     // this lane's group is in the aligned words w
+    uint32_t w[4], prev, g_lo, g_hi;
+
+    __device__ __forceinline__ void issue(const uint8_t *__restrict__ in, uint64_t off_esc, uint64_t r0_, uint32_t k_,
+                                          uint32_t blen_, uint32_t lo_, uint64_t e_total_)
+    {
+        esc = in + off_esc;
+        r0 = r0_;
+        k = k_;
+        blen = blen_;
+        lo = lo_;
+        e_total = e_total_;
+        const uint32_t s = lo / SPAN;
+        const uint32_t margin = 64 + (k >> 6);
+        const uint32_t share_lo = (k * s) >> kLog2D;              // k * s < 2^21
+        const uint32_t share_hi = lo + SPAN >= blen ? k : (k * (s + 1)) >> kLog2D;
+        w0 = share_lo > margin ? share_lo - margin : 0;
+        w1 = std::min(share_hi + margin, k);
+        light = w1 - w0 <= 4 * kSpanThreads;
+        const uint32_t r = w0 + 4 * threadIdx.x;
+        const bool mine = light && r < w1;
+        fast = mine && r0 + r + 5 < e_total;
+        const uint32_t *wp = fast ? reinterpret_cast<const uint32_t *>(esc + ((3 * (r0 + r)) & ~uint64_t(3)))
+                                  : reinterpret_cast<const uint32_t *>(in);
+        w[0] = wp[0];
+        w[1] = wp[1];
+        w[2] = wp[2];
+        w[3] = wp[3];
+        prev = record_pos(esc, r0 + (mine && r > 0 ? r - 1 : 0));
+        g_lo = record_pos(esc, r0 + (w0 > 0 ? w0 - 1 : 0));
+        g_hi = record_pos(esc, r0 + (w1 < k ? w1 : 0));
     }
-    const uint32_t lane = lane_id();
-    const uint32_t rbase = (tid / 64) * kRow;
-    const bool full_row = rbase + kRow <= blen;
-    const uint8_t *nib_base = in + a.off_nib;
-    const uint8_t *sm_base = in + a.off_sm;
-    const uint64_t sm_end = a.off_sm + 3 * ((a.n + 7) / 8);
-    uint4 nib[kE5Chunks];
-    uint32_t sm3[kE5Chunks][3];
+
+    __device__ __forceinline__ void apply(uint8_t *plane, uint32_t symbols, int32_t *__restrict__ status) const
+    {
+        const uint32_t tid = threadIdx.x;
+        const uint32_t hi = lo + SPAN;
+        if (light) {
+            const uint32_t r = w0 + 4 * tid;
+            bool bad = false;
+            if (r < w1) {
+                const uint32_t cnt = std::min<uint32_t>(4, w1 - r);
+                uint32_t pos[4], e[4];
+                if (fast) {
+                    records4_from_words(w, (uint32_t)((3 * (r0 + r)) & 3), pos, e);
+                } else {
 #pragma unroll
-    for (int j = 0; j < kE5Chunks; ++j) {
-        const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
-        const uint64_t g = e0 + c;
-        if (full_row || c + 32 <= blen) {
-            nib[j] = load_nt(reinterpret_cast<const uint4 *>(nib_base + g / 2));
-            load3_nt(reinterpret_cast<const uint32_t *>(sm_base + (g / 32) * 12), sm3[j]);
-        } else if (c < blen) {
-            nib[j] = *reinterpret_cast<const uint4 *>(nib_base + g / 2);
-            sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
-            const uint64_t start = a.off_sm + (g / 32) * 12;
-            for (uint32_t i = 0; i < 12 && start + i < sm_end; ++i)
-                sm3[j][i / 4] |= (uint32_t)in[start + i] << (8 * (i & 3));
-        } else {
-            nib[j] = make_uint4(0, 0, 0, 0);
-            sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
-        }
-    }
-    const uint64_t r0 = block_escape_offset(in, a, b, blen, e_total, block_offsets, k, status, prefix_part);
-    const bool heavy = k > kMappedEscapes;                        // workgroup-uniform
-    if (heavy) {
-        const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
-        const CodebookRegs cb = {cbw[0], cbw[1], cbw[2], cbw[3]};
+                    for (uint32_t q = 0; q < 4; ++q) {
+                        pos[q] = 0xFFFFFFFFu;
+                        e[q] = 0;
+                        if (q < cnt) read_record(esc, r0 + r + q, pos[q], e[q]);
+                    }
+                }
 #pragma unroll
-        for (int j = 0; j < kE5Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
-            if (c >= blen) continue;
-            const uint32_t nw[4] = {nib[j].x, nib[j].y, nib[j].z, nib[j].w};
-#pragma unroll
-            for (int s8 = 0; s8 < 4; ++s8) *reinterpret_cast<uint2 *>(plane + c + 8 * s8) = lookup_codes8(nw[s8], cb);
-        }
-        __syncthreads();
-        overwrite_exponents(esc, r0, k, blen, 32, e_total, plane, status);
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kE5Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
-            if (c >= blen) continue;
-            const uint32_t grp[4] = {sm3[j][0] & 0xFFFFFFu, (sm3[j][0] >> 24) | ((sm3[j][1] & 0xFFFFu) << 8),
-                                     (sm3[j][1] >> 16) | ((sm3[j][2] & 0xFFu) << 16), sm3[j][2] >> 8};
-            uint32_t o[8];
-#pragma unroll
-            for (int s8 = 0; s8 < 4; ++s8) {
-                const uint2 ex = *reinterpret_cast<const uint2 *>(plane + c + 8 * s8);
-                const uint32_t t_lo = unpack_sm3_x4(grp[s8] & 0xFFFu);
-                const uint32_t t_hi = unpack_sm3_x4(grp[s8] >> 12);
-                o[2 * s8] = ((t_lo & 0x04040404u) << 5) | (t_lo & 0x03030303u) | (ex.x << 2);
-                o[2 * s8 + 1] = ((t_hi & 0x04040404u) << 5) | (t_hi & 0x03030303u) | (ex.y << 2);
-            }
-            const uint64_t g = e0 + c;
-            if (full_row) {
-                store_chunk_pairs(out + e0 + rbase + j * 2048, o, lane);
-            } else if (c + 32 <= blen) {
-                store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
-                store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
-            } else {
-                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint8_t)(o[i / 4] >> (8 * (i & 3)));
-            }
-        }
-        return;
-    }
-    if (k) {
-        if (tid < kBlock / 32 / 8) reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
-        load_block_records(esc, r0, k, e_total, rec);
-    }
-    __syncthreads();
-    if (k) map_block_escapes<5>(rec, k, blen, 32, first, status);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kE5Chunks; ++j) {
-        const uint32_t c = rbase + (j * 64 + e5m2_chunk_of_lane(lane)) * 32;
-        if (c >= blen) continue;
-        uint32_t o[8];
-        decode_chunk_e5m2(nib[j], sm3[j], table, o);
-        if (k) {
-            uint32_t r = first[c >> 5];
-            if (r != kNoEscape) {
-                for (; r < k; ++r) {
-                    const uint32_t v = rec[r];
-                    const uint32_t pos = v & 0xFFFFu, e = v >> 16;
-                    if ((pos >> 5) != (c >> 5)) break;
-                    const uint32_t p = pos & 31;
-                    const uint32_t sh = 8 * (p & 3) + 2;
-                    const uint32_t clear = ~(0x1Fu << sh);
-#pragma unroll
-                    for (int w = 0; w < 8; ++w)
-                        if ((uint32_t)w == (p >> 2)) o[w] = (o[w] & clear) | (e << sh);
+                for (uint32_t q = 0; q < 4; ++q) {
+                    if (q >= cnt) continue;
+                    const uint32_t before = q == 0 ? prev : pos[q - 1];
+                    if (pos[q] < blen && e[q] < symbols && (r + q == 0 || pos[q] > before)) {
+                        if (pos[q] - lo < SPAN) plane[pos[q] - lo] = (uint8_t)e[q];
+                    } else {
+                        bad = true;
+                    }
                 }
             }
+            if (bad) atomicExch(status, SZ_E_FORMAT);
+        } else {
+            overwrite_exponents(esc, r0, w0, w1, blen, symbols, e_total, plane, lo, SPAN, status);
         }
+        if (!((w0 > 0 && g_lo >= lo) || (w1 < k && g_hi < hi))) return;      // workgroup-uniform
+        const uint32_t stride = (k + kSpanThreads - 1) / kSpanThreads;         // 1 .. 256
+        const uint32_t p = tid * stride < k ? record_pos(esc, r0 + tid * stride) : 0xFFFFFFFFu;
+        const uint32_t c_lo = __syncthreads_count(p < lo);
+        const uint32_t c_hi = __syncthreads_count(p < hi);
+        // The number of records below x is 0 when no sample is below x
+        // (c = 0), else it lies in ((c - 1) stride, min(c stride, k)]: the
+        // records strictly between those two indices settle it.
+        const uint32_t b_lo = c_lo ? (c_lo - 1) * stride + 1 : 0, e_lo = c_lo ? std::min(c_lo * stride, k) : 0;
+        const uint32_t b_hi = c_hi ? (c_hi - 1) * stride + 1 : 0, e_hi = c_hi ? std::min(c_hi * stride, k) : 0;
+        const uint32_t q_lo = b_lo + tid < e_lo ? record_pos(esc, r0 + b_lo + tid) : 0xFFFFFFFFu;
+        const uint32_t q_hi = b_hi + tid < e_hi ? record_pos(esc, r0 + b_hi + tid) : 0xFFFFFFFFu;
+        const uint32_t first = b_lo + __syncthreads_count(q_lo < lo);
+        const uint32_t last = b_hi + __syncthreads_count(q_hi < hi);
+        overwrite_exponents(esc, r0, first, last, blen, symbols, e_total, plane, lo, SPAN, status);
+    }
+};
+
+template <int CPL>
+__global__ __launch_bounds__(kSpanThreads) void sz_dec_bf16_span(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                                 const uint64_t *__restrict__ block_offsets,
+                                                                 int32_t *__restrict__ status,
+                                                                 uint16_t *__restrict__ out)
+{
+    constexpr uint32_t kSpan = kSpanThreads * 8 * CPL;
+    constexpr uint32_t kSpans = kBlock / kSpan;
+    __shared__ __align__(16) uint8_t plane[kSpan];
+    if (status[1] != 0) return;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t b = blockIdx.x / kSpans;
+    const uint32_t lo = (blockIdx.x % kSpans) * kSpan;            // block-local; the grid keeps lo < blen
+    const uint64_t e0 = b * kBlock;
+    const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
+    const bool full = lo + kSpan <= blen;
+    const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
+    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
+    const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
+    const CodebookRegs cb = {cbw[0], cbw[1], cbw[2], cbw[3]};
+    const uint8_t *nib_base = in + a.off_nib;
+    const uint8_t *sm_base = in + a.off_sm;
+    // chunk j of a lane: span-local element (j kSpanThreads + tid) 8; every
+    // lane loads (lanes past the block's end load the span's first chunk,
+    // unused): no branch around the loads
+    uint32_t nib[CPL];
+    uint2 sm[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t c = lo + (j * kSpanThreads + tid) * 8;
+        const uint64_t g = e0 + (full || c < blen ? c : lo);
+        nib[j] = load_nt(reinterpret_cast<const uint32_t *>(nib_base + g / 2));
+        sm[j] = load_nt(reinterpret_cast<const uint2 *>(sm_base + g));
+    }
+    const uint64_t r0 = block_offsets[b];
+    SpanEscapes<kSpan> records;
+    if (k) records.issue(in, a.off_esc, r0, k, blen, lo, e_total);   // workgroup-uniform
+    uint2 ex[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) ex[j] = lookup_codes8(nib[j], cb);
+    if (k) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) *reinterpret_cast<uint2 *>(plane + (j * kSpanThreads + tid) * 8) = ex[j];
+        __syncthreads();
+        records.apply(plane, 256, status);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) ex[j] = *reinterpret_cast<const uint2 *>(plane + (j * kSpanThreads + tid) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t c = lo + (j * kSpanThreads + tid) * 8;
+        if (!full && c >= blen) continue;
+        const uint4 o = assemble_bf16(sm[j], ex[j]);
         const uint64_t g = e0 + c;
-        if (full_row) {
-            store_chunk_pairs(out + e0 + rbase + j * 2048, o, lane);
+        if (full || c + 8 <= blen) {
+            store_nt(reinterpret_cast<uint4 *>(out + g), o);
+        } else {
+            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+            for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+        }
+    }
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kSpanThreads) void sz_dec_e5m2_span(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                                 const uint64_t *__restrict__ block_offsets,
+                                                                 int32_t *__restrict__ status,
+                                                                 uint8_t *__restrict__ out)
+{
+    constexpr uint32_t kSpan = kSpanThreads * 32 * CPL;
+    constexpr uint32_t kSpans = kBlock / kSpan;
+    constexpr uint32_t kWaves = kSpanThreads / 64;
+    __shared__ __align__(16) uint8_t plane[kSpan];
+    if (status[1] != 0) return;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = lane_id();
+    const uint64_t b = blockIdx.x / kSpans;
+    const uint32_t lo = (blockIdx.x % kSpans) * kSpan;            // block-local; the grid keeps lo < blen
+    const uint64_t e0 = b * kBlock;
+    const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
+    const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
+    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
+    const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
+    const CodebookRegs cb = {cbw[0], cbw[1], cbw[2], cbw[3]};
+    const uint8_t *nib_base = in + a.off_nib;
+    const uint64_t sm_end = a.off_sm + 3 * ((a.n + 7) / 8);
+    // row j of a wave: the 2048 span-local elements at (j kWaves + wave) 2048
+    // (64 chunks, paired for the stores).  Every lane loads, without a branch:
+    // a lane whose chunk is not whole reads the stream header instead (the
+    // only bytes sure to exist: the last chunk's sign/mantissa bytes may end
+    // the stream) and its own bytes below.
+    uint32_t cl[CPL];
+    uint4 nib[CPL];
+    uint32_t sm3[CPL][3];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        cl[j] = (j * kWaves + tid / 64) * 2048 + e5m2_chunk_of_lane(lane) * 32;
+        const uint64_t g = e0 + lo + cl[j];
+        const bool whole = lo + cl[j] + 32 <= blen;
+        nib[j] = load_nt(reinterpret_cast<const uint4 *>(whole ? nib_base + g / 2 : in));
+        load3_nt(reinterpret_cast<const uint32_t *>(whole ? in + a.off_sm + (g / 32) * 12 : in), sm3[j]);
+    }
+    const uint64_t r0 = block_offsets[b];
+    SpanEscapes<kSpan> records;
+    if (k) records.issue(in, a.off_esc, r0, k, blen, lo, e_total);   // workgroup-uniform
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t c = lo + cl[j];
+        if (c < blen && c + 32 > blen) {
+            // the stream's last, partial chunk: its sign/mantissa bytes end at sm_end
+            const uint64_t g = e0 + c;
+            nib[j] = *reinterpret_cast<const uint4 *>(nib_base + g / 2);
+            const uint64_t start = a.off_sm + (g / 32) * 12;
+            sm3[j][0] = sm3[j][1] = sm3[j][2] = 0;
+            for (uint32_t i = 0; i < 12 && start + i < sm_end; ++i)
+                sm3[j][i / 4] |= (uint32_t)in[start + i] << (8 * (i & 3));
+        }
+    }
+    uint2 ex[CPL][4];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        ex[j][0] = lookup_codes8(nib[j].x, cb);
+        ex[j][1] = lookup_codes8(nib[j].y, cb);
+        ex[j][2] = lookup_codes8(nib[j].z, cb);
+        ex[j][3] = lookup_codes8(nib[j].w, cb);
+    }
+    if (k) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int s8 = 0; s8 < 4; ++s8) *reinterpret_cast<uint2 *>(plane + cl[j] + 8 * s8) = ex[j][s8];
+        __syncthreads();
+        records.apply(plane, 32, status);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int s8 = 0; s8 < 4; ++s8) ex[j][s8] = *reinterpret_cast<const uint2 *>(plane + cl[j] + 8 * s8);
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        uint32_t o[8];
+        assemble_e5m2(sm3[j], ex[j], o);
+        const uint32_t wbase = lo + (j * kWaves + tid / 64) * 2048;
+        const uint32_t c = lo + cl[j];
+        const uint64_t g = e0 + c;
+        if (wbase + 2048 <= blen) {
+            store_chunk_pairs(out + e0 + wbase, o, lane);
         } else if (c + 32 <= blen) {
             store_nt(reinterpret_cast<uint4 *>(out + g), make_uint4(o[0], o[1], o[2], o[3]));
             store_nt(reinterpret_cast<uint4 *>(out + g + 16), make_uint4(o[4], o[5], o[6], o[7]));
-        } else {
+        } else if (c < blen) {
             for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint8_t)(o[i / 4] >> (8 * (i & 3)));
         }
     }
@@ -904,11 +978,9 @@ int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype
     a.item = escape_item_bytes(version);
     a.entries = book_entries(version);
     const uint8_t *in = static_cast<const uint8_t *>(d_in);
-    if (g.nb <= kFusedPrefixBlocks) {
-        // the decoders sum the counts before their block themselves
-        block_offsets = nullptr;
-        LaunchScope scope("sz_dec_head", s);
-        hipLaunchKernelGGL(sz_dec_head, dim3(1), dim3(64), 0, s, in, a, status);
+    if (g.nb <= kSmallScanBlocks) {
+        LaunchScope scope("sz_dec_scan_small", s);
+        hipLaunchKernelGGL(sz_dec_scan_small, dim3(1), dim3(64), 0, s, in, a, block_offsets, status);
     } else {
         LaunchScope scope("sz_dec_scan", s);
         hipLaunchKernelGGL(sz_dec_scan, dim3(1), dim3(kScanThreads), 0, s, in, a, block_offsets, status);
@@ -921,14 +993,23 @@ int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype
         LaunchScope scope("sz_dec_top15s", s);
         hipLaunchKernelGGL(sz_dec_variant<kTop15S>, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a,
                            block_offsets, status, static_cast<uint16_t *>(d_out));
-    } else if (g.nb && dtype == SZ_BF16) {
-        LaunchScope scope("sz_dec_bf16", s);
-        hipLaunchKernelGGL(sz_dec_bf16, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, block_offsets,
-                           status, static_cast<uint16_t *>(d_out));
     } else if (g.nb) {
-        LaunchScope scope("sz_dec_e5m2", s);
-        hipLaunchKernelGGL(sz_dec_e5m2, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, block_offsets,
-                           status, static_cast<uint8_t *>(d_out));
+        // a lane holds two or four 8-element chunks (BF16) or one 32-element
+        // chunk (E5M2)
+        if (dtype == SZ_BF16) {
+            const bool wide = g.nb > kSpanWideBlocks;
+            const uint32_t span = kSpanThreads * 8 * (wide ? 4 : 2);
+            const dim3 grid((uint32_t)((g.n + span - 1) / span));
+            uint16_t *out16 = static_cast<uint16_t *>(d_out);
+            LaunchScope scope("sz_dec_bf16_span", s);
+            if (wide) hipLaunchKernelGGL(sz_dec_bf16_span<4>, grid, dim3(kSpanThreads), 0, s, in, a, block_offsets, status, out16);
+            else hipLaunchKernelGGL(sz_dec_bf16_span<2>, grid, dim3(kSpanThreads), 0, s, in, a, block_offsets, status, out16);
+        } else {
+            const uint32_t span = kSpanThreads * 32;
+            LaunchScope scope("sz_dec_e5m2_span", s);
+            hipLaunchKernelGGL(sz_dec_e5m2_span<1>, dim3((uint32_t)((g.n + span - 1) / span)), dim3(kSpanThreads), 0, s,
+                               in, a, block_offsets, status, static_cast<uint8_t *>(d_out));
+        }
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }

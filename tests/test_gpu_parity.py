@@ -77,6 +77,17 @@ def roundtrip_check(bits, dtype, cb):
     return expect
 
 
+# Escape-free 64K blocks put in front of a test case: 0 keeps the stream
+# small (one-wave decode scan, 4096-element BF16 spans), 256 moves it to
+# 8192-element BF16 spans, 1024 past the one-wave scan's 1024 blocks to the
+# one-workgroup scan.
+PAD_BLOCKS = [0, 256, 1024]
+
+
+def _pad_front(bits, pad_blocks, fill):
+    return np.concatenate([np.full(pad_blocks * 65536, fill, dtype=bits.dtype), bits])
+
+
 EDGE_SIZES = [0, 1, 2, 3, 7, 8, 9, 15, 16, 17, 511, 512, 513, 4095, 4096, 4097, 16383, 16384,
               16385, 65535, 65536, 65537, 3 * 65536 + 1003]
 
@@ -174,6 +185,34 @@ def test_single_escapes_at_block_edges():
     assert list(sec["pos"]) == [0, 65535, 0, 7, 65535]
 
 
+@pytest.mark.parametrize("pad_blocks", PAD_BLOCKS)
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_clustered_escapes(dtype, pad_blocks):
+    """Escapes bunched into one run per block (a few hundred to a few thousand
+    records, at a random place, some across span and block edges), so that
+    a span's records are far from where evenly spread escapes would put them."""
+    rng = np.random.default_rng(13)
+    nblk = 6
+    n = nblk * 65536 - 1234
+    if dtype == 0:
+        bits = np.full(n, 0x3F80, dtype=np.uint16)            # exponent 127
+        esc_val = lambda m: (0x0080 | (rng.integers(0, 2, m) << 15) | rng.integers(0, 128, m)).astype(np.uint16)
+        cb = np.array([127] + list(range(100, 115)), dtype=np.uint8)
+    else:
+        bits = np.full(n, 0x3C, dtype=np.uint8)               # exponent 15
+        esc_val = lambda m: (0x04 | (rng.integers(0, 2, m) << 7) | rng.integers(0, 4, m)).astype(np.uint8)
+        cb = np.array([15] + list(range(16, 31)), dtype=np.uint8)
+    for b, m in enumerate([300, 1500, 5000, 9000, 20000, 700]):
+        start = b * 65536 + int(rng.integers(0, 65536 - m))
+        if b == 2:
+            start = 3 * 65536 - m // 2                        # run across a block edge
+        end = min(start + m, n)
+        bits[start:end] = esc_val(end - start)
+    bits = _pad_front(bits, pad_blocks, bits[0])
+    expect = roundtrip_check(bits, dtype, cb)
+    assert streamfmt.header(expect)["escapes"] > 30000
+
+
 def test_no_escapes_single_exponent():
     bits = synth.as_bits_numpy(synth.single_exponent(41, 300000, 127))
     cb = oracle.calibrate(synth.as_bits_numpy(synth.calibration_tensor("kv1m")), 0)
@@ -262,12 +301,14 @@ def _corrupt_cases(stream, n):
     yield "cb_range", lambda t: t.__setitem__(32, 255)          # fine for BF16: stays valid
 
 
-def test_device_validation_matches_oracle():
-    n = 70000
+@pytest.mark.parametrize("pad_blocks", PAD_BLOCKS)
+def test_device_validation_matches_oracle(pad_blocks):
     rng = np.random.default_rng(9)
-    bits = np.full(n, 0x3F80, dtype=np.uint16)
-    idx = np.sort(rng.choice(n - 1, 40, replace=False))
+    bits = np.full(70000, 0x3F80, dtype=np.uint16)
+    idx = np.sort(rng.choice(bits.size - 1, 40, replace=False))
     bits[idx] = 0x0001
+    bits = _pad_front(bits, pad_blocks, 0x3F80)
+    n = bits.size
     cb = np.array([127] + list(range(100, 115)), dtype=np.uint8)
     good = oracle.encode(bits, 0, cb)
     for name, mutate in _corrupt_cases(good, n):
@@ -298,14 +339,16 @@ def test_profile_hooks_record_kernels():
     sz.decode(buf[:size], 0, x.numel())
     stats = sz.profile_collect()
     sz.profile_enable(False)
-    assert stats["sz_enc_dense_bf16"][0] == 1 and stats["sz_dec_bf16"][0] == 1
+    assert stats["sz_enc_dense_bf16"][0] == 1 and stats["sz_dec_bf16_span"][0] == 1
     assert all(ms >= 0 for _, ms in stats.values())
 
 
-def test_e5m2_device_validation():
-    n = 5000
-    bits = np.full(n, 0x3C, dtype=np.uint8)                  # 1.0: exponent 15
+@pytest.mark.parametrize("pad_blocks", PAD_BLOCKS)
+def test_e5m2_device_validation(pad_blocks):
+    bits = np.full(5000, 0x3C, dtype=np.uint8)               # 1.0: exponent 15
     bits[[10, 20, 4000]] = 0x01                              # exponent 0
+    bits = _pad_front(bits, pad_blocks, 0x3C)
+    n = bits.size
     cb = np.array([15] + list(range(1, 15)) + [16], dtype=np.uint8)
     good = oracle.encode(bits, 1, cb)
     first = streamfmt.layout(1, n)["off_esc"]
@@ -319,8 +362,9 @@ def test_e5m2_device_validation():
         assert int(ws[:4].cpu().view(torch.int32)[0]) == want == oracle.E_FORMAT, name
 
 
+@pytest.mark.parametrize("pad_blocks", PAD_BLOCKS)
 @pytest.mark.parametrize("dtype", [0, 1])
-def test_device_validation_heavy_blocks(dtype):
+def test_device_validation_heavy_blocks(dtype, pad_blocks):
     """Malformed records inside blocks with more escapes than the LDS map
     holds (the exponent-plane decode path) are reported like the light ones."""
     n = 65536 + 20000
@@ -331,9 +375,12 @@ def test_device_validation_heavy_blocks(dtype):
     else:
         e = rng.integers(16, 32, n).astype(np.uint8)
         bits = ((rng.integers(0, 2, n).astype(np.uint8) << 7) | (e << 2) | rng.integers(0, 4, n).astype(np.uint8)).astype(np.uint8)
+    # padding value: exponent 1, inside the book [0..15]
+    bits = _pad_front(bits, pad_blocks, 0x0080 if dtype == 0 else 0x04)
+    n = bits.size
     cb = np.arange(16, dtype=np.uint8)
     good = oracle.encode(bits, dtype, cb)
-    assert streamfmt.sections(good)["counts"][0] > 8192
+    assert streamfmt.sections(good)["counts"][pad_blocks] > 8192
     first = streamfmt.layout(dtype, n)["off_esc"]
     second_block = first + 3 * 65536
     cases = [("repeat", lambda t: t.__setitem__(slice(first + 3000, first + 3002), t[first + 2997:first + 2999].copy())),
