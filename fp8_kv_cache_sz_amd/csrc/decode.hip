@@ -199,6 +199,8 @@ constexpr uint32_t kNoEscape = 0xFFFFu;
 // Blocks with up to this many escapes decode through an LDS map of their
 // records; blocks with more go through the exponent plane.
 constexpr uint32_t kMappedEscapes = 8192;
+// four-record windows a lane has in flight when it walks escape records
+constexpr uint32_t kRecordGroups = 2;
 
 // Escape record r of the stream: position and exponent.
 __device__ __forceinline__ void read_record(const uint8_t *esc, uint64_t r, uint32_t &pos, uint32_t &e)
@@ -348,53 +350,54 @@ __device__ __forceinline__ uint4 assemble_bf16(uint2 sm, uint2 ex)
 
 // Checks records i0 .. i1-1 of a block (each against the one before it) and
 // overwrites plane[pos - lo] with the exponent of each whose position lies in
-// [lo, lo + span), four records per aligned three-word window; invalid records
-// (position out of the block or not ascending, exponent out of range) are
-// skipped and reported through the status word.
+// [lo, lo + span); invalid records (position out of the block or not
+// ascending, exponent out of range) are skipped and reported through the
+// status word.  A lane takes 4 G consecutive records per pass, read as G
+// aligned three-word windows issued together, so that a workgroup has G
+// windows per lane in flight at each wait.
+template <uint32_t G>
 __device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ esc, uint64_t r0, uint32_t i0,
                                                     uint32_t i1, uint32_t blen, uint32_t symbols, uint64_t e_total,
                                                     uint8_t *plane, uint32_t lo, uint32_t span,
                                                     int32_t *__restrict__ status)
 {
+    constexpr uint32_t kPer = 4 * G;
     const uint32_t lane = lane_id();
-    const uint32_t step = 4 * blockDim.x;
+    const uint32_t step = kPer * blockDim.x;
     bool bad = false;
-    // the aligned words of a four-record group, loaded one group ahead so that
-    // a load is always in flight while the previous group is applied
-    auto window = [&](uint32_t r, uint32_t (&w)[4]) {
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(esc + ((3 * (r0 + r)) & ~uint64_t(3)));
-        w[0] = p[0];
-        w[1] = p[1];
-        w[2] = p[2];
-        w[3] = p[3];
-    };
-    uint32_t w[4] = {0, 0, 0, 0};
-    uint32_t r = i0 + 4 * threadIdx.x;
-    bool fast = r < i1 && r0 + r + 5 < e_total;
-    if (fast) window(r, w);
-    for (; r < i1; r += step) {
-        uint32_t pos[4], e[4];
-        const uint32_t cnt = std::min<uint32_t>(4, i1 - r);
-        if (fast) {
-            records4_from_words(w, (uint32_t)((3 * (r0 + r)) & 3), pos, e);
+    for (uint32_t r = i0 + kPer * threadIdx.x; r < i1; r += step) {
+        uint32_t pos[kPer], e[kPer];
+        const uint32_t cnt = std::min<uint32_t>(kPer, i1 - r);
+        if (cnt == kPer && r0 + r + kPer + 1 < e_total) {
+            // every window starts at most 3 bytes before its first record and
+            // ends at most 3 bytes after its last: all inside the section
+            uint32_t w[G][4];
+#pragma unroll
+            for (uint32_t g = 0; g < G; ++g) {
+                const uint32_t *p = reinterpret_cast<const uint32_t *>(esc + ((3 * (r0 + r + 4 * g)) & ~uint64_t(3)));
+                w[g][0] = p[0];
+                w[g][1] = p[1];
+                w[g][2] = p[2];
+                w[g][3] = p[3];
+            }
+#pragma unroll
+            for (uint32_t g = 0; g < G; ++g)
+                records4_from_words(w[g], (uint32_t)((3 * (r0 + r + 4 * g)) & 3), pos + 4 * g, e + 4 * g);
         } else {
 #pragma unroll
-            for (uint32_t q = 0; q < 4; ++q) {
+            for (uint32_t q = 0; q < kPer; ++q) {
                 pos[q] = 0xFFFFFFFFu;
                 e[q] = 0;
                 if (q < cnt) read_record(esc, r0 + r + q, pos[q], e[q]);
             }
         }
-        const uint32_t rn = r + step;
-        fast = rn < i1 && r0 + rn + 5 < e_total;
-        if (fast) window(rn, w);
-        uint32_t prev = __shfl_up(pos[3], 1, 64);        // lane l-1 holds records r-4..r-1
+        uint32_t prev = __shfl_up(pos[kPer - 1], 1, 64);   // lane l-1 holds records r-kPer..r-1
         if (lane == 0 && r > 0) {
             uint32_t pe;
             read_record(esc, r0 + r - 1, prev, pe);
         }
 #pragma unroll
-        for (uint32_t q = 0; q < 4; ++q) {
+        for (uint32_t q = 0; q < kPer; ++q) {
             if (q >= cnt) continue;
             const uint32_t before = q == 0 ? prev : pos[q - 1];
             if (pos[q] < blen && e[q] < symbols && (r + q == 0 || pos[q] > before)) {
@@ -546,7 +549,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_variant(const uint8_t *__r
                                                                    perm(cb1, cb0, spread_codes3x4(code[j] >> 12)));
         }
         __syncthreads();
-        overwrite_exponents(esc, r0, 0, k, blen, 256, e_total, plane, 0, kBlock, status);
+        overwrite_exponents<kRecordGroups>(esc, r0, 0, k, blen, 256, e_total, plane, 0, kBlock, status);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kBf16Chunks; ++j) {
@@ -682,9 +685,11 @@ __device__ __forceinline__ uint32_t record_pos(const uint8_t *esc, uint64_t r)
 // share [k s / D, k (s+1) / D) of its records (D = kBlock / SPAN; the block's
 // last span takes the rest), so the span workgroups of a block together
 // check all k.  Each workgroup reads its share widened by a margin of
-// 64 + k / 64 on both sides (about four standard deviations of where a span's
-// records start when the escapes are spread evenly), checks those records and
-// applies the ones inside its span to the span's exponent plane.  The record
+// 64 + min(k / 64, 256) records on both sides, checks those records and
+// applies the ones inside its span to the span's exponent plane.  When the
+// escapes are spread evenly over the block, the number of records before a
+// span start has a standard deviation of at most sqrt(k (1 - k / B)) / 2,
+// which never exceeds 64: the margin covers four of them.  The record
 // just before the window and the one just after it show whether the window
 // holds every record of the span (positions are sorted); if not, the span's
 // records are found by a two-round search (every stride-th record, then the
@@ -720,7 +725,7 @@ struct SpanEscapes {
         lo = lo_;
         e_total = e_total_;
         const uint32_t s = lo / SPAN;
-        const uint32_t margin = 64 + (k >> 6);
+        const uint32_t margin = 64 + std::min<uint32_t>(k >> 6, 256);
         const uint32_t share_lo = (k * s) >> kLog2D;              // k * s < 2^21
         const uint32_t share_hi = lo + SPAN >= blen ? k : (k * (s + 1)) >> kLog2D;
         w0 = share_lo > margin ? share_lo - margin : 0;
@@ -773,7 +778,7 @@ struct SpanEscapes {
             }
             if (bad) atomicExch(status, SZ_E_FORMAT);
         } else {
-            overwrite_exponents(esc, r0, w0, w1, blen, symbols, e_total, plane, lo, SPAN, status);
+            overwrite_exponents<kRecordGroups>(esc, r0, w0, w1, blen, symbols, e_total, plane, lo, SPAN, status);
         }
         if (!((w0 > 0 && g_lo >= lo) || (w1 < k && g_hi < hi))) return;      // workgroup-uniform
         const uint32_t stride = (k + kSpanThreads - 1) / kSpanThreads;         // 1 .. 256
@@ -789,7 +794,7 @@ struct SpanEscapes {
         const uint32_t q_hi = b_hi + tid < e_hi ? record_pos(esc, r0 + b_hi + tid) : 0xFFFFFFFFu;
         const uint32_t first = b_lo + __syncthreads_count(q_lo < lo);
         const uint32_t last = b_hi + __syncthreads_count(q_hi < hi);
-        overwrite_exponents(esc, r0, first, last, blen, symbols, e_total, plane, lo, SPAN, status);
+        overwrite_exponents<kRecordGroups>(esc, r0, first, last, blen, symbols, e_total, plane, lo, SPAN, status);
     }
 };
 
