@@ -285,16 +285,21 @@ constexpr uint32_t kDirectRecords = 32;
 // Tiles with more escapes than this are not staged: the compaction kernel
 // derives their records again from the input, which moves 2 bytes per
 // element instead of writing and re-reading 3 bytes per escape.  Their tile
-// count carries kRederiveFlag.
+// count carries kRederiveFlag.  The smallest streams stage every tile
+// (kStageAll; see sz_enc_compact_small).
 constexpr uint32_t kRederiveRecords = kEncTile / 4;
+constexpr uint32_t kStageAll = 0xFFFFFFFFu;
 constexpr uint32_t kRederiveFlag = 0x80000000u;
 
 // ---------------------------------------------------------------------------
-// Kernel: BF16 dense encode + escape staging.  One 256-lane workgroup per
-// 16K-element tile; wave w streams elements [4096w, 4096w + 4096) of it.  The
+// Kernel: BF16 dense encode + escape staging.  One workgroup per 16K-element
+// tile; a lane holds C 8-element chunks of its wave's row of 512 C elements
+// (C = 8: 256 lanes, wave w streams elements [4096w, 4096w + 4096); small
+// streams use C = 2, 1024 lanes, so that each lane's serial work is a
+// quarter and a tile's loads go out from four times the lanes).  The
 // tile's records are staged in element order in the tile's slot (3 bytes per
 // element); tile_counts[tile] gets their number.  A tile with more than
-// kRederiveRecords escapes stages nothing and is flagged with kRederiveFlag:
+// `rederive_above` escapes stages nothing and is flagged with kRederiveFlag:
 // the compaction kernel derives its records again from the input, which
 // costs less traffic than writing and re-reading them.
 // ---------------------------------------------------------------------------
@@ -321,29 +326,34 @@ __device__ __forceinline__ void put_exponents(uint8_t *tstage, uint32_t rank, ui
     }
 }
 
-template <int V>
-__global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t *__restrict__ in, uint64_t n,
+template <int V, int C = kBf16Chunks>
+__global__ __launch_bounds__(kEncTile / (8 * C)) void sz_enc_dense_bf16(const uint16_t *__restrict__ in, uint64_t n,
                                                               uint8_t *__restrict__ out, uint64_t off_nib,
                                                               uint64_t off_sm, Codebook4 cb,
                                                               const uint32_t *__restrict__ cb_dev,
                                                               uint32_t *__restrict__ tile_counts,
-                                                              uint8_t *__restrict__ stage)
+                                                              uint8_t *__restrict__ stage, uint32_t rederive_above)
 {
+    // C chunks of 8 elements per lane: a wave row is 512 C elements, a tile
+    // 16384 / (512 C) waves
+    constexpr uint32_t kWaves = kEncTile / (512 * C);
+    constexpr uint32_t kRowLen = 512 * C;
+    static_assert(V != kTop8 || C == kBf16Chunks, "the Top-8 code rows are laid out for eight chunks");
     __shared__ uint32_t table32[64];
-    __shared__ uint32_t wave_totals[kEncThreads / 64];
-    __shared__ __align__(16) uint8_t seg_buf[kEncThreads / 64][kSegBytes];
+    __shared__ uint32_t wave_totals[kWaves];
+    __shared__ __align__(16) uint8_t seg_buf[kWaves][kSegBytes];
     // exponents of chunks that hold escapes, parked until the ranks are known
-    __shared__ uint64_t ex_park[kEncThreads / 64][kBf16Chunks][64];
+    __shared__ uint64_t ex_park[kWaves][C][64];
     const uint32_t lane = lane_id();
     const uint32_t wave = threadIdx.x / 64;
     const uint64_t tile = blockIdx.x;
-    const uint64_t base = tile * kEncTile + (uint64_t)wave * kRow;
-    const bool full_row = base + kRow <= n;
+    const uint64_t base = tile * kEncTile + (uint64_t)wave * kRowLen;
+    const bool full_row = base + kRowLen <= n;
 
     // the row's loads are issued first and stay in flight while the table is built
-    uint4 q[kBf16Chunks];
+    uint4 q[C];
 #pragma unroll
-    for (int j = 0; j < kBf16Chunks; ++j) {
+    for (int j = 0; j < C; ++j) {
         const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
         if (full_row || c0 + 8 <= n) {
             q[j] = load_nt(reinterpret_cast<const uint4 *>(in + c0));
@@ -360,10 +370,10 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
     __syncthreads();
     const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
     uint8_t *buf = seg_buf[wave];
-    uint32_t esc[kBf16Chunks];
-    uint32_t cnt[kBf16Chunks];
+    uint32_t esc[C];
+    uint32_t cnt[C];
 #pragma unroll
-    for (int j = 0; j < kBf16Chunks; ++j) {
+    for (int j = 0; j < C; ++j) {
         const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
         uint32_t nib;
         uint2 sm;
@@ -411,16 +421,16 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_bf16(const uint16_t 
         }
         wave_lds_fence();
     }
-    uint32_t row_base[kBf16Chunks], row_total[kBf16Chunks], lane_before[kBf16Chunks];
-    const uint32_t wave_total = wave_chunk_ranks<kBf16Chunks>(cnt, row_base, row_total, lane_before);
+    uint32_t row_base[C], row_total[C], lane_before[C];
+    const uint32_t wave_total = wave_chunk_ranks<C>(cnt, row_base, row_total, lane_before);
     uint32_t tile_total;
-    const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
+    const uint32_t wave_before = workgroup_wave_prefix<kWaves>(wave_total, wave_totals, tile_total);
     // only the Top-16 format re-derives escape-heavy tiles in the compaction
-    const bool rederive = V == kTop16 && tile_total > kRederiveRecords;
+    const bool rederive = V == kTop16 && tile_total > rederive_above;
     if (wave_total && !rederive) {
         uint8_t *tstage = stage + tile * (3ull * kEncTile);
 #pragma unroll
-        for (int j = 0; j < kBf16Chunks; ++j) {
+        for (int j = 0; j < C; ++j) {
             const uint32_t pos0 = (uint32_t)((base + (uint64_t)(j * 64 + lane) * 8) & 0xFFFFu);
             const uint32_t rank = wave_before + row_base[j];
             constexpr uint32_t item = escape_item_bytes(V);
@@ -459,7 +469,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
                                                               Codebook4 cb,
                                                               const uint32_t *__restrict__ cb_dev,
                                                               uint32_t *__restrict__ tile_counts,
-                                                              uint8_t *__restrict__ stage)
+                                                              uint8_t *__restrict__ stage, uint32_t rederive_above)
 {
     __shared__ uint32_t table32[64];
     __shared__ uint32_t table16x2[512];
@@ -536,7 +546,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
     const uint32_t wave_total = wave_chunk_ranks<kE5Chunks>(cnt, row_base, row_total, lane_before);
     uint32_t tile_total;
     const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
-    if (wave_total && tile_total <= kRederiveRecords) {
+    if (wave_total && tile_total <= rederive_above) {
         uint8_t *tstage = stage + tile * (3ull * kEncTile);
         uint8_t *buf = seg_buf[wave];
 #pragma unroll
@@ -585,7 +595,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
             }
         }
     }
-    if (threadIdx.x == 0) tile_counts[tile] = tile_total | (tile_total > kRederiveRecords ? kRederiveFlag : 0u);
+    if (threadIdx.x == 0) tile_counts[tile] = tile_total | (tile_total > rederive_above ? kRederiveFlag : 0u);
 }
 
 struct HeaderArgs {
@@ -1029,6 +1039,108 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(8
                       seg_buf[wave], item);
 }
 
+// ---------------------------------------------------------------------------
+// Kernel: compaction with its own prefix for the smallest streams (up to
+// kSmallCompactBlocks blocks, one layer of a KV cache), in place of
+// sz_enc_compact_fused.  One 1024-lane workgroup per block: its lanes sum the
+// counts of the tiles before the block, and each 256-lane quarter then copies
+// one of the block's four tiles from its staging slot to its place in the
+// stream; the counts, E, the header, the padding and the status word are
+// written as sz_enc_compact_fused writes them.  The dense encoders stage
+// every tile of these streams, escape-heavy ones included, so that copying
+// them takes 1024 lanes per block: a 1M-element stream of random bits encodes
+// in 28 us on MI355X, against 297 us when one wave per block re-derived its
+// tiles.  A flagged tile, which the dense encoders do not produce for these
+// streams, would be re-derived by the first wave of its quarter.  Beyond 16
+// blocks this shape costs more than it saves on ordinary streams (3 us at 4M
+// elements, 11 us at 16M), so larger streams keep sz_enc_compact_fused.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSmallThreads = 1024;
+constexpr uint32_t kSmallGroup = kSmallThreads / kTilesPerBlock;   // lanes per tile
+constexpr uint64_t kSmallCompactBlocks = 16;
+
+template <int DT>
+__global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_compact_small(
+    const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts, uint8_t *__restrict__ out,
+    uint64_t off_esc, uint64_t nt, const void *__restrict__ in, HeaderArgs h, const uint32_t *__restrict__ cb_dev,
+    int32_t *__restrict__ status, uint32_t item)
+{
+    __shared__ uint32_t table32[64];
+    __shared__ __align__(16) uint8_t seg_buf[kTilesPerBlock][kSegBytes];
+    __shared__ uint64_t wave_part[kSmallThreads / 64];
+    const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
+    const uint64_t nb = h.nb;
+    const uint64_t b = blockIdx.x;                              // the grid has max(1, nb) workgroups
+    Codebook4 cb = h.cb;
+    const int32_t verdict = device_codebook_verdict(cb_dev, h.dtype, cb);
+    build_encode_table(table32, cb, DT == SZ_BF16 ? 256 : 32);
+    // escapes of the tiles before this block (a multiple of 4 tiles, all of
+    // them below nt)
+    const uint64_t t0 = kTilesPerBlock * b;
+    uint64_t part = 0;
+#pragma unroll 2
+    for (uint64_t t = 4 * tid; t < t0; t += 4 * kSmallThreads) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(tile_counts + t);
+        part += (uint64_t)(v.x & ~kRederiveFlag) + (v.y & ~kRederiveFlag) + (v.z & ~kRederiveFlag) +
+                (v.w & ~kRederiveFlag);
+    }
+    part = wave_sum_u64(part);
+    if (lane == 0) wave_part[wave] = part;
+    // the block's four tile counts (flag bit included; 0 past the last tile)
+    uint32_t meta[kTilesPerBlock];
+#pragma unroll
+    for (uint32_t t = 0; t < kTilesPerBlock; ++t) meta[t] = b < nb && t0 + t < nt ? tile_counts[t0 + t] : 0u;
+    __syncthreads();
+    uint64_t acc = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kSmallThreads / 64; ++w) acc += wave_part[w];
+    const uint64_t off = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(acc >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)acc);
+    const uint32_t g = tid / kSmallGroup;                     // this quarter's tile
+    uint32_t total = 0, before = 0, k = 0;
+    bool flagged = false;
+#pragma unroll
+    for (uint32_t t = 0; t < kTilesPerBlock; ++t) {
+        const uint32_t c = meta[t] & ~kRederiveFlag;
+        if (t < g) before += c;
+        if (t == g) {
+            k = c;
+            flagged = meta[t] >> 31;
+        }
+        total += c;
+    }
+    uint32_t *header32 = reinterpret_cast<uint32_t *>(out);
+    if (b < nb && tid == 0) {
+        reinterpret_cast<uint32_t *>(out + 64)[b] = total;
+        if (b == nb - 1) {
+            const uint64_t e = off + total;
+            header32[4] = (uint32_t)e;
+            header32[5] = (uint32_t)(e >> 32);
+        }
+    }
+    if (blockIdx.x == 0) write_header(out, h, cb, verdict, nb == 0, status);
+    if (b >= nb || k == 0) return;
+    const uint64_t dst0 = off_esc + item * (off + before);
+    if (flagged) {
+        if (tid % kSmallGroup < 64) {
+            const uint8_t *table = reinterpret_cast<const uint8_t *>(table32);
+            if (DT == SZ_BF16)
+                rederive_tile_bf16(static_cast<const uint16_t *>(in), h.n, t0 + g, table, seg_buf[g],
+                                   out + (dst0 & ~uint64_t(3)), (uint32_t)(dst0 & 3));
+            else
+                rederive_tile_e5m2(static_cast<const uint8_t *>(in), h.n, t0 + g, table, seg_buf[g],
+                                   out + (dst0 & ~uint64_t(3)), (uint32_t)(dst0 & 3));
+        }
+    } else {
+        copy_records(stage + (t0 + g) * (3ull * kEncTile), out, dst0, item * k, tid % kSmallGroup, kSmallGroup);
+    }
+}
+
+// Streams of up to this many tiles (8M elements) use the BF16 dense encoder
+// with two chunks per lane (1024-lane workgroups): on MI355X 1.5 us faster
+// per encode at 1M-4M elements, slower from 16M on.
+constexpr uint64_t kSmallEncodeTiles = 512;
+
 // Encode behind sz_encode (host codebook cb4), sz_encode_devcb (cb_dev) and
 // sz_encode_format (version 2, 3).
 int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems, const Codebook4 &cb4,
@@ -1050,26 +1162,32 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
     uint8_t *stage = ws + w.stage;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
+    // the smallest streams stage every tile (see sz_enc_compact_small)
+    const uint32_t rederive_above = g.nb <= kSmallCompactBlocks ? kStageAll : kRederiveRecords;
     if (g.nt && dtype == SZ_BF16) {
         const uint16_t *in16 = static_cast<const uint16_t *>(d_in);
         if (version == kTop8) {
             LaunchScope scope("sz_enc_dense_top8", s);
             hipLaunchKernelGGL(sz_enc_dense_bf16<kTop8>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16, g.n,
-                               out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage);
+                               out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, rederive_above);
         } else if (version == kTop15S) {
             LaunchScope scope("sz_enc_dense_top15s", s);
             hipLaunchKernelGGL(sz_enc_dense_bf16<kTop15S>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16,
-                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage);
+                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, rederive_above);
+        } else if (g.nt <= kSmallEncodeTiles) {
+            LaunchScope scope("sz_enc_dense_bf16", s);
+            hipLaunchKernelGGL((sz_enc_dense_bf16<kTop16, 2>), dim3((uint32_t)g.nt), dim3(kEncTile / 16), 0, s,
+                               in16, g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, rederive_above);
         } else {
             LaunchScope scope("sz_enc_dense_bf16", s);
             hipLaunchKernelGGL(sz_enc_dense_bf16<kTop16>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16,
-                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage);
+                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, rederive_above);
         }
     } else if (g.nt) {
         LaunchScope scope("sz_enc_dense_e5m2", s);
         hipLaunchKernelGGL(sz_enc_dense_e5m2, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s,
                            static_cast<const uint8_t *>(d_in), g.n, out, g.off_nib, g.off_sm, g.sm_bytes,
-                           cb4, cb_dev, tile_counts, stage);
+                           cb4, cb_dev, tile_counts, stage, rederive_above);
     }
     {
         HeaderArgs h;
@@ -1086,6 +1204,18 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
         h.pad_end[2] = g.off_esc;
         if (g.nt <= kFusedPrefixTiles) {
             // one launch orders the records and writes the header
+            if (g.nb <= kSmallCompactBlocks) {
+                const uint32_t blocks = (uint32_t)std::max<uint64_t>(1, g.nb);
+                LaunchScope scope("sz_enc_compact_small", s);
+                if (dtype == SZ_BF16)
+                    hipLaunchKernelGGL(sz_enc_compact_small<SZ_BF16>, dim3(blocks), dim3(kSmallThreads), 0, s, stage,
+                                       tile_counts, out, g.off_esc, g.nt, d_in, h, cb_dev, status,
+                                       escape_item_bytes(version));
+                else
+                    hipLaunchKernelGGL(sz_enc_compact_small<SZ_FP8_E5M2>, dim3(blocks), dim3(kSmallThreads), 0, s,
+                                       stage, tile_counts, out, g.off_esc, g.nt, d_in, h, cb_dev, status, 3u);
+                return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
+            }
             const uint32_t groups = (uint32_t)std::max<uint64_t>(1, (g.nb + kFusedBlocks - 1) / kFusedBlocks);
             LaunchScope scope("sz_enc_compact_fused", s);
             if (dtype == SZ_BF16)

@@ -173,6 +173,31 @@ def test_every_element_escapes():
     assert streamfmt.header(expect)["escapes"] == n
 
 
+@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("n", [16 * 65536, 40 * 65536 + 1234])
+def test_escape_heavy_compaction_paths(dtype, n):
+    """Random bits (escape-heavy tiles mixed with light ones) at a size that
+    stages every tile (16 blocks) and at one whose compaction re-derives the
+    heavy tiles from the input (40 blocks)."""
+    rng = np.random.default_rng(17)
+    if dtype == 0:
+        bits = rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16)
+        bits[((bits >> 7) & 0xFF) == 0xFF] &= 0x807F             # no NaN/Inf exponent
+        cb = np.arange(120, 136, dtype=np.uint8)
+    else:
+        bits = rng.integers(0, 256, n, dtype=np.uint32).astype(np.uint8)
+        cb = np.arange(8, 24, dtype=np.uint8)
+    # a light stretch: one block of in-book exponents
+    light = slice(65536, 2 * 65536)
+    if dtype == 0:
+        bits[light] = (bits[light] & 0x807F) | (np.uint16(127) << 7)
+    else:
+        bits[light] = (bits[light] & 0x83) | (np.uint8(15) << 2)
+    expect = roundtrip_check(bits, dtype, cb)
+    counts = streamfmt.sections(expect)["counts"]
+    assert counts[1] == 0 and max(counts) > 16384
+
+
 def test_single_escapes_at_block_edges():
     n = 3 * 65536
     bits = np.full(n, 0x3F80, dtype=np.uint16)
