@@ -668,7 +668,6 @@ __device__ __forceinline__ void store_chunk_pairs(uint8_t *row_out, const uint32
 // exponents in an LDS plane, lets its records overwrite them, then rebuilds
 // the values and stores once.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kSpanThreads = 256;
 // BF16 streams of more than this many blocks use spans of 8192 elements
 // (four chunks per lane): at 16M elements the 4096-element grid needs two
 // rounds of resident workgroups, and the wide one decodes 16% faster; below
@@ -703,10 +702,13 @@ __device__ __forceinline__ uint32_t record_pos(const uint8_t *esc, uint64_t r)
 // before them, and every lane loads both guard records, all without branches
 // (lanes with nothing to load read the stream header instead).  apply() runs
 // after the dense exponents are in the plane.
-template <uint32_t SPAN>
+template <uint32_t SPAN, uint32_t T>
 struct SpanEscapes {
     static constexpr uint32_t kLog2D = kLog2Block - __builtin_ctz(SPAN);
-    static_assert((kBlock >> kLog2D) == SPAN && SPAN >= 4096, "span: a power of two of 4096 elements or more");
+    static_assert((kBlock >> kLog2D) == SPAN && SPAN >= 512, "span: a power of two of 512 elements or more");
+    // the search samples 256 records (kSamples per lane) and its brackets
+    // hold fewer than 256
+    static constexpr uint32_t kSamples = T >= 256 ? 1 : 256 / T;
 
     const uint8_t *esc;
     uint64_t r0, e_total;
@@ -730,7 +732,7 @@ struct SpanEscapes {
         const uint32_t share_hi = lo + SPAN >= blen ? k : (k * (s + 1)) >> kLog2D;
         w0 = share_lo > margin ? share_lo - margin : 0;
         w1 = std::min(share_hi + margin, k);
-        light = w1 - w0 <= 4 * kSpanThreads;
+        light = w1 - w0 <= 4 * T;
         const uint32_t r = w0 + 4 * threadIdx.x;
         const bool mine = light && r < w1;
         fast = mine && r0 + r + 5 < e_total;
@@ -781,30 +783,40 @@ struct SpanEscapes {
             overwrite_exponents<kRecordGroups>(esc, r0, w0, w1, blen, symbols, e_total, plane, lo, SPAN, status);
         }
         if (!((w0 > 0 && g_lo >= lo) || (w1 < k && g_hi < hi))) return;      // workgroup-uniform
-        const uint32_t stride = (k + kSpanThreads - 1) / kSpanThreads;         // 1 .. 256
-        const uint32_t p = tid * stride < k ? record_pos(esc, r0 + tid * stride) : 0xFFFFFFFFu;
-        const uint32_t c_lo = __syncthreads_count(p < lo);
-        const uint32_t c_hi = __syncthreads_count(p < hi);
+        const uint32_t stride = (k + kSamples * T - 1) / (kSamples * T);       // 1 .. 256
+        uint32_t c_lo = 0, c_hi = 0;
+#pragma unroll
+        for (uint32_t m = 0; m < kSamples; ++m) {
+            const uint32_t i = (tid + m * T) * stride;
+            const uint32_t p = i < k ? record_pos(esc, r0 + i) : 0xFFFFFFFFu;
+            c_lo += __syncthreads_count(p < lo);
+            c_hi += __syncthreads_count(p < hi);
+        }
         // The number of records below x is 0 when no sample is below x
         // (c = 0), else it lies in ((c - 1) stride, min(c stride, k)]: the
         // records strictly between those two indices settle it.
         const uint32_t b_lo = c_lo ? (c_lo - 1) * stride + 1 : 0, e_lo = c_lo ? std::min(c_lo * stride, k) : 0;
         const uint32_t b_hi = c_hi ? (c_hi - 1) * stride + 1 : 0, e_hi = c_hi ? std::min(c_hi * stride, k) : 0;
-        const uint32_t q_lo = b_lo + tid < e_lo ? record_pos(esc, r0 + b_lo + tid) : 0xFFFFFFFFu;
-        const uint32_t q_hi = b_hi + tid < e_hi ? record_pos(esc, r0 + b_hi + tid) : 0xFFFFFFFFu;
-        const uint32_t first = b_lo + __syncthreads_count(q_lo < lo);
-        const uint32_t last = b_hi + __syncthreads_count(q_hi < hi);
+        uint32_t first = b_lo, last = b_hi;
+#pragma unroll
+        for (uint32_t m = 0; m < kSamples; ++m) {
+            const uint32_t i = tid + m * T;
+            const uint32_t q_lo = b_lo + i < e_lo ? record_pos(esc, r0 + b_lo + i) : 0xFFFFFFFFu;
+            const uint32_t q_hi = b_hi + i < e_hi ? record_pos(esc, r0 + b_hi + i) : 0xFFFFFFFFu;
+            first += __syncthreads_count(q_lo < lo);
+            last += __syncthreads_count(q_hi < hi);
+        }
         overwrite_exponents<kRecordGroups>(esc, r0, first, last, blen, symbols, e_total, plane, lo, SPAN, status);
     }
 };
 
-template <int CPL>
-__global__ __launch_bounds__(kSpanThreads) void sz_dec_bf16_span(const uint8_t *__restrict__ in, DecodeArgs a,
+template <int T, int CPL>
+__global__ __launch_bounds__(T) void sz_dec_bf16_span(const uint8_t *__restrict__ in, DecodeArgs a,
                                                                  const uint64_t *__restrict__ block_offsets,
                                                                  int32_t *__restrict__ status,
                                                                  uint16_t *__restrict__ out)
 {
-    constexpr uint32_t kSpan = kSpanThreads * 8 * CPL;
+    constexpr uint32_t kSpan = T * 8 * CPL;
     constexpr uint32_t kSpans = kBlock / kSpan;
     __shared__ __align__(16) uint8_t plane[kSpan];
     if (status[1] != 0) return;
@@ -820,36 +832,36 @@ __global__ __launch_bounds__(kSpanThreads) void sz_dec_bf16_span(const uint8_t *
     const CodebookRegs cb = {cbw[0], cbw[1], cbw[2], cbw[3]};
     const uint8_t *nib_base = in + a.off_nib;
     const uint8_t *sm_base = in + a.off_sm;
-    // chunk j of a lane: span-local element (j kSpanThreads + tid) 8; every
+    // chunk j of a lane: span-local element (j T + tid) 8; every
     // lane loads (lanes past the block's end load the span's first chunk,
     // unused): no branch around the loads
     uint32_t nib[CPL];
     uint2 sm[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const uint32_t c = lo + (j * kSpanThreads + tid) * 8;
+        const uint32_t c = lo + (j * T + tid) * 8;
         const uint64_t g = e0 + (full || c < blen ? c : lo);
         nib[j] = load_nt(reinterpret_cast<const uint32_t *>(nib_base + g / 2));
         sm[j] = load_nt(reinterpret_cast<const uint2 *>(sm_base + g));
     }
     const uint64_t r0 = block_offsets[b];
-    SpanEscapes<kSpan> records;
+    SpanEscapes<kSpan, T> records;
     if (k) records.issue(in, a.off_esc, r0, k, blen, lo, e_total);   // workgroup-uniform
     uint2 ex[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) ex[j] = lookup_codes8(nib[j], cb);
     if (k) {
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) *reinterpret_cast<uint2 *>(plane + (j * kSpanThreads + tid) * 8) = ex[j];
+        for (int j = 0; j < CPL; ++j) *reinterpret_cast<uint2 *>(plane + (j * T + tid) * 8) = ex[j];
         __syncthreads();
         records.apply(plane, 256, status);
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) ex[j] = *reinterpret_cast<const uint2 *>(plane + (j * kSpanThreads + tid) * 8);
+        for (int j = 0; j < CPL; ++j) ex[j] = *reinterpret_cast<const uint2 *>(plane + (j * T + tid) * 8);
     }
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const uint32_t c = lo + (j * kSpanThreads + tid) * 8;
+        const uint32_t c = lo + (j * T + tid) * 8;
         if (!full && c >= blen) continue;
         const uint4 o = assemble_bf16(sm[j], ex[j]);
         const uint64_t g = e0 + c;
@@ -862,15 +874,15 @@ __global__ __launch_bounds__(kSpanThreads) void sz_dec_bf16_span(const uint8_t *
     }
 }
 
-template <int CPL>
-__global__ __launch_bounds__(kSpanThreads) void sz_dec_e5m2_span(const uint8_t *__restrict__ in, DecodeArgs a,
+template <int T, int CPL>
+__global__ __launch_bounds__(T) void sz_dec_e5m2_span(const uint8_t *__restrict__ in, DecodeArgs a,
                                                                  const uint64_t *__restrict__ block_offsets,
                                                                  int32_t *__restrict__ status,
                                                                  uint8_t *__restrict__ out)
 {
-    constexpr uint32_t kSpan = kSpanThreads * 32 * CPL;
+    constexpr uint32_t kSpan = T * 32 * CPL;
     constexpr uint32_t kSpans = kBlock / kSpan;
-    constexpr uint32_t kWaves = kSpanThreads / 64;
+    constexpr uint32_t kWaves = T / 64;
     __shared__ __align__(16) uint8_t plane[kSpan];
     if (status[1] != 0) return;
     const uint32_t tid = threadIdx.x;
@@ -902,7 +914,7 @@ __global__ __launch_bounds__(kSpanThreads) void sz_dec_e5m2_span(const uint8_t *
         load3_nt(reinterpret_cast<const uint32_t *>(whole ? in + a.off_sm + (g / 32) * 12 : in), sm3[j]);
     }
     const uint64_t r0 = block_offsets[b];
-    SpanEscapes<kSpan> records;
+    SpanEscapes<kSpan, T> records;
     if (k) records.issue(in, a.off_esc, r0, k, blen, lo, e_total);   // workgroup-uniform
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -956,6 +968,28 @@ __global__ __launch_bounds__(kSpanThreads) void sz_dec_e5m2_span(const uint8_t *
     }
 }
 
+// Span decoder shapes: lanes per workgroup and chunks per lane (8 elements
+// each for BF16, 32 for E5M2).  Smaller workgroups with one chunk per lane
+// stream faster in isolation, but as decoders they measured 20-28% slower on
+// MI355X: the per-workgroup offset, record and plane work then weighs more.
+constexpr int kBf16SpanThreads = 256, kBf16SpanChunks = 2;     // up to kSpanWideBlocks blocks
+constexpr int kBf16WideThreads = 256, kBf16WideChunks = 4;     // above
+constexpr int kE5SpanThreads = 256;
+
+template <int T, int CPL, int DT>
+void launch_span(const uint8_t *in, const DecodeArgs &a, const uint64_t *block_offsets, int32_t *status,
+                 void *d_out, hipStream_t s)
+{
+    constexpr uint32_t span = T * CPL * (DT == SZ_BF16 ? 8 : 32);
+    const dim3 grid((uint32_t)((a.n + span - 1) / span));
+    if constexpr (DT == SZ_BF16)
+        hipLaunchKernelGGL((sz_dec_bf16_span<T, CPL>), grid, dim3(T), 0, s, in, a, block_offsets, status,
+                           static_cast<uint16_t *>(d_out));
+    else
+        hipLaunchKernelGGL((sz_dec_e5m2_span<T, CPL>), grid, dim3(T), 0, s, in, a, block_offsets, status,
+                           static_cast<uint8_t *>(d_out));
+}
+
 int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
                 void *d_ws, uint64_t ws_bytes, void *stream)
 {
@@ -998,23 +1032,15 @@ int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype
         LaunchScope scope("sz_dec_top15s", s);
         hipLaunchKernelGGL(sz_dec_variant<kTop15S>, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a,
                            block_offsets, status, static_cast<uint16_t *>(d_out));
+    } else if (g.nb && dtype == SZ_BF16) {
+        LaunchScope scope("sz_dec_bf16_span", s);
+        if (g.nb > kSpanWideBlocks)
+            launch_span<kBf16WideThreads, kBf16WideChunks, SZ_BF16>(in, a, block_offsets, status, d_out, s);
+        else
+            launch_span<kBf16SpanThreads, kBf16SpanChunks, SZ_BF16>(in, a, block_offsets, status, d_out, s);
     } else if (g.nb) {
-        // a lane holds two or four 8-element chunks (BF16) or one 32-element
-        // chunk (E5M2)
-        if (dtype == SZ_BF16) {
-            const bool wide = g.nb > kSpanWideBlocks;
-            const uint32_t span = kSpanThreads * 8 * (wide ? 4 : 2);
-            const dim3 grid((uint32_t)((g.n + span - 1) / span));
-            uint16_t *out16 = static_cast<uint16_t *>(d_out);
-            LaunchScope scope("sz_dec_bf16_span", s);
-            if (wide) hipLaunchKernelGGL(sz_dec_bf16_span<4>, grid, dim3(kSpanThreads), 0, s, in, a, block_offsets, status, out16);
-            else hipLaunchKernelGGL(sz_dec_bf16_span<2>, grid, dim3(kSpanThreads), 0, s, in, a, block_offsets, status, out16);
-        } else {
-            const uint32_t span = kSpanThreads * 32;
-            LaunchScope scope("sz_dec_e5m2_span", s);
-            hipLaunchKernelGGL(sz_dec_e5m2_span<1>, dim3((uint32_t)((g.n + span - 1) / span)), dim3(kSpanThreads), 0, s,
-                               in, a, block_offsets, status, static_cast<uint8_t *>(d_out));
-        }
+        LaunchScope scope("sz_dec_e5m2_span", s);
+        launch_span<kE5SpanThreads, 1, SZ_FP8_E5M2>(in, a, block_offsets, status, d_out, s);
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }
