@@ -87,11 +87,11 @@ def load_traffic(kernel: str, workload: str):
     return entry.get("bytes_per_launch")
 
 
-# kernel template instances -> the names the library's instrumentation uses
+# kernel templates, by their first template argument -> the names the
+# library's instrumentation uses
 LAUNCH_NAMES = {
     "sz_enc_dense_bf16<1>": "sz_enc_dense_bf16", "sz_enc_dense_bf16<2>": "sz_enc_dense_top8",
-    "sz_enc_dense_bf16<3>": "sz_enc_dense_top15s", "sz_dec_variant<2>": "sz_dec_top8",
-    "sz_dec_variant<3>": "sz_dec_top15s", "sz_enc_compact<0>": "sz_enc_compact",
+    "sz_enc_dense_bf16<3>": "sz_enc_dense_top15s", "sz_enc_compact<0>": "sz_enc_compact",
     "sz_enc_compact<1>": "sz_enc_compact", "sz_cal_hist<0>": "sz_cal_hist_bf16",
     "sz_cal_hist<1>": "sz_cal_hist_e5m2", "sz_cal_select<0>": "sz_cal_select",
     "sz_cal_select<1>": "sz_cal_select",
@@ -105,7 +105,9 @@ def short_kernel_name(name: str) -> str:
     if name.startswith("void "):
         name = name[5:]
     name = name.strip().split("::")[-1]
-    return LAUNCH_NAMES.get(name, name.split("<")[0])
+    base = name.split("<")[0]
+    first = name[len(base) + 1:].split(",")[0].rstrip(">").strip() if "<" in name else ""
+    return LAUNCH_NAMES.get("%s<%s>" % (base, first), base)
 
 
 def _pmc_per_kernel(csv_path, counter):

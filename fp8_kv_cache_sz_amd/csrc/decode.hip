@@ -188,17 +188,8 @@ __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__res
 }
 
 // ---------------------------------------------------------------------------
-// Escape records, code lookup and value assembly shared by the decoders.  The
-// block-wide pieces (an LDS map from each chunk to the first escape record
-// inside it, built from all of a block's records while checking their order
-// and range) serve the ablation decoders, which give a 64K block to one
-// 1024-lane workgroup.
+// Escape records, code lookup and value assembly shared by the decoders.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kNoEscape = 0xFFFFu;
-
-// Blocks with up to this many escapes decode through an LDS map of their
-// records; blocks with more go through the exponent plane.
-constexpr uint32_t kMappedEscapes = 8192;
 // four-record windows a lane has in flight when it walks escape records
 constexpr uint32_t kRecordGroups = 2;
 
@@ -228,92 +219,6 @@ __device__ __forceinline__ void records4_from_words(const uint32_t (&w)[4], uint
     e[3] = d2 >> 24;
 }
 
-// Four consecutive records from one 16-byte window of aligned words.  The
-// window never leaves the record section: it starts at most 3 bytes before
-// record R and ends at most 3 bytes after record R+3, and callers use it only
-// while a whole record group past R+3 remains in the stream (otherwise they
-// read the records byte by byte).
-__device__ __forceinline__ void read_records4(const uint8_t *esc, uint64_t r, uint32_t pos[4], uint32_t e[4])
-{
-    const uint64_t byte0 = 3 * r;
-    const uint32_t *p = reinterpret_cast<const uint32_t *>(esc + (byte0 & ~uint64_t(3)));
-    const uint32_t w[4] = {p[0], p[1], p[2], p[3]};
-    records4_from_words(w, (uint32_t)(byte0 & 3), pos, e);
-}
-
-// Loads the k (<= kMappedEscapes) records of a block into LDS as
-// pos | exponent << 16, four records per aligned three-word window where the
-// window stays inside the record section, one by one at its end.
-__device__ __forceinline__ void load_block_records(const uint8_t *esc, uint64_t r0, uint32_t k, uint64_t e_total,
-                                                   uint32_t *rec)
-{
-    for (uint32_t r = 4 * threadIdx.x; r < k; r += 4 * blockDim.x) {
-        uint32_t pos[4], e[4];
-        if (r0 + r + 5 < e_total) {
-            read_records4(esc, r0 + r, pos, e);
-        } else {
-#pragma unroll
-            for (uint32_t q = 0; q < 4; ++q) {
-                pos[q] = e[q] = 0;
-                if (r + q < k) read_record(esc, r0 + r + q, pos[q], e[q]);
-            }
-        }
-#pragma unroll
-        for (uint32_t q = 0; q < 4; ++q)
-            if (r + q < k) rec[r + q] = pos[q] | (e[q] << 16);
-    }
-}
-
-// Builds first[chunk] for the k records of a block held in LDS (chunk =
-// pos >> log2_chunk) and reports malformed records through the status word.
-template <int LOG2_CHUNK>
-__device__ __forceinline__ void map_block_escapes(const uint32_t *rec, uint32_t k, uint32_t blen, uint32_t symbols,
-                                                  uint16_t *first, int32_t *status)
-{
-    bool bad = false;
-    for (uint32_t r = threadIdx.x; r < k; r += blockDim.x) {
-        const uint32_t v = rec[r];
-        const uint32_t pos = v & 0xFFFFu;
-        const int32_t prev = r > 0 ? (int32_t)(rec[r - 1] & 0xFFFFu) : -1;
-        if (pos >= blen || (int32_t)pos <= prev || (v >> 16) >= symbols) {
-            bad = true;
-            continue;
-        }
-        if (r == 0 || (uint32_t)(prev >> LOG2_CHUNK) != (pos >> LOG2_CHUNK)) first[pos >> LOG2_CHUNK] = (uint16_t)r;
-    }
-    if (bad) atomicExch(status, SZ_E_FORMAT);
-}
-
-__device__ __forceinline__ uint4 decode_chunk_bf16(uint32_t nib, uint2 sm, const uint32_t *table)
-{
-    // table[b] = cb[b & 15] << 7 | cb[b >> 4] << 23: both exponents of a
-    // code byte, already in place for two packed BF16 values
-    uint4 o;
-    o.x = (perm(sm.x, sm.x, 0x01010000u) & 0x807F807Fu) | table[nib & 0xFFu];
-    o.y = (perm(sm.x, sm.x, 0x03030202u) & 0x807F807Fu) | table[(nib >> 8) & 0xFFu];
-    o.z = (perm(sm.y, sm.y, 0x01010000u) & 0x807F807Fu) | table[(nib >> 16) & 0xFFu];
-    o.w = (perm(sm.y, sm.y, 0x03030202u) & 0x807F807Fu) | table[nib >> 24];
-    return o;
-}
-
-__device__ __forceinline__ void patch_bf16(uint4 &o, uint32_t k, uint32_t e)
-{
-    const uint32_t sh = 7 + 16 * (k & 1);
-    const uint32_t clear = ~(0xFFu << sh);
-    const uint32_t set = e << sh;
-    switch (k >> 1) {
-    case 0: o.x = (o.x & clear) | set; break;
-    case 1: o.y = (o.y & clear) | set; break;
-    case 2: o.z = (o.z & clear) | set; break;
-    default: o.w = (o.w & clear) | set; break;
-    }
-}
-
-// Blocks with more than kMappedEscapes escapes decode through an exponent
-// plane: every element's dense exponent goes to a 64 KB LDS byte array, the
-// block's records overwrite their entries (validated on the way), and the
-// values are rebuilt from the plane and stored once.
-
 // Register code -> exponent lookup for the eight codes of a code word d
 // (element 2k in the low nibble of byte k); cb0..cb3 = codebook bytes.
 // v_perm_b32 indexes eight bytes, so each half of the book is one v_perm and
@@ -335,6 +240,14 @@ __device__ __forceinline__ uint2 lookup_codes8(uint32_t d, const CodebookRegs &c
     const uint32_t e_odd = (perm(cb.w3, cb.w2, sel_o) & m_o) | (perm(cb.w1, cb.w0, sel_o) & ~m_o);
     return make_uint2(perm(e_odd, e_even, 0x05010400u), perm(e_odd, e_even, 0x07030602u));
 }
+
+// Four 3-bit Top-8 codes (12 bits) -> one code per byte, as v_perm selectors
+// over the first eight codebook bytes.
+__device__ __forceinline__ uint32_t spread_codes3x4(uint32_t x)
+{
+    return (x & 7u) | ((x << 5) & 0x700u) | ((x << 10) & 0x70000u) | ((x << 15) & 0x7000000u);
+}
+
 
 // Eight BF16 values from their sign/mantissa bytes and their exponents
 // (both in element order).
@@ -411,69 +324,61 @@ __device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Decode of the ablation formats (BF16): one 1024-lane workgroup per 64K
-// block, one 4096-element row per wave, eight 8-element chunks per lane, one
-// store per chunk.
-//   Version 2 (Top-8): a chunk's codes are the 3 bytes at 3 * chunk, taken
-//   from two aligned words; a 64-entry LDS table turns each pair of 3-bit
-//   codes into both exponents.  Escapes are position records, patched in
-//   registers before the store through the LDS map of the block's records
-//   (blocks with up to kMappedEscapes records) or through the exponent plane
-//   (blocks with more).
-//   Version 3 (Top-15 + sentinel): nibble codes as in version 1, code 15
-//   marks an escape whose exponent is the next byte of the block's escape
-//   bytes.  Each sentinel's rank inside its block comes from per-chunk
-//   counts, a wave prefix sum and a prefix over the waves; the block's
-//   sentinels must number exactly its count.
+// Top-15 + sentinel ablation decode (BF16): nibble codes as in the Top-16
+// format, code 15 marks an escape whose exponent is the next byte of the
+// block's escape bytes.  One 1024-lane workgroup per 64K block, one
+// 4096-element row per wave, eight 8-element chunks per lane.  Each
+// sentinel's rank inside its block comes from per-chunk counts, a wave prefix
+// sum and a prefix over the waves; the block's sentinels must number exactly
+// its count.  (The Top-8 ablation carries position records and decodes
+// through the span decoder.)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint4 decode_chunk_top8(uint32_t code24, uint2 sm, const uint32_t *table64)
+__device__ __forceinline__ uint4 decode_chunk_bf16(uint32_t nib, uint2 sm, const uint32_t *table)
 {
-    // table64[p] = cb[p & 7] << 7 | cb[p >> 3] << 23 for a pair p of 3-bit codes
+    // table[b] = cb[b & 15] << 7 | cb[b >> 4] << 23: both exponents of a
+    // code byte, already in place for two packed BF16 values
     uint4 o;
-    o.x = (perm(sm.x, sm.x, 0x01010000u) & 0x807F807Fu) | table64[code24 & 63u];
-    o.y = (perm(sm.x, sm.x, 0x03030202u) & 0x807F807Fu) | table64[(code24 >> 6) & 63u];
-    o.z = (perm(sm.y, sm.y, 0x01010000u) & 0x807F807Fu) | table64[(code24 >> 12) & 63u];
-    o.w = (perm(sm.y, sm.y, 0x03030202u) & 0x807F807Fu) | table64[(code24 >> 18) & 63u];
+    o.x = (perm(sm.x, sm.x, 0x01010000u) & 0x807F807Fu) | table[nib & 0xFFu];
+    o.y = (perm(sm.x, sm.x, 0x03030202u) & 0x807F807Fu) | table[(nib >> 8) & 0xFFu];
+    o.z = (perm(sm.y, sm.y, 0x01010000u) & 0x807F807Fu) | table[(nib >> 16) & 0xFFu];
+    o.w = (perm(sm.y, sm.y, 0x03030202u) & 0x807F807Fu) | table[nib >> 24];
     return o;
 }
 
-// Four 3-bit codes (12 bits) -> one code per byte, as v_perm selectors.
-__device__ __forceinline__ uint32_t spread_codes3x4(uint32_t x)
+__device__ __forceinline__ void patch_bf16(uint4 &o, uint32_t k, uint32_t e)
 {
-    return (x & 7u) | ((x << 5) & 0x700u) | ((x << 10) & 0x70000u) | ((x << 15) & 0x7000000u);
+    const uint32_t sh = 7 + 16 * (k & 1);
+    const uint32_t clear = ~(0xFFu << sh);
+    const uint32_t set = e << sh;
+    switch (k >> 1) {
+    case 0: o.x = (o.x & clear) | set; break;
+    case 1: o.y = (o.y & clear) | set; break;
+    case 2: o.z = (o.z & clear) | set; break;
+    default: o.w = (o.w & clear) | set; break;
+    }
 }
 
-// Nibbles equal to 15 (the version 3 sentinel): bit 4k set for element k.
+// Nibbles equal to 15 (the sentinel): bit 4k set for element k.
 __device__ __forceinline__ uint32_t sentinel_bits(uint32_t nib)
 {
     return nib & (nib >> 1) & (nib >> 2) & (nib >> 3) & 0x11111111u;
 }
 
-template <int V>
-__global__ __launch_bounds__(kDecThreads) void sz_dec_variant(const uint8_t *__restrict__ in, DecodeArgs a,
-                                                              const uint64_t *__restrict__ block_offsets,
-                                                              int32_t *__restrict__ status,
-                                                              uint16_t *__restrict__ out)
+__global__ __launch_bounds__(kDecThreads) void sz_dec_top15s(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                             const uint64_t *__restrict__ block_offsets,
+                                                             int32_t *__restrict__ status,
+                                                             uint16_t *__restrict__ out)
 {
     __shared__ uint32_t table[256];
     __shared__ uint32_t wave_totals[kDecThreads / 64];
-    __shared__ __align__(16) uint8_t pool[V == kTop8 ? kBlock : 16];
-    uint16_t *first = reinterpret_cast<uint16_t *>(pool);
-    uint32_t *rec = reinterpret_cast<uint32_t *>(pool + kBlock / 4);
-    uint8_t *plane = pool;
     if (status[1] != 0) return;
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x;
     const uint64_t e0 = b * kBlock;
     const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
-    uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
-    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
+    const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
     const uint8_t *esc = in + a.off_esc;
-    if (V == kTop8) {
-        if (tid < 64) table[tid] = ((uint32_t)in[32 + (tid & 7)] << 7) | ((uint32_t)in[32 + (tid >> 3)] << 23);
-    } else if (tid < 256) {
-        table[tid] = ((uint32_t)in[32 + (tid & 15)] << 7) | ((uint32_t)in[32 + (tid >> 4)] << 23);
-    }
+    if (tid < 256) table[tid] = ((uint32_t)in[32 + (tid & 15)] << 7) | ((uint32_t)in[32 + (tid >> 4)] << 23);
     const uint32_t lane = lane_id();
     const uint32_t rbase = (tid / 64) * kRow;
     const bool full_row = rbase + kRow <= blen;
@@ -486,112 +391,36 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_variant(const uint8_t *__r
         code[j] = 0;
         sm[j] = make_uint2(0, 0);
         if (full_row || c < blen) {
-            if (V == kTop8) {
-                const uint64_t byte0 = 3 * (g / 8);
-                const uint32_t *w = reinterpret_cast<const uint32_t *>(in + a.off_nib + (byte0 & ~uint64_t(3)));
-                code[j] = __builtin_amdgcn_alignbit(w[1], w[0], 8 * (uint32_t)(byte0 & 3)) & 0xFFFFFFu;
-            } else {
-                code[j] = load_nt(reinterpret_cast<const uint32_t *>(in + a.off_nib + g / 2));
-            }
+            code[j] = load_nt(reinterpret_cast<const uint32_t *>(in + a.off_nib + g / 2));
             sm[j] = load_nt(reinterpret_cast<const uint2 *>(in + a.off_sm + g));
         }
     }
     const uint64_t r0 = block_offsets[b];
-    const bool heavy = V == kTop8 && k > kMappedEscapes;          // workgroup-uniform
-    if (V == kTop15S) {
-        // ranks of the sentinels inside the block
-        uint32_t sbits[kBf16Chunks], cnt[kBf16Chunks];
+    uint32_t sbits[kBf16Chunks], cnt[kBf16Chunks];
 #pragma unroll
-        for (int j = 0; j < kBf16Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 8;
-            sbits[j] = sentinel_bits(code[j]);
-            if (c >= blen) sbits[j] = 0;
-            else if (c + 8 > blen) sbits[j] &= (1u << (4 * (blen - c))) - 1;   // padding nibbles do not count
-            cnt[j] = __popc(sbits[j]);
-        }
-        uint32_t row_base[kBf16Chunks], row_total[kBf16Chunks], lane_before[kBf16Chunks];
-        const uint32_t wave_total = wave_chunk_ranks<kBf16Chunks>(cnt, row_base, row_total, lane_before);
-        uint32_t block_total;
-        const uint32_t wave_before = workgroup_wave_prefix<kDecThreads / 64>(wave_total, wave_totals, block_total);
-        bool bad = block_total != k;
-#pragma unroll
-        for (int j = 0; j < kBf16Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 8;
-            if (c >= blen) continue;
-            uint4 o = decode_chunk_bf16(code[j], sm[j], table);
-            uint32_t rank = wave_before + row_base[j] + lane_before[j];
-            for (uint32_t m = sbits[j]; m; m &= m - 1, ++rank) {
-                uint32_t e = 0;
-                if (rank < k) e = esc[r0 + rank];
-                else bad = true;
-                patch_bf16(o, (uint32_t)__builtin_ctz(m) / 4, e);
-            }
-            const uint64_t g = e0 + c;
-            if (full_row || c + 8 <= blen) {
-                store_nt(reinterpret_cast<uint4 *>(out + g), o);
-            } else {
-                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
-                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
-            }
-        }
-        if (bad) atomicExch(status, SZ_E_FORMAT);
-        return;
+    for (int j = 0; j < kBf16Chunks; ++j) {
+        const uint32_t c = rbase + (j * 64 + lane) * 8;
+        sbits[j] = sentinel_bits(code[j]);
+        if (c >= blen) sbits[j] = 0;
+        else if (c + 8 > blen) sbits[j] &= (1u << (4 * (blen - c))) - 1;   // padding nibbles do not count
+        cnt[j] = __popc(sbits[j]);
     }
-    // version 2: position records
-    if (heavy) {
-        const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
-        const uint32_t cb0 = cbw[0], cb1 = cbw[1];
-#pragma unroll
-        for (int j = 0; j < kBf16Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 8;
-            if (c < blen)
-                *reinterpret_cast<uint2 *>(plane + c) = make_uint2(perm(cb1, cb0, spread_codes3x4(code[j] & 0xFFFu)),
-                                                                   perm(cb1, cb0, spread_codes3x4(code[j] >> 12)));
-        }
-        __syncthreads();
-        overwrite_exponents<kRecordGroups>(esc, r0, 0, k, blen, 256, e_total, plane, 0, kBlock, status);
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kBf16Chunks; ++j) {
-            const uint32_t c = rbase + (j * 64 + lane) * 8;
-            if (c >= blen) continue;
-            const uint2 ex = *reinterpret_cast<const uint2 *>(plane + c);
-            uint4 o;
-            o.x = (perm(sm[j].x, sm[j].x, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C010C00u) << 7);
-            o.y = (perm(sm[j].x, sm[j].x, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C030C02u) << 7);
-            o.z = (perm(sm[j].y, sm[j].y, 0x01010000u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C050C04u) << 7);
-            o.w = (perm(sm[j].y, sm[j].y, 0x03030202u) & 0x807F807Fu) | (perm(ex.y, ex.x, 0x0C070C06u) << 7);
-            const uint64_t g = e0 + c;
-            if (full_row || c + 8 <= blen) {
-                store_nt(reinterpret_cast<uint4 *>(out + g), o);
-            } else {
-                const uint32_t w[4] = {o.x, o.y, o.z, o.w};
-                for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
-            }
-        }
-        return;
-    }
-    if (k) {
-        reinterpret_cast<uint4 *>(first)[tid] = make_uint4(~0u, ~0u, ~0u, ~0u);
-        load_block_records(esc, r0, k, e_total, rec);
-    }
-    __syncthreads();
-    if (k) map_block_escapes<3>(rec, k, blen, 256, first, status);
-    __syncthreads();
+    uint32_t row_base[kBf16Chunks], row_total[kBf16Chunks], lane_before[kBf16Chunks];
+    const uint32_t wave_total = wave_chunk_ranks<kBf16Chunks>(cnt, row_base, row_total, lane_before);
+    uint32_t block_total;
+    const uint32_t wave_before = workgroup_wave_prefix<kDecThreads / 64>(wave_total, wave_totals, block_total);
+    bool bad = block_total != k;
 #pragma unroll
     for (int j = 0; j < kBf16Chunks; ++j) {
         const uint32_t c = rbase + (j * 64 + lane) * 8;
         if (c >= blen) continue;
-        uint4 o = decode_chunk_top8(code[j], sm[j], table);
-        if (k) {
-            uint32_t r = first[c >> 3];
-            if (r != kNoEscape) {
-                for (; r < k; ++r) {
-                    const uint32_t v = rec[r];
-                    if (((v & 0xFFFFu) >> 3) != (c >> 3)) break;
-                    patch_bf16(o, v & 7, v >> 16);
-                }
-            }
+        uint4 o = decode_chunk_bf16(code[j], sm[j], table);
+        uint32_t rank = wave_before + row_base[j] + lane_before[j];
+        for (uint32_t m = sbits[j]; m; m &= m - 1, ++rank) {
+            uint32_t e = 0;
+            if (rank < k) e = esc[r0 + rank];
+            else bad = true;
+            patch_bf16(o, (uint32_t)__builtin_ctz(m) / 4, e);
         }
         const uint64_t g = e0 + c;
         if (full_row || c + 8 <= blen) {
@@ -601,6 +430,7 @@ __global__ __launch_bounds__(kDecThreads) void sz_dec_variant(const uint8_t *__r
             for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
         }
     }
+    if (bad) atomicExch(status, SZ_E_FORMAT);
 }
 
 // FP8 E5M2 decode: a lane decodes two 32-element chunks (16 code bytes + 12
@@ -810,11 +640,14 @@ struct SpanEscapes {
     }
 };
 
-template <int T, int CPL>
-__global__ __launch_bounds__(T) void sz_dec_bf16_span(const uint8_t *__restrict__ in, DecodeArgs a,
-                                                                 const uint64_t *__restrict__ block_offsets,
-                                                                 int32_t *__restrict__ status,
-                                                                 uint16_t *__restrict__ out)
+// BF16 span decode of format V: Top-16 (nibble codes) or Top-8 (3-bit codes,
+// the 3 bytes at 3 * chunk, taken from two aligned words; one v_perm over
+// the eight book bytes turns four codes into exponents).  Both carry
+// position records.
+template <int T, int CPL, int V>
+__device__ __forceinline__ void bf16_span_decode(const uint8_t *__restrict__ in, const DecodeArgs &a,
+                                                 const uint64_t *__restrict__ block_offsets,
+                                                 int32_t *__restrict__ status, uint16_t *__restrict__ out)
 {
     constexpr uint32_t kSpan = T * 8 * CPL;
     constexpr uint32_t kSpans = kBlock / kSpan;
@@ -835,13 +668,21 @@ __global__ __launch_bounds__(T) void sz_dec_bf16_span(const uint8_t *__restrict_
     // chunk j of a lane: span-local element (j T + tid) 8; every
     // lane loads (lanes past the block's end load the span's first chunk,
     // unused): no branch around the loads
-    uint32_t nib[CPL];
+    uint32_t code[CPL];
     uint2 sm[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const uint32_t c = lo + (j * T + tid) * 8;
         const uint64_t g = e0 + (full || c < blen ? c : lo);
-        nib[j] = load_nt(reinterpret_cast<const uint32_t *>(nib_base + g / 2));
+        if constexpr (V == kTop8) {
+            // the chunk's 3 code bytes; the second word ends at most 5 bytes
+            // past them, inside the stream (the sign/mantissa section follows)
+            const uint64_t byte0 = 3 * (g / 8);
+            const uint32_t *w = reinterpret_cast<const uint32_t *>(nib_base + (byte0 & ~uint64_t(3)));
+            code[j] = __builtin_amdgcn_alignbit(w[1], w[0], 8 * (uint32_t)(byte0 & 3)) & 0xFFFFFFu;
+        } else {
+            code[j] = load_nt(reinterpret_cast<const uint32_t *>(nib_base + g / 2));
+        }
         sm[j] = load_nt(reinterpret_cast<const uint2 *>(sm_base + g));
     }
     const uint64_t r0 = block_offsets[b];
@@ -849,7 +690,13 @@ __global__ __launch_bounds__(T) void sz_dec_bf16_span(const uint8_t *__restrict_
     if (k) records.issue(in, a.off_esc, r0, k, blen, lo, e_total);   // workgroup-uniform
     uint2 ex[CPL];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) ex[j] = lookup_codes8(nib[j], cb);
+    for (int j = 0; j < CPL; ++j) {
+        if constexpr (V == kTop8)
+            ex[j] = make_uint2(perm(cb.w1, cb.w0, spread_codes3x4(code[j] & 0xFFFu)),
+                               perm(cb.w1, cb.w0, spread_codes3x4(code[j] >> 12)));
+        else
+            ex[j] = lookup_codes8(code[j], cb);
+    }
     if (k) {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) *reinterpret_cast<uint2 *>(plane + (j * T + tid) * 8) = ex[j];
@@ -872,6 +719,22 @@ __global__ __launch_bounds__(T) void sz_dec_bf16_span(const uint8_t *__restrict_
             for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
         }
     }
+}
+
+template <int T, int CPL>
+__global__ __launch_bounds__(T) void sz_dec_bf16_span(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                      const uint64_t *__restrict__ block_offsets,
+                                                      int32_t *__restrict__ status, uint16_t *__restrict__ out)
+{
+    bf16_span_decode<T, CPL, kTop16>(in, a, block_offsets, status, out);
+}
+
+template <int T, int CPL>
+__global__ __launch_bounds__(T) void sz_dec_top8_span(const uint8_t *__restrict__ in, DecodeArgs a,
+                                                      const uint64_t *__restrict__ block_offsets,
+                                                      int32_t *__restrict__ status, uint16_t *__restrict__ out)
+{
+    bf16_span_decode<T, CPL, kTop8>(in, a, block_offsets, status, out);
 }
 
 template <int T, int CPL>
@@ -976,13 +839,16 @@ constexpr int kBf16SpanThreads = 256, kBf16SpanChunks = 2;     // up to kSpanWid
 constexpr int kBf16WideThreads = 256, kBf16WideChunks = 4;     // above
 constexpr int kE5SpanThreads = 256;
 
-template <int T, int CPL, int DT>
+template <int T, int CPL, int DT, int V = kTop16>
 void launch_span(const uint8_t *in, const DecodeArgs &a, const uint64_t *block_offsets, int32_t *status,
                  void *d_out, hipStream_t s)
 {
     constexpr uint32_t span = T * CPL * (DT == SZ_BF16 ? 8 : 32);
     const dim3 grid((uint32_t)((a.n + span - 1) / span));
-    if constexpr (DT == SZ_BF16)
+    if constexpr (V == kTop8)
+        hipLaunchKernelGGL((sz_dec_top8_span<T, CPL>), grid, dim3(T), 0, s, in, a, block_offsets, status,
+                           static_cast<uint16_t *>(d_out));
+    else if constexpr (DT == SZ_BF16)
         hipLaunchKernelGGL((sz_dec_bf16_span<T, CPL>), grid, dim3(T), 0, s, in, a, block_offsets, status,
                            static_cast<uint16_t *>(d_out));
     else
@@ -1025,13 +891,15 @@ int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype
         hipLaunchKernelGGL(sz_dec_scan, dim3(1), dim3(kScanThreads), 0, s, in, a, block_offsets, status);
     }
     if (g.nb && version == kTop8) {
-        LaunchScope scope("sz_dec_top8", s);
-        hipLaunchKernelGGL(sz_dec_variant<kTop8>, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a,
-                           block_offsets, status, static_cast<uint16_t *>(d_out));
+        LaunchScope scope("sz_dec_top8_span", s);
+        if (g.nb > kSpanWideBlocks)
+            launch_span<kBf16WideThreads, kBf16WideChunks, SZ_BF16, kTop8>(in, a, block_offsets, status, d_out, s);
+        else
+            launch_span<kBf16SpanThreads, kBf16SpanChunks, SZ_BF16, kTop8>(in, a, block_offsets, status, d_out, s);
     } else if (g.nb && version == kTop15S) {
         LaunchScope scope("sz_dec_top15s", s);
-        hipLaunchKernelGGL(sz_dec_variant<kTop15S>, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a,
-                           block_offsets, status, static_cast<uint16_t *>(d_out));
+        hipLaunchKernelGGL(sz_dec_top15s, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, block_offsets, status,
+                           static_cast<uint16_t *>(d_out));
     } else if (g.nb && dtype == SZ_BF16) {
         LaunchScope scope("sz_dec_bf16_span", s);
         if (g.nb > kSpanWideBlocks)

@@ -164,3 +164,40 @@ def test_full_size_llama3_kv(fmt):
         assert counts[b] == int(ref[64:68].view(np.uint32)[0])
     del x, buf
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("pad_blocks", [0, 256])
+@pytest.mark.parametrize("heavy", [False, True])
+def test_top8_record_validation(heavy, pad_blocks):
+    """Malformed position records of the Top-8 format, in blocks with a few
+    records and in blocks where most values escape, behind 0 or 256 blocks of
+    escape-free padding (the narrow and the wide span shapes): the device
+    verdict equals the oracle's, and the untouched stream decodes."""
+    rng = np.random.default_rng(21)
+    n = BLOCK + 20000
+    if heavy:
+        e = rng.integers(100, 140, n)                       # about 80 % outside the book
+    else:
+        e = np.full(n, 124)
+        e[rng.choice(n, 60, replace=False)] = 90
+    bits = ((rng.integers(0, 2, n) << 15) | (e << 7) | rng.integers(0, 128, n)).astype(np.uint16)
+    bits = np.concatenate([np.full(pad_blocks * BLOCK, 124 << 7, dtype=np.uint16), bits])
+    n = bits.size
+    good = oracle.encode_variant(bits, 2, range(120, 128))
+    e_total = int(good[16:24].view(np.uint64)[0])
+    first = good.size - 3 * e_total
+    cases = [("repeat", lambda t: t.__setitem__(slice(first + 3, first + 5), t[first:first + 2].copy())),
+             ("middle_range", lambda t: t.__setitem__(slice(first + 3 * (e_total // 2), first + 3 * (e_total // 2) + 2),
+                                                      [0xFF, 0xFF])),
+             ("range_last_block", lambda t: t.__setitem__(slice(good.size - 3, good.size - 1), [0x30, 0x75]))]
+    for name, mutate in cases:
+        print("top8 record case", name, "heavy", heavy, "pad", pad_blocks, flush=True)
+        t = good.copy()
+        mutate(t)
+        want = oracle.validate_variant(t, 2, n)
+        assert want == oracle.E_FORMAT, name
+        _, ws = _decode(torch.from_numpy(t).cuda(), 2, n, check=False)
+        assert int(ws[:4].cpu().view(torch.int32)[0]) == want, name
+    out, ws = _decode(torch.from_numpy(good).cuda(), 2, n, check=False)
+    assert int(ws[:4].cpu().view(torch.int32)[0]) == 0
+    assert np.array_equal(out.cpu().numpy()[:2 * n].view(np.uint16), bits)
