@@ -459,8 +459,10 @@ __global__ __launch_bounds__(kEncTile / (8 * C)) void sz_enc_dense_bf16(const ui
 // ---------------------------------------------------------------------------
 // Kernel: FP8 E5M2 dense encode + escape staging (the page's FP8 extension,
 // Contributions item 4).  Same tiling as BF16; a lane holds two 32-element
-// chunks of its wave's row.  A chunk row with many escapes is staged through
-// LDS as four segments of 16 lanes.
+// chunks of its wave's row.  In a chunk row with few escapes each lane walks
+// its chunk's escape mask and writes the records itself, taking each
+// exponent from its 8-byte input group with one v_perm; a row with many is
+// staged through LDS as four segments of 16 lanes.
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *__restrict__ in, uint64_t n,
@@ -553,9 +555,31 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
         for (int j = 0; j < kE5Chunks; ++j) {
             const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
             const uint32_t rank = wave_before + row_base[j];
-            // escape masks and exponents of the chunk, from its flag words and input words
             const uint32_t dw[8] = {q[j][0].x, q[j][0].y, q[j][0].z, q[j][0].w,
                                     q[j][1].x, q[j][1].y, q[j][1].z, q[j][1].w};
+            if (row_total[j] <= kDirectRecords) {                      // wave-uniform
+                if (cnt[j]) {
+                    // the chunk's escapes in element order; each one's exponent is
+                    // picked from the group of 8 input bytes that holds it
+                    uint32_t m = flags_to_mask8(fl[j][0]) | (flags_to_mask8(fl[j][1]) << 8) |
+                                 (flags_to_mask8(fl[j][2]) << 16) | (flags_to_mask8(fl[j][3]) << 24);
+                    uint8_t *rec = tstage + 3ull * (rank + lane_before[j]);
+                    const uint32_t pos0 = (uint32_t)(c0 & 0xFFFFu);
+                    while (m) {
+                        const uint32_t k = (uint32_t)__builtin_ctz(m);
+                        m &= m - 1;
+                        const uint32_t g = k >> 3;
+                        const uint32_t lo = g == 0 ? dw[0] : g == 1 ? dw[2] : g == 2 ? dw[4] : dw[6];
+                        const uint32_t hi = g == 0 ? dw[1] : g == 1 ? dw[3] : g == 2 ? dw[5] : dw[7];
+                        const uint32_t pos = pos0 + k;
+                        rec[0] = (uint8_t)pos;
+                        rec[1] = (uint8_t)(pos >> 8);
+                        rec[2] = (uint8_t)((perm(hi, lo, k & 7u) >> 2) & 0x1Fu);
+                        rec += 3;
+                    }
+                }
+                continue;
+            }
             uint32_t esc8[4];
             uint64_t ex[4];
 #pragma unroll
@@ -563,17 +587,6 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
                 esc8[s8] = flags_to_mask8(fl[j][s8]);
                 ex[s8] = (uint64_t)((dw[2 * s8] >> 2) & 0x1F1F1F1Fu) |
                          ((uint64_t)((dw[2 * s8 + 1] >> 2) & 0x1F1F1F1Fu) << 32);
-            }
-            if (row_total[j] <= kDirectRecords) {                      // wave-uniform
-                if (cnt[j]) {
-                    uint32_t r = rank + lane_before[j];
-#pragma unroll
-                    for (int s8 = 0; s8 < 4; ++s8) {
-                        put_records(tstage, r, esc8[s8], ex[s8], (uint32_t)((c0 + 8 * s8) & 0xFFFFu));
-                        r += __popc(esc8[s8]);
-                    }
-                }
-                continue;
             }
             // four segments of 16 lanes x 32 elements
 #pragma unroll
