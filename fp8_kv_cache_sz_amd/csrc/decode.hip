@@ -1,7 +1,8 @@
 // SplitZip decode for MI355X: stream validation and block escape offsets
 // (a one-workgroup scan, or one wave for small streams), the span decoders
-// with the escape patch fused before the store, the ablation-format
-// decoders, and the decode entry points of the C ABI
+// (Top-16 and the Top-8 ablation) with the escape patch fused before the
+// store, the Top-15 + sentinel ablation decoder, and the decode entry points
+// of the C ABI
 // ("SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
 // Serving", gist.science summary page, Method, decoding bullets).
 #include "common.hpp"

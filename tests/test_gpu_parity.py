@@ -390,8 +390,9 @@ def test_e5m2_device_validation(pad_blocks):
 @pytest.mark.parametrize("pad_blocks", PAD_BLOCKS)
 @pytest.mark.parametrize("dtype", [0, 1])
 def test_device_validation_heavy_blocks(dtype, pad_blocks):
-    """Malformed records inside blocks with more escapes than the LDS map
-    holds (the exponent-plane decode path) are reported like the light ones."""
+    """Malformed records inside blocks where most values escape (each span
+    then takes more records than its light window holds and goes through the
+    exponent plane) are reported like the light ones."""
     n = 65536 + 20000
     rng = np.random.default_rng(11)
     if dtype == 0:
