@@ -285,8 +285,9 @@ constexpr uint32_t kDirectRecords = 32;
 // Tiles with more escapes than this are not staged: the compaction kernel
 // derives their records again from the input, which moves 2 bytes per
 // element instead of writing and re-reading 3 bytes per escape.  Their tile
-// count carries kRederiveFlag.  The smallest streams stage every tile
-// (kStageAll; see sz_enc_compact_small).
+// count carries kRederiveFlag.  Streams of up to kFusedPrefixTiles tiles,
+// whose compaction kernels have few waves, stage every tile (kStageAll; see
+// sz_enc_compact_small and sz_enc_compact_fused).
 constexpr uint32_t kRederiveRecords = kEncTile / 4;
 constexpr uint32_t kStageAll = 0xFFFFFFFFu;
 constexpr uint32_t kRederiveFlag = 0x80000000u;
@@ -982,7 +983,10 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
 // The tile counts before a workgroup are re-read by every later workgroup, a
 // cost that grows with the square of the tile count: on MI355X this path
 // saves 2-3 us per encode up to 16M elements, breaks even at 32M and loses
-// beyond, so larger streams take the scan.
+// beyond, so larger streams take the scan.  The dense encoders stage every
+// tile of these streams, escape-heavy ones included: a wave copies a heavy
+// block's staged records faster than it re-derives them (random bits, 2M to
+// 32M elements: 234-278 us per encode against 300-322 us).
 // ---------------------------------------------------------------------------
 constexpr uint32_t kFusedThreads = 1024;
 constexpr uint32_t kFusedBlocks = kFusedThreads / 64;
@@ -1175,8 +1179,8 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
     uint8_t *stage = ws + w.stage;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    // the smallest streams stage every tile (see sz_enc_compact_small)
-    const uint32_t rederive_above = g.nb <= kSmallCompactBlocks ? kStageAll : kRederiveRecords;
+    // streams that take a compaction with its own prefix stage every tile
+    const uint32_t rederive_above = g.nt <= kFusedPrefixTiles ? kStageAll : kRederiveRecords;
     if (g.nt && dtype == SZ_BF16) {
         const uint16_t *in16 = static_cast<const uint16_t *>(d_in);
         if (version == kTop8) {

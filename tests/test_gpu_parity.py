@@ -174,11 +174,12 @@ def test_every_element_escapes():
 
 
 @pytest.mark.parametrize("dtype", [0, 1])
-@pytest.mark.parametrize("n", [16 * 65536, 40 * 65536 + 1234])
+@pytest.mark.parametrize("n", [16 * 65536, 40 * 65536 + 1234, 2049 * 16384 + 1234])
 def test_escape_heavy_compaction_paths(dtype, n):
-    """Random bits (escape-heavy tiles mixed with light ones) at a size that
-    stages every tile (16 blocks) and at one whose compaction re-derives the
-    heavy tiles from the input (40 blocks)."""
+    """Random bits (escape-heavy tiles mixed with light ones) at sizes whose
+    dense encoders stage every tile, copied by 1024 lanes per block (16
+    blocks) or by one wave per block (40 blocks), and at one past 2,048
+    tiles, whose compaction re-derives the heavy tiles from the input."""
     rng = np.random.default_rng(17)
     if dtype == 0:
         bits = rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16)
