@@ -858,6 +858,26 @@ void launch_span(const uint8_t *in, const DecodeArgs &a, const uint64_t *block_o
                            static_cast<uint8_t *>(d_out));
 }
 
+// BF16 span shape by stream size: 4096-element spans up to kSpanWideBlocks
+// blocks, 16384-element spans (eight chunks per lane) from 256 to 384 blocks
+// (16M-24M elements: half the workgroups of the 8192-element grid, which
+// there decode 3 us slower, about 15 %, on MI355X; at 12M and at 32M the
+// 8192-element spans are faster again), 8192-element spans otherwise.
+constexpr uint64_t kSpanHugeFirst = 256, kSpanHugeLast = 384;
+constexpr int kBf16HugeChunks = 8;
+
+template <int V>
+void launch_bf16_spans(const uint8_t *in, const DecodeArgs &a, const uint64_t *block_offsets, int32_t *status,
+                       void *d_out, hipStream_t s)
+{
+    if (a.nb <= kSpanWideBlocks)
+        launch_span<kBf16SpanThreads, kBf16SpanChunks, SZ_BF16, V>(in, a, block_offsets, status, d_out, s);
+    else if (a.nb >= kSpanHugeFirst && a.nb <= kSpanHugeLast)
+        launch_span<kBf16WideThreads, kBf16HugeChunks, SZ_BF16, V>(in, a, block_offsets, status, d_out, s);
+    else
+        launch_span<kBf16WideThreads, kBf16WideChunks, SZ_BF16, V>(in, a, block_offsets, status, d_out, s);
+}
+
 int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
                 void *d_ws, uint64_t ws_bytes, void *stream)
 {
@@ -894,20 +914,14 @@ int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype
     }
     if (g.nb && version == kTop8) {
         LaunchScope scope("sz_dec_top8_span", s);
-        if (g.nb > kSpanWideBlocks)
-            launch_span<kBf16WideThreads, kBf16WideChunks, SZ_BF16, kTop8>(in, a, block_offsets, status, d_out, s);
-        else
-            launch_span<kBf16SpanThreads, kBf16SpanChunks, SZ_BF16, kTop8>(in, a, block_offsets, status, d_out, s);
+        launch_bf16_spans<kTop8>(in, a, block_offsets, status, d_out, s);
     } else if (g.nb && version == kTop15S) {
         LaunchScope scope("sz_dec_top15s", s);
         hipLaunchKernelGGL(sz_dec_top15s, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, block_offsets, status,
                            static_cast<uint16_t *>(d_out));
     } else if (g.nb && dtype == SZ_BF16) {
         LaunchScope scope("sz_dec_bf16_span", s);
-        if (g.nb > kSpanWideBlocks)
-            launch_span<kBf16WideThreads, kBf16WideChunks, SZ_BF16>(in, a, block_offsets, status, d_out, s);
-        else
-            launch_span<kBf16SpanThreads, kBf16SpanChunks, SZ_BF16>(in, a, block_offsets, status, d_out, s);
+        launch_bf16_spans<kTop16>(in, a, block_offsets, status, d_out, s);
     } else if (g.nb) {
         LaunchScope scope("sz_dec_e5m2_span", s);
         if (g.nb > kSpanWideBlocks)
