@@ -1157,6 +1157,11 @@ __global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(8
 // with two chunks per lane (1024-lane workgroups): on MI355X 1.5 us faster
 // per encode at 1M-4M elements, slower from 16M on.
 constexpr uint64_t kSmallEncodeTiles = 512;
+// Up to this many tiles (64M elements) the Top-16 BF16 encoder runs 512-lane
+// workgroups, four chunks per lane: 3 % faster than 256 lanes with eight from
+// 32M to 64M elements on MI355X (31.0 -> 29.9 us at 32M, 50.5 -> 48.8 us at
+// 64M), the same from 12M to 24M; larger streams keep 256 lanes.
+constexpr uint64_t kMidEncodeTiles = 4096;
 
 // Encode behind sz_encode (host codebook cb4), sz_encode_devcb (cb_dev) and
 // sz_encode_format (version 2, 3).
@@ -1194,6 +1199,10 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
         } else if (g.nt <= kSmallEncodeTiles) {
             LaunchScope scope("sz_enc_dense_bf16", s);
             hipLaunchKernelGGL((sz_enc_dense_bf16<kTop16, 2>), dim3((uint32_t)g.nt), dim3(kEncTile / 16), 0, s,
+                               in16, g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, rederive_above);
+        } else if (g.nt <= kMidEncodeTiles) {
+            LaunchScope scope("sz_enc_dense_bf16", s);
+            hipLaunchKernelGGL((sz_enc_dense_bf16<kTop16, 4>), dim3((uint32_t)g.nt), dim3(kEncTile / 32), 0, s,
                                in16, g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, rederive_above);
         } else {
             LaunchScope scope("sz_enc_dense_bf16", s);
