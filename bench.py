@@ -1,21 +1,28 @@
 #!/usr/bin/env python3
 """SplitZip codec benchmark on one MI355X.
 
-One step = one pass of the whole hot path over one batch: encode the
-Llama-3-8B-shaped KV cache (32 layers x {K,V} x 8 KV heads x 128 dims x
-8192 tokens = 536,870,912 BF16 values, 1 GiB) into a SplitZip stream and
-decode it back.  Inputs are generated on the device and resident in HBM
-before the timed region; the codebook is calibrated offline (host, untimed)
-on a layer-0 calibration tensor.
+One step = one pass of the whole hot path over one batch: encode a KV
+payload into a SplitZip stream and decode it back.  The headline workload is
+the largest single-GPU one, the long-context transfer payload (28 layers x
+{K,V} x 4 KV heads x 128 dims x 65,536 tokens = 1,879,048,192 BF16 values,
+3.76 GB).  Inputs are generated on the device and resident in HBM before the
+timed region; each workload's codebook is calibrated offline (host,
+untimed) on its own calibration tensor.
 
 Prints one JSON line:
-  value       uncompressed GB/s of the round trip = 2 N bytes / (encode + decode time)
-  encode_GBps / decode_GBps    the two directions, timed separately
-  ratio, escape_rate           compression ratio (input bytes / stream bytes) and E / N
-  roofline    the dominant kernel's algorithmic bytes / average duration
-              (HIP events recorded on the launch stream by the library's
-              instrumentation) against the 8 TB/s HBM peak
+  value        uncompressed GB/s of the round trip = 2 N bytes / ms_per_step
+               (K steps timed with perf_counter, synchronised on both sides)
+  encode / decode   per direction, median and min of >= 20 runs, each
+               bracketed by its own pair of HIP events on the launch stream
+  ratio, escape_rate   input bytes / stream bytes, and E / N
+  roofline     the dominant kernel's algorithmic bytes / its average duration
+               (HIP events recorded on the launch stream by the library's
+               instrumentation) against the 8 TB/s HBM peak
   cpu_baseline the CPU oracle (single thread) on a bounded sample
+  parity       the whole GPU stream equals the oracle's stream of the whole
+               tensor, byte for byte
+  configs      the same per-direction figures, ratio, escape rate, oracle
+               baseline and parity verdict for every workload
 """
 from __future__ import annotations
 
@@ -31,26 +38,38 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-WORKLOAD = "llama3_8b_kv"
+WORKLOAD = "longctx_kv"
+# every workload the configs key reports, in this order
+ALL_WORKLOADS = ("kv1m", "llama3_8b_kv", "longctx_kv", "stress_t3", "stress_oneexp", "stress_random",
+                 "llama3_8b_kv_e5m2")
 
 
-def parse_args():
+def parse_args(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default=WORKLOAD)
-    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--configs", default="all",
+                   help="workloads for the per-config rows: 'all', 'none' or a comma-separated list")
+    p.add_argument("--runs", type=int, default=20,
+                   help="event-timed runs per direction for the median and min (at least 20)")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the oracle leg (baseline timings and the whole-stream parity checks)")
     p.add_argument("--core-only", action="store_true",
-                   help="time only the encode+decode step (no calibration, format or transfer sections), "
-                        "e.g. under a profiler")
+                   help="time only the encode+decode step of the headline workload (no per-config rows, "
+                        "calibration, format or transfer sections), e.g. under a profiler")
     p.add_argument("--cpu-sample-log2", type=int, default=29,
-                   help="elements of the workload the CPU oracle encodes and decodes (log2; the default, 2^29, is the "
-                        "whole Llama-3-8B cache, about 12 s of single-core work)")
+                   help="elements of the headline workload the oracle baseline encodes and decodes (log2; "
+                        "2^29 is about 12 s of single-core work)")
+    p.add_argument("--config-sample-log2", type=int, default=25,
+                   help="elements of each per-config row's oracle baseline sample (log2)")
     p.add_argument("--ingest-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_BYTES"),
                    help="record HBM traffic per kernel from two rocprofv3 --pmc runs of this "
                         "benchmark (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json and exit")
-    return p.parse_args()
+    args = p.parse_args(argv)
+    args.runs = max(20, args.runs)
+    return args
 
 
 def kernel_source_hash() -> str:
@@ -165,26 +184,159 @@ def cpu_model() -> str:
     return platform.processor() or platform.machine()
 
 
-def cpu_baseline(x_dev, cb, dtype, log2_sample):
+def alg_bytes(dtype, n, escapes):
+    """Bytes the method must move per direction: BF16 2 B in, 0.5 B of codes
+    and 1 B of sign/mantissa per element; E5M2 1 + 0.5 + 0.375 B; 3 B per
+    escape record."""
+    return (int(3.5 * n) if dtype == 0 else int(1.875 * n)) + 3 * escapes
+
+
+def median(v):
+    v = sorted(v)
+    m = len(v) // 2
+    return v[m] if len(v) % 2 else 0.5 * (v[m - 1] + v[m])
+
+
+# ---------------------------------------------------------------------------
+# The oracle leg: baseline timings of the single-threaded CPU oracle on a
+# bounded sample, and whole-stream parity checks against it
+# ---------------------------------------------------------------------------
+def oracle_baseline(bits, cb_exps, dtype, n_sample):
+    """Times one oracle encode and one decode of the first n_sample elements
+    (single thread, nothing else running on the host)."""
     import oracle
-    import synth
-    n = min(x_dev.numel(), 1 << log2_sample)
-    bits = synth.as_bits_numpy(x_dev[:n])
-    cbn = list(cb.exps)
+    part = bits[:n_sample]
     t0 = time.perf_counter()
-    stream = oracle.encode(bits, dtype, cbn)
+    stream = oracle.encode(part, dtype, cb_exps)
     t1 = time.perf_counter()
-    back = oracle.decode(stream, dtype, n)
+    back = oracle.decode(stream, dtype, part.size)
     t2 = time.perf_counter()
-    assert (back == bits).all()
+    assert (back == part).all()
     elem = 2 if dtype == 0 else 1
-    gbps = 2 * n * elem / (t2 - t0) / 1e9
     return {
-        "value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": "first %d elements (%d MiB) of the workload; one encode (%.2f s) and one "
-                  "decode (%.2f s), single-threaded C, host %s, %d logical CPUs"
-                  % (n, n * elem >> 20, t1 - t0, t2 - t1, cpu_model(), os.cpu_count()),
+        "value": round(2 * part.size * elem / (t2 - t0) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": "first %d elements (%d MiB) of the workload; one encode (%.2f s) and one decode (%.2f s), "
+                  "single-threaded C, host %s, %d logical CPUs"
+                  % (part.size, part.size * elem >> 20, t1 - t0, t2 - t1, cpu_model(), os.cpu_count()),
     }
+
+
+def oracle_parity(bits, cb_exps, dtype, gpu_stream):
+    """The GPU's stream of the whole tensor against the oracle's, byte for
+    byte; returns (equal, detail)."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    expect = oracle.encode(bits, dtype, cb_exps)
+    secs = time.perf_counter() - t0
+    if expect.size != gpu_stream.size:
+        return False, "size %d, oracle %d" % (gpu_stream.size, expect.size)
+    diff = np.flatnonzero(expect != gpu_stream)
+    if diff.size:
+        return False, "%d bytes differ, first at %d" % (diff.size, int(diff[0]))
+    return True, "%d bytes equal (oracle encode %.1f s)" % (expect.size, secs)
+
+
+def parity_all(jobs, workers=4):
+    """Whole-stream parity of every collected workload, the oracle encodes
+    running in parallel threads (the ctypes calls release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        futs = {name: pool.submit(oracle_parity, *job) for name, job in jobs.items()}
+        return {name: f.result() for name, f in futs.items()}
+
+
+# ---------------------------------------------------------------------------
+# GPU measurement
+# ---------------------------------------------------------------------------
+class Codec:
+    """One workload resident on the device with its stream buffer, encode and
+    decode workspaces and output tensor."""
+
+    def __init__(self, sz, name, dev):
+        import synth
+        import torch
+        self.name = name
+        self.x, self.dtype = synth.workload(name, device=dev)
+        self.cal = synth.calibration_tensor(name, device="cpu")
+        self.cb = sz.calibrate(self.cal)
+        self.n = self.x.numel()
+        self.elem = 2 if self.dtype == 0 else 1
+        self.sz = sz
+        self.buf = torch.empty(sz.encoded_size(self.dtype, self.n, self.n), dtype=torch.uint8, device=dev)
+        self.ws = sz.workspace(self.dtype, self.n, dev)
+        self.ws_dec = sz.decode_workspace(self.dtype, self.n, dev)
+        self.y = torch.empty_like(self.x)
+        self.stream = torch.cuda.current_stream(dev)
+        # first pass: learn the stream size, check the round trip
+        self.encode()
+        torch.cuda.synchronize()
+        self.escapes = sz.read_escape_count(self.buf)
+        self.size = sz.encoded_size(self.dtype, self.n, self.escapes)
+        self.decode()
+        torch.cuda.synchronize()
+        if int(self.ws_dec[:4].cpu().view(torch.int32)[0]) != 0 or not torch.equal(
+                self.y.view(torch.uint8), self.x.view(torch.uint8)):
+            raise SystemExit("round trip mismatch on %s" % name)
+
+    def encode(self):
+        self.sz.encode(self.x, self.cb, out=self.buf, ws=self.ws, sync=False)
+
+    def decode(self):
+        self.sz.decode(self.buf, self.dtype, self.n, out=self.y, ws=self.ws_dec, check=False,
+                       in_bytes=getattr(self, "size", None))
+
+    def time_runs(self, fn, runs, warmup=3):
+        """Per-run milliseconds: each run bracketed by its own event pair on
+        the launch stream."""
+        import torch
+        for _ in range(warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+        for a, b in ev:
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    def directions(self, runs):
+        """Median and min of the encode and decode times, GB/s (uncompressed)
+        and the share of the 8 TB/s peak on algorithmic bytes."""
+        out = {}
+        alg = alg_bytes(self.dtype, self.n, self.escapes)
+        for d, fn in (("encode", self.encode), ("decode", self.decode)):
+            t = self.time_runs(fn, runs)
+            med, lo = median(t), min(t)
+            out[d] = {"median_ms": round(med, 5), "min_ms": round(lo, 5), "runs": len(t),
+                      "GBps": round(self.n * self.elem / (med * 1e-3) / 1e9, 2),
+                      "GBps_best": round(self.n * self.elem / (lo * 1e-3) / 1e9, 2),
+                      "alg_GBps": round(alg / (med * 1e-3) / 1e9, 1),
+                      "frac_of_peak": round(alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        return out
+
+    def kernel_stats(self, reps):
+        """Average duration of every kernel launch through the library's event
+        instrumentation."""
+        sz = self.sz
+        sz.profile_enable(True)
+        for _ in range(reps):
+            self.encode()
+            self.decode()
+        stats = sz.profile_collect()
+        sz.profile_enable(False)
+        return {k: {"launches": c, "avg_ms": round(ms / c, 5)} for k, (c, ms) in stats.items()}
+
+    def host_copies(self):
+        """The input's raw bits and the encoded stream, on the host."""
+        import synth
+        return synth.as_bits_numpy(self.x), self.buf[:self.size].cpu().numpy()
+
+    def summary(self):
+        return {"elements": self.n, "bytes": self.n * self.elem, "escapes": self.escapes,
+                "escape_rate": round(self.escapes / self.n, 6), "stream_bytes": self.size,
+                "ratio": round(self.n * self.elem / self.size, 6),
+                "alg_bytes_per_direction": alg_bytes(self.dtype, self.n, self.escapes)}
 
 
 def main():
@@ -204,100 +356,86 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x, dtype = synth.workload(args.workload, device=dev)
-    cal = synth.calibration_tensor(args.workload, device="cpu")
-    cb = sz.calibrate(cal)
-    n = x.numel()
-    elem = 2 if dtype == 0 else 1
-    cap = sz.encoded_size(dtype, n, n)
-    buf = torch.empty(cap, dtype=torch.uint8, device=dev)
-    ws = sz.workspace(dtype, n, dev)
-    ws_dec = sz.workspace(dtype, n, dev)
-    y = torch.empty_like(x)
-    stream = torch.cuda.current_stream(dev)
+    oracle_leg = not args.no_cpu_baseline
+    if args.core_only or args.configs == "none":
+        config_names = []
+    elif args.configs == "all":
+        config_names = [w for w in ALL_WORKLOADS if w != args.workload]
+    else:
+        config_names = [w for w in args.configs.split(",") if w and w != args.workload]
+    parity_jobs = {}
 
-    def encode():
-        sz.encode(x, cb, out=buf, ws=ws, sync=False)
-
-    def decode(in_bytes):
-        sz.decode(buf, dtype, n, out=y, ws=ws_dec, check=False, in_bytes=in_bytes)
-
-    # first pass: learn the stream size, check the round trip
-    encode()
-    torch.cuda.synchronize()
-    escapes = sz.read_escape_count(buf)
-    size = sz.encoded_size(dtype, n, escapes)
-    decode(size)
-    torch.cuda.synchronize()
-    if int(ws_dec[:4].cpu().view(torch.int32)[0]) != 0 or not torch.equal(
-            y.view(torch.uint8), x.view(torch.uint8)):
-        print("round trip mismatch", file=sys.stderr)
-        sys.exit(1)
-
+    # ---- the headline workload: the timed steps --------------------------
+    c = Codec(sz, args.workload, dev)
+    n, dtype, elem = c.n, c.dtype, c.elem
     for _ in range(args.warmup):
-        encode()
-        decode(size)
+        c.encode()
+        c.decode()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        encode()
-        decode(size)
+        c.encode()
+        c.decode()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = 2 * n * elem / (ms_per_step * 1e-3) / 1e9
 
-    # per-direction timing (events on the launch stream)
-    def time_loop(fn, reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) / reps
-
-    reps = max(5, args.steps)
-    enc_ms = time_loop(encode, reps)
-    dec_ms = time_loop(lambda: decode(size), reps)
-
-    # per-kernel durations through the library's event instrumentation
-    sz.profile_enable(True)
-    for _ in range(reps):
-        encode()
-        decode(size)
-    stats = sz.profile_collect()
-    sz.profile_enable(False)
-    per_kernel = {k: {"launches": c, "avg_ms": round(ms / c, 5)} for k, (c, ms) in stats.items()}
+    dirs = c.directions(args.runs)
+    per_kernel = c.kernel_stats(args.runs)
     dense = {k: v for k, v in per_kernel.items() if k.startswith(("sz_enc_dense", "sz_dec_bf16", "sz_dec_e5m2"))}
     dominant = max(dense, key=lambda k: dense[k]["avg_ms"])
-    alg_bytes = int(3.5 * n) + 3 * escapes if dtype == 0 else int(1.875 * n) + 3 * escapes
-    avg_s = dense[dominant]["avg_ms"] * 1e-3
-    achieved = alg_bytes / avg_s / 1e9
+    alg = alg_bytes(dtype, n, c.escapes)
+    achieved = alg / (dense[dominant]["avg_ms"] * 1e-3) / 1e9
     traffic = load_traffic(dominant, args.workload)
 
     calibration = formats = transfer = None
     if not args.core_only:
-        calibration, formats, transfer = extra_sections(sz, x, cb, dtype, n, elem, buf, ws, ws_dec, y, dev,
-                                                        time_loop, reps, enc_ms, dec_ms)
+        calibration, formats, transfer = extra_sections(sz, c, args.runs, dirs)
+    copy = reference_copy_rate(sz, alg, args.runs, dev)
 
-    # the library's streaming copy of the same bytes (non-temporal dwordx4, the
-    # fastest plain copy shape), as the practical streaming ceiling
-    alg_per_direction = alg_bytes // 2 // 16 * 16          # read half, write half
-    src = torch.empty(alg_per_direction, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    # timed per launch through the library's event instrumentation, as the
-    # codec kernels are, so that host gaps between launches do not count
-    sz.reference_copy(src, dst)
-    sz.profile_enable(True)
-    for _ in range(reps):
-        sz.reference_copy(src, dst)
-    launches, total_ms = sz.profile_collect()["sz_ref_copy"]
-    sz.profile_enable(False)
-    copy_ms = total_ms / launches
-    copy_gbps = 2 * src.numel() / (copy_ms * 1e-3) / 1e9
-    del src, dst
+    headline_bits = headline_stream = None
+    if oracle_leg:
+        headline_bits, headline_stream = c.host_copies()
+        parity_jobs[args.workload] = (headline_bits, list(c.cb.exps), dtype, headline_stream)
+    head_summary = c.summary()
+    del c
+    torch.cuda.empty_cache()
 
+    # ---- every other workload: per-direction rows -------------------------
+    configs = {args.workload: dict(head_summary, **dirs, kernels=per_kernel)}
+    config_samples = {}
+    for name in config_names:
+        print("config %s" % name, file=sys.stderr, flush=True)
+        w = Codec(sz, name, dev)
+        row = dict(w.summary(), **w.directions(args.runs))
+        row["kernels"] = w.kernel_stats(args.runs)
+        configs[name] = row
+        if oracle_leg:
+            bits, stream = w.host_copies()
+            parity_jobs[name] = (bits, list(w.cb.exps), w.dtype, stream)
+            config_samples[name] = (bits, list(w.cb.exps), w.dtype)
+        del w
+        torch.cuda.empty_cache()
+
+    # ---- the oracle leg ----------------------------------------------------
+    cpu = None
+    parity = None
+    if oracle_leg:
+        print("oracle baselines", file=sys.stderr, flush=True)
+        cpu = oracle_baseline(headline_bits, list(parity_jobs[args.workload][1]), dtype,
+                              min(n, 1 << args.cpu_sample_log2))
+        configs[args.workload]["cpu_baseline"] = cpu
+        for name, (bits, cbx, dt) in config_samples.items():
+            configs[name]["cpu_baseline"] = oracle_baseline(bits, cbx, dt, min(bits.size, 1 << args.config_sample_log2))
+        print("whole-stream parity of %d workloads" % len(parity_jobs), file=sys.stderr, flush=True)
+        verdicts = parity_all(parity_jobs)
+        for name, (ok, detail) in verdicts.items():
+            configs[name]["parity"] = ok
+            configs[name]["parity_detail"] = detail
+        parity = all(ok for ok, _ in verdicts.values())
+
+    enc, dec = dirs["encode"], dirs["decode"]
     result = {
         "metric": "encode/decode GB/s (uncompressed) + % of 8 TB/s HBM peak; compression ratio",
         "value": round(value, 2),
@@ -312,28 +450,23 @@ def main():
         "dtype": "u16" if dtype == 0 else "u8",
         "data": "synthetic",
         "config": {"workload": args.workload, "description": synth.DESCRIPTION[args.workload],
-                   "elements": n, "bytes": n * elem, "codebook": list(cb.exps),
-                   "step": "encode + decode of the whole tensor"},
-        "encode_GBps": round(n * elem / (enc_ms * 1e-3) / 1e9, 2),
-        "decode_GBps": round(n * elem / (dec_ms * 1e-3) / 1e9, 2),
-        "encode_ms": round(enc_ms, 4),
-        "decode_ms": round(dec_ms, 4),
-        "ratio": round(n * elem / size, 6),
-        "escape_rate": round(escapes / n, 6),
-        "escapes": escapes,
-        "stream_bytes": size,
+                   "elements": n, "bytes": n * elem, "codebook": list(parity_jobs[args.workload][1])
+                   if oracle_leg else None, "step": "encode + decode of the whole tensor"},
+        "encode_GBps": enc["GBps"],
+        "decode_GBps": dec["GBps"],
+        "encode_ms": {"median": enc["median_ms"], "min": enc["min_ms"], "runs": enc["runs"]},
+        "decode_ms": {"median": dec["median_ms"], "min": dec["min_ms"], "runs": dec["runs"]},
+        "encode_frac_of_peak": enc["frac_of_peak"],
+        "decode_frac_of_peak": dec["frac_of_peak"],
+        "ratio": head_summary["ratio"],
+        "escape_rate": head_summary["escape_rate"],
+        "escapes": head_summary["escapes"],
+        "stream_bytes": head_summary["stream_bytes"],
+        "parity": parity,
         "kernels": per_kernel,
-        "calibration": calibration,
-        "formats": formats,
-        "transfer": transfer,
         "hbm": hbm_rates(per_kernel, args.workload),
-        "page_numbers": {"encode_GBps": 613.3, "decode_GBps": 2181.8, "ratio": 1.324,
-                         "hardware": "not named on the page", "workload": "real BF16 activations",
-                         "note": "context only, not this workload or machine"},
-        "copy_GBps": round(copy_gbps, 1),
-        "copy_bytes": alg_per_direction,
-        "copy_kernel": "sz_ref_copy: one non-temporal dwordx4 per lane, 4 KB per 256-lane workgroup",
-        "dominant_vs_copy": round(achieved / copy_gbps, 4),
+        "copy": copy,
+        "dominant_vs_copy": round(achieved / copy["GBps"], 4),
         "roofline": {
             "bound": "hbm",
             "kernel": dominant,
@@ -343,11 +476,39 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
         },
+        "configs": configs,
+        "calibration": calibration,
+        "formats": formats,
+        "transfer": transfer,
+        "page_numbers": {"encode_GBps": 613.3, "decode_GBps": 2181.8, "ratio": 1.324,
+                         "hardware": "not named on the page", "workload": "real BF16 activations",
+                         "note": "context only, not this workload or machine"},
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(x, cb, dtype, args.cpu_sample_log2)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
+    if parity is False:
+        sys.exit(1)
 
+
+def reference_copy_rate(sz, alg, runs, dev):
+    """The library's streaming copy of half the dominant kernel's algorithmic
+    bytes (read and written once, non-temporal dwordx4, the fastest plain
+    copy shape), timed per launch like the codec kernels: the practical
+    streaming ceiling."""
+    import torch
+    per_direction = alg // 2 // 16 * 16
+    src = torch.empty(per_direction, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    sz.reference_copy(src, dst)
+    sz.profile_enable(True)
+    for _ in range(runs):
+        sz.reference_copy(src, dst)
+    launches, total_ms = sz.profile_collect()["sz_ref_copy"]
+    sz.profile_enable(False)
+    ms = total_ms / launches
+    return {"GBps": round(2 * per_direction / (ms * 1e-3) / 1e9, 1), "bytes": per_direction,
+            "kernel": "sz_ref_copy: one non-temporal dwordx4 per lane, 4 KB per 256-lane workgroup"}
 
 
 def hbm_rates(per_kernel, workload):
@@ -362,22 +523,27 @@ def hbm_rates(per_kernel, workload):
     return out or None
 
 
-def extra_sections(sz, x, cb, dtype, n, elem, buf, ws, ws_dec, y, dev, time_loop, reps, enc_ms, dec_ms):
-    """Rows beyond the encode+decode step: on-device calibration, the
-    ablation formats and the chunked transfer."""
+def extra_sections(sz, c, runs, dirs):
+    """Rows beyond the encode+decode step, on the headline tensor: on-device
+    calibration, the ablation formats and the chunked transfer."""
     import torch
+    x, cb, dtype, n, elem, dev = c.x, c.cb, c.dtype, c.n, c.elem, c.x.device
+    enc_ms, dec_ms = dirs["encode"]["median_ms"], dirs["decode"]["median_ms"]
+
+    def med(fn):
+        return median(c.time_runs(fn, runs))
+
     # on-device calibration (per-tensor codebook at run time): the whole
     # tensor, and every 16th 64K block; then encode with the device codebook
     cal_ws = torch.empty(sz._native.sz_calibrate_workspace_size(dtype), dtype=torch.uint8, device=dev)
     d_cb = torch.zeros(sz.DEVICE_CODEBOOK_BYTES, dtype=torch.uint8, device=dev)
-    cal_full_ms = time_loop(lambda: sz.calibrate_device(x, 1, out=d_cb, ws=cal_ws), reps)
-    cal_s16_ms = time_loop(lambda: sz.calibrate_device(x, 16, out=d_cb, ws=cal_ws), reps)
+    cal_full_ms = med(lambda: sz.calibrate_device(x, 1, out=d_cb, ws=cal_ws))
+    cal_s16_ms = med(lambda: sz.calibrate_device(x, 16, out=d_cb, ws=cal_ws))
     sz.calibrate_device(x, 1, out=d_cb, ws=cal_ws)
-    enc_dcb_ms = time_loop(lambda: sz.encode(x, d_cb, out=buf, ws=ws, sync=False), reps)
+    enc_dcb_ms = med(lambda: sz.encode(x, d_cb, out=c.buf, ws=c.ws, sync=False))
     torch.cuda.synchronize()
-    if int(ws[:4].cpu().view(torch.int32)[0]) != 0:
-        print("device codebook rejected", file=sys.stderr)
-        sys.exit(1)
+    if int(c.ws[:4].cpu().view(torch.int32)[0]) != 0:
+        raise SystemExit("device codebook rejected")
     dyn_cb = sz.codebook_from_device(d_cb)
     calibration = {
         "device_full_ms": round(cal_full_ms, 4),
@@ -388,23 +554,24 @@ def extra_sections(sz, x, cb, dtype, n, elem, buf, ws, ws_dec, y, dev, time_loop
         "per_tensor_codebook": list(dyn_cb.exps),
         "per_tensor_codebook_equals_offline": list(dyn_cb.exps) == list(cb.exps),
     }
+    # re-encode with the offline book: c.buf holds the measured stream again
+    c.encode()
 
     # the page's ablation formats on the same tensor (BF16 only): Top-8 and
-    # Top-15 with a sentinel code, against the Top-16 numbers above
+    # Top-15 with a sentinel code, against the Top-16 numbers
     formats = None
     if dtype == 0:
         formats = {}
         for name, fmt in (("top8", sz.TOP8), ("top15_sentinel", sz.TOP15S)):
-            cap_f = sz.encoded_size(dtype, n, n, fmt)
-            buf_f = torch.empty(cap_f, dtype=torch.uint8, device=dev)
-            _, size_f, esc_f = sz.encode(x, cb, out=buf_f, ws=ws, fmt=fmt)
-            sz.decode(buf_f, dtype, n, out=y, ws=ws_dec, in_bytes=size_f, fmt=fmt)
-            if not torch.equal(y.view(torch.uint8), x.view(torch.uint8)):
-                print("round trip mismatch (%s)" % name, file=sys.stderr)
-                sys.exit(1)
-            e_ms = time_loop(lambda: sz.encode(x, cb, out=buf_f, ws=ws, sync=False, fmt=fmt), reps)
-            d_ms = time_loop(lambda: sz.decode(buf_f, dtype, n, out=y, ws=ws_dec, check=False,
-                                               in_bytes=size_f, fmt=fmt), reps)
+            buf_f = torch.empty(sz.encoded_size(dtype, n, n, fmt), dtype=torch.uint8, device=dev)
+            ws_f = sz.workspace(dtype, n, dev, fmt)
+            _, size_f, esc_f = sz.encode(x, cb, out=buf_f, ws=ws_f, fmt=fmt)
+            sz.decode(buf_f, dtype, n, out=c.y, ws=c.ws_dec, in_bytes=size_f, fmt=fmt)
+            if not torch.equal(c.y.view(torch.uint8), x.view(torch.uint8)):
+                raise SystemExit("round trip mismatch (%s)" % name)
+            e_ms = med(lambda: sz.encode(x, cb, out=buf_f, ws=ws_f, sync=False, fmt=fmt))
+            d_ms = med(lambda: sz.decode(buf_f, dtype, n, out=c.y, ws=c.ws_dec, check=False, in_bytes=size_f,
+                                         fmt=fmt))
             formats[name] = {
                 "encode_GBps": round(n * elem / (e_ms * 1e-3) / 1e9, 1),
                 "decode_GBps": round(n * elem / (d_ms * 1e-3) / 1e9, 1),
@@ -413,51 +580,51 @@ def extra_sections(sz, x, cb, dtype, n, elem, buf, ws, ws_dec, y, dev, time_loop
                 "top16_decode_speedup": round(d_ms / dec_ms, 3),
                 "top16_encode_speedup": round(e_ms / enc_ms, 3),
             }
-            del buf_f
+            del buf_f, ws_f
 
     # chunked transfer through pinned host memory (PCIe both ways stands in
     # for the prefill-to-decode link): raw against SplitZip-compressed, one
-    # 2^24-value chunk (one Llama-3-8B layer, K and V) at a time
-    chunk = min(n, 1 << 24)
+    # layer (K and V) per chunk
+    chunk = min(n, 1 << 24 if c.name != "longctx_kv" else 1 << 26)
     staging = sz.transfer_buffers(dtype, n, chunk, 3, dev)
-    runs = {}
+    runs_t = {}
     for mode, book in (("raw", None), ("splitzip", cb)):
         best = None
         for _ in range(3):
-            _, st = sz.transfer(x, chunk, book, depth=3, out=y, staging=staging)
+            _, st = sz.transfer(x, chunk, book, depth=3, out=c.y, staging=staging)
             if best is None or st["total_ms"] < best["total_ms"]:
                 best = st
-        if not torch.equal(y.view(torch.uint8), x.view(torch.uint8)):
-            print("transfer mismatch (%s)" % mode, file=sys.stderr)
-            sys.exit(1)
-        runs[mode] = best
+        if not torch.equal(c.y.view(torch.uint8), x.view(torch.uint8)):
+            raise SystemExit("transfer mismatch (%s)" % mode)
+        runs_t[mode] = best
     # the codec's own time per chunk (encode + decode of one chunk on the
     # device, no link), and its share of the compressed transfer's wall time
     xc = x[:chunk]
     bc = torch.empty(sz.encoded_size(dtype, chunk, chunk), dtype=torch.uint8, device=dev)
-    wc_e, wc_d = sz.workspace(dtype, chunk, dev), sz.workspace(dtype, chunk, dev)
+    wc_e, wc_d = sz.workspace(dtype, chunk, dev), sz.decode_workspace(dtype, chunk, dev)
     yc = torch.empty_like(xc)
 
     def chunk_codec():
         sz.encode(xc, cb, out=bc, ws=wc_e, sync=False)
         sz.decode(bc, dtype, chunk, out=yc, ws=wc_d, check=False)
-    codec_ms = time_loop(chunk_codec, reps)
+    codec_ms = med(chunk_codec)
     del bc, wc_e, wc_d, yc
     transfer = {
         "link": "PCIe via pinned host memory, device->host then host->device, pipelined (depth 3)",
         "chunk_elems": chunk,
-        "chunks": runs["raw"]["chunks"],
-        "raw_ms": round(runs["raw"]["total_ms"], 3),
-        "raw_GBps": round(n * elem / (runs["raw"]["total_ms"] * 1e-3) / 1e9, 2),
-        "splitzip_ms": round(runs["splitzip"]["total_ms"], 3),
-        "splitzip_GBps": round(n * elem / (runs["splitzip"]["total_ms"] * 1e-3) / 1e9, 2),
-        "wire_bytes": runs["splitzip"]["wire_bytes"],
-        "wire_ratio": round(n * elem / runs["splitzip"]["wire_bytes"], 6),
-        "speedup": round(runs["raw"]["total_ms"] / runs["splitzip"]["total_ms"], 4),
+        "chunks": runs_t["raw"]["chunks"],
+        "raw_ms": round(runs_t["raw"]["total_ms"], 3),
+        "raw_GBps": round(n * elem / (runs_t["raw"]["total_ms"] * 1e-3) / 1e9, 2),
+        "splitzip_ms": round(runs_t["splitzip"]["total_ms"], 3),
+        "splitzip_GBps": round(n * elem / (runs_t["splitzip"]["total_ms"] * 1e-3) / 1e9, 2),
+        "wire_bytes": runs_t["splitzip"]["wire_bytes"],
+        "wire_ratio": round(n * elem / runs_t["splitzip"]["wire_bytes"], 6),
+        "speedup": round(runs_t["raw"]["total_ms"] / runs_t["splitzip"]["total_ms"], 4),
         "codec_ms_per_chunk": round(codec_ms, 4),
-        "codec_share": round(runs["splitzip"]["chunks"] * codec_ms / runs["splitzip"]["total_ms"], 4),
+        "codec_share": round(runs_t["splitzip"]["chunks"] * codec_ms / runs_t["splitzip"]["total_ms"], 4),
     }
     del staging
+    torch.cuda.synchronize()
     return calibration, formats, transfer
 
 

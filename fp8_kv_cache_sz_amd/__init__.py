@@ -26,7 +26,8 @@ TOP8 = SZ_FORMAT_TOP8
 TOP15S = SZ_FORMAT_TOP15_SENTINEL
 
 __all__ = ["BF16", "E5M2", "TOP16", "TOP8", "TOP15S", "Codebook", "SplitZipError", "calibrate", "calibrate_device",
-           "codebook_from_device", "encoded_size", "workspace_size", "workspace", "encode", "decode",
+           "codebook_from_device", "encoded_size", "workspace_size", "workspace", "decode_workspace_size",
+           "decode_workspace", "encode", "decode",
            "read_escape_count", "transfer", "transfer_buffers", "reference_copy", "profile_enable",
            "profile_collect"]
 
@@ -68,6 +69,35 @@ def _stream_handle(stream, device) -> int:
     return stream.cuda_stream
 
 
+def _side_stream(stream, device):
+    """The caller's stream when it is not the current one, else None.  On a
+    side stream the tensors this layer allocates are marked as used by it
+    (record_stream), and host reads of results wait for it first."""
+    if stream is None or stream == torch.cuda.current_stream(device):
+        return None
+    return stream
+
+
+def _adopt(side, device, tensors) -> None:
+    """Before a launch on a side stream: memory this layer just took from the
+    current stream's pool may still be in use by work queued there, so the
+    side stream waits for that work."""
+    if side is not None and any(t is not None for t in tensors):
+        side.wait_stream(torch.cuda.current_stream(device))
+
+
+def _owned_by(side, *tensors) -> None:
+    if side is not None:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(side)
+
+
+def _before_host_read(side) -> None:
+    if side is not None:
+        side.synchronize()
+
+
 def calibrate(t: torch.Tensor) -> Codebook:
     """Offline Top-16 calibration on the host (sz_calibrate)."""
     dtype = dtype_of(t)
@@ -87,15 +117,22 @@ def calibrate_device(t: torch.Tensor, sample_every: int = 1, out: torch.Tensor |
     if not t.is_contiguous():
         raise ValueError("calibrate_device needs a contiguous tensor")
     n = t.numel()
+    side = _side_stream(stream, t.device)
+    owned = []
     if out is None:
         out = torch.zeros(DEVICE_CODEBOOK_BYTES, dtype=torch.uint8, device=t.device)
+        owned.append(out)
     h = torch.empty(256 if dtype == BF16 else 32, dtype=torch.int64, device=t.device) if hist else None
+    owned.append(h)
     if ws is None:
         ws = torch.empty(_native.sz_calibrate_workspace_size(dtype), dtype=torch.uint8, device=t.device)
+        owned.append(ws)
+    _adopt(side, t.device, owned)       # also orders the zero fill of `out`
     rc = _native.sz_calibrate_device(dtype, t.data_ptr() if n else None, n, sample_every, out.data_ptr(),
                                      h.data_ptr() if h is not None else None, ws.data_ptr(), ws.numel(),
                                      _stream_handle(stream, t.device))
     _native.check("sz_calibrate_device", rc)
+    _owned_by(side, *owned)
     return (out, h) if hist else out
 
 
@@ -111,12 +148,25 @@ def encoded_size(dtype: int, n: int, n_escapes: int, fmt: int = TOP16) -> int:
     return _native.sz_encoded_size_format(fmt, dtype, n, n_escapes)
 
 
-def workspace_size(dtype: int, n: int) -> int:
-    return _native.sz_workspace_size(dtype, n)
+def workspace_size(dtype: int, n: int, fmt: int = TOP16) -> int:
+    """Bytes of encode workspace (sz_workspace_size / sz_workspace_size_format)."""
+    if fmt == TOP16:
+        return _native.sz_workspace_size(dtype, n)
+    return _native.sz_workspace_size_format(fmt, dtype, n)
 
 
-def workspace(dtype: int, n: int, device="cuda") -> torch.Tensor:
-    return torch.empty(workspace_size(dtype, n), dtype=torch.uint8, device=device)
+def decode_workspace_size(dtype: int, n: int) -> int:
+    """Bytes of decode workspace (sz_decode_workspace_size)."""
+    return _native.sz_decode_workspace_size(dtype, n)
+
+
+def workspace(dtype: int, n: int, device="cuda", fmt: int = TOP16) -> torch.Tensor:
+    """An encode workspace (also large enough for decode)."""
+    return torch.empty(workspace_size(dtype, n, fmt), dtype=torch.uint8, device=device)
+
+
+def decode_workspace(dtype: int, n: int, device="cuda") -> torch.Tensor:
+    return torch.empty(decode_workspace_size(dtype, n), dtype=torch.uint8, device=device)
 
 
 def read_escape_count(buf: torch.Tensor) -> int:
@@ -143,10 +193,15 @@ def encode(x: torch.Tensor, cb, out: torch.Tensor | None = None,
         raise ValueError("encode needs a contiguous tensor")
     n = x.numel()
     cap = encoded_size(dtype, n, n, fmt)
+    side = _side_stream(stream, x.device)
+    owned = []
     if out is None:
         out = torch.empty(max(cap, 1), dtype=torch.uint8, device=x.device)
+        owned.append(out)
     if ws is None:
-        ws = workspace(dtype, n, x.device)
+        ws = workspace(dtype, n, x.device, fmt)
+        owned.append(ws)
+    _adopt(side, x.device, owned)
     if fmt != TOP16:
         rc = _native.sz_encode_format(fmt, dtype, x.data_ptr() if n else None, n, cb.to_c(), out.data_ptr(),
                                       out.numel(), ws.data_ptr(), ws.numel(), _stream_handle(stream, x.device))
@@ -159,8 +214,10 @@ def encode(x: torch.Tensor, cb, out: torch.Tensor | None = None,
         rc = _native.sz_encode(dtype, x.data_ptr() if n else None, n, cb.to_c(), out.data_ptr(),
                                out.numel(), ws.data_ptr(), ws.numel(), _stream_handle(stream, x.device))
         _native.check("sz_encode", rc)
+    _owned_by(side, *owned)
     if not sync:
         return out, None, None
+    _before_host_read(side)
     if on_device:
         status = int(ws[:4].cpu().view(torch.int32)[0])
         if status != 0:
@@ -174,12 +231,17 @@ def decode(buf: torch.Tensor, dtype: int, n: int, out: torch.Tensor | None = Non
            in_bytes: int | None = None, fmt: int = TOP16) -> torch.Tensor:
     """Decode a device stream into ``n`` values.  With ``check`` the call
     synchronises and raises if the device-side validation failed."""
+    side = _side_stream(stream, buf.device)
+    owned = []
     if out is None:
         out = torch.empty(n, dtype=torch.bfloat16 if dtype == BF16 else torch.uint8, device=buf.device)
+        owned.append(out)
     if out.numel() * out.element_size() < n * _elem_size(dtype):
         raise ValueError("output tensor too small")
     if ws is None:
-        ws = workspace(dtype, n, buf.device)
+        ws = decode_workspace(dtype, n, buf.device)
+        owned.append(ws)
+    _adopt(side, buf.device, owned)
     nbytes = buf.numel() if in_bytes is None else in_bytes
     if fmt != TOP16:
         rc = _native.sz_decode_format(fmt, buf.data_ptr(), nbytes, dtype, out.data_ptr() if n else None, n,
@@ -189,7 +251,9 @@ def decode(buf: torch.Tensor, dtype: int, n: int, out: torch.Tensor | None = Non
         rc = _native.sz_decode(buf.data_ptr(), nbytes, dtype, out.data_ptr() if n else None, n,
                                ws.data_ptr(), ws.numel(), _stream_handle(stream, buf.device))
         _native.check("sz_decode", rc)
+    _owned_by(side, *owned)
     if check:
+        _before_host_read(side)
         status = int(ws[:4].cpu().view(torch.int32)[0])
         if status != 0:
             raise SplitZipError("sz_decode (device check)", status)

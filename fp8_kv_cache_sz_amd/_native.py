@@ -52,6 +52,10 @@ lib.sz_encoded_size.argtypes = [_i32, _u64, _u64]
 lib.sz_encoded_size.restype = _u64
 lib.sz_workspace_size.argtypes = [_i32, _u64]
 lib.sz_workspace_size.restype = _u64
+lib.sz_workspace_size_format.argtypes = [_i32, _i32, _u64]
+lib.sz_workspace_size_format.restype = _u64
+lib.sz_decode_workspace_size.argtypes = [_i32, _u64]
+lib.sz_decode_workspace_size.restype = _u64
 lib.sz_encode.argtypes = [_i32, _vp, _u64, ctypes.POINTER(sz_codebook), _vp, _u64, _vp, _u64, _vp]
 lib.sz_encode.restype = _i32
 lib.sz_encode_devcb.argtypes = [_i32, _vp, _u64, _vp, _vp, _u64, _vp, _u64, _vp]
@@ -82,7 +86,8 @@ lib.sz_profile_collect.restype = _i32
 lib.sz_reference_copy.argtypes = [_vp, _vp, _u64, _vp]
 lib.sz_reference_copy.restype = _i32
 
-EXPORTS = ("sz_calibrate", "sz_encoded_size", "sz_workspace_size", "sz_encode", "sz_encode_devcb",
+EXPORTS = ("sz_calibrate", "sz_encoded_size", "sz_workspace_size", "sz_workspace_size_format",
+           "sz_decode_workspace_size", "sz_encode", "sz_encode_devcb",
            "sz_calibrate_workspace_size", "sz_calibrate_device", "sz_decode", "sz_encoded_size_format",
            "sz_encode_format", "sz_decode_format", "sz_transfer_workspace_size", "sz_transfer_host_bytes",
            "sz_transfer", "sz_profile_enable", "sz_profile_collect", "sz_reference_copy")
@@ -116,6 +121,14 @@ def sz_encoded_size(dtype: int, n: int, n_escapes: int) -> int:
 
 def sz_workspace_size(dtype: int, n: int) -> int:
     return int(lib.sz_workspace_size(dtype, n))
+
+
+def sz_workspace_size_format(fmt: int, dtype: int, n: int) -> int:
+    return int(lib.sz_workspace_size_format(fmt, dtype, n))
+
+
+def sz_decode_workspace_size(dtype: int, n: int) -> int:
+    return int(lib.sz_decode_workspace_size(dtype, n))
 
 
 def sz_encode(dtype, d_in, n, cb, d_out, out_capacity, d_ws, ws_bytes, stream) -> int:

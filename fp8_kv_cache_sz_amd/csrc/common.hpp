@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -74,22 +75,47 @@ inline Geometry geometry(int dtype, uint64_t n, uint32_t version = 1)
     return g;
 }
 
-// Workspace layout (byte offsets): status word, tile counts, tile offsets
-// (encode) / block offsets (decode), escape staging (encode).
+// Escape staging.  Tiles with more escapes than kRederiveRecords are not
+// staged in streams of more than kFusedPrefixTiles tiles: the compaction
+// kernel derives their records again from the input, which moves 2 bytes per
+// element instead of writing and re-reading 3 bytes per escape.  Streams of
+// up to kFusedPrefixTiles tiles, whose compaction kernels have few waves, and
+// the ablation formats stage every tile.  A tile's staging slot holds the
+// most records it can stage.
+constexpr uint32_t kRederiveRecords = kEncTile / 4;
+constexpr uint64_t kFusedPrefixTiles = 2048;
+
+inline uint64_t stage_slot_bytes(uint32_t version, uint64_t nt)
+{
+    if (version == 3) return kEncTile;                         // one exponent byte per escape
+    if (version == 2 || nt <= kFusedPrefixTiles) return 3ull * kEncTile;
+    return 3ull * kRederiveRecords;
+}
+
+// Encode workspace layout (byte offsets): status words, tile counts, block
+// offsets, escape staging (stage_slot_bytes per tile).
 struct WsLayout {
-    uint64_t counts, offsets, stage, total;
+    uint64_t counts, offsets, stage, slot, total;
 };
 
-inline WsLayout ws_layout(int dtype, uint64_t n)
+inline WsLayout ws_layout(uint32_t version, int dtype, uint64_t n)
 {
-    Geometry g = geometry(dtype, n);
+    Geometry g = geometry(dtype, n, version);
     WsLayout w;
     w.counts = 256;
     w.offsets = w.counts + up256(4 * g.nt + 16);
-    const uint64_t offsets_bytes = std::max<uint64_t>(8 * g.nt, 8 * g.nb);
-    w.stage = w.offsets + up256(offsets_bytes + 16);
-    w.total = w.stage + up256(3 * g.nt * kEncTile + 16);
+    w.stage = w.offsets + up256(8 * g.nb + 16);
+    w.slot = stage_slot_bytes(version, g.nt);
+    // 16 bytes past the last slot: the record copies read whole words
+    w.total = w.stage + up256(w.slot * g.nt + 16);
     return w;
+}
+
+// Decode workspace layout: status words, then the block offsets.
+constexpr uint64_t kDecOffsets = 256;
+inline uint64_t decode_ws_bytes(int dtype, uint64_t n)
+{
+    return kDecOffsets + up256(8 * geometry(dtype, n).nb + 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -327,8 +353,12 @@ struct ProfRecord {
 };
 
 // Instrumentation state (defined with sz_profile_enable / sz_profile_collect).
+// g_prof_on is read without the lock on every launch, so launches never
+// serialise on the mutex while instrumentation is off (its default); the
+// mutex guards the event pool and the records, which exist only while it is
+// on.
 extern std::mutex g_prof_mutex;
-extern bool g_prof_on;
+extern std::atomic<bool> g_prof_on;
 extern std::vector<ProfRecord> g_prof_records;
 extern std::vector<hipEvent_t> g_event_pool;
 hipEvent_t take_event();
@@ -340,8 +370,9 @@ struct LaunchScope {
     hipEvent_t start = nullptr, stop = nullptr;
     LaunchScope(const char *n, hipStream_t s) : name(n), stream(s)
     {
+        if (!g_prof_on.load(std::memory_order_acquire)) return;
         std::lock_guard<std::mutex> lock(g_prof_mutex);
-        if (!g_prof_on) return;
+        if (!g_prof_on.load(std::memory_order_relaxed)) return;
         start = take_event();
         stop = take_event();
         if (start && stop) (void)hipEventRecord(start, stream);

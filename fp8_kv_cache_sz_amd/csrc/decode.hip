@@ -885,12 +885,11 @@ int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype
     if (!d_in || !d_ws || (n_elems && !d_out)) return SZ_E_ARG;
     if (!aligned16(d_in) || !aligned16(d_ws) || (n_elems && !aligned16(d_out))) return SZ_E_ALIGN;
     if (in_bytes < encoded_size_v(version, dtype, n_elems, 0)) return SZ_E_FORMAT;
-    if (ws_bytes < sz_workspace_size(dtype, n_elems)) return SZ_E_WORKSPACE;
+    if (ws_bytes < decode_ws_bytes(dtype, n_elems)) return SZ_E_WORKSPACE;
     const Geometry g = geometry(dtype, n_elems, version);
-    const WsLayout w = ws_layout(dtype, n_elems);
     uint8_t *ws = static_cast<uint8_t *>(d_ws);
     int32_t *status = reinterpret_cast<int32_t *>(ws);
-    uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
+    uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + kDecOffsets);
     hipStream_t s = static_cast<hipStream_t>(stream);
     DecodeArgs a;
     a.n = g.n;
@@ -936,6 +935,12 @@ int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype
 }  // namespace sz
 
 using namespace sz;
+
+extern "C" uint64_t sz_decode_workspace_size(int dtype, uint64_t n_elems)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return 0;
+    return decode_ws_bytes(dtype, n_elems);
+}
 
 extern "C" int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
                          void *d_ws, uint64_t ws_bytes, void *stream)

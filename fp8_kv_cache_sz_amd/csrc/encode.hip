@@ -282,13 +282,8 @@ __device__ __forceinline__ void put_records(uint8_t *tstage, uint32_t rank, uint
 
 // Rows with more escapes than this go through the LDS segment buffer.
 constexpr uint32_t kDirectRecords = 32;
-// Tiles with more escapes than this are not staged: the compaction kernel
-// derives their records again from the input, which moves 2 bytes per
-// element instead of writing and re-reading 3 bytes per escape.  Their tile
-// count carries kRederiveFlag.  Streams of up to kFusedPrefixTiles tiles,
-// whose compaction kernels have few waves, stage every tile (kStageAll; see
-// sz_enc_compact_small and sz_enc_compact_fused).
-constexpr uint32_t kRederiveRecords = kEncTile / 4;
+// Tiles above the re-derive limit (kRederiveRecords, or none: kStageAll)
+// stage nothing; their tile count carries kRederiveFlag.
 constexpr uint32_t kStageAll = 0xFFFFFFFFu;
 constexpr uint32_t kRederiveFlag = 0x80000000u;
 
@@ -333,7 +328,8 @@ __global__ __launch_bounds__(kEncTile / (8 * C)) void sz_enc_dense_bf16(const ui
                                                               uint64_t off_sm, Codebook4 cb,
                                                               const uint32_t *__restrict__ cb_dev,
                                                               uint32_t *__restrict__ tile_counts,
-                                                              uint8_t *__restrict__ stage, uint32_t rederive_above)
+                                                              uint8_t *__restrict__ stage, uint32_t slot,
+                                                              uint32_t rederive_above)
 {
     // C chunks of 8 elements per lane: a wave row is 512 C elements, a tile
     // 16384 / (512 C) waves
@@ -429,7 +425,7 @@ __global__ __launch_bounds__(kEncTile / (8 * C)) void sz_enc_dense_bf16(const ui
     // only the Top-16 format re-derives escape-heavy tiles in the compaction
     const bool rederive = V == kTop16 && tile_total > rederive_above;
     if (wave_total && !rederive) {
-        uint8_t *tstage = stage + tile * (3ull * kEncTile);
+        uint8_t *tstage = stage + tile * slot;
 #pragma unroll
         for (int j = 0; j < C; ++j) {
             const uint32_t pos0 = (uint32_t)((base + (uint64_t)(j * 64 + lane) * 8) & 0xFFFFu);
@@ -472,7 +468,8 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
                                                               Codebook4 cb,
                                                               const uint32_t *__restrict__ cb_dev,
                                                               uint32_t *__restrict__ tile_counts,
-                                                              uint8_t *__restrict__ stage, uint32_t rederive_above)
+                                                              uint8_t *__restrict__ stage, uint32_t slot,
+                                                              uint32_t rederive_above)
 {
     __shared__ uint32_t table32[64];
     __shared__ uint32_t table16x2[512];
@@ -550,7 +547,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
     uint32_t tile_total;
     const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
     if (wave_total && tile_total <= rederive_above) {
-        uint8_t *tstage = stage + tile * (3ull * kEncTile);
+        uint8_t *tstage = stage + tile * slot;
         uint8_t *buf = seg_buf[wave];
 #pragma unroll
         for (int j = 0; j < kE5Chunks; ++j) {
@@ -901,7 +898,7 @@ template <int DT>
 __device__ __forceinline__ void compact_block(const uint8_t *__restrict__ stage, uint32_t meta, uint64_t b,
                                               uint64_t off, uint8_t *__restrict__ out, uint64_t off_esc,
                                               const void *__restrict__ in, uint64_t n, const uint8_t *table,
-                                              uint8_t *buf, uint32_t item)
+                                              uint8_t *buf, uint32_t item, uint32_t slot)
 {
     const uint32_t lane = lane_id();
     const uint64_t t0 = kTilesPerBlock * b;
@@ -924,7 +921,7 @@ __device__ __forceinline__ void compact_block(const uint8_t *__restrict__ stage,
                 k = cnt[t];
                 bef = before[t];
             }
-        if (k) copy_records(stage + (t0 + g) * (3ull * kEncTile), out, off_esc + item * (off + bef), item * k, lane & 15, 16);
+        if (k) copy_records(stage + (t0 + g) * (uint64_t)slot, out, off_esc + item * (off + bef), item * k, lane & 15, 16);
         return;
     }
 #pragma unroll
@@ -939,7 +936,7 @@ __device__ __forceinline__ void compact_block(const uint8_t *__restrict__ stage,
                 rederive_tile_e5m2(static_cast<const uint8_t *>(in), n, t0 + t, table, buf, out + (dst0 & ~uint64_t(3)),
                                    (uint32_t)(dst0 & 3));
         } else {
-            copy_records(stage + (t0 + t) * (3ull * kEncTile), out, dst0, item * cnt[t], lane, 64);
+            copy_records(stage + (t0 + t) * (uint64_t)slot, out, dst0, item * cnt[t], lane, 64);
         }
     }
 }
@@ -949,7 +946,7 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
     const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
     uint64_t nb, const void *__restrict__ in, uint64_t n, Codebook4 cb, const uint32_t *__restrict__ cb_dev,
-    uint32_t item)
+    uint32_t item, uint32_t slot)
 {
     __shared__ uint32_t table32[64];
     __shared__ __align__(16) uint8_t seg_buf[kCompactThreads / 64][kSegBytes];
@@ -967,7 +964,7 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
     const uint64_t off = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(meta >> 32), kTilesPerBlock) << 32) |
                          (uint32_t)__builtin_amdgcn_readlane((uint32_t)meta, kTilesPerBlock);
     compact_block<DT>(stage, (uint32_t)meta, b, off, out, off_esc, in, n, reinterpret_cast<const uint8_t *>(table32),
-                      seg_buf[threadIdx.x / 64], item);
+                      seg_buf[threadIdx.x / 64], item, slot);
 }
 
 // ---------------------------------------------------------------------------
@@ -990,13 +987,12 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
 // ---------------------------------------------------------------------------
 constexpr uint32_t kFusedThreads = 1024;
 constexpr uint32_t kFusedBlocks = kFusedThreads / 64;
-constexpr uint64_t kFusedPrefixTiles = 2048;
 
 template <int DT>
 __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_compact_fused(
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts, uint8_t *__restrict__ out,
     uint64_t off_esc, uint64_t nt, const void *__restrict__ in, HeaderArgs h, const uint32_t *__restrict__ cb_dev,
-    int32_t *__restrict__ status, uint32_t item)
+    int32_t *__restrict__ status, uint32_t item, uint32_t slot)
 {
     __shared__ uint32_t table32[64];
     __shared__ __align__(16) uint8_t seg_buf[kFusedBlocks][kSegBytes];
@@ -1053,7 +1049,7 @@ __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(8
     if (blockIdx.x == 0) write_header(out, h, cb, verdict, nb == 0, status);
     if (b >= nb) return;
     compact_block<DT>(stage, meta, b, off, out, off_esc, in, h.n, reinterpret_cast<const uint8_t *>(table32),
-                      seg_buf[wave], item);
+                      seg_buf[wave], item, slot);
 }
 
 // ---------------------------------------------------------------------------
@@ -1080,7 +1076,7 @@ template <int DT>
 __global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_compact_small(
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts, uint8_t *__restrict__ out,
     uint64_t off_esc, uint64_t nt, const void *__restrict__ in, HeaderArgs h, const uint32_t *__restrict__ cb_dev,
-    int32_t *__restrict__ status, uint32_t item)
+    int32_t *__restrict__ status, uint32_t item, uint32_t slot)
 {
     __shared__ uint32_t table32[64];
     __shared__ __align__(16) uint8_t seg_buf[kTilesPerBlock][kSegBytes];
@@ -1149,7 +1145,7 @@ __global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(8
                                    out + (dst0 & ~uint64_t(3)), (uint32_t)(dst0 & 3));
         }
     } else {
-        copy_records(stage + (t0 + g) * (3ull * kEncTile), out, dst0, item * k, tid % kSmallGroup, kSmallGroup);
+        copy_records(stage + (t0 + g) * (uint64_t)slot, out, dst0, item * k, tid % kSmallGroup, kSmallGroup);
     }
 }
 
@@ -1173,9 +1169,9 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
     if (!d_out || !d_ws || (n_elems && !d_in)) return SZ_E_ARG;
     if (!aligned16(d_out) || !aligned16(d_ws) || (n_elems && !aligned16(d_in))) return SZ_E_ALIGN;
     if (out_capacity < encoded_size_v(version, dtype, n_elems, n_elems)) return SZ_E_CAPACITY;
-    if (ws_bytes < sz_workspace_size(dtype, n_elems)) return SZ_E_WORKSPACE;
+    const WsLayout w = ws_layout(version, dtype, n_elems);
+    if (ws_bytes < w.total) return SZ_E_WORKSPACE;
     const Geometry g = geometry(dtype, n_elems, version);
-    const WsLayout w = ws_layout(dtype, n_elems);
     uint8_t *ws = static_cast<uint8_t *>(d_ws);
     uint8_t *out = static_cast<uint8_t *>(d_out);
     int32_t *status = reinterpret_cast<int32_t *>(ws);
@@ -1191,29 +1187,29 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
         if (version == kTop8) {
             LaunchScope scope("sz_enc_dense_top8", s);
             hipLaunchKernelGGL(sz_enc_dense_bf16<kTop8>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16, g.n,
-                               out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, rederive_above);
+                               out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, (uint32_t)w.slot, rederive_above);
         } else if (version == kTop15S) {
             LaunchScope scope("sz_enc_dense_top15s", s);
             hipLaunchKernelGGL(sz_enc_dense_bf16<kTop15S>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16,
-                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, rederive_above);
+                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, (uint32_t)w.slot, rederive_above);
         } else if (g.nt <= kSmallEncodeTiles) {
             LaunchScope scope("sz_enc_dense_bf16", s);
             hipLaunchKernelGGL((sz_enc_dense_bf16<kTop16, 2>), dim3((uint32_t)g.nt), dim3(kEncTile / 16), 0, s,
-                               in16, g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, rederive_above);
+                               in16, g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, (uint32_t)w.slot, rederive_above);
         } else if (g.nt <= kMidEncodeTiles) {
             LaunchScope scope("sz_enc_dense_bf16", s);
             hipLaunchKernelGGL((sz_enc_dense_bf16<kTop16, 4>), dim3((uint32_t)g.nt), dim3(kEncTile / 32), 0, s,
-                               in16, g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, rederive_above);
+                               in16, g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, (uint32_t)w.slot, rederive_above);
         } else {
             LaunchScope scope("sz_enc_dense_bf16", s);
             hipLaunchKernelGGL(sz_enc_dense_bf16<kTop16>, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s, in16,
-                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, rederive_above);
+                               g.n, out, g.off_nib, g.off_sm, cb4, cb_dev, tile_counts, stage, (uint32_t)w.slot, rederive_above);
         }
     } else if (g.nt) {
         LaunchScope scope("sz_enc_dense_e5m2", s);
         hipLaunchKernelGGL(sz_enc_dense_e5m2, dim3((uint32_t)g.nt), dim3(kEncThreads), 0, s,
                            static_cast<const uint8_t *>(d_in), g.n, out, g.off_nib, g.off_sm, g.sm_bytes,
-                           cb4, cb_dev, tile_counts, stage, rederive_above);
+                           cb4, cb_dev, tile_counts, stage, (uint32_t)w.slot, rederive_above);
     }
     {
         HeaderArgs h;
@@ -1236,10 +1232,10 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
                 if (dtype == SZ_BF16)
                     hipLaunchKernelGGL(sz_enc_compact_small<SZ_BF16>, dim3(blocks), dim3(kSmallThreads), 0, s, stage,
                                        tile_counts, out, g.off_esc, g.nt, d_in, h, cb_dev, status,
-                                       escape_item_bytes(version));
+                                       escape_item_bytes(version), (uint32_t)w.slot);
                 else
                     hipLaunchKernelGGL(sz_enc_compact_small<SZ_FP8_E5M2>, dim3(blocks), dim3(kSmallThreads), 0, s,
-                                       stage, tile_counts, out, g.off_esc, g.nt, d_in, h, cb_dev, status, 3u);
+                                       stage, tile_counts, out, g.off_esc, g.nt, d_in, h, cb_dev, status, 3u, (uint32_t)w.slot);
                 return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
             }
             const uint32_t groups = (uint32_t)std::max<uint64_t>(1, (g.nb + kFusedBlocks - 1) / kFusedBlocks);
@@ -1247,10 +1243,10 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
             if (dtype == SZ_BF16)
                 hipLaunchKernelGGL(sz_enc_compact_fused<SZ_BF16>, dim3(groups), dim3(kFusedThreads), 0, s, stage,
                                    tile_counts, out, g.off_esc, g.nt, d_in, h, cb_dev, status,
-                                   escape_item_bytes(version));
+                                   escape_item_bytes(version), (uint32_t)w.slot);
             else
                 hipLaunchKernelGGL(sz_enc_compact_fused<SZ_FP8_E5M2>, dim3(groups), dim3(kFusedThreads), 0, s, stage,
-                                   tile_counts, out, g.off_esc, g.nt, d_in, h, cb_dev, status, 3u);
+                                   tile_counts, out, g.off_esc, g.nt, d_in, h, cb_dev, status, 3u, (uint32_t)w.slot);
             return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
         }
         LaunchScope scope("sz_enc_scan", s);
@@ -1263,10 +1259,10 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
         if (dtype == SZ_BF16)
             hipLaunchKernelGGL(sz_enc_compact<SZ_BF16>, dim3(groups), dim3(kCompactThreads), 0, s, stage, tile_counts,
                                block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev,
-                               escape_item_bytes(version));
+                               escape_item_bytes(version), (uint32_t)w.slot);
         else
             hipLaunchKernelGGL(sz_enc_compact<SZ_FP8_E5M2>, dim3(groups), dim3(kCompactThreads), 0, s, stage,
-                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev, 3u);
+                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev, 3u, (uint32_t)w.slot);
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }
@@ -1285,7 +1281,14 @@ extern "C" uint64_t sz_encoded_size(int dtype, uint64_t n_elems, uint64_t n_esca
 extern "C" uint64_t sz_workspace_size(int dtype, uint64_t n_elems)
 {
     if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return 0;
-    return ws_layout(dtype, n_elems).total;
+    return ws_layout(kTop16, dtype, n_elems).total;
+}
+
+extern "C" uint64_t sz_workspace_size_format(int format, int dtype, uint64_t n_elems)
+{
+    if (format == SZ_FORMAT_TOP16) return sz_workspace_size(dtype, n_elems);
+    if ((format != SZ_FORMAT_TOP8 && format != SZ_FORMAT_TOP15_SENTINEL) || dtype != SZ_BF16) return 0;
+    return ws_layout((uint32_t)format, dtype, n_elems).total;
 }
 
 extern "C" int sz_encode(int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *cb, void *d_out,

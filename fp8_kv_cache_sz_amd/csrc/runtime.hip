@@ -6,7 +6,7 @@
 namespace sz {
 
 std::mutex g_prof_mutex;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};
 std::vector<ProfRecord> g_prof_records;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -77,7 +77,7 @@ extern "C" int sz_profile_enable(int on)
         (void)hipEventSynchronize(r.stop);
     }
     release_records();
-    g_prof_on = on != 0;
+    g_prof_on.store(on != 0, std::memory_order_release);
     return SZ_OK;
 }
 

@@ -24,7 +24,6 @@
 #include <chrono>
 #include <cstdint>
 #include <cstring>
-#include <mutex>
 #include <vector>
 
 #include "splitzip.h"
@@ -32,37 +31,32 @@
 namespace {
 
 constexpr int kMaxDepth = 8;
-constexpr int kMaxDevices = 64;
 constexpr uint64_t kHeaderBytes = 64;
 
 uint64_t up256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 
+// The pipeline's streams, created by each sz_transfer call and destroyed
+// before it returns (the library keeps no streams between calls): default
+// priority, non-blocking with respect to the null stream; `dec` is `enc`.
 struct PipelineStreams {
     hipStream_t enc = nullptr, d2h = nullptr, h2d = nullptr, dec = nullptr;
-    bool ready = false;
-};
-
-std::mutex g_stream_mutex;
-PipelineStreams g_streams[kMaxDevices];
-
-// The pipeline's streams on the current device, created once (default
-// priority, non-blocking with respect to the null stream); `dec` is `enc`.
-int pipeline_streams(PipelineStreams &out)
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SZ_E_HIP;
-    std::lock_guard<std::mutex> lock(g_stream_mutex);
-    PipelineStreams &p = g_streams[dev];
-    if (!p.ready) {
-        hipStream_t *all[3] = {&p.enc, &p.d2h, &p.h2d};
+    int create()
+    {
+        hipStream_t *all[3] = {&enc, &d2h, &h2d};
         for (hipStream_t *s : all)
             if (hipStreamCreateWithFlags(s, hipStreamNonBlocking) != hipSuccess) return SZ_E_HIP;
-        p.dec = p.enc;
-        p.ready = true;
+        dec = enc;
+        return SZ_OK;
     }
-    out = p;
-    return SZ_OK;
-}
+    ~PipelineStreams()
+    {
+        // every use has been synchronised by then; destroying waits for the
+        // stream's work anyway
+        hipStream_t all[3] = {enc, d2h, h2d};
+        for (hipStream_t s : all)
+            if (s) (void)hipStreamDestroy(s);
+    }
+};
 
 struct Events {
     std::vector<hipEvent_t> all;
@@ -107,8 +101,9 @@ __global__ void sz_copy_words(const uint32_t *__restrict__ src, uint32_t *__rest
 extern "C" uint64_t sz_transfer_workspace_size(int dtype, uint64_t chunk_elems, int depth)
 {
     if ((dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) || depth < 1 || depth > kMaxDepth) return 0;
-    // send and receive slot buffers, then one encode and one decode workspace
-    return 2 * (uint64_t)depth * slot_bytes(dtype, chunk_elems) + 2 * up256(sz_workspace_size(dtype, chunk_elems));
+    // send and receive slot buffers, then the encode and the decode workspace
+    return 2 * (uint64_t)depth * slot_bytes(dtype, chunk_elems) + up256(sz_workspace_size(dtype, chunk_elems)) +
+           up256(sz_decode_workspace_size(dtype, chunk_elems));
 }
 
 extern "C" uint64_t sz_transfer_host_bytes(int dtype, uint64_t n_elems, uint64_t chunk_elems, int depth)
@@ -131,7 +126,7 @@ extern "C" int sz_transfer(int dtype, const void *d_src, uint64_t n_elems, uint6
     if (ws_bytes < sz_transfer_workspace_size(dtype, chunk_elems, depth)) return SZ_E_WORKSPACE;
 
     PipelineStreams st;
-    int rc = pipeline_streams(st);
+    int rc = st.create();
     if (rc) return rc;
     const uint64_t esz = elem_bytes(dtype);
     const uint64_t chunks = chunk_count(n_elems, chunk_elems);
@@ -141,6 +136,7 @@ extern "C" int sz_transfer(int dtype, const void *d_src, uint64_t n_elems, uint6
     uint8_t *recv = dws + (uint64_t)depth * slot;                // depth slots
     uint8_t *enc_ws = dws + 2 * (uint64_t)depth * slot;
     const uint64_t codec_ws = up256(sz_workspace_size(dtype, chunk_elems));
+    const uint64_t dec_ws_bytes = up256(sz_decode_workspace_size(dtype, chunk_elems));
     uint8_t *dec_ws = enc_ws + codec_ws;
     uint8_t *wire = static_cast<uint8_t *>(h_staging);
     uint8_t *headers = wire + (uint64_t)depth * slot;
@@ -227,7 +223,7 @@ extern "C" int sz_transfer(int dtype, const void *d_src, uint64_t n_elems, uint6
                 SZ_HIP_TRY(hipMemcpyAsync(recv + k * slot, wire + k * slot, bytes, hipMemcpyHostToDevice, st.h2d));
                 SZ_HIP_TRY(hipEventRecord(received[k], st.h2d));
                 SZ_HIP_TRY(hipStreamWaitEvent(st.dec, received[k], 0));
-                rc = sz_decode(recv + k * slot, bytes, dtype, dst + i * chunk_elems * esz, m, dec_ws, codec_ws, st.dec);
+                rc = sz_decode(recv + k * slot, bytes, dtype, dst + i * chunk_elems * esz, m, dec_ws, dec_ws_bytes, st.dec);
                 if (rc) return rc;
                 hipLaunchKernelGGL(sz_copy_words, dim3(1), dim3(64), 0, st.dec, reinterpret_cast<const uint32_t *>(dec_ws),
                                    reinterpret_cast<uint32_t *>(statuses_dev + i), 1u);

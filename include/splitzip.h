@@ -29,8 +29,12 @@
  *       size    = off_esc + 3E
  *     Escaped elements carry code 0.  All padding and reserved bytes are 0.
  *   - Device pointers must be 16-byte aligned (torch allocations are).
- *     The caller allocates and owns every buffer; the library keeps no
- *     buffers between calls.
+ *     The caller allocates and owns every buffer.  The library keeps no
+ *     state between calls (no buffers, streams or caches) and takes no lock
+ *     on the codec path, so calls on different streams with their own
+ *     workspaces run concurrently.  The one process-wide state is the
+ *     optional instrumentation record (sz_profile_enable): while it is off,
+ *     its default, a launch only reads an atomic flag.
  *   - Device calls only enqueue work on `stream` (a hipStream_t; NULL is the
  *     null stream) and return once it is launched.  Calls that share a
  *     workspace must not overlap.  sz_encode, sz_encode_devcb,
@@ -66,7 +70,7 @@ enum {
     SZ_E_ALIGN = -4,     /* device pointer not 16-byte aligned */
     SZ_E_FORMAT = -5,    /* malformed or truncated stream */
     SZ_E_HIP = -6,       /* a HIP launch or runtime call failed */
-    SZ_E_WORKSPACE = -7  /* workspace smaller than sz_workspace_size() */
+    SZ_E_WORKSPACE = -7  /* workspace smaller than the call's *_workspace_size() */
 };
 
 /* Top-16 exponent codebook: exp[c] is the exponent that code c stands for.
@@ -91,11 +95,21 @@ int sz_calibrate(int dtype, const void *host_data, uint64_t n_elems, sz_codebook
  * as output capacity.  Returns 0 for an unknown dtype. */
 uint64_t sz_encoded_size(int dtype, uint64_t n_elems, uint64_t n_escapes);
 
-/* Device workspace that sz_encode and sz_decode need for n_elems values
- * (tile escape counts and offsets, block offsets, the status word and the
- * escape staging area of up to 3 bytes per element).  Returns 0 for an
+/* Device workspace that sz_encode (and sz_encode_devcb) needs for n_elems
+ * values: the status word, tile escape counts, block offsets and the escape
+ * staging area.  Staging takes one slot per 16384-element tile: 49,152
+ * bytes (3 per element) for streams of up to 2,048 tiles (32M elements),
+ * whose tiles are all staged, and 12,288 bytes above that, where a tile
+ * with more than 4,096 escapes stages nothing (the compaction derives its
+ * records again from the input).  About 3 bytes per element up to 32M
+ * elements, 0.75 above.  Also enough for sz_decode.  Returns 0 for an
  * unknown dtype. */
 uint64_t sz_workspace_size(int dtype, uint64_t n_elems);
+
+/* Device workspace that sz_decode (and sz_decode_format) needs for n_elems
+ * values: the status words (256 bytes) and one u64 escape offset per 64K
+ * block, 8 bytes per 65,536 elements.  Returns 0 for an unknown dtype. */
+uint64_t sz_decode_workspace_size(int dtype, uint64_t n_elems);
 
 /* Encode (page: Method, encoding bullets).  d_in: n_elems raw values on the
  * device.  d_out: stream buffer of out_capacity >= sz_encoded_size(dtype,
@@ -163,12 +177,17 @@ int sz_calibrate_device(int dtype, const void *d_in, uint64_t n_elems, uint64_t 
  * number exactly its count (format 3).  sz_encoded_size_format returns 0
  * for an unknown format or a dtype other than BF16 with formats 2 and 3;
  * the calls return SZ_E_ARG for an unknown format and SZ_E_DTYPE for E5M2
- * with formats 2 and 3.  Workspace, capacity, alignment and status rules as
- * for sz_encode / sz_decode; the output capacity is
- * sz_encoded_size_format(format, dtype, n_elems, n_elems). */
+ * with formats 2 and 3.  Capacity, alignment and status rules as for
+ * sz_encode / sz_decode; the output capacity is
+ * sz_encoded_size_format(format, dtype, n_elems, n_elems).  These formats
+ * stage every tile, so sz_encode_format needs
+ * sz_workspace_size_format(format, dtype, n_elems) bytes of workspace (3
+ * bytes per element for Top-8, 1 for Top-15 + sentinel; 0 for an unknown
+ * format or dtype); sz_decode_format needs sz_decode_workspace_size. */
 enum { SZ_FORMAT_TOP16 = 1, SZ_FORMAT_TOP8 = 2, SZ_FORMAT_TOP15_SENTINEL = 3 };
 
 uint64_t sz_encoded_size_format(int format, int dtype, uint64_t n_elems, uint64_t n_escapes);
+uint64_t sz_workspace_size_format(int format, int dtype, uint64_t n_elems);
 int sz_encode_format(int format, int dtype, const void *d_in, uint64_t n_elems, const sz_codebook *cb,
                      void *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes, void *stream);
 int sz_decode_format(int format, const void *d_in, uint64_t in_bytes, int dtype, void *d_out,
@@ -222,7 +241,7 @@ int sz_transfer(int dtype, const void *d_src, uint64_t n_elems, uint64_t chunk_e
 /* Decode (page: Method, decoding bullets: dense unpack + lookup table, then
  * the sparse escape stream overwrites the escaped exponents).  d_in: a
  * stream of in_bytes bytes on the device.  d_out: n_elems values.  d_ws:
- * ws_bytes >= sz_workspace_size(dtype, n_elems).  The host checks the
+ * ws_bytes >= sz_decode_workspace_size(dtype, n_elems).  The host checks the
  * arguments and in_bytes >= sz_encoded_size(dtype, n_elems, 0); the device
  * checks the header (magic, version, dtype, N, nb), the escape counts (each
  * at most its block length, summing to E), that the E records fit in

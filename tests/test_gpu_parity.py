@@ -43,7 +43,8 @@ def _encode_gpu(x, cb_exps, dtype):
 def _decode_gpu(stream_dev, dtype, n, in_bytes=None, check=True):
     sz = _sz()
     out = torch.full((max(n, 1) * (2 if dtype == 0 else 1),), POISON, dtype=torch.uint8, device="cuda")
-    ws = torch.full((sz.workspace_size(dtype, n),), POISON, dtype=torch.uint8, device="cuda")
+    # exactly the decode workspace: the kernels must stay inside it
+    ws = torch.full((sz.decode_workspace_size(dtype, n),), POISON, dtype=torch.uint8, device="cuda")
     view = out.view(torch.bfloat16) if dtype == 0 else out
     sz.decode(stream_dev, dtype, n, out=view[:n] if n else view[:0], ws=ws, check=check, in_bytes=in_bytes)
     return out, ws
@@ -311,6 +312,30 @@ def test_concurrent_streams_with_own_workspaces():
         assert size == expect.size
         assert np.array_equal(buf[:size].cpu().numpy(), expect)
         assert int(ws_dec[:4].cpu().view(torch.int32)[0]) == 0
+        assert torch.equal(y.view(torch.int16), x.view(torch.int16))
+
+
+def test_side_stream_with_library_allocations():
+    """encode / decode on a side stream with their default host reads
+    (size, escape count, decode status) and buffers the Python layer
+    allocates itself: the reads wait for the side stream, and memory taken
+    from the current stream's pool is not reused while the side stream
+    still works on it."""
+    sz = _sz()
+    cb = sz.calibrate(synth.calibration_tensor("kv1m"))
+    s = torch.cuda.Stream()
+    for name in ("stress_t3", "llama3_8b_kv"):
+        x = synth.workload(name, size="small")[0].cuda()
+        n = x.numel()
+        expect = oracle.encode(synth.as_bits_numpy(x), 0, list(cb.exps))
+        junk = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        junk.fill_(7)                      # current-stream work queued ahead of the side stream
+        del junk
+        buf, size, esc = sz.encode(x, cb, stream=s)
+        assert size == expect.size and esc == int(expect[16:24].view(np.uint64)[0])
+        y = sz.decode(buf[:size], 0, n, stream=s)
+        s.synchronize()
+        assert np.array_equal(buf[:size].cpu().numpy(), expect)
         assert torch.equal(y.view(torch.int16), x.view(torch.int16))
 
 

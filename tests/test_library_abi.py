@@ -76,11 +76,28 @@ def test_encoded_size_matches_oracle():
                 assert nat.sz_encoded_size(dtype, n, e) == oracle.encoded_size(dtype, n, e), (dtype, n, e)
     assert nat.sz_encoded_size(9, 10, 0) == 0
     assert nat.sz_workspace_size(9, 10) == 0
+    up = lambda x: (x + 255) // 256 * 256
     for dtype in (0, 1):
-        for n in (0, 1, 1 << 20, 1879048192):
+        for n in (0, 1, 1 << 20, (1 << 25) - 1, 1 << 25, (1 << 25) + 1, 1879048192):
             ws = nat.sz_workspace_size(dtype, n)
-            assert ws >= 256 and ws % 256 == 0
-            assert ws >= 3 * n                      # escape staging, 3 bytes per element
+            nt, nb = (n + 16383) // 16384, (n + 65535) // 65536
+            assert ws % 256 == 0
+            # status, tile counts, block offsets, then one staging slot per
+            # 16K tile: 3 bytes per element up to 2,048 tiles, 12 KB per tile
+            # (4,096 records) above
+            slot = 3 * 16384 if nt <= 2048 else 3 * 4096
+            assert ws == 256 + up(4 * nt + 16) + up(8 * nb + 16) + up(slot * nt + 16), (dtype, n)
+            dws = nat.sz_decode_workspace_size(dtype, n)
+            assert dws == 256 + up(8 * nb + 16) and dws <= ws
+            if dtype == 0:
+                assert nat.sz_workspace_size_format(1, 0, n) == ws
+                assert nat.sz_workspace_size_format(2, 0, n) == 256 + up(4 * nt + 16) + up(8 * nb + 16) + \
+                    up(3 * 16384 * nt + 16)
+                assert nat.sz_workspace_size_format(3, 0, n) == 256 + up(4 * nt + 16) + up(8 * nb + 16) + \
+                    up(16384 * nt + 16)
+            else:
+                assert nat.sz_workspace_size_format(2, 1, n) == 0 and nat.sz_workspace_size_format(3, 1, n) == 0
+    assert nat.sz_decode_workspace_size(9, 10) == 0 and nat.sz_workspace_size_format(4, 0, 10) == 0
 
 
 @pytest.mark.parametrize("source", ["kv1m", "bruteforce", "random_cb_data", "empty"])
@@ -132,6 +149,8 @@ def test_host_argument_checks():
     assert nat.sz_decode(dummy, fixed, 3, dummy, 1000, dummy, 1 << 30, None) == -2
     assert nat.sz_decode(dummy + 8, fixed, 0, dummy, 1000, dummy, 1 << 30, None) == -4
     assert nat.sz_decode(dummy, fixed, 0, dummy, 1000, dummy, 16, None) == -7
+    dws = nat.sz_decode_workspace_size(0, 1000)
+    assert nat.sz_decode(dummy, fixed, 0, dummy, 1000, dummy, dws - 1, None) == -7
 
 
 def test_host_argument_checks_device_calibration():
@@ -173,7 +192,7 @@ def test_host_argument_checks_formats():
             assert nat.sz_encoded_size_format(fmt, 0, n, e) == oracle.encoded_size_variant(fmt, n, e)
         assert nat.sz_encoded_size_format(fmt, 1, 100, 0) == 0
         cap = nat.sz_encoded_size_format(fmt, 0, 16, 16)
-        ws = nat.sz_workspace_size(0, 16)
+        ws = nat.sz_workspace_size_format(fmt, 0, 16)
         assert nat.sz_encode_format(fmt, 1, dummy, 16, cb, dummy, cap, dummy, ws, None) == -2
         assert nat.sz_decode_format(fmt, dummy, 1 << 20, 1, dummy, 16, dummy, ws, None) == -2
         assert nat.sz_encode_format(fmt, 0, dummy, 16, cb, dummy, cap - 1, dummy, ws, None) == -3
@@ -202,7 +221,8 @@ def test_host_argument_checks_transfer():
     ws = nat.sz_transfer_workspace_size(0, 65536, 3)
     hb = nat.sz_transfer_host_bytes(0, 1 << 20, 65536, 3)
     slot = (nat.sz_encoded_size(0, 65536, 65536) + 255) // 256 * 256
-    assert ws == 2 * 3 * slot + 2 * ((nat.sz_workspace_size(0, 65536) + 255) // 256 * 256)
+    assert ws == 2 * 3 * slot + (nat.sz_workspace_size(0, 65536) + 255) // 256 * 256 + \
+        (nat.sz_decode_workspace_size(0, 65536) + 255) // 256 * 256
     assert hb == 3 * slot + 3 * 64 + 256
     assert nat.sz_transfer_workspace_size(0, 65536, 0) == 0 and nat.sz_transfer_workspace_size(0, 65536, 9) == 0
     assert nat.sz_transfer_host_bytes(5, 100, 16, 1) == 0
