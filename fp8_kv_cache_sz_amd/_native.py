@@ -26,7 +26,7 @@ SZ_FP8_E5M2 = 1
 
 ERRORS = {
     0: "SZ_OK", -1: "SZ_E_ARG", -2: "SZ_E_DTYPE", -3: "SZ_E_CAPACITY", -4: "SZ_E_ALIGN",
-    -5: "SZ_E_FORMAT", -6: "SZ_E_HIP", -7: "SZ_E_WORKSPACE",
+    -5: "SZ_E_FORMAT", -6: "SZ_E_HIP", -7: "SZ_E_WORKSPACE", -8: "SZ_E_SCRATCH",
 }
 
 
@@ -79,6 +79,10 @@ lib.sz_transfer.argtypes = [_i32, _vp, _u64, _u64, _vp, _i32, _i32, _vp, _u64, _
 lib.sz_transfer.restype = _i32
 lib.sz_decode.argtypes = [_vp, _u64, _i32, _vp, _u64, _vp, _u64, _vp]
 lib.sz_decode.restype = _i32
+lib.sz_decode_noalloc_max_elems.argtypes = []
+lib.sz_decode_noalloc_max_elems.restype = _u64
+lib.sz_decode_noalloc.argtypes = [_vp, _u64, _i32, _vp, _u64, _vp, _vp]
+lib.sz_decode_noalloc.restype = _i32
 lib.sz_profile_enable.argtypes = [_i32]
 lib.sz_profile_enable.restype = _i32
 lib.sz_profile_collect.argtypes = [ctypes.POINTER(sz_kernel_stat), _i32]
@@ -90,7 +94,8 @@ EXPORTS = ("sz_calibrate", "sz_encoded_size", "sz_workspace_size", "sz_workspace
            "sz_decode_workspace_size", "sz_encode", "sz_encode_devcb",
            "sz_calibrate_workspace_size", "sz_calibrate_device", "sz_decode", "sz_encoded_size_format",
            "sz_encode_format", "sz_decode_format", "sz_transfer_workspace_size", "sz_transfer_host_bytes",
-           "sz_transfer", "sz_profile_enable", "sz_profile_collect", "sz_reference_copy")
+           "sz_transfer", "sz_profile_enable", "sz_profile_collect", "sz_reference_copy",
+           "sz_decode_noalloc_max_elems", "sz_decode_noalloc")
 
 SZ_FORMAT_TOP16 = 1
 SZ_FORMAT_TOP8 = 2
@@ -179,6 +184,14 @@ def sz_transfer(dtype, d_src, n, chunk, cb, compress, depth, h_staging, h_bytes,
 
 def sz_decode(d_in, in_bytes, dtype, d_out, n, d_ws, ws_bytes, stream) -> int:
     return int(lib.sz_decode(d_in, in_bytes, dtype, d_out, n, d_ws, ws_bytes, stream))
+
+
+def sz_decode_noalloc_max_elems() -> int:
+    return int(lib.sz_decode_noalloc_max_elems())
+
+
+def sz_decode_noalloc(d_in, in_bytes, dtype, d_out, n, d_status, stream) -> int:
+    return int(lib.sz_decode_noalloc(d_in, in_bytes, dtype, d_out, n, d_status, stream))
 
 
 def sz_reference_copy(d_src, d_dst, nbytes, stream) -> int:

@@ -14,9 +14,9 @@ namespace {
 // Kernel: decode scan.  One workgroup validates the header and the block
 // counts (each at most its block length, summing to E) and writes the
 // exclusive escape offset of every block.  It writes its verdict (0 or a
-// negative error code) to status[0], the caller-visible status word, and to
-// status[1], which the decoders read: they only ever write status[0], so
-// every wave of a decode workgroup sees the same verdict.
+// negative error code) to *status, the caller-visible status word, and to
+// *verdict, which the decoders read: they only ever write *status, so every
+// wave of a decode workgroup sees the same verdict.
 // ---------------------------------------------------------------------------
 struct DecodeArgs {
     uint64_t n, nb, in_bytes, off_nib, off_sm, off_esc;
@@ -59,7 +59,7 @@ constexpr uint64_t kSmallScanBlocks = 1024;
 
 __global__ __launch_bounds__(64) void sz_dec_scan_small(const uint8_t *__restrict__ in, DecodeArgs a,
                                                         uint64_t *__restrict__ block_offsets,
-                                                        int32_t *__restrict__ status)
+                                                        int32_t *__restrict__ status, int32_t *__restrict__ verdict)
 {
     const uint32_t lane = threadIdx.x;
     const uint32_t nb = (uint32_t)a.nb;
@@ -111,15 +111,16 @@ __global__ __launch_bounds__(64) void sz_dec_scan_small(const uint8_t *__restric
     }
     const bool bad = __ballot(too_many) != 0 || total != e_hdr;
     if (lane == 0) {
-        const int32_t verdict = err ? err : bad ? SZ_E_FORMAT : 0;
-        status[0] = verdict;
-        status[1] = verdict;
+        const int32_t v = err ? err : bad ? SZ_E_FORMAT : 0;
+        status[0] = v;
+        verdict[0] = v;
     }
 }
 
 __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__restrict__ in, DecodeArgs a,
                                                             uint64_t *__restrict__ block_offsets,
-                                                            int32_t *__restrict__ status)
+                                                            int32_t *__restrict__ status,
+                                                            int32_t *__restrict__ verdict)
 {
     __shared__ ScanLds lds;
     __shared__ int32_t bad;
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__res
     if (err) {
         if (tid == 0) {
             status[0] = err;
-            status[1] = err;
+            verdict[0] = err;
         }
         return;
     }
@@ -182,9 +183,9 @@ __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__res
     if (too_many) bad = 1;
     __syncthreads();
     if (tid == 0) {
-        const int32_t verdict = (bad || lds.carry != e_hdr) ? SZ_E_FORMAT : 0;
-        status[0] = verdict;
-        status[1] = verdict;
+        const int32_t v = (bad || lds.carry != e_hdr) ? SZ_E_FORMAT : 0;
+        status[0] = v;
+        verdict[0] = v;
     }
 }
 
@@ -368,11 +369,12 @@ __device__ __forceinline__ uint32_t sentinel_bits(uint32_t nib)
 __global__ __launch_bounds__(kDecThreads) void sz_dec_top15s(const uint8_t *__restrict__ in, DecodeArgs a,
                                                              const uint64_t *__restrict__ block_offsets,
                                                              int32_t *__restrict__ status,
+                                                             const int32_t *__restrict__ verdict,
                                                              uint16_t *__restrict__ out)
 {
     __shared__ uint32_t table[256];
     __shared__ uint32_t wave_totals[kDecThreads / 64];
-    if (status[1] != 0) return;
+    if (verdict[0] != 0) return;
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x;
     const uint64_t e0 = b * kBlock;
@@ -649,12 +651,13 @@ struct SpanEscapes {
 template <int T, int CPL, int V>
 __device__ __forceinline__ void bf16_span_decode(const uint8_t *__restrict__ in, const DecodeArgs &a,
                                                  const uint64_t *__restrict__ block_offsets,
-                                                 int32_t *__restrict__ status, uint16_t *__restrict__ out)
+                                                 int32_t *__restrict__ status,
+                                                 const int32_t *__restrict__ verdict, uint16_t *__restrict__ out)
 {
     constexpr uint32_t kSpan = T * 8 * CPL;
     constexpr uint32_t kSpans = kBlock / kSpan;
     __shared__ __align__(16) uint8_t plane[kSpan];
-    if (status[1] != 0) return;
+    if (verdict[0] != 0) return;
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x / kSpans;
     const uint32_t lo = (blockIdx.x % kSpans) * kSpan;            // block-local; the grid keeps lo < blen
@@ -726,30 +729,33 @@ __device__ __forceinline__ void bf16_span_decode(const uint8_t *__restrict__ in,
 template <int T, int CPL>
 __global__ __launch_bounds__(T) void sz_dec_bf16_span(const uint8_t *__restrict__ in, DecodeArgs a,
                                                       const uint64_t *__restrict__ block_offsets,
-                                                      int32_t *__restrict__ status, uint16_t *__restrict__ out)
+                                                      int32_t *__restrict__ status,
+                                                      const int32_t *__restrict__ verdict, uint16_t *__restrict__ out)
 {
-    bf16_span_decode<T, CPL, kTop16>(in, a, block_offsets, status, out);
+    bf16_span_decode<T, CPL, kTop16>(in, a, block_offsets, status, verdict, out);
 }
 
 template <int T, int CPL>
 __global__ __launch_bounds__(T) void sz_dec_top8_span(const uint8_t *__restrict__ in, DecodeArgs a,
                                                       const uint64_t *__restrict__ block_offsets,
-                                                      int32_t *__restrict__ status, uint16_t *__restrict__ out)
+                                                      int32_t *__restrict__ status,
+                                                      const int32_t *__restrict__ verdict, uint16_t *__restrict__ out)
 {
-    bf16_span_decode<T, CPL, kTop8>(in, a, block_offsets, status, out);
+    bf16_span_decode<T, CPL, kTop8>(in, a, block_offsets, status, verdict, out);
 }
 
 template <int T, int CPL>
 __global__ __launch_bounds__(T) void sz_dec_e5m2_span(const uint8_t *__restrict__ in, DecodeArgs a,
                                                                  const uint64_t *__restrict__ block_offsets,
                                                                  int32_t *__restrict__ status,
+                                                                 const int32_t *__restrict__ verdict,
                                                                  uint8_t *__restrict__ out)
 {
     constexpr uint32_t kSpan = T * 32 * CPL;
     constexpr uint32_t kSpans = kBlock / kSpan;
     constexpr uint32_t kWaves = T / 64;
     __shared__ __align__(16) uint8_t plane[kSpan];
-    if (status[1] != 0) return;
+    if (verdict[0] != 0) return;
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
     const uint64_t b = blockIdx.x / kSpans;
@@ -841,21 +847,28 @@ constexpr int kBf16SpanThreads = 256, kBf16SpanChunks = 2;     // up to kSpanWid
 constexpr int kBf16WideThreads = 256, kBf16WideChunks = 4;     // above
 constexpr int kE5SpanThreads = 256, kE5WideChunks = 2;         // one chunk per lane up to kSpanWideBlocks blocks
 
+// Where a decode keeps its device-side words: the caller-visible status
+// word, the verdict word the decoders read, and the per-block escape offsets.
+struct DecodeScratch {
+    int32_t *status;
+    int32_t *verdict;
+    uint64_t *block_offsets;
+};
+
 template <int T, int CPL, int DT, int V = kTop16>
-void launch_span(const uint8_t *in, const DecodeArgs &a, const uint64_t *block_offsets, int32_t *status,
-                 void *d_out, hipStream_t s)
+void launch_span(const uint8_t *in, const DecodeArgs &a, const DecodeScratch &w, void *d_out, hipStream_t s)
 {
     constexpr uint32_t span = T * CPL * (DT == SZ_BF16 ? 8 : 32);
     const dim3 grid((uint32_t)((a.n + span - 1) / span));
     if constexpr (V == kTop8)
-        hipLaunchKernelGGL((sz_dec_top8_span<T, CPL>), grid, dim3(T), 0, s, in, a, block_offsets, status,
-                           static_cast<uint16_t *>(d_out));
+        hipLaunchKernelGGL((sz_dec_top8_span<T, CPL>), grid, dim3(T), 0, s, in, a, w.block_offsets, w.status,
+                           w.verdict, static_cast<uint16_t *>(d_out));
     else if constexpr (DT == SZ_BF16)
-        hipLaunchKernelGGL((sz_dec_bf16_span<T, CPL>), grid, dim3(T), 0, s, in, a, block_offsets, status,
-                           static_cast<uint16_t *>(d_out));
+        hipLaunchKernelGGL((sz_dec_bf16_span<T, CPL>), grid, dim3(T), 0, s, in, a, w.block_offsets, w.status,
+                           w.verdict, static_cast<uint16_t *>(d_out));
     else
-        hipLaunchKernelGGL((sz_dec_e5m2_span<T, CPL>), grid, dim3(T), 0, s, in, a, block_offsets, status,
-                           static_cast<uint8_t *>(d_out));
+        hipLaunchKernelGGL((sz_dec_e5m2_span<T, CPL>), grid, dim3(T), 0, s, in, a, w.block_offsets, w.status,
+                           w.verdict, static_cast<uint8_t *>(d_out));
 }
 
 // BF16 span shape by stream size: 4096-element spans up to kSpanWideBlocks
@@ -867,29 +880,33 @@ constexpr uint64_t kSpanHugeFirst = 256, kSpanHugeLast = 384;
 constexpr int kBf16HugeChunks = 8;
 
 template <int V>
-void launch_bf16_spans(const uint8_t *in, const DecodeArgs &a, const uint64_t *block_offsets, int32_t *status,
-                       void *d_out, hipStream_t s)
+void launch_bf16_spans(const uint8_t *in, const DecodeArgs &a, const DecodeScratch &w, void *d_out, hipStream_t s)
 {
     if (a.nb <= kSpanWideBlocks)
-        launch_span<kBf16SpanThreads, kBf16SpanChunks, SZ_BF16, V>(in, a, block_offsets, status, d_out, s);
+        launch_span<kBf16SpanThreads, kBf16SpanChunks, SZ_BF16, V>(in, a, w, d_out, s);
     else if (a.nb >= kSpanHugeFirst && a.nb <= kSpanHugeLast)
-        launch_span<kBf16WideThreads, kBf16HugeChunks, SZ_BF16, V>(in, a, block_offsets, status, d_out, s);
+        launch_span<kBf16WideThreads, kBf16HugeChunks, SZ_BF16, V>(in, a, w, d_out, s);
     else
-        launch_span<kBf16WideThreads, kBf16WideChunks, SZ_BF16, V>(in, a, block_offsets, status, d_out, s);
+        launch_span<kBf16WideThreads, kBf16WideChunks, SZ_BF16, V>(in, a, w, d_out, s);
 }
 
-int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
-                void *d_ws, uint64_t ws_bytes, void *stream)
+// Host checks shared by every decode entry point (the workspace aside).
+int decode_args_check(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype, void *d_out,
+                      uint64_t n_elems)
 {
     if (n_elems > kMaxElems) return SZ_E_ARG;
-    if (!d_in || !d_ws || (n_elems && !d_out)) return SZ_E_ARG;
-    if (!aligned16(d_in) || !aligned16(d_ws) || (n_elems && !aligned16(d_out))) return SZ_E_ALIGN;
+    if (!d_in || (n_elems && !d_out)) return SZ_E_ARG;
+    if (!aligned16(d_in) || (n_elems && !aligned16(d_out))) return SZ_E_ALIGN;
     if (in_bytes < encoded_size_v(version, dtype, n_elems, 0)) return SZ_E_FORMAT;
-    if (ws_bytes < decode_ws_bytes(dtype, n_elems)) return SZ_E_WORKSPACE;
+    return SZ_OK;
+}
+
+// The decode launches: the scan (validation and block offsets), then the
+// decoder of the stream's format.
+int decode_launch(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
+                  const DecodeScratch &w, void *stream)
+{
     const Geometry g = geometry(dtype, n_elems, version);
-    uint8_t *ws = static_cast<uint8_t *>(d_ws);
-    int32_t *status = reinterpret_cast<int32_t *>(ws);
-    uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + kDecOffsets);
     hipStream_t s = static_cast<hipStream_t>(stream);
     DecodeArgs a;
     a.n = g.n;
@@ -906,29 +923,74 @@ int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype
     const uint8_t *in = static_cast<const uint8_t *>(d_in);
     if (g.nb <= kSmallScanBlocks) {
         LaunchScope scope("sz_dec_scan_small", s);
-        hipLaunchKernelGGL(sz_dec_scan_small, dim3(1), dim3(64), 0, s, in, a, block_offsets, status);
+        hipLaunchKernelGGL(sz_dec_scan_small, dim3(1), dim3(64), 0, s, in, a, w.block_offsets, w.status, w.verdict);
     } else {
         LaunchScope scope("sz_dec_scan", s);
-        hipLaunchKernelGGL(sz_dec_scan, dim3(1), dim3(kScanThreads), 0, s, in, a, block_offsets, status);
+        hipLaunchKernelGGL(sz_dec_scan, dim3(1), dim3(kScanThreads), 0, s, in, a, w.block_offsets, w.status,
+                           w.verdict);
     }
     if (g.nb && version == kTop8) {
         LaunchScope scope("sz_dec_top8_span", s);
-        launch_bf16_spans<kTop8>(in, a, block_offsets, status, d_out, s);
+        launch_bf16_spans<kTop8>(in, a, w, d_out, s);
     } else if (g.nb && version == kTop15S) {
         LaunchScope scope("sz_dec_top15s", s);
-        hipLaunchKernelGGL(sz_dec_top15s, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, block_offsets, status,
-                           static_cast<uint16_t *>(d_out));
+        hipLaunchKernelGGL(sz_dec_top15s, dim3((uint32_t)g.nb), dim3(kDecThreads), 0, s, in, a, w.block_offsets,
+                           w.status, w.verdict, static_cast<uint16_t *>(d_out));
     } else if (g.nb && dtype == SZ_BF16) {
         LaunchScope scope("sz_dec_bf16_span", s);
-        launch_bf16_spans<kTop16>(in, a, block_offsets, status, d_out, s);
+        launch_bf16_spans<kTop16>(in, a, w, d_out, s);
     } else if (g.nb) {
         LaunchScope scope("sz_dec_e5m2_span", s);
         if (g.nb > kSpanWideBlocks)
-            launch_span<kE5SpanThreads, kE5WideChunks, SZ_FP8_E5M2>(in, a, block_offsets, status, d_out, s);
+            launch_span<kE5SpanThreads, kE5WideChunks, SZ_FP8_E5M2>(in, a, w, d_out, s);
         else
-            launch_span<kE5SpanThreads, 1, SZ_FP8_E5M2>(in, a, block_offsets, status, d_out, s);
+            launch_span<kE5SpanThreads, 1, SZ_FP8_E5M2>(in, a, w, d_out, s);
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
+}
+
+int decode_impl(uint32_t version, const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
+                void *d_ws, uint64_t ws_bytes, void *stream)
+{
+    const int rc = decode_args_check(version, d_in, in_bytes, dtype, d_out, n_elems);
+    if (rc) return rc;
+    if (!d_ws) return SZ_E_ARG;
+    if (!aligned16(d_ws)) return SZ_E_ALIGN;
+    if (ws_bytes < decode_ws_bytes(dtype, n_elems)) return SZ_E_WORKSPACE;
+    uint8_t *ws = static_cast<uint8_t *>(d_ws);
+    const DecodeScratch w = {reinterpret_cast<int32_t *>(ws), reinterpret_cast<int32_t *>(ws) + 1,
+                             reinterpret_cast<uint64_t *>(ws + kDecOffsets)};
+    return decode_launch(version, d_in, in_bytes, dtype, d_out, n_elems, w, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Decode scratch in a fixed device array, for callers that cannot allocate
+// (sz_decode_noalloc): the verdict word and the block offsets.  Each device
+// the library runs on holds its own copy for the life of the process; host
+// code reaches it only through the address hipGetSymbolAddress returns on
+// that device (the array's name is a host-side stand-in there).
+// ---------------------------------------------------------------------------
+constexpr uint64_t kNoAllocScratchBytes = 1ull << 20;
+constexpr uint64_t kNoAllocMaxBlocks = (kNoAllocScratchBytes - kDecOffsets - 16) / 8;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::atomic<uint8_t *> g_scratch_addr[kMaxDevices];
+
+// The current device's scratch address, looked up on the first call on that
+// device (with it current) and kept; nullptr on failure.
+uint8_t *device_scratch()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    uint8_t *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void *addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    p = static_cast<uint8_t *>(addr);
+    g_scratch_addr[dev].store(p, std::memory_order_release);     // the same value whichever thread wins
+    return p;
 }
 
 }  // namespace
@@ -947,6 +1009,24 @@ extern "C" int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d
 {
     if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
     return decode_impl(kTop16, d_in, in_bytes, dtype, d_out, n_elems, d_ws, ws_bytes, stream);
+}
+
+extern "C" uint64_t sz_decode_noalloc_max_elems(void) { return kNoAllocMaxBlocks * kBlock; }
+
+extern "C" int sz_decode_noalloc(const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
+                                 int32_t *d_status, void *stream)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    const int rc = decode_args_check(kTop16, d_in, in_bytes, dtype, d_out, n_elems);
+    if (rc) return rc;
+    if (!d_status) return SZ_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(d_status) & 3u) != 0) return SZ_E_ALIGN;
+    if (geometry(dtype, n_elems).nb > kNoAllocMaxBlocks) return SZ_E_SCRATCH;
+    uint8_t *sc = device_scratch();
+    if (!sc) return SZ_E_HIP;
+    const DecodeScratch w = {d_status, reinterpret_cast<int32_t *>(sc),
+                             reinterpret_cast<uint64_t *>(sc + kDecOffsets)};
+    return decode_launch(kTop16, d_in, in_bytes, dtype, d_out, n_elems, w, stream);
 }
 
 extern "C" int sz_decode_format(int format, const void *d_in, uint64_t in_bytes, int dtype, void *d_out,

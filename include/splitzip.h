@@ -70,7 +70,8 @@ enum {
     SZ_E_ALIGN = -4,     /* device pointer not 16-byte aligned */
     SZ_E_FORMAT = -5,    /* malformed or truncated stream */
     SZ_E_HIP = -6,       /* a HIP launch or runtime call failed */
-    SZ_E_WORKSPACE = -7  /* workspace smaller than the call's *_workspace_size() */
+    SZ_E_WORKSPACE = -7, /* workspace smaller than the call's *_workspace_size() */
+    SZ_E_SCRATCH = -8    /* request larger than sz_decode_noalloc's fixed scratch */
 };
 
 /* Top-16 exponent codebook: exp[c] is the exponent that code c stands for.
@@ -252,6 +253,30 @@ int sz_transfer(int dtype, const void *d_src, uint64_t n_elems, uint64_t chunk_e
  * applied like any other. */
 int sz_decode(const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
               void *d_ws, uint64_t ws_bytes, void *stream);
+
+/* sz_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same decode as sz_decode (same kernels, checks and output), with its
+ * scratch (the verdict word and the per-block escape offsets) in a fixed
+ * 1 MiB array in device memory that the library holds on each device it
+ * runs on until the process ends, instead of a caller workspace.  The call
+ * itself allocates nothing and issues no memset.
+ *   d_status: a caller-owned device int32 (4-byte aligned) that receives the
+ *     status: 0, or the negative SZ_E_* code of a failed device check;
+ *     valid once the stream has run past the call.
+ *   n_elems <= sz_decode_noalloc_max_elems() (8,587,706,368 values:
+ *     131,038 blocks of 65,536); larger requests return SZ_E_SCRATCH
+ *     before any launch.
+ * The first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress, with the device current); a failed lookup returns
+ * SZ_E_HIP.  Every call on one device shares its array and the array keeps
+ * the last call's contents (each call rewrites what it reads before reading
+ * it): calls that overlap on one device, on any streams, race and must be
+ * serialised by the caller.  Other arguments and return codes as
+ * sz_decode. */
+uint64_t sz_decode_noalloc_max_elems(void);
+int sz_decode_noalloc(const void *d_in, uint64_t in_bytes, int dtype, void *d_out, uint64_t n_elems,
+                      int32_t *d_status, void *stream);
 
 /* Instrumentation (not part of the codec).  While enabled, every kernel the
  * library launches is bracketed by a pair of HIP events recorded on the

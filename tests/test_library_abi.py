@@ -251,3 +251,22 @@ def test_host_argument_checks_reference_copy():
     assert nat.sz_reference_copy(a, b + 4, 32, None) == -4
     assert nat.sz_reference_copy(a, a + 16, 32, None) == -1            # overlapping ranges
     assert nat.sz_reference_copy(a + 16, a, 32, None) == -1
+
+
+def test_host_argument_checks_decode_noalloc():
+    """sz_decode_noalloc rejects bad arguments, and requests beyond its fixed
+    scratch, on the host before any launch."""
+    nat = _native()
+    dummy = 1 << 20
+    cap = nat.sz_decode_noalloc_max_elems()
+    assert cap == ((1 << 20) - 256 - 16) // 8 * 65536
+    big = nat.sz_encoded_size(0, cap + 1, 0)
+    assert nat.sz_decode_noalloc(dummy, big, 0, dummy, cap + 1, dummy, None) == -8
+    assert nat.sz_decode_noalloc(dummy, big, 0, dummy, (1 << 40) + 1, dummy, None) == -1
+    fixed = nat.sz_encoded_size(0, 1000, 0)
+    assert nat.sz_decode_noalloc(dummy, fixed, 0, dummy, 1000, None, None) == -1
+    assert nat.sz_decode_noalloc(dummy, fixed, 0, dummy, 1000, dummy + 2, None) == -4
+    assert nat.sz_decode_noalloc(dummy, fixed - 1, 0, dummy, 1000, dummy, None) == -5
+    assert nat.sz_decode_noalloc(dummy, fixed, 3, dummy, 1000, dummy, None) == -2
+    assert nat.sz_decode_noalloc(dummy + 8, fixed, 0, dummy, 1000, dummy, None) == -4
+
