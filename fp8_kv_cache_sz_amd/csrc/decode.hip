@@ -192,8 +192,8 @@ __global__ __launch_bounds__(kScanThreads) void sz_dec_scan(const uint8_t *__res
 // ---------------------------------------------------------------------------
 // Escape records, code lookup and value assembly shared by the decoders.
 // ---------------------------------------------------------------------------
-// four-record windows a lane has in flight when it walks escape records
-constexpr uint32_t kRecordGroups = 2;
+// 16-record groups a lane has in flight when it walks escape records
+constexpr uint32_t kRecordGroups = 1;
 
 // Escape record r of the stream: position and exponent.
 __device__ __forceinline__ void read_record(const uint8_t *esc, uint64_t r, uint32_t &pos, uint32_t &e)
@@ -201,6 +201,13 @@ __device__ __forceinline__ void read_record(const uint8_t *esc, uint64_t r, uint
     const uint8_t *p = esc + 3 * r;
     pos = (uint32_t)p[0] | ((uint32_t)p[1] << 8);
     e = p[2];
+}
+
+// Position of escape record r of the stream.
+__device__ __forceinline__ uint32_t record_pos(const uint8_t *esc, uint64_t r)
+{
+    const uint8_t *p = esc + 3 * r;
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8);
 }
 
 // Four consecutive records from the 16 bytes w[0..3] of aligned words that
@@ -267,58 +274,71 @@ __device__ __forceinline__ uint4 assemble_bf16(uint2 sm, uint2 ex)
 // overwrites plane[pos - lo] with the exponent of each whose position lies in
 // [lo, lo + span); invalid records (position out of the block or not
 // ascending, exponent out of range) are skipped and reported through the
-// status word.  A lane takes 4 G consecutive records per pass, read as G
-// aligned three-word windows issued together, so that a workgroup has G
-// windows per lane in flight at each wait.
+// status word.
+// The stream's records are taken in aligned groups of 16 (48 bytes, three dwordx4 loads
+// per lane; a group never straddles a lane, so no byte realignment is
+// needed), G groups per lane in flight at once.  Record R of the stream
+// (the block's record R - r0) is applied when r0 + i0 <= R < r0 + i1; the
+// record before a lane's group comes from its own two-byte load.  Groups
+// that reach past the stream's last record are read record by record.
 template <uint32_t G>
-__device__ __forceinline__ void overwrite_exponents(const uint8_t *__restrict__ esc, uint64_t r0, uint32_t i0,
-                                                    uint32_t i1, uint32_t blen, uint32_t symbols, uint64_t e_total,
-                                                    uint8_t *plane, uint32_t lo, uint32_t span,
-                                                    int32_t *__restrict__ status)
+__device__ __forceinline__ void overwrite_exponents_grouped(const uint8_t *__restrict__ esc, uint64_t r0, uint32_t i0,
+                                                            uint32_t i1, uint32_t blen, uint32_t symbols,
+                                                            uint64_t e_total, uint8_t *plane, uint32_t lo,
+                                                            uint32_t span, int32_t *__restrict__ status)
 {
-    constexpr uint32_t kPer = 4 * G;
-    const uint32_t lane = lane_id();
-    const uint32_t step = kPer * blockDim.x;
+    if (i0 >= i1) return;
+    const uint64_t first = r0 + i0, last = r0 + i1;              // stream record range [first, last)
+    const uint64_t gA = first >> 4;
+    const uint32_t groups = (uint32_t)(((last - 1) >> 4) - gA + 1);
     bool bad = false;
-    for (uint32_t r = i0 + kPer * threadIdx.x; r < i1; r += step) {
-        uint32_t pos[kPer], e[kPer];
-        const uint32_t cnt = std::min<uint32_t>(kPer, i1 - r);
-        if (cnt == kPer && r0 + r + kPer + 1 < e_total) {
-            // every window starts at most 3 bytes before its first record and
-            // ends at most 3 bytes after its last: all inside the section
-            uint32_t w[G][4];
+    for (uint32_t g0 = 0; g0 < groups; g0 += G * blockDim.x) {
+        uint32_t w[G][13], prev[G];
 #pragma unroll
-            for (uint32_t g = 0; g < G; ++g) {
-                const uint32_t *p = reinterpret_cast<const uint32_t *>(esc + ((3 * (r0 + r + 4 * g)) & ~uint64_t(3)));
-                w[g][0] = p[0];
-                w[g][1] = p[1];
-                w[g][2] = p[2];
-                w[g][3] = p[3];
-            }
+        for (uint32_t k = 0; k < G; ++k) {
+            const uint32_t g = g0 + k * blockDim.x + threadIdx.x;
+            const uint64_t R0 = (gA + g) * 16;
+            w[k][12] = 0;
+            prev[k] = 0;
+            if (g < groups) {
+                if (R0 + 16 <= e_total) {
+                    const uint4 *p = reinterpret_cast<const uint4 *>(esc + 3 * R0);   // 16-byte aligned
 #pragma unroll
-            for (uint32_t g = 0; g < G; ++g)
-                records4_from_words(w[g], (uint32_t)((3 * (r0 + r + 4 * g)) & 3), pos + 4 * g, e + 4 * g);
-        } else {
+                    for (int v = 0; v < 3; ++v) {
+                        const uint4 x = p[v];
+                        w[k][4 * v] = x.x;
+                        w[k][4 * v + 1] = x.y;
+                        w[k][4 * v + 2] = x.z;
+                        w[k][4 * v + 3] = x.w;
+                    }
+                } else {
 #pragma unroll
-            for (uint32_t q = 0; q < kPer; ++q) {
-                pos[q] = 0xFFFFFFFFu;
-                e[q] = 0;
-                if (q < cnt) read_record(esc, r0 + r + q, pos[q], e[q]);
+                    for (int i = 0; i < 12; ++i) w[k][i] = 0;
+                    for (uint32_t b = 0; b < 48 && 3 * R0 + b < 3 * e_total; ++b)
+                        w[k][b / 4] |= (uint32_t)esc[3 * R0 + b] << (8 * (b & 3));
+                }
+                if (R0 > 0) prev[k] = record_pos(esc, R0 - 1);
             }
         }
-        uint32_t prev = __shfl_up(pos[kPer - 1], 1, 64);   // lane l-1 holds records r-kPer..r-1
-        if (lane == 0 && r > 0) {
-            uint32_t pe;
-            read_record(esc, r0 + r - 1, prev, pe);
-        }
 #pragma unroll
-        for (uint32_t q = 0; q < kPer; ++q) {
-            if (q >= cnt) continue;
-            const uint32_t before = q == 0 ? prev : pos[q - 1];
-            if (pos[q] < blen && e[q] < symbols && (r + q == 0 || pos[q] > before)) {
-                if (pos[q] - lo < span) plane[pos[q] - lo] = (uint8_t)e[q];
-            } else {
-                bad = true;
+        for (uint32_t k = 0; k < G; ++k) {
+            const uint32_t g = g0 + k * blockDim.x + threadIdx.x;
+            if (g >= groups) continue;
+            const uint64_t R0 = (gA + g) * 16;
+            uint32_t before = prev[k];
+#pragma unroll
+            for (uint32_t q = 0; q < 16; ++q) {
+                const uint32_t d = __builtin_amdgcn_alignbyte(w[k][(3 * q) / 4 + 1], w[k][(3 * q) / 4], (3 * q) & 3);
+                const uint32_t pos = d & 0xFFFFu, e = (d >> 16) & 0xFFu;
+                const uint64_t R = R0 + q;
+                if (R >= first && R < last) {
+                    if (pos < blen && e < symbols && (R == r0 || pos > before)) {
+                        if (pos - lo < span) plane[pos - lo] = (uint8_t)e;
+                    } else {
+                        bad = true;
+                    }
+                }
+                before = pos;
             }
         }
     }
@@ -508,21 +528,17 @@ __device__ __forceinline__ void store_chunk_pairs(uint8_t *row_out, const uint32
 // narrow spans are as fast or faster.
 constexpr uint64_t kSpanWideBlocks = 128;
 
-__device__ __forceinline__ uint32_t record_pos(const uint8_t *esc, uint64_t r)
-{
-    const uint8_t *p = esc + 3 * r;
-    return (uint32_t)p[0] | ((uint32_t)p[1] << 8);
-}
-
 // The escape records of one span workgroup.  The block's span s has the
 // share [k s / D, k (s+1) / D) of its records (D = kBlock / SPAN; the block's
 // last span takes the rest), so the span workgroups of a block together
 // check all k.  Each workgroup reads its share widened by a margin of
-// 64 + min(k / 64, 256) records on both sides, checks those records and
+// 64 + min(k / 256, 128) records on both sides, checks those records and
 // applies the ones inside its span to the span's exponent plane.  When the
 // escapes are spread evenly over the block, the number of records before a
 // span start has a standard deviation of at most sqrt(k (1 - k / B)) / 2,
-// which never exceeds 64: the margin covers four of them.  The record
+// which never exceeds 64: the margin covers at least three of them, and
+// keeps the window of an 8192-element span of a block whose elements nearly
+// all escape within 8192 records, one round of group loads.  The record
 // just before the window and the one just after it show whether the window
 // holds every record of the span (positions are sorted); if not, the span's
 // records are found by a two-round search (every stride-th record, then the
@@ -561,7 +577,7 @@ struct SpanEscapes {
         lo = lo_;
         e_total = e_total_;
         const uint32_t s = lo / SPAN;
-        const uint32_t margin = 64 + std::min<uint32_t>(k >> 6, 256);
+        const uint32_t margin = 64 + std::min<uint32_t>(k >> 8, 128);
         const uint32_t share_lo = (k * s) >> kLog2D;              // k * s < 2^21
         const uint32_t share_hi = lo + SPAN >= blen ? k : (k * (s + 1)) >> kLog2D;
         w0 = share_lo > margin ? share_lo - margin : 0;
@@ -614,7 +630,8 @@ struct SpanEscapes {
             }
             if (bad) atomicExch(status, SZ_E_FORMAT);
         } else {
-            overwrite_exponents<kRecordGroups>(esc, r0, w0, w1, blen, symbols, e_total, plane, lo, SPAN, status);
+            overwrite_exponents_grouped<kRecordGroups>(esc, r0, w0, w1, blen, symbols, e_total, plane, lo, SPAN,
+                                                       status);
         }
         if (!((w0 > 0 && g_lo >= lo) || (w1 < k && g_hi < hi))) return;      // workgroup-uniform
         const uint32_t stride = (k + kSamples * T - 1) / (kSamples * T);       // 1 .. 256
@@ -640,7 +657,8 @@ struct SpanEscapes {
             first += __syncthreads_count(q_lo < lo);
             last += __syncthreads_count(q_hi < hi);
         }
-        overwrite_exponents<kRecordGroups>(esc, r0, first, last, blen, symbols, e_total, plane, lo, SPAN, status);
+        overwrite_exponents_grouped<kRecordGroups>(esc, r0, first, last, blen, symbols, e_total, plane, lo, SPAN,
+                                                   status);
     }
 };
 

@@ -682,32 +682,40 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
                                                             uint64_t *__restrict__ block_offsets,
                                                             uint8_t *__restrict__ out, HeaderArgs h,
                                                             const uint32_t *__restrict__ cb_dev,
-                                                            int32_t *__restrict__ status)
+                                                            int32_t *__restrict__ status,
+                                                            uint32_t *__restrict__ heavy_list,
+                                                            uint32_t *__restrict__ heavy_count)
 {
     __shared__ ScanLds lds;
-    const uint32_t tid = threadIdx.x;
+    __shared__ uint32_t heavy;
+    const uint32_t tid = threadIdx.x, lane = lane_id();
     // a bad device codebook zeroes the magic and sets the status word
     Codebook4 cb = h.cb;
     const int32_t verdict = device_codebook_verdict(cb_dev, h.dtype, cb);
     const uint32_t nb = (uint32_t)h.nb;
-    if (tid == 0) lds.carry = 0;
+    if (tid == 0) {
+        lds.carry = 0;
+        heavy = 0;
+    }
     uint32_t *block_counts = reinterpret_cast<uint32_t *>(out + 64);
     for (uint32_t b0 = 0; b0 < nb; b0 += kScanBatch * kScanThreads) {
-        uint32_t x[kScanBatch];
+        uint32_t x[kScanBatch], flags[kScanBatch];
 #pragma unroll
         for (int i = 0; i < kScanBatch; ++i) {
             const uint32_t b = b0 + i * kScanThreads + tid;
             x[i] = 0;
+            flags[i] = 0;
             if (b < nb) {
                 const uint4 v = *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b);
                 const uint32_t t = kTilesPerBlock * b;
                 const uint32_t m = ~kRederiveFlag;
-                x[i] = (v.x & m) + ((t + 1 < nt) ? v.y & m : 0) + ((t + 2 < nt) ? v.z & m : 0) +
-                       ((t + 3 < nt) ? v.w & m : 0);
+                const uint32_t vy = (t + 1 < nt) ? v.y : 0, vz = (t + 2 < nt) ? v.z : 0, vw = (t + 3 < nt) ? v.w : 0;
+                x[i] = (v.x & m) + (vy & m) + (vz & m) + (vw & m);
+                flags[i] = (v.x >> 31) | ((vy >> 31) << 1) | ((vz >> 31) << 2) | ((vw >> 31) << 3);
             }
         }
         uint64_t base[kScanBatch];
-        scan_batch(x, base, lds);
+        scan_batch(x, base, lds);       // its barriers also publish `heavy` before the first append
 #pragma unroll
         for (int i = 0; i < kScanBatch; ++i) {
             const uint32_t b = b0 + i * kScanThreads + tid;
@@ -715,13 +723,26 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
                 block_counts[b] = x[i];
                 block_offsets[b] = base[i];
             }
+            // flagged tiles go to the list of tiles the re-derivation kernel
+            // takes (in no particular order: each tile's records have a fixed place)
+            const uint32_t nf = __popc(flags[i]);
+            const uint32_t incl = wave_inclusive_sum(nf);
+            const uint32_t wave_total = read_lane63(incl);
+            if (wave_total) {                                          // wave-uniform
+                uint32_t at = 0;
+                if (lane == 63) at = atomicAdd(&heavy, wave_total);
+                at = __builtin_amdgcn_readlane(at, 63) + incl - nf;
+                for (uint32_t f = flags[i]; f; f &= f - 1) heavy_list[at++] = kTilesPerBlock * b + __builtin_ctz(f);
+            }
         }
     }
+    __syncthreads();
     const uint64_t total = lds.carry;
     write_header(out, h, cb, verdict, false, status);
     if (tid == 0) {
         reinterpret_cast<uint32_t *>(out)[4] = (uint32_t)total;
         reinterpret_cast<uint32_t *>(out)[5] = (uint32_t)(total >> 32);
+        *heavy_count = heavy;
     }
 }
 
@@ -885,6 +906,197 @@ __device__ __forceinline__ void rederive_tile_e5m2(const uint8_t *__restrict__ i
     }
 }
 
+// ---------------------------------------------------------------------------
+// Escape-heavy tiles of large streams (sz_enc_rederive below): the records of
+// a tile are derived again from the input and written to their final place
+// two chunk rows (1024 elements) at a time, in three steps:
+//   * each lane turns an 8-element chunk into the compacted byte string of
+//     its records in registers: a 256-entry table gives, for the chunk's
+//     escape mask, the element index of each record slot, and v_perm picks
+//     the position and exponent bytes by those indices;
+//   * the lane ORs the string, shifted to its byte offset, into the wave's
+//     LDS segment as whole dwords (the segment is zeroed first; two lanes can
+//     share a dword at their edge, and OR keeps both);
+//   * the wave stores the segment's whole 16-byte words with dwordx4 stores
+//     and carries the last, partial one over to the next two rows, so only
+//     the first and last words of the wave's records take byte stores.
+// ---------------------------------------------------------------------------
+// records of two chunk rows, the 16-byte lead and the overhang of the last
+// lane's dword writes, in 16-byte words
+constexpr uint32_t kRdSegWords = (3 * 2 * 512 + 64) / 16;
+
+struct RederiveLds {
+    uint32_t table32[64];      // exponent -> code byte, bit 7 = escape
+    uint32_t esc32[64];        // exponent -> 1 if it escapes, else 0 (one byte each)
+    uint32_t slots[256];       // escape mask -> element index of record slot j in nibble j (12: unused slot)
+    uint4 seg[kRdSegWords];
+};
+
+// The encode table and the slot table of one wave (its lanes only, no
+// workgroup barrier).
+__device__ __forceinline__ void build_wave_tables(RederiveLds &L, const Codebook4 &cb, uint32_t symbols)
+{
+    const uint32_t lane = lane_id();
+    uint32_t word = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) {
+        const uint32_t v = lane * 4 + k;
+        uint32_t code = 0x80u;
+#pragma unroll
+        for (uint32_t c = 0; c < 16; ++c)
+            if (cb_entry(cb, c) == v) code = c;
+        word |= (v < symbols ? code : 0x80u) << (8 * k);
+    }
+    L.table32[lane] = word;
+    L.esc32[lane] = (word >> 7) & 0x01010101u;
+#pragma unroll
+    for (uint32_t r = 0; r < 4; ++r) {
+        const uint32_t m = lane * 4 + r;
+        uint32_t e = 0xCCCCCCCCu, j = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < 8; ++k) {
+            if ((m >> k) & 1u) {
+                e = (e & ~(0xFu << (4 * j))) | (k << (4 * j));
+                ++j;
+            }
+        }
+        L.slots[m] = e;
+    }
+    wave_lds_fence();
+}
+
+// ORs the records of one 8-element chunk (escape mask m, exponents of
+// elements 0..3 in ea and 4..7 in eb, block-local position pos0 of element
+// 0, a multiple of 8) into seg32 from byte S on.  Record slot j holds
+// (pos lo, pos hi, exponent) of the chunk's j-th escaped element.
+__device__ __forceinline__ void or_records8(uint32_t *seg32, uint32_t S, uint32_t m, uint32_t ea, uint32_t eb,
+                                            uint32_t pos0, const uint32_t *slots)
+{
+    const uint32_t sl = slots[m];
+    const uint32_t ev = sl & 0x0F0F0F0Fu, od = (sl >> 4) & 0x0F0F0F0Fu;
+    const uint32_t k_lo = perm(od, ev, 0x05010400u);              // slot indices 0..3, one per byte
+    const uint32_t k_hi = perm(od, ev, 0x07030602u);              // slot indices 4..7
+    const uint32_t pl = perm(pos0, pos0, 0x00000000u);            // low position byte in every byte
+    const uint32_t posb_lo = pl | 0x03020100u, posb_hi = pl | 0x07060504u;
+    const uint32_t hw = perm(pos0, pos0, 0x01010101u);            // high position byte in every byte
+    // index 12 selects a zero byte: unused slots come out as zero bytes
+    const uint32_t p_lo = perm(posb_hi, posb_lo, k_lo), p_hi = perm(posb_hi, posb_lo, k_hi);
+    const uint32_t e_lo = perm(eb, ea, k_lo), e_hi = perm(eb, ea, k_hi);
+    const uint32_t h_lo = perm(hw, hw, k_lo), h_hi = perm(hw, hw, k_hi);
+    uint32_t d[8];
+    {
+        const uint32_t ph01 = perm(h_lo, p_lo, 0x05010400u);      // P0 H0 P1 H1
+        const uint32_t ph23 = perm(h_lo, p_lo, 0x07030602u);      // P2 H2 P3 H3
+        d[1] = perm(e_lo, ph01, 0x02040100u);                       // P0 H0 E0 P1
+        const uint32_t x = perm(e_lo, ph01, 0x0C0C0503u);          // H1 E1
+        d[2] = perm(ph23, x, 0x05040100u);                          // H1 E1 P2 H2
+        d[3] = perm(e_lo, ph23, 0x07030206u);                       // E2 P3 H3 E3
+    }
+    {
+        const uint32_t ph01 = perm(h_hi, p_hi, 0x05010400u);
+        const uint32_t ph23 = perm(h_hi, p_hi, 0x07030602u);
+        d[4] = perm(e_hi, ph01, 0x02040100u);
+        const uint32_t x = perm(e_hi, ph01, 0x0C0C0503u);
+        d[5] = perm(ph23, x, 0x05040100u);
+        d[6] = perm(e_hi, ph23, 0x07030206u);
+    }
+    d[0] = 0;
+    d[7] = 0;
+    const uint32_t dw = S >> 2;
+    const uint32_t rs = 32 - 8 * (S & 3u);                        // 8 .. 32
+    // the string's bytes past its records are zero, so all seven words are
+    // ORed: the ones past the records change nothing
+#pragma unroll
+    for (uint32_t i = 0; i < 7; ++i) {
+        const uint32_t w = (uint32_t)((((uint64_t)d[i + 1] << 32) | d[i]) >> rs);
+        __hip_atomic_fetch_or(seg32 + dw + i, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    }
+}
+
+// Writes a tile's records to the stream from its LDS segment.  LDS word 0
+// stands for the 16-byte aligned stream word at a0: its first `lead` bytes
+// are already in place (records carried over from the previous half pass,
+// or, before the first store, bytes that belong to the records before this
+// tile, which this wave never writes: `own0` of them).  After each half pass
+// the whole 16-byte words are stored and the last, partial one is carried
+// into word 0, so only the tile's first and last words take byte stores.
+struct RecordWriter {
+    uint64_t a0;
+    uint32_t lead, own0;
+
+    __device__ __forceinline__ void begin(RederiveLds &L, uint64_t dst0)
+    {
+        a0 = dst0 & ~uint64_t(15);
+        lead = own0 = (uint32_t)(dst0 & 15);
+        if (lane_id() == 0) L.seg[0] = make_uint4(0, 0, 0, 0);
+    }
+
+    // Zeroes the words after word 0 that `count` records (and the overhang of
+    // the lanes' dword writes) will touch; returns the byte of word 0 where
+    // the half pass's records start.
+    __device__ __forceinline__ uint32_t open(RederiveLds &L, uint32_t count) const
+    {
+        const uint32_t words = (lead + 3 * count + 32 + 15) / 16;
+        for (uint32_t i = 1 + lane_id(); i < words; i += 64) L.seg[i] = make_uint4(0, 0, 0, 0);
+        wave_lds_fence();
+        return lead;
+    }
+
+    __device__ __forceinline__ void flush(RederiveLds &L, uint8_t *__restrict__ out, uint32_t count)
+    {
+        wave_lds_fence();
+        const uint32_t lane = lane_id();
+        const uint32_t end = lead + 3 * count;
+        const uint32_t full = end / 16;
+        for (uint32_t i = lane; i < full; i += 64) {
+            const uint4 v = L.seg[i];
+            if (i == 0 && own0) {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                for (uint32_t b = own0; b < 16; ++b) out[a0 + b] = (uint8_t)(w[b / 4] >> (8 * (b & 3)));
+            } else {
+                store_nt(reinterpret_cast<uint4 *>(out + a0 + 16ull * i), v);
+            }
+        }
+        if (full) {
+            wave_lds_fence();
+            if (lane == 0) L.seg[0] = L.seg[full];          // the partial word carries over
+            wave_lds_fence();
+            a0 += 16ull * full;
+            own0 = 0;
+        }
+        lead = end & 15;
+        if (!full) lead = end;
+    }
+
+    // The tile's last, partial word.
+    __device__ __forceinline__ void finish(RederiveLds &L, uint8_t *__restrict__ out) const
+    {
+        wave_lds_fence();
+        if (lane_id() == 0 && lead > own0) {
+            const uint4 v = L.seg[0];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (uint32_t b = own0; b < lead; ++b) out[a0 + b] = (uint8_t)(w[b / 4] >> (8 * (b & 3)));
+        }
+    }
+};
+
+// Escape mask of 8 BF16 values (bit k = element k) and their exponent bytes
+// (elements 0..3 in ea, 4..7 in eb), from the escape-flag table.
+__device__ __forceinline__ uint32_t escapes8_bf16(const uint4 q, const uint8_t *esc8, uint32_t &ea, uint32_t &eb)
+{
+    const uint32_t lo_a = perm(q.y, q.x, 0x06040200u), hi_a = perm(q.y, q.x, 0x07050301u);
+    const uint32_t lo_b = perm(q.w, q.z, 0x06040200u), hi_b = perm(q.w, q.z, 0x07050301u);
+    ea = ((hi_a << 1) & 0xFEFEFEFEu) | ((lo_a >> 7) & 0x01010101u);
+    eb = ((hi_b << 1) & 0xFEFEFEFEu) | ((lo_b >> 7) & 0x01010101u);
+    uint32_t m = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) {
+        m |= (uint32_t)esc8[(ea >> (8 * k)) & 0xFFu] << k;
+        m |= (uint32_t)esc8[(eb >> (8 * k)) & 0xFFu] << (k + 4);
+    }
+    return m;
+}
+
 // Tiles with at most this many records are copied by 16-lane groups, the
 // block's four tiles at once; heavier blocks copy tile after tile with the
 // whole wave.
@@ -941,18 +1153,17 @@ __device__ __forceinline__ void compact_block(const uint8_t *__restrict__ stage,
     }
 }
 
+// Kernel: escape compaction of the staged tiles.  One wave per 64K block,
+// four blocks per workgroup: a wave copies the staged records of its block's
+// tiles to their place (16-lane groups copy the four tiles at once when none
+// is flagged and none holds more than kGroupCopyRecords records).  Flagged
+// (escape-heavy) tiles are left to sz_enc_rederive.
 template <int DT>
 __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_compact(
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
     const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
-    uint64_t nb, const void *__restrict__ in, uint64_t n, Codebook4 cb, const uint32_t *__restrict__ cb_dev,
-    uint32_t item, uint32_t slot)
+    uint64_t nb, uint32_t item, uint32_t slot)
 {
-    __shared__ uint32_t table32[64];
-    __shared__ __align__(16) uint8_t seg_buf[kCompactThreads / 64][kSegBytes];
-    if (cb_dev) cb = load_codebook(cb_dev);
-    build_encode_table(table32, cb, DT == SZ_BF16 ? 256 : 32);
-    __syncthreads();
     const uint64_t b = (uint64_t)blockIdx.x * (kCompactThreads / 64) + threadIdx.x / 64;
     if (b >= nb) return;
     const uint32_t lane = lane_id();
@@ -963,8 +1174,168 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
     else if (lane == kTilesPerBlock) meta = block_offsets[b];
     const uint64_t off = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(meta >> 32), kTilesPerBlock) << 32) |
                          (uint32_t)__builtin_amdgcn_readlane((uint32_t)meta, kTilesPerBlock);
-    compact_block<DT>(stage, (uint32_t)meta, b, off, out, off_esc, in, n, reinterpret_cast<const uint8_t *>(table32),
-                      seg_buf[threadIdx.x / 64], item, slot);
+    uint32_t cnt[kTilesPerBlock], before[kTilesPerBlock], most = 0, run = 0, flagged = 0;
+#pragma unroll
+    for (uint32_t t = 0; t < kTilesPerBlock; ++t) {
+        const uint32_t v = __builtin_amdgcn_readlane((uint32_t)meta, t);
+        cnt[t] = v & ~kRederiveFlag;
+        flagged |= (v >> 31) << t;
+        before[t] = run;
+        run += cnt[t];
+        most = std::max(most, cnt[t]);
+    }
+    if (!flagged && most <= kGroupCopyRecords) {               // wave-uniform
+        const uint32_t g = lane >> 4;
+        uint32_t k = 0, bef = 0;
+#pragma unroll
+        for (uint32_t t = 0; t < kTilesPerBlock; ++t)
+            if (g == t) {
+                k = cnt[t];
+                bef = before[t];
+            }
+        if (k) copy_records(stage + (t0 + g) * (uint64_t)slot, out, off_esc + item * (off + bef), item * k, lane & 15,
+                            16);
+        return;
+    }
+#pragma unroll
+    for (uint32_t t = 0; t < kTilesPerBlock; ++t)
+        if (cnt[t] && !((flagged >> t) & 1u))
+            copy_records(stage + (t0 + t) * (uint64_t)slot, out, off_esc + item * (off + before[t]), item * cnt[t],
+                         lane, 64);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: re-derivation of the flagged (escape-heavy) tiles, which the dense
+// encoders did not stage, listed by sz_enc_scan.  Its grid fills the GPU once
+// (kRederiveGroups workgroups at most) and takes the listed tiles in turn,
+// workgroup g the entries g, g + G, g + 2G, ...; with no flagged tile every
+// workgroup exits after one load.  A tile's first record follows its block's
+// offset and the counts of the block's tiles before it.
+//   BF16: the eight waves share a tile, wave w its 2048 elements
+//   [2048 w, 2048 w + 2048), all loaded at once (a wave waits for its loads
+//   only once per tile, not behind the stores of earlier passes); the wave
+//   totals meet in LDS and each wave writes its records after those of the
+//   waves before it, two chunk rows at a time.
+//   E5M2: each wave re-derives a whole tile of its own.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kRederiveThreads = 512;
+constexpr uint32_t kRederiveGroups = 1024;        // 4 workgroups of 8 waves on each of 256 compute units
+constexpr int kRdRowChunks = kEncTile / (kRederiveThreads / 64) / 512;   // 4 chunks per lane
+
+// The first record of tile t: its block's offset plus the block's tiles before it.
+__device__ __forceinline__ uint64_t tile_first_record(const uint32_t *__restrict__ tile_counts,
+                                                      const uint64_t *__restrict__ block_offsets, uint32_t t)
+{
+    const uint32_t b = t / kTilesPerBlock;
+    uint64_t first = block_offsets[b];
+    for (uint32_t u = kTilesPerBlock * b; u < t; ++u) first += tile_counts[u] & ~kRederiveFlag;
+    return first;
+}
+
+__device__ __forceinline__ void rederive_tile_bf16_group(const uint16_t *__restrict__ in, uint64_t n, uint32_t t,
+                                                         uint64_t dst_first, RederiveLds &L, uint32_t *wave_totals,
+                                                         uint8_t *__restrict__ out)
+{
+    constexpr int C = kRdRowChunks;
+    const uint32_t lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const uint64_t base = (uint64_t)t * kEncTile + (uint64_t)wave * (512 * C);
+    const bool whole = base + 512 * C <= n;                      // wave-uniform
+    uint4 q[C];
+    if (whole) {
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+            q[j] = load_nt(reinterpret_cast<const uint4 *>(in + base + (uint64_t)(j * 64 + lane) * 8));
+    } else {
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+            uint16_t v[8];
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) v[k] = (c0 + k < n) ? in[c0 + k] : 0;
+            q[j] = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
+                              v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
+        }
+    }
+    const uint8_t *esc8 = reinterpret_cast<const uint8_t *>(L.esc32);
+    uint32_t m[C], lane_total = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        uint32_t ea, eb;
+        m[j] = escapes8_bf16(q[j], esc8, ea, eb);
+        if (!whole) {
+            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+            if (c0 >= n) m[j] = 0;
+            else if (c0 + 8 > n) m[j] &= (1u << (uint32_t)(n - c0)) - 1;
+        }
+        lane_total += __popc(m[j]);
+    }
+    const uint32_t wave_total = read_lane63(wave_inclusive_sum(lane_total));
+    if (lane == 0) wave_totals[wave] = wave_total;
+    __syncthreads();
+    uint32_t before = 0;
+    for (uint32_t w = 0; w < wave; ++w) before += wave_totals[w];
+    RecordWriter wr;
+    wr.begin(L, dst_first + 3ull * before);
+    uint32_t *seg32 = reinterpret_cast<uint32_t *>(L.seg);
+#pragma unroll
+    for (int h = 0; h < C / 2; ++h) {
+        const uint32_t cnt2[2] = {(uint32_t)__popc(m[2 * h]), (uint32_t)__popc(m[2 * h + 1])};
+        uint32_t row_base[2], row_total[2], lane_before[2];
+        const uint32_t count = wave_chunk_ranks<2>(cnt2, row_base, row_total, lane_before);
+        if (count == 0) continue;                                // wave-uniform
+        const uint32_t lead = wr.open(L, count);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int j = 2 * h + k;
+            if (m[j]) {
+                uint32_t ea, eb;
+                (void)escapes8_bf16(q[j], esc8, ea, eb);         // exponent bytes again (the mask is known)
+                const uint32_t pos0 = (uint32_t)((base + (uint64_t)(j * 64 + lane) * 8) & 0xFFFFu);
+                or_records8(seg32, lead + 3 * (row_base[k] + lane_before[k]), m[j], ea, eb, pos0, L.slots);
+            }
+        }
+        wr.flush(L, out, count);
+    }
+    wr.finish(L, out);
+    __syncthreads();                                              // wave_totals is reused by the next tile
+}
+
+template <int DT>
+__global__ __launch_bounds__(kRederiveThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_rederive(
+    const uint32_t *__restrict__ heavy_list, const uint32_t *__restrict__ heavy_count,
+    const uint32_t *__restrict__ tile_counts, const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out,
+    uint64_t off_esc, const void *__restrict__ in, uint64_t n, Codebook4 cb, const uint32_t *__restrict__ cb_dev)
+{
+    __shared__ RederiveLds lds[kRederiveThreads / 64];
+    __shared__ uint32_t wave_totals[kRederiveThreads / 64];
+    const uint32_t count = *heavy_count;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    RederiveLds &L = lds[wave];
+    if (DT == SZ_BF16) {
+        if (blockIdx.x >= count) return;                          // workgroup-uniform
+        if (cb_dev) cb = load_codebook(cb_dev);
+        build_wave_tables(L, cb, 256);
+#pragma unroll 1
+        for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) {
+            const uint32_t t = heavy_list[g];
+            const uint64_t dst = off_esc + 3 * tile_first_record(tile_counts, block_offsets, t);
+            rederive_tile_bf16_group(static_cast<const uint16_t *>(in), n, t, dst, L, wave_totals, out);
+        }
+    } else {
+        const uint32_t waves = gridDim.x * (kRederiveThreads / 64);
+        uint32_t i = blockIdx.x * (kRederiveThreads / 64) + wave;
+        if (i >= count) return;
+        if (cb_dev) cb = load_codebook(cb_dev);
+        build_wave_tables(L, cb, 32);
+#pragma unroll 1
+        for (; i < count; i += waves) {
+            const uint32_t t = heavy_list[i];
+            const uint64_t dst0 = off_esc + 3 * tile_first_record(tile_counts, block_offsets, t);
+            rederive_tile_e5m2(static_cast<const uint8_t *>(in), n, t, reinterpret_cast<const uint8_t *>(L.table32),
+                               reinterpret_cast<uint8_t *>(L.seg), out + (dst0 & ~uint64_t(3)), (uint32_t)(dst0 & 3));
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1177,6 +1548,8 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
     int32_t *status = reinterpret_cast<int32_t *>(ws);
     uint32_t *tile_counts = reinterpret_cast<uint32_t *>(ws + w.counts);
     uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
+    uint32_t *heavy_list = reinterpret_cast<uint32_t *>(ws + w.heavy);
+    uint32_t *heavy_count = reinterpret_cast<uint32_t *>(ws + kHeavyCount);
     uint8_t *stage = ws + w.stage;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -1251,18 +1624,28 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
         }
         LaunchScope scope("sz_enc_scan", s);
         hipLaunchKernelGGL(sz_enc_scan, dim3(1), dim3(kScanThreads), 0, s, tile_counts, (uint32_t)g.nt,
-                           block_offsets, out, h, cb_dev, status);
+                           block_offsets, out, h, cb_dev, status, heavy_list, heavy_count);
     }
     if (g.nt) {
         LaunchScope scope("sz_enc_compact", s);
         const uint32_t groups = (uint32_t)((g.nb + kCompactThreads / 64 - 1) / (kCompactThreads / 64));
         if (dtype == SZ_BF16)
             hipLaunchKernelGGL(sz_enc_compact<SZ_BF16>, dim3(groups), dim3(kCompactThreads), 0, s, stage, tile_counts,
-                               block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev,
-                               escape_item_bytes(version), (uint32_t)w.slot);
+                               block_offsets, out, g.off_esc, g.nt, g.nb, escape_item_bytes(version), (uint32_t)w.slot);
         else
             hipLaunchKernelGGL(sz_enc_compact<SZ_FP8_E5M2>, dim3(groups), dim3(kCompactThreads), 0, s, stage,
-                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, d_in, g.n, cb4, cb_dev, 3u, (uint32_t)w.slot);
+                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, 3u, (uint32_t)w.slot);
+    }
+    if (g.nt && version == kTop16) {
+        // the formats other than Top-16 stage every tile: no tile is flagged
+        LaunchScope scope("sz_enc_rederive", s);
+        const uint32_t groups = (uint32_t)std::min<uint64_t>(kRederiveGroups, g.nt);
+        if (dtype == SZ_BF16)
+            hipLaunchKernelGGL(sz_enc_rederive<SZ_BF16>, dim3(groups), dim3(kRederiveThreads), 0, s, heavy_list,
+                               heavy_count, tile_counts, block_offsets, out, g.off_esc, d_in, g.n, cb4, cb_dev);
+        else
+            hipLaunchKernelGGL(sz_enc_rederive<SZ_FP8_E5M2>, dim3(groups), dim3(kRederiveThreads), 0, s, heavy_list,
+                               heavy_count, tile_counts, block_offsets, out, g.off_esc, d_in, g.n, cb4, cb_dev);
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }
