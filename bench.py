@@ -59,6 +59,8 @@ def parse_args(argv=None):
     p.add_argument("--core-only", action="store_true",
                    help="time only the encode+decode step of the headline workload (no per-config rows, "
                         "calibration, format or transfer sections), e.g. under a profiler")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the calibration, format and transfer sections (the per-config rows stay)")
     p.add_argument("--cpu-sample-log2", type=int, default=29,
                    help="elements of the headline workload the oracle baseline encodes and decodes (log2; "
                         "2^29 is about 12 s of single-core work)")
@@ -390,7 +392,7 @@ def main():
     traffic = load_traffic(dominant, args.workload)
 
     calibration = formats = transfer = None
-    if not args.core_only:
+    if not args.core_only and not args.no_extras:
         calibration, formats, transfer = extra_sections(sz, c, args.runs, dirs)
     copy = reference_copy_rate(sz, alg, args.runs, dev)
 

@@ -50,7 +50,6 @@ constexpr uint32_t kEncTile = kRow * (kEncThreads / 64);  // 16384
 constexpr uint32_t kTilesPerBlock = kBlock / kEncTile;    // 4
 constexpr uint32_t kDecThreads = 1024;                    // 16 waves = one 64K block
 constexpr uint32_t kScanThreads = 1024;
-constexpr uint32_t kCompactThreads = 256;                 // one wave per tile of a block
 
 constexpr uint64_t up256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 
@@ -92,13 +91,11 @@ inline uint64_t stage_slot_bytes(uint32_t version, uint64_t nt)
     return 3ull * kRederiveRecords;
 }
 
-// Encode workspace layout (byte offsets): the status word (byte 0) and the
-// number of flagged tiles (byte 8) in the first 256 bytes, then tile counts,
-// block offsets, the list of flagged tiles and the escape staging
-// (stage_slot_bytes per tile).
-constexpr uint64_t kHeavyCount = 8;
+// Encode workspace layout (byte offsets): the status word (first 256 bytes),
+// tile counts, block offsets and the escape staging (stage_slot_bytes per
+// tile).
 struct WsLayout {
-    uint64_t counts, offsets, heavy, stage, slot, total;
+    uint64_t counts, offsets, stage, slot, total;
 };
 
 inline WsLayout ws_layout(uint32_t version, int dtype, uint64_t n)
@@ -107,8 +104,7 @@ inline WsLayout ws_layout(uint32_t version, int dtype, uint64_t n)
     WsLayout w;
     w.counts = 256;
     w.offsets = w.counts + up256(4 * g.nt + 16);
-    w.heavy = w.offsets + up256(8 * g.nb + 16);
-    w.stage = w.heavy + up256(4 * g.nt + 16);
+    w.stage = w.offsets + up256(8 * g.nb + 16);
     w.slot = stage_slot_bytes(version, g.nt);
     // 16 bytes past the last slot: the record copies read whole words
     w.total = w.stage + up256(w.slot * g.nt + 16);

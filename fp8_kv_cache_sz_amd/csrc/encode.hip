@@ -682,40 +682,32 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
                                                             uint64_t *__restrict__ block_offsets,
                                                             uint8_t *__restrict__ out, HeaderArgs h,
                                                             const uint32_t *__restrict__ cb_dev,
-                                                            int32_t *__restrict__ status,
-                                                            uint32_t *__restrict__ heavy_list,
-                                                            uint32_t *__restrict__ heavy_count)
+                                                            int32_t *__restrict__ status)
 {
     __shared__ ScanLds lds;
-    __shared__ uint32_t heavy;
-    const uint32_t tid = threadIdx.x, lane = lane_id();
+    const uint32_t tid = threadIdx.x;
     // a bad device codebook zeroes the magic and sets the status word
     Codebook4 cb = h.cb;
     const int32_t verdict = device_codebook_verdict(cb_dev, h.dtype, cb);
     const uint32_t nb = (uint32_t)h.nb;
-    if (tid == 0) {
-        lds.carry = 0;
-        heavy = 0;
-    }
+    if (tid == 0) lds.carry = 0;
     uint32_t *block_counts = reinterpret_cast<uint32_t *>(out + 64);
     for (uint32_t b0 = 0; b0 < nb; b0 += kScanBatch * kScanThreads) {
-        uint32_t x[kScanBatch], flags[kScanBatch];
+        uint32_t x[kScanBatch];
 #pragma unroll
         for (int i = 0; i < kScanBatch; ++i) {
             const uint32_t b = b0 + i * kScanThreads + tid;
             x[i] = 0;
-            flags[i] = 0;
             if (b < nb) {
                 const uint4 v = *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b);
                 const uint32_t t = kTilesPerBlock * b;
                 const uint32_t m = ~kRederiveFlag;
-                const uint32_t vy = (t + 1 < nt) ? v.y : 0, vz = (t + 2 < nt) ? v.z : 0, vw = (t + 3 < nt) ? v.w : 0;
-                x[i] = (v.x & m) + (vy & m) + (vz & m) + (vw & m);
-                flags[i] = (v.x >> 31) | ((vy >> 31) << 1) | ((vz >> 31) << 2) | ((vw >> 31) << 3);
+                x[i] = (v.x & m) + ((t + 1 < nt) ? v.y & m : 0) + ((t + 2 < nt) ? v.z & m : 0) +
+                       ((t + 3 < nt) ? v.w & m : 0);
             }
         }
         uint64_t base[kScanBatch];
-        scan_batch(x, base, lds);       // its barriers also publish `heavy` before the first append
+        scan_batch(x, base, lds);
 #pragma unroll
         for (int i = 0; i < kScanBatch; ++i) {
             const uint32_t b = b0 + i * kScanThreads + tid;
@@ -723,39 +715,26 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
                 block_counts[b] = x[i];
                 block_offsets[b] = base[i];
             }
-            // flagged tiles go to the list of tiles the re-derivation kernel
-            // takes (in no particular order: each tile's records have a fixed place)
-            const uint32_t nf = __popc(flags[i]);
-            const uint32_t incl = wave_inclusive_sum(nf);
-            const uint32_t wave_total = read_lane63(incl);
-            if (wave_total) {                                          // wave-uniform
-                uint32_t at = 0;
-                if (lane == 63) at = atomicAdd(&heavy, wave_total);
-                at = __builtin_amdgcn_readlane(at, 63) + incl - nf;
-                for (uint32_t f = flags[i]; f; f &= f - 1) heavy_list[at++] = kTilesPerBlock * b + __builtin_ctz(f);
-            }
         }
     }
-    __syncthreads();
     const uint64_t total = lds.carry;
     write_header(out, h, cb, verdict, false, status);
     if (tid == 0) {
         reinterpret_cast<uint32_t *>(out)[4] = (uint32_t)total;
         reinterpret_cast<uint32_t *>(out)[5] = (uint32_t)(total >> 32);
-        *heavy_count = heavy;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Kernel: escape compaction.  One wave per block (four blocks per workgroup)
-// copies the staged records of the block's four tiles (3 bytes each) to
-// out[off_esc + 3 * offset ...), tile after tile; when no tile of the block
-// holds more than kGroupCopyRecords records, four 16-lane groups copy the four
-// tiles at once.  The body of each copy is written with 16-byte aligned
-// dwordx4 stores assembled by v_alignbyte_b32 from five staged words; the
-// unaligned bytes at both ends, whose dwords the neighbouring tiles share, are
-// written byte by byte.  Flagged (escape-heavy) tiles are re-encoded from the
-// input instead and their records written straight to their final place.
+// Escape compaction: staged records (3 bytes each) are copied to
+// out[off_esc + 3 * offset ...), one wave per block, tile after tile; when no
+// tile of the block holds more than kGroupCopyRecords records, four 16-lane
+// groups copy the four tiles at once.  The body of each copy is written with
+// 16-byte aligned dwordx4 stores assembled by v_alignbyte_b32 from five staged
+// words; the unaligned bytes at both ends, whose dwords the neighbouring tiles
+// share, are written byte by byte.  Flagged (escape-heavy) tiles are derived
+// again from the input instead and their records written straight to their
+// final place.
 // ---------------------------------------------------------------------------
 // Copies len bytes of staged records to out[dst0, dst0 + len) with the lanes
 // [0, width) of a lane group (lane = index inside the group).
@@ -907,7 +886,7 @@ __device__ __forceinline__ void rederive_tile_e5m2(const uint8_t *__restrict__ i
 }
 
 // ---------------------------------------------------------------------------
-// Escape-heavy tiles of large streams (sz_enc_rederive below): the records of
+// Escape-heavy tiles of large streams (sz_enc_compact below): the records of
 // a tile are derived again from the input and written to their final place
 // two chunk rows (1024 elements) at a time, in three steps:
 //   * each lane turns an 8-element chunk into the compacted byte string of
@@ -1153,19 +1132,14 @@ __device__ __forceinline__ void compact_block(const uint8_t *__restrict__ stage,
     }
 }
 
-// Kernel: escape compaction of the staged tiles.  One wave per 64K block,
-// four blocks per workgroup: a wave copies the staged records of its block's
-// tiles to their place (16-lane groups copy the four tiles at once when none
-// is flagged and none holds more than kGroupCopyRecords records).  Flagged
-// (escape-heavy) tiles are left to sz_enc_rederive.
-template <int DT>
-__global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_compact(
-    const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
-    const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
-    uint64_t nb, uint32_t item, uint32_t slot)
+// Copies the staged records of block b's unflagged tiles to their place with
+// one wave (16-lane groups copy the four tiles at once when none is flagged
+// and none holds more than kGroupCopyRecords records).
+__device__ __forceinline__ void copy_block_records(const uint8_t *__restrict__ stage,
+                                                   const uint32_t *__restrict__ tile_counts,
+                                                   const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out,
+                                                   uint64_t off_esc, uint64_t nt, uint64_t b, uint32_t item, uint32_t slot)
 {
-    const uint64_t b = (uint64_t)blockIdx.x * (kCompactThreads / 64) + threadIdx.x / 64;
-    if (b >= nb) return;
     const uint32_t lane = lane_id();
     // lanes 0..3 fetch the tile counts, lane 4 the block's escape offset
     const uint64_t t0 = kTilesPerBlock * b;
@@ -1205,21 +1179,25 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
 }
 
 // ---------------------------------------------------------------------------
-// Kernel: re-derivation of the flagged (escape-heavy) tiles, which the dense
-// encoders did not stage, listed by sz_enc_scan.  Its grid fills the GPU once
-// (kRederiveGroups workgroups at most) and takes the listed tiles in turn,
-// workgroup g the entries g, g + G, g + 2G, ...; with no flagged tile every
-// workgroup exits after one load.  A tile's first record follows its block's
-// offset and the counts of the block's tiles before it.
+// Kernel: escape compaction of streams above kFusedPrefixTiles tiles, after
+// sz_enc_scan.  512-lane workgroups; wave w of workgroup g copies the staged
+// records of block 8 g + w.  Then the flagged (escape-heavy) tiles, which the
+// dense encoders did not stage, are derived again from the input: workgroup
+// g takes the tiles g, g + G, g + 2G, ... (G workgroups, at least
+// kRederiveGroups when the stream has that many tiles, so that the GPU is
+// full), reads their tile counts (one per tile and thread), lists the
+// flagged ones in LDS in order, and re-derives them; with no flagged tile
+// that one load is all.  A tile's first record follows its block's offset
+// and the counts of the block's tiles before it.
 //   BF16: the eight waves share a tile, wave w its 2048 elements
-//   [2048 w, 2048 w + 2048), all loaded at once (a wave waits for its loads
-//   only once per tile, not behind the stores of earlier passes); the wave
-//   totals meet in LDS and each wave writes its records after those of the
-//   waves before it, two chunk rows at a time.
-//   E5M2: each wave re-derives a whole tile of its own.
+//   [2048 w, 2048 w + 2048), all loaded at once; the wave totals meet in LDS
+//   and each wave writes its records after those of the waves before it, two
+//   chunk rows at a time.  The next tile's loads are issued before the
+//   current tile's records are written.
+//   E5M2: each wave re-derives whole tiles of the list on its own.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kRederiveThreads = 512;
-constexpr uint32_t kRederiveGroups = 1024;        // 4 workgroups of 8 waves on each of 256 compute units
+constexpr uint32_t kRederiveGroups = 768;         // 3 workgroups of 8 waves (80 registers) on each compute unit
 constexpr int kRdRowChunks = kEncTile / (kRederiveThreads / 64) / 512;   // 4 chunks per lane
 
 // The first record of tile t: its block's offset plus the block's tiles before it.
@@ -1232,17 +1210,16 @@ __device__ __forceinline__ uint64_t tile_first_record(const uint32_t *__restrict
     return first;
 }
 
-__device__ __forceinline__ void rederive_tile_bf16_group(const uint16_t *__restrict__ in, uint64_t n, uint32_t t,
-                                                         uint64_t dst_first, RederiveLds &L, uint32_t *wave_totals,
-                                                         uint8_t *__restrict__ out)
+// This wave's 512 C elements of tile t: plain dwordx4 loads, or guarded ones
+// for the part that holds the end of the input.
+template <int C>
+__device__ __forceinline__ void load_tile_part_bf16(const uint16_t *__restrict__ in, uint64_t n, uint32_t t,
+                                                    uint4 (&q)[C])
 {
-    constexpr int C = kRdRowChunks;
     const uint32_t lane = lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const uint64_t base = (uint64_t)t * kEncTile + (uint64_t)wave * (512 * C);
-    const bool whole = base + 512 * C <= n;                      // wave-uniform
-    uint4 q[C];
-    if (whole) {
+    if (base + 512 * C <= n) {                                    // wave-uniform
 #pragma unroll
         for (int j = 0; j < C; ++j)
             q[j] = load_nt(reinterpret_cast<const uint4 *>(in + base + (uint64_t)(j * 64 + lane) * 8));
@@ -1257,83 +1234,144 @@ __device__ __forceinline__ void rederive_tile_bf16_group(const uint16_t *__restr
                               v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
         }
     }
+}
+
+// The BF16 tiles list[0 .. count) (in LDS) of this workgroup, in order.
+// Per tile: escape masks and exponent bytes from the loaded words, the wave
+// totals' prefix through LDS, then each wave's records after those of the
+// waves before it.  The next tile's loads are issued before this tile's
+// records are written, so its words arrive while the stores go out (and
+// waiting for them does not wait for those stores, which come later in the
+// in-order counter).
+__device__ __forceinline__ void rederive_tiles_bf16(const uint16_t *__restrict__ in, uint64_t n, const uint32_t *list,
+                                                    uint32_t count, const uint32_t *__restrict__ tile_counts,
+                                                    const uint64_t *__restrict__ block_offsets, uint64_t off_esc,
+                                                    RederiveLds &L, uint32_t *wave_totals, uint8_t *__restrict__ out)
+{
+    constexpr int C = kRdRowChunks;
+    const uint32_t lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const uint8_t *esc8 = reinterpret_cast<const uint8_t *>(L.esc32);
-    uint32_t m[C], lane_total = 0;
+    uint32_t *seg32 = reinterpret_cast<uint32_t *>(L.seg);
+    uint32_t t = list[0];
+    uint4 q[C];
+    load_tile_part_bf16<C>(in, n, t, q);
+#pragma unroll 1
+    for (uint32_t i = 0; i < count; ++i) {
+        const uint64_t base = (uint64_t)t * kEncTile + (uint64_t)wave * (512 * C);
+        uint32_t m[C], ea[C], eb[C], lane_total = 0;
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-        uint32_t ea, eb;
-        m[j] = escapes8_bf16(q[j], esc8, ea, eb);
-        if (!whole) {
+        for (int j = 0; j < C; ++j) {
+            m[j] = escapes8_bf16(q[j], esc8, ea[j], eb[j]);
             const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
             if (c0 >= n) m[j] = 0;
             else if (c0 + 8 > n) m[j] &= (1u << (uint32_t)(n - c0)) - 1;
+            lane_total += __popc(m[j]);
         }
-        lane_total += __popc(m[j]);
-    }
-    const uint32_t wave_total = read_lane63(wave_inclusive_sum(lane_total));
-    if (lane == 0) wave_totals[wave] = wave_total;
-    __syncthreads();
-    uint32_t before = 0;
-    for (uint32_t w = 0; w < wave; ++w) before += wave_totals[w];
-    RecordWriter wr;
-    wr.begin(L, dst_first + 3ull * before);
-    uint32_t *seg32 = reinterpret_cast<uint32_t *>(L.seg);
+        // the next tile (this one again after the last: no branch around the loads)
+        const uint32_t tn = i + 1 < count ? list[i + 1] : t;
+        load_tile_part_bf16<C>(in, n, tn, q);
+        const uint64_t first = tile_first_record(tile_counts, block_offsets, t);
+        const uint32_t wave_total = read_lane63(wave_inclusive_sum(lane_total));
+        if (lane == 0) wave_totals[wave] = wave_total;
+        __syncthreads();
+        uint32_t before = 0;
+        for (uint32_t w = 0; w < wave; ++w) before += wave_totals[w];
+        RecordWriter wr;
+        wr.begin(L, off_esc + 3 * (first + before));
 #pragma unroll
-    for (int h = 0; h < C / 2; ++h) {
-        const uint32_t cnt2[2] = {(uint32_t)__popc(m[2 * h]), (uint32_t)__popc(m[2 * h + 1])};
-        uint32_t row_base[2], row_total[2], lane_before[2];
-        const uint32_t count = wave_chunk_ranks<2>(cnt2, row_base, row_total, lane_before);
-        if (count == 0) continue;                                // wave-uniform
-        const uint32_t lead = wr.open(L, count);
+        for (int h = 0; h < C / 2; ++h) {
+            const uint32_t cnt2[2] = {(uint32_t)__popc(m[2 * h]), (uint32_t)__popc(m[2 * h + 1])};
+            uint32_t row_base[2], row_total[2], lane_before[2];
+            const uint32_t cnt = wave_chunk_ranks<2>(cnt2, row_base, row_total, lane_before);
+            if (cnt == 0) continue;                              // wave-uniform
+            const uint32_t lead = wr.open(L, cnt);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int j = 2 * h + k;
-            if (m[j]) {
-                uint32_t ea, eb;
-                (void)escapes8_bf16(q[j], esc8, ea, eb);         // exponent bytes again (the mask is known)
+            for (int k = 0; k < 2; ++k) {
+                const int j = 2 * h + k;
                 const uint32_t pos0 = (uint32_t)((base + (uint64_t)(j * 64 + lane) * 8) & 0xFFFFu);
-                or_records8(seg32, lead + 3 * (row_base[k] + lane_before[k]), m[j], ea, eb, pos0, L.slots);
+                if (m[j]) or_records8(seg32, lead + 3 * (row_base[k] + lane_before[k]), m[j], ea[j], eb[j], pos0,
+                                      L.slots);
             }
+            wr.flush(L, out, cnt);
         }
-        wr.flush(L, out, count);
+        wr.finish(L, out);
+        __syncthreads();                                          // wave_totals is reused by the next tile
+        t = tn;
     }
-    wr.finish(L, out);
-    __syncthreads();                                              // wave_totals is reused by the next tile
+}
+
+// Flagged tiles among first + stride (i0 + k), k = 0 .. threads - 1, below
+// nt, into list (in order); returns their number.  One tile count per tile
+// and thread.
+__device__ __forceinline__ uint32_t list_flagged_tiles(const uint32_t *__restrict__ tile_counts, uint32_t nt,
+                                                       uint32_t first, uint32_t stride, uint32_t i0, uint32_t *list,
+                                                       uint32_t *wave_sums)
+{
+    const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
+    const uint64_t t64 = first + (uint64_t)stride * (i0 + tid);
+    const bool flagged = t64 < nt && (tile_counts[t64 < nt ? t64 : 0] & kRederiveFlag);
+    const uint32_t nf = flagged ? 1u : 0u;
+    const uint32_t incl = wave_inclusive_sum(nf);
+    if (lane == 63) wave_sums[wave] = incl;
+    __syncthreads();
+    uint32_t at = incl - nf, total = 0;
+    for (uint32_t w = 0; w < kRederiveThreads / 64; ++w) {
+        const uint32_t v = wave_sums[w];
+        if (w < wave) at += v;
+        total += v;
+    }
+    if (flagged) list[at] = (uint32_t)t64;
+    __syncthreads();
+    return total;
 }
 
 template <int DT>
-__global__ __launch_bounds__(kRederiveThreads) __attribute__((amdgpu_waves_per_eu(8))) void sz_enc_rederive(
-    const uint32_t *__restrict__ heavy_list, const uint32_t *__restrict__ heavy_count,
-    const uint32_t *__restrict__ tile_counts, const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out,
-    uint64_t off_esc, const void *__restrict__ in, uint64_t n, Codebook4 cb, const uint32_t *__restrict__ cb_dev)
+__global__ __launch_bounds__(kRederiveThreads) __attribute__((amdgpu_waves_per_eu(6))) void sz_enc_compact(
+    const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
+    const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
+    uint64_t nb, uint32_t item, uint32_t slot, const void *__restrict__ in, uint64_t n, Codebook4 cb,
+    const uint32_t *__restrict__ cb_dev, uint32_t rederive)
 {
-    __shared__ RederiveLds lds[kRederiveThreads / 64];
-    __shared__ uint32_t wave_totals[kRederiveThreads / 64];
-    const uint32_t count = *heavy_count;
+    constexpr uint32_t kWaves = kRederiveThreads / 64;
+    __shared__ RederiveLds lds[kWaves];
+    __shared__ uint32_t list[kRederiveThreads];
+    __shared__ uint32_t wave_sums[kWaves];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    // staged records: one wave per block
+    const uint64_t b = (uint64_t)blockIdx.x * kWaves + wave;
+    if (b < nb) copy_block_records(stage, tile_counts, block_offsets, out, off_esc, nt, b, item, slot);
+    if (!rederive) return;
     RederiveLds &L = lds[wave];
-    if (DT == SZ_BF16) {
-        if (blockIdx.x >= count) return;                          // workgroup-uniform
-        if (cb_dev) cb = load_codebook(cb_dev);
-        build_wave_tables(L, cb, 256);
+    // flagged tiles: workgroup g takes the tiles g, g + G, g + 2G, ...: the
+    // tiles that the workgroups work on at one time lie next to each other in
+    // memory (which measured markedly faster than giving each workgroup a
+    // contiguous range).  Tile indices fit 32 bits (n <= 2^40 gives at most
+    // 2^26 tiles).
+    const uint32_t tiles = blockIdx.x < nt ? (uint32_t)((nt - blockIdx.x + gridDim.x - 1) / gridDim.x) : 0;
+    bool built = false;
 #pragma unroll 1
-        for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) {
-            const uint32_t t = heavy_list[g];
-            const uint64_t dst = off_esc + 3 * tile_first_record(tile_counts, block_offsets, t);
-            rederive_tile_bf16_group(static_cast<const uint16_t *>(in), n, t, dst, L, wave_totals, out);
+    for (uint32_t i0 = 0; i0 < tiles; i0 += kRederiveThreads) {
+        const uint32_t count =
+            list_flagged_tiles(tile_counts, (uint32_t)nt, blockIdx.x, gridDim.x, i0, list, wave_sums);
+        if (count == 0) continue;                                  // workgroup-uniform
+        if (!built) {
+            if (cb_dev) cb = load_codebook(cb_dev);
+            build_wave_tables(L, cb, DT == SZ_BF16 ? 256 : 32);
+            built = true;
         }
-    } else {
-        const uint32_t waves = gridDim.x * (kRederiveThreads / 64);
-        uint32_t i = blockIdx.x * (kRederiveThreads / 64) + wave;
-        if (i >= count) return;
-        if (cb_dev) cb = load_codebook(cb_dev);
-        build_wave_tables(L, cb, 32);
+        if (DT == SZ_BF16) {
+            rederive_tiles_bf16(static_cast<const uint16_t *>(in), n, list, count, tile_counts, block_offsets, off_esc,
+                                L, wave_sums, out);
+        } else {
 #pragma unroll 1
-        for (; i < count; i += waves) {
-            const uint32_t t = heavy_list[i];
-            const uint64_t dst0 = off_esc + 3 * tile_first_record(tile_counts, block_offsets, t);
-            rederive_tile_e5m2(static_cast<const uint8_t *>(in), n, t, reinterpret_cast<const uint8_t *>(L.table32),
-                               reinterpret_cast<uint8_t *>(L.seg), out + (dst0 & ~uint64_t(3)), (uint32_t)(dst0 & 3));
+            for (uint32_t i = wave; i < count; i += kWaves) {
+                const uint32_t t = list[i];
+                const uint64_t dst0 = off_esc + 3 * tile_first_record(tile_counts, block_offsets, t);
+                rederive_tile_e5m2(static_cast<const uint8_t *>(in), n, t, reinterpret_cast<const uint8_t *>(L.table32),
+                                   reinterpret_cast<uint8_t *>(L.seg), out + (dst0 & ~uint64_t(3)), (uint32_t)(dst0 & 3));
+            }
+            __syncthreads();                                      // the list is rebuilt for the next range
         }
     }
 }
@@ -1548,8 +1586,6 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
     int32_t *status = reinterpret_cast<int32_t *>(ws);
     uint32_t *tile_counts = reinterpret_cast<uint32_t *>(ws + w.counts);
     uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
-    uint32_t *heavy_list = reinterpret_cast<uint32_t *>(ws + w.heavy);
-    uint32_t *heavy_count = reinterpret_cast<uint32_t *>(ws + kHeavyCount);
     uint8_t *stage = ws + w.stage;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -1624,28 +1660,24 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
         }
         LaunchScope scope("sz_enc_scan", s);
         hipLaunchKernelGGL(sz_enc_scan, dim3(1), dim3(kScanThreads), 0, s, tile_counts, (uint32_t)g.nt,
-                           block_offsets, out, h, cb_dev, status, heavy_list, heavy_count);
+                           block_offsets, out, h, cb_dev, status);
     }
     if (g.nt) {
+        // one wave per block for the staged records; for Top-16 at least
+        // kRederiveGroups workgroups (the formats other than Top-16 stage
+        // every tile: no tile is flagged)
         LaunchScope scope("sz_enc_compact", s);
-        const uint32_t groups = (uint32_t)((g.nb + kCompactThreads / 64 - 1) / (kCompactThreads / 64));
+        const uint32_t rederive = version == kTop16 ? 1u : 0u;
+        uint64_t groups = (g.nb + kRederiveThreads / 64 - 1) / (kRederiveThreads / 64);
+        if (rederive) groups = std::max<uint64_t>(groups, std::min<uint64_t>(kRederiveGroups, g.nt));
         if (dtype == SZ_BF16)
-            hipLaunchKernelGGL(sz_enc_compact<SZ_BF16>, dim3(groups), dim3(kCompactThreads), 0, s, stage, tile_counts,
-                               block_offsets, out, g.off_esc, g.nt, g.nb, escape_item_bytes(version), (uint32_t)w.slot);
+            hipLaunchKernelGGL(sz_enc_compact<SZ_BF16>, dim3((uint32_t)groups), dim3(kRederiveThreads), 0, s, stage,
+                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, escape_item_bytes(version),
+                               (uint32_t)w.slot, d_in, g.n, cb4, cb_dev, rederive);
         else
-            hipLaunchKernelGGL(sz_enc_compact<SZ_FP8_E5M2>, dim3(groups), dim3(kCompactThreads), 0, s, stage,
-                               tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, 3u, (uint32_t)w.slot);
-    }
-    if (g.nt && version == kTop16) {
-        // the formats other than Top-16 stage every tile: no tile is flagged
-        LaunchScope scope("sz_enc_rederive", s);
-        const uint32_t groups = (uint32_t)std::min<uint64_t>(kRederiveGroups, g.nt);
-        if (dtype == SZ_BF16)
-            hipLaunchKernelGGL(sz_enc_rederive<SZ_BF16>, dim3(groups), dim3(kRederiveThreads), 0, s, heavy_list,
-                               heavy_count, tile_counts, block_offsets, out, g.off_esc, d_in, g.n, cb4, cb_dev);
-        else
-            hipLaunchKernelGGL(sz_enc_rederive<SZ_FP8_E5M2>, dim3(groups), dim3(kRederiveThreads), 0, s, heavy_list,
-                               heavy_count, tile_counts, block_offsets, out, g.off_esc, d_in, g.n, cb4, cb_dev);
+            hipLaunchKernelGGL(sz_enc_compact<SZ_FP8_E5M2>, dim3((uint32_t)groups), dim3(kRederiveThreads), 0, s,
+                               stage, tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, 3u, (uint32_t)w.slot, d_in,
+                               g.n, cb4, cb_dev, rederive);
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }

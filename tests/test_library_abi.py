@@ -82,11 +82,11 @@ def test_encoded_size_matches_oracle():
             ws = nat.sz_workspace_size(dtype, n)
             nt, nb = (n + 16383) // 16384, (n + 65535) // 65536
             assert ws % 256 == 0
-            # status, tile counts, block offsets, the list of flagged tiles,
-            # then one staging slot per 16K tile: 3 bytes per element up to
-            # 2,048 tiles, 12 KB per tile (4,096 records) above
+            # status, tile counts, block offsets, then one staging slot per
+            # 16K tile: 3 bytes per element up to 2,048 tiles, 12 KB per tile
+            # (4,096 records) above
             slot = 3 * 16384 if nt <= 2048 else 3 * 4096
-            fixed = 256 + up(4 * nt + 16) + up(8 * nb + 16) + up(4 * nt + 16)
+            fixed = 256 + up(4 * nt + 16) + up(8 * nb + 16)
             assert ws == fixed + up(slot * nt + 16), (dtype, n)
             dws = nat.sz_decode_workspace_size(dtype, n)
             assert dws == 256 + up(8 * nb + 16) and dws <= ws
