@@ -210,6 +210,17 @@ __device__ __forceinline__ uint32_t cb_entry(const Codebook4 &cb, uint32_t c)
     return (cb.w[c >> 2] >> (8 * (c & 3))) & 0xFFu;
 }
 
+// Entry c (0..15) where c differs between lanes: two byte selects of the
+// codebook words, so that the compiler does not index the struct (which
+// would place a copy of it in per-thread memory).
+__device__ __forceinline__ uint32_t cb_entry_lane(const Codebook4 &cb, uint32_t c)
+{
+    const uint32_t sel = (c & 7u) | 0x0C0C0C00u;          // byte c & 7, three zero bytes
+    const uint32_t lo = perm(cb.w[1], cb.w[0], sel);
+    const uint32_t hi = perm(cb.w[3], cb.w[2], sel);
+    return c < 8 ? lo : hi;
+}
+
 // A codebook that lives in device memory as an sz_codebook (word 0 = dtype,
 // words 1..4 = the 16 exponent bytes), as sz_calibrate_device writes it.
 __device__ __forceinline__ Codebook4 load_codebook(const uint32_t *cb_dev)

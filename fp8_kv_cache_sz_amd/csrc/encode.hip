@@ -9,27 +9,31 @@
 namespace sz {
 namespace {
 
+// LDS operations of one wave complete in order; this only keeps the compiler
+// from moving LDS accesses of the wave across the hand-over point.
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Exponent -> code table for encode.  Byte v = code of exponent v, or
 // `escape` (the escape flag 0x80 plus the code an escaped element carries)
-// when v is not among the first `entries` codebook entries.  Threads 0..63
-// fill 4 entries each.
+// when v is not among the first `entries` codebook entries.  Wave 0 builds
+// it: its lanes fill the table with `escape`, then lane c < entries stores
+// code c at byte cb[c].  Entries at or above `symbols` (possible only in a
+// device codebook, whose stream the header check then invalidates) store
+// nothing.  The caller synchronises the workgroup before the table is read.
 __device__ __forceinline__ void build_encode_table(uint32_t *table32, const Codebook4 &cb,
                                                    uint32_t symbols, uint32_t entries = 16,
                                                    uint32_t escape = 0x80u)
 {
     const uint32_t t = threadIdx.x;
-    if (t < 64 && t * 4 < symbols) {
-        uint32_t word = 0;
-#pragma unroll
-        for (uint32_t k = 0; k < 4; ++k) {
-            const uint32_t v = t * 4 + k;
-            uint32_t code = escape;
-#pragma unroll
-            for (uint32_t c = 0; c < 16; ++c)
-                if (c < entries && cb_entry(cb, c) == v) code = c;
-            word |= code << (8 * k);
-        }
-        table32[t] = word;
+    if (t < 64) {
+        if (t * 4 < symbols) table32[t] = escape * 0x01010101u;
+        wave_lds_fence();
+        const uint32_t v = cb_entry_lane(cb, t & 15u);
+        if (t < entries && v < symbols) reinterpret_cast<uint8_t *>(table32)[v] = (uint8_t)t;
     }
 }
 
@@ -133,49 +137,75 @@ __device__ __forceinline__ void encode_chunk_e5m2(const uint4 q0, const uint4 q1
     sm3[2] = (grp[2] >> 16) | (grp[3] << 8);
 }
 
-// E5M2 encode through a code-pair table: table16[e0 | e1 << 5] holds, for
-// two neighbouring elements with exponents e0 and e1, their two codes as one
-// code byte (low byte: code0 | code1 << 4, escapes coded 0) and their escape
-// flags (high byte: bit 0 = element 0, bit 1 = element 1).  One LDS read per
-// two elements replaces two reads, the nibble packing and the escape-mask
-// arithmetic of the byte table.
-__device__ __forceinline__ void build_pair_table(uint32_t *table16x2, const uint8_t *tab8)
+// E5M2 encode through a code-pair table.  Two neighbouring input bytes
+// w = b0 | b1 << 8 (elements 0 and 1 of a pair) are looked up at the LDS byte
+// address (w >> 1) & kPairMask: exponent e0 in address bits 1-5, the sign of
+// element 0 in bit 6, e1 in bits 9-13.  The sign does not change the entry;
+// it is kept in the address because it falls in the bank bits, where it
+// spreads a wave's reads over twice as many banks as e0 alone.  Entry (16
+// bits): low byte = code0 | code1 << 4 (escapes coded 0), high byte = escape
+// flags (bit 0 = element 0, bit 1 = element 1).  One LDS read per two
+// elements, and the address takes two VALU operations per input word (a
+// shift shared by the word's two pairs, one mask each).
+constexpr uint32_t kPairMask = 0x3E7Eu;
+constexpr uint32_t kPairTableBytes = kPairMask + 2;
+
+// Address of the pair in bits 16..31 of x (already shifted right by one):
+// one SDWA AND that reads the upper half-word of x.
+__device__ __forceinline__ uint32_t pair_addr_hi(uint32_t x, uint32_t mask)
 {
-    // thread t fills entries 4t .. 4t+3 (two words); e1 is the same for all four
+    uint32_t r;
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 src1_sel:DWORD"
+        : "=v"(r)
+        : "v"(x), "v"(mask));
+    return r;
+}
+
+// Builds the pair table from the byte table tab8 (build_encode_table, 32
+// symbols).  Row (s0, e1) holds the 32 entries of e0 = 0..31 at byte
+// s0 << 6 | e1 << 9; thread t < 256 writes entries 8q .. 8q+7 (q = t & 3) of
+// row t >> 2 as one 16-byte store.
+__device__ __forceinline__ void build_pair_table(uint32_t *pair32, const uint32_t *table32)
+{
     const uint32_t t = threadIdx.x;
     if (t < 256) {
-        const uint32_t c1 = tab8[t >> 3];
-        const uint32_t hi = ((c1 & 0xFu) << 4) | ((c1 >> 7) << 9);
+        const uint32_t row = t >> 2, q = t & 3u;
+        const uint32_t e1 = row >> 1;
+        const uint32_t c1 = (table32[e1 >> 2] >> (8 * (e1 & 3u))) & 0xFFu;
+        const uint32_t hi = (((c1 & 0xFu) << 4) | ((c1 >> 7) << 9)) * 0x00010001u;
         uint32_t e[4];
 #pragma unroll
-        for (uint32_t k = 0; k < 4; ++k) {
-            const uint32_t c0 = tab8[(4 * t + k) & 31u];
-            e[k] = (c0 & 0xFu) | ((c0 >> 7) << 8) | hi;
+        for (uint32_t h = 0; h < 2; ++h) {
+            const uint32_t w = table32[2 * q + h];                  // codes of e0 = 8q + 4h .. 8q + 4h + 3
+            const uint32_t nib = w & 0x0F0F0F0Fu, flg = (w >> 7) & 0x01010101u;
+            e[2 * h] = perm(flg, nib, 0x05010400u) | hi;            // entries of e0 = 8q + 4h, +1
+            e[2 * h + 1] = perm(flg, nib, 0x07030602u) | hi;        // entries of +2, +3
         }
-        table16x2[2 * t] = e[0] | (e[1] << 16);
-        table16x2[2 * t + 1] = e[2] | (e[3] << 16);
+        const uint32_t addr = ((row & 1u) << 6) | (e1 << 9) | (q << 4);
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(pair32) + addr) = make_uint4(e[0], e[1], e[2], e[3]);
     }
 }
 
-// One 32-element chunk: 16 code bytes, 12 sign/mantissa bytes, and per group
-// of 8 elements a flag word fl[s] whose byte k holds the escape flags of
-// elements 2k (bit 0) and 2k + 1 (bit 1) of the group.
-__device__ __forceinline__ void encode_chunk_e5m2_pairs(const uint4 q0, const uint4 q1, const uint16_t *table16,
-                                                        uint4 &nib, uint32_t sm3[3], uint32_t fl[4])
+// One 32-element chunk: 16 code bytes, 12 sign/mantissa bytes, and the
+// chunk's escape flags in one word F: bit 8k + 2s + h is element 8s + 2k + h
+// (s = group of 8 elements, k = pair in the group, h = element of the pair).
+__device__ __forceinline__ void encode_chunk_e5m2_pairs(const uint4 q0, const uint4 q1, const uint8_t *pairs,
+                                                        uint32_t mask, uint4 &nib, uint32_t sm3[3], uint32_t &F)
 {
     const uint32_t d[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
     uint32_t nibw[4], grp[4];
+    F = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const uint32_t a = d[2 * s], b = d[2 * s + 1];
-        // pair index e0 | e1 << 5 of elements (0,1) and (2,3) of a word
-        const uint32_t p0 = table16[((a >> 2) & 0x1Fu) | ((a >> 5) & 0x3E0u)];
-        const uint32_t p1 = table16[((a >> 18) & 0x1Fu) | ((a >> 21) & 0x3E0u)];
-        const uint32_t p2 = table16[((b >> 2) & 0x1Fu) | ((b >> 5) & 0x3E0u)];
-        const uint32_t p3 = table16[((b >> 18) & 0x1Fu) | ((b >> 21) & 0x3E0u)];
-        const uint32_t lo = perm(p1, p0, 0x0C0C0400u), hi = perm(p3, p2, 0x04000C0Cu);
-        nibw[s] = lo | hi;
-        fl[s] = perm(p1, p0, 0x0C0C0501u) | perm(p3, p2, 0x05010C0Cu);
+        const uint32_t a1 = a >> 1, b1 = b >> 1;
+        const uint32_t p0 = *reinterpret_cast<const uint16_t *>(pairs + (a1 & kPairMask));
+        const uint32_t p1 = *reinterpret_cast<const uint16_t *>(pairs + pair_addr_hi(a1, mask));
+        const uint32_t p2 = *reinterpret_cast<const uint16_t *>(pairs + (b1 & kPairMask));
+        const uint32_t p3 = *reinterpret_cast<const uint16_t *>(pairs + pair_addr_hi(b1, mask));
+        const uint32_t lo = perm(p1, p0, 0x05040100u), hi = perm(p3, p2, 0x05040100u);   // p0 | p1 << 16, p2 | p3 << 16
+        nibw[s] = perm(hi, lo, 0x06040200u);
+        F |= perm(hi, lo, 0x07050301u) << (2 * s);
         const uint32_t s_a = ((a >> 5) & 0x04040404u) | (a & 0x03030303u);
         const uint32_t s_b = ((b >> 5) & 0x04040404u) | (b & 0x03030303u);
         grp[s] = pack_sym3x4(s_a) | (pack_sym3x4(s_b) << 12);
@@ -186,18 +216,31 @@ __device__ __forceinline__ void encode_chunk_e5m2_pairs(const uint4 q0, const ui
     sm3[2] = (grp[2] >> 16) | (grp[3] << 8);
 }
 
-// Flag word of a group (byte k = flags of elements 2k, 2k+1) -> 8-bit mask.
-__device__ __forceinline__ uint32_t flags_to_mask8(uint32_t f)
+// Element index (0..31) of flag bit p of a chunk's flag word F.
+__device__ __forceinline__ uint32_t flag_element(uint32_t p)
 {
-    return (f & 3u) | ((f >> 6) & 0xCu) | ((f >> 12) & 0x30u) | ((f >> 18) & 0xC0u);
+    return ((p << 2) & 0x18u) | ((p >> 2) & 0x6u) | (p & 1u);
 }
 
-// Flag bits of the first v elements of a group (v in 0..8).
-__device__ __forceinline__ uint32_t group_flag_keep(int v)
+// Flag word -> escape mask in element order (bit i = element i).  F holds
+// 2-bit cells: cell (k, s) at bit 8k + 2s; the mask wants cell (s, k) at
+// 8s + 2k.  A 4 x 4 transpose of the cells in two delta swaps: the off-
+// diagonal 2 x 2 blocks (distance 12), then the off-diagonal cells inside
+// each block (distance 6).
+__device__ __forceinline__ uint32_t flags_to_elements(uint32_t F)
+{
+    uint32_t t = ((F >> 12) ^ F) & 0x0000F0F0u;
+    F ^= t ^ (t << 12);
+    t = ((F >> 6) ^ F) & 0x00CC00CCu;
+    return F ^ t ^ (t << 6);
+}
+
+// Flag-word bits of the first v elements of a chunk (v in 0..32).
+__device__ __forceinline__ uint32_t chunk_flag_keep(uint32_t v)
 {
     uint32_t m = 0;
-    for (int i = 0; i < 8; ++i)
-        if (i < v) m |= 1u << ((i / 2) * 8 + (i & 1));
+    for (uint32_t p = 0; p < 32; ++p)
+        if (flag_element(p) < v) m |= 1u << p;
     return m;
 }
 
@@ -230,14 +273,6 @@ __device__ __forceinline__ uint32_t lds_put_records(uint8_t *buf, uint32_t off, 
         off += 3;
     }
     return off;
-}
-
-__device__ __forceinline__ void wave_lds_fence()
-{
-    // LDS operations of one wave complete in order; this only keeps the
-    // compiler from moving LDS accesses across the hand-over point
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Copies `len` bytes, held in buf[g0 & 3, (g0 & 3) + len), to dst[g0, g0 + len).
@@ -471,8 +506,8 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
                                                               uint8_t *__restrict__ stage, uint32_t slot,
                                                               uint32_t rederive_above)
 {
-    __shared__ uint32_t table32[64];
-    __shared__ uint32_t table16x2[512];
+    __shared__ uint32_t table32[8];
+    __shared__ __align__(16) uint32_t pair32[kPairTableBytes / 4];
     __shared__ uint32_t wave_totals[kEncThreads / 64];
     __shared__ __align__(16) uint8_t seg_buf[kEncThreads / 64][kSegBytes];
     const uint32_t lane = lane_id();
@@ -498,17 +533,18 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
     if (cb_dev) cb = load_codebook(cb_dev);
     build_encode_table(table32, cb, 32);
     __syncthreads();
-    build_pair_table(table16x2, reinterpret_cast<const uint8_t *>(table32));
+    build_pair_table(pair32, table32);
     __syncthreads();
-    const uint16_t *table16 = reinterpret_cast<const uint16_t *>(table16x2);
-    uint32_t fl[kE5Chunks][4];
+    const uint8_t *pairs = reinterpret_cast<const uint8_t *>(pair32);
+    const uint32_t pair_mask = kPairMask;
+    uint32_t F[kE5Chunks];
     uint32_t cnt[kE5Chunks];
 #pragma unroll
     for (int j = 0; j < kE5Chunks; ++j) {
         const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 32;
         uint4 nib;
         uint32_t sm3[3];
-        encode_chunk_e5m2_pairs(q[j][0], q[j][1], table16, nib, sm3, fl[j]);
+        encode_chunk_e5m2_pairs(q[j][0], q[j][1], pairs, pair_mask, nib, sm3, F[j]);
         uint32_t *sm_dst = reinterpret_cast<uint32_t *>(out + off_sm + (c0 / 32) * 12);
         if (full_row || c0 + 32 <= n) {
             store_nt(reinterpret_cast<uint4 *>(out + off_nib + c0 / 2), nib);
@@ -522,8 +558,8 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
             for (int s = 0; s < 4; ++s) {
                 const int v = (int)valid - 8 * s;
                 nw[s] &= v >= 8 ? 0xFFFFFFFFu : (v <= 0 ? 0u : (uint32_t)((1ull << (4 * v)) - 1));
-                fl[j][s] &= group_flag_keep(v);
             }
+            F[j] &= chunk_flag_keep(valid);
             *reinterpret_cast<uint4 *>(out + off_nib + c0 / 2) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
             uint32_t sw[3] = {sm3[0], sm3[1], sm3[2]};
             const uint32_t bits = 3 * valid;
@@ -537,10 +573,9 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
             for (uint32_t i = 0; i < 12 && sm_start + i < sm_end; ++i)
                 out[sm_start + i] = (uint8_t)(sw[i / 4] >> (8 * (i & 3)));
         } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) fl[j][s] = 0;
+            F[j] = 0;
         }
-        cnt[j] = __popc(fl[j][0]) + __popc(fl[j][1]) + __popc(fl[j][2]) + __popc(fl[j][3]);
+        cnt[j] = __popc(F[j]);
     }
     uint32_t row_base[kE5Chunks], row_total[kE5Chunks], lane_before[kE5Chunks];
     const uint32_t wave_total = wave_chunk_ranks<kE5Chunks>(cnt, row_base, row_total, lane_before);
@@ -559,8 +594,7 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
                 if (cnt[j]) {
                     // the chunk's escapes in element order; each one's exponent is
                     // picked from the group of 8 input bytes that holds it
-                    uint32_t m = flags_to_mask8(fl[j][0]) | (flags_to_mask8(fl[j][1]) << 8) |
-                                 (flags_to_mask8(fl[j][2]) << 16) | (flags_to_mask8(fl[j][3]) << 24);
+                    uint32_t m = flags_to_elements(F[j]);
                     uint8_t *rec = tstage + 3ull * (rank + lane_before[j]);
                     const uint32_t pos0 = (uint32_t)(c0 & 0xFFFFu);
                     while (m) {
@@ -580,9 +614,10 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
             }
             uint32_t esc8[4];
             uint64_t ex[4];
+            const uint32_t m32 = flags_to_elements(F[j]);
 #pragma unroll
             for (int s8 = 0; s8 < 4; ++s8) {
-                esc8[s8] = flags_to_mask8(fl[j][s8]);
+                esc8[s8] = (m32 >> (8 * s8)) & 0xFFu;
                 ex[s8] = (uint64_t)((dw[2 * s8] >> 2) & 0x1F1F1F1Fu) |
                          ((uint64_t)((dw[2 * s8 + 1] >> 2) & 0x1F1F1F1Fu) << 32);
             }
