@@ -488,6 +488,40 @@ __global__ __launch_bounds__(kEncTile / (8 * C)) void sz_enc_dense_bf16(const ui
     if (threadIdx.x == 0) tile_counts[tile] = tile_total | (rederive ? kRederiveFlag : 0u);
 }
 
+// Writes the records of one E5M2 chunk (escape mask m in element order, the
+// chunk's 32 input bytes in dw, block-local position pos0 of element 0) to
+// rec, ascending.  Each exponent is picked from the group of 8 input bytes
+// that holds it.  rec is LDS or global memory (the caller's pointer decides).
+__device__ __forceinline__ void put_chunk_records_e5m2(uint8_t *rec, uint32_t m, const uint32_t (&dw)[8],
+                                                       uint32_t pos0)
+{
+    while (m) {
+        const uint32_t k = (uint32_t)__builtin_ctz(m);
+        m &= m - 1;
+        const uint32_t g = k >> 3;
+        const uint32_t lo = g == 0 ? dw[0] : g == 1 ? dw[2] : g == 2 ? dw[4] : dw[6];
+        const uint32_t hi = g == 0 ? dw[1] : g == 1 ? dw[3] : g == 2 ? dw[5] : dw[7];
+        const uint32_t pos = pos0 + k;
+        rec[0] = (uint8_t)pos;
+        rec[1] = (uint8_t)(pos >> 8);
+        rec[2] = (uint8_t)((perm(hi, lo, k & 7u) >> 2) & 0x1Fu);
+        rec += 3;
+    }
+}
+
+// Stores the first `bytes` bytes of an LDS tile buffer to a tile's staging
+// slot as whole dwords (the slot starts on a dword boundary; up to three
+// bytes past the records are written, inside the slot).  All threads of the
+// workgroup take part.
+template <uint32_t THREADS>
+__device__ __forceinline__ void store_tile_buffer(const uint8_t *tile_buf, uint8_t *tstage, uint32_t bytes)
+{
+    const uint32_t words = (bytes + 3) / 4;
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(tile_buf);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(tstage);
+    for (uint32_t i = threadIdx.x; i < words; i += THREADS) dst[i] = src[i];
+}
+
 // ---------------------------------------------------------------------------
 // Kernel: FP8 E5M2 dense encode + escape staging (the page's FP8 extension,
 // Contributions item 4).  Same tiling as BF16; a lane holds two 32-element
@@ -581,6 +615,14 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
     const uint32_t wave_total = wave_chunk_ranks<kE5Chunks>(cnt, row_base, row_total, lane_before);
     uint32_t tile_total;
     const uint32_t wave_before = workgroup_wave_prefix<kEncThreads / 64>(wave_total, wave_totals, tile_total);
+    // The records of a tile that fit the LDS tile buffer (all of seg_buf) are
+    // gathered there at their rank in the tile and leave as whole dwords
+    // after one more barrier (fewer, wider stores than a record at a time);
+    // otherwise rows with few records write them straight to the staging slot
+    // and rows with many go through the wave's LDS segment buffer.
+    constexpr uint32_t kTileBufRecords = (kEncThreads / 64) * kSegBytes / 3;
+    const bool to_tile_buf = tile_total <= kTileBufRecords;           // workgroup-uniform
+    uint8_t *tile_buf = &seg_buf[0][0];
     if (wave_total && tile_total <= rederive_above) {
         uint8_t *tstage = stage + tile * slot;
         uint8_t *buf = seg_buf[wave];
@@ -590,26 +632,15 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
             const uint32_t rank = wave_before + row_base[j];
             const uint32_t dw[8] = {q[j][0].x, q[j][0].y, q[j][0].z, q[j][0].w,
                                     q[j][1].x, q[j][1].y, q[j][1].z, q[j][1].w};
+            const uint32_t pos0 = (uint32_t)(c0 & 0xFFFFu);
+            if (to_tile_buf) {
+                if (cnt[j])
+                    put_chunk_records_e5m2(tile_buf + 3 * (rank + lane_before[j]), flags_to_elements(F[j]), dw, pos0);
+                continue;
+            }
             if (row_total[j] <= kDirectRecords) {                      // wave-uniform
-                if (cnt[j]) {
-                    // the chunk's escapes in element order; each one's exponent is
-                    // picked from the group of 8 input bytes that holds it
-                    uint32_t m = flags_to_elements(F[j]);
-                    uint8_t *rec = tstage + 3ull * (rank + lane_before[j]);
-                    const uint32_t pos0 = (uint32_t)(c0 & 0xFFFFu);
-                    while (m) {
-                        const uint32_t k = (uint32_t)__builtin_ctz(m);
-                        m &= m - 1;
-                        const uint32_t g = k >> 3;
-                        const uint32_t lo = g == 0 ? dw[0] : g == 1 ? dw[2] : g == 2 ? dw[4] : dw[6];
-                        const uint32_t hi = g == 0 ? dw[1] : g == 1 ? dw[3] : g == 2 ? dw[5] : dw[7];
-                        const uint32_t pos = pos0 + k;
-                        rec[0] = (uint8_t)pos;
-                        rec[1] = (uint8_t)(pos >> 8);
-                        rec[2] = (uint8_t)((perm(hi, lo, k & 7u) >> 2) & 0x1Fu);
-                        rec += 3;
-                    }
-                }
+                if (cnt[j])
+                    put_chunk_records_e5m2(tstage + 3ull * (rank + lane_before[j]), flags_to_elements(F[j]), dw, pos0);
                 continue;
             }
             uint32_t esc8[4];
@@ -640,6 +671,10 @@ __global__ __launch_bounds__(kEncThreads) void sz_enc_dense_e5m2(const uint8_t *
                 wave_lds_fence();
             }
         }
+    }
+    if (tile_total && tile_total <= rederive_above && to_tile_buf) {   // workgroup-uniform
+        __syncthreads();
+        store_tile_buffer<kEncThreads>(tile_buf, stage + tile * slot, 3 * tile_total);
     }
     if (threadIdx.x == 0) tile_counts[tile] = tile_total | (tile_total > rederive_above ? kRederiveFlag : 0u);
 }
