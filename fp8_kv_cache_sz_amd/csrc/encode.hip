@@ -1205,17 +1205,27 @@ __device__ __forceinline__ void compact_block(const uint8_t *__restrict__ stage,
 // Copies the staged records of block b's unflagged tiles to their place with
 // one wave (16-lane groups copy the four tiles at once when none is flagged
 // and none holds more than kGroupCopyRecords records).
-__device__ __forceinline__ void copy_block_records(const uint8_t *__restrict__ stage,
-                                                   const uint32_t *__restrict__ tile_counts,
-                                                   const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out,
-                                                   uint64_t off_esc, uint64_t nt, uint64_t b, uint32_t item, uint32_t slot)
+// The metadata of block b, one value per lane: lanes 0..3 the tile counts,
+// lane 4 the block's escape offset.
+__device__ __forceinline__ uint64_t block_meta(const uint32_t *__restrict__ tile_counts,
+                                               const uint64_t *__restrict__ block_offsets, uint64_t nt, uint64_t b)
 {
     const uint32_t lane = lane_id();
-    // lanes 0..3 fetch the tile counts, lane 4 the block's escape offset
     const uint64_t t0 = kTilesPerBlock * b;
     uint64_t meta = 0;
     if (lane < kTilesPerBlock && t0 + lane < nt) meta = tile_counts[t0 + lane];
     else if (lane == kTilesPerBlock) meta = block_offsets[b];
+    return meta;
+}
+
+// Copies the staged records of block b (metadata from block_meta) to their
+// place in the stream.
+__device__ __forceinline__ void copy_block_records(uint64_t meta, const uint8_t *__restrict__ stage,
+                                                   uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
+                                                   uint64_t b, uint32_t item, uint32_t slot)
+{
+    const uint32_t lane = lane_id();
+    const uint64_t t0 = kTilesPerBlock * b;
     const uint64_t off = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(meta >> 32), kTilesPerBlock) << 32) |
                          (uint32_t)__builtin_amdgcn_readlane((uint32_t)meta, kTilesPerBlock);
     uint32_t cnt[kTilesPerBlock], before[kTilesPerBlock], most = 0, run = 0, flagged = 0;
@@ -1251,8 +1261,9 @@ __device__ __forceinline__ void copy_block_records(const uint8_t *__restrict__ s
 // ---------------------------------------------------------------------------
 // Kernel: escape compaction of streams above kFusedPrefixTiles tiles, after
 // sz_enc_scan.  512-lane workgroups; wave w of workgroup g copies the staged
-// records of block 8 g + w.  Then the flagged (escape-heavy) tiles, which the
-// dense encoders did not stage, are derived again from the input: workgroup
+// records of blocks 8 g + w, 8 (g + G) + w, ... (G workgroups).  Then the
+// flagged (escape-heavy) tiles, which the dense encoders did not stage, are
+// derived again from the input: workgroup
 // g takes the tiles g, g + G, g + 2G, ... (G workgroups, at least
 // kRederiveGroups when the stream has that many tiles, so that the GPU is
 // full), reads their tile counts (one per tile and thread), lists the
@@ -1268,6 +1279,9 @@ __device__ __forceinline__ void copy_block_records(const uint8_t *__restrict__ s
 // ---------------------------------------------------------------------------
 constexpr uint32_t kRederiveThreads = 512;
 constexpr uint32_t kRederiveGroups = 768;         // 3 workgroups of 8 waves (80 registers) on each compute unit
+// Blocks whose staged records one wave copies (at most): fewer waves, each
+// overlapping the next block's metadata fetch with the current copy.
+constexpr uint64_t kCopyBlocksPerWave = 4;
 constexpr int kRdRowChunks = kEncTile / (kRederiveThreads / 64) / 512;   // 4 chunks per lane
 
 // The first record of tile t: its block's offset plus the block's tiles before it.
@@ -1408,9 +1422,21 @@ __global__ __launch_bounds__(kRederiveThreads) __attribute__((amdgpu_waves_per_e
     __shared__ uint32_t list[kRederiveThreads];
     __shared__ uint32_t wave_sums[kWaves];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-    // staged records: one wave per block
-    const uint64_t b = (uint64_t)blockIdx.x * kWaves + wave;
-    if (b < nb) copy_block_records(stage, tile_counts, block_offsets, out, off_esc, nt, b, item, slot);
+    // staged records: wave w of workgroup g copies blocks 8 g + w, 8 (g + G) + w,
+    // ...; the next block's metadata is fetched before the current block's
+    // records are copied
+    {
+        const uint64_t stride = (uint64_t)gridDim.x * kWaves;
+        uint64_t b = (uint64_t)blockIdx.x * kWaves + wave;
+        uint64_t meta = b < nb ? block_meta(tile_counts, block_offsets, nt, b) : 0;
+        while (b < nb) {                                           // wave-uniform
+            const uint64_t b_next = b + stride;
+            const uint64_t meta_next = b_next < nb ? block_meta(tile_counts, block_offsets, nt, b_next) : 0;
+            copy_block_records(meta, stage, out, off_esc, nt, b, item, slot);
+            meta = meta_next;
+            b = b_next;
+        }
+    }
     if (!rederive) return;
     RederiveLds &L = lds[wave];
     // flagged tiles: workgroup g takes the tiles g, g + G, g + 2G, ...: the
@@ -1733,12 +1759,13 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
                            block_offsets, out, h, cb_dev, status);
     }
     if (g.nt) {
-        // one wave per block for the staged records; for Top-16 at least
-        // kRederiveGroups workgroups (the formats other than Top-16 stage
-        // every tile: no tile is flagged)
+        // up to kCopyBlocksPerWave blocks per wave for the staged records;
+        // for Top-16 at least kRederiveGroups workgroups (the formats other
+        // than Top-16 stage every tile: no tile is flagged)
         LaunchScope scope("sz_enc_compact", s);
         const uint32_t rederive = version == kTop16 ? 1u : 0u;
-        uint64_t groups = (g.nb + kRederiveThreads / 64 - 1) / (kRederiveThreads / 64);
+        const uint64_t per_group = kCopyBlocksPerWave * (kRederiveThreads / 64);
+        uint64_t groups = (g.nb + per_group - 1) / per_group;
         if (rederive) groups = std::max<uint64_t>(groups, std::min<uint64_t>(kRederiveGroups, g.nt));
         if (dtype == SZ_BF16)
             hipLaunchKernelGGL(sz_enc_compact<SZ_BF16>, dim3((uint32_t)groups), dim3(kRederiveThreads), 0, s, stage,
