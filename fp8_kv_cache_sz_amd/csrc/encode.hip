@@ -762,19 +762,29 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
     const uint32_t nb = (uint32_t)h.nb;
     if (tid == 0) lds.carry = 0;
     uint32_t *block_counts = reinterpret_cast<uint32_t *>(out + 64);
-    for (uint32_t b0 = 0; b0 < nb; b0 += kScanBatch * kScanThreads) {
-        uint32_t x[kScanBatch];
+    // the tile counts of block b (four per block, the last block's past nt
+    // read as 0); the next batch's loads are issued before this batch's scan
+    auto load_batch = [&](uint32_t b0, uint4 (&v)[kScanBatch]) {
 #pragma unroll
         for (int i = 0; i < kScanBatch; ++i) {
             const uint32_t b = b0 + i * kScanThreads + tid;
-            x[i] = 0;
-            if (b < nb) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b);
-                const uint32_t t = kTilesPerBlock * b;
-                const uint32_t m = ~kRederiveFlag;
-                x[i] = (v.x & m) + ((t + 1 < nt) ? v.y & m : 0) + ((t + 2 < nt) ? v.z & m : 0) +
-                       ((t + 3 < nt) ? v.w & m : 0);
-            }
+            v[i] = b < nb ? *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    uint4 v_next[kScanBatch];
+    load_batch(0, v_next);
+    for (uint32_t b0 = 0; b0 < nb; b0 += kScanBatch * kScanThreads) {
+        uint4 v[kScanBatch];
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) v[i] = v_next[i];
+        if (b0 + kScanBatch * kScanThreads < nb) load_batch(b0 + kScanBatch * kScanThreads, v_next);
+        uint32_t x[kScanBatch];
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) {
+            const uint32_t t = kTilesPerBlock * (b0 + i * kScanThreads + tid);
+            const uint32_t m = ~kRederiveFlag;
+            x[i] = (v[i].x & m) + ((t + 1 < nt) ? v[i].y & m : 0) + ((t + 2 < nt) ? v[i].z & m : 0) +
+                   ((t + 3 < nt) ? v[i].w & m : 0);
         }
         uint64_t base[kScanBatch];
         scan_batch(x, base, lds);
