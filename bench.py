@@ -18,6 +18,10 @@ Prints one JSON line:
   roofline     the dominant kernel's algorithmic bytes / its average duration
                (HIP events recorded on the launch stream by the library's
                instrumentation) against the 8 TB/s HBM peak
+  copy, encoder_pattern   in-run streaming references: the library's plain
+               copy, and its copy of the dense encoder's memory pattern
+               (same grid, lanes and memory instructions, trivial
+               arithmetic) with the encoder's time relative to it
   cpu_baseline the CPU oracle (single thread) on a bounded sample
   parity       the whole GPU stream equals the oracle's stream of the whole
                tensor, byte for byte
@@ -395,6 +399,7 @@ def main():
     if not args.core_only and not args.no_extras:
         calibration, formats, transfer = extra_sections(sz, c, args.runs, dirs)
     copy = reference_copy_rate(sz, alg, args.runs, dev)
+    pattern = encoder_pattern_rate(sz, c.x, dtype, n, args.runs, per_kernel)
 
     headline_bits = headline_stream = None
     if oracle_leg:
@@ -405,13 +410,14 @@ def main():
     torch.cuda.empty_cache()
 
     # ---- every other workload: per-direction rows -------------------------
-    configs = {args.workload: dict(head_summary, **dirs, kernels=per_kernel)}
+    configs = {args.workload: dict(head_summary, **dirs, kernels=per_kernel, encoder_pattern=pattern)}
     config_samples = {}
     for name in config_names:
         print("config %s" % name, file=sys.stderr, flush=True)
         w = Codec(sz, name, dev)
         row = dict(w.summary(), **w.directions(args.runs))
         row["kernels"] = w.kernel_stats(args.runs)
+        row["encoder_pattern"] = encoder_pattern_rate(sz, w.x, w.dtype, w.n, args.runs, row["kernels"])
         configs[name] = row
         if oracle_leg:
             bits, stream = w.host_copies()
@@ -469,6 +475,7 @@ def main():
         "hbm": hbm_rates(per_kernel, args.workload),
         "copy": copy,
         "dominant_vs_copy": round(achieved / copy["GBps"], 4),
+        "encoder_pattern": pattern,
         "roofline": {
             "bound": "hbm",
             "kernel": dominant,
@@ -511,6 +518,31 @@ def reference_copy_rate(sz, alg, runs, dev):
     ms = total_ms / launches
     return {"GBps": round(2 * per_direction / (ms * 1e-3) / 1e9, 1), "bytes": per_direction,
             "kernel": "sz_ref_copy: one non-temporal dwordx4 per lane, 4 KB per 256-lane workgroup"}
+
+
+def encoder_pattern_rate(sz, x, dtype, n, runs, per_kernel):
+    """The library's reference of the dense encoder's memory pattern
+    (sz_reference_split: the encoder's grid, lanes and memory instructions,
+    trivial arithmetic) on the same tensor, timed per launch like the codec
+    kernels: the practical ceiling of the encoder's stream mix.  None when
+    the tensor is not whole 16K tiles."""
+    if n % 16384:
+        return None
+    out = sz.reference_split(x)
+    sz.profile_enable(True)
+    for _ in range(runs):
+        sz.reference_split(x)
+    launches, total_ms = sz.profile_collect()["sz_ref_split"]
+    sz.profile_enable(False)
+    del out
+    ms = total_ms / launches
+    moved = n * (2 if dtype == 0 else 1) + n // 2 + (n if dtype == 0 else 3 * n // 8)
+    dense = "sz_enc_dense_bf16" if dtype == 0 else "sz_enc_dense_e5m2"
+    row = {"kernel": "sz_ref_split", "bytes": moved, "avg_ms": round(ms, 5),
+           "GBps": round(moved / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    if dense in per_kernel:
+        row["dense_encoder_ms_vs_pattern"] = round(per_kernel[dense]["avg_ms"] / ms, 4)
+    return row
 
 
 def hbm_rates(per_kernel, workload):

@@ -28,7 +28,7 @@ TOP15S = SZ_FORMAT_TOP15_SENTINEL
 __all__ = ["BF16", "E5M2", "TOP16", "TOP8", "TOP15S", "Codebook", "SplitZipError", "calibrate", "calibrate_device",
            "codebook_from_device", "encoded_size", "workspace_size", "workspace", "decode_workspace_size",
            "decode_workspace", "encode", "decode",
-           "read_escape_count", "transfer", "transfer_buffers", "reference_copy", "profile_enable",
+           "read_escape_count", "transfer", "transfer_buffers", "reference_copy", "reference_split", "profile_enable",
            "profile_collect"]
 
 # An sz_codebook in device memory: u32 dtype, 16 exponent bytes (20 bytes,
@@ -305,6 +305,23 @@ def reference_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.T
                                    nbytes, _stream_handle(stream, src.device))
     _native.check("sz_reference_copy", rc)
     return dst
+
+
+def reference_split(x: torch.Tensor, stream=None):
+    """The library's reference of the dense encoders' memory pattern
+    (sz_reference_split) on a contiguous BF16 or E5M2-byte device tensor of
+    whole 16K-element tiles; not part of the codec, it times the practical
+    ceiling of the encoders' stream mix.  Returns (codes, sym) byte tensors."""
+    dtype = dtype_of(x)
+    if not x.is_contiguous():
+        raise ValueError("reference_split needs a contiguous tensor")
+    n = x.numel()
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=x.device)
+    sym = torch.empty(n if dtype == SZ_BF16 else 3 * n // 8, dtype=torch.uint8, device=x.device)
+    rc = _native.sz_reference_split(dtype, x.data_ptr() if n else None, n, codes.data_ptr() if n else None,
+                                    sym.data_ptr() if n else None, _stream_handle(stream, x.device))
+    _native.check("sz_reference_split", rc)
+    return codes, sym
 
 
 def profile_enable(on: bool = True) -> None:

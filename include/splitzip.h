@@ -303,6 +303,25 @@ int sz_profile_collect(sz_kernel_stat *stats, int max_stats);
  * of 16, overlapping ranges), SZ_E_ALIGN or SZ_E_HIP. */
 int sz_reference_copy(const void *d_src, void *d_dst, uint64_t bytes, void *stream);
 
+/* Reference of the dense encoders' memory pattern (not part of the codec).
+ * Reads n_elems elements of dtype (SZ_BF16: 2 bytes each, SZ_FP8_E5M2: 1
+ * byte) at d_in and writes n_elems / 2 bytes to d_codes and, per element,
+ * the sign/mantissa section's share to d_sym (BF16: n_elems bytes, E5M2:
+ * 3 n_elems / 8 bytes), with the grid, tile and lane mapping and the memory
+ * instructions of the dense encoder of that dtype (BF16: its shape for
+ * streams above 4096 tiles, eight 8-element chunks per lane) and trivial
+ * arithmetic:
+ *   BF16, per 8 elements: d_sym gets the 8 low bytes, d_codes 4 bytes, the
+ *     high bytes of elements 0..3 XOR those of elements 4..7;
+ *   E5M2, per 32 bytes a (bytes 0..15) and b (16..31): d_codes gets a XOR b,
+ *     d_sym bytes 0..11 of b.
+ * Its rate is the practical ceiling of the encoders' one-read, two-write
+ * stream mix.  n_elems must be a multiple of 16384 (whole encoder tiles);
+ * all pointers 16-byte aligned, caller-owned, not overlapping.  Enqueue
+ * only.  Returns SZ_OK (also for n_elems = 0), SZ_E_DTYPE, SZ_E_ARG (null
+ * pointer, n_elems not a multiple of 16384), SZ_E_ALIGN or SZ_E_HIP. */
+int sz_reference_split(int dtype, const void *d_in, uint64_t n_elems, void *d_codes, void *d_sym, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,3 +26,27 @@ def test_reference_copy_rejects_overlap():
     with pytest.raises(sz.SplitZipError) as e:
         sz.reference_copy(buf[:2048], buf[1024:3072])
     assert e.value.code == -1
+
+
+@pytest.mark.parametrize("dtype,tiles", [(0, 1), (0, 3), (1, 1), (1, 5)])
+def test_reference_split(dtype, tiles):
+    """sz_reference_split (the dense encoders' memory pattern, which bench.py
+    times as their ceiling) writes exactly the bytes its header states."""
+    import fp8_kv_cache_sz_amd as sz
+    n = tiles * 16384
+    print("reference_split", dtype, n, flush=True)
+    g = torch.Generator(device="cpu").manual_seed(100 * tiles + dtype)
+    raw = torch.randint(0, 256, (n * (2 if dtype == 0 else 1),), dtype=torch.uint8, generator=g)
+    x = (raw.view(torch.bfloat16) if dtype == 0 else raw).cuda()
+    codes, sym = sz.reference_split(x)
+    torch.cuda.synchronize()
+    if dtype == 0:
+        b = raw.view(-1, 8, 2)                       # chunk, element, byte (low first)
+        want_sym = b[:, :, 0].reshape(-1)
+        want_codes = (b[:, :4, 1] ^ b[:, 4:, 1]).reshape(-1)
+    else:
+        b = raw.view(-1, 32)
+        want_codes = (b[:, :16] ^ b[:, 16:]).reshape(-1)
+        want_sym = b[:, 16:28].reshape(-1)
+    assert torch.equal(codes.cpu(), want_codes)
+    assert torch.equal(sym.cpu(), want_sym)

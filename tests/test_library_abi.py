@@ -252,6 +252,22 @@ def test_host_argument_checks_reference_copy():
     assert nat.sz_reference_copy(a + 16, a, 32, None) == -1
 
 
+def test_host_argument_checks_reference_split():
+    """sz_reference_split checks dtype, size, pointers and alignment on the
+    host, before any launch."""
+    nat = _native()
+    a, b, c = 1 << 20, 1 << 30, 1 << 31
+    assert nat.sz_reference_split(0, None, 0, None, None, None) == 0    # nothing to do
+    assert nat.sz_reference_split(2, a, 16384, b, c, None) == -2
+    assert nat.sz_reference_split(0, a, 16384 + 8, b, c, None) == -1     # not whole tiles
+    assert nat.sz_reference_split(1, None, 16384, b, c, None) == -1
+    assert nat.sz_reference_split(1, a, 16384, None, c, None) == -1
+    assert nat.sz_reference_split(1, a, 16384, b, None, None) == -1
+    assert nat.sz_reference_split(0, a + 8, 16384, b, c, None) == -4
+    assert nat.sz_reference_split(0, a, 16384, b + 4, c, None) == -4
+    assert nat.sz_reference_split(0, a, 16384, b, c + 2, None) == -4
+
+
 def test_host_argument_checks_decode_noalloc():
     """sz_decode_noalloc rejects bad arguments, and requests beyond its fixed
     scratch, on the host before any launch."""
