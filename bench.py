@@ -18,10 +18,11 @@ Prints one JSON line:
   roofline     the dominant kernel's algorithmic bytes / its average duration
                (HIP events recorded on the launch stream by the library's
                instrumentation) against the 8 TB/s HBM peak
-  copy, encoder_pattern   in-run streaming references: the library's plain
-               copy, and its copy of the dense encoder's memory pattern
-               (same grid, lanes and memory instructions, trivial
-               arithmetic) with the encoder's time relative to it
+  copy, encoder_pattern, decoder_pattern   in-run streaming references:
+               the library's plain copy, and its copies of the dense
+               encoder's and the span decoder's memory patterns (same grid,
+               lanes and memory instructions, trivial arithmetic) with the
+               codec kernel's time relative to them
   cpu_baseline the CPU oracle (single thread) on a bounded sample
   parity       the whole GPU stream equals the oracle's stream of the whole
                tensor, byte for byte
@@ -400,6 +401,7 @@ def main():
         calibration, formats, transfer = extra_sections(sz, c, args.runs, dirs)
     copy = reference_copy_rate(sz, alg, args.runs, dev)
     pattern = encoder_pattern_rate(sz, c.x, dtype, n, args.runs, per_kernel)
+    dpattern = decoder_pattern_rate(sz, c, args.runs, per_kernel)
 
     headline_bits = headline_stream = None
     if oracle_leg:
@@ -410,7 +412,8 @@ def main():
     torch.cuda.empty_cache()
 
     # ---- every other workload: per-direction rows -------------------------
-    configs = {args.workload: dict(head_summary, **dirs, kernels=per_kernel, encoder_pattern=pattern)}
+    configs = {args.workload: dict(head_summary, **dirs, kernels=per_kernel, encoder_pattern=pattern,
+                                  decoder_pattern=dpattern)}
     config_samples = {}
     for name in config_names:
         print("config %s" % name, file=sys.stderr, flush=True)
@@ -418,6 +421,7 @@ def main():
         row = dict(w.summary(), **w.directions(args.runs))
         row["kernels"] = w.kernel_stats(args.runs)
         row["encoder_pattern"] = encoder_pattern_rate(sz, w.x, w.dtype, w.n, args.runs, row["kernels"])
+        row["decoder_pattern"] = decoder_pattern_rate(sz, w, args.runs, row["kernels"])
         configs[name] = row
         if oracle_leg:
             bits, stream = w.host_copies()
@@ -476,6 +480,7 @@ def main():
         "copy": copy,
         "dominant_vs_copy": round(achieved / copy["GBps"], 4),
         "encoder_pattern": pattern,
+        "decoder_pattern": dpattern,
         "roofline": {
             "bound": "hbm",
             "kernel": dominant,
@@ -542,6 +547,37 @@ def encoder_pattern_rate(sz, x, dtype, n, runs, per_kernel):
            "GBps": round(moved / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     if dense in per_kernel:
         row["dense_encoder_ms_vs_pattern"] = round(per_kernel[dense]["avg_ms"] / ms, 4)
+    return row
+
+
+def decoder_pattern_rate(sz, c, runs, per_kernel):
+    """The library's reference of the span decoders' memory pattern
+    (sz_reference_join: the wide-span grid, lanes and memory instructions,
+    trivial arithmetic) over the code and sign/mantissa sections of the
+    workload's own stream into its decode output, timed per launch: the
+    practical ceiling of the decoders' stream mix.  None when the tensor is
+    not whole 16K tiles or takes the narrow spans."""
+    n, dtype = c.n, c.dtype
+    if n % 16384 or (n + 65535) // 65536 <= 128:
+        return None
+    up256 = lambda v: (v + 255) // 256 * 256
+    off_nib = up256(64 + 4 * ((n + 65535) // 65536))
+    off_sm = off_nib + up256((n + 1) // 2)
+    sm_bytes = n if dtype == 0 else 3 * n // 8
+    codes, sym = c.buf[off_nib:off_nib + n // 2], c.buf[off_sm:off_sm + sm_bytes]
+    sz.reference_join(codes, sym, dtype, n, out=c.y)
+    sz.profile_enable(True)
+    for _ in range(runs):
+        sz.reference_join(codes, sym, dtype, n, out=c.y)
+    launches, total_ms = sz.profile_collect()["sz_ref_join"]
+    sz.profile_enable(False)
+    ms = total_ms / launches
+    moved = n // 2 + sm_bytes + n * (2 if dtype == 0 else 1)
+    dense = "sz_dec_bf16_span" if dtype == 0 else "sz_dec_e5m2_span"
+    row = {"kernel": "sz_ref_join", "bytes": moved, "avg_ms": round(ms, 5),
+           "GBps": round(moved / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    if dense in per_kernel:
+        row["decoder_ms_vs_pattern"] = round(per_kernel[dense]["avg_ms"] / ms, 4)
     return row
 
 

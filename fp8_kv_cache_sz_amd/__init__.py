@@ -28,7 +28,8 @@ TOP15S = SZ_FORMAT_TOP15_SENTINEL
 __all__ = ["BF16", "E5M2", "TOP16", "TOP8", "TOP15S", "Codebook", "SplitZipError", "calibrate", "calibrate_device",
            "codebook_from_device", "encoded_size", "workspace_size", "workspace", "decode_workspace_size",
            "decode_workspace", "encode", "decode",
-           "read_escape_count", "transfer", "transfer_buffers", "reference_copy", "reference_split", "profile_enable",
+           "read_escape_count", "transfer", "transfer_buffers", "reference_copy", "reference_split",
+           "reference_join", "profile_enable",
            "profile_collect"]
 
 # An sz_codebook in device memory: u32 dtype, 16 exponent bytes (20 bytes,
@@ -322,6 +323,20 @@ def reference_split(x: torch.Tensor, stream=None):
                                     sym.data_ptr() if n else None, _stream_handle(stream, x.device))
     _native.check("sz_reference_split", rc)
     return codes, sym
+
+
+def reference_join(codes: torch.Tensor, sym: torch.Tensor, dtype: int, n: int, out: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """The library's reference of the span decoders' memory pattern
+    (sz_reference_join): reads the code and sign/mantissa byte tensors of n
+    elements (whole 16K tiles) and writes n elements; not part of the codec,
+    it times the practical ceiling of the decoders' stream mix."""
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16 if dtype == BF16 else torch.uint8, device=codes.device)
+    rc = _native.sz_reference_join(dtype, codes.data_ptr() if n else None, sym.data_ptr() if n else None, n,
+                                   out.data_ptr() if n else None, _stream_handle(stream, codes.device))
+    _native.check("sz_reference_join", rc)
+    return out
 
 
 def profile_enable(on: bool = True) -> None:

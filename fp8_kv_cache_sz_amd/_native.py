@@ -91,13 +91,15 @@ lib.sz_reference_copy.argtypes = [_vp, _vp, _u64, _vp]
 lib.sz_reference_copy.restype = _i32
 lib.sz_reference_split.argtypes = [_i32, _vp, _u64, _vp, _vp, _vp]
 lib.sz_reference_split.restype = _i32
+lib.sz_reference_join.argtypes = [_i32, _vp, _vp, _u64, _vp, _vp]
+lib.sz_reference_join.restype = _i32
 
 EXPORTS = ("sz_calibrate", "sz_encoded_size", "sz_workspace_size", "sz_workspace_size_format",
            "sz_decode_workspace_size", "sz_encode", "sz_encode_devcb",
            "sz_calibrate_workspace_size", "sz_calibrate_device", "sz_decode", "sz_encoded_size_format",
            "sz_encode_format", "sz_decode_format", "sz_transfer_workspace_size", "sz_transfer_host_bytes",
            "sz_transfer", "sz_profile_enable", "sz_profile_collect", "sz_reference_copy",
-           "sz_reference_split", "sz_decode_noalloc_max_elems", "sz_decode_noalloc")
+           "sz_reference_split", "sz_reference_join", "sz_decode_noalloc_max_elems", "sz_decode_noalloc")
 
 SZ_FORMAT_TOP16 = 1
 SZ_FORMAT_TOP8 = 2
@@ -202,6 +204,10 @@ def sz_reference_copy(d_src, d_dst, nbytes, stream) -> int:
 
 def sz_reference_split(dtype, d_in, n, d_codes, d_sym, stream) -> int:
     return int(lib.sz_reference_split(dtype, d_in, n, d_codes, d_sym, stream))
+
+
+def sz_reference_join(dtype, d_codes, d_sym, n, d_out, stream) -> int:
+    return int(lib.sz_reference_join(dtype, d_codes, d_sym, n, d_out, stream))
 
 
 def sz_profile_enable(on: bool) -> int:

@@ -889,6 +889,63 @@ void launch_span(const uint8_t *in, const DecodeArgs &a, const DecodeScratch &w,
                            w.verdict, static_cast<uint8_t *>(d_out));
 }
 
+// ---------------------------------------------------------------------------
+// Kernel: reference of the span decoders' memory pattern on large streams
+// (not part of the codec).  The wide-span grid, lane mapping and memory
+// instructions of sz_dec_bf16_span / sz_dec_e5m2_span on whole spans, with
+// trivial arithmetic in place of the decoding and no records:
+//   BF16 (256 lanes, four 8-element chunks each, 8192-element spans): per
+//     chunk a code dword and a sign/mantissa dwordx2 in, 16 bytes out =
+//     sym (8 bytes), codes (4), codes XOR sym bytes 0..3 (4);
+//   E5M2 (256 lanes, two 32-element chunks each, 16384-element spans, the
+//     decoder's chunk-pair stores): per chunk 16 code bytes and 12
+//     sign/mantissa bytes in, 32 bytes out = codes, sym, codes XOR sym
+//     bytes 0..3.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void sz_ref_join(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ sym,
+                                                   uint8_t *__restrict__ out)
+{
+    const uint32_t tid = threadIdx.x;
+    if (DT == SZ_BF16) {
+        constexpr uint32_t T = kBf16WideThreads, CPL = kBf16WideChunks;
+        static_assert(T == 256, "launched with 256 lanes");
+        const uint64_t span0 = (uint64_t)blockIdx.x * (T * 8 * CPL);
+        uint32_t code[CPL];
+        uint2 sm[CPL];
+#pragma unroll
+        for (uint32_t j = 0; j < CPL; ++j) {
+            const uint64_t g = span0 + (j * T + tid) * 8;
+            code[j] = load_nt(reinterpret_cast<const uint32_t *>(codes + g / 2));
+            sm[j] = load_nt(reinterpret_cast<const uint2 *>(sym + g));
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < CPL; ++j) {
+            const uint64_t g = span0 + (j * T + tid) * 8;
+            store_nt(reinterpret_cast<uint4 *>(out + 2 * g), make_uint4(sm[j].x, sm[j].y, code[j], code[j] ^ sm[j].x));
+        }
+    } else {
+        constexpr uint32_t T = kE5SpanThreads, CPL = kE5WideChunks, kWaves = T / 64;
+        static_assert(T == 256, "launched with 256 lanes");
+        const uint32_t lane = lane_id();
+        const uint64_t span0 = (uint64_t)blockIdx.x * (T * 32 * CPL);
+        uint4 nib[CPL];
+        uint32_t sm3[CPL][3];
+#pragma unroll
+        for (uint32_t j = 0; j < CPL; ++j) {
+            const uint64_t g = span0 + (j * kWaves + tid / 64) * 2048 + e5m2_chunk_of_lane(lane) * 32;
+            nib[j] = load_nt(reinterpret_cast<const uint4 *>(codes + g / 2));
+            load3_nt(reinterpret_cast<const uint32_t *>(sym + (g / 32) * 12), sm3[j]);
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < CPL; ++j) {
+            const uint32_t o[8] = {nib[j].x, nib[j].y, nib[j].z, nib[j].w,
+                                   sm3[j][0], sm3[j][1], sm3[j][2], nib[j].x ^ sm3[j][0]};
+            store_chunk_pairs(out + span0 + (j * kWaves + tid / 64) * 2048, o, lane);
+        }
+    }
+}
+
 // BF16 span shape by stream size: 4096-element spans up to kSpanWideBlocks
 // blocks, 16384-element spans (eight chunks per lane) from 256 to 384 blocks
 // (16M-24M elements: half the workgroups of the 8192-element grid, which
@@ -1056,3 +1113,27 @@ extern "C" int sz_decode_format(int format, const void *d_in, uint64_t in_bytes,
     return decode_impl((uint32_t)format, d_in, in_bytes, dtype, d_out, n_elems, d_ws, ws_bytes, stream);
 }
 
+extern "C" int sz_reference_join(int dtype, const void *d_codes, const void *d_sym, uint64_t n_elems, void *d_out,
+                                 void *stream)
+{
+    if (dtype != SZ_BF16 && dtype != SZ_FP8_E5M2) return SZ_E_DTYPE;
+    if (n_elems % kEncTile != 0) return SZ_E_ARG;
+    if (n_elems == 0) return SZ_OK;
+    if (!d_codes || !d_sym || !d_out) return SZ_E_ARG;
+    if (!aligned16(d_codes) || !aligned16(d_sym) || !aligned16(d_out)) return SZ_E_ALIGN;
+    const uint64_t span = dtype == SZ_BF16 ? (uint64_t)kBf16WideThreads * 8 * kBf16WideChunks
+                                           : (uint64_t)kE5SpanThreads * 32 * kE5WideChunks;
+    const uint64_t groups = n_elems / span;
+    if (groups > 0xFFFFFFFFull) return SZ_E_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    LaunchScope scope("sz_ref_join", s);
+    if (dtype == SZ_BF16)
+        hipLaunchKernelGGL(sz_ref_join<SZ_BF16>, dim3((uint32_t)groups), dim3(256), 0, s,
+                           static_cast<const uint8_t *>(d_codes), static_cast<const uint8_t *>(d_sym),
+                           static_cast<uint8_t *>(d_out));
+    else
+        hipLaunchKernelGGL(sz_ref_join<SZ_FP8_E5M2>, dim3((uint32_t)groups), dim3(256), 0, s,
+                           static_cast<const uint8_t *>(d_codes), static_cast<const uint8_t *>(d_sym),
+                           static_cast<uint8_t *>(d_out));
+    return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
+}

@@ -322,6 +322,23 @@ int sz_reference_copy(const void *d_src, void *d_dst, uint64_t bytes, void *stre
  * pointer, n_elems not a multiple of 16384), SZ_E_ALIGN or SZ_E_HIP. */
 int sz_reference_split(int dtype, const void *d_in, uint64_t n_elems, void *d_codes, void *d_sym, void *stream);
 
+/* Reference of the span decoders' memory pattern on large streams (not part
+ * of the codec): the inverse stream mix of sz_reference_split.  Reads
+ * n_elems / 2 code bytes at d_codes and the sign/mantissa share at d_sym
+ * (BF16: n_elems bytes, E5M2: 3 n_elems / 8) and writes n_elems elements
+ * (BF16: 2 n_elems bytes, E5M2: n_elems) to d_out, with the wide-span grid,
+ * lane mapping and memory instructions of the decoder of that dtype and
+ * trivial arithmetic:
+ *   BF16, per 8 elements: 16 bytes = the 8 sym bytes, the 4 code bytes,
+ *     then those code bytes XOR sym bytes 0..3;
+ *   E5M2, per 32 elements: 32 bytes = the 16 code bytes, the 12 sym bytes,
+ *     then code bytes 0..3 XOR sym bytes 0..3.
+ * n_elems must be a multiple of 16384; all pointers 16-byte aligned,
+ * caller-owned, not overlapping.  Enqueue only.  Returns SZ_OK (also for
+ * n_elems = 0), SZ_E_DTYPE, SZ_E_ARG (null pointer, n_elems not a multiple
+ * of 16384), SZ_E_ALIGN or SZ_E_HIP. */
+int sz_reference_join(int dtype, const void *d_codes, const void *d_sym, uint64_t n_elems, void *d_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,3 +50,25 @@ def test_reference_split(dtype, tiles):
         want_sym = b[:, 16:28].reshape(-1)
     assert torch.equal(codes.cpu(), want_codes)
     assert torch.equal(sym.cpu(), want_sym)
+
+
+@pytest.mark.parametrize("dtype,tiles", [(0, 1), (0, 3), (1, 1), (1, 5)])
+def test_reference_join(dtype, tiles):
+    """sz_reference_join (the span decoders' memory pattern, which bench.py
+    times as their ceiling) writes exactly the bytes its header states."""
+    import fp8_kv_cache_sz_amd as sz
+    n = tiles * 16384
+    print("reference_join", dtype, n, flush=True)
+    g = torch.Generator(device="cpu").manual_seed(200 * tiles + dtype)
+    codes = torch.randint(0, 256, (n // 2,), dtype=torch.uint8, generator=g)
+    sym = torch.randint(0, 256, (n if dtype == 0 else 3 * n // 8,), dtype=torch.uint8, generator=g)
+    out = sz.reference_join(codes.cuda(), sym.cuda(), dtype, n)
+    torch.cuda.synchronize()
+    got = out.view(torch.uint8).cpu()
+    if dtype == 0:
+        c, s = codes.view(-1, 4), sym.view(-1, 8)
+        want = torch.cat([s, c, c ^ s[:, :4]], dim=1).reshape(-1)
+    else:
+        c, s = codes.view(-1, 16), sym.view(-1, 12)
+        want = torch.cat([c, s, c[:, :4] ^ s[:, :4]], dim=1).reshape(-1)
+    assert torch.equal(got, want)

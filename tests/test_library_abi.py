@@ -268,6 +268,22 @@ def test_host_argument_checks_reference_split():
     assert nat.sz_reference_split(0, a, 16384, b, c + 2, None) == -4
 
 
+def test_host_argument_checks_reference_join():
+    """sz_reference_join checks dtype, size, pointers and alignment on the
+    host, before any launch."""
+    nat = _native()
+    a, b, c = 1 << 20, 1 << 30, 1 << 31
+    assert nat.sz_reference_join(0, None, None, 0, None, None) == 0     # nothing to do
+    assert nat.sz_reference_join(2, a, b, 16384, c, None) == -2
+    assert nat.sz_reference_join(1, a, b, 16384 + 32, c, None) == -1     # not whole tiles
+    assert nat.sz_reference_join(0, None, b, 16384, c, None) == -1
+    assert nat.sz_reference_join(0, a, None, 16384, c, None) == -1
+    assert nat.sz_reference_join(0, a, b, 16384, None, None) == -1
+    assert nat.sz_reference_join(1, a + 8, b, 16384, c, None) == -4
+    assert nat.sz_reference_join(1, a, b + 4, 16384, c, None) == -4
+    assert nat.sz_reference_join(1, a, b, 16384, c + 2, None) == -4
+
+
 def test_host_argument_checks_decode_noalloc():
     """sz_decode_noalloc rejects bad arguments, and requests beyond its fixed
     scratch, on the host before any launch."""
