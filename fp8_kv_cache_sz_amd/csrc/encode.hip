@@ -1290,8 +1290,11 @@ __device__ __forceinline__ void copy_block_records(uint64_t meta, const uint8_t 
 constexpr uint32_t kRederiveThreads = 512;
 constexpr uint32_t kRederiveGroups = 768;         // 3 workgroups of 8 waves (80 registers) on each compute unit
 // Blocks whose staged records one wave copies (at most): fewer waves, each
-// overlapping the next block's metadata fetch with the current copy.
-constexpr uint64_t kCopyBlocksPerWave = 4;
+// overlapping the next block's metadata fetch with the current copy.  With
+// eight, every large Top-16 stream gets the kRederiveGroups workgroups, one
+// resident round; with four, the long-context payload (28,672 blocks) had
+// 896 workgroups, a second round, and its compaction took 23 us against 18.
+constexpr uint64_t kCopyBlocksPerWave = 8;
 constexpr int kRdRowChunks = kEncTile / (kRederiveThreads / 64) / 512;   // 4 chunks per lane
 
 // The first record of tile t: its block's offset plus the block's tiles before it.
