@@ -200,6 +200,45 @@ def test_escape_heavy_compaction_paths(dtype, n):
     assert counts[1] == 0 and max(counts) > 16384
 
 
+# Escapes per 16K tile around the encoders' staging limits: a row's direct
+# records (up to 32 per chunk row) against its LDS segments, the E5M2 tile
+# buffer (2,058 records), and the re-derivation above 4,096 records.
+TILE_ESCAPES = [0, 1, 31, 32, 33, 200, 500, 2057, 2058, 2059, 3000, 4095, 4096, 4097, 9000, 16384]
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("clustered", [False, True])
+def test_tile_escape_counts_around_staging_limits(dtype, clustered):
+    """A stream past 2,048 tiles (where the limits apply) whose tiles carry
+    the escape counts of TILE_ESCAPES in turn, spread over the tile or in one
+    run at a random place; the other tiles have none."""
+    rng = np.random.default_rng(31 + dtype + 2 * clustered)
+    tiles = 2049 + len(TILE_ESCAPES)
+    n = tiles * 16384 - 77
+    if dtype == 0:
+        bits = np.full(n, 0x3F80, dtype=np.uint16)            # exponent 127
+        esc_val = lambda m: (0x0080 | (rng.integers(0, 2, m) << 15) | rng.integers(0, 128, m)).astype(np.uint16)
+        cb = np.array([127] + list(range(100, 115)), dtype=np.uint8)
+    else:
+        bits = np.full(n, 0x3C, dtype=np.uint8)               # exponent 15
+        esc_val = lambda m: (0x04 | (rng.integers(0, 2, m) << 7) | rng.integers(0, 4, m)).astype(np.uint8)
+        cb = np.array([15] + list(range(16, 31)), dtype=np.uint8)
+    want = np.zeros(tiles, dtype=np.int64)
+    for i, k in enumerate(TILE_ESCAPES):
+        t = 5 + 97 * i                                        # tiles spread over the stream
+        lo, hi = t * 16384, min((t + 1) * 16384, n)
+        k = min(k, hi - lo)
+        if clustered:
+            start = lo + int(rng.integers(0, hi - lo - k + 1))
+            idx = np.arange(start, start + k)
+        else:
+            idx = lo + rng.choice(hi - lo, size=k, replace=False)
+        bits[idx] = esc_val(k)
+        want[t] = k
+    expect = roundtrip_check(bits, dtype, cb)
+    assert streamfmt.header(expect)["escapes"] == int(want.sum())
+
+
 def test_single_escapes_at_block_edges():
     n = 3 * 65536
     bits = np.full(n, 0x3F80, dtype=np.uint16)
