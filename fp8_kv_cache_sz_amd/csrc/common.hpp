@@ -50,6 +50,7 @@ constexpr uint32_t kEncTile = kRow * (kEncThreads / 64);  // 16384
 constexpr uint32_t kTilesPerBlock = kBlock / kEncTile;    // 4
 constexpr uint32_t kDecThreads = 1024;                    // 16 waves = one 64K block
 constexpr uint32_t kScanThreads = 1024;
+constexpr int kScanBatch = 8;                             // passes of kScanThreads items per scan batch
 
 constexpr uint64_t up256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 
@@ -91,11 +92,16 @@ inline uint64_t stage_slot_bytes(uint32_t version, uint64_t nt)
     return 3ull * kRederiveRecords;
 }
 
+// Blocks whose escape offsets one scan workgroup computes (kScanBatch passes
+// of kScanThreads blocks); larger streams take one workgroup per this many
+// blocks, after a reduction of their escape totals.
+constexpr uint64_t kScanSuper = (uint64_t)kScanBatch * kScanThreads;
+
 // Encode workspace layout (byte offsets): the status word (first 256 bytes),
-// tile counts, block offsets and the escape staging (stage_slot_bytes per
-// tile).
+// tile counts, block offsets, the scan workgroups' escape totals and the
+// escape staging (stage_slot_bytes per tile).
 struct WsLayout {
-    uint64_t counts, offsets, stage, slot, total;
+    uint64_t counts, offsets, totals, stage, slot, total;
 };
 
 inline WsLayout ws_layout(uint32_t version, int dtype, uint64_t n)
@@ -104,7 +110,8 @@ inline WsLayout ws_layout(uint32_t version, int dtype, uint64_t n)
     WsLayout w;
     w.counts = 256;
     w.offsets = w.counts + up256(4 * g.nt + 16);
-    w.stage = w.offsets + up256(8 * g.nb + 16);
+    w.totals = w.offsets + up256(8 * g.nb + 16);
+    w.stage = w.totals + up256(8 * ((g.nb + kScanSuper - 1) / kScanSuper));
     w.slot = stage_slot_bytes(version, g.nt);
     // 16 bytes past the last slot: the record copies read whole words
     w.total = w.stage + up256(w.slot * g.nt + 16);
@@ -301,7 +308,6 @@ __host__ __device__ constexpr uint32_t escape_item_bytes(uint32_t v) { return v 
 // thread per pass turns them into exclusive offsets.  A running 64-bit carry
 // joins successive batches.
 // ---------------------------------------------------------------------------
-constexpr int kScanBatch = 8;
 constexpr uint32_t kScanWaves = kScanThreads / 64;
 
 struct ScanLds {

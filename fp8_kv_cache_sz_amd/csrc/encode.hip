@@ -741,26 +741,88 @@ __device__ __forceinline__ void write_header(uint8_t *__restrict__ out, const He
     }
 }
 
+// The escape count of block b: its four tile counts, without the re-derive
+// flags and without tiles past nt.
+__device__ __forceinline__ uint32_t block_escapes(uint4 v, uint32_t b, uint32_t nt)
+{
+    const uint32_t t = kTilesPerBlock * b;
+    const uint32_t m = ~kRederiveFlag;
+    return (v.x & m) + ((t + 1 < nt) ? v.y & m : 0) + ((t + 2 < nt) ? v.z & m : 0) + ((t + 3 < nt) ? v.w & m : 0);
+}
+
+// Sum of a 64-bit value over the workgroup (kScanThreads lanes); every
+// thread gets it.
+__device__ __forceinline__ uint64_t workgroup_sum_u64(uint64_t v, uint64_t *lds)
+{
+    const uint32_t lane = lane_id(), wave = threadIdx.x / 64;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, d), hi = __shfl_xor((uint32_t)(v >> 32), d);
+        v += ((uint64_t)hi << 32) | lo;
+    }
+    if (lane == 0) lds[wave] = v;
+    __syncthreads();
+    uint64_t sum = 0;
+    for (uint32_t w = 0; w < kScanWaves; ++w) sum += lds[w];
+    __syncthreads();
+    return sum;
+}
+
 // ---------------------------------------------------------------------------
-// Kernel: encode scan.  One workgroup turns the tile escape counts into the
-// per-block escape counts of the stream and the exclusive escape offset of
-// every block, then writes the header (with E) and the zero padding between
-// sections.
+// Kernel: escape totals of the scan's workgroups, for streams of more than
+// kScanSuper blocks.  Workgroup g sums the tile counts of blocks
+// [g kScanSuper, (g + 1) kScanSuper) into totals[g].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kScanThreads) void sz_enc_scan_reduce(const uint32_t *__restrict__ tile_counts,
+                                                                   uint32_t nt, uint32_t nb,
+                                                                   uint64_t *__restrict__ totals)
+{
+    __shared__ uint64_t lds[kScanWaves];
+    const uint32_t b0 = blockIdx.x * (uint32_t)kScanSuper;
+    uint4 v[kScanBatch];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) {
+        const uint32_t b = b0 + i * kScanThreads + threadIdx.x;
+        v[i] = b < nb ? *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b) : make_uint4(0, 0, 0, 0);
+    }
+    uint64_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) sum += block_escapes(v[i], b0 + i * kScanThreads + threadIdx.x, nt);
+    sum = workgroup_sum_u64(sum, lds);
+    if (threadIdx.x == 0) totals[blockIdx.x] = sum;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel: encode scan.  Workgroup g turns the tile escape counts of blocks
+// [g kScanSuper, (g + 1) kScanSuper) into the per-block escape counts of the
+// stream and the exclusive escape offset of every block, starting from the
+// escapes of the blocks before it (the sum of totals[0 .. g), from
+// sz_enc_scan_reduce; one workgroup when the stream has at most kScanSuper
+// blocks).  Workgroup 0 writes the header and the zero padding between
+// sections, the last workgroup E.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__restrict__ tile_counts,
                                                             uint32_t nt,
                                                             uint64_t *__restrict__ block_offsets,
                                                             uint8_t *__restrict__ out, HeaderArgs h,
                                                             const uint32_t *__restrict__ cb_dev,
-                                                            int32_t *__restrict__ status)
+                                                            int32_t *__restrict__ status,
+                                                            const uint64_t *__restrict__ totals)
 {
     __shared__ ScanLds lds;
+    __shared__ uint64_t sum_lds[kScanWaves];
     const uint32_t tid = threadIdx.x;
     // a bad device codebook zeroes the magic and sets the status word
     Codebook4 cb = h.cb;
     const int32_t verdict = device_codebook_verdict(cb_dev, h.dtype, cb);
     const uint32_t nb = (uint32_t)h.nb;
-    if (tid == 0) lds.carry = 0;
+    // this workgroup's blocks, and the escapes of the blocks before them
+    const uint32_t first = blockIdx.x * (uint32_t)kScanSuper;
+    const uint32_t last = (uint32_t)std::min<uint64_t>(nb, (uint64_t)first + kScanSuper);
+    uint64_t before = 0;
+    for (uint32_t w = tid; w < blockIdx.x; w += kScanThreads) before += totals[w];
+    if (gridDim.x > 1) before = workgroup_sum_u64(before, sum_lds);
+    if (tid == 0) lds.carry = before;
     uint32_t *block_counts = reinterpret_cast<uint32_t *>(out + 64);
     // the tile counts of block b (four per block, the last block's past nt
     // read as 0); the next batch's loads are issued before this batch's scan
@@ -768,38 +830,33 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
 #pragma unroll
         for (int i = 0; i < kScanBatch; ++i) {
             const uint32_t b = b0 + i * kScanThreads + tid;
-            v[i] = b < nb ? *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b) : make_uint4(0, 0, 0, 0);
+            v[i] = b < last ? *reinterpret_cast<const uint4 *>(tile_counts + kTilesPerBlock * b) : make_uint4(0, 0, 0, 0);
         }
     };
     uint4 v_next[kScanBatch];
-    load_batch(0, v_next);
-    for (uint32_t b0 = 0; b0 < nb; b0 += kScanBatch * kScanThreads) {
+    load_batch(first, v_next);
+    for (uint32_t b0 = first; b0 < last; b0 += kScanBatch * kScanThreads) {
         uint4 v[kScanBatch];
 #pragma unroll
         for (int i = 0; i < kScanBatch; ++i) v[i] = v_next[i];
-        if (b0 + kScanBatch * kScanThreads < nb) load_batch(b0 + kScanBatch * kScanThreads, v_next);
+        if (b0 + kScanBatch * kScanThreads < last) load_batch(b0 + kScanBatch * kScanThreads, v_next);
         uint32_t x[kScanBatch];
 #pragma unroll
-        for (int i = 0; i < kScanBatch; ++i) {
-            const uint32_t t = kTilesPerBlock * (b0 + i * kScanThreads + tid);
-            const uint32_t m = ~kRederiveFlag;
-            x[i] = (v[i].x & m) + ((t + 1 < nt) ? v[i].y & m : 0) + ((t + 2 < nt) ? v[i].z & m : 0) +
-                   ((t + 3 < nt) ? v[i].w & m : 0);
-        }
+        for (int i = 0; i < kScanBatch; ++i) x[i] = block_escapes(v[i], b0 + i * kScanThreads + tid, nt);
         uint64_t base[kScanBatch];
         scan_batch(x, base, lds);
 #pragma unroll
         for (int i = 0; i < kScanBatch; ++i) {
             const uint32_t b = b0 + i * kScanThreads + tid;
-            if (b < nb) {
+            if (b < last) {
                 block_counts[b] = x[i];
                 block_offsets[b] = base[i];
             }
         }
     }
     const uint64_t total = lds.carry;
-    write_header(out, h, cb, verdict, false, status);
-    if (tid == 0) {
+    if (blockIdx.x == 0) write_header(out, h, cb, verdict, false, status);
+    if (tid == 0 && blockIdx.x == gridDim.x - 1) {
         reinterpret_cast<uint32_t *>(out)[4] = (uint32_t)total;
         reinterpret_cast<uint32_t *>(out)[5] = (uint32_t)(total >> 32);
     }
@@ -1695,6 +1752,7 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
     int32_t *status = reinterpret_cast<int32_t *>(ws);
     uint32_t *tile_counts = reinterpret_cast<uint32_t *>(ws + w.counts);
     uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
+    uint64_t *scan_totals = reinterpret_cast<uint64_t *>(ws + w.totals);
     uint8_t *stage = ws + w.stage;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -1767,9 +1825,17 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
                                    tile_counts, out, g.off_esc, g.nt, d_in, h, cb_dev, status, 3u, (uint32_t)w.slot);
             return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
         }
+        // one scan workgroup per kScanSuper blocks, after the reduction of
+        // their escape totals when there are several
+        const uint32_t scan_groups = (uint32_t)((g.nb + kScanSuper - 1) / kScanSuper);
+        if (scan_groups > 1) {
+            LaunchScope scope("sz_enc_scan_reduce", s);
+            hipLaunchKernelGGL(sz_enc_scan_reduce, dim3(scan_groups), dim3(kScanThreads), 0, s, tile_counts,
+                               (uint32_t)g.nt, (uint32_t)g.nb, scan_totals);
+        }
         LaunchScope scope("sz_enc_scan", s);
-        hipLaunchKernelGGL(sz_enc_scan, dim3(1), dim3(kScanThreads), 0, s, tile_counts, (uint32_t)g.nt,
-                           block_offsets, out, h, cb_dev, status);
+        hipLaunchKernelGGL(sz_enc_scan, dim3(scan_groups), dim3(kScanThreads), 0, s, tile_counts, (uint32_t)g.nt,
+                           block_offsets, out, h, cb_dev, status, scan_totals);
     }
     if (g.nt) {
         // up to kCopyBlocksPerWave blocks per wave for the staged records;

@@ -82,11 +82,12 @@ def test_encoded_size_matches_oracle():
             ws = nat.sz_workspace_size(dtype, n)
             nt, nb = (n + 16383) // 16384, (n + 65535) // 65536
             assert ws % 256 == 0
-            # status, tile counts, block offsets, then one staging slot per
-            # 16K tile: 3 bytes per element up to 2,048 tiles, 12 KB per tile
+            # status, tile counts, block offsets, the scan workgroups' escape
+            # totals (one u64 per 8,192 blocks), then one staging slot per 16K
+            # tile: 3 bytes per element up to 2,048 tiles, 12 KB per tile
             # (4,096 records) above
             slot = 3 * 16384 if nt <= 2048 else 3 * 4096
-            fixed = 256 + up(4 * nt + 16) + up(8 * nb + 16)
+            fixed = 256 + up(4 * nt + 16) + up(8 * nb + 16) + up(8 * ((nb + 8191) // 8192))
             assert ws == fixed + up(slot * nt + 16), (dtype, n)
             dws = nat.sz_decode_workspace_size(dtype, n)
             assert dws == 256 + up(8 * nb + 16) and dws <= ws
