@@ -1030,16 +1030,22 @@ __device__ __forceinline__ void rederive_tile_e5m2(const uint8_t *__restrict__ i
 //     its records in registers: a 256-entry table gives, for the chunk's
 //     escape mask, the element index of each record slot, and v_perm picks
 //     the position and exponent bytes by those indices;
-//   * the lane ORs the string, shifted to its byte offset, into the wave's
-//     LDS segment as whole dwords (the segment is zeroed first; two lanes can
+//   * the lane ORs the string, shifted to its byte offset (one v_perm per
+//     dword), into the wave's LDS segment as whole dwords (the segment's
+//     words are zero: the writer clears what it has read; two lanes can
 //     share a dword at their edge, and OR keeps both);
-//   * the wave stores the segment's whole 16-byte words with dwordx4 stores
-//     and carries the last, partial one over to the next two rows, so only
-//     the first and last words of the wave's records take byte stores.
+//   * the wave stores the segment's whole kLineBytes lines with dwordx4 stores
+//     (whole, aligned lines of the stream: no line is written in parts by
+//     two stores) and carries the last, partial line over to the next two
+//     rows, so only the first and last words of the wave's records take
+//     byte stores.
 // ---------------------------------------------------------------------------
-// records of two chunk rows, the 16-byte lead and the overhang of the last
-// lane's dword writes, in 16-byte words
-constexpr uint32_t kRdSegWords = (3 * 2 * 512 + 64) / 16;
+// The stream lines that the record writer stores whole (bytes, 16-byte words).
+constexpr uint32_t kLineBytes = 128;
+constexpr uint32_t kLineWords = kLineBytes / 16;
+// records of two chunk rows, the lead (up to a line) and the overhang of the
+// last lane's dword writes, in 16-byte words
+constexpr uint32_t kRdSegWords = (3 * 2 * 512 + kLineBytes + 64) / 16;
 
 struct RederiveLds {
     uint32_t table32[64];      // exponent -> code byte, bit 7 = escape
@@ -1048,8 +1054,8 @@ struct RederiveLds {
     uint4 seg[kRdSegWords];
 };
 
-// The encode table and the slot table of one wave (its lanes only, no
-// workgroup barrier).
+// The encode table and the slot table of one wave, and its zeroed record
+// segment (its lanes only, no workgroup barrier).
 __device__ __forceinline__ void build_wave_tables(RederiveLds &L, const Codebook4 &cb, uint32_t symbols)
 {
     const uint32_t lane = lane_id();
@@ -1078,6 +1084,8 @@ __device__ __forceinline__ void build_wave_tables(RederiveLds &L, const Codebook
         }
         L.slots[m] = e;
     }
+    // the record segment starts zeroed (the BF16 record writer keeps it so)
+    for (uint32_t i = lane; i < kRdSegWords; i += 64) L.seg[i] = make_uint4(0, 0, 0, 0);
     wave_lds_fence();
 }
 
@@ -1119,80 +1127,140 @@ __device__ __forceinline__ void or_records8(uint32_t *seg32, uint32_t S, uint32_
     d[0] = 0;
     d[7] = 0;
     const uint32_t dw = S >> 2;
-    const uint32_t rs = 32 - 8 * (S & 3u);                        // 8 .. 32
+    // LDS word dw + i takes bytes 4 - (S & 3) .. 7 - (S & 3) of {d[i + 1], d[i]}
+    const uint32_t sel = 0x03020100u + (4u - (S & 3u)) * 0x01010101u;
     // the string's bytes past its records are zero, so all seven words are
     // ORed: the ones past the records change nothing
 #pragma unroll
-    for (uint32_t i = 0; i < 7; ++i) {
-        const uint32_t w = (uint32_t)((((uint64_t)d[i + 1] << 32) | d[i]) >> rs);
-        __hip_atomic_fetch_or(seg32 + dw + i, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    for (uint32_t i = 0; i < 7; ++i)
+        __hip_atomic_fetch_or(seg32 + dw + i, perm(d[i + 1], d[i], sel), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
+// Buffer-resource word 3 for untyped (raw) buffer access on this part: the
+// hardware drops every store whose offset lies at or past the resource's byte
+// count, so a store instruction that all lanes execute can still write only
+// some of them, with no branch.
+constexpr int32_t kRawBufferWord3 = 0x00020000;
+constexpr uint32_t kDroppedOffset = 0x80000000u;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Where byte lane `lane` of store_span stores for the range [from, to) of a
+// segment: lanes 0..15 the bytes of the word that holds `from` (when `from`
+// is not word-aligned), lanes 16..31 those of the word that holds `to` (when
+// `to` is not word-aligned and that word is another one); 0 (and `keep`
+// false) for the other lanes.
+__device__ __forceinline__ uint32_t span_byte(uint32_t from, uint32_t to, bool &keep)
+{
+    const uint32_t lane = lane_id();
+    const uint32_t hw = from / 16, tw = to / 16;
+    uint32_t x = 0;
+    keep = false;
+    if (lane < 16) {
+        x = 16 * hw + lane;
+        keep = (from & 15u) && x >= from && x < to;
+    } else if (lane < 32) {
+        x = 16 * tw + lane - 16;
+        keep = (to & 15u) && (tw > hw || (from & 15u) == 0) && x >= from && x < to;
     }
+    return keep ? x : 0u;
+}
+
+// Stores bytes [from, to) of a segment to dst (a line-aligned stream
+// address): its whole words by dwordx4 lanes (word lane + 64 k in v[k]), the
+// partial words at either end by the byte lanes of span_byte (byte b, read
+// at the position that span_byte gave).  Always the same K + 1 store
+// instructions: the buffer's range drops what lies outside.
+template <int K>
+__device__ __forceinline__ void store_span(const uint4 (&v)[K], uint8_t b, bool keep_b, uint32_t x_b, uint8_t *dst,
+                                           uint32_t from, uint32_t to)
+{
+    const uint32_t lane = lane_id();
+    const uint32_t wlo = (from + 15) / 16, whi = to / 16;
+    const auto words = __builtin_amdgcn_make_buffer_rsrc(dst, 0, (int32_t)__builtin_amdgcn_readfirstlane(16 * whi),
+                                                         kRawBufferWord3);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const uint32_t i = lane + 64 * k;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{v[k].x, v[k].y, v[k].z, v[k].w}, words,
+                                               i >= wlo && i < whi ? 16 * i : kDroppedOffset, 0, 2 /* nt */);
+    }
+    const auto bytes =
+        __builtin_amdgcn_make_buffer_rsrc(dst, 0, (int32_t)__builtin_amdgcn_readfirstlane(to), kRawBufferWord3);
+    __builtin_amdgcn_raw_buffer_store_b8(b, bytes, keep_b ? x_b : kDroppedOffset, 0, 0);
 }
 
 // Writes a tile's records to the stream from its LDS segment.  LDS word 0
-// stands for the 16-byte aligned stream word at a0: its first `lead` bytes
-// are already in place (records carried over from the previous half pass,
-// or, before the first store, bytes that belong to the records before this
-// tile, which this wave never writes: `own0` of them).  After each half pass
-// the whole 16-byte words are stored and the last, partial one is carried
-// into word 0, so only the tile's first and last words take byte stores.
+// stands for the line-aligned stream address a0: the segment's first
+// `lead` bytes are already in place (records carried over from the previous
+// half pass, or, before the first store, bytes that belong to the records
+// before this tile, which this wave never writes: `own0` of them).  After
+// each half pass the whole lines are stored and the last, partial one (up
+// to eight words) is carried to the front, so every store writes whole
+// aligned lines except at the tile's first and last line.  Every half pass
+// issues the same store instructions (three dwordx4 and one byte store; the
+// buffer's range drops what lies outside), so the wait for the next tile's
+// loads, issued before these stores, needs no wait for the stores
+// themselves.
 struct RecordWriter {
     uint64_t a0;
     uint32_t lead, own0;
 
     __device__ __forceinline__ void begin(RederiveLds &L, uint64_t dst0)
     {
-        a0 = dst0 & ~uint64_t(15);
-        lead = own0 = (uint32_t)(dst0 & 15);
-        if (lane_id() == 0) L.seg[0] = make_uint4(0, 0, 0, 0);
+        a0 = dst0 & ~uint64_t(kLineBytes - 1);
+        lead = own0 = (uint32_t)(dst0 & (kLineBytes - 1));
+        if (lane_id() < kLineWords) L.seg[lane_id()] = make_uint4(0, 0, 0, 0);
     }
 
-    // Zeroes the words after word 0 that `count` records (and the overhang of
-    // the lanes' dword writes) will touch; returns the byte of word 0 where
-    // the half pass's records start.
-    __device__ __forceinline__ uint32_t open(RederiveLds &L, uint32_t count) const
-    {
-        const uint32_t words = (lead + 3 * count + 32 + 15) / 16;
-        for (uint32_t i = 1 + lane_id(); i < words; i += 64) L.seg[i] = make_uint4(0, 0, 0, 0);
-        wave_lds_fence();
-        return lead;
-    }
+    // The byte of the segment where the half pass's records start (the words
+    // past the first line are zero: set up by build_wave_tables, kept by
+    // flush).
+    __device__ __forceinline__ uint32_t open() const { return lead; }
 
+    // Stores the half pass's whole lines (below a line of lead plus 3 * 1024
+    // record bytes: at most 3072 bytes, three words per lane), zeroes the
+    // words past the first line that its records (and the overhang of the
+    // lanes' dword writes) touched, and carries the last, partial line to
+    // the front; count may be 0.
     __device__ __forceinline__ void flush(RederiveLds &L, uint8_t *__restrict__ out, uint32_t count)
     {
         wave_lds_fence();
         const uint32_t lane = lane_id();
         const uint32_t end = lead + 3 * count;
-        const uint32_t full = end / 16;
-        for (uint32_t i = lane; i < full; i += 64) {
-            const uint4 v = L.seg[i];
-            if (i == 0 && own0) {
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                for (uint32_t b = own0; b < 16; ++b) out[a0 + b] = (uint8_t)(w[b / 4] >> (8 * (b & 3)));
-            } else {
-                store_nt(reinterpret_cast<uint4 *>(out + a0 + 16ull * i), v);
-            }
+        const uint32_t F = __builtin_amdgcn_readfirstlane((end / kLineBytes) * kLineWords);   // whole lines
+        const uint32_t to = 16 * F;
+        uint4 v[3];
+#pragma unroll
+        for (uint32_t k = 0; k < 3; ++k) v[k] = L.seg[lane + 64 * k];
+        bool keep_b;
+        const uint32_t x_b = span_byte(own0, to, keep_b);
+        const uint8_t b = reinterpret_cast<const uint8_t *>(L.seg)[x_b];
+        const uint4 carry = L.seg[F + lane % kLineWords];
+        // the words the half pass touched: (end + 28 + 3) / 16 < kRdSegWords
+        const uint32_t touched = (end + 32 + 15) / 16;
+#pragma unroll
+        for (uint32_t k = 0; k < 4; ++k) {
+            const uint32_t i = kLineWords + lane + 64 * k;
+            if (i < touched) L.seg[i] = make_uint4(0, 0, 0, 0);
         }
-        if (full) {
-            wave_lds_fence();
-            if (lane == 0) L.seg[0] = L.seg[full];          // the partial word carries over
-            wave_lds_fence();
-            a0 += 16ull * full;
+        store_span<3>(v, b, keep_b, x_b, out + a0, own0, to);
+        if (F) {
+            if (lane < kLineWords) L.seg[lane] = carry;
+            a0 += to;
             own0 = 0;
         }
-        lead = end & 15;
-        if (!full) lead = end;
+        lead = end - to;
     }
 
-    // The tile's last, partial word.
+    // The tile's last, partial line.
     __device__ __forceinline__ void finish(RederiveLds &L, uint8_t *__restrict__ out) const
     {
         wave_lds_fence();
-        if (lane_id() == 0 && lead > own0) {
-            const uint4 v = L.seg[0];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            for (uint32_t b = own0; b < lead; ++b) out[a0 + b] = (uint8_t)(w[b / 4] >> (8 * (b & 3)));
-        }
+        const uint4 v[1] = {L.seg[lane_id() % kLineWords]};
+        bool keep_b;
+        const uint32_t x_b = span_byte(own0, lead, keep_b);
+        store_span<1>(v, reinterpret_cast<const uint8_t *>(L.seg)[x_b], keep_b, x_b, out + a0, own0, lead);
     }
 };
 
@@ -1374,29 +1442,57 @@ __device__ __forceinline__ void load_tile_part_bf16(const uint16_t *__restrict__
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const uint64_t base = (uint64_t)t * kEncTile + (uint64_t)wave * (512 * C);
     if (base + 512 * C <= n) {                                    // wave-uniform
+        const uint4 *mine = reinterpret_cast<const uint4 *>(in + base) + lane;
 #pragma unroll
-        for (int j = 0; j < C; ++j)
-            q[j] = load_nt(reinterpret_cast<const uint4 *>(in + base + (uint64_t)(j * 64 + lane) * 8));
+        for (int j = 0; j < C; ++j) q[j] = load_nt(mine + 64 * j);
     } else {
+        const uint32_t valid = n > base ? (uint32_t)(n - base) : 0u;   // below 512 C here
+        const uint16_t *part = in + base;
 #pragma unroll
         for (int j = 0; j < C; ++j) {
-            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
+            const uint32_t e0 = (j * 64 + lane) * 8;
             uint16_t v[8];
 #pragma unroll
-            for (uint32_t k = 0; k < 8; ++k) v[k] = (c0 + k < n) ? in[c0 + k] : 0;
+            for (uint32_t k = 0; k < 8; ++k) v[k] = (e0 + k < valid) ? part[e0 + k] : 0;
             q[j] = make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16,
                               v[4] | (uint32_t)v[5] << 16, v[6] | (uint32_t)v[7] << 16);
         }
     }
 }
 
+// Escape masks and exponent bytes of this wave's part of tile t from its
+// loaded words (elements past the end of the input do not escape); returns
+// the lane's escape count.
+template <int C>
+__device__ __forceinline__ uint32_t tile_part_escapes_bf16(const uint4 (&q)[C], const uint8_t *esc8, uint64_t n,
+                                                           uint32_t t, uint32_t (&m)[C], uint32_t (&ea)[C],
+                                                           uint32_t (&eb)[C])
+{
+    const uint32_t lane = lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const uint64_t base = (uint64_t)t * kEncTile + (uint64_t)wave * (512 * C);
+    // elements of this part before the end of the input (wave-uniform)
+    const uint32_t valid = n > base ? (uint32_t)std::min<uint64_t>(n - base, 512 * C) : 0u;
+    uint32_t lane_total = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        m[j] = escapes8_bf16(q[j], esc8, ea[j], eb[j]);
+        const uint32_t e0 = (j * 64 + lane) * 8;
+        if (e0 >= valid) m[j] = 0;
+        else if (e0 + 8 > valid) m[j] &= (1u << (valid - e0)) - 1;
+        lane_total += __popc(m[j]);
+    }
+    return lane_total;
+}
+
 // The BF16 tiles list[0 .. count) (in LDS) of this workgroup, in order.
-// Per tile: escape masks and exponent bytes from the loaded words, the wave
-// totals' prefix through LDS, then each wave's records after those of the
-// waves before it.  The next tile's loads are issued before this tile's
-// records are written, so its words arrive while the stores go out (and
-// waiting for them does not wait for those stores, which come later in the
-// in-order counter).
+// Per tile: the wave totals' prefix through LDS, then each wave's records
+// after those of the waves before it.  The next tile's loads are issued
+// before this tile's records are written and turned into escape masks after
+// them, so its words arrive while the stores go out; the stores are a fixed
+// number of instructions, so the wait for those loads counts the stores
+// issued after them and does not wait for the stores (the vector memory
+// counter completes in issue order).
 __device__ __forceinline__ void rederive_tiles_bf16(const uint16_t *__restrict__ in, uint64_t n, const uint32_t *list,
                                                     uint32_t count, const uint32_t *__restrict__ tile_counts,
                                                     const uint64_t *__restrict__ block_offsets, uint64_t off_esc,
@@ -1409,28 +1505,22 @@ __device__ __forceinline__ void rederive_tiles_bf16(const uint16_t *__restrict__
     uint32_t *seg32 = reinterpret_cast<uint32_t *>(L.seg);
     uint32_t t = list[0];
     uint4 q[C];
+    uint32_t m[C], ea[C], eb[C];
     load_tile_part_bf16<C>(in, n, t, q);
+    uint32_t lane_total = tile_part_escapes_bf16<C>(q, esc8, n, t, m, ea, eb);
 #pragma unroll 1
     for (uint32_t i = 0; i < count; ++i) {
-        const uint64_t base = (uint64_t)t * kEncTile + (uint64_t)wave * (512 * C);
-        uint32_t m[C], ea[C], eb[C], lane_total = 0;
-#pragma unroll
-        for (int j = 0; j < C; ++j) {
-            m[j] = escapes8_bf16(q[j], esc8, ea[j], eb[j]);
-            const uint64_t c0 = base + (uint64_t)(j * 64 + lane) * 8;
-            if (c0 >= n) m[j] = 0;
-            else if (c0 + 8 > n) m[j] &= (1u << (uint32_t)(n - c0)) - 1;
-            lane_total += __popc(m[j]);
-        }
         // the next tile (this one again after the last: no branch around the loads)
         const uint32_t tn = i + 1 < count ? list[i + 1] : t;
         load_tile_part_bf16<C>(in, n, tn, q);
+        const uint32_t base = t * kEncTile + wave * (512 * C);     // low bits: the block positions
         const uint64_t first = tile_first_record(tile_counts, block_offsets, t);
         const uint32_t wave_total = read_lane63(wave_inclusive_sum(lane_total));
         if (lane == 0) wave_totals[wave] = wave_total;
         __syncthreads();
         uint32_t before = 0;
         for (uint32_t w = 0; w < wave; ++w) before += wave_totals[w];
+        before = __builtin_amdgcn_readfirstlane(before);            // wave-uniform: the store base
         RecordWriter wr;
         wr.begin(L, off_esc + 3 * (first + before));
 #pragma unroll
@@ -1438,12 +1528,11 @@ __device__ __forceinline__ void rederive_tiles_bf16(const uint16_t *__restrict__
             const uint32_t cnt2[2] = {(uint32_t)__popc(m[2 * h]), (uint32_t)__popc(m[2 * h + 1])};
             uint32_t row_base[2], row_total[2], lane_before[2];
             const uint32_t cnt = wave_chunk_ranks<2>(cnt2, row_base, row_total, lane_before);
-            if (cnt == 0) continue;                              // wave-uniform
-            const uint32_t lead = wr.open(L, cnt);
+            const uint32_t lead = wr.open();
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int j = 2 * h + k;
-                const uint32_t pos0 = (uint32_t)((base + (uint64_t)(j * 64 + lane) * 8) & 0xFFFFu);
+                const uint32_t pos0 = (base + (j * 64 + lane) * 8) & 0xFFFFu;
                 if (m[j]) or_records8(seg32, lead + 3 * (row_base[k] + lane_before[k]), m[j], ea[j], eb[j], pos0,
                                       L.slots);
             }
@@ -1451,6 +1540,7 @@ __device__ __forceinline__ void rederive_tiles_bf16(const uint16_t *__restrict__
         }
         wr.finish(L, out);
         __syncthreads();                                          // wave_totals is reused by the next tile
+        lane_total = tile_part_escapes_bf16<C>(q, esc8, n, tn, m, ea, eb);
         t = tn;
     }
 }
