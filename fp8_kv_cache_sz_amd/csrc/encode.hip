@@ -252,7 +252,11 @@ __device__ __forceinline__ uint32_t chunk_flag_keep(uint32_t v)
 // wave's LDS buffer, shifted by the byte misalignment of the segment's
 // destination, and the wave then copies the buffer to the tile's staging
 // slot with aligned dword stores; the dwords at both ends, which neighbouring
-// segments (possibly of another wave) share, are written byte by byte.
+// segments (possibly of another wave) share, are written byte by byte.  A
+// BF16 row with at most 512 records goes through the buffer as one segment
+// (one copy: fewer stream lines written in parts by two copies, 2.4 % off
+// the dense encode of 1.9 %-escape BF16); a row with at most kDirectRecords
+// records skips the buffer.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kSegElems = 512;
 constexpr uint32_t kSegBytes = 3 * kSegElems + 8;          // + alignment shift, rounded to dwords
@@ -459,7 +463,25 @@ __global__ __launch_bounds__(kEncTile / (8 * C)) void sz_enc_dense_bf16(const ui
     const uint32_t wave_before = workgroup_wave_prefix<kWaves>(wave_total, wave_totals, tile_total);
     // only the Top-16 format re-derives escape-heavy tiles in the compaction
     const bool rederive = V == kTop16 && tile_total > rederive_above;
-    if (wave_total && !rederive) {
+    constexpr uint32_t kItem = escape_item_bytes(V);
+    if (wave_total > kDirectRecords && kItem * wave_total + 3 <= kSegBytes && !rederive) {
+        // the row's records gathered in the wave's LDS buffer (at most 512:
+        // the alignment shift of up to 3 bytes fits), one flush
+        uint8_t *tstage = stage + tile * slot;
+        const uint32_t g0 = kItem * wave_before;
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            if (esc[j]) {
+                const uint32_t pos0 = (uint32_t)((base + (uint64_t)(j * 64 + lane) * 8) & 0xFFFFu);
+                const uint32_t at = (g0 & 3) + kItem * (row_base[j] + lane_before[j]);
+                if (V == kTop15S) lds_put_exponents(buf, at, esc[j], ex_park[wave][j][lane]);
+                else lds_put_records(buf, at, esc[j], ex_park[wave][j][lane], pos0);
+            }
+        }
+        wave_lds_fence();
+        flush_segment(buf, tstage, g0, kItem * wave_total);
+        wave_lds_fence();
+    } else if (wave_total && !rederive) {
         uint8_t *tstage = stage + tile * slot;
 #pragma unroll
         for (int j = 0; j < C; ++j) {
