@@ -98,10 +98,10 @@ inline uint64_t stage_slot_bytes(uint32_t version, uint64_t nt)
 constexpr uint64_t kScanSuper = (uint64_t)kScanBatch * kScanThreads;
 
 // Encode workspace layout (byte offsets): the status word (first 256 bytes),
-// tile counts, block offsets, the scan workgroups' escape totals and the
-// escape staging (stage_slot_bytes per tile).
+// tile counts, block offsets, the scan workgroups' escape totals, their
+// flagged-tile words and the escape staging (stage_slot_bytes per tile).
 struct WsLayout {
-    uint64_t counts, offsets, totals, stage, slot, total;
+    uint64_t counts, offsets, totals, flags, stage, slot, total;
 };
 
 inline WsLayout ws_layout(uint32_t version, int dtype, uint64_t n)
@@ -111,7 +111,9 @@ inline WsLayout ws_layout(uint32_t version, int dtype, uint64_t n)
     w.counts = 256;
     w.offsets = w.counts + up256(4 * g.nt + 16);
     w.totals = w.offsets + up256(8 * g.nb + 16);
-    w.stage = w.totals + up256(8 * ((g.nb + kScanSuper - 1) / kScanSuper));
+    const uint64_t scan_groups = (g.nb + kScanSuper - 1) / kScanSuper;
+    w.flags = w.totals + up256(8 * scan_groups);
+    w.stage = w.flags + up256(4 * (kScanThreads / 64) * scan_groups);   // one word per scan wave
     w.slot = stage_slot_bytes(version, g.nt);
     // 16 bytes past the last slot: the record copies read whole words
     w.total = w.stage + up256(w.slot * g.nt + 16);

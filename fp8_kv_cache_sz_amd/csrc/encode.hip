@@ -772,6 +772,14 @@ __device__ __forceinline__ uint32_t block_escapes(uint4 v, uint32_t b, uint32_t 
     return (v.x & m) + ((t + 1 < nt) ? v.y & m : 0) + ((t + 2 < nt) ? v.z & m : 0) + ((t + 3 < nt) ? v.w & m : 0);
 }
 
+// Nonzero when a tile of block b (below nt) carries kRederiveFlag.
+__device__ __forceinline__ uint32_t block_flags(uint4 v, uint32_t b, uint32_t nt)
+{
+    const uint32_t t = kTilesPerBlock * b;
+    const uint32_t f = v.x | ((t + 1 < nt) ? v.y : 0) | ((t + 2 < nt) ? v.z : 0) | ((t + 3 < nt) ? v.w : 0);
+    return f & kRederiveFlag;
+}
+
 // Sum of a 64-bit value over the workgroup (kScanThreads lanes); every
 // thread gets it.
 __device__ __forceinline__ uint64_t workgroup_sum_u64(uint64_t v, uint64_t *lds)
@@ -820,8 +828,9 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan_reduce(const uint32_
 // stream and the exclusive escape offset of every block, starting from the
 // escapes of the blocks before it (the sum of totals[0 .. g), from
 // sz_enc_scan_reduce; one workgroup when the stream has at most kScanSuper
-// blocks).  Workgroup 0 writes the header and the zero padding between
-// sections, the last workgroup E.
+// blocks), and whether one of those tiles is flagged (one word per wave,
+// flagged[g kScanWaves + w]).  Workgroup 0 writes the header and the zero padding between sections, the
+// last workgroup E.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__restrict__ tile_counts,
                                                             uint32_t nt,
@@ -829,7 +838,8 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
                                                             uint8_t *__restrict__ out, HeaderArgs h,
                                                             const uint32_t *__restrict__ cb_dev,
                                                             int32_t *__restrict__ status,
-                                                            const uint64_t *__restrict__ totals)
+                                                            const uint64_t *__restrict__ totals,
+                                                            uint32_t *__restrict__ flagged)
 {
     __shared__ ScanLds lds;
     __shared__ uint64_t sum_lds[kScanWaves];
@@ -856,6 +866,7 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
         }
     };
     uint4 v_next[kScanBatch];
+    uint32_t any_flagged = 0;
     load_batch(first, v_next);
     for (uint32_t b0 = first; b0 < last; b0 += kScanBatch * kScanThreads) {
         uint4 v[kScanBatch];
@@ -864,7 +875,10 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
         if (b0 + kScanBatch * kScanThreads < last) load_batch(b0 + kScanBatch * kScanThreads, v_next);
         uint32_t x[kScanBatch];
 #pragma unroll
-        for (int i = 0; i < kScanBatch; ++i) x[i] = block_escapes(v[i], b0 + i * kScanThreads + tid, nt);
+        for (int i = 0; i < kScanBatch; ++i) {
+            x[i] = block_escapes(v[i], b0 + i * kScanThreads + tid, nt);
+            any_flagged |= block_flags(v[i], b0 + i * kScanThreads + tid, nt);
+        }
         uint64_t base[kScanBatch];
         scan_batch(x, base, lds);
 #pragma unroll
@@ -877,6 +891,10 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
         }
     }
     const uint64_t total = lds.carry;
+    // whether a tile of this wave's blocks is flagged, one word per wave (the
+    // compaction skips the re-derivation when none of the words is set)
+    any_flagged = __any(any_flagged);
+    if (lane_id() == 0) flagged[blockIdx.x * kScanWaves + tid / 64] = any_flagged ? 1u : 0u;
     if (blockIdx.x == 0) write_header(out, h, cb, verdict, false, status);
     if (tid == 0 && blockIdx.x == gridDim.x - 1) {
         reinterpret_cast<uint32_t *>(out)[4] = (uint32_t)total;
@@ -1418,15 +1436,14 @@ __device__ __forceinline__ void copy_block_records(uint64_t meta, const uint8_t 
 // ---------------------------------------------------------------------------
 // Kernel: escape compaction of streams above kFusedPrefixTiles tiles, after
 // sz_enc_scan.  512-lane workgroups; wave w of workgroup g copies the staged
-// records of blocks 8 g + w, 8 (g + G) + w, ... (G workgroups).  Then the
-// flagged (escape-heavy) tiles, which the dense encoders did not stage, are
-// derived again from the input: workgroup
-// g takes the tiles g, g + G, g + 2G, ... (G workgroups, at least
-// kRederiveGroups when the stream has that many tiles, so that the GPU is
-// full), reads their tile counts (one per tile and thread), lists the
-// flagged ones in LDS in order, and re-derives them; with no flagged tile
-// that one load is all.  A tile's first record follows its block's offset
-// and the counts of the block's tiles before it.
+// records of blocks 8 g + w, 8 (g + G) + w, ... (G workgroups).  Then, when
+// one of the scan's flagged-tile words is set, the flagged (escape-heavy)
+// tiles, which the dense encoders did not stage, are derived again from the
+// input: workgroup g takes the tiles g, g + G, g + 2G, ... (G workgroups, at
+// least kRederiveGroups when the stream has that many tiles, so that the GPU
+// is full), reads their tile counts (one per tile and thread), lists the
+// flagged ones in LDS in order, and re-derives them.  A tile's first record
+// follows its block's offset and the counts of the block's tiles before it.
 //   BF16: the eight waves share a tile, wave w its 2048 elements
 //   [2048 w, 2048 w + 2048), all loaded at once; the wave totals meet in LDS
 //   and each wave writes its records after those of the waves before it, two
@@ -1597,13 +1614,17 @@ __global__ __launch_bounds__(kRederiveThreads) __attribute__((amdgpu_waves_per_e
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
     const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
     uint64_t nb, uint32_t item, uint32_t slot, const void *__restrict__ in, uint64_t n, Codebook4 cb,
-    const uint32_t *__restrict__ cb_dev, uint32_t rederive)
+    const uint32_t *__restrict__ cb_dev, const uint32_t *__restrict__ flagged, uint32_t flag_words)
 {
     constexpr uint32_t kWaves = kRederiveThreads / 64;
     __shared__ RederiveLds lds[kWaves];
     __shared__ uint32_t list[kRederiveThreads];
     __shared__ uint32_t wave_sums[kWaves];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    // whether the scan saw a flagged tile (its words are loaded first, so that
+    // their latency hides behind the copies)
+    uint32_t any_flagged = 0;
+    for (uint32_t i = lane_id(); i < flag_words; i += 64) any_flagged |= flagged[i];
     // staged records: wave w of workgroup g copies blocks 8 g + w, 8 (g + G) + w,
     // ...; the next block's metadata is fetched before the current block's
     // records are copied
@@ -1619,7 +1640,7 @@ __global__ __launch_bounds__(kRederiveThreads) __attribute__((amdgpu_waves_per_e
             b = b_next;
         }
     }
-    if (!rederive) return;
+    if (!__any(any_flagged)) return;                               // the same in every wave
     RederiveLds &L = lds[wave];
     // flagged tiles: workgroup g takes the tiles g, g + G, g + 2G, ...: the
     // tiles that the workgroups work on at one time lie next to each other in
@@ -1865,6 +1886,7 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
     uint32_t *tile_counts = reinterpret_cast<uint32_t *>(ws + w.counts);
     uint64_t *block_offsets = reinterpret_cast<uint64_t *>(ws + w.offsets);
     uint64_t *scan_totals = reinterpret_cast<uint64_t *>(ws + w.totals);
+    uint32_t *scan_flagged = reinterpret_cast<uint32_t *>(ws + w.flags);
     uint8_t *stage = ws + w.stage;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -1947,25 +1969,26 @@ int encode_impl(uint32_t version, int dtype, const void *d_in, uint64_t n_elems,
         }
         LaunchScope scope("sz_enc_scan", s);
         hipLaunchKernelGGL(sz_enc_scan, dim3(scan_groups), dim3(kScanThreads), 0, s, tile_counts, (uint32_t)g.nt,
-                           block_offsets, out, h, cb_dev, status, scan_totals);
+                           block_offsets, out, h, cb_dev, status, scan_totals, scan_flagged);
     }
     if (g.nt) {
         // up to kCopyBlocksPerWave blocks per wave for the staged records;
         // for Top-16 at least kRederiveGroups workgroups (the formats other
         // than Top-16 stage every tile: no tile is flagged)
         LaunchScope scope("sz_enc_compact", s);
-        const uint32_t rederive = version == kTop16 ? 1u : 0u;
+        const bool rederive = version == kTop16;
+        const uint32_t flag_words = rederive ? (uint32_t)((g.nb + kScanSuper - 1) / kScanSuper) * kScanWaves : 0u;
         const uint64_t per_group = kCopyBlocksPerWave * (kRederiveThreads / 64);
         uint64_t groups = (g.nb + per_group - 1) / per_group;
         if (rederive) groups = std::max<uint64_t>(groups, std::min<uint64_t>(kRederiveGroups, g.nt));
         if (dtype == SZ_BF16)
             hipLaunchKernelGGL(sz_enc_compact<SZ_BF16>, dim3((uint32_t)groups), dim3(kRederiveThreads), 0, s, stage,
                                tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, escape_item_bytes(version),
-                               (uint32_t)w.slot, d_in, g.n, cb4, cb_dev, rederive);
+                               (uint32_t)w.slot, d_in, g.n, cb4, cb_dev, scan_flagged, flag_words);
         else
             hipLaunchKernelGGL(sz_enc_compact<SZ_FP8_E5M2>, dim3((uint32_t)groups), dim3(kRederiveThreads), 0, s,
                                stage, tile_counts, block_offsets, out, g.off_esc, g.nt, g.nb, 3u, (uint32_t)w.slot, d_in,
-                               g.n, cb4, cb_dev, rederive);
+                               g.n, cb4, cb_dev, scan_flagged, flag_words);
     }
     return hipGetLastError() == hipSuccess ? SZ_OK : SZ_E_HIP;
 }

@@ -98,8 +98,8 @@ uint64_t sz_encoded_size(int dtype, uint64_t n_elems, uint64_t n_escapes);
 
 /* Device workspace that sz_encode (and sz_encode_devcb) needs for n_elems
  * values: the status word, tile escape counts, block offsets, one escape
- * total per 8,192 blocks (the scan's workgroups) and the escape staging
- * area.  Staging takes one slot per 16384-element tile: 49,152
+ * total and 16 flagged-tile words per 8,192 blocks (the scan's workgroups)
+ * and the escape staging area.  Staging takes one slot per 16384-element tile: 49,152
  * bytes (3 per element) for streams of up to 2,048 tiles (32M elements),
  * whose tiles are all staged, and 12,288 bytes above that, where a tile
  * with more than 4,096 escapes stages nothing (the compaction derives its

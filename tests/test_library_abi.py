@@ -83,11 +83,13 @@ def test_encoded_size_matches_oracle():
             nt, nb = (n + 16383) // 16384, (n + 65535) // 65536
             assert ws % 256 == 0
             # status, tile counts, block offsets, the scan workgroups' escape
-            # totals (one u64 per 8,192 blocks), then one staging slot per 16K
+            # totals and flagged-tile words (one u64 and sixteen u32 per 8,192
+            # blocks), then one staging slot per 16K
             # tile: 3 bytes per element up to 2,048 tiles, 12 KB per tile
             # (4,096 records) above
             slot = 3 * 16384 if nt <= 2048 else 3 * 4096
-            fixed = 256 + up(4 * nt + 16) + up(8 * nb + 16) + up(8 * ((nb + 8191) // 8192))
+            groups = (nb + 8191) // 8192
+            fixed = 256 + up(4 * nt + 16) + up(8 * nb + 16) + up(8 * groups) + up(64 * groups)
             assert ws == fixed + up(slot * nt + 16), (dtype, n)
             dws = nat.sz_decode_workspace_size(dtype, n)
             assert dws == 256 + up(8 * nb + 16) and dws <= ws
