@@ -921,22 +921,30 @@ __device__ __forceinline__ void copy_records(const uint8_t *__restrict__ src, ui
     const uint64_t end = dst0 + len;
     const uint64_t body_begin = std::min<uint64_t>((dst0 + 15) & ~uint64_t(15), end);
     const uint64_t body_end = std::max<uint64_t>(end & ~uint64_t(15), body_begin);
-    const uint32_t head = (uint32_t)(body_begin - dst0);
-    for (uint32_t i = lane; i < head; i += width) out[dst0 + i] = src[i];
+    const uint32_t head = (uint32_t)(body_begin - dst0);                  // < 16 <= width
+    const uint32_t tail_src = (uint32_t)(body_end - dst0);
+    const uint32_t tail = (uint32_t)(end - body_end);                     // < 16
     const uint32_t *src32 = reinterpret_cast<const uint32_t *>(src);
     const uint32_t chunks = (uint32_t)((body_end - body_begin) / 16);
     const uint32_t sh = head & 3;
-#pragma unroll 4
-    for (uint32_t c = lane; c < chunks; c += width) {
+    auto chunk = [&](uint32_t c) {
         const uint32_t w0 = (head >> 2) + 4 * c;                 // first source word
         const uint32_t a0 = src32[w0], a1 = src32[w0 + 1], a2 = src32[w0 + 2], a3 = src32[w0 + 3],
                        a4 = src32[w0 + 4];
-        const uint4 v = make_uint4(__builtin_amdgcn_alignbyte(a1, a0, sh), __builtin_amdgcn_alignbyte(a2, a1, sh),
-                                   __builtin_amdgcn_alignbyte(a3, a2, sh), __builtin_amdgcn_alignbyte(a4, a3, sh));
-        *reinterpret_cast<uint4 *>(out + body_begin + 16ull * c) = v;
-    }
-    const uint32_t tail_src = (uint32_t)(body_end - dst0);
-    for (uint32_t i = lane; body_end + i < end; i += width) out[body_end + i] = src[tail_src + i];
+        return make_uint4(__builtin_amdgcn_alignbyte(a1, a0, sh), __builtin_amdgcn_alignbyte(a2, a1, sh),
+                          __builtin_amdgcn_alignbyte(a3, a2, sh), __builtin_amdgcn_alignbyte(a4, a3, sh));
+    };
+    // the loads of the head byte, the tail byte and the first body chunk of
+    // each lane go out before any store: one memory latency for a short tile
+    const uint8_t hb = lane < head ? src[lane] : 0;
+    const uint8_t tb = lane < tail ? src[tail_src + lane] : 0;
+    const uint4 v0 = lane < chunks ? chunk(lane) : make_uint4(0, 0, 0, 0);
+    if (lane < head) out[dst0 + lane] = hb;
+    if (lane < tail) out[body_end + lane] = tb;
+    if (lane < chunks) *reinterpret_cast<uint4 *>(out + body_begin + 16ull * lane) = v0;
+#pragma unroll 4
+    for (uint32_t c = lane + width; c < chunks; c += width)
+        *reinterpret_cast<uint4 *>(out + body_begin + 16ull * c) = chunk(c);
 }
 
 // Derives the records of an escape-heavy tile again from the input, with one
