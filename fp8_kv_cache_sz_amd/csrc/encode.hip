@@ -1385,9 +1385,6 @@ __device__ __forceinline__ void compact_block(const uint8_t *__restrict__ stage,
     }
 }
 
-// Copies the staged records of block b's unflagged tiles to their place with
-// one wave (16-lane groups copy the four tiles at once when none is flagged
-// and none holds more than kGroupCopyRecords records).
 // The metadata of block b, one value per lane: lanes 0..3 the tile counts,
 // lane 4 the block's escape offset.
 __device__ __forceinline__ uint64_t block_meta(const uint32_t *__restrict__ tile_counts,
@@ -1401,8 +1398,10 @@ __device__ __forceinline__ uint64_t block_meta(const uint32_t *__restrict__ tile
     return meta;
 }
 
-// Copies the staged records of block b (metadata from block_meta) to their
-// place in the stream.
+// Copies the staged records of block b's unflagged tiles (metadata from
+// block_meta) to their place in the stream with one wave: 16-lane groups copy
+// the four tiles at once when none is flagged and none holds more than
+// kGroupCopyRecords records, else the wave copies them tile after tile.
 __device__ __forceinline__ void copy_block_records(uint64_t meta, const uint8_t *__restrict__ stage,
                                                    uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
                                                    uint64_t b, uint32_t item, uint32_t slot)
