@@ -914,14 +914,14 @@ __global__ __launch_bounds__(kScanThreads) void sz_enc_scan(const uint32_t *__re
 // final place.
 // ---------------------------------------------------------------------------
 // Copies len bytes of staged records to out[dst0, dst0 + len) with the lanes
-// [0, width) of a lane group (lane = index inside the group).
+// [0, width) of a lane group (lane = index inside the group; width >= 8).
 __device__ __forceinline__ void copy_records(const uint8_t *__restrict__ src, uint8_t *__restrict__ out,
                                              uint64_t dst0, uint32_t len, uint32_t lane, uint32_t width)
 {
     const uint64_t end = dst0 + len;
     const uint64_t body_begin = std::min<uint64_t>((dst0 + 15) & ~uint64_t(15), end);
     const uint64_t body_end = std::max<uint64_t>(end & ~uint64_t(15), body_begin);
-    const uint32_t head = (uint32_t)(body_begin - dst0);                  // < 16 <= width
+    const uint32_t head = (uint32_t)(body_begin - dst0);                  // < 16 <= 2 width
     const uint32_t tail_src = (uint32_t)(body_end - dst0);
     const uint32_t tail = (uint32_t)(end - body_end);                     // < 16
     const uint32_t *src32 = reinterpret_cast<const uint32_t *>(src);
@@ -934,13 +934,19 @@ __device__ __forceinline__ void copy_records(const uint8_t *__restrict__ src, ui
         return make_uint4(__builtin_amdgcn_alignbyte(a1, a0, sh), __builtin_amdgcn_alignbyte(a2, a1, sh),
                           __builtin_amdgcn_alignbyte(a3, a2, sh), __builtin_amdgcn_alignbyte(a4, a3, sh));
     };
-    // the loads of the head byte, the tail byte and the first body chunk of
-    // each lane go out before any store: one memory latency for a short tile
+    // the loads of the head bytes, the tail bytes (two of each per lane when
+    // the group is 8 lanes wide) and the first body chunk of each lane go out
+    // before any store: one memory latency for a short tile
+    const uint32_t lane2 = lane + width;
     const uint8_t hb = lane < head ? src[lane] : 0;
+    const uint8_t hb2 = lane2 < head ? src[lane2] : 0;
     const uint8_t tb = lane < tail ? src[tail_src + lane] : 0;
+    const uint8_t tb2 = lane2 < tail ? src[tail_src + lane2] : 0;
     const uint4 v0 = lane < chunks ? chunk(lane) : make_uint4(0, 0, 0, 0);
     if (lane < head) out[dst0 + lane] = hb;
+    if (lane2 < head) out[dst0 + lane2] = hb2;
     if (lane < tail) out[body_end + lane] = tb;
+    if (lane2 < tail) out[body_end + lane2] = tb2;
     if (lane < chunks) *reinterpret_cast<uint4 *>(out + body_begin + 16ull * lane) = v0;
 #pragma unroll 4
     for (uint32_t c = lane + width; c < chunks; c += width)
@@ -1440,6 +1446,79 @@ __device__ __forceinline__ void copy_block_records(uint64_t meta, const uint8_t 
                          lane, 64);
 }
 
+// Tiles with at most this many records are copied by 8-lane groups when a
+// wave copies two blocks at once.
+constexpr uint32_t kPairCopyRecords = 256;
+
+// The metadata of blocks b0 (lanes 0..4, as block_meta) and b1 (lanes
+// 32..36; zero when b1 >= nb).
+__device__ __forceinline__ uint64_t pair_meta(const uint32_t *__restrict__ tile_counts,
+                                              const uint64_t *__restrict__ block_offsets, uint64_t nt, uint64_t nb,
+                                              uint64_t b0, uint64_t b1)
+{
+    const uint32_t lane = lane_id();
+    const uint32_t l = lane & 31u;
+    const uint64_t b = lane < 32 ? b0 : b1;
+    uint64_t meta = 0;
+    if (b < nb) {
+        const uint64_t t0 = kTilesPerBlock * b;
+        if (l < kTilesPerBlock && t0 + l < nt) meta = tile_counts[t0 + l];
+        else if (l == kTilesPerBlock) meta = block_offsets[b];
+    }
+    return meta;
+}
+
+// Copies the staged records of blocks b0 and b1 (metadata from pair_meta)
+// with one wave: when no tile of either is flagged and none holds more than
+// kPairCopyRecords records, eight 8-lane groups copy the eight tiles at once
+// (one memory latency for both blocks); else block after block as
+// copy_block_records does.
+__device__ __forceinline__ void copy_pair_records(uint64_t meta, const uint32_t *__restrict__ tile_counts,
+                                                  const uint64_t *__restrict__ block_offsets,
+                                                  const uint8_t *__restrict__ stage, uint8_t *__restrict__ out,
+                                                  uint64_t off_esc, uint64_t nt, uint64_t nb, uint64_t b0, uint64_t b1,
+                                                  uint32_t item, uint32_t slot)
+{
+    const uint32_t lane = lane_id();
+    uint32_t cnt[2][kTilesPerBlock], before[2][kTilesPerBlock], most = 0, flagged = 0;
+    uint64_t off[2];
+#pragma unroll
+    for (uint32_t h = 0; h < 2; ++h) {
+        off[h] = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(meta >> 32), 32 * h + kTilesPerBlock) << 32) |
+                 (uint32_t)__builtin_amdgcn_readlane((uint32_t)meta, 32 * h + kTilesPerBlock);
+        uint32_t run = 0;
+#pragma unroll
+        for (uint32_t t = 0; t < kTilesPerBlock; ++t) {
+            const uint32_t v = __builtin_amdgcn_readlane((uint32_t)meta, 32 * h + t);
+            cnt[h][t] = v & ~kRederiveFlag;
+            flagged |= v & kRederiveFlag;
+            before[h][t] = run;
+            run += cnt[h][t];
+            most = std::max(most, cnt[h][t]);
+        }
+    }
+    if (!flagged && most <= kPairCopyRecords) {                 // wave-uniform
+        const uint32_t g = lane >> 3, h = g >> 2, t = g & 3u;
+        uint32_t k = 0, bef = 0;
+#pragma unroll
+        for (uint32_t hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (uint32_t tt = 0; tt < kTilesPerBlock; ++tt)
+                if (h == hh && t == tt) {
+                    k = cnt[hh][tt];
+                    bef = before[hh][tt];
+                }
+        const uint64_t b = h ? b1 : b0;
+        if (k)
+            copy_records(stage + (kTilesPerBlock * b + t) * (uint64_t)slot, out, off_esc + item * (off[h] + bef),
+                         item * k, lane & 7u, 8);
+        return;
+    }
+    copy_block_records(block_meta(tile_counts, block_offsets, nt, b0), stage, out, off_esc, nt, b0, item, slot);
+    if (b1 < nb)
+        copy_block_records(block_meta(tile_counts, block_offsets, nt, b1), stage, out, off_esc, nt, b1, item, slot);
+}
+
 // ---------------------------------------------------------------------------
 // Kernel: escape compaction of streams above kFusedPrefixTiles tiles, after
 // sz_enc_scan.  512-lane workgroups; wave w of workgroup g copies the staged
@@ -1454,17 +1533,20 @@ __device__ __forceinline__ void copy_block_records(uint64_t meta, const uint8_t 
 //   BF16: the eight waves share a tile, wave w its 2048 elements
 //   [2048 w, 2048 w + 2048), all loaded at once; the wave totals meet in LDS
 //   and each wave writes its records after those of the waves before it, two
-//   chunk rows at a time.  The next tile's loads are issued before the
-//   current tile's records are written.
+//   chunk rows at a time.  The loads of the tile after next are issued
+//   before the current tile's records are written.
 //   E5M2: each wave re-derives whole tiles of the list on its own.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kRederiveThreads = 512;
-constexpr uint32_t kRederiveGroups = 768;         // 3 workgroups of 8 waves (80 registers) on each compute unit
-// Blocks whose staged records one wave copies (at most): fewer waves, each
-// overlapping the next block's metadata fetch with the current copy.  With
+// 2 workgroups of 8 waves (128 registers: two tiles of loads in flight per
+// wave) on each compute unit.  Against 3 workgroups of 80 registers and one
+// tile ahead, random-bit BF16 (every tile re-derived, 512 MiB) takes 255 us
+// instead of 262; the staged copies of the long-context payload 0.5 us more.
+constexpr uint32_t kRederiveGroups = 512;
+// Blocks whose staged records one wave copies (at most), two at a time: with
 // eight, every large Top-16 stream gets the kRederiveGroups workgroups, one
-// resident round; with four, the long-context payload (28,672 blocks) had
-// 896 workgroups, a second round, and its compaction took 23 us against 18.
+// resident round (a second round of workgroups costs more than the longer
+// chain of copies per wave).
 constexpr uint64_t kCopyBlocksPerWave = 8;
 constexpr int kRdRowChunks = kEncTile / (kRederiveThreads / 64) / 512;   // 4 chunks per lane
 
@@ -1533,12 +1615,13 @@ __device__ __forceinline__ uint32_t tile_part_escapes_bf16(const uint4 (&q)[C], 
 
 // The BF16 tiles list[0 .. count) (in LDS) of this workgroup, in order.
 // Per tile: the wave totals' prefix through LDS, then each wave's records
-// after those of the waves before it.  The next tile's loads are issued
-// before this tile's records are written and turned into escape masks after
-// them, so its words arrive while the stores go out; the stores are a fixed
-// number of instructions, so the wait for those loads counts the stores
-// issued after them and does not wait for the stores (the vector memory
-// counter completes in issue order).
+// after those of the waves before it.  The loads run two tiles ahead in two
+// register sets used in turn (the loop body is written out for each): the
+// loads of tile i + 2 are issued before tile i's records are written, and
+// tile i + 1's words, loaded one tile earlier, are turned into escape masks
+// after them.  The stores are a fixed number of instructions, so the wait
+// for those loads counts the stores issued after them and does not wait for
+// the stores (the vector memory counter completes in issue order).
 __device__ __forceinline__ void rederive_tiles_bf16(const uint16_t *__restrict__ in, uint64_t n, const uint32_t *list,
                                                     uint32_t count, const uint32_t *__restrict__ tile_counts,
                                                     const uint64_t *__restrict__ block_offsets, uint64_t off_esc,
@@ -1550,15 +1633,18 @@ __device__ __forceinline__ void rederive_tiles_bf16(const uint16_t *__restrict__
     const uint8_t *esc8 = reinterpret_cast<const uint8_t *>(L.esc32);
     uint32_t *seg32 = reinterpret_cast<uint32_t *>(L.seg);
     uint32_t t = list[0];
-    uint4 q[C];
+    uint32_t tn = 1 < count ? list[1] : t;
+    uint4 qa[C], qb[C];
     uint32_t m[C], ea[C], eb[C];
-    load_tile_part_bf16<C>(in, n, t, q);
-    uint32_t lane_total = tile_part_escapes_bf16<C>(q, esc8, n, t, m, ea, eb);
-#pragma unroll 1
-    for (uint32_t i = 0; i < count; ++i) {
-        // the next tile (this one again after the last: no branch around the loads)
-        const uint32_t tn = i + 1 < count ? list[i + 1] : t;
-        load_tile_part_bf16<C>(in, n, tn, q);
+    load_tile_part_bf16<C>(in, n, t, qa);
+    load_tile_part_bf16<C>(in, n, tn, qb);
+    uint32_t lane_total = tile_part_escapes_bf16<C>(qa, esc8, n, t, m, ea, eb);
+    // tile t = list[i] (its masks in m, ea, eb); cur held its words and now
+    // takes tile i + 2's, nxt holds tile i + 1's
+    auto body = [&](uint4 (&cur)[C], uint4 (&nxt)[C], uint32_t i) {
+        // the tile after next (the last again past the end: no branch around the loads)
+        const uint32_t tn2 = i + 2 < count ? list[i + 2] : tn;
+        load_tile_part_bf16<C>(in, n, tn2, cur);
         const uint32_t base = t * kEncTile + wave * (512 * C);     // low bits: the block positions
         const uint64_t first = tile_first_record(tile_counts, block_offsets, t);
         const uint32_t wave_total = read_lane63(wave_inclusive_sum(lane_total));
@@ -1586,8 +1672,14 @@ __device__ __forceinline__ void rederive_tiles_bf16(const uint16_t *__restrict__
         }
         wr.finish(L, out);
         __syncthreads();                                          // wave_totals is reused by the next tile
-        lane_total = tile_part_escapes_bf16<C>(q, esc8, n, tn, m, ea, eb);
+        lane_total = tile_part_escapes_bf16<C>(nxt, esc8, n, tn, m, ea, eb);
         t = tn;
+        tn = tn2;
+    };
+#pragma unroll 1
+    for (uint32_t i = 0; i < count; i += 2) {
+        body(qa, qb, i);
+        if (i + 1 < count) body(qb, qa, i + 1);
     }
 }
 
@@ -1617,7 +1709,7 @@ __device__ __forceinline__ uint32_t list_flagged_tiles(const uint32_t *__restric
 }
 
 template <int DT>
-__global__ __launch_bounds__(kRederiveThreads) __attribute__((amdgpu_waves_per_eu(6))) void sz_enc_compact(
+__global__ __launch_bounds__(kRederiveThreads) __attribute__((amdgpu_waves_per_eu(4))) void sz_enc_compact(
     const uint8_t *__restrict__ stage, const uint32_t *__restrict__ tile_counts,
     const uint64_t *__restrict__ block_offsets, uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
     uint64_t nb, uint32_t item, uint32_t slot, const void *__restrict__ in, uint64_t n, Codebook4 cb,
@@ -1632,17 +1724,19 @@ __global__ __launch_bounds__(kRederiveThreads) __attribute__((amdgpu_waves_per_e
     // their latency hides behind the copies)
     uint32_t any_flagged = 0;
     for (uint32_t i = lane_id(); i < flag_words; i += 64) any_flagged |= flagged[i];
-    // staged records: wave w of workgroup g copies blocks 8 g + w, 8 (g + G) + w,
-    // ...; the next block's metadata is fetched before the current block's
-    // records are copied
+    // staged records: wave w of workgroup g copies the blocks b = 8 g + w +
+    // 8 G i, two at a time (b and b + 8 G); the next pair's metadata is
+    // fetched before the current pair's records are copied
     {
         const uint64_t stride = (uint64_t)gridDim.x * kWaves;
         uint64_t b = (uint64_t)blockIdx.x * kWaves + wave;
-        uint64_t meta = b < nb ? block_meta(tile_counts, block_offsets, nt, b) : 0;
+        uint64_t meta = b < nb ? pair_meta(tile_counts, block_offsets, nt, nb, b, b + stride) : 0;
         while (b < nb) {                                           // wave-uniform
-            const uint64_t b_next = b + stride;
-            const uint64_t meta_next = b_next < nb ? block_meta(tile_counts, block_offsets, nt, b_next) : 0;
-            copy_block_records(meta, stage, out, off_esc, nt, b, item, slot);
+            const uint64_t b_next = b + 2 * stride;
+            const uint64_t meta_next =
+                b_next < nb ? pair_meta(tile_counts, block_offsets, nt, nb, b_next, b_next + stride) : 0;
+            copy_pair_records(meta, tile_counts, block_offsets, stage, out, off_esc, nt, nb, b, b + stride, item,
+                              slot);
             meta = meta_next;
             b = b_next;
         }
