@@ -239,6 +239,83 @@ def test_tile_escape_counts_around_staging_limits(dtype, clustered):
     assert streamfmt.header(expect)["escapes"] == int(want.sum())
 
 
+# Record counts around the compaction's copy limits: 256 (8-lane groups, two
+# blocks per wave), 1,024 (16-lane groups) and 4,096 (staging; a heavier
+# tile is re-derived from the input).
+PAIR_COUNTS = [1, 255, 256, 257, 1024, 1025, 4096, 4097]
+
+
+def _escape_stream(dtype, n, rng):
+    """A stream of n escape-free values, a value generator for escapes and
+    the codebook that makes them so."""
+    if dtype == 0:
+        bits = np.full(n, 0x3F80, dtype=np.uint16)            # exponent 127
+        esc_val = lambda m: (0x0080 | (rng.integers(0, 2, m) << 15) | rng.integers(0, 128, m)).astype(np.uint16)
+        cb = np.array([127] + list(range(100, 115)), dtype=np.uint8)
+    else:
+        bits = np.full(n, 0x3C, dtype=np.uint8)               # exponent 15
+        esc_val = lambda m: (0x04 | (rng.integers(0, 2, m) << 7) | rng.integers(0, 4, m)).astype(np.uint8)
+        cb = np.array([15] + list(range(16, 31)), dtype=np.uint8)
+    return bits, esc_val, cb
+
+
+def _set_tile_escapes(bits, fill, esc_val, rng, tile, k):
+    """Tile `tile` gets exactly k escapes (at random places) and no others."""
+    lo, hi = tile * 16384, min((tile + 1) * 16384, bits.size)
+    bits[lo:hi] = fill
+    k = min(k, hi - lo)
+    bits[lo + rng.choice(hi - lo, size=k, replace=False)] = esc_val(k)
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_paired_block_copies(dtype):
+    """A stream above 4,096 blocks, where a compaction wave copies the staged
+    records of blocks b and b + 4,096 at once (512 workgroups of eight
+    waves): every tile holds a few escapes, and tiles with the record counts
+    of PAIR_COUNTS sit in the first block of a pair, in the second, in both,
+    and in blocks without a partner."""
+    rng = np.random.default_rng(71 + dtype)
+    nb = 4096 + 300
+    n = nb * 65536 - 4321
+    bits, esc_val, cb = _escape_stream(dtype, n, rng)
+    fill = bits[0]
+    nt = (n + 16383) // 16384
+    for t in range(nt):                                       # light records everywhere
+        _set_tile_escapes(bits, fill, esc_val, rng, t, 3)
+    heavy = {}
+    for i, k in enumerate(PAIR_COUNTS):
+        for b in (5 + 9 * i,                                  # first block of a pair
+                  4096 + 100 + 9 * i,                         # second block of a pair
+                  200 + 9 * i, 4096 + 200 + 9 * i,            # both blocks of one pair
+                  1000 + 37 * i):                             # no partner (b + 4096 >= nb)
+            heavy[4 * b + i % 4] = k
+    for t, k in heavy.items():
+        _set_tile_escapes(bits, fill, esc_val, rng, t, k)
+    expect = roundtrip_check(bits, dtype, cb)
+    escaped = bits != fill
+    assert streamfmt.header(expect)["escapes"] == int(np.count_nonzero(escaped))
+    per_block = np.add.reduceat(escaped, np.arange(0, n, 65536))
+    assert np.array_equal(streamfmt.sections(expect)["counts"], per_block)
+
+
+@pytest.mark.parametrize("where", ["first", "last"])
+def test_one_flagged_tile_past_8192_blocks(where):
+    """Above 8,192 blocks the scan runs in two workgroups; a single tile
+    heavy enough to be re-derived, the stream's first or its last, must still
+    make the compaction re-derive it (the scan's flagged-tile words)."""
+    rng = np.random.default_rng(5 if where == "first" else 6)
+    nb = 8192 + 24
+    n = nb * 65536 - 999
+    bits, esc_val, cb = _escape_stream(0, n, rng)
+    fill = bits[0]
+    nt = (n + 16383) // 16384
+    tile = 0 if where == "first" else nt - 1
+    _set_tile_escapes(bits, fill, esc_val, rng, tile, 9000)
+    _set_tile_escapes(bits, fill, esc_val, rng, nt // 2, 17)     # one light tile elsewhere
+    expect = roundtrip_check(bits, 0, cb)
+    assert streamfmt.header(expect)["escapes"] == 9000 + 17
+
+
 def test_single_escapes_at_block_edges():
     n = 3 * 65536
     bits = np.full(n, 0x3F80, dtype=np.uint16)
