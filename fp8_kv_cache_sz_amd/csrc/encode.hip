@@ -1,7 +1,8 @@
 // SplitZip encode for MI355X: the dense kernels (codes, sign/mantissa
-// bytes, escape staging), the ordering of the escape records (one-workgroup
-// scan + compaction, or for small streams one compaction launch that finds
-// its own offsets), the stream header, and the encode entry points of the
+// bytes, escape staging), the ordering of the escape records (a scan, one
+// workgroup per 8,192 blocks, + compaction, or for small streams one
+// compaction launch that finds its own offsets), the stream header, and the
+// encode entry points of the
 // C ABI ("SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
 // Serving", gist.science summary page, Method, encoding bullets).
 #include "common.hpp"
