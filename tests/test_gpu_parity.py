@@ -298,13 +298,13 @@ def test_paired_block_copies(dtype):
     assert np.array_equal(streamfmt.sections(expect)["counts"], per_block)
 
 
-@pytest.mark.parametrize("where", ["first", "last"])
-def test_one_flagged_tile_past_8192_blocks(where):
-    """Above 8,192 blocks the scan runs in two workgroups; a single tile
-    heavy enough to be re-derived, the stream's first or its last, must still
-    make the compaction re-derive it (the scan's flagged-tile words)."""
-    rng = np.random.default_rng(5 if where == "first" else 6)
-    nb = 8192 + 24
+@pytest.mark.parametrize("where,nb", [("first", 8216), ("last", 8216), ("last", 8193)])
+def test_one_flagged_tile_past_8192_blocks(where, nb):
+    """Above 8,192 blocks the scan runs in two workgroups (the second one
+    holding a single block at 8,193); a single tile heavy enough to be
+    re-derived, the stream's first or its last, must still make the
+    compaction re-derive it (the scan's flagged-tile words)."""
+    rng = np.random.default_rng(nb + (5 if where == "first" else 6))
     n = nb * 65536 - 999
     bits, esc_val, cb = _escape_stream(0, n, rng)
     fill = bits[0]
