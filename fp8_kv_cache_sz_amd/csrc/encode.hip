@@ -1410,8 +1410,8 @@ __device__ __forceinline__ uint64_t block_meta(const uint32_t *__restrict__ tile
 // the four tiles at once when none is flagged and none holds more than
 // kGroupCopyRecords records, else the wave copies them tile after tile.
 __device__ __forceinline__ void copy_block_records(uint64_t meta, const uint8_t *__restrict__ stage,
-                                                   uint8_t *__restrict__ out, uint64_t off_esc, uint64_t nt,
-                                                   uint64_t b, uint32_t item, uint32_t slot)
+                                                   uint8_t *__restrict__ out, uint64_t off_esc, uint64_t b,
+                                                   uint32_t item, uint32_t slot)
 {
     const uint32_t lane = lane_id();
     const uint64_t t0 = kTilesPerBlock * b;
@@ -1515,9 +1515,9 @@ __device__ __forceinline__ void copy_pair_records(uint64_t meta, const uint32_t 
                          item * k, lane & 7u, 8);
         return;
     }
-    copy_block_records(block_meta(tile_counts, block_offsets, nt, b0), stage, out, off_esc, nt, b0, item, slot);
+    copy_block_records(block_meta(tile_counts, block_offsets, nt, b0), stage, out, off_esc, b0, item, slot);
     if (b1 < nb)
-        copy_block_records(block_meta(tile_counts, block_offsets, nt, b1), stage, out, off_esc, nt, b1, item, slot);
+        copy_block_records(block_meta(tile_counts, block_offsets, nt, b1), stage, out, off_esc, b1, item, slot);
 }
 
 // ---------------------------------------------------------------------------
