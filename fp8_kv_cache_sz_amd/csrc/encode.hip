@@ -1721,10 +1721,11 @@ __global__ __launch_bounds__(kRederiveThreads) __attribute__((amdgpu_waves_per_e
     __shared__ uint32_t list[kRederiveThreads];
     __shared__ uint32_t wave_sums[kWaves];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-    // whether the scan saw a flagged tile (its words are loaded first, so that
-    // their latency hides behind the copies)
+    // whether the scan saw a flagged tile: the workgroup's lanes share the
+    // scan's words (loaded first, so that their latency hides behind the
+    // copies) and meet after the copies
     uint32_t any_flagged = 0;
-    for (uint32_t i = lane_id(); i < flag_words; i += 64) any_flagged |= flagged[i];
+    for (uint32_t i = threadIdx.x; i < flag_words; i += kRederiveThreads) any_flagged |= flagged[i];
     // staged records: wave w of workgroup g copies the blocks b = 8 g + w +
     // 8 G i, two at a time (b and b + 8 G); the next pair's metadata is
     // fetched before the current pair's records are copied
@@ -1742,7 +1743,7 @@ __global__ __launch_bounds__(kRederiveThreads) __attribute__((amdgpu_waves_per_e
             b = b_next;
         }
     }
-    if (!__any(any_flagged)) return;                               // the same in every wave
+    if (!__syncthreads_or(any_flagged)) return;                   // workgroup-uniform
     RederiveLds &L = lds[wave];
     // flagged tiles: workgroup g takes the tiles g, g + G, g + 2G, ...: the
     // tiles that the workgroups work on at one time lie next to each other in
