@@ -316,6 +316,47 @@ def test_one_flagged_tile_past_8192_blocks(where, nb):
     assert streamfmt.header(expect)["escapes"] == 9000 + 17
 
 
+# Streams above 128 blocks decode BF16 in 8192-element spans (256 lanes,
+# four chunks each; each span's records checked in a window around its share
+# of the block's records).  Last blocks of every length class around the
+# 2048-element chunk rows and the span edges.
+WIDE_TAILS = [1, 2047, 2048, 2049, 8191, 8192, 8193, 30001, 65535, 65536]
+
+
+@pytest.mark.parametrize("tail", WIDE_TAILS)
+def test_wide_decode_block_tails(tail):
+    """Escapes on both sides of every 2048-element edge (first block, last
+    full block, last block), a block where every element escapes (windows far
+    above the light limit), a block with about 3,500 scattered escapes, and a
+    run of 5,000 crossing a span edge (the windows miss it, the search finds
+    it)."""
+    rng = np.random.default_rng(tail + 101)
+    full = 130
+    n = full * 65536 + tail
+    bits = np.full(n, 0x3F80, dtype=np.uint16)                # exponent 127, in the book
+    esc_val = lambda m: (0x0080 | (rng.integers(0, 2, m) << 15) | rng.integers(0, 128, m)).astype(np.uint16)
+    cb = np.array([127] + list(range(100, 115)), dtype=np.uint8)
+    last0 = full * 65536                                      # first element of the last block
+    edges = []
+    for b0 in (0, (full - 1) * 65536, full * 65536):
+        for m in range(33):
+            for p in (b0 + 2048 * m - 1, b0 + 2048 * m):
+                if b0 <= p < min(b0 + 65536, n):
+                    edges.append(p)
+    edges = np.array(sorted(set(edges)))
+    bits[edges] = esc_val(edges.size)
+    heavy = 5 * 65536
+    bits[heavy:heavy + 65536] = esc_val(65536)
+    scattered = 7 * 65536 + rng.choice(65536, 3500, replace=False)
+    bits[scattered] = esc_val(3500)
+    run = 9 * 65536 + 8192 - 2000
+    bits[run:run + 5000] = esc_val(5000)
+    tail_hits = last0 + rng.choice(n - last0, min(n - last0, 300), replace=False)
+    bits[tail_hits] = esc_val(tail_hits.size)
+    expect = roundtrip_check(bits, 0, cb)
+    assert streamfmt.header(expect)["escapes"] == int(np.count_nonzero(bits != 0x3F80))
+
+
 def test_single_escapes_at_block_edges():
     n = 3 * 65536
     bits = np.full(n, 0x3F80, dtype=np.uint16)
