@@ -49,10 +49,12 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
+    """The oracle library; SPLITZIP_ORACLE_LIB names another build of the
+    same source to load instead (the sanitizer test's instrumented copy)."""
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("SPLITZIP_ORACLE_LIB") or build()
+        L = ctypes.CDLL(path)
         u64, i64, vp, i32 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.szo_encoded_size.argtypes = [i32, u64, u64]
         L.szo_encoded_size.restype = u64
