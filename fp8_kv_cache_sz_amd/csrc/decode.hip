@@ -274,7 +274,8 @@ __device__ __forceinline__ uint4 assemble_bf16(uint2 sm, uint2 ex)
 // overwrites plane[pos - lo] with the exponent of each whose position lies in
 // [lo, lo + span); invalid records (position out of the block or not
 // ascending, exponent out of range) are skipped and reported through the
-// status word.
+// status word.  The `lanes` lanes that call it (the workgroup, or one wave)
+// share the work; `me` is the caller's index among them.
 // The stream's records are taken in aligned groups of 16 (48 bytes, three dwordx4 loads
 // per lane; a group never straddles a lane, so no byte realignment is
 // needed), G groups per lane in flight at once.  Record R of the stream
@@ -285,18 +286,19 @@ template <uint32_t G>
 __device__ __forceinline__ void overwrite_exponents_grouped(const uint8_t *__restrict__ esc, uint64_t r0, uint32_t i0,
                                                             uint32_t i1, uint32_t blen, uint32_t symbols,
                                                             uint64_t e_total, uint8_t *plane, uint32_t lo,
-                                                            uint32_t span, int32_t *__restrict__ status)
+                                                            uint32_t span, int32_t *__restrict__ status,
+                                                            uint32_t lanes, uint32_t me)
 {
     if (i0 >= i1) return;
     const uint64_t first = r0 + i0, last = r0 + i1;              // stream record range [first, last)
     const uint64_t gA = first >> 4;
     const uint32_t groups = (uint32_t)(((last - 1) >> 4) - gA + 1);
     bool bad = false;
-    for (uint32_t g0 = 0; g0 < groups; g0 += G * blockDim.x) {
+    for (uint32_t g0 = 0; g0 < groups; g0 += G * lanes) {
         uint32_t w[G][13], prev[G];
 #pragma unroll
         for (uint32_t k = 0; k < G; ++k) {
-            const uint32_t g = g0 + k * blockDim.x + threadIdx.x;
+            const uint32_t g = g0 + k * lanes + me;
             const uint64_t R0 = (gA + g) * 16;
             w[k][12] = 0;
             prev[k] = 0;
@@ -322,7 +324,7 @@ __device__ __forceinline__ void overwrite_exponents_grouped(const uint8_t *__res
         }
 #pragma unroll
         for (uint32_t k = 0; k < G; ++k) {
-            const uint32_t g = g0 + k * blockDim.x + threadIdx.x;
+            const uint32_t g = g0 + k * lanes + me;
             if (g >= groups) continue;
             const uint64_t R0 = (gA + g) * 16;
             uint32_t before = prev[k];
@@ -551,9 +553,20 @@ constexpr uint64_t kSpanWideBlocks = 128;
 // lane, each lane loads the aligned words of its four records and the record
 // before them, and every lane loads both guard records, all without branches
 // (lanes with nothing to load read the stream header instead).  apply() runs
-// after the dense exponents are in the plane.
-template <uint32_t SPAN, uint32_t T>
+// after the dense exponents are in the plane.  With kWave one wave handles the
+// records of its span on its own (counts by ballot, no workgroup barrier).
+template <uint32_t SPAN, uint32_t T, bool kWave = false>
 struct SpanEscapes {
+    // the lanes that handle the records: the workgroup's T, or one wave
+    static_assert(!kWave || T == 64, "a wave has 64 lanes");
+    static __device__ __forceinline__ uint32_t me() { return kWave ? lane_id() : threadIdx.x; }
+    static __device__ __forceinline__ uint32_t count(bool p)
+    {
+        if constexpr (kWave)
+            return (uint32_t)__popcll(__ballot(p));
+        else
+            return (uint32_t)__syncthreads_count(p);
+    }
     static constexpr uint32_t kLog2D = kLog2Block - __builtin_ctz(SPAN);
     static_assert((kBlock >> kLog2D) == SPAN && SPAN >= 512, "span: a power of two of 512 elements or more");
     // the search samples 256 records (kSamples per lane) and its brackets
@@ -583,7 +596,7 @@ struct SpanEscapes {
         w0 = share_lo > margin ? share_lo - margin : 0;
         w1 = std::min(share_hi + margin, k);
         light = w1 - w0 <= 4 * T;
-        const uint32_t r = w0 + 4 * threadIdx.x;
+        const uint32_t r = w0 + 4 * me();
         const bool mine = light && r < w1;
         fast = mine && r0 + r + 5 < e_total;
         const uint32_t *wp = fast ? reinterpret_cast<const uint32_t *>(esc + ((3 * (r0 + r)) & ~uint64_t(3)))
@@ -599,7 +612,7 @@ struct SpanEscapes {
 
     __device__ __forceinline__ void apply(uint8_t *plane, uint32_t symbols, int32_t *__restrict__ status) const
     {
-        const uint32_t tid = threadIdx.x;
+        const uint32_t tid = me();
         const uint32_t hi = lo + SPAN;
         if (light) {
             const uint32_t r = w0 + 4 * tid;
@@ -631,7 +644,7 @@ struct SpanEscapes {
             if (bad) atomicExch(status, SZ_E_FORMAT);
         } else {
             overwrite_exponents_grouped<kRecordGroups>(esc, r0, w0, w1, blen, symbols, e_total, plane, lo, SPAN,
-                                                       status);
+                                                       status, T, tid);
         }
         if (!((w0 > 0 && g_lo >= lo) || (w1 < k && g_hi < hi))) return;      // workgroup-uniform
         const uint32_t stride = (k + kSamples * T - 1) / (kSamples * T);       // 1 .. 256
@@ -640,8 +653,8 @@ struct SpanEscapes {
         for (uint32_t m = 0; m < kSamples; ++m) {
             const uint32_t i = (tid + m * T) * stride;
             const uint32_t p = i < k ? record_pos(esc, r0 + i) : 0xFFFFFFFFu;
-            c_lo += __syncthreads_count(p < lo);
-            c_hi += __syncthreads_count(p < hi);
+            c_lo += count(p < lo);
+            c_hi += count(p < hi);
         }
         // The number of records below x is 0 when no sample is below x
         // (c = 0), else it lies in ((c - 1) stride, min(c stride, k)]: the
@@ -654,11 +667,11 @@ struct SpanEscapes {
             const uint32_t i = tid + m * T;
             const uint32_t q_lo = b_lo + i < e_lo ? record_pos(esc, r0 + b_lo + i) : 0xFFFFFFFFu;
             const uint32_t q_hi = b_hi + i < e_hi ? record_pos(esc, r0 + b_hi + i) : 0xFFFFFFFFu;
-            first += __syncthreads_count(q_lo < lo);
-            last += __syncthreads_count(q_hi < hi);
+            first += count(q_lo < lo);
+            last += count(q_hi < hi);
         }
         overwrite_exponents_grouped<kRecordGroups>(esc, r0, first, last, blen, symbols, e_total, plane, lo, SPAN,
-                                                   status);
+                                                   status, T, tid);
     }
 };
 
@@ -678,9 +691,10 @@ __device__ __forceinline__ void bf16_span_decode(const uint8_t *__restrict__ in,
     if (verdict[0] != 0) return;
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x / kSpans;
-    const uint32_t lo = (blockIdx.x % kSpans) * kSpan;            // block-local; the grid keeps lo < blen
+    const uint32_t lo = (blockIdx.x % kSpans) * kSpan;            // block-local
     const uint64_t e0 = b * kBlock;
     const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
+    if (lo >= blen) return;                                       // the strided grid's extra workgroups
     const bool full = lo + kSpan <= blen;
     const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
     const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
@@ -744,13 +758,114 @@ __device__ __forceinline__ void bf16_span_decode(const uint8_t *__restrict__ in,
     }
 }
 
-template <int T, int CPL>
+// Strided BF16 span decode (Top-16).  A block is cut into 32 sub-spans of
+// 2048 elements (4 KB of output each); workgroup r of the block's G = 32 / CPL
+// workgroups decodes the CPL sub-spans r, r + G, r + 2G, ... rather than one
+// contiguous span: lane t holds element 8t of each (one chunk per sub-span).
+// The GPU deals workgroup i to XCD i mod 8, so every workgroup on an XCD
+// writes output 4 KB pieces of one residue modulo 8.  On MI355X the
+// decoder's loads and stores with trivial arithmetic stream at about 79 % of
+// the HBM peak in this layout against 71 % in contiguous 8192-element spans.
+// Wave w < CPL handles the escape records of sub-span w (its window as in
+// SpanEscapes, with D = 32) in the plane's w-th 2 KB.  The grid holds G
+// workgroups per block, and ceil(len / 2048) up to G for a last block of len
+// elements, so every workgroup's first sub-span starts inside its block.
+template <int CPL>
+__device__ __forceinline__ void bf16_strided_decode(const uint8_t *__restrict__ in, const DecodeArgs &a,
+                                                    const uint64_t *__restrict__ block_offsets,
+                                                    int32_t *__restrict__ status,
+                                                    const int32_t *__restrict__ verdict, uint16_t *__restrict__ out)
+{
+    constexpr uint32_t kSub = 2048;
+    constexpr uint32_t kGroups = kBlock / (kSub * CPL);            // workgroups per block, the sub-span stride
+    static_assert(kGroups * kSub * CPL == kBlock && CPL <= 4, "CPL sub-spans of 2048 elements, one wave each");
+    __shared__ __align__(16) uint8_t plane[CPL * kSub];
+    if (verdict[0] != 0) return;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t wave = tid / 64;
+    const uint64_t b = blockIdx.x / kGroups;
+    const uint32_t r = blockIdx.x % kGroups;                        // the grid keeps r kSub < blen
+    const uint64_t e0 = b * kBlock;
+    const uint32_t blen = (uint32_t)std::min<uint64_t>(kBlock, a.n - e0);
+    const bool full = blen == kBlock;
+    const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[b];
+    const uint64_t e_total = *reinterpret_cast<const uint64_t *>(in + 16);
+    const uint32_t *cbw = reinterpret_cast<const uint32_t *>(in + 32);
+    const CodebookRegs cb = {cbw[0], cbw[1], cbw[2], cbw[3]};
+    const uint8_t *nib_base = in + a.off_nib;
+    const uint8_t *sm_base = in + a.off_sm;
+    // chunk j of a lane: block-local element (r + G j) kSub + 8 tid; lanes
+    // past the block's end load the first sub-span's first chunk, unused
+    uint32_t code[CPL];
+    uint2 sm[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t c = (r + kGroups * j) * kSub + tid * 8;
+        const uint64_t g = e0 + (full || c < blen ? c : r * kSub);
+        code[j] = load_nt(reinterpret_cast<const uint32_t *>(nib_base + g / 2));
+        sm[j] = load_nt(reinterpret_cast<const uint2 *>(sm_base + g));
+    }
+    const uint64_t r0 = block_offsets[b];
+    const uint32_t my_lo = (r + kGroups * wave) * kSub;             // the sub-span whose records this wave handles
+    const bool owner = wave < CPL && my_lo < blen;                  // wave-uniform
+    SpanEscapes<kSub, 64, true> records;
+    if (k && owner) records.issue(in, a.off_esc, r0, k, blen, my_lo, e_total);
+    uint2 ex[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) ex[j] = lookup_codes8(code[j], cb);
+    if (k) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) *reinterpret_cast<uint2 *>(plane + j * kSub + tid * 8) = ex[j];
+        __syncthreads();
+        if (owner) records.apply(plane + wave * kSub, 256, status);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) ex[j] = *reinterpret_cast<const uint2 *>(plane + j * kSub + tid * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t c = (r + kGroups * j) * kSub + tid * 8;
+        if (!full && c >= blen) continue;
+        const uint4 o = assemble_bf16(sm[j], ex[j]);
+        const uint64_t g = e0 + c;
+        if (full || c + 8 <= blen) {
+            store_nt(reinterpret_cast<uint4 *>(out + g), o);
+        } else {
+            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+            for (uint32_t i = 0; i < blen - c; ++i) out[g + i] = (uint16_t)(w[i / 2] >> (16 * (i & 1)));
+        }
+    }
+}
+
+// Blocks of at most this many records take the strided layout (every wave's
+// window then holds at most 64 + 145 records: one four-record group per
+// lane); heavier blocks are decoded in the same grid as contiguous
+// 8192-element spans, whose single window per workgroup reads fewer
+// records than four per-wave windows would (workgroups past the last
+// block's end then have nothing to do).
+constexpr uint32_t kStridedRecords = 2048;
+
+// kStrided (T = 256, CPL = 4): eight workgroups per block, each decoding
+// the block's sub-spans r, r + 8, r + 16, r + 24 when the block has at most
+// kStridedRecords records, else the block's 8192-element span r.
+template <int T, int CPL, bool kStrided = false>
 __global__ __launch_bounds__(T) void sz_dec_bf16_span(const uint8_t *__restrict__ in, DecodeArgs a,
                                                       const uint64_t *__restrict__ block_offsets,
                                                       int32_t *__restrict__ status,
                                                       const int32_t *__restrict__ verdict, uint16_t *__restrict__ out)
 {
-    bf16_span_decode<T, CPL, kTop16>(in, a, block_offsets, status, verdict, out);
+    if constexpr (kStrided) {
+        static_assert(T == 256 && CPL == 4, "eight workgroups of 256 lanes per block in either layout");
+        // the block's record count (inside the count section of any stream
+        // the host accepted; both layouts check the verdict before use)
+        const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[blockIdx.x / 8];
+        if (k <= kStridedRecords)
+            bf16_strided_decode<CPL>(in, a, block_offsets, status, verdict, out);
+        else
+            bf16_span_decode<T, CPL, kTop16>(in, a, block_offsets, status, verdict, out);
+    } else {
+        bf16_span_decode<T, CPL, kTop16>(in, a, block_offsets, status, verdict, out);
+    }
 }
 
 template <int T, int CPL>
@@ -949,10 +1064,25 @@ __global__ __launch_bounds__(256) void sz_ref_join(const uint8_t *__restrict__ c
 // BF16 span shape by stream size: 4096-element spans up to kSpanWideBlocks
 // blocks, 16384-element spans (eight chunks per lane) from 256 to 384 blocks
 // (16M-24M elements: half the workgroups of the 8192-element grid, which
-// there decode 3 us slower, about 15 %, on MI355X; at 12M and at 32M the
-// 8192-element spans are faster again), 8192-element spans otherwise.
+// there decode 3 us slower, about 15 %, on MI355X, and the strided grid 14-19 %
+// slower; at 12M and at 32M the eight-workgroup grids are faster again);
+// otherwise eight workgroups per block: the strided/contiguous grid for Top-16
+// (on the long-context payload 6 % faster than contiguous spans alone),
+// 8192-element spans for Top-8.
 constexpr uint64_t kSpanHugeFirst = 256, kSpanHugeLast = 384;
 constexpr int kBf16HugeChunks = 8;
+
+// The strided Top-16 grid: eight workgroups per block, ceil(len / 2048) up
+// to eight for a last block of len elements.
+void launch_bf16_strided(const uint8_t *in, const DecodeArgs &a, const DecodeScratch &w, void *d_out, hipStream_t s)
+{
+    constexpr uint64_t kGroups = 8;
+    const uint64_t last = a.n - (a.nb - 1) * kBlock;                // elements of the last block, 1 .. kBlock
+    const uint64_t grid = (a.nb - 1) * kGroups + std::min<uint64_t>(kGroups, (last + 2047) / 2048);
+    hipLaunchKernelGGL((sz_dec_bf16_span<kBf16WideThreads, kBf16WideChunks, true>), dim3((uint32_t)grid),
+                       dim3(kBf16WideThreads), 0, s, in, a, w.block_offsets, w.status, w.verdict,
+                       static_cast<uint16_t *>(d_out));
+}
 
 template <int V>
 void launch_bf16_spans(const uint8_t *in, const DecodeArgs &a, const DecodeScratch &w, void *d_out, hipStream_t s)
@@ -961,6 +1091,8 @@ void launch_bf16_spans(const uint8_t *in, const DecodeArgs &a, const DecodeScrat
         launch_span<kBf16SpanThreads, kBf16SpanChunks, SZ_BF16, V>(in, a, w, d_out, s);
     else if (a.nb >= kSpanHugeFirst && a.nb <= kSpanHugeLast)
         launch_span<kBf16WideThreads, kBf16HugeChunks, SZ_BF16, V>(in, a, w, d_out, s);
+    else if (V == kTop16)
+        launch_bf16_strided(in, a, w, d_out, s);
     else
         launch_span<kBf16WideThreads, kBf16WideChunks, SZ_BF16, V>(in, a, w, d_out, s);
 }

@@ -316,20 +316,23 @@ def test_one_flagged_tile_past_8192_blocks(where, nb):
     assert streamfmt.header(expect)["escapes"] == 9000 + 17
 
 
-# Streams above 128 blocks decode BF16 in 8192-element spans (256 lanes,
-# four chunks each; each span's records checked in a window around its share
-# of the block's records).  Last blocks of every length class around the
-# 2048-element chunk rows and the span edges.
-WIDE_TAILS = [1, 2047, 2048, 2049, 8191, 8192, 8193, 30001, 65535, 65536]
+# Streams above 128 blocks decode BF16 with eight workgroups per block: a
+# block of at most 2048 records in strided 2048-element sub-spans (workgroup
+# r: sub-spans r, r + 8, r + 16, r + 24, one wave per sub-span's records), a
+# heavier one in contiguous 8192-element spans; the last block gets only as
+# many workgroups as it has sub-spans (up to 8).  Last blocks of every length
+# class around the sub-span and span edges.
+WIDE_TAILS = [1, 2047, 2048, 2049, 8191, 8192, 8193, 8 * 2048 + 1, 30001, 65535, 65536]
 
 
 @pytest.mark.parametrize("tail", WIDE_TAILS)
 def test_wide_decode_block_tails(tail):
     """Escapes on both sides of every 2048-element edge (first block, last
-    full block, last block), a block where every element escapes (windows far
-    above the light limit), a block with about 3,500 scattered escapes, and a
-    run of 5,000 crossing a span edge (the windows miss it, the search finds
-    it)."""
+    full block, last block); blocks of 2,048 and 2,049 scattered escapes (the
+    two layouts' limit), 3,500 scattered and 65,536 (every element); a run
+    of 1,500 across two sub-spans (strided: the per-wave windows miss it
+    and the per-wave search finds it) and a run of 5,000 across a span edge
+    (contiguous: the same for the workgroup's window)."""
     rng = np.random.default_rng(tail + 101)
     full = 130
     n = full * 65536 + tail
@@ -345,15 +348,19 @@ def test_wide_decode_block_tails(tail):
                     edges.append(p)
     edges = np.array(sorted(set(edges)))
     bits[edges] = esc_val(edges.size)
-    heavy = 5 * 65536
-    bits[heavy:heavy + 65536] = esc_val(65536)
-    scattered = 7 * 65536 + rng.choice(65536, 3500, replace=False)
-    bits[scattered] = esc_val(3500)
+    bits[5 * 65536:6 * 65536] = esc_val(65536)
+    for blk, m in ((7, 3500), (8, 2048), (11, 2049)):
+        where = blk * 65536 + rng.choice(65536, m, replace=False)
+        bits[where] = esc_val(m)
     run = 9 * 65536 + 8192 - 2000
     bits[run:run + 5000] = esc_val(5000)
+    run = 10 * 65536 + 5 * 2048 - 700
+    bits[run:run + 1500] = esc_val(1500)
     tail_hits = last0 + rng.choice(n - last0, min(n - last0, 300), replace=False)
     bits[tail_hits] = esc_val(tail_hits.size)
     expect = roundtrip_check(bits, 0, cb)
+    counts = streamfmt.sections(expect)["counts"]
+    assert [int(counts[b]) for b in (5, 7, 8, 9, 10, 11)] == [65536, 3500, 2048, 5000, 1500, 2049]
     assert streamfmt.header(expect)["escapes"] == int(np.count_nonzero(bits != 0x3F80))
 
 
