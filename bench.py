@@ -79,17 +79,25 @@ def parse_args(argv=None):
     return args
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources (every file under csrc/, in name order) with
+# the source file that defines each kernel family (every kernel also
+# includes common.hpp)
+KERNEL_SOURCES = (("sz_enc_", "encode.hip"), ("sz_dec_", "decode.hip"), ("sz_ref_join", "decode.hip"),
+                  ("sz_cal_", "calibrate.hip"), ("sz_copy_", "transfer.hip"), ("sz_ref_", "runtime.hip"))
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the source that defines `kernel` and of common.hpp, with
     comments and blank space removed, so that recorded counters stay tied to
-    the code, not to its commentary."""
+    that kernel's code, not to its commentary or to other kernels."""
     import re
     csrc = os.path.join(ROOT, "fp8_kv_cache_sz_amd", "csrc")
+    files = ["common.hpp"] + [f for p, f in KERNEL_SOURCES if kernel.startswith(p)][:1]
+    if len(files) == 1:
+        files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
     src = ""
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name)) as f:
-                src += f.read() + "\n"
+    for name in files:
+        with open(os.path.join(csrc, name)) as f:
+            src += f.read() + "\n"
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())
@@ -108,7 +116,7 @@ def load_traffic(kernel: str, workload: str):
     with open(TRAFFIC_PATH) as f:
         rec = json.load(f)
     entry = rec.get(workload, {}).get(kernel)
-    if not entry or entry.get("source_hash") != kernel_source_hash():
+    if not entry or entry.get("source_hash") != kernel_source_hash(kernel):
         return None
     return entry.get("bytes_per_launch")
 
@@ -168,7 +176,7 @@ def ingest_pmc(workload, fetch_csv, write_csv, copy_bytes):
             continue
         fk = sum(fetch[k]) / len(fetch[k])
         wk = sum(write[k]) / len(write[k])
-        entry[k] = {"source_hash": kernel_source_hash(),
+        entry[k] = {"source_hash": kernel_source_hash(k),
                     "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
                     "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
                     "bytes_per_launch": int(fk * 1024 * f_scale + wk * 1024 * w_scale)}

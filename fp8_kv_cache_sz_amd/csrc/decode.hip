@@ -845,9 +845,9 @@ __device__ __forceinline__ void bf16_strided_decode(const uint8_t *__restrict__ 
 // block's end then have nothing to do).
 constexpr uint32_t kStridedRecords = 2048;
 
-// kStrided (T = 256, CPL = 4): eight workgroups per block, each decoding
-// the block's sub-spans r, r + 8, r + 16, r + 24 when the block has at most
-// kStridedRecords records, else the block's 8192-element span r.
+// kStrided (T = 256): 32 / CPL workgroups per block, each decoding the
+// block's sub-spans r, r + G, ... (G = 32 / CPL) when the block has at most
+// kStridedRecords records, else the block's 2048 CPL-element span r.
 template <int T, int CPL, bool kStrided = false>
 __global__ __launch_bounds__(T) void sz_dec_bf16_span(const uint8_t *__restrict__ in, DecodeArgs a,
                                                       const uint64_t *__restrict__ block_offsets,
@@ -855,10 +855,10 @@ __global__ __launch_bounds__(T) void sz_dec_bf16_span(const uint8_t *__restrict_
                                                       const int32_t *__restrict__ verdict, uint16_t *__restrict__ out)
 {
     if constexpr (kStrided) {
-        static_assert(T == 256 && CPL == 4, "eight workgroups of 256 lanes per block in either layout");
+        static_assert(T == 256 && (CPL == 2 || CPL == 4), "256 lanes, 2048 CPL elements per workgroup in either layout");
         // the block's record count (inside the count section of any stream
         // the host accepted; both layouts check the verdict before use)
-        const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[blockIdx.x / 8];
+        const uint32_t k = reinterpret_cast<const uint32_t *>(in + 64)[blockIdx.x / (32 / CPL)];
         if (k <= kStridedRecords)
             bf16_strided_decode<CPL>(in, a, block_offsets, status, verdict, out);
         else
@@ -1072,14 +1072,20 @@ __global__ __launch_bounds__(256) void sz_ref_join(const uint8_t *__restrict__ c
 constexpr uint64_t kSpanHugeFirst = 256, kSpanHugeLast = 384;
 constexpr int kBf16HugeChunks = 8;
 
-// The strided Top-16 grid: eight workgroups per block, ceil(len / 2048) up
-// to eight for a last block of len elements.
+// The strided Top-16 grid: 32 / kStridedChunks workgroups per block, each
+// with kStridedChunks sub-spans (heavy blocks: 2048 kStridedChunks-element
+// spans), and ceil(len / 2048) up to that many for a last block of len
+// elements.  Four sub-spans per workgroup (eight workgroups per block); two
+// (sixteen per block) decoded the 1 GiB and long-context caches 11-13 % and
+// the escape-heavy inputs 13-21 % slower on MI355X.
+constexpr int kStridedChunks = 4;
+
 void launch_bf16_strided(const uint8_t *in, const DecodeArgs &a, const DecodeScratch &w, void *d_out, hipStream_t s)
 {
-    constexpr uint64_t kGroups = 8;
+    constexpr uint64_t kGroups = 32 / kStridedChunks;
     const uint64_t last = a.n - (a.nb - 1) * kBlock;                // elements of the last block, 1 .. kBlock
     const uint64_t grid = (a.nb - 1) * kGroups + std::min<uint64_t>(kGroups, (last + 2047) / 2048);
-    hipLaunchKernelGGL((sz_dec_bf16_span<kBf16WideThreads, kBf16WideChunks, true>), dim3((uint32_t)grid),
+    hipLaunchKernelGGL((sz_dec_bf16_span<kBf16WideThreads, kStridedChunks, true>), dim3((uint32_t)grid),
                        dim3(kBf16WideThreads), 0, s, in, a, w.block_offsets, w.status, w.verdict,
                        static_cast<uint16_t *>(d_out));
 }
