@@ -320,25 +320,35 @@ def test_one_flagged_tile_past_8192_blocks(where, nb):
 # block of at most 2048 records in strided 2048-element sub-spans (workgroup
 # r: sub-spans r, r + 8, r + 16, r + 24, one wave per sub-span's records), a
 # heavier one in contiguous 8192-element spans; the last block gets only as
-# many workgroups as it has sub-spans (up to 8).  Last blocks of every length
-# class around the sub-span and span edges.
+# many workgroups as it has sub-spans (up to 8).  E5M2 decodes them in
+# contiguous 16384-element spans (four workgroups per block, fewer in the
+# last).  Last blocks of every length class around the sub-span, row and
+# span edges.
 WIDE_TAILS = [1, 2047, 2048, 2049, 8191, 8192, 8193, 8 * 2048 + 1, 30001, 65535, 65536]
+WIDE_TAILS_E5M2 = [1, 31, 33, 2047, 2049, 16383, 16384, 16385, 32769, 49153, 65535, 65536]
 
 
-@pytest.mark.parametrize("tail", WIDE_TAILS)
-def test_wide_decode_block_tails(tail):
+@pytest.mark.parametrize("dtype,tail", [(0, t) for t in WIDE_TAILS] + [(1, t) for t in WIDE_TAILS_E5M2])
+def test_wide_decode_block_tails(dtype, tail):
     """Escapes on both sides of every 2048-element edge (first block, last
     full block, last block); blocks of 2,048 and 2,049 scattered escapes (the
     two layouts' limit), 3,500 scattered and 65,536 (every element); a run
-    of 1,500 across two sub-spans (strided: the per-wave windows miss it
-    and the per-wave search finds it) and a run of 5,000 across a span edge
+    of 1,500 across two sub-spans (strided: the per-wave windows miss it and
+    the per-wave search finds it) and a run of 5,000 across a span edge
     (contiguous: the same for the workgroup's window)."""
     rng = np.random.default_rng(tail + 101)
     full = 130
     n = full * 65536 + tail
-    bits = np.full(n, 0x3F80, dtype=np.uint16)                # exponent 127, in the book
-    esc_val = lambda m: (0x0080 | (rng.integers(0, 2, m) << 15) | rng.integers(0, 128, m)).astype(np.uint16)
-    cb = np.array([127] + list(range(100, 115)), dtype=np.uint8)
+    if dtype == 0:
+        fill = 0x3F80                                         # exponent 127, in the book
+        bits = np.full(n, fill, dtype=np.uint16)
+        esc_val = lambda m: (0x0080 | (rng.integers(0, 2, m) << 15) | rng.integers(0, 128, m)).astype(np.uint16)
+        cb = np.array([127] + list(range(100, 115)), dtype=np.uint8)
+    else:
+        fill = 0x3C                                           # exponent 15, in the book
+        bits = np.full(n, fill, dtype=np.uint8)
+        esc_val = lambda m: (0x04 | (rng.integers(0, 2, m) << 7) | rng.integers(0, 4, m)).astype(np.uint8)
+        cb = np.array([15] + list(range(16, 31)), dtype=np.uint8)
     last0 = full * 65536                                      # first element of the last block
     edges = []
     for b0 in (0, (full - 1) * 65536, full * 65536):
@@ -358,10 +368,10 @@ def test_wide_decode_block_tails(tail):
     bits[run:run + 1500] = esc_val(1500)
     tail_hits = last0 + rng.choice(n - last0, min(n - last0, 300), replace=False)
     bits[tail_hits] = esc_val(tail_hits.size)
-    expect = roundtrip_check(bits, 0, cb)
+    expect = roundtrip_check(bits, dtype, cb)
     counts = streamfmt.sections(expect)["counts"]
     assert [int(counts[b]) for b in (5, 7, 8, 9, 10, 11)] == [65536, 3500, 2048, 5000, 1500, 2049]
-    assert streamfmt.header(expect)["escapes"] == int(np.count_nonzero(bits != 0x3F80))
+    assert streamfmt.header(expect)["escapes"] == int(np.count_nonzero(bits != fill))
 
 
 def test_single_escapes_at_block_edges():
